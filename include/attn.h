@@ -1,0 +1,155 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused scaled-dot-product attention
+ * library: forward (O and the per-row logsumexp LSE) and backward (dQ, dK,
+ * dV) under generalized sliding-window masks, for dense and packed
+ * variable-length inputs.
+ *
+ * The operation is FlashAttention, the one kernel family of the AOTriton
+ * README ("Kernel Support"):  O = softmax(scale * Q K^T + mask) V and
+ * LSE_i = ln sum_{j visible} exp(scale * q_i . k_j).
+ *
+ * Mask (AOTriton 0.10b release notes, "Major Changes": generalized sliding
+ * window, negative bounds allowed; AOTriton 0.15b release notes,
+ * "Bottom-Right Aligned Sliding Windows"): with 0-based indices local to one
+ * sequence, key j is visible to query i iff  i - L <= j <= i + R.  L and R
+ * are window_left and window_right, except that under ATTN_BOTTOM_RIGHT a
+ * window whose both sides are finite becomes L = wl - d, R = wr + d with
+ * d = seqlen_k - seqlen_q of that sequence.  A window with an unbounded side
+ * (ATTN_WINDOW_INF; causal is (ATTN_WINDOW_INF, 0)) is never shifted.
+ *
+ * Rows with no visible key get O = 0 (only the head_dim columns are written)
+ * and LSE = +inf, as in the early-exit fixes of the AOTriton 0.15b and 0.14b
+ * release notes ("Kernel Bug Fixes"); their dQ is 0, and keys seen by no row
+ * get dK = dV = 0.
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers are device pointers, owned by the caller, and must stay
+ *    valid until the work enqueued on `stream` has finished.  The library
+ *    allocates nothing and keeps no pointer after returning.
+ *  - Calls are asynchronous on `stream`; the device is the stream's device
+ *    (hipStreamGetDevice), not the calling thread's current device (the
+ *    AOTriton 0.14b release notes, "Runtime Bug Fixes").  The null stream
+ *    means the current device's null stream.
+ *  - Every output element is overwritten; nothing needs pre-zeroing.
+ *  - Errors are returned, never printed: hipErrorInvalidValue for a malformed
+ *    call (null required pointer, version or flags mismatch, negative or
+ *    zero sizes where a size is needed, unit-stride or 16-byte alignment
+ *    violated, workspace too small), hipErrorNotSupported for a well-formed
+ *    call outside the built set (head_dim not in {64, 80, 128}), or the HIP
+ *    error of the launch.  Validation makes no HIP call.  The contents of
+ *    cu_seqlens arrays are a precondition (0 first, non-decreasing, last
+ *    entry equal to total_q / total_k, every length <= the seqlen_q /
+ *    seqlen_k maximum) and are not checked: reading them would need a sync.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Version of the params structs below; a mismatch is hipErrorInvalidValue
+ * (the versioned-params idea of the AOTriton 0.15b release notes, "API
+ * Changes": kVersion fields, reserved bits rejected). */
+#define ATTN_PARAMS_VERSION 1u
+
+/* Unbounded side of a window. */
+#define ATTN_WINDOW_INF 2147483647
+
+/* Element type of q, k, v, o, dout, dq, dk, dv.  LSE and the workspace are
+ * always fp32. */
+#define ATTN_FP32 0
+#define ATTN_FP16 1
+#define ATTN_BF16 2
+
+/* ATTN_BHSD: dense [batch, heads, seq, head_dim] addressed with strides
+ *            {batch, head, row}.
+ * ATTN_THD:  packed [total, heads, head_dim]; sequence b owns rows
+ *            cu_seqlens[b] .. cu_seqlens[b+1]-1 ("stacked" varlen of the
+ *            AOTriton 0.14b release notes, "VarlenBits supersedes
+ *            VarlenType"); strides {ignored, head, row}. */
+#define ATTN_BHSD 0
+#define ATTN_THD 1
+
+/* Principal diagonal (AOTriton 0.15b, VarlenPrincipalDiagonal). */
+#define ATTN_TOP_LEFT 0
+#define ATTN_BOTTOM_RIGHT 1
+
+typedef struct {
+  uint32_t version;        /* ATTN_PARAMS_VERSION */
+  uint32_t flags;          /* reserved, must be 0 */
+  int32_t dtype;           /* ATTN_FP32 / ATTN_FP16 / ATTN_BF16 */
+  int32_t layout;          /* ATTN_BHSD / ATTN_THD */
+  int32_t batch;           /* BHSD: batch; THD: number of sequences (>= 1) */
+  int32_t heads;           /* >= 1; Q, K and V have the same head count */
+  int32_t head_dim;        /* 64, 80 or 128; V/O share it */
+  int32_t seqlen_q;        /* BHSD: Sq (>= 0); THD: max sequence length of Q */
+  int32_t seqlen_k;        /* BHSD: Sk (>= 0); THD: max sequence length of K */
+  int32_t window_left;     /* any int32; ATTN_WINDOW_INF = unbounded */
+  int32_t window_right;    /* any int32; ATTN_WINDOW_INF = unbounded */
+  int32_t diag;            /* ATTN_TOP_LEFT / ATTN_BOTTOM_RIGHT */
+  float scale;             /* any finite value, 0 and negatives included */
+  int32_t reserved0;       /* must be 0 */
+  int64_t total_q;         /* THD: rows of Q/O/dO (= cu_seqlens_q[batch]) */
+  int64_t total_k;         /* THD: rows of K/V (= cu_seqlens_k[batch]) */
+  const void *q;           /* input */
+  const void *k;           /* input */
+  const void *v;           /* input */
+  void *o;                 /* fwd: output; bwd: input (the forward's O) */
+  float *lse;              /* fwd: output; bwd: input.  BHSD: contiguous
+                              [batch, heads, seqlen_q]; THD: contiguous
+                              [heads, total_q] (the "HT" layout). */
+  const int32_t *cu_seqlens_q; /* THD: device int32[batch+1]; BHSD: NULL */
+  const int32_t *cu_seqlens_k; /* THD: device int32[batch+1]; BHSD: NULL */
+  int64_t q_stride[3];     /* element strides {batch, head, row}; the */
+  int64_t k_stride[3];     /* head_dim stride is 1.  Base pointers and */
+  int64_t v_stride[3];     /* strides must keep every row 16-byte */
+  int64_t o_stride[3];     /* aligned. */
+} attn_fwd_params;
+
+typedef struct {
+  attn_fwd_params fwd;     /* problem, inputs q/k/v and the forward's o/lse */
+  const void *dout;        /* input, laid out like o (own strides) */
+  void *dq;                /* outputs, laid out like q, k, v (own strides) */
+  void *dk;
+  void *dv;
+  int64_t do_stride[3];
+  int64_t dq_stride[3];
+  int64_t dk_stride[3];
+  int64_t dv_stride[3];
+  void *workspace;         /* device, caller-owned, 256-byte aligned */
+  uint64_t workspace_bytes;/* >= attn_bwd_workspace_size(this) */
+} attn_bwd_params;
+
+/* Forward: writes o and lse.  Enqueues one kernel on `stream`. */
+hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
+
+/* Backward: reads q, k, v, o, lse, dout; writes dq, dk, dv.  Enqueues, in
+ * stream order, the row-sum preprocess Delta_i = sum_d dO_id O_id (the
+ * "bwd_preprocess" of the AOTriton 0.14b release notes) into the workspace,
+ * the per-key-block dK/dV kernel and the per-query-block dQ kernel (the
+ * split backward, "triton_split" in the same notes).  The dK/dV and dQ
+ * sums are computed without atomics: results are run-to-run identical. */
+hipError_t attn_bwd(const attn_bwd_params *p, hipStream_t stream);
+
+/* Workspace bytes attn_bwd needs for this problem (fp32 Delta per query row
+ * and head, rounded up to 256 bytes); 0 when the problem is malformed. */
+uint64_t attn_bwd_workspace_size(const attn_bwd_params *p);
+
+/* Host-only validation of a call, the same checks attn_fwd / attn_bwd make
+ * first; no HIP call is made.  Returns hipSuccess or the error the call
+ * would return before launching. */
+hipError_t attn_fwd_check(const attn_fwd_params *p);
+hipError_t attn_bwd_check(const attn_bwd_params *p);
+
+/* ATTN_PARAMS_VERSION of the built library. */
+uint32_t attn_params_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_H */

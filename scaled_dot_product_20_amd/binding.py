@@ -1,0 +1,248 @@
+"""Thin ctypes binding of ``include/attn.h``.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libsdpa20.so``.  torch supplies device memory (output and
+workspace allocation) and the current stream; there is no CPU or eager
+fallback, and calling into a missing library raises immediately.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (both carry the same soname), and the
+streams and device pointers torch hands over belong to that runtime.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsdpa20.so")
+
+WINDOW_INF = 2147483647
+PARAMS_VERSION = 1
+FP32, FP16, BF16 = 0, 1, 2
+BHSD, THD = 0, 1
+TOP_LEFT, BOTTOM_RIGHT = 0, 1
+
+_DTYPE = {torch.float32: FP32, torch.float16: FP16, torch.bfloat16: BF16}
+_HIP_ERRORS = {1: "hipErrorInvalidValue", 801: "hipErrorNotSupported", 98: "hipErrorInvalidDeviceFunction",
+               209: "hipErrorNoBinaryForGpu", 200: "hipErrorInvalidImage"}
+
+_I64x3 = ctypes.c_int64 * 3
+
+
+class FwdParams(ctypes.Structure):
+    _fields_ = [
+        ("version", ctypes.c_uint32), ("flags", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("seqlen_q", ctypes.c_int32), ("seqlen_k", ctypes.c_int32),
+        ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
+        ("diag", ctypes.c_int32), ("scale", ctypes.c_float), ("reserved0", ctypes.c_int32),
+        ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("q_stride", _I64x3), ("k_stride", _I64x3), ("v_stride", _I64x3), ("o_stride", _I64x3),
+    ]
+
+
+class BwdParams(ctypes.Structure):
+    _fields_ = [
+        ("fwd", FwdParams),
+        ("dout", ctypes.c_void_p), ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p),
+        ("dv", ctypes.c_void_p),
+        ("do_stride", _I64x3), ("dq_stride", _I64x3), ("dk_stride", _I64x3), ("dv_stride", _I64x3),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m scaled_dot_product_20_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, ptype in (("attn_fwd", FwdParams), ("attn_bwd", BwdParams)):
+            f = getattr(l, name)
+            f.argtypes = [ctypes.POINTER(ptype), ctypes.c_void_p]
+            f.restype = ctypes.c_int
+        l.attn_fwd_check.argtypes = [ctypes.POINTER(FwdParams)]
+        l.attn_fwd_check.restype = ctypes.c_int
+        l.attn_bwd_check.argtypes = [ctypes.POINTER(BwdParams)]
+        l.attn_bwd_check.restype = ctypes.c_int
+        l.attn_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdParams)]
+        l.attn_bwd_workspace_size.restype = ctypes.c_uint64
+        l.attn_params_version.restype = ctypes.c_uint32
+        _lib = l
+    return _lib
+
+
+class AttnError(RuntimeError):
+    def __init__(self, call: str, code: int):
+        self.code = code
+        super().__init__(f"{call} failed: {_HIP_ERRORS.get(code, 'hipError')} ({code})")
+
+
+def _diag(diag) -> int:
+    if diag in ("top_left", TOP_LEFT):
+        return TOP_LEFT
+    if diag in ("bottom_right", BOTTOM_RIGHT):
+        return BOTTOM_RIGHT
+    raise ValueError("diag must be 'top_left' or 'bottom_right'")
+
+
+def _strides(t: torch.Tensor):
+    """{batch, head, row} element strides; head_dim must be contiguous."""
+    if t.stride(-1) != 1:
+        raise ValueError("the head_dim axis must be contiguous")
+    if t.dim() == 4:  # [B, H, S, D]
+        return _I64x3(t.stride(0), t.stride(1), t.stride(2))
+    return _I64x3(0, t.stride(1), t.stride(0))  # [T, H, D]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens_k,
+               max_seqlen_q, max_seqlen_k) -> FwdParams:
+    """Fill an attn_fwd_params from tensors (no device work)."""
+    p = FwdParams()
+    p.version = PARAMS_VERSION
+    if q.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    p.dtype = _DTYPE[q.dtype]
+    p.window_left, p.window_right = int(window[0]), int(window[1])
+    p.diag = _diag(diag)
+    p.scale = float(scale)
+    p.q, p.k, p.v, p.o, p.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)
+    p.q_stride, p.k_stride, p.v_stride, p.o_stride = _strides(q), _strides(k), _strides(v), _strides(o)
+    if q.dim() == 4:
+        p.layout = BHSD
+        p.batch, p.heads, p.seqlen_q, p.head_dim = q.shape
+        p.seqlen_k = k.shape[2]
+    elif q.dim() == 3:
+        if cu_seqlens_q is None or cu_seqlens_k is None:
+            raise ValueError("packed [T, H, D] inputs need cu_seqlens_q and cu_seqlens_k")
+        p.layout = THD
+        p.batch = cu_seqlens_q.numel() - 1
+        p.total_q, p.heads, p.head_dim = q.shape
+        p.total_k = k.shape[0]
+        p.seqlen_q, p.seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+        p.cu_seqlens_q, p.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
+    else:
+        raise ValueError("inputs are [B, H, S, D] or [T, H, D]")
+    return p
+
+
+def _max_len(cu: torch.Tensor) -> int:
+    # Reads the lengths back to the host (a sync); pass max_seqlen_* to avoid it.
+    return int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+
+
+def _check_inputs(*ts):
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    for t in ts:
+        if t.device != dev or t.dtype != ts[0].dtype:
+            raise ValueError("q, k, v (o, dout) must share device and dtype")
+
+
+def _cu(cu, dev):
+    if cu is None:
+        return None
+    if cu.dtype != torch.int32 or cu.device != dev:
+        raise ValueError("cu_seqlens must be int32 tensors on the inputs' device")
+    return cu.contiguous()
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+             window: Tuple[int, int] = (WINDOW_INF, WINDOW_INF), diag="top_left",
+             cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
+             max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Forward: returns (O, LSE).  LSE is fp32 [B, H, Sq] (dense) or [H, T] (packed)."""
+    _check_inputs(q, k, v)
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    cu_q, cu_k = _cu(cu_seqlens_q, dev), _cu(cu_seqlens_k, dev)
+    if q.dim() == 3:
+        max_seqlen_q = _max_len(cu_q) if max_seqlen_q is None else max_seqlen_q
+        max_seqlen_k = _max_len(cu_k) if max_seqlen_k is None else max_seqlen_k
+        lse_shape = (q.shape[1], q.shape[0])
+    else:
+        lse_shape = tuple(q.shape[:3])
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse is None else lse
+    p = fwd_params(q, k, v, o, lse, scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q,
+                   cu_seqlens_k=cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+    rc = lib().attn_fwd(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
+    if rc:
+        raise AttnError("attn_fwd", rc)
+    return o, lse
+
+
+def bwd_params(dout, q, k, v, o, lse, dq, dk, dv, workspace, **kw) -> BwdParams:
+    p = BwdParams()
+    p.fwd = fwd_params(q, k, v, o, lse, **kw)
+    p.dout, p.dq, p.dk, p.dv = _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv)
+    p.do_stride, p.dq_stride = _strides(dout), _strides(dq)
+    p.dk_stride, p.dv_stride = _strides(dk), _strides(dv)
+    if workspace is not None:
+        p.workspace = _ptr(workspace)
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    return p
+
+
+def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             lse: torch.Tensor, *, scale: Optional[float] = None,
+             window: Tuple[int, int] = (WINDOW_INF, WINDOW_INF), diag="top_left",
+             cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
+             max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Backward: returns (dQ, dK, dV) given the forward's O and LSE."""
+    _check_inputs(q, k, v, o, dout)
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    cu_q, cu_k = _cu(cu_seqlens_q, dev), _cu(cu_seqlens_k, dev)
+    if q.dim() == 3:
+        max_seqlen_q = _max_len(cu_q) if max_seqlen_q is None else max_seqlen_q
+        max_seqlen_k = _max_len(cu_k) if max_seqlen_k is None else max_seqlen_k
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    kw = dict(scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **kw)
+    if workspace is None:
+        need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().attn_bwd(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
+    if rc:
+        raise AttnError("attn_bwd", rc)
+    return dq, dk, dv
+
+
+def workspace_size(dout, q, k, v, o, lse, **kw) -> int:
+    """Bytes attn_bwd needs for its Delta workspace."""
+    p = bwd_params(dout, q, k, v, o, lse, dout, dout, dout, None, **kw)
+    return int(lib().attn_bwd_workspace_size(ctypes.byref(p)))

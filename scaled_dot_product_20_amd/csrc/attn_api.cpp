@@ -1,0 +1,252 @@
+// attn_api.cpp - the C ABI declared in include/attn.h: validation, argument
+// marshalling into kernel argument blocks, and the device taken from the
+// stream.  No allocation, no global mutable state, nothing printed.
+#include "attn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "attn_launch.hpp"
+
+namespace {
+
+using sdpa::Operand;
+
+bool dtype_ok(int32_t d) { return d == ATTN_FP32 || d == ATTN_FP16 || d == ATTN_BF16; }
+int64_t elem_bytes(int32_t d) { return d == ATTN_FP32 ? 4 : 2; }
+bool head_dim_built(int32_t d) { return d == 64 || d == 80 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte range [lo, hi) an operand can touch, for the overlap check.
+struct Extent {
+  uintptr_t lo, hi;
+};
+
+Extent extent_of(const void* ptr, const int64_t* stride, int64_t nb, int64_t nh, int64_t nrows,
+                 int64_t d, int64_t esz, bool packed) {
+  int64_t span = d;  // the last row's head_dim elements
+  if (!packed && nb > 0) span += (nb - 1) * std::llabs(stride[0]);
+  if (nh > 0) span += (nh - 1) * std::llabs(stride[1]);
+  if (nrows > 0) span += (nrows - 1) * std::llabs(stride[2]);
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+  return Extent{lo, lo + (uintptr_t)(span * esz)};
+}
+
+bool overlap(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool strides_ok(const int64_t* stride, int64_t esz, bool packed) {
+  for (int i = packed ? 1 : 0; i < 3; ++i)
+    if ((stride[i] * esz) % 16 != 0) return false;
+  return true;
+}
+
+// Rows of the Q side / K side of the whole tensor.
+int64_t q_rows(const attn_fwd_params* p) {
+  return p->layout == ATTN_THD ? p->total_q : (int64_t)p->seqlen_q;
+}
+int64_t k_rows(const attn_fwd_params* p) {
+  return p->layout == ATTN_THD ? p->total_k : (int64_t)p->seqlen_k;
+}
+
+hipError_t check_problem(const attn_fwd_params* p) {
+  if (!p) return hipErrorInvalidValue;
+  if (p->version != ATTN_PARAMS_VERSION || p->flags != 0 || p->reserved0 != 0)
+    return hipErrorInvalidValue;
+  if (!dtype_ok(p->dtype)) return hipErrorInvalidValue;
+  if (p->layout != ATTN_BHSD && p->layout != ATTN_THD) return hipErrorInvalidValue;
+  if (p->diag != ATTN_TOP_LEFT && p->diag != ATTN_BOTTOM_RIGHT) return hipErrorInvalidValue;
+  if (p->heads < 1 || p->head_dim < 1 || p->seqlen_q < 0 || p->seqlen_k < 0)
+    return hipErrorInvalidValue;
+  if (!std::isfinite(p->scale)) return hipErrorInvalidValue;
+  if (p->layout == ATTN_BHSD) {
+    if (p->batch < 0) return hipErrorInvalidValue;
+    if (p->cu_seqlens_q || p->cu_seqlens_k) return hipErrorInvalidValue;
+  } else {
+    if (p->batch < 1) return hipErrorInvalidValue;
+    if (!p->cu_seqlens_q || !p->cu_seqlens_k) return hipErrorInvalidValue;
+    if (p->total_q < 0 || p->total_k < 0 || p->total_q > INT32_MAX || p->total_k > INT32_MAX)
+      return hipErrorInvalidValue;
+  }
+  // A pointer may be NULL only when its tensor has no elements.
+  const int64_t nb = p->layout == ATTN_THD ? 1 : p->batch;
+  const bool no_q = nb == 0 || q_rows(p) == 0, no_k = nb == 0 || k_rows(p) == 0;
+  if ((!p->q && !no_q) || (!p->o && !no_q) || (!p->lse && !no_q) || (!p->k && !no_k) ||
+      (!p->v && !no_k))
+    return hipErrorInvalidValue;
+  const int64_t esz = elem_bytes(p->dtype);
+  const bool packed = p->layout == ATTN_THD;
+  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
+    return hipErrorInvalidValue;
+  if (!strides_ok(p->q_stride, esz, packed) || !strides_ok(p->k_stride, esz, packed) ||
+      !strides_ok(p->v_stride, esz, packed) || !strides_ok(p->o_stride, esz, packed))
+    return hipErrorInvalidValue;
+  if (!head_dim_built(p->head_dim)) return hipErrorNotSupported;
+  return hipSuccess;
+}
+
+Extent lse_extent(const attn_fwd_params* p) {
+  const int64_t n = p->layout == ATTN_THD ? (int64_t)p->heads * p->total_q
+                                          : (int64_t)p->batch * p->heads * p->seqlen_q;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p->lse);
+  return Extent{lo, lo + (uintptr_t)(n * 4)};
+}
+
+uint64_t delta_bytes(const attn_fwd_params* p) {
+  const int64_t n = p->layout == ATTN_THD ? (int64_t)p->heads * p->total_q
+                                          : (int64_t)p->batch * p->heads * p->seqlen_q;
+  return ((uint64_t)n * 4 + 255) / 256 * 256;
+}
+
+sdpa::ProblemArgs problem_args(const attn_fwd_params* p) {
+  sdpa::ProblemArgs a{};
+  a.varlen = p->layout == ATTN_THD;
+  a.cu_q = a.varlen ? p->cu_seqlens_q : nullptr;
+  a.cu_k = a.varlen ? p->cu_seqlens_k : nullptr;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.Sq = p->seqlen_q;
+  a.Sk = p->seqlen_k;
+  a.wl = p->window_left;
+  a.wr = p->window_right;
+  a.diag = p->diag;
+  a.scale = p->scale;
+  a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  if (a.varlen) {
+    a.lse_sb = 0;
+    a.lse_sh = p->total_q;
+  } else {
+    a.lse_sb = (int64_t)p->heads * p->seqlen_q;
+    a.lse_sh = p->seqlen_q;
+  }
+  a.total_q = a.varlen ? p->total_q : 0;
+  return a;
+}
+
+Operand operand(const void* ptr, const int64_t* stride, bool packed) {
+  return Operand{ptr, packed ? 0 : stride[0], stride[1], stride[2]};
+}
+
+// Runs `launch` with the stream's device current, restoring the caller's.
+template <typename F>
+hipError_t on_stream_device(hipStream_t stream, F launch) {
+  int dev = -1, cur = -1;
+  hipError_t err = hipStreamGetDevice(stream, &dev);
+  if (err != hipSuccess) return err;
+  err = hipGetDevice(&cur);
+  if (err != hipSuccess) return err;
+  if (dev != cur && (err = hipSetDevice(dev)) != hipSuccess) return err;
+  const hipError_t lerr = launch();
+  if (dev != cur) {
+    err = hipSetDevice(cur);
+    if (lerr == hipSuccess && err != hipSuccess) return err;
+  }
+  return lerr;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t attn_params_version(void) { return ATTN_PARAMS_VERSION; }
+
+hipError_t attn_fwd_check(const attn_fwd_params* p) {
+  hipError_t err = check_problem(p);
+  if (err != hipSuccess) return err;
+  const bool packed = p->layout == ATTN_THD;
+  const int64_t esz = elem_bytes(p->dtype);
+  const int64_t B = packed ? 1 : p->batch;
+  const Extent o = extent_of(p->o, p->o_stride, B, p->heads, q_rows(p), p->head_dim, esz, packed);
+  const Extent ins[3] = {
+      extent_of(p->q, p->q_stride, B, p->heads, q_rows(p), p->head_dim, esz, packed),
+      extent_of(p->k, p->k_stride, B, p->heads, k_rows(p), p->head_dim, esz, packed),
+      extent_of(p->v, p->v_stride, B, p->heads, k_rows(p), p->head_dim, esz, packed)};
+  const Extent l = lse_extent(p);
+  for (const Extent& in : ins)
+    if (overlap(o, in) || overlap(l, in)) return hipErrorInvalidValue;
+  if (overlap(o, l)) return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t attn_fwd(const attn_fwd_params* p, hipStream_t stream) {
+  hipError_t err = attn_fwd_check(p);
+  if (err != hipSuccess) return err;
+  const bool packed = p->layout == ATTN_THD;
+  sdpa::FwdArgs a{};
+  a.p = problem_args(p);
+  a.q = operand(p->q, p->q_stride, packed);
+  a.k = operand(p->k, p->k_stride, packed);
+  a.v = operand(p->v, p->v_stride, packed);
+  a.o = operand(p->o, p->o_stride, packed);
+  a.lse = p->lse;
+  return on_stream_device(stream, [&] { return sdpa::launch_fwd(p->dtype, p->head_dim, a, stream); });
+}
+
+uint64_t attn_bwd_workspace_size(const attn_bwd_params* p) {
+  if (!p || check_problem(&p->fwd) != hipSuccess) return 0;
+  return delta_bytes(&p->fwd);
+}
+
+hipError_t attn_bwd_check(const attn_bwd_params* p) {
+  if (!p) return hipErrorInvalidValue;
+  const attn_fwd_params* f = &p->fwd;
+  hipError_t err = check_problem(f);
+  if (err != hipSuccess) return err;
+  const int64_t nb = f->layout == ATTN_THD ? 1 : f->batch;
+  const bool no_q = nb == 0 || q_rows(f) == 0, no_k = nb == 0 || k_rows(f) == 0;
+  if ((!p->dout && !no_q) || (!p->dq && !no_q) || (!p->dk && !no_k) || (!p->dv && !no_k) ||
+      !p->workspace)
+    return hipErrorInvalidValue;
+  if (p->workspace_bytes < delta_bytes(f)) return hipErrorInvalidValue;
+  if ((reinterpret_cast<uintptr_t>(p->workspace) & 255u) != 0) return hipErrorInvalidValue;
+  const bool packed = f->layout == ATTN_THD;
+  const int64_t esz = elem_bytes(f->dtype);
+  if (!aligned16(p->dout) || !aligned16(p->dq) || !aligned16(p->dk) || !aligned16(p->dv))
+    return hipErrorInvalidValue;
+  if (!strides_ok(p->do_stride, esz, packed) || !strides_ok(p->dq_stride, esz, packed) ||
+      !strides_ok(p->dk_stride, esz, packed) || !strides_ok(p->dv_stride, esz, packed))
+    return hipErrorInvalidValue;
+  const int64_t B = packed ? 1 : f->batch, H = f->heads, D = f->head_dim;
+  const Extent outs[4] = {
+      extent_of(p->dq, p->dq_stride, B, H, q_rows(f), D, esz, packed),
+      extent_of(p->dk, p->dk_stride, B, H, k_rows(f), D, esz, packed),
+      extent_of(p->dv, p->dv_stride, B, H, k_rows(f), D, esz, packed),
+      Extent{reinterpret_cast<uintptr_t>(p->workspace),
+             reinterpret_cast<uintptr_t>(p->workspace) + (uintptr_t)delta_bytes(f)}};
+  const Extent ins[6] = {
+      extent_of(f->q, f->q_stride, B, H, q_rows(f), D, esz, packed),
+      extent_of(f->k, f->k_stride, B, H, k_rows(f), D, esz, packed),
+      extent_of(f->v, f->v_stride, B, H, k_rows(f), D, esz, packed),
+      extent_of(f->o, f->o_stride, B, H, q_rows(f), D, esz, packed),
+      extent_of(p->dout, p->do_stride, B, H, q_rows(f), D, esz, packed),
+      lse_extent(f)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Extent& in : ins)
+      if (overlap(outs[i], in)) return hipErrorInvalidValue;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+hipError_t attn_bwd(const attn_bwd_params* p, hipStream_t stream) {
+  hipError_t err = attn_bwd_check(p);
+  if (err != hipSuccess) return err;
+  const attn_fwd_params* f = &p->fwd;
+  const bool packed = f->layout == ATTN_THD;
+  sdpa::BwdArgs a{};
+  a.p = problem_args(f);
+  a.q = operand(f->q, f->q_stride, packed);
+  a.k = operand(f->k, f->k_stride, packed);
+  a.v = operand(f->v, f->v_stride, packed);
+  a.o = operand(f->o, f->o_stride, packed);
+  a.dout = operand(p->dout, p->do_stride, packed);
+  a.dq = operand(p->dq, p->dq_stride, packed);
+  a.dk = operand(p->dk, p->dk_stride, packed);
+  a.dv = operand(p->dv, p->dv_stride, packed);
+  a.lse = f->lse;
+  a.delta = static_cast<float*>(p->workspace);
+  return on_stream_device(stream, [&] { return sdpa::launch_bwd(f->dtype, f->head_dim, a, stream); });
+}
+
+}  // extern "C"

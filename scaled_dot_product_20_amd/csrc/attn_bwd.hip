@@ -1,0 +1,476 @@
+// attn_bwd.hip - fused attention backward for gfx950: the row-sum
+// preprocess and the split dK/dV and dQ kernels (the "bwd_preprocess" and
+// "triton_split" steps named in the AOTriton 0.14b release notes).
+//
+// With P recomputed from the forward's LSE (P_ij = exp(scale q_i.k_j -
+// LSE_i) on visible pairs), Delta_i = sum_d dO_id O_id, dP = dO V^T and
+// dS = P o (dP - Delta):
+//   dV = P^T dO,  dK = scale dS^T Q   (per key block, kernel 2)
+//   dQ = scale dS K                   (per query block, kernel 3)
+// No atomics: every output element is summed by one lane in a fixed order,
+// so results are run-to-run identical.
+#include "attn_device.hpp"
+#include "attn_launch.hpp"
+
+namespace sdpa {
+
+template <typename T>
+__device__ __forceinline__ void store4b(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  } else {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 v;
+    v[0] = (T)a; v[1] = (T)b; v[2] = (T)c; v[3] = (T)d;
+    *reinterpret_cast<t4*>(p) = v;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float dot_chunk(uint4 x, uint4 y) {
+  if constexpr (sizeof(T) == 4) {
+    return __uint_as_float(x.x) * __uint_as_float(y.x) + __uint_as_float(x.y) * __uint_as_float(y.y) +
+           __uint_as_float(x.z) * __uint_as_float(y.z) + __uint_as_float(x.w) * __uint_as_float(y.w);
+  } else {
+    typedef T t8 __attribute__((ext_vector_type(8)));
+    t8 a = __builtin_bit_cast(t8, x), b = __builtin_bit_cast(t8, y);
+    float s = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) s += (float)a[t] * (float)b[t];
+    return s;
+  }
+}
+
+// ------------------------------------------------------------ preprocess
+
+// Delta_i = sum_d dO_id * O_id in fp32, one group of G lanes per row, each
+// lane one 16-byte chunk.  Rows are (b, h, i) for the dense layout and
+// (packed row t, h) for the packed one.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a, long long nrows) {
+  constexpr int CE = 16 / (int)sizeof(T), CH = D / CE;
+  constexpr int G = CH <= 8 ? 8 : (CH <= 16 ? 16 : 32);
+  const ProblemArgs& P = a.p;
+  const long long row = (long long)blockIdx.x * (256 / G) + threadIdx.x / G;
+  const int c = threadIdx.x % G;
+  if (row >= nrows) return;  // whole groups leave together
+  long long b, h, i;
+  if (P.varlen) {
+    i = row / P.H;  // packed row
+    h = row % P.H;
+    b = 0;
+  } else {
+    const long long bh = row / P.Sq;
+    i = row % P.Sq;
+    h = bh % P.H;
+    b = bh / P.H;
+  }
+  float s = 0.f;
+  if (c < CH) {
+    const T* op = (const T*)a.o.ptr + b * a.o.sb + h * a.o.sh + i * a.o.ss + c * CE;
+    const T* dp = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + i * a.dout.ss + c * CE;
+    s = dot_chunk<T>(*reinterpret_cast<const uint4*>(op), *reinterpret_cast<const uint4*>(dp));
+  }
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, G);
+  if (c == 0) a.delta[b * P.lse_sb + h * P.lse_sh + i] = s;
+}
+
+// ------------------------------------------------------------ dK / dV
+
+// One workgroup = 32*NW keys of one (sequence, head), each wave 32 keys with
+// its K and V rows held in registers; the workgroup walks the query tiles
+// (BMQ rows) that can see its keys.  Per tile, Q and dO are staged both
+// row-major (A operands of S = Q K^T and dP = dO V^T) and transposed (A
+// operands of dK^T += Q^T dS and dV^T += dO^T P), with LSE and Delta.
+template <typename M, int D, int NW, int BMQ>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
+  using T = typename M::elem;
+  constexpr int NT = NW * 64, BNK = NW * 32, KPL = M::KPL;
+  constexpr int DVT = (D + 31) / 32, DPAD = DVT * 32;
+  constexpr int PAD = 16 / (int)sizeof(T);
+  constexpr int RLD = D + PAD, TLD = BMQ + PAD;
+  constexpr int MQ = BMQ / 32;
+  constexpr int NS = D / (2 * KPL);
+  constexpr int STAGE_T = 2 * BMQ * RLD + 2 * DPAD * TLD;
+  __shared__ __attribute__((aligned(16))) T smem[2 * STAGE_T];
+  __shared__ __attribute__((aligned(16))) float stats[2][2][BMQ];  // [buf][lse2, delta][row]
+
+  const ProblemArgs& P = a.p;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int nkb = (int)(gridDim.x / (P.B * P.H));
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = blk / nkb, h = bh % P.H, b = bh / P.H;
+  const int kb = blk % nkb;
+
+  long long q0 = 0, k0 = 0;
+  int sq = P.Sq, sk = P.Sk;
+  if (P.varlen) {
+    q0 = P.cu_q[b];
+    sq = P.cu_q[b + 1] - (int)q0;
+    k0 = P.cu_k[b];
+    sk = P.cu_k[b + 1] - (int)k0;
+  }
+  const int j0 = kb * BNK;
+  if (j0 >= sk) return;
+  const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
+
+  const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
+  const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
+  const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
+  const T* dop = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + q0 * a.dout.ss;
+  T* dkp = (T*)a.dk.ptr + b * a.dk.sb + h * a.dk.sh + k0 * a.dk.ss;
+  T* dvp = (T*)a.dv.ptr + b * a.dv.sb + h * a.dv.sh + k0 * a.dv.ss;
+  const float* lsep = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
+
+  // Queries that can see the block's keys.
+  const int jlast = min(j0 + BNK, sk) - 1;
+  const long long ilo = max(0LL, (long long)j0 - w.hi);
+  const long long ihi = min((long long)sq - 1, (long long)jlast - w.lo);
+  const bool block_empty = w.lo > w.hi || ilo > ihi;
+
+  const int jw0 = j0 + 32 * wave;
+  const bool wave_live = jw0 < sk;
+  const int kj = jw0 + r;  // this lane's key
+
+  RowFrags<M, D> kf, vf;
+  kf.load(kp + (long long)kj * a.k.ss, wave_live && kj < sk, g);
+  vf.load(vp + (long long)kj * a.v.ss, wave_live && kj < sk, g);
+
+  if constexpr (DPAD != D) {
+    for (int x = tid; x < (DPAD - D) * TLD; x += NT)
+#pragma unroll
+      for (int bf = 0; bf < 2; ++bf)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          smem[bf * STAGE_T + 2 * BMQ * RLD + tt * DPAD * TLD + D * TLD + x] = (T)0.f;
+  }
+
+  f32x16 dk[DVT], dv[DVT];
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) {
+    dk[dt] = zero16();
+    dv[dt] = zero16();
+  }
+
+  if (!block_empty) {
+    const int t0 = (int)(ilo / BMQ), t1 = (int)(ihi / BMQ);
+    TileStage<T, BMQ, D, NT> qs, dos;
+    float st_l = INFINITY, st_d = 0.f;  // this thread's LSE/Delta entry (tid < BMQ)
+    auto load_tile = [&](int i0) {
+      qs.load(qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, tid);
+      dos.load(dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, tid);
+      if (tid < BMQ) {
+        const bool ok = i0 + tid < sq;
+        st_l = ok ? lsep[i0 + tid] * kLog2e : INFINITY;
+        st_d = ok ? delp[i0 + tid] : 0.f;
+      }
+    };
+    auto store_tile = [&](int bf) {
+      T* base = smem + bf * STAGE_T;
+      qs.store_rows(base, RLD, tid);
+      dos.store_rows(base + BMQ * RLD, RLD, tid);
+      qs.store_transposed(base + 2 * BMQ * RLD, TLD, tid);
+      dos.store_transposed(base + 2 * BMQ * RLD + DPAD * TLD, TLD, tid);
+      if (tid < BMQ) {
+        stats[bf][0][tid] = st_l;
+        stats[bf][1][tid] = st_d;
+      }
+    };
+    load_tile(t0 * BMQ);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = t0; t <= t1; ++t) {
+      const int bf = (t - t0) & 1;
+      const int i0 = t * BMQ;
+      if (t < t1) load_tile(i0 + BMQ);
+      const T* Qs = smem + bf * STAGE_T;
+      const T* dOs = Qs + BMQ * RLD;
+      const T* Qt = Qs + 2 * BMQ * RLD;
+      const T* dOt = Qt + DPAD * TLD;
+      const int cls = wave_live ? classify(w, i0, BMQ, jw0, 32, sk) : kEmpty;
+      if (cls != kEmpty) {
+#pragma unroll
+        for (int mq = 0; mq < MQ; ++mq) {
+          // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
+          f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            const int off = (32 * mq + r) * RLD + 2 * KPL * st + KPL * g;
+            s = M::mma(load_frag<M>(Qs + off), kf.f[st], s);
+            dp = M::mma(load_frag<M>(dOs + off), vf.f[st], dp);
+          }
+          float p[16], ds[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int il = 32 * mq + acc_row(e, g);
+            float pe = __builtin_amdgcn_exp2f(s[e] * P.scale_log2 - stats[bf][0][il]);
+            if (cls == kPartial) {
+              const int diff = kj - (i0 + il);
+              if (!(diff >= w.lo && diff <= w.hi && kj < sk)) pe = 0.f;
+            }
+            p[e] = pe;
+            ds[e] = pe * (dp[e] - stats[bf][1][il]);
+          }
+          // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end).
+#pragma unroll
+          for (int st = 0; st < 16 / KPL; ++st) {
+            typename M::frag pf, dsf;
+            M::pack(&p[KPL * st], pf);
+            M::pack(&ds[KPL * st], dsf);
+            const int pos = 32 * mq + perm_pos(KPL * st, g);
+#pragma unroll
+            for (int dt = 0; dt < DVT; ++dt) {
+              dv[dt] = M::mma(load_frag<M>(dOt + (32 * dt + r) * TLD + pos), pf, dv[dt]);
+              dk[dt] = M::mma(load_frag<M>(Qt + (32 * dt + r) * TLD + pos), dsf, dk[dt]);
+            }
+          }
+        }
+      }
+      if (t < t1) store_tile(bf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (wave_live && kj < sk) {
+    T* dkrow = dkp + (long long)kj * a.dk.ss;
+    T* dvrow = dvp + (long long)kj * a.dv.ss;
+    const float sc = P.scale;
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * dt + 8 * q4 + 4 * g;
+        if (d < D) {
+          store4b<T>(dkrow + d, dk[dt][4 * q4] * sc, dk[dt][4 * q4 + 1] * sc,
+                     dk[dt][4 * q4 + 2] * sc, dk[dt][4 * q4 + 3] * sc);
+          store4b<T>(dvrow + d, dv[dt][4 * q4], dv[dt][4 * q4 + 1], dv[dt][4 * q4 + 2],
+                     dv[dt][4 * q4 + 3]);
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------ dQ
+
+// One workgroup = 32*NW queries, each wave 32 queries with its Q and dO rows,
+// LSE and Delta in registers; the workgroup walks the key tiles its window
+// can see, staging K (row-major and transposed) and V (row-major).
+template <typename M, int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
+  using T = typename M::elem;
+  constexpr int NT = NW * 64, BM = NW * 32, KPL = M::KPL;
+  constexpr int DVT = (D + 31) / 32, DPAD = DVT * 32;
+  constexpr int PAD = 16 / (int)sizeof(T);
+  constexpr int RLD = D + PAD, TLD = BN + PAD;
+  constexpr int KT = BN / 32;
+  constexpr int NS = D / (2 * KPL);
+  constexpr int STAGE = 2 * BN * RLD + DPAD * TLD;
+  __shared__ __attribute__((aligned(16))) T smem[2 * STAGE];
+
+  const ProblemArgs& P = a.p;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int nq = (int)(gridDim.x / (P.B * P.H));
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - (blk % nq);
+
+  long long q0 = 0, k0 = 0;
+  int sq = P.Sq, sk = P.Sk;
+  if (P.varlen) {
+    q0 = P.cu_q[b];
+    sq = P.cu_q[b + 1] - (int)q0;
+    k0 = P.cu_k[b];
+    sk = P.cu_k[b + 1] - (int)k0;
+  }
+  const int i0 = qb * BM;
+  if (i0 >= sq) return;
+  const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
+
+  const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
+  const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
+  const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
+  const T* dop = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + q0 * a.dout.ss;
+  T* dqp = (T*)a.dq.ptr + b * a.dq.sb + h * a.dq.sh + q0 * a.dq.ss;
+  const float* lsep = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
+
+  const int ilast = min(i0 + BM, sq) - 1;
+  const long long jlo = max(0LL, (long long)i0 + w.lo);
+  const long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
+  const bool block_empty = w.lo > w.hi || jlo > jhi;
+
+  const int iw0 = i0 + 32 * wave;
+  const bool wave_live = iw0 < sq;
+  const int qi = iw0 + r;
+  const bool row_ok = wave_live && qi < sq;
+
+  RowFrags<M, D> qf, dof;
+  qf.load(qp + (long long)qi * a.q.ss, row_ok, g);
+  dof.load(dop + (long long)qi * a.dout.ss, row_ok, g);
+  const float lse2 = row_ok ? lsep[qi] * kLog2e : INFINITY;
+  const float delta = row_ok ? delp[qi] : 0.f;
+
+  if constexpr (DPAD != D) {
+    for (int x = tid; x < (DPAD - D) * TLD; x += NT) {
+      smem[2 * BN * RLD + D * TLD + x] = (T)0.f;
+      smem[STAGE + 2 * BN * RLD + D * TLD + x] = (T)0.f;
+    }
+  }
+
+  f32x16 dq[DVT];
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) dq[dt] = zero16();
+
+  if (!block_empty) {
+    const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
+    TileStage<T, BN, D, NT> ks, vs;
+    auto load_tile = [&](int j0) {
+      ks.load(kp + (long long)j0 * a.k.ss, a.k.ss, sk - j0, tid);
+      vs.load(vp + (long long)j0 * a.v.ss, a.v.ss, sk - j0, tid);
+    };
+    auto store_tile = [&](int bf) {
+      T* base = smem + bf * STAGE;
+      ks.store_rows(base, RLD, tid);
+      vs.store_rows(base + BN * RLD, RLD, tid);
+      ks.store_transposed(base + 2 * BN * RLD, TLD, tid);
+    };
+    load_tile(t0 * BN);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = t0; t <= t1; ++t) {
+      const int bf = (t - t0) & 1;
+      const int j0 = t * BN;
+      if (t < t1) load_tile(j0 + BN);
+      const T* Ks = smem + bf * STAGE;
+      const T* Vs = Ks + BN * RLD;
+      const T* Kt = Ks + 2 * BN * RLD;
+      const int cls = wave_live ? classify(w, iw0, 32, j0, BN, sk) : kEmpty;
+      if (cls != kEmpty) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          // S^T = K Q^T and dP^T = V dO^T for 32 keys x this wave's queries.
+          f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            const int off = (32 * kt + r) * RLD + 2 * KPL * st + KPL * g;
+            s = M::mma(load_frag<M>(Ks + off), qf.f[st], s);
+            dp = M::mma(load_frag<M>(Vs + off), dof.f[st], dp);
+          }
+          float ds[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float pe = __builtin_amdgcn_exp2f(s[e] * P.scale_log2 - lse2);
+            if (cls == kPartial) {
+              const int j = j0 + 32 * kt + acc_row(e, g);
+              const int diff = j - qi;
+              if (!(diff >= w.lo && diff <= w.hi && j < sk)) pe = 0.f;
+            }
+            ds[e] = pe * (dp[e] - delta);
+          }
+          // dQ^T += K^T dS^T (scale applied at the end).
+#pragma unroll
+          for (int st = 0; st < 16 / KPL; ++st) {
+            typename M::frag dsf;
+            M::pack(&ds[KPL * st], dsf);
+            const int pos = 32 * kt + perm_pos(KPL * st, g);
+#pragma unroll
+            for (int dt = 0; dt < DVT; ++dt)
+              dq[dt] = M::mma(load_frag<M>(Kt + (32 * dt + r) * TLD + pos), dsf, dq[dt]);
+          }
+        }
+      }
+      if (t < t1) store_tile(bf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (row_ok) {
+    T* dqrow = dqp + (long long)qi * a.dq.ss;
+    const float sc = P.scale;
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * dt + 8 * q4 + 4 * g;
+        if (d < D)
+          store4b<T>(dqrow + d, dq[dt][4 * q4] * sc, dq[dt][4 * q4 + 1] * sc,
+                     dq[dt][4 * q4 + 2] * sc, dq[dt][4 * q4 + 3] * sc);
+      }
+  }
+}
+
+// ------------------------------------------------------------ launch
+
+template <typename M, int D>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  using T = typename M::elem;
+  // fp32 tiles are halved along the key axis of the dQ kernel to fit LDS.
+  constexpr int NW_KV = 4, BMQ = 32, NW_Q = 4, BN = sizeof(T) == 4 ? 32 : 64;
+  BwdArgs args = a;
+  void* kargs[] = {&args};
+  hipError_t err;
+  // 1. Delta.
+  {
+    const long long nrows =
+        a.p.varlen ? a.p.total_q * a.p.H : (long long)a.p.B * a.p.H * a.p.Sq;
+    constexpr int CE = 16 / (int)sizeof(T), CH = D / CE;
+    constexpr int G = CH <= 8 ? 8 : (CH <= 16 ? 16 : 32);
+    const long long nblk = (nrows + (256 / G) - 1) / (256 / G);
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (nblk > 0) {
+      long long nr = nrows;
+      void* pargs[] = {&args, &nr};
+      err = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_pre_kernel<T, D>),
+                            dim3((unsigned)nblk), dim3(256), pargs, 0, stream);
+      if (err != hipSuccess) return err;
+    }
+  }
+  // 2. dK, dV.
+  {
+    const long long nkb = (a.p.Sk + NW_KV * 32 - 1) / (NW_KV * 32);
+    const long long nblk = nkb * a.p.H * a.p.B;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (nblk > 0) {
+      err = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>),
+                            dim3((unsigned)nblk), dim3(NW_KV * 64), kargs, 0, stream);
+      if (err != hipSuccess) return err;
+    }
+  }
+  // 3. dQ.
+  {
+    const long long nq = (a.p.Sq + NW_Q * 32 - 1) / (NW_Q * 32);
+    const long long nblk = nq * a.p.H * a.p.B;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (nblk > 0) {
+      err = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN>),
+                            dim3((unsigned)nblk), dim3(NW_Q * 64), kargs, 0, stream);
+      if (err != hipSuccess) return err;
+    }
+  }
+  return hipSuccess;
+}
+
+template <typename M>
+static hipError_t launch_bwd_d(int head_dim, const BwdArgs& a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_bwd_t<M, 64>(a, stream);
+    case 80: return launch_bwd_t<M, 80>(a, stream);
+    case 128: return launch_bwd_t<M, 128>(a, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream) {
+  switch (dtype) {
+    case 0: return launch_bwd_d<MmaF32>(head_dim, a, stream);
+    case 1: return launch_bwd_d<MmaF16>(head_dim, a, stream);
+    case 2: return launch_bwd_d<MmaBF16>(head_dim, a, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace sdpa

@@ -1,0 +1,262 @@
+// attn_device.hpp - gfx950 device building blocks shared by the forward and
+// backward kernels: MFMA operand types, register fragments, LDS tile staging,
+// the window predicate and the XCD-aware block order.
+//
+// Matrix-core convention (CDNA 32x32xK MFMA, 64-wide wavefront).  For lane
+// l let r = l % 32 and g = l / 32.  An A operand (M x K) holds A[r][KPL*g +
+// t], t < KPL; a B operand (K x N) holds B[KPL*g + t][r]; the 32x32 fp32
+// accumulator holds C[8*(e/4) + 4*g + e%4][r] in element e < 16.  KPL is 8
+// for bf16/fp16 (v_mfma_f32_32x32x16_{bf16,f16}) and 1 for fp32
+// (v_mfma_f32_32x32x2_f32).
+//
+// The kernels compute transposed products (S^T = K Q^T, O^T = V^T P^T, ...)
+// so that each lane owns one query (or key) column of every accumulator:
+// row statistics are then in-lane except for one exchange between the two
+// half-waves, and an accumulator can be fed straight back as the B operand
+// of the next product.  The K index order of such a B operand is the
+// accumulator's row order; the matching A operand is read from an LDS tile
+// stored transposed with the row index permuted by `perm16` below, which
+// makes the KPL values one lane needs contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kWindowInf = 2147483647;
+constexpr int kBig = 2147483647;  // |j - i| never exceeds this
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- MFMA types
+
+struct MmaBF16 {
+  using elem = __bf16;
+  using frag = bf16x8;
+  static constexpr int KPL = 8;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void pack(const float* x, frag& f) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f[t] = (__bf16)x[t];  // RNE
+  }
+};
+
+struct MmaF16 {
+  using elem = _Float16;
+  using frag = f16x8;
+  static constexpr int KPL = 8;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void pack(const float* x, frag& f) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f[t] = (_Float16)x[t];  // RNE
+  }
+};
+
+struct MmaF32 {
+  using elem = float;
+  using frag = float;
+  static constexpr int KPL = 1;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void pack(const float* x, frag& f) { f = x[0]; }
+};
+
+template <typename M>
+__device__ __forceinline__ typename M::frag load_frag(const typename M::elem* p) {
+  return *reinterpret_cast<const typename M::frag*>(p);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) z[e] = 0.f;
+  return z;
+}
+
+// Row of accumulator element e for half-wave g.
+__host__ __device__ __forceinline__ int acc_row(int e, int g) { return 8 * (e >> 2) + 4 * g + (e & 3); }
+
+// Position, inside a 32-row block of a transposed LDS tile, of the row held
+// by accumulator element e of half-wave g: the A-operand side of a product
+// whose B operand is that accumulator.
+__host__ __device__ __forceinline__ int perm_pos(int e, int g) { return 16 * (e >> 3) + 8 * g + (e & 7); }
+
+// Same map written on the row index: swaps bits 2 and 3.
+__host__ __device__ constexpr int perm16(int row) {
+  return (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1);
+}
+
+// Sum / max of a value over the two half-waves (lanes r and r + 32).
+__device__ __forceinline__ float halves_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// ------------------------------------------------------------------- window
+
+// Bounds lo <= j - i <= hi of one sequence (0-based local indices), clamped
+// to the int32 range, where |j - i| always lies.
+struct Window {
+  int lo, hi;
+};
+
+__host__ __device__ __forceinline__ Window seq_window(int wl, int wr, int diag, int sq, int sk) {
+  const bool left_inf = wl == kWindowInf, right_inf = wr == kWindowInf;
+  long long L = wl, R = wr;
+  if (diag == 1 && !left_inf && !right_inf) {
+    const long long d = (long long)sk - sq;
+    L -= d;
+    R += d;
+  }
+  long long lo = left_inf ? -(long long)kBig : -L;
+  long long hi = right_inf ? (long long)kBig : R;
+  lo = lo < -(long long)kBig ? -(long long)kBig : (lo > kBig ? kBig : lo);
+  hi = hi < -(long long)kBig ? -(long long)kBig : (hi > kBig ? kBig : hi);
+  return Window{(int)lo, (int)hi};
+}
+
+enum TileClass { kEmpty = 0, kPartial = 1, kFull = 2 };
+
+// Class of the rectangle rows [i0, i0+nr) x cols [j0, j0+nc) of the
+// visibility matrix; cols at or beyond `sk` count as masked.
+__host__ __device__ __forceinline__ int classify(Window w, long long i0, int nr, long long j0, int nc,
+                                        long long sk) {
+  const long long dmin = j0 - (i0 + nr - 1), dmax = j0 + nc - 1 - i0;
+  if (dmax < w.lo || dmin > w.hi || j0 >= sk || w.lo > w.hi) return kEmpty;
+  if (dmin >= w.lo && dmax <= w.hi && j0 + nc <= sk) return kFull;
+  return kPartial;
+}
+
+// --------------------------------------------------------------- grid order
+
+// Blocks are dealt round-robin to the 8 XCDs; remap the hardware block id so
+// that each XCD receives one contiguous range of logical blocks (the blocks
+// of the same heads share K/V in that XCD's L2).
+__host__ __device__ __forceinline__ int xcd_remap(int hw, int n) {
+  const int x = hw & 7, local = hw >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return x * per + (x < rem ? x : rem) + local;
+}
+
+// ---------------------------------------------------------- global -> LDS
+
+// A ROWS x D tile of T staged through registers by NT threads.  Each work
+// unit is four consecutive rows x one 16-byte column chunk, so the tile can
+// be written to LDS both row-major and transposed (4 rows become 4
+// consecutive positions of a transposed row).
+template <typename T, int ROWS, int D, int NT>
+struct TileStage {
+  static constexpr int CE = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int CH = D / CE;              // chunks per row
+  static constexpr int UNITS = (ROWS / 4) * CH;
+  static constexpr int U = (UNITS + NT - 1) / NT;
+  static_assert(D % CE == 0, "head_dim must be a multiple of 16 bytes");
+  static_assert(ROWS % 16 == 0, "tile rows must be a multiple of 16");
+  uint4 buf[U][4];
+
+  // Rows at or beyond `nvalid` are zero-filled.
+  __device__ __forceinline__ void load(const T* __restrict__ base, long long row_stride,
+                                       int nvalid, int tid) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int unit = tid + u * NT;
+      if (UNITS % NT == 0 || unit < UNITS) {
+        const int rg = unit / CH, c = unit % CH;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * rg + r;
+          if (row < nvalid)
+            buf[u][r] = *reinterpret_cast<const uint4*>(base + row * row_stride + c * CE);
+          else
+            buf[u][r] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // lds[row * ld + d]
+  __device__ __forceinline__ void store_rows(T* lds, int ld, int tid) const {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int unit = tid + u * NT;
+      if (UNITS % NT == 0 || unit < UNITS) {
+        const int rg = unit / CH, c = unit % CH;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<uint4*>(lds + (4 * rg + r) * ld + c * CE) = buf[u][r];
+      }
+    }
+  }
+
+  // ldsT[d * ldT + perm16(row)], rows permuted within each 16-row group.
+  __device__ __forceinline__ void store_transposed(T* ldsT, int ldT, int tid) const {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int unit = tid + u * NT;
+      if (UNITS % NT == 0 || unit < UNITS) {
+        const int rg = unit / CH, c = unit % CH;
+        const int p0 = perm16(4 * rg);
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int w = e >> 1, sh = (e & 1) * 16;
+            auto word = [&](int r) {
+              const uint4& b = buf[u][r];
+              const uint32_t x = w == 0 ? b.x : (w == 1 ? b.y : (w == 2 ? b.z : b.w));
+              return (x >> sh) & 0xffffu;
+            };
+            uint2 out;
+            out.x = word(0) | (word(1) << 16);
+            out.y = word(2) | (word(3) << 16);
+            *reinterpret_cast<uint2*>(ldsT + (c * 8 + e) * ldT + p0) = out;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            auto word = [&](int r) {
+              const uint4& b = buf[u][r];
+              return e == 0 ? b.x : (e == 1 ? b.y : (e == 2 ? b.z : b.w));
+            };
+            *reinterpret_cast<uint4*>(ldsT + (c * 4 + e) * ldT + p0) =
+                make_uint4(word(0), word(1), word(2), word(3));
+          }
+        }
+      }
+    }
+  }
+};
+
+// B-operand fragments of 32 rows held in registers for a whole kernel: lane
+// (r, g) holds row r, columns 2*KPL*s + KPL*g .. +KPL-1 of every K step s.
+template <typename M, int DK>
+struct RowFrags {
+  static constexpr int NS = DK / (2 * M::KPL);
+  typename M::frag f[NS];
+  __device__ __forceinline__ void load(const typename M::elem* __restrict__ row_ptr, bool valid,
+                                       int g) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (valid)
+        f[s] = load_frag<M>(row_ptr + 2 * M::KPL * s + M::KPL * g);
+      else
+        f[s] = typename M::frag{};
+    }
+  }
+};
+
+}  // namespace sdpa

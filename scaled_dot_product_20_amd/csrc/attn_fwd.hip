@@ -1,0 +1,250 @@
+// attn_fwd.hip - fused attention forward for gfx950.
+//
+// One workgroup = NW waves = one block of 32*NW query rows of one (sequence,
+// head); each wave owns 32 query rows.  The workgroup walks the key tiles
+// its window can see (FlashAttention, the kernel family of the AOTriton
+// README, "Kernel Support"); tiles outside the window of a wave's rows are
+// skipped and only tiles cut by the window edge, the diagonal or the ragged
+// end of the sequence are masked element by element (generalized sliding
+// window of the AOTriton 0.10b release notes; diagonal choice of the 0.15b
+// notes, "Bottom-Right Aligned Sliding Windows").
+//
+// Per key tile of BN keys:
+//   K (row-major) and V (transposed) are staged HBM -> registers -> LDS,
+//     double-buffered, the next tile's loads in flight during this tile;
+//   S^T = K Q^T on the matrix cores (Q fragments stay in registers), scaled
+//     into the log2 domain;
+//   online softmax: running max m and sum l per query row, in-lane plus one
+//     exchange between half-waves;
+//   P is rounded to the working type (round to nearest even, the fix in the
+//     AOTriton 0.15b notes) and O^T += V^T P^T on the matrix cores.
+// Epilogue: O = acc / l, LSE = ln(2) * (m + log2 l); rows with no visible key
+// get O = 0 and LSE = +inf.
+#include "attn_device.hpp"
+#include "attn_launch.hpp"
+
+namespace sdpa {
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  } else {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 v;
+    v[0] = (T)a; v[1] = (T)b; v[2] = (T)c; v[3] = (T)d;
+    *reinterpret_cast<t4*>(p) = v;
+  }
+}
+
+template <typename M, int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
+  using T = typename M::elem;
+  constexpr int NT = NW * 64, BM = NW * 32, KPL = M::KPL;
+  constexpr int DVT = (D + 31) / 32, DPAD = DVT * 32;
+  constexpr int PAD = 16 / (int)sizeof(T);
+  constexpr int KLD = D + PAD, VLD = BN + PAD;
+  constexpr int KT = BN / 32;
+  constexpr int NS = D / (2 * KPL);
+  constexpr int STAGE = BN * KLD + DPAD * VLD;
+  __shared__ __attribute__((aligned(16))) T smem[2 * STAGE];
+
+  const ProblemArgs& P = a.p;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int nq = (int)(gridDim.x / (P.B * P.H));
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - (blk % nq);  // longest rows (under causal) first
+
+  long long q0 = 0, k0 = 0;
+  int sq = P.Sq, sk = P.Sk;
+  if (P.varlen) {
+    q0 = P.cu_q[b];
+    sq = P.cu_q[b + 1] - (int)q0;
+    k0 = P.cu_k[b];
+    sk = P.cu_k[b + 1] - (int)k0;
+  }
+  const int i0 = qb * BM;
+  if (i0 >= sq) return;
+  const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
+
+  const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
+  const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
+  const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
+  T* op = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + q0 * a.o.ss;
+  float* lp = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+
+  // Keys the block can see.
+  const int ilast = min(i0 + BM, sq) - 1;
+  const long long jlo = max(0LL, (long long)i0 + w.lo);
+  const long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
+  const bool block_empty = w.lo > w.hi || jlo > jhi;
+
+  const int iw0 = i0 + 32 * wave;
+  const bool wave_live = iw0 < sq;
+  const int qi = iw0 + r;  // this lane's query row
+
+  RowFrags<M, D> qf;
+  qf.load(qp + (long long)qi * a.q.ss, wave_live && qi < sq, g);
+
+  if constexpr (DPAD != D) {  // padding rows of the transposed V tile
+    for (int x = tid; x < (DPAD - D) * VLD; x += NT) {
+      smem[BN * KLD + D * VLD + x] = (T)0.f;
+      smem[STAGE + BN * KLD + D * VLD + x] = (T)0.f;
+    }
+  }
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[DVT];
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) acc[dt] = zero16();
+
+  if (!block_empty) {
+    const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
+    TileStage<T, BN, D, NT> ks, vs;
+    {
+      const int j0 = t0 * BN;
+      ks.load(kp + (long long)j0 * a.k.ss, a.k.ss, sk - j0, tid);
+      vs.load(vp + (long long)j0 * a.v.ss, a.v.ss, sk - j0, tid);
+      ks.store_rows(smem, KLD, tid);
+      vs.store_transposed(smem + BN * KLD, VLD, tid);
+    }
+    __syncthreads();
+
+    for (int t = t0; t <= t1; ++t) {
+      const int buf = (t - t0) & 1;
+      const int j0 = t * BN;
+      if (t < t1) {
+        const int jn = j0 + BN;
+        ks.load(kp + (long long)jn * a.k.ss, a.k.ss, sk - jn, tid);
+        vs.load(vp + (long long)jn * a.v.ss, a.v.ss, sk - jn, tid);
+      }
+      const T* Ks = smem + buf * STAGE;
+      const T* Vt = Ks + BN * KLD;
+      const int cls = wave_live ? classify(w, iw0, 32, j0, BN, sk) : kEmpty;
+      if (cls != kEmpty) {
+        // S^T = K Q^T, 32 keys per sub-tile.
+        f32x16 s[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          s[kt] = zero16();
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            const auto A = load_frag<M>(Ks + (32 * kt + r) * KLD + 2 * KPL * st + KPL * g);
+            s[kt] = M::mma(A, qf.f[st], s[kt]);
+          }
+        }
+        float x[KT][16];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) x[kt][e] = s[kt][e] * P.scale_log2;
+        if (cls == kPartial) {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int j = j0 + 32 * kt + acc_row(e, g);
+              const int diff = j - qi;
+              if (!(diff >= w.lo && diff <= w.hi && j < sk)) x[kt][e] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, x[kt][e]);
+        mx = halves_max(mx);
+        const float mnew = fmaxf(m, mx);
+        const float muse = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m - muse);
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            x[kt][e] = __builtin_amdgcn_exp2f(x[kt][e] - muse);
+            ls += x[kt][e];
+          }
+        l = l * alpha + ls;
+        m = mnew;
+#pragma unroll
+        for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+        // O^T += V^T P^T
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int st = 0; st < 16 / KPL; ++st) {
+            typename M::frag pf;
+            M::pack(&x[kt][KPL * st], pf);
+            const int pos = 32 * kt + perm_pos(KPL * st, g);
+#pragma unroll
+            for (int dt = 0; dt < DVT; ++dt) {
+              const auto A = load_frag<M>(Vt + (32 * dt + r) * VLD + pos);
+              acc[dt] = M::mma(A, pf, acc[dt]);
+            }
+          }
+      }
+      if (t < t1) {
+        T* nb = smem + (buf ^ 1) * STAGE;
+        ks.store_rows(nb, KLD, tid);
+        vs.store_transposed(nb + BN * KLD, VLD, tid);
+      }
+      __syncthreads();
+    }
+  }
+
+  if (wave_live) {
+    const float lt = halves_sum(l);
+    if (qi < sq) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      T* orow = op + (long long)qi * a.o.ss;
+#pragma unroll
+      for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * dt + 8 * q4 + 4 * g;
+          if (d < D)
+            store4<T>(orow + d, acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
+                      acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+        }
+      if (g == 0) lp[qi] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+    }
+  }
+}
+
+template <typename M, int D>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  constexpr int NW = 4, BN = 64, BM = NW * 32;
+  const long long nq = (a.p.Sq + BM - 1) / BM;
+  const long long nblk = nq * a.p.H * a.p.B;
+  if (nblk == 0) return hipSuccess;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+  FwdArgs args = a;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, NW, BN>), dim3((unsigned)nblk),
+                         dim3(NW * 64), kargs, 0, stream);
+}
+
+template <typename M>
+static hipError_t launch_fwd_d(int head_dim, const FwdArgs& a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_fwd_t<M, 64>(a, stream);
+    case 80: return launch_fwd_t<M, 80>(a, stream);
+    case 128: return launch_fwd_t<M, 128>(a, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, hipStream_t stream) {
+  switch (dtype) {
+    case 0: return launch_fwd_d<MmaF32>(head_dim, a, stream);
+    case 1: return launch_fwd_d<MmaF16>(head_dim, a, stream);
+    case 2: return launch_fwd_d<MmaBF16>(head_dim, a, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace sdpa

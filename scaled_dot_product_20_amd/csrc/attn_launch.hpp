@@ -1,0 +1,46 @@
+// attn_launch.hpp - kernel argument blocks and the launchers the C ABI calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+// Element strides of one operand: base + b*sb + h*sh + row*ss + d.  For the
+// packed layout sb is 0 and `row` is the packed row (cu_seqlens[b] + i).
+struct Operand {
+  const void* ptr;
+  long long sb, sh, ss;
+};
+
+struct ProblemArgs {
+  const int* cu_q;   // packed layout only
+  const int* cu_k;
+  int varlen;
+  int B, H;
+  int Sq, Sk;        // dense: exact lengths; packed: maxima
+  int wl, wr, diag;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  long long lse_sb, lse_sh;  // LSE / Delta: base + b*lse_sb + h*lse_sh + row
+  long long total_q;         // packed layout: rows of Q
+};
+
+struct FwdArgs {
+  ProblemArgs p;
+  Operand q, k, v, o;
+  float* lse;
+};
+
+struct BwdArgs {
+  ProblemArgs p;
+  Operand q, k, v, o, dout, dq, dk, dv;
+  const float* lse;
+  float* delta;
+};
+
+// dtype codes follow the C ABI: 0 fp32, 1 fp16, 2 bf16.
+hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream);
+
+}  // namespace sdpa

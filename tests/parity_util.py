@@ -1,0 +1,114 @@
+"""Shared helpers of the GPU parity tests: seeded inputs, the HIP path through
+the C ABI, the oracle on the same inputs, and the max-abs comparison at the
+tolerances the attention path is held to (O and LSE: fp32 1e-5, fp16 5e-3,
+bf16 2e-2; dQ/dK/dV twice those)."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+from oracle import oracle as orc
+from scaled_dot_product_20_amd import binding as bd
+from scaled_dot_product_20_amd import workloads as wl
+
+INF = wl.WINDOW_INF
+TOL = {torch.float32: 1e-5, torch.float16: 5e-3, torch.bfloat16: 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def max_err(name, got, ref, tol, inf_exact=False):
+    """Max |got - ref| over all elements; +inf in ref must be matched exactly."""
+    g = got.detach().double().cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (name, g.shape, r.shape)
+    assert not np.isnan(g).any(), f"{name}: NaN in GPU output"
+    if inf_exact:
+        inf = np.isinf(r)
+        assert np.array_equal(g[inf], r[inf]), f"{name}: +inf rows differ"
+        assert np.isfinite(g[~inf]).all(), f"{name}: unexpected inf"
+        g, r = g[~inf], r[~inf]
+    err = float(np.abs(g - r).max()) if g.size else 0.0
+    assert err <= tol, f"{name}: max abs err {err:.3e} > {tol:.1e}"
+    return err
+
+
+class Case:
+    """A small problem run end to end on the GPU and on the oracle."""
+
+    def __init__(self, *, layout="bhsd", B=1, H=2, Sq=64, Sk=None, D=64, dtype=torch.bfloat16,
+                 window=(INF, INF), diag="top_left", scale=None, seed=0, lens_q=None, lens_k=None,
+                 bshd=False):
+        self.layout, self.B, self.H, self.D, self.dtype = layout, B, H, D, dtype
+        self.Sq, self.Sk = Sq, (Sq if Sk is None else Sk)
+        self.window, self.diag = window, diag
+        self.scale = 1.0 / math.sqrt(D) if scale is None else scale
+        self.seed, self.bshd = seed, bshd
+        if layout == "thd":
+            self.lens_q, self.lens_k = list(lens_q), list(lens_k)
+            self.cu_q, self.cu_k = wl.prefix(self.lens_q), wl.prefix(self.lens_k)
+            tq, tk = int(self.cu_q[-1]), int(self.cu_k[-1])
+            shapes = [(tq, H, D), (tk, H, D), (tk, H, D), (tq, H, D)]
+        elif bshd:  # drawn as [B, S, H, D] and viewed as [B, H, S, D]
+            shapes = [(B, self.Sq, H, D), (B, self.Sk, H, D), (B, self.Sk, H, D), (B, self.Sq, H, D)]
+        else:
+            shapes = [(B, H, self.Sq, D), (B, H, self.Sk, D), (B, H, self.Sk, D), (B, H, self.Sq, D)]
+        q, k, v, do = wl.draw(shapes, seed, dtype)
+        if bshd:
+            q, k, v, do = (t.permute(0, 2, 1, 3) for t in (q, k, v, do))
+        self.cpu = (q, k, v, do)
+
+    def kw_oracle(self):
+        kw = dict(scale=self.scale, window=self.window, diag=self.diag)
+        if self.layout == "thd":
+            kw.update(cu_seqlens_q=self.cu_q, cu_seqlens_k=self.cu_k)
+        return kw
+
+    def kw_gpu(self, dev):
+        kw = dict(scale=self.scale, window=self.window, diag=self.diag)
+        if self.layout == "thd":
+            kw.update(cu_seqlens_q=torch.from_numpy(self.cu_q).to(dev),
+                      cu_seqlens_k=torch.from_numpy(self.cu_k).to(dev),
+                      max_seqlen_q=max(self.lens_q + [0]), max_seqlen_k=max(self.lens_k + [0]))
+        return kw
+
+    def gpu(self, dev="cuda", bwd=True):
+        q, k, v, do = (t.to(dev) for t in self.cpu)  # strides kept (bshd views stay views)
+        if self.bshd:
+            q, k, v, do = (t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (q, k, v, do))
+        kw = self.kw_gpu(dev)
+        o, lse = bd.attn_fwd(q, k, v, **kw)
+        out = {"o": o, "lse": lse}
+        if bwd:
+            dq, dk, dv = bd.attn_bwd(do, q, k, v, o, lse, **kw)
+            out.update(dq=dq, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        return out
+
+    def oracle(self, bwd=True):
+        q, k, v, do = (t.contiguous() for t in self.cpu)
+        if bwd:
+            o, lse, dq, dk, dv = orc.bwd(q, k, v, do, **self.kw_oracle())
+            return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+        o, lse = orc.fwd(q, k, v, **self.kw_oracle())
+        return {"o": o, "lse": lse}
+
+    def check(self, bwd=True, dev="cuda"):
+        say(f"case layout={self.layout} B={self.B} H={self.H} Sq={self.Sq} Sk={self.Sk} D={self.D} "
+            f"dtype={self.dtype} window={self.window} diag={self.diag} scale={self.scale} seed={self.seed}")
+        got = self.gpu(dev, bwd)
+        ref = self.oracle(bwd)
+        tol = TOL[self.dtype]
+        errs = {"o": max_err("O", got["o"], ref["o"], tol),
+                "lse": max_err("LSE", got["lse"], ref["lse"], tol, inf_exact=True)}
+        if bwd:
+            for n in ("dq", "dk", "dv"):
+                errs[n] = max_err(n, got[n], ref[n], 2 * tol)
+        say("  errs", {k: f"{v:.2e}" for k, v in errs.items()})
+        return got, ref, errs
