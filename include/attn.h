@@ -136,6 +136,19 @@ hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
  * sums are computed without atomics: results are run-to-run identical. */
 hipError_t attn_bwd(const attn_bwd_params *p, hipStream_t stream);
 
+/* The three steps of attn_bwd as separate calls, for callers that schedule
+ * or time them one by one.  Same parameters, validation and errors as
+ * attn_bwd; each enqueues one kernel on `stream`.  They must run in this
+ * order on one stream (or be ordered by events): attn_bwd_dkdv and
+ * attn_bwd_dq read the Delta that attn_bwd_preprocess leaves in the
+ * workspace, which must not be touched in between.
+ *   attn_bwd_preprocess: Delta_i = sum_d dO_id O_id into the workspace.
+ *   attn_bwd_dkdv:       dK and dV, one workgroup per block of keys.
+ *   attn_bwd_dq:         dQ, one workgroup per block of queries. */
+hipError_t attn_bwd_preprocess(const attn_bwd_params *p, hipStream_t stream);
+hipError_t attn_bwd_dkdv(const attn_bwd_params *p, hipStream_t stream);
+hipError_t attn_bwd_dq(const attn_bwd_params *p, hipStream_t stream);
+
 /* Workspace bytes attn_bwd needs for this problem (fp32 Delta per query row
  * and head, rounded up to 256 bytes); 0 when the problem is malformed. */
 uint64_t attn_bwd_workspace_size(const attn_bwd_params *p);

@@ -71,7 +71,9 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m scaled_dot_product_20_amd.build`")
         l = ctypes.CDLL(LIB_PATH)
-        for name, ptype in (("attn_fwd", FwdParams), ("attn_bwd", BwdParams)):
+        for name, ptype in (("attn_fwd", FwdParams), ("attn_bwd", BwdParams),
+                            ("attn_bwd_preprocess", BwdParams), ("attn_bwd_dkdv", BwdParams),
+                            ("attn_bwd_dq", BwdParams)):
             f = getattr(l, name)
             f.argtypes = [ctypes.POINTER(ptype), ctypes.c_void_p]
             f.restype = ctypes.c_int
@@ -207,6 +209,47 @@ def bwd_params(dout, q, k, v, o, lse, dq, dk, dv, workspace, **kw) -> BwdParams:
         p.workspace = _ptr(workspace)
         p.workspace_bytes = workspace.numel() * workspace.element_size()
     return p
+
+
+def prepare_bwd(dout, q, k, v, o, lse, *, scale=None, window=(WINDOW_INF, WINDOW_INF), diag="top_left",
+                cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+                dq=None, dk=None, dv=None, workspace=None):
+    """Allocate the outputs and workspace of a backward and fill its params
+    once, for callers that launch it repeatedly or step by step.  Returns
+    (params, (dq, dk, dv, workspace)); the tensors must outlive every launch
+    made with the params."""
+    _check_inputs(q, k, v, o, dout)
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    cu_q, cu_k = _cu(cu_seqlens_q, dev), _cu(cu_seqlens_k, dev)
+    if q.dim() == 3:
+        max_seqlen_q = _max_len(cu_q) if max_seqlen_q is None else max_seqlen_q
+        max_seqlen_k = _max_len(cu_k) if max_seqlen_k is None else max_seqlen_k
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    kw = dict(scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **kw)
+    if workspace is None:
+        need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    p._keep = (cu_q, cu_k)  # device cu_seqlens referenced by the params
+    return p, (dq, dk, dv, workspace)
+
+
+def launch(name: str, params, stream: Optional[int] = None) -> None:
+    """Call one C entry point (``attn_fwd``, ``attn_bwd``,
+    ``attn_bwd_preprocess``, ``attn_bwd_dkdv`` or ``attn_bwd_dq``) with
+    filled params on ``stream`` (default: torch's current stream)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    rc = getattr(lib(), name)(ctypes.byref(params), ctypes.c_void_p(stream))
+    if rc:
+        raise AttnError(name, rc)
 
 
 def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,

@@ -229,7 +229,11 @@ hipError_t attn_bwd_check(const attn_bwd_params* p) {
   return hipSuccess;
 }
 
-hipError_t attn_bwd(const attn_bwd_params* p, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+hipError_t bwd_stages(const attn_bwd_params* p, int stages, hipStream_t stream) {
   hipError_t err = attn_bwd_check(p);
   if (err != hipSuccess) return err;
   const attn_fwd_params* f = &p->fwd;
@@ -246,7 +250,28 @@ hipError_t attn_bwd(const attn_bwd_params* p, hipStream_t stream) {
   a.dv = operand(p->dv, p->dv_stride, packed);
   a.lse = f->lse;
   a.delta = static_cast<float*>(p->workspace);
-  return on_stream_device(stream, [&] { return sdpa::launch_bwd(f->dtype, f->head_dim, a, stream); });
+  return on_stream_device(stream,
+                          [&] { return sdpa::launch_bwd(f->dtype, f->head_dim, a, stages, stream); });
+}
+
+}  // namespace
+
+extern "C" {
+
+hipError_t attn_bwd(const attn_bwd_params* p, hipStream_t stream) {
+  return bwd_stages(p, sdpa::kStageAll, stream);
+}
+
+hipError_t attn_bwd_preprocess(const attn_bwd_params* p, hipStream_t stream) {
+  return bwd_stages(p, sdpa::kStageDelta, stream);
+}
+
+hipError_t attn_bwd_dkdv(const attn_bwd_params* p, hipStream_t stream) {
+  return bwd_stages(p, sdpa::kStageDkDv, stream);
+}
+
+hipError_t attn_bwd_dq(const attn_bwd_params* p, hipStream_t stream) {
+  return bwd_stages(p, sdpa::kStageDq, stream);
 }
 
 }  // extern "C"

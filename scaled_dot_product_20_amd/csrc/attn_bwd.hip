@@ -406,7 +406,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 // ------------------------------------------------------------ launch
 
 template <typename M, int D>
-static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   using T = typename M::elem;
   // fp32 tiles are halved along the key axis of the dQ kernel to fit LDS.
   constexpr int NW_KV = 4, BMQ = 32, NW_Q = 4, BN = sizeof(T) == 4 ? 32 : 64;
@@ -414,7 +414,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   void* kargs[] = {&args};
   hipError_t err;
   // 1. Delta.
-  {
+  if (stages & kStageDelta) {
     const long long nrows =
         a.p.varlen ? a.p.total_q * a.p.H : (long long)a.p.B * a.p.H * a.p.Sq;
     constexpr int CE = 16 / (int)sizeof(T), CH = D / CE;
@@ -430,7 +430,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     }
   }
   // 2. dK, dV.
-  {
+  if (stages & kStageDkDv) {
     const long long nkb = (a.p.Sk + NW_KV * 32 - 1) / (NW_KV * 32);
     const long long nblk = nkb * a.p.H * a.p.B;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -441,7 +441,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     }
   }
   // 3. dQ.
-  {
+  if (stages & kStageDq) {
     const long long nq = (a.p.Sq + NW_Q * 32 - 1) / (NW_Q * 32);
     const long long nblk = nq * a.p.H * a.p.B;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -455,20 +455,20 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 }
 
 template <typename M>
-static hipError_t launch_bwd_d(int head_dim, const BwdArgs& a, hipStream_t stream) {
+static hipError_t launch_bwd_d(int head_dim, const BwdArgs& a, int stages, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_bwd_t<M, 64>(a, stream);
-    case 80: return launch_bwd_t<M, 80>(a, stream);
-    case 128: return launch_bwd_t<M, 128>(a, stream);
+    case 64: return launch_bwd_t<M, 64>(a, stages, stream);
+    case 80: return launch_bwd_t<M, 80>(a, stages, stream);
+    case 128: return launch_bwd_t<M, 128>(a, stages, stream);
     default: return hipErrorNotSupported;
   }
 }
 
-hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, hipStream_t stream) {
   switch (dtype) {
-    case 0: return launch_bwd_d<MmaF32>(head_dim, a, stream);
-    case 1: return launch_bwd_d<MmaF16>(head_dim, a, stream);
-    case 2: return launch_bwd_d<MmaBF16>(head_dim, a, stream);
+    case 0: return launch_bwd_d<MmaF32>(head_dim, a, stages, stream);
+    case 1: return launch_bwd_d<MmaF16>(head_dim, a, stages, stream);
+    case 2: return launch_bwd_d<MmaBF16>(head_dim, a, stages, stream);
     default: return hipErrorNotSupported;
   }
 }

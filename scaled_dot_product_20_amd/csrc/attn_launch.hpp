@@ -39,8 +39,11 @@ struct BwdArgs {
   float* delta;
 };
 
+// Steps of the backward, as a bit mask of `stages`; they run in this order.
+constexpr int kStageDelta = 1, kStageDkDv = 2, kStageDq = 4, kStageAll = 7;
+
 // dtype codes follow the C ABI: 0 fp32, 1 fp16, 2 bf16.
 hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, hipStream_t stream);
 
 }  // namespace sdpa

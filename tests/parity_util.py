@@ -64,6 +64,13 @@ class Case:
             q, k, v, do = (t.permute(0, 2, 1, 3) for t in (q, k, v, do))
         self.cpu = (q, k, v, do)
 
+    def tol_factor(self):
+        """1 at the configs' scale 1/sqrt(D).  Off that scale the logits, the
+        exponent errors and the gradient magnitudes all grow with
+        |scale| * sqrt(D) (the logit standard deviation for N(0,1) inputs), so
+        the absolute bound grows with it."""
+        return max(1.0, abs(self.scale) * math.sqrt(self.D))
+
     def kw_oracle(self):
         kw = dict(scale=self.scale, window=self.window, diag=self.diag)
         if self.layout == "thd":
@@ -104,7 +111,7 @@ class Case:
             f"dtype={self.dtype} window={self.window} diag={self.diag} scale={self.scale} seed={self.seed}")
         got = self.gpu(dev, bwd)
         ref = self.oracle(bwd)
-        tol = TOL[self.dtype]
+        tol = TOL[self.dtype] * self.tol_factor()
         errs = {"o": max_err("O", got["o"], ref["o"], tol),
                 "lse": max_err("LSE", got["lse"], ref["lse"], tol, inf_exact=True)}
         if bwd:
