@@ -77,6 +77,17 @@ __device__ __forceinline__ typename M::frag load_frag(const typename M::elem* p)
   return *reinterpret_cast<const typename M::frag*>(p);
 }
 
+// Exact negation of every element of a fragment (flips the sign bits).
+template <typename F>
+__device__ __forceinline__ F negate_frag(F f) {
+  if constexpr (sizeof(F) == 4) {
+    return __builtin_bit_cast(F, __builtin_bit_cast(uint32_t, f) ^ 0x80000000u);
+  } else {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(F, __builtin_bit_cast(u4, f) ^ 0x80008000u);
+  }
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -256,6 +267,10 @@ struct RowFrags {
       else
         f[s] = typename M::frag{};
     }
+  }
+  __device__ __forceinline__ void negate() {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) f[s] = negate_frag(f[s]);
   }
 };
 

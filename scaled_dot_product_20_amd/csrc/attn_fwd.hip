@@ -12,10 +12,13 @@
 // Per key tile of BN keys:
 //   K (row-major) and V (transposed) are staged HBM -> registers -> LDS,
 //     double-buffered, the next tile's loads in flight during this tile;
-//   S^T = K Q^T on the matrix cores (Q fragments stay in registers), scaled
-//     into the log2 domain;
-//   online softmax: running max m and sum l per query row, in-lane plus one
-//     exchange between half-waves;
+//   S^T = K Q^T on the matrix cores (Q fragments stay in registers);
+//   online softmax in the log2 domain: x = c*s with c = |scale|*log2(e)
+//     (a negative scale is moved into Q, so c >= 0 and max_j x_j is
+//     c * max_j s_j), p = 2^(x - m) in one FMA and one exp;
+//   the reference max m of a row is only raised when the tile's max exceeds
+//     it by more than kRescaleSlack (so p <= 2^kRescaleSlack); O and l are
+//     rescaled only then, and skipped when no row of the wave moved;
 //   P is rounded to the working type (round to nearest even, the fix in the
 //     AOTriton 0.15b notes) and O^T += V^T P^T on the matrix cores.
 // Epilogue: O = acc / l, LSE = ln(2) * (m + log2 l); rows with no visible key
@@ -24,6 +27,9 @@
 #include "attn_launch.hpp"
 
 namespace sdpa {
+
+// Largest log2 growth of a row max absorbed without rescaling.
+constexpr float kRescaleSlack = 8.f;
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
@@ -86,6 +92,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
 
   RowFrags<M, D> qf;
   qf.load(qp + (long long)qi * a.q.ss, wave_live && qi < sq, g);
+  const float c = fabsf(P.scale_log2);
+  if (P.scale_log2 < 0.f) qf.negate();
 
   if constexpr (DPAD != D) {  // padding rows of the transposed V tile
     for (int x = tid; x < (DPAD - D) * VLD; x += NT) {
@@ -134,44 +142,49 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
             s[kt] = M::mma(A, qf.f[st], s[kt]);
           }
         }
-        float x[KT][16];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) x[kt][e] = s[kt][e] * P.scale_log2;
-        if (cls == kPartial) {
+        const bool partial = cls == kPartial;
+        if (partial) {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
               const int j = j0 + 32 * kt + acc_row(e, g);
               const int diff = j - qi;
-              if (!(diff >= w.lo && diff <= w.hi && j < sk)) x[kt][e] = -INFINITY;
+              if (!(diff >= w.lo && diff <= w.hi && j < sk)) s[kt][e] = -INFINITY;
             }
         }
-        float mx = -INFINITY;
+        float smax = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, x[kt][e]);
-        mx = halves_max(mx);
-        const float mnew = fmaxf(m, mx);
-        const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m - muse);
+          for (int e = 0; e < 16; ++e) smax = fmaxf(smax, s[kt][e]);
+        smax = halves_max(smax);
+        // Max of x = c*s over the row's visible keys of this tile.
+        const float mx = smax == -INFINITY ? -INFINITY : smax * c;
+        const bool raise = mx > m + kRescaleSlack;  // also when m is still -inf
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+          const float alpha = raise ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+          if (raise) m = mx;
+          l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+        }
+        // A row with no visible key so far keeps m = -inf; its p must be 0.
+        const float nm = m == -INFINITY ? 0.f : -m;
+        float x[KT][16];
         float ls = 0.f;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            x[kt][e] = __builtin_amdgcn_exp2f(x[kt][e] - muse);
-            ls += x[kt][e];
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, nm));
+            if (partial && s[kt][e] == -INFINITY) pe = 0.f;
+            x[kt][e] = pe;
+            ls += pe;
           }
-        l = l * alpha + ls;
-        m = mnew;
-#pragma unroll
-        for (int dt = 0; dt < DVT; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+        l += ls;
         // O^T += V^T P^T
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
@@ -215,9 +228,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// Workgroup shape per element type: 8 waves (two per SIMD) for the 16-bit
+// types; the fp32 tiles are twice as large in LDS and registers, so 4 waves.
+template <typename M>
+struct FwdShape {
+  static constexpr int NW = sizeof(typename M::elem) == 4 ? 4 : 8;
+  static constexpr int BN = 64;
+};
+
 template <typename M, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NW = 4, BN = 64, BM = NW * 32;
+  constexpr int NW = FwdShape<M>::NW, BN = FwdShape<M>::BN, BM = NW * 32;
   const long long nq = (a.p.Sq + BM - 1) / BM;
   const long long nblk = nq * a.p.H * a.p.B;
   if (nblk == 0) return hipSuccess;
