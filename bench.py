@@ -131,6 +131,24 @@ def cpu_baseline(w, dtype, min_seconds=10.0, max_slices=32):
             "seconds": round(spent, 2)}
 
 
+def copy_probe(mib: int, steps: int) -> None:
+    """A plain copy of `mib` MiB between two device buffers, `steps` times:
+    each launch reads and writes exactly mib MiB, so what an HBM byte
+    counter reports per launch, divided by that, is the counter's scale."""
+    import torch
+    n = mib * 2**20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_probe_bytes": n, "launches": steps, "ms": round(dt * 1e3, 4),
+                      "gb_s_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +158,9 @@ def main():
     ap.add_argument("--dtype", default=None, help="bf16 / fp16 / fp32 (default: the workload's first)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--passes", default=None, help="fwd or fwd,bwd (default: the workload's)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the attention step, run a plain device-to-device copy of MIB "
+                         "MiB (the calibration kernel for HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -155,6 +176,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
     W = wls.workloads()[args.workload]
     names = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
     dtype = names[args.dtype] if args.dtype else W.dtypes[0]

@@ -1,0 +1,106 @@
+"""GPU parity at the full sizes of the timed workloads, on sampled outputs.
+
+Each workload of ``workloads.workloads()`` runs on the GPU exactly as
+``bench.py`` launches it (the same C entry points, the same filled params,
+torch's current stream).  The fp64 oracle then computes, one by one, sampled
+rows of O / LSE / dQ and sampled key rows of dK / dV of a few (sequence,
+head) slices -- first and last rows, rows on both sides of every block size
+the kernels use, the ragged tail, a few seeded random rows -- and each is
+compared element by element at the path's tolerances.  Every full output is
+also checked for NaN, and LSE for finiteness where every row sees a key.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from parity_util import TOL, max_err, say
+from scaled_dot_product_20_amd import binding as bd
+from scaled_dot_product_20_amd import workloads as wls
+
+pytestmark = pytest.mark.gpu
+
+# Block edges of the kernels' tiles (32-row waves, 64/128/256-row blocks).
+EDGES = (0, 1, 31, 32, 63, 64, 127, 128, 255, 256)
+
+
+def sample_rows(n, seed, extra=4):
+    if n <= 0:
+        return []
+    rng = np.random.default_rng(seed)
+    rows = {r for r in EDGES if r < n}
+    rows |= {n // 2, max(0, n - 2), n - 1}
+    rows |= {int(x) for x in rng.integers(0, n, size=extra)}
+    return sorted(rows)
+
+
+def slices_of(w):
+    """(b, h) pairs to sample: first, last and one in the middle; for packed
+    inputs the longest, shortest and most shifted sequences."""
+    if w.layout == "bhsd":
+        pairs = {(0, 0), (w.batch - 1, w.heads - 1), (w.batch // 2, w.heads // 2)}
+    else:
+        lq, lk = np.array(w.lens_q), np.array(w.lens_k)
+        pairs = {(int(lq.argmax()), 0), (int(lq.argmin()), w.heads - 1),
+                 (int((lk - lq).argmax()), w.heads // 2)}
+    return sorted(pairs)
+
+
+FULL = [(name, dt) for name, w in wls.workloads().items() if name != "tiny_f32" for dt in w.dtypes]
+
+
+@pytest.mark.parametrize("name,dtype", FULL, ids=[f"{n}-{str(d).split('.')[-1]}" for n, d in FULL])
+def test_full_size_sampled(name, dtype):
+    w = wls.workloads()[name]
+    dev = torch.device("cuda:0")
+    say(f"full-size case {name} dtype={dtype} layout={w.layout} B={w.batch} H={w.heads} "
+        f"D={w.head_dim} Sq={w.seqlen_q} Sk={w.seqlen_k} window={w.window} diag={w.diag}")
+    q, k, v, do = w.inputs(dtype)
+    cu_q, cu_k = w.cu_seqlens()
+    kw = dict(scale=w.scale, window=w.window, diag=w.diag)
+    okw = dict(kw)
+    if w.layout == "thd":
+        kw.update(cu_seqlens_q=torch.from_numpy(cu_q).to(dev), cu_seqlens_k=torch.from_numpy(cu_k).to(dev),
+                  max_seqlen_q=w.seqlen_q, max_seqlen_k=w.seqlen_k)
+        okw.update(cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
+    gq, gk, gv, gdo = (t.to(dev) for t in (q, k, v, do))
+
+    # The bench's launch sequence: attn_fwd, then the three backward steps.
+    o, lse = bd.attn_fwd(gq, gk, gv, **kw)
+    fkw = dict(cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None)
+    fkw.update(kw)
+    fp = bd.fwd_params(gq, gk, gv, o, lse, **fkw)
+    bp, (dq, dk, dv, _ws) = bd.prepare_bwd(gdo, gq, gk, gv, o, lse, **kw)
+    for entry, params in (("attn_fwd", fp), ("attn_bwd_preprocess", bp), ("attn_bwd_dkdv", bp),
+                          ("attn_bwd_dq", bp)):
+        bd.launch(entry, params)
+    torch.cuda.synchronize()
+    for nm, t in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert not torch.isnan(t).any().item(), f"{nm}: NaN in the full output"
+    if w.window[0] == wls.WINDOW_INF or w.diag == "bottom_right":
+        # No mask, causal, or a bottom-right window with Sk >= Sq: every row sees a key.
+        assert torch.isfinite(lse).all().item()
+
+    tol = TOL[dtype]
+    lens = list(zip(w.lens_q, w.lens_k)) if w.layout == "thd" else None
+    for (b, h) in slices_of(w):
+        sq, sk = lens[b] if lens else (w.seqlen_q, w.seqlen_k)
+        rows = sample_rows(sq, 1000 * b + h)
+        cols = sample_rows(sk, 7000 + 1000 * b + h)
+        say(f"  slice b={b} h={h} Sq={sq} Sk={sk}: {len(rows)} rows, {len(cols)} key rows")
+        if lens:
+            qi = torch.tensor([int(cu_q[b]) + r for r in rows])
+            kj = torch.tensor([int(cu_k[b]) + c for c in cols])
+            g_o, g_l, g_dq = o[qi, h].cpu(), lse[h, qi].cpu(), dq[qi, h].cpu()
+            g_dk, g_dv = dk[kj, h].cpu(), dv[kj, h].cpu()
+        else:
+            ri, cj = torch.tensor(rows), torch.tensor(cols)
+            g_o, g_l, g_dq = o[b, h, ri].cpu(), lse[b, h, ri].cpu(), dq[b, h, ri].cpu()
+            g_dk, g_dv = dk[b, h, cj].cpu(), dv[b, h, cj].cpu()
+        r_o, r_l = orc.fwd_rows(q, k, v, b, h, rows, **okw)
+        r_dq = orc.bwd_dq_rows(q, k, v, do, b, h, rows, **okw)
+        r_dk, r_dv = orc.bwd_dkdv_cols(q, k, v, do, b, h, cols, **okw)
+        errs = {"o": max_err("O", g_o, r_o, tol), "lse": max_err("LSE", g_l, r_l, tol, inf_exact=True),
+                "dq": max_err("dQ", g_dq, r_dq, 2 * tol), "dk": max_err("dK", g_dk, r_dk, 2 * tol),
+                "dv": max_err("dV", g_dv, r_dv, 2 * tol)}
+        say("    errs", {n: f"{e:.2e}" for n, e in errs.items()})
