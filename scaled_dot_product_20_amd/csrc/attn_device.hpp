@@ -275,3 +275,100 @@ struct RowFrags {
 };
 
 }  // namespace sdpa
+
+namespace sdpa {
+
+// ------------------------------------------- swizzled 16-bit LDS tiles
+
+// A tile of 16-bit rows kept row-major in LDS, each row in 16-byte chunks.
+// Chunk c of row r sits at chunk slot c ^ sigma(r) of that row, so that
+//  - a 128-bit read of one chunk by 16 consecutive rows (an MFMA operand
+//    read straight from rows), and
+//  - a 64-bit transposing read of 4 consecutive rows (aligned to 4) x 4
+//    consecutive chunks (aligned to 4) by 32 lanes (an operand read across
+//    rows, see tr_frag)
+// both touch every bank once.  Rows are 8 chunk slots (head_dim 64) or 16
+// (head_dim 80 and 128; 80 leaves slots unused).
+template <int D>
+struct Swz {
+  static constexpr int CH = D / 8;                // chunks holding data
+  static constexpr int SLOTS = D <= 64 ? 8 : 16;  // chunk slots per row
+  static constexpr int PITCH = SLOTS * 8;         // elements per row
+  static_assert(D % 16 == 0 && D <= 128, "head_dim must be a multiple of 16, at most 128");
+  __host__ __device__ static constexpr int sigma(int r) {
+    return SLOTS == 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+  // Element offset of chunk c of row r.
+  __host__ __device__ static constexpr int off(int r, int c) { return r * PITCH + ((c ^ sigma(r)) << 3); }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copies rows [0, ROWS) of a row-major global tile into a swizzled LDS tile
+// with direct global->LDS loads (16 bytes per lane, 64 lanes filling 1 KiB of
+// consecutive slots).  Rows at or beyond `nvalid` (>= 1) repeat row
+// nvalid-1, so every loaded value is a finite input value.  The loads are
+// asynchronous: a barrier after `s_waitcnt vmcnt(0)` publishes them.
+template <typename T, int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(T* lds, const T* __restrict__ g, long long row_stride, int nvalid,
+                                         int wave, int lane) {
+  using L = Swz<D>;
+  constexpr int RPI = 64 / L::SLOTS;  // rows per instruction
+  constexpr int NI = ROWS / RPI;
+  static_assert(ROWS % RPI == 0, "tile rows");
+  const int rl = lane / L::SLOTS, slot = lane % L::SLOTS;
+#pragma unroll
+  for (int i = wave; i < NI; i += NW) {
+    const int row = i * RPI + rl;
+    const int c = slot ^ L::sigma(row);
+    const int src = row < nvalid ? row : nvalid - 1;
+    if (L::CH == L::SLOTS || c < L::CH)
+      __builtin_amdgcn_global_load_lds((const void*)(g + (long long)src * row_stride + c * 8),
+                                       (lds_void*)(lds + i * RPI * L::PITCH), 16, 0, 0);
+  }
+}
+
+// Zeroes the chunk slots of a tile that dma_tile never writes (head_dim 80).
+template <typename T, int D, int ROWS, int NT>
+__device__ __forceinline__ void zero_unused_slots(T* lds, int tid) {
+  using L = Swz<D>;
+  if constexpr (L::CH < L::SLOTS) {
+    constexpr int PER_ROW = L::SLOTS - L::CH;
+    for (int x = tid; x < ROWS * PER_ROW; x += NT) {
+      const int row = x / PER_ROW, c = L::CH + x % PER_ROW;
+      *reinterpret_cast<uint4*>(lds + L::off(row, c)) = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// A operand (32 x 16) read straight from rows row0 .. row0+31 of a swizzled
+// tile, K step st: lane (r, g) gets chunk 2*st + g of row row0 + r.
+template <typename M, int D>
+__device__ __forceinline__ typename M::frag row_frag(const typename M::elem* lds, int row0, int st, int r, int g) {
+  return *reinterpret_cast<const typename M::frag*>(lds + Swz<D>::off(row0 + r, 2 * st + g));
+}
+
+// A operand (32 columns x 16 rows of the tile, i.e. the transpose of a
+// 16 x 32 block) read with two transposing loads: lane (r, g) gets column
+// 32*dt + r of rows ra + 4*g + {0..3} (elements 0..3) and rb + 4*g + {0..3}
+// (elements 4..7); ra and rb are multiples of 8.  Within each 16-lane group
+// the transposing load hands lane j the j-th column of the 4 rows x 16
+// columns the group's lanes address, 4 consecutive elements per lane.
+template <typename M, int D>
+__device__ __forceinline__ typename M::frag tr_frag(const typename M::elem* lds, int ra, int rb, int dt, int lane) {
+  using L = Swz<D>;
+  const int s = lane & 15, grp = lane >> 4, g = lane >> 5;
+  const int col = 32 * dt + 16 * (grp & 1) + 4 * (s & 3);
+  const int c = col >> 3, half = (col >> 2) & 1;
+  const int dr = 4 * g + (s >> 2);
+  const auto* pa = lds + L::off(ra + dr, c) + 4 * half;
+  const auto* pb = lds + L::off(rb + dr, c) + 4 * half;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)pa);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)pb);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(typename M::frag, v);
+}
+
+}  // namespace sdpa

@@ -228,11 +228,185 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
-// Workgroup shape per element type: 8 waves (two per SIMD) for the 16-bit
-// types; the fp32 tiles are twice as large in LDS and registers, so 4 waves.
+// ------------------------------------------------------ 16-bit kernel
+//
+// The bf16 / fp16 forward.  K and V tiles are copied HBM -> LDS with direct
+// loads into swizzled row-major tiles (two stages, the next tile's copy in
+// flight while this one is used); K feeds S^T = K Q^T with 128-bit row
+// reads and V feeds O^T += V^T P^T through transposing reads, so no tile is
+// ever rearranged by the waves.  Tiles the window leaves whole run a path
+// with no masking at all.
+template <typename M, int D, int NW, int BN>
+__device__ __forceinline__ void fwd16_tile(const typename M::elem* Ks, const typename M::elem* Vs,
+                                           const typename M::frag* qf, f32x16* acc, float& m, float& l,
+                                           float c, bool masked, Window w, int j0, int qi, int sk,
+                                           int r, int g, int lane) {
+  constexpr int KT = BN / 32, NS = D / 16, DVT = (D + 31) / 32;
+  f32x16 s[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    s[kt] = zero16();
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      s[kt] = M::mma(row_frag<M, D>(Ks, 32 * kt, st, r, g), qf[st], s[kt]);
+  }
+  if (masked) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = j0 + 32 * kt + acc_row(e, g);
+        const int diff = j - qi;
+        if (!(diff >= w.lo && diff <= w.hi && j < sk)) s[kt][e] = -INFINITY;
+      }
+  }
+  float smax = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) smax = fmaxf(smax, s[kt][e]);
+  smax = halves_max(smax);
+  const float mx = smax == -INFINITY ? -INFINITY : smax * c;
+  const bool raise = mx > m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(raise)) {
+    const float alpha = raise ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+    if (raise) m = mx;
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+  }
+  const float nm = m == -INFINITY ? 0.f : -m;
+  float ls = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, nm));
+      if (masked && s[kt][e] == -INFINITY) pe = 0.f;  // also when c == 0
+      x[e] = pe;
+      ls += pe;
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      typename M::frag pf;
+      M::pack(&x[8 * st], pf);
+      const int ra = 32 * kt + 16 * st;
+#pragma unroll
+      for (int dt = 0; dt < DVT; ++dt) acc[dt] = M::mma(tr_frag<M, D>(Vs, ra, ra + 8, dt, lane), pf, acc[dt]);
+    }
+  }
+  l += ls;
+}
+
+template <typename M, int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64) void attn_fwd16_kernel(FwdArgs a) {
+  using T = typename M::elem;
+  using L = Swz<D>;
+  constexpr int NT = NW * 64, BM = NW * 32, DVT = (D + 31) / 32;
+  constexpr int TILE = BN * L::PITCH;  // elements of one K or V tile
+  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];  // [stage][K, V]
+
+  const ProblemArgs& P = a.p;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int nq = (int)(gridDim.x / (P.B * P.H));
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - (blk % nq);
+
+  long long q0 = 0, k0 = 0;
+  int sq = P.Sq, sk = P.Sk;
+  if (P.varlen) {
+    q0 = P.cu_q[b];
+    sq = P.cu_q[b + 1] - (int)q0;
+    k0 = P.cu_k[b];
+    sk = P.cu_k[b + 1] - (int)k0;
+  }
+  const int i0 = qb * BM;
+  if (i0 >= sq) return;
+  const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
+
+  const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
+  const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
+  const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
+  T* op = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + q0 * a.o.ss;
+  float* lp = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+
+  const int ilast = min(i0 + BM, sq) - 1;
+  const long long jlo = max(0LL, (long long)i0 + w.lo);
+  const long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
+  const bool block_empty = w.lo > w.hi || jlo > jhi;
+
+  const int iw0 = i0 + 32 * wave;
+  const bool wave_live = iw0 < sq;
+  const int qi = iw0 + r;
+
+  RowFrags<M, D> qf;
+  qf.load(qp + (long long)qi * a.q.ss, wave_live && qi < sq, g);
+  const float c = fabsf(P.scale_log2);
+  if (P.scale_log2 < 0.f) qf.negate();
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[DVT];
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) acc[dt] = zero16();
+
+  if (!block_empty) {
+    zero_unused_slots<T, D, 4 * BN, NT>(smem, tid);
+    const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
+    {
+      const int j0 = t0 * BN;
+      dma_tile<T, D, BN, NW>(smem, kp + (long long)j0 * a.k.ss, a.k.ss, sk - j0, wave, lane);
+      dma_tile<T, D, BN, NW>(smem + TILE, vp + (long long)j0 * a.v.ss, a.v.ss, sk - j0, wave, lane);
+    }
+    __syncthreads();
+    for (int t = t0; t <= t1; ++t) {
+      const int stg = (t - t0) & 1;
+      const int j0 = t * BN;
+      if (t < t1) {
+        T* nb = smem + (stg ^ 1) * 2 * TILE;
+        const int jn = j0 + BN;
+        dma_tile<T, D, BN, NW>(nb, kp + (long long)jn * a.k.ss, a.k.ss, sk - jn, wave, lane);
+        dma_tile<T, D, BN, NW>(nb + TILE, vp + (long long)jn * a.v.ss, a.v.ss, sk - jn, wave, lane);
+      }
+      const T* Ks = smem + stg * 2 * TILE;
+      const int cls = wave_live ? classify(w, iw0, 32, j0, BN, sk) : kEmpty;
+      if (cls == kFull)
+        fwd16_tile<M, D, NW, BN>(Ks, Ks + TILE, qf.f, acc, m, l, c, false, w, j0, qi, sk, r, g, lane);
+      else if (cls == kPartial)
+        fwd16_tile<M, D, NW, BN>(Ks, Ks + TILE, qf.f, acc, m, l, c, true, w, j0, qi, sk, r, g, lane);
+      __syncthreads();
+    }
+  }
+
+  if (wave_live) {
+    const float lt = halves_sum(l);
+    if (qi < sq) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      T* orow = op + (long long)qi * a.o.ss;
+#pragma unroll
+      for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * dt + 8 * q4 + 4 * g;
+          if (d < D)
+            store4<T>(orow + d, acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
+                      acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+        }
+      if (g == 0) lp[qi] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+    }
+  }
+}
+
+// Workgroup shapes: the fp32 kernel (tiles twice as large in LDS and
+// registers) runs 4 waves; the 16-bit kernel 8 waves (two per SIMD) over
+// 64-key tiles.
 template <typename M>
 struct FwdShape {
-  static constexpr int NW = sizeof(typename M::elem) == 4 ? 4 : 8;
+  static constexpr bool k16 = sizeof(typename M::elem) == 2;
+  static constexpr int NW = k16 ? 8 : 4;
   static constexpr int BN = 64;
 };
 
@@ -245,8 +419,12 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
   FwdArgs args = a;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, NW, BN>), dim3((unsigned)nblk),
-                         dim3(NW * 64), kargs, 0, stream);
+  const void* fn;
+  if constexpr (FwdShape<M>::k16)
+    fn = reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, NW, BN>);
+  else
+    fn = reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, NW, BN>);
+  return hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NW * 64), kargs, 0, stream);
 }
 
 template <typename M>
