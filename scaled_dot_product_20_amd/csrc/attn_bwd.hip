@@ -403,13 +403,345 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------- 16-bit dK / dV kernel
+//
+// bf16 / fp16.  One workgroup = 32*NW keys of one (sequence, head); each
+// wave keeps its 32 keys' K and V rows in registers (B operands).  Query
+// tiles of BMQ rows of Q and dO are copied HBM -> LDS with direct loads into
+// swizzled row-major tiles, two stages deep, with the tile's LSE (as log2)
+// and Delta beside them; query rows past the sequence get LSE = +inf, so
+// their P is exactly 0.  Per 32-query slice:
+//   S = Q K^T and dP = dO V^T from 128-bit row reads of the Q and dO tiles;
+//   P = 2^(S scale log2(e) - LSE log2(e)), dS = P o (dP - Delta);
+//   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T taken by
+//   transposing reads of the same tiles.
+template <typename M, int D, int BMQ, bool MASKED>
+__device__ __forceinline__ void dkdv16_tile(const typename M::elem* Qs, const typename M::elem* dOs,
+                                            const float* lse2s, const float* dels, const typename M::frag* kf,
+                                            const typename M::frag* vf, f32x16* dk, f32x16* dv, float sl2,
+                                            Window w, int i0, int kj, int r, int g, int lane) {
+  constexpr int MQ = BMQ / 32, NS = D / 16, DVT = (D + 31) / 32;
+#pragma unroll
+  for (int mq = 0; mq < MQ; ++mq) {
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      s = M::mma(row_frag<M, D>(Qs, 32 * mq, st, r, g), kf[st], s);
+      dp = M::mma(row_frag<M, D>(dOs, 32 * mq, st, r, g), vf[st], dp);
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int il = 32 * mq + 8 * q4 + 4 * g;  // rows il .. il+3 of the tile
+      const float4 ll = *reinterpret_cast<const float4*>(lse2s + il);
+      const float4 dd = *reinterpret_cast<const float4*>(dels + il);
+      const float lv[4] = {ll.x, ll.y, ll.z, ll.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = 4 * q4 + u;
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -lv[u]));
+        if (MASKED) {
+          const int diff = kj - (i0 + il + u);
+          if (!(diff >= w.lo && diff <= w.hi)) pe = 0.f;
+        }
+        p[e] = pe;
+        ds[e] = pe * (dp[e] - dv4[u]);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      typename M::frag pf, dsf;
+      M::pack(&p[8 * st], pf);
+      M::pack(&ds[8 * st], dsf);
+      const int ra = 32 * mq + 16 * st;
+#pragma unroll
+      for (int dt = 0; dt < DVT; ++dt) {
+        dv[dt] = M::mma(tr_frag<M, D>(dOs, ra, ra + 8, dt, lane), pf, dv[dt]);
+        dk[dt] = M::mma(tr_frag<M, D>(Qs, ra, ra + 8, dt, lane), dsf, dk[dt]);
+      }
+    }
+  }
+}
+
+template <typename M, int D, int NW, int BMQ>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv16_kernel(BwdArgs a) {
+  using T = typename M::elem;
+  using L = Swz<D>;
+  constexpr int NT = NW * 64, BNK = NW * 32, DVT = (D + 31) / 32;
+  constexpr int TILE = BMQ * L::PITCH;
+  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];  // [stage][Q, dO]
+  __shared__ __attribute__((aligned(16))) float stats[2][2][BMQ];  // [stage][lse2, delta][row]
+
+  const ProblemArgs& P = a.p;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int nkb = (int)(gridDim.x / (P.B * P.H));
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = blk / nkb, h = bh % P.H, b = bh / P.H;
+  const int kb = blk % nkb;
+
+  long long q0 = 0, k0 = 0;
+  int sq = P.Sq, sk = P.Sk;
+  if (P.varlen) {
+    q0 = P.cu_q[b];
+    sq = P.cu_q[b + 1] - (int)q0;
+    k0 = P.cu_k[b];
+    sk = P.cu_k[b + 1] - (int)k0;
+  }
+  const int j0 = kb * BNK;
+  if (j0 >= sk) return;
+  const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
+
+  const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
+  const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
+  const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
+  const T* dop = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + q0 * a.dout.ss;
+  T* dkp = (T*)a.dk.ptr + b * a.dk.sb + h * a.dk.sh + k0 * a.dk.ss;
+  T* dvp = (T*)a.dv.ptr + b * a.dv.sb + h * a.dv.sh + k0 * a.dv.ss;
+  const float* lsep = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
+
+  const int jlast = min(j0 + BNK, sk) - 1;
+  const long long ilo = max(0LL, (long long)j0 - w.hi);
+  const long long ihi = min((long long)sq - 1, (long long)jlast - w.lo);
+  const bool block_empty = w.lo > w.hi || ilo > ihi;
+
+  const int jw0 = j0 + 32 * wave;
+  const bool wave_live = jw0 < sk;
+  const int kj = jw0 + r;
+
+  RowFrags<M, D> kf, vf;
+  kf.load(kp + (long long)kj * a.k.ss, wave_live && kj < sk, g);
+  vf.load(vp + (long long)kj * a.v.ss, wave_live && kj < sk, g);
+
+  f32x16 dk[DVT], dv[DVT];
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) {
+    dk[dt] = zero16();
+    dv[dt] = zero16();
+  }
+
+  if (!block_empty) {
+    zero_unused_slots<T, D, 4 * BMQ, NT>(smem, tid);
+    const int t0 = (int)(ilo / BMQ), t1 = (int)(ihi / BMQ);
+    auto issue = [&](int stg, int i0) {
+      T* base = smem + stg * 2 * TILE;
+      dma_tile<T, D, BMQ, NW>(base, qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
+      dma_tile<T, D, BMQ, NW>(base + TILE, dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, wave, lane);
+    };
+    float st_l = INFINITY, st_d = 0.f;
+    auto load_stats = [&](int i0) {
+      if (tid < BMQ) {
+        const bool ok = i0 + tid < sq;
+        st_l = ok ? lsep[i0 + tid] * kLog2e : INFINITY;
+        st_d = ok ? delp[i0 + tid] : 0.f;
+      }
+    };
+    auto store_stats = [&](int stg) {
+      if (tid < BMQ) {
+        stats[stg][0][tid] = st_l;
+        stats[stg][1][tid] = st_d;
+      }
+    };
+    issue(0, t0 * BMQ);
+    load_stats(t0 * BMQ);
+    store_stats(0);
+    __syncthreads();
+    const float sl2 = P.scale_log2;
+    for (int t = t0; t <= t1; ++t) {
+      const int stg = (t - t0) & 1;
+      const int i0 = t * BMQ;
+      if (t < t1) {
+        issue(stg ^ 1, i0 + BMQ);
+        load_stats(i0 + BMQ);
+      }
+      const T* Qs = smem + stg * 2 * TILE;
+      const int cls = wave_live ? classify(w, i0, BMQ, jw0, 32, sk) : kEmpty;
+      if (cls == kFull)
+        dkdv16_tile<M, D, BMQ, false>(Qs, Qs + TILE, stats[stg][0], stats[stg][1], kf.f, vf.f, dk, dv, sl2, w,
+                                      i0, kj, r, g, lane);
+      else if (cls == kPartial)
+        dkdv16_tile<M, D, BMQ, true>(Qs, Qs + TILE, stats[stg][0], stats[stg][1], kf.f, vf.f, dk, dv, sl2, w,
+                                     i0, kj, r, g, lane);
+      if (t < t1) store_stats(stg ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (wave_live && kj < sk) {
+    T* dkrow = dkp + (long long)kj * a.dk.ss;
+    T* dvrow = dvp + (long long)kj * a.dv.ss;
+    const float sc = P.scale;
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * dt + 8 * q4 + 4 * g;
+        if (d < D) {
+          store4b<T>(dkrow + d, dk[dt][4 * q4] * sc, dk[dt][4 * q4 + 1] * sc,
+                     dk[dt][4 * q4 + 2] * sc, dk[dt][4 * q4 + 3] * sc);
+          store4b<T>(dvrow + d, dv[dt][4 * q4], dv[dt][4 * q4 + 1], dv[dt][4 * q4 + 2],
+                     dv[dt][4 * q4 + 3]);
+        }
+      }
+  }
+}
+
+// ------------------------------------------------- 16-bit dQ kernel
+//
+// One workgroup = 32*NW queries; each wave keeps its 32 queries' Q and dO
+// rows, LSE and Delta in registers and walks the key tiles its window can
+// see, K and V copied HBM -> LDS as in the forward.  Per 32-key slice:
+// S^T = K Q^T and dP^T = V dO^T from row reads, dS^T = P^T o (dP^T - Delta),
+// dQ^T += K^T dS^T with K^T taken by transposing reads.  Key rows past the
+// sequence are copies of its last key and are masked out.
+template <typename M, int D, int BN, bool MASKED>
+__device__ __forceinline__ void dq16_tile(const typename M::elem* Ks, const typename M::elem* Vs,
+                                          const typename M::frag* qf, const typename M::frag* dof, f32x16* dq,
+                                          float sl2, float lse2, float delta, Window w, int j0, int qi, int sk,
+                                          int r, int g, int lane) {
+  constexpr int KT = BN / 32, NS = D / 16, DVT = (D + 31) / 32;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      s = M::mma(row_frag<M, D>(Ks, 32 * kt, st, r, g), qf[st], s);
+      dp = M::mma(row_frag<M, D>(Vs, 32 * kt, st, r, g), dof[st], dp);
+    }
+    float ds[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -lse2));
+      if (MASKED) {
+        const int j = j0 + 32 * kt + acc_row(e, g);
+        const int diff = j - qi;
+        if (!(diff >= w.lo && diff <= w.hi && j < sk)) pe = 0.f;
+      }
+      ds[e] = pe * (dp[e] - delta);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      typename M::frag dsf;
+      M::pack(&ds[8 * st], dsf);
+      const int ra = 32 * kt + 16 * st;
+#pragma unroll
+      for (int dt = 0; dt < DVT; ++dt) dq[dt] = M::mma(tr_frag<M, D>(Ks, ra, ra + 8, dt, lane), dsf, dq[dt]);
+    }
+  }
+}
+
+template <typename M, int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq16_kernel(BwdArgs a) {
+  using T = typename M::elem;
+  using L = Swz<D>;
+  constexpr int NT = NW * 64, BM = NW * 32, DVT = (D + 31) / 32;
+  constexpr int TILE = BN * L::PITCH;
+  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];  // [stage][K, V]
+
+  const ProblemArgs& P = a.p;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int nq = (int)(gridDim.x / (P.B * P.H));
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - (blk % nq);
+
+  long long q0 = 0, k0 = 0;
+  int sq = P.Sq, sk = P.Sk;
+  if (P.varlen) {
+    q0 = P.cu_q[b];
+    sq = P.cu_q[b + 1] - (int)q0;
+    k0 = P.cu_k[b];
+    sk = P.cu_k[b + 1] - (int)k0;
+  }
+  const int i0 = qb * BM;
+  if (i0 >= sq) return;
+  const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
+
+  const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
+  const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
+  const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
+  const T* dop = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + q0 * a.dout.ss;
+  T* dqp = (T*)a.dq.ptr + b * a.dq.sb + h * a.dq.sh + q0 * a.dq.ss;
+  const float* lsep = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
+
+  const int ilast = min(i0 + BM, sq) - 1;
+  const long long jlo = max(0LL, (long long)i0 + w.lo);
+  const long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
+  const bool block_empty = w.lo > w.hi || jlo > jhi;
+
+  const int iw0 = i0 + 32 * wave;
+  const bool wave_live = iw0 < sq;
+  const int qi = iw0 + r;
+  const bool row_ok = wave_live && qi < sq;
+
+  RowFrags<M, D> qf, dof;
+  qf.load(qp + (long long)qi * a.q.ss, row_ok, g);
+  dof.load(dop + (long long)qi * a.dout.ss, row_ok, g);
+  const float lse2 = row_ok ? lsep[qi] * kLog2e : INFINITY;
+  const float delta = row_ok ? delp[qi] : 0.f;
+
+  f32x16 dq[DVT];
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) dq[dt] = zero16();
+
+  if (!block_empty) {
+    zero_unused_slots<T, D, 4 * BN, NT>(smem, tid);
+    const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
+    auto issue = [&](int stg, int j0) {
+      T* base = smem + stg * 2 * TILE;
+      dma_tile<T, D, BN, NW>(base, kp + (long long)j0 * a.k.ss, a.k.ss, sk - j0, wave, lane);
+      dma_tile<T, D, BN, NW>(base + TILE, vp + (long long)j0 * a.v.ss, a.v.ss, sk - j0, wave, lane);
+    };
+    issue(0, t0 * BN);
+    __syncthreads();
+    const float sl2 = P.scale_log2;
+    for (int t = t0; t <= t1; ++t) {
+      const int stg = (t - t0) & 1;
+      const int j0 = t * BN;
+      if (t < t1) issue(stg ^ 1, j0 + BN);
+      const T* Ks = smem + stg * 2 * TILE;
+      const int cls = wave_live ? classify(w, iw0, 32, j0, BN, sk) : kEmpty;
+      if (cls == kFull)
+        dq16_tile<M, D, BN, false>(Ks, Ks + TILE, qf.f, dof.f, dq, sl2, lse2, delta, w, j0, qi, sk, r, g, lane);
+      else if (cls == kPartial)
+        dq16_tile<M, D, BN, true>(Ks, Ks + TILE, qf.f, dof.f, dq, sl2, lse2, delta, w, j0, qi, sk, r, g, lane);
+      __syncthreads();
+    }
+  }
+
+  if (row_ok) {
+    T* dqrow = dqp + (long long)qi * a.dq.ss;
+    const float sc = P.scale;
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * dt + 8 * q4 + 4 * g;
+        if (d < D)
+          store4b<T>(dqrow + d, dq[dt][4 * q4] * sc, dq[dt][4 * q4 + 1] * sc,
+                     dq[dt][4 * q4 + 2] * sc, dq[dt][4 * q4 + 3] * sc);
+      }
+  }
+}
+
 // ------------------------------------------------------------ launch
+
+// Workgroup shapes.  16-bit: dK/dV 4 waves (128 keys) over 64-row query
+// tiles, dQ 8 waves (256 queries) over 64-key tiles.  fp32 (register-staged
+// kernels): 4 waves each, dQ key tiles of 32 to fit LDS.
+template <typename M>
+struct BwdShape {
+  static constexpr bool k16 = sizeof(typename M::elem) == 2;
+  static constexpr int NW_KV = 4, BMQ = k16 ? 64 : 32;
+  static constexpr int NW_Q = k16 ? 8 : 4, BN = k16 ? 64 : 32;
+};
 
 template <typename M, int D>
 static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   using T = typename M::elem;
-  // fp32 tiles are halved along the key axis of the dQ kernel to fit LDS.
-  constexpr int NW_KV = 4, BMQ = 32, NW_Q = 4, BN = sizeof(T) == 4 ? 32 : 64;
+  using S = BwdShape<M>;
+  constexpr int NW_KV = S::NW_KV, BMQ = S::BMQ, NW_Q = S::NW_Q, BN = S::BN;
   BwdArgs args = a;
   void* kargs[] = {&args};
   hipError_t err;
@@ -435,8 +767,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
     const long long nblk = nkb * a.p.H * a.p.B;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (nblk > 0) {
-      err = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>),
-                            dim3((unsigned)nblk), dim3(NW_KV * 64), kargs, 0, stream);
+      const void* fn;
+      if constexpr (S::k16)
+        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ>);
+      else
+        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>);
+      err = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NW_KV * 64), kargs, 0, stream);
       if (err != hipSuccess) return err;
     }
   }
@@ -446,8 +782,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
     const long long nblk = nq * a.p.H * a.p.B;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (nblk > 0) {
-      err = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN>),
-                            dim3((unsigned)nblk), dim3(NW_Q * 64), kargs, 0, stream);
+      const void* fn;
+      if constexpr (S::k16)
+        fn = reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN>);
+      else
+        fn = reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN>);
+      err = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NW_Q * 64), kargs, 0, stream);
       if (err != hipSuccess) return err;
     }
   }
