@@ -9,6 +9,8 @@
 //   dQ = scale dS K                   (per query block, kernel 3)
 // No atomics: every output element is summed by one lane in a fixed order,
 // so results are run-to-run identical.
+#include <type_traits>
+
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
 
@@ -97,7 +99,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float stats[2][2][BMQ];  // [buf][lse2, delta][row]
 
   const ProblemArgs& P = a.p;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nkb = (int)(gridDim.x / (P.B * P.H));
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / nkb, h = bh % P.H, b = bh / P.H;
@@ -271,7 +274,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T smem[2 * STAGE];
 
   const ProblemArgs& P = a.p;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = (int)(gridDim.x / (P.B * P.H));
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
@@ -412,68 +416,84 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 // and Delta beside them; query rows past the sequence get LSE = +inf, so
 // their P is exactly 0.  Per 32-query slice:
 //   S = Q K^T and dP = dO V^T from 128-bit row reads of the Q and dO tiles;
-//   P = 2^(S scale log2(e) - LSE log2(e)), dS = P o (dP - Delta);
+//   P = 2^(c S - LSE log2(e)) with c = |scale| log2(e) (a negative scale is
+//   moved into the K operand), dS = P o (dP - Delta);
 //   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T taken by
 //   transposing reads of the same tiles.
-template <typename M, int D, int BMQ, bool MASKED>
-__device__ __forceinline__ void dkdv16_tile(const typename M::elem* Qs, const typename M::elem* dOs,
-                                            const float* lse2s, const float* dels, const typename M::frag* kf,
-                                            const typename M::frag* vf, f32x16* dk, f32x16* dv, float sl2,
-                                            Window w, int i0, int kj, int r, int g, int lane) {
-  constexpr int MQ = BMQ / 32, NS = D / 16, DVT = (D + 31) / 32;
+// Each wave visits only the query tiles that can see its keys; tiles cut
+// by the window have their scores set to -inf where masked.
+template <typename M, int D, int BMQ>
+struct Dkdv16 {
+  using T = typename M::elem;
+  using L = Swz<D>;
+  using frag = typename M::frag;
+  static constexpr int MQ = BMQ / 32, NS = D / 16, DVT = (D + 31) / 32;
+  static constexpr int TILE = BMQ * L::PITCH;
+  // LDS, in elements: Q stage 0, Q stage 1, dO stage 0, dO stage 1.
+  static constexpr int qOff(int stage) { return stage * TILE; }
+  static constexpr int dOff(int stage) { return (2 + stage) * TILE; }
+
+  template <int QOFF, int DOFF>
+  static __device__ __forceinline__ void tile(const T* smem, const LdsOffsets<M, D>& lo, const float* lse2s,
+                                              const float* dels, const RowFrags<M, D>& kf,
+                                              const RowFrags<M, D>& vf, f32x16* dk, f32x16* dv, float c,
+                                              bool masked, Window w, int i0, int kj, int g) {
 #pragma unroll
-  for (int mq = 0; mq < MQ; ++mq) {
-    f32x16 s = zero16(), dp = zero16();
+    for (int mq = 0; mq < MQ; ++mq) {
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      s = M::mma(row_frag<M, D>(Qs, 32 * mq, st, r, g), kf[st], s);
-      dp = M::mma(row_frag<M, D>(dOs, 32 * mq, st, r, g), vf[st], dp);
-    }
-    float p[16], ds[16];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int il = 32 * mq + 8 * q4 + 4 * g;  // rows il .. il+3 of the tile
-      const float4 ll = *reinterpret_cast<const float4*>(lse2s + il);
-      const float4 dd = *reinterpret_cast<const float4*>(dels + il);
-      const float lv[4] = {ll.x, ll.y, ll.z, ll.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = 4 * q4 + u;
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -lv[u]));
-        if (MASKED) {
-          const int diff = kj - (i0 + il + u);
-          if (!(diff >= w.lo && diff <= w.hi)) pe = 0.f;
-        }
-        p[e] = pe;
-        ds[e] = pe * (dp[e] - dv4[u]);
+      for (int st = 0; st < NS; ++st) {
+        s = M::mma(ld_row<M>(smem + QOFF + 32 * mq * L::PITCH, lo.row[st]), kf.f[st], s);
+        dp = M::mma(ld_row<M>(smem + DOFF + 32 * mq * L::PITCH, lo.row[st]), vf.f[st], dp);
       }
-    }
+      if (masked) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      typename M::frag pf, dsf;
-      M::pack(&p[8 * st], pf);
-      M::pack(&ds[8 * st], dsf);
-      const int ra = 32 * mq + 16 * st;
+        for (int e = 0; e < 16; ++e) {
+          const int diff = kj - (i0 + 32 * mq + acc_row(e, g));
+          if (!(diff >= w.lo && diff <= w.hi)) s[e] = -INFINITY;
+        }
+      }
+      float p[16], ds[16];
 #pragma unroll
-      for (int dt = 0; dt < DVT; ++dt) {
-        dv[dt] = M::mma(tr_frag<M, D>(dOs, ra, ra + 8, dt, lane), pf, dv[dt]);
-        dk[dt] = M::mma(tr_frag<M, D>(Qs, ra, ra + 8, dt, lane), dsf, dk[dt]);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int il = 32 * mq + 8 * q4 + 4 * g;  // rows il .. il+3 of the tile
+        const float4 ll = *reinterpret_cast<const float4*>(lse2s + il);
+        const float4 dd = *reinterpret_cast<const float4*>(dels + il);
+        const float lv[4] = {ll.x, ll.y, ll.z, ll.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = 4 * q4 + u;
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
+          ds[e] = p[e] * (dp[e] - dv4[u]);
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        frag pf, dsf;
+        M::pack(&p[8 * st], pf);
+        M::pack(&ds[8 * st], dsf);
+        const int rbase = (32 * mq + 16 * st) * L::PITCH;
+#pragma unroll
+        for (int dt = 0; dt < DVT; ++dt) {
+          dv[dt] = M::mma(ld_tr<M>(smem + DOFF + rbase, lo.tra[dt], lo.trb[dt]), pf, dv[dt]);
+          dk[dt] = M::mma(ld_tr<M>(smem + QOFF + rbase, lo.tra[dt], lo.trb[dt]), dsf, dk[dt]);
+        }
       }
     }
   }
-}
+};
 
-template <typename M, int D, int NW, int BMQ>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv16_kernel(BwdArgs a) {
+template <typename M, int D, int NW, int BMQ, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dkdv16_kernel(BwdArgs a) {
+  using F = Dkdv16<M, D, BMQ>;
   using T = typename M::elem;
-  using L = Swz<D>;
-  constexpr int NT = NW * 64, BNK = NW * 32, DVT = (D + 31) / 32;
-  constexpr int TILE = BMQ * L::PITCH;
-  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];  // [stage][Q, dO]
+  constexpr int NT = NW * 64, BNK = NW * 32, DVT = F::DVT;
+  __shared__ __attribute__((aligned(1024))) T smem[4 * F::TILE];
   __shared__ __attribute__((aligned(16))) float stats[2][2][BMQ];  // [stage][lse2, delta][row]
 
   const ProblemArgs& P = a.p;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nkb = (int)(gridDim.x / (P.B * P.H));
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / nkb, h = bh % P.H, b = bh / P.H;
@@ -500,6 +520,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv16_kernel(BwdArgs a) {
   const float* lsep = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
   const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
 
+  // Queries that can see the block's keys, and the tiles of this wave's keys.
   const int jlast = min(j0 + BNK, sk) - 1;
   const long long ilo = max(0LL, (long long)j0 - w.hi);
   const long long ihi = min((long long)sq - 1, (long long)jlast - w.lo);
@@ -508,10 +529,21 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv16_kernel(BwdArgs a) {
   const int jw0 = j0 + 32 * wave;
   const bool wave_live = jw0 < sk;
   const int kj = jw0 + r;
+  int tw0 = 0x7fffffff, tw1 = -1;
+  if (wave_live && w.lo <= w.hi) {
+    const long long a0 = max(0LL, (long long)jw0 - w.hi);
+    const long long a1 = min((long long)sq - 1, (long long)min(jw0 + 31, sk - 1) - w.lo);
+    if (a0 <= a1) {
+      tw0 = (int)(a0 / BMQ);
+      tw1 = (int)(a1 / BMQ);
+    }
+  }
 
   RowFrags<M, D> kf, vf;
   kf.load(kp + (long long)kj * a.k.ss, wave_live && kj < sk, g);
   vf.load(vp + (long long)kj * a.v.ss, wave_live && kj < sk, g);
+  const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
+  if (P.scale_log2 < 0.f) kf.negate();
 
   f32x16 dk[DVT], dv[DVT];
 #pragma unroll
@@ -521,49 +553,55 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv16_kernel(BwdArgs a) {
   }
 
   if (!block_empty) {
+    LdsOffsets<M, D> lo;
+    lo.init(lane);
+    DmaLane<T, D, BMQ, NW> qd, dd;
+    qd.init(a.q.ss, wave, lane);
+    dd.init(a.dout.ss, wave, lane);
     zero_unused_slots<T, D, 4 * BMQ, NT>(smem, tid);
     const int t0 = (int)(ilo / BMQ), t1 = (int)(ihi / BMQ);
-    auto issue = [&](int stg, int i0) {
-      T* base = smem + stg * 2 * TILE;
-      dma_tile<T, D, BMQ, NW>(base, qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
-      dma_tile<T, D, BMQ, NW>(base + TILE, dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, wave, lane);
+    auto dma = [&](int stage, int t) {
+      const int i0 = t * BMQ;
+      qd.issue(smem + F::qOff(stage), qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
+      dd.issue(smem + F::dOff(stage), dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, wave, lane);
     };
-    float st_l = INFINITY, st_d = 0.f;
-    auto load_stats = [&](int i0) {
+    float st_l = INFINITY, st_d = 0.f;  // this thread's LSE / Delta entry (tid < BMQ)
+    auto load_stats = [&](int t) {
       if (tid < BMQ) {
-        const bool ok = i0 + tid < sq;
-        st_l = ok ? lsep[i0 + tid] * kLog2e : INFINITY;
-        st_d = ok ? delp[i0 + tid] : 0.f;
+        const int i = t * BMQ + tid;
+        st_l = i < sq ? lsep[i] * kLog2e : INFINITY;
+        st_d = i < sq ? delp[i] : 0.f;
       }
     };
-    auto store_stats = [&](int stg) {
+    auto store_stats = [&](int stage) {
       if (tid < BMQ) {
-        stats[stg][0][tid] = st_l;
-        stats[stg][1][tid] = st_d;
+        stats[stage][0][tid] = st_l;
+        stats[stage][1][tid] = st_d;
       }
     };
-    issue(0, t0 * BMQ);
-    load_stats(t0 * BMQ);
+    dma(0, t0);
+    load_stats(t0);
     store_stats(0);
     __syncthreads();
-    const float sl2 = P.scale_log2;
-    for (int t = t0; t <= t1; ++t) {
-      const int stg = (t - t0) & 1;
-      const int i0 = t * BMQ;
-      if (t < t1) {
-        issue(stg ^ 1, i0 + BMQ);
-        load_stats(i0 + BMQ);
+    // Step t: the tiles of query tile t sit in stage P = (t - t0) & 1; the
+    // copies of tile t+1 into stage P^1 fly during the step.
+    auto step = [&](auto parity, int t) {
+      constexpr int Pq = decltype(parity)::value;
+      if (t + 1 <= t1) {
+        dma(Pq ^ 1, t + 1);
+        load_stats(t + 1);
       }
-      const T* Qs = smem + stg * 2 * TILE;
-      const int cls = wave_live ? classify(w, i0, BMQ, jw0, 32, sk) : kEmpty;
-      if (cls == kFull)
-        dkdv16_tile<M, D, BMQ, false>(Qs, Qs + TILE, stats[stg][0], stats[stg][1], kf.f, vf.f, dk, dv, sl2, w,
-                                      i0, kj, r, g, lane);
-      else if (cls == kPartial)
-        dkdv16_tile<M, D, BMQ, true>(Qs, Qs + TILE, stats[stg][0], stats[stg][1], kf.f, vf.f, dk, dv, sl2, w,
-                                     i0, kj, r, g, lane);
-      if (t < t1) store_stats(stg ^ 1);
+      if (tw0 <= t && t <= tw1) {
+        const bool masked = classify(w, (long long)t * BMQ, BMQ, jw0, 32, sk) == kPartial;
+        F::template tile<F::qOff(Pq), F::dOff(Pq)>(smem, lo, stats[Pq][0], stats[Pq][1], kf, vf, dk, dv, c,
+                                                  masked, w, t * BMQ, kj, g);
+      }
+      if (t + 1 <= t1) store_stats(Pq ^ 1);
       __syncthreads();
+    };
+    for (int t = t0; t <= t1; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 <= t1) step(std::integral_constant<int, 1>{}, t + 1);
     }
   }
 
@@ -589,57 +627,70 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv16_kernel(BwdArgs a) {
 // ------------------------------------------------- 16-bit dQ kernel
 //
 // One workgroup = 32*NW queries; each wave keeps its 32 queries' Q and dO
-// rows, LSE and Delta in registers and walks the key tiles its window can
+// rows, LSE and Delta in registers and walks the key tiles its rows can
 // see, K and V copied HBM -> LDS as in the forward.  Per 32-key slice:
 // S^T = K Q^T and dP^T = V dO^T from row reads, dS^T = P^T o (dP^T - Delta),
 // dQ^T += K^T dS^T with K^T taken by transposing reads.  Key rows past the
 // sequence are copies of its last key and are masked out.
-template <typename M, int D, int BN, bool MASKED>
-__device__ __forceinline__ void dq16_tile(const typename M::elem* Ks, const typename M::elem* Vs,
-                                          const typename M::frag* qf, const typename M::frag* dof, f32x16* dq,
-                                          float sl2, float lse2, float delta, Window w, int j0, int qi, int sk,
-                                          int r, int g, int lane) {
-  constexpr int KT = BN / 32, NS = D / 16, DVT = (D + 31) / 32;
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      s = M::mma(row_frag<M, D>(Ks, 32 * kt, st, r, g), qf[st], s);
-      dp = M::mma(row_frag<M, D>(Vs, 32 * kt, st, r, g), dof[st], dp);
-    }
-    float ds[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -lse2));
-      if (MASKED) {
-        const int j = j0 + 32 * kt + acc_row(e, g);
-        const int diff = j - qi;
-        if (!(diff >= w.lo && diff <= w.hi && j < sk)) pe = 0.f;
-      }
-      ds[e] = pe * (dp[e] - delta);
-    }
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      typename M::frag dsf;
-      M::pack(&ds[8 * st], dsf);
-      const int ra = 32 * kt + 16 * st;
-#pragma unroll
-      for (int dt = 0; dt < DVT; ++dt) dq[dt] = M::mma(tr_frag<M, D>(Ks, ra, ra + 8, dt, lane), dsf, dq[dt]);
-    }
-  }
-}
-
-template <typename M, int D, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dq16_kernel(BwdArgs a) {
+template <typename M, int D, int BN>
+struct Dq16 {
   using T = typename M::elem;
   using L = Swz<D>;
-  constexpr int NT = NW * 64, BM = NW * 32, DVT = (D + 31) / 32;
-  constexpr int TILE = BN * L::PITCH;
-  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];  // [stage][K, V]
+  using frag = typename M::frag;
+  static constexpr int KT = BN / 32, NS = D / 16, DVT = (D + 31) / 32;
+  static constexpr int TILE = BN * L::PITCH;
+  // LDS, in elements: K stage 0, K stage 1, V stage 0, V stage 1.
+  static constexpr int kOff(int stage) { return stage * TILE; }
+  static constexpr int vOff(int stage) { return (2 + stage) * TILE; }
+
+  template <int KOFF, int VOFF>
+  static __device__ __forceinline__ void tile(const T* smem, const LdsOffsets<M, D>& lo,
+                                              const RowFrags<M, D>& qf, const RowFrags<M, D>& dof, f32x16* dq,
+                                              float c, float lse2, float delta, bool masked, Window w, int j0,
+                                              int qi, int sk, int g) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s = M::mma(ld_row<M>(smem + KOFF + 32 * kt * L::PITCH, lo.row[st]), qf.f[st], s);
+        dp = M::mma(ld_row<M>(smem + VOFF + 32 * kt * L::PITCH, lo.row[st]), dof.f[st], dp);
+      }
+      if (masked) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = j0 + 32 * kt + acc_row(e, g);
+          const int diff = j - qi;
+          if (!(diff >= w.lo && diff <= w.hi && j < sk)) s[e] = -INFINITY;
+        }
+      }
+      float ds[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lse2)) * (dp[e] - delta);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        frag dsf;
+        M::pack(&ds[8 * st], dsf);
+        const int rbase = (32 * kt + 16 * st) * L::PITCH;
+#pragma unroll
+        for (int dt = 0; dt < DVT; ++dt)
+          dq[dt] = M::mma(ld_tr<M>(smem + KOFF + rbase, lo.tra[dt], lo.trb[dt]), dsf, dq[dt]);
+      }
+    }
+  }
+};
+
+template <typename M, int D, int NW, int BN, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dq16_kernel(BwdArgs a) {
+  using F = Dq16<M, D, BN>;
+  using T = typename M::elem;
+  constexpr int NT = NW * 64, BM = NW * 32, DVT = F::DVT;
+  __shared__ __attribute__((aligned(1024))) T smem[4 * F::TILE];
 
   const ProblemArgs& P = a.p;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = (int)(gridDim.x / (P.B * P.H));
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
@@ -674,39 +725,55 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq16_kernel(BwdArgs a) {
   const bool wave_live = iw0 < sq;
   const int qi = iw0 + r;
   const bool row_ok = wave_live && qi < sq;
+  int tw0 = 0x7fffffff, tw1 = -1;
+  if (wave_live && w.lo <= w.hi) {
+    const long long a0 = max(0LL, (long long)iw0 + w.lo);
+    const long long a1 = min((long long)sk - 1, (long long)min(iw0 + 31, sq - 1) + w.hi);
+    if (a0 <= a1) {
+      tw0 = (int)(a0 / BN);
+      tw1 = (int)(a1 / BN);
+    }
+  }
 
   RowFrags<M, D> qf, dof;
   qf.load(qp + (long long)qi * a.q.ss, row_ok, g);
   dof.load(dop + (long long)qi * a.dout.ss, row_ok, g);
   const float lse2 = row_ok ? lsep[qi] * kLog2e : INFINITY;
   const float delta = row_ok ? delp[qi] : 0.f;
+  const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
+  if (P.scale_log2 < 0.f) qf.negate();
 
   f32x16 dq[DVT];
 #pragma unroll
   for (int dt = 0; dt < DVT; ++dt) dq[dt] = zero16();
 
   if (!block_empty) {
+    LdsOffsets<M, D> lo;
+    lo.init(lane);
+    DmaLane<T, D, BN, NW> kd, vd;
+    kd.init(a.k.ss, wave, lane);
+    vd.init(a.v.ss, wave, lane);
     zero_unused_slots<T, D, 4 * BN, NT>(smem, tid);
     const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
-    auto issue = [&](int stg, int j0) {
-      T* base = smem + stg * 2 * TILE;
-      dma_tile<T, D, BN, NW>(base, kp + (long long)j0 * a.k.ss, a.k.ss, sk - j0, wave, lane);
-      dma_tile<T, D, BN, NW>(base + TILE, vp + (long long)j0 * a.v.ss, a.v.ss, sk - j0, wave, lane);
+    auto dma = [&](int stage, int t) {
+      kd.issue(smem + F::kOff(stage), kp + (long long)t * BN * a.k.ss, a.k.ss, sk - t * BN, wave, lane);
+      vd.issue(smem + F::vOff(stage), vp + (long long)t * BN * a.v.ss, a.v.ss, sk - t * BN, wave, lane);
     };
-    issue(0, t0 * BN);
+    dma(0, t0);
     __syncthreads();
-    const float sl2 = P.scale_log2;
-    for (int t = t0; t <= t1; ++t) {
-      const int stg = (t - t0) & 1;
-      const int j0 = t * BN;
-      if (t < t1) issue(stg ^ 1, j0 + BN);
-      const T* Ks = smem + stg * 2 * TILE;
-      const int cls = wave_live ? classify(w, iw0, 32, j0, BN, sk) : kEmpty;
-      if (cls == kFull)
-        dq16_tile<M, D, BN, false>(Ks, Ks + TILE, qf.f, dof.f, dq, sl2, lse2, delta, w, j0, qi, sk, r, g, lane);
-      else if (cls == kPartial)
-        dq16_tile<M, D, BN, true>(Ks, Ks + TILE, qf.f, dof.f, dq, sl2, lse2, delta, w, j0, qi, sk, r, g, lane);
+    auto step = [&](auto parity, int t) {
+      constexpr int Pq = decltype(parity)::value;
+      if (t + 1 <= t1) dma(Pq ^ 1, t + 1);
+      if (tw0 <= t && t <= tw1) {
+        const bool masked = classify(w, iw0, 32, (long long)t * BN, BN, sk) == kPartial;
+        F::template tile<F::kOff(Pq), F::vOff(Pq)>(smem, lo, qf, dof, dq, c, lse2, delta, masked, w, t * BN, qi,
+                                                  sk, g);
+      }
       __syncthreads();
+    };
+    for (int t = t0; t <= t1; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 <= t1) step(std::integral_constant<int, 1>{}, t + 1);
     }
   }
 
@@ -728,19 +795,24 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq16_kernel(BwdArgs a) {
 // ------------------------------------------------------------ launch
 
 // Workgroup shapes.  16-bit: dK/dV 4 waves (128 keys) over 64-row query
-// tiles, dQ 8 waves (256 queries) over 64-key tiles.  fp32 (register-staged
-// kernels): 4 waves each, dQ key tiles of 32 to fit LDS.
-template <typename M>
+// tiles, two waves per SIMD where the registers allow (head_dim <= 80), one
+// at head_dim 128; dQ 4 waves (128 queries) over 64-key tiles, two per SIMD.
+// fp32 (register-staged kernels): 4 waves each, dQ key tiles of 32 to fit
+// LDS.
+#ifndef BWD16_NWQ
+#define BWD16_NWQ 4
+#endif
+template <typename M, int D>
 struct BwdShape {
   static constexpr bool k16 = sizeof(typename M::elem) == 2;
-  static constexpr int NW_KV = 4, BMQ = k16 ? 64 : 32;
-  static constexpr int NW_Q = k16 ? 8 : 4, BN = k16 ? 64 : 32;
+  static constexpr int NW_KV = 4, BMQ = k16 ? 64 : 32, WPE_KV = D > 80 ? 1 : 2;
+  static constexpr int NW_Q = k16 ? BWD16_NWQ : 4, BN = k16 ? 64 : 32;
 };
 
 template <typename M, int D>
 static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   using T = typename M::elem;
-  using S = BwdShape<M>;
+  using S = BwdShape<M, D>;
   constexpr int NW_KV = S::NW_KV, BMQ = S::BMQ, NW_Q = S::NW_Q, BN = S::BN;
   BwdArgs args = a;
   void* kargs[] = {&args};
@@ -769,7 +841,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
     if (nblk > 0) {
       const void* fn;
       if constexpr (S::k16)
-        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ>);
+        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV>);
       else
         fn = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>);
       err = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NW_KV * 64), kargs, 0, stream);
@@ -784,7 +856,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
     if (nblk > 0) {
       const void* fn;
       if constexpr (S::k16)
-        fn = reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN>);
+        fn = reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, 2>);
       else
         fn = reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN>);
       err = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NW_Q * 64), kargs, 0, stream);

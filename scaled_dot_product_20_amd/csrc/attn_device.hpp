@@ -372,3 +372,88 @@ __device__ __forceinline__ typename M::frag tr_frag(const typename M::elem* lds,
 }
 
 }  // namespace sdpa
+
+namespace sdpa {
+
+// Per-lane element offsets into swizzled 16-bit tiles, computed once per
+// kernel so that every operand read in the hot loops is one LDS instruction
+// whose tile, stage and row block are folded into its immediate offset.
+//   row[st]: chunk 2*st + g of row r (row_frag of any 32-row block);
+//   tra[dt] / trb[dt]: the transposing-read addresses of tr_frag for rows
+//   4g + (s>>2) and 8 + 4g + (s>>2) of any 16-row block, column block dt.
+template <typename M, int D>
+struct LdsOffsets {
+  using L = Swz<D>;
+  static constexpr int NS = D / 16, DVT = (D + 31) / 32;
+  int row[NS], tra[DVT], trb[DVT];
+  __device__ __forceinline__ void init(int lane) {
+    const int r = lane & 31, g = lane >> 5, s = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) row[st] = L::off(r, 2 * st + g);
+    const int dr = 4 * g + (s >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt) {
+      const int col = 32 * dt + 16 * (grp & 1) + 4 * (s & 3);
+      const int c = col >> 3, half = (col >> 2) & 1;
+      tra[dt] = L::off(dr, c) + 4 * half;
+      trb[dt] = L::off(8 + dr, c) + 4 * half;
+    }
+  }
+};
+
+// A operand straight from rows: row block starting at element offset `base`
+// (a multiple of 16 rows), K step st.
+template <typename M>
+__device__ __forceinline__ typename M::frag ld_row(const typename M::elem* lds, int off) {
+  return *reinterpret_cast<const typename M::frag*>(lds + off);
+}
+
+// A operand by transposing reads (see tr_frag): `lds` points at the first
+// row of a 16-row block.
+template <typename M>
+__device__ __forceinline__ typename M::frag ld_tr(const typename M::elem* lds, int offa, int offb) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds + offa));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds + offb));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(typename M::frag, v);
+}
+
+// One lane's share of the direct loads that fill a ROWS-row swizzled tile
+// (see dma_tile), with the source offsets of full tiles precomputed.
+template <typename T, int D, int ROWS, int NW>
+struct DmaLane {
+  using L = Swz<D>;
+  static constexpr int RPI = 64 / L::SLOTS, NI = ROWS / RPI, PER = (NI + NW - 1) / NW;
+  static_assert(ROWS % RPI == 0, "tile rows");
+  long long goff[PER];  // element offset of the lane's chunk in a full tile
+  static __device__ __forceinline__ int row_of(int u, int wave, int lane) {
+    return (wave + u * NW) * RPI + lane / L::SLOTS;
+  }
+  static __device__ __forceinline__ int chunk_of(int row, int lane) { return (lane % L::SLOTS) ^ L::sigma(row); }
+  __device__ __forceinline__ void init(long long row_stride, int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int row = row_of(u, wave, lane);
+      goff[u] = (long long)row * row_stride + chunk_of(row, lane) * 8;
+    }
+  }
+  // Copies the tile whose first row is g (rows >= nvalid repeat row nvalid-1).
+  __device__ __forceinline__ void issue(T* lds, const T* __restrict__ g, long long row_stride, int nvalid,
+                                        int wave, int lane) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = wave + u * NW;
+      if (NI % NW == 0 || i < NI) {
+        const int row = row_of(u, wave, lane);
+        if (L::CH == L::SLOTS || chunk_of(row, lane) < L::CH) {
+          const T* src = nvalid >= ROWS ? g + goff[u]
+                                        : g + (long long)min(row, nvalid - 1) * row_stride + chunk_of(row, lane) * 8;
+          __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds + i * RPI * L::PITCH), 16, 0, 0);
+        }
+      }
+    }
+  }
+};
+
+}  // namespace sdpa

@@ -23,6 +23,8 @@
 //     AOTriton 0.15b notes) and O^T += V^T P^T on the matrix cores.
 // Epilogue: O = acc / l, LSE = ln(2) * (m + log2 l); rows with no visible key
 // get O = 0 and LSE = +inf.
+#include <type_traits>
+
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
 
@@ -56,7 +58,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) T smem[2 * STAGE];
 
   const ProblemArgs& P = a.p;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = (int)(gridDim.x / (P.B * P.H));
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
@@ -231,86 +234,130 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
 // ------------------------------------------------------ 16-bit kernel
 //
 // The bf16 / fp16 forward.  K and V tiles are copied HBM -> LDS with direct
-// loads into swizzled row-major tiles (two stages, the next tile's copy in
-// flight while this one is used); K feeds S^T = K Q^T with 128-bit row
-// reads and V feeds O^T += V^T P^T through transposing reads, so no tile is
-// ever rearranged by the waves.  Tiles the window leaves whole run a path
-// with no masking at all.
-template <typename M, int D, int NW, int BN>
-__device__ __forceinline__ void fwd16_tile(const typename M::elem* Ks, const typename M::elem* Vs,
-                                           const typename M::frag* qf, f32x16* acc, float& m, float& l,
-                                           float c, bool masked, Window w, int j0, int qi, int sk,
-                                           int r, int g, int lane) {
-  constexpr int KT = BN / 32, NS = D / 16, DVT = (D + 31) / 32;
-  f32x16 s[KT];
+// loads into swizzled row-major tiles, two stages deep (the next tile's copy
+// in flight while this one is used); K feeds S^T = K Q^T through 128-bit
+// row reads and V feeds O^T += V^T P^T through transposing reads, so the
+// waves never rearrange a tile.  Each wave owns RB blocks of 32 query rows:
+// every K or V operand read from LDS feeds RB products, and the RB blocks'
+// independent chains keep the matrix cores busy while the vector units work
+// on another block's probabilities.  Each wave only visits the tiles its own
+// rows can see (a contiguous range under a band window); tiles cut by the
+// window, the diagonal or the ragged end are masked after their scores are
+// computed.
+template <typename M, int D, int BN, int RB>
+struct Fwd16 {
+  using T = typename M::elem;
+  using L = Swz<D>;
+  using frag = typename M::frag;
+  static constexpr int KT = BN / 32, NS = D / 16, DVT = (D + 31) / 32;
+  static constexpr int TILE = BN * L::PITCH;
+  // LDS, in elements: K stage 0, K stage 1, V stage 0, V stage 1.
+  static constexpr int kOff(int stage) { return stage * TILE; }
+  static constexpr int vOff(int stage) { return (2 + stage) * TILE; }
+
+  // s[rb][kt] = (K Q^T) of one tile for every row block.
+  template <int KOFF>
+  static __device__ __forceinline__ void scores(const T* smem, const LdsOffsets<M, D>& lo,
+                                                const RowFrags<M, D>* qf, f32x16 (*s)[KT]) {
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    s[kt] = zero16();
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-    for (int st = 0; st < NS; ++st)
-      s[kt] = M::mma(row_frag<M, D>(Ks, 32 * kt, st, r, g), qf[st], s[kt]);
+      for (int rb = 0; rb < RB; ++rb) s[rb][kt] = zero16();
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const frag A = ld_row<M>(smem + KOFF + 32 * kt * L::PITCH, lo.row[st]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb][kt] = M::mma(A, qf[rb].f[st], s[rb][kt]);
+      }
+    }
   }
-  if (masked) {
+
+  // Masks one row block's scores of a tile cut by the window or the
+  // sequence end, then raises the row's reference max m when the tile's max
+  // exceeds it by more than kRescaleSlack, rescaling l and O.  c >= 1e-30,
+  // so a masked score (-inf) always maps to -inf and then to p = 0.
+  static __device__ __forceinline__ void finalize(f32x16* s, bool masked, Window w, int j0, int qi, int sk,
+                                                  float c, float& m, float& l, f32x16* acc, int g) {
+    if (masked) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = j0 + 32 * kt + acc_row(e, g);
+          const int diff = j - qi;
+          if (!(diff >= w.lo && diff <= w.hi && j < sk)) s[kt][e] = -INFINITY;
+        }
+    }
+    float smax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = j0 + 32 * kt + acc_row(e, g);
-        const int diff = j - qi;
-        if (!(diff >= w.lo && diff <= w.hi && j < sk)) s[kt][e] = -INFINITY;
-      }
-  }
-  float smax = -INFINITY;
+      for (int e = 0; e < 16; ++e) smax = fmaxf(smax, s[kt][e]);
+    const float mx = halves_max(smax) * c;
+    const bool raise = mx > m + kRescaleSlack;  // also when m is still -inf
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+      if (raise) m = mx;
+      l *= alpha;
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt)
+      for (int dt = 0; dt < DVT; ++dt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) smax = fmaxf(smax, s[kt][e]);
-  smax = halves_max(smax);
-  const float mx = smax == -INFINITY ? -INFINITY : smax * c;
-  const bool raise = mx > m + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(raise)) {
-    const float alpha = raise ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
-    if (raise) m = mx;
-    l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < DVT; ++dt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
-  }
-  const float nm = m == -INFINITY ? 0.f : -m;
-  float ls = 0.f;
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    float x[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, nm));
-      if (masked && s[kt][e] == -INFINITY) pe = 0.f;  // also when c == 0
-      x[e] = pe;
-      ls += pe;
-    }
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      typename M::frag pf;
-      M::pack(&x[8 * st], pf);
-      const int ra = 32 * kt + 16 * st;
-#pragma unroll
-      for (int dt = 0; dt < DVT; ++dt) acc[dt] = M::mma(tr_frag<M, D>(Vs, ra, ra + 8, dt, lane), pf, acc[dt]);
+        for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
     }
   }
-  l += ls;
-}
 
-template <typename M, int D, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void attn_fwd16_kernel(FwdArgs a) {
+  // P = 2^(c s - m), rounded to the working type, and O^T += V^T P^T, for
+  // every row block.
+  template <int VOFF>
+  static __device__ __forceinline__ void softmax_pv(const T* smem, const LdsOffsets<M, D>& lo,
+                                                    const f32x16 (*s)[KT], f32x16 (*acc)[DVT], const float* m,
+                                                    float c, float* l) {
+    float nm[RB], ls[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      nm[rb] = m[rb] == -INFINITY ? 0.f : -m[rb];  // nothing visible yet: p = 0
+      ls[rb] = 0.f;
+    }
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      frag pf[RB][2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float x[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][kt][e], c, nm[rb]));
+          ls[rb] += x[e];
+        }
+        M::pack(&x[0], pf[rb][0]);
+        M::pack(&x[8], pf[rb][1]);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const T* vb = smem + VOFF + (32 * kt + 16 * st) * L::PITCH;
+#pragma unroll
+        for (int dt = 0; dt < DVT; ++dt) {
+          const frag A = ld_tr<M>(vb, lo.tra[dt], lo.trb[dt]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc[rb][dt] = M::mma(A, pf[rb][st], acc[rb][dt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l[rb] += ls[rb];
+  }
+};
+
+template <typename M, int D, int NW, int BN, int RB, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_fwd16_kernel(FwdArgs a) {
+  using F = Fwd16<M, D, BN, RB>;
   using T = typename M::elem;
-  using L = Swz<D>;
-  constexpr int NT = NW * 64, BM = NW * 32, DVT = (D + 31) / 32;
-  constexpr int TILE = BN * L::PITCH;  // elements of one K or V tile
-  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];  // [stage][K, V]
+  constexpr int NT = NW * 64, WR = 32 * RB, BM = NW * WR, KT = F::KT, DVT = F::DVT;
+  __shared__ __attribute__((aligned(1024))) T smem[4 * F::TILE];
 
   const ProblemArgs& P = a.p;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = (int)(gridDim.x / (P.B * P.H));
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
@@ -334,85 +381,127 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd16_kernel(FwdArgs a) {
   T* op = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + q0 * a.o.ss;
   float* lp = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
 
+  // Keys the block can see, and the tiles of this wave's rows.
   const int ilast = min(i0 + BM, sq) - 1;
   const long long jlo = max(0LL, (long long)i0 + w.lo);
   const long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
   const bool block_empty = w.lo > w.hi || jlo > jhi;
 
-  const int iw0 = i0 + 32 * wave;
+  const int iw0 = i0 + WR * wave;
   const bool wave_live = iw0 < sq;
-  const int qi = iw0 + r;
+  int tw0 = 0x7fffffff, tw1 = -1;
+  if (wave_live && w.lo <= w.hi) {
+    const long long a0 = max(0LL, (long long)iw0 + w.lo);
+    const long long a1 = min((long long)sk - 1, (long long)min(iw0 + WR - 1, sq - 1) + w.hi);
+    if (a0 <= a1) {
+      tw0 = (int)(a0 / BN);
+      tw1 = (int)(a1 / BN);
+    }
+  }
 
-  RowFrags<M, D> qf;
-  qf.load(qp + (long long)qi * a.q.ss, wave_live && qi < sq, g);
-  const float c = fabsf(P.scale_log2);
-  if (P.scale_log2 < 0.f) qf.negate();
-
-  float m = -INFINITY, l = 0.f;
-  f32x16 acc[DVT];
+  const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
+  RowFrags<M, D> qf[RB];
 #pragma unroll
-  for (int dt = 0; dt < DVT; ++dt) acc[dt] = zero16();
+  for (int rb = 0; rb < RB; ++rb) {
+    const int qi = iw0 + 32 * rb + r;
+    qf[rb].load(qp + (long long)qi * a.q.ss, wave_live && qi < sq, g);
+    if (P.scale_log2 < 0.f) qf[rb].negate();
+  }
+
+  float m[RB], l[RB];
+  f32x16 acc[RB][DVT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt) acc[rb][dt] = zero16();
+  }
 
   if (!block_empty) {
+    LdsOffsets<M, D> lo;
+    lo.init(lane);
+    DmaLane<T, D, BN, NW> kd, vd;
+    kd.init(a.k.ss, wave, lane);
+    vd.init(a.v.ss, wave, lane);
     zero_unused_slots<T, D, 4 * BN, NT>(smem, tid);
     const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
-    {
-      const int j0 = t0 * BN;
-      dma_tile<T, D, BN, NW>(smem, kp + (long long)j0 * a.k.ss, a.k.ss, sk - j0, wave, lane);
-      dma_tile<T, D, BN, NW>(smem + TILE, vp + (long long)j0 * a.v.ss, a.v.ss, sk - j0, wave, lane);
-    }
+    auto dma = [&](int stage, int t) {
+      kd.issue(smem + F::kOff(stage), kp + (long long)t * BN * a.k.ss, a.k.ss, sk - t * BN, wave, lane);
+      vd.issue(smem + F::vOff(stage), vp + (long long)t * BN * a.v.ss, a.v.ss, sk - t * BN, wave, lane);
+    };
+    // Step t: K_t and V_t sit in stage P = (t - t0) & 1; the copies of K_{t+1}
+    // and V_{t+1} into stage P^1 fly during the step.
+    dma(0, t0);
     __syncthreads();
-    for (int t = t0; t <= t1; ++t) {
-      const int stg = (t - t0) & 1;
-      const int j0 = t * BN;
-      if (t < t1) {
-        T* nb = smem + (stg ^ 1) * 2 * TILE;
-        const int jn = j0 + BN;
-        dma_tile<T, D, BN, NW>(nb, kp + (long long)jn * a.k.ss, a.k.ss, sk - jn, wave, lane);
-        dma_tile<T, D, BN, NW>(nb + TILE, vp + (long long)jn * a.v.ss, a.v.ss, sk - jn, wave, lane);
+    auto step = [&](auto parity, int t) {
+      constexpr int Pq = decltype(parity)::value;
+      if (t + 1 <= t1) dma(Pq ^ 1, t + 1);
+      if (tw0 <= t && t <= tw1) {
+        f32x16 s[RB][KT];
+        F::template scores<F::kOff(Pq)>(smem, lo, qf, s);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int rb0 = iw0 + 32 * rb;
+          const bool masked = classify(w, rb0, 32, (long long)t * BN, BN, sk) == kPartial;
+          F::finalize(s[rb], masked, w, t * BN, rb0 + r, sk, c, m[rb], l[rb], acc[rb], g);
+        }
+        F::template softmax_pv<F::vOff(Pq)>(smem, lo, s, acc, m, c, l);
       }
-      const T* Ks = smem + stg * 2 * TILE;
-      const int cls = wave_live ? classify(w, iw0, 32, j0, BN, sk) : kEmpty;
-      if (cls == kFull)
-        fwd16_tile<M, D, NW, BN>(Ks, Ks + TILE, qf.f, acc, m, l, c, false, w, j0, qi, sk, r, g, lane);
-      else if (cls == kPartial)
-        fwd16_tile<M, D, NW, BN>(Ks, Ks + TILE, qf.f, acc, m, l, c, true, w, j0, qi, sk, r, g, lane);
       __syncthreads();
+    };
+    for (int t = t0; t <= t1; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 <= t1) step(std::integral_constant<int, 1>{}, t + 1);
     }
   }
 
   if (wave_live) {
-    const float lt = halves_sum(l);
-    if (qi < sq) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      T* orow = op + (long long)qi * a.o.ss;
 #pragma unroll
-      for (int dt = 0; dt < DVT; ++dt)
+    for (int rb = 0; rb < RB; ++rb) {
+      const int qi = iw0 + 32 * rb + r;
+      const float lt = halves_sum(l[rb]);
+      if (qi < sq) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        T* orow = op + (long long)qi * a.o.ss;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = 32 * dt + 8 * q4 + 4 * g;
-          if (d < D)
-            store4<T>(orow + d, acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
-                      acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
-        }
-      if (g == 0) lp[qi] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+        for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = 32 * dt + 8 * q4 + 4 * g;
+            if (d < D)
+              store4<T>(orow + d, acc[rb][dt][4 * q4] * inv, acc[rb][dt][4 * q4 + 1] * inv,
+                        acc[rb][dt][4 * q4 + 2] * inv, acc[rb][dt][4 * q4 + 3] * inv);
+          }
+        if (g == 0) lp[qi] = lt > 0.f ? (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+      }
     }
   }
 }
 
-// Workgroup shapes: the fp32 kernel (tiles twice as large in LDS and
-// registers) runs 4 waves; the 16-bit kernel 8 waves (two per SIMD) over
-// 64-key tiles.
-template <typename M>
+// Workgroup shapes.  fp32 (register-staged kernel, tiles twice as large):
+// 4 waves, 64-key tiles.  16-bit, 64-key tiles: head_dim <= 80, 8 waves of
+// one 32-row block (two waves per SIMD); head_dim 128, FWD16_NW_BIG waves of
+// FWD16_RB_BIG row blocks.
+#ifndef FWD16_NW_BIG
+#define FWD16_NW_BIG 4
+#endif
+#ifndef FWD16_RB_BIG
+#define FWD16_RB_BIG 1
+#endif
+template <typename M, int D>
 struct FwdShape {
   static constexpr bool k16 = sizeof(typename M::elem) == 2;
-  static constexpr int NW = k16 ? 8 : 4;
+  static constexpr bool big = D > 80;
+  static constexpr int RB = k16 && big ? FWD16_RB_BIG : 1;
+  static constexpr int NW = k16 ? (big ? FWD16_NW_BIG : 8) : 4;
   static constexpr int BN = 64;
+  static constexpr int WPE = RB >= 2 ? 1 : 2;  // waves per SIMD the registers allow
 };
 
 template <typename M, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NW = FwdShape<M>::NW, BN = FwdShape<M>::BN, BM = NW * 32;
+  constexpr int NW = FwdShape<M, D>::NW, BN = FwdShape<M, D>::BN, BM = NW * 32 * FwdShape<M, D>::RB;
   const long long nq = (a.p.Sq + BM - 1) / BM;
   const long long nblk = nq * a.p.H * a.p.B;
   if (nblk == 0) return hipSuccess;
@@ -420,8 +509,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   FwdArgs args = a;
   void* kargs[] = {&args};
   const void* fn;
-  if constexpr (FwdShape<M>::k16)
-    fn = reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, NW, BN>);
+  if constexpr (FwdShape<M, D>::k16)
+    fn = reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, NW, BN, FwdShape<M, D>::RB, FwdShape<M, D>::WPE>);
   else
     fn = reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, NW, BN>);
   return hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NW * 64), kargs, 0, stream);
