@@ -142,15 +142,18 @@ hipError_t attn_bwd(const attn_bwd_params *p, hipStream_t stream);
  * order on one stream (or be ordered by events): attn_bwd_dkdv and
  * attn_bwd_dq read the Delta that attn_bwd_preprocess leaves in the
  * workspace, which must not be touched in between.
- *   attn_bwd_preprocess: Delta_i = sum_d dO_id O_id into the workspace.
+ *   attn_bwd_preprocess: Delta_i = sum_d dO_id O_id and LSE_i log2(e) into
+ *                        the workspace.
  *   attn_bwd_dkdv:       dK and dV, one workgroup per block of keys.
  *   attn_bwd_dq:         dQ, one workgroup per block of queries. */
 hipError_t attn_bwd_preprocess(const attn_bwd_params *p, hipStream_t stream);
 hipError_t attn_bwd_dkdv(const attn_bwd_params *p, hipStream_t stream);
 hipError_t attn_bwd_dq(const attn_bwd_params *p, hipStream_t stream);
 
-/* Workspace bytes attn_bwd needs for this problem (fp32 Delta per query row
- * and head, rounded up to 256 bytes); 0 when the problem is malformed. */
+/* Workspace bytes attn_bwd needs for this problem: two fp32 values per query
+ * row and head (Delta_i and LSE_i * log2(e), written by attn_bwd_preprocess
+ * and read by the other two steps), each array rounded up to 256 bytes;
+ * 0 when the problem is malformed. */
 uint64_t attn_bwd_workspace_size(const attn_bwd_params *p);
 
 /* Host-only validation of a call, the same checks attn_fwd / attn_bwd make

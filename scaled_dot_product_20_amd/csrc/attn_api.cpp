@@ -92,11 +92,14 @@ Extent lse_extent(const attn_fwd_params* p) {
   return Extent{lo, lo + (uintptr_t)(n * 4)};
 }
 
-uint64_t delta_bytes(const attn_fwd_params* p) {
+// Workspace: Delta, then LSE * log2(e), one fp32 per (head, query row)
+// each, each section rounded up to 256 bytes.
+uint64_t stat_section_bytes(const attn_fwd_params* p) {
   const int64_t n = p->layout == ATTN_THD ? (int64_t)p->heads * p->total_q
                                           : (int64_t)p->batch * p->heads * p->seqlen_q;
   return ((uint64_t)n * 4 + 255) / 256 * 256;
 }
+uint64_t delta_bytes(const attn_fwd_params* p) { return 2 * stat_section_bytes(p); }
 
 sdpa::ProblemArgs problem_args(const attn_fwd_params* p) {
   sdpa::ProblemArgs a{};
@@ -250,6 +253,7 @@ hipError_t bwd_stages(const attn_bwd_params* p, int stages, hipStream_t stream) 
   a.dv = operand(p->dv, p->dv_stride, packed);
   a.lse = f->lse;
   a.delta = static_cast<float*>(p->workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(p->workspace) + stat_section_bytes(f));
   return on_stream_device(stream,
                           [&] { return sdpa::launch_bwd(f->dtype, f->head_dim, a, stages, stream); });
 }

@@ -46,7 +46,8 @@ __device__ __forceinline__ float dot_chunk(uint4 x, uint4 y) {
 // ------------------------------------------------------------ preprocess
 
 // Delta_i = sum_d dO_id * O_id in fp32, one group of G lanes per row, each
-// lane one 16-byte chunk.  Rows are (b, h, i) for the dense layout and
+// lane one 16-byte chunk; beside it LSE_i * log2(e), the form the 16-bit
+// kernels use.  Rows are (b, h, i) for the dense layout and
 // (packed row t, h) for the packed one.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a, long long nrows) {
@@ -75,7 +76,11 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a, long long 
   }
 #pragma unroll
   for (int off = G / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, G);
-  if (c == 0) a.delta[b * P.lse_sb + h * P.lse_sh + i] = s;
+  if (c == 0) {
+    const long long idx = b * P.lse_sb + h * P.lse_sh + i;
+    a.delta[idx] = s;
+    a.lse2[idx] = a.lse[idx] * kLog2e;  // +inf (empty row) stays +inf
+  }
 }
 
 // ------------------------------------------------------------ dK / dV
@@ -422,37 +427,105 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 //   transposing reads of the same tiles.
 // Each wave visits only the query tiles that can see its keys; tiles cut
 // by the window have their scores set to -inf where masked.
-template <typename M, int D, int BMQ>
+template <typename M, int D, int BMQ, int ST, bool PHASED>
 struct Dkdv16 {
   using T = typename M::elem;
   using L = Swz<D>;
   using frag = typename M::frag;
   static constexpr int MQ = BMQ / 32, NS = D / 16, DVT = (D + 31) / 32;
   static constexpr int TILE = BMQ * L::PITCH;
-  // LDS, in elements: Q stage 0, Q stage 1, dO stage 0, dO stage 1.
-  static constexpr int qOff(int stage) { return stage * TILE; }
-  static constexpr int dOff(int stage) { return (2 + stage) * TILE; }
 
-  template <int QOFF, int DOFF>
-  static __device__ __forceinline__ void tile(const T* smem, const LdsOffsets<M, D>& lo, const float* lse2s,
+  // PHASED (one wave per SIMD): all S and dP products of the tile come first
+  // (one straight run of matrix work), then the masking of a tile cut by the
+  // window or the sequence end (one uniform branch), then per 32-row slice
+  // the probabilities and the dV / dK products, so one slice's vector work
+  // overlaps the next slice's products.  Otherwise slice by slice.
+  static __device__ __forceinline__ void tile(const T* Qs, const T* dOs, const LdsOffsets<M, D>& lo, const float* lse2s,
                                               const float* dels, const RowFrags<M, D>& kf,
                                               const RowFrags<M, D>& vf, f32x16* dk, f32x16* dv, float c,
-                                              bool masked, Window w, int i0, int kj, int g) {
+                                              bool masked, Window w, int i0, int kj, int sq, int g) {
+    if constexpr (!PHASED) {
+      // Two waves per SIMD: one slice at a time keeps the registers low.
 #pragma unroll
-    for (int mq = 0; mq < MQ; ++mq) {
-      f32x16 s = zero16(), dp = zero16();
+      for (int mq = 0; mq < MQ; ++mq) {
+        f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        s = M::mma(ld_row<M>(smem + QOFF + 32 * mq * L::PITCH, lo.row[st]), kf.f[st], s);
-        dp = M::mma(ld_row<M>(smem + DOFF + 32 * mq * L::PITCH, lo.row[st]), vf.f[st], dp);
-      }
-      if (masked) {
+        for (int st = 0; st < NS; ++st) {
+          s = M::mma(ld_row<M>(Qs + 32 * mq * L::PITCH, lo.row[st]), kf.f[st], s);
+          dp = M::mma(ld_row<M>(dOs + 32 * mq * L::PITCH, lo.row[st]), vf.f[st], dp);
+        }
+        if (masked) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int diff = kj - (i0 + 32 * mq + acc_row(e, g));
-          if (!(diff >= w.lo && diff <= w.hi)) s[e] = -INFINITY;
+          for (int e = 0; e < 16; ++e) {
+            const int i = i0 + 32 * mq + acc_row(e, g);
+            const int diff = kj - i;
+            if (!(diff >= w.lo && diff <= w.hi && i < sq)) s[e] = -INFINITY;
+          }
+        }
+        float p[16], ds[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int il = 32 * mq + 8 * q4 + 4 * g;
+          const float4 ll = *reinterpret_cast<const float4*>(lse2s + il);
+          const float4 dd = *reinterpret_cast<const float4*>(dels + il);
+          const float lv[4] = {ll.x, ll.y, ll.z, ll.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = 4 * q4 + u;
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
+            ds[e] = p[e] * (dp[e] - dv4[u]);
+          }
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          frag pf, dsf;
+          M::pack(&p[8 * st], pf);
+          M::pack(&ds[8 * st], dsf);
+          const int rbase = (32 * mq + 16 * st) * L::PITCH;
+#pragma unroll
+          for (int dt = 0; dt < DVT; ++dt) {
+            dv[dt] = M::mma(ld_tr<M>(dOs + rbase, lo.tra[dt], lo.trb[dt]), pf, dv[dt]);
+            dk[dt] = M::mma(ld_tr<M>(Qs + rbase, lo.tra[dt], lo.trb[dt]), dsf, dk[dt]);
+          }
         }
       }
+      return;
+    }
+    f32x16 s[MQ], dp[MQ];
+#pragma unroll
+    for (int mq = 0; mq < MQ; ++mq) {
+      s[mq] = zero16();
+      dp[mq] = zero16();
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s[mq] = M::mma(ld_row<M>(Qs + 32 * mq * L::PITCH, lo.row[st]), kf.f[st], s[mq]);
+        dp[mq] = M::mma(ld_row<M>(dOs + 32 * mq * L::PITCH, lo.row[st]), vf.f[st], dp[mq]);
+      }
+    }
+#ifdef BWD16_SGB
+    // Issue order: 8 operand reads ahead, then one product per read.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * MQ * NS - 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#endif
+    if (masked) {
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int i = i0 + 32 * mq + acc_row(e, g);
+          const int diff = kj - i;
+          if (!(diff >= w.lo && diff <= w.hi && i < sq)) s[mq][e] = -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int mq = 0; mq < MQ; ++mq) {
       float p[16], ds[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -463,8 +536,8 @@ struct Dkdv16 {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int e = 4 * q4 + u;
-          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
-          ds[e] = p[e] * (dp[e] - dv4[u]);
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mq][e], c, -lv[u]));
+          ds[e] = p[e] * (dp[mq][e] - dv4[u]);
         }
       }
 #pragma unroll
@@ -475,21 +548,44 @@ struct Dkdv16 {
         const int rbase = (32 * mq + 16 * st) * L::PITCH;
 #pragma unroll
         for (int dt = 0; dt < DVT; ++dt) {
-          dv[dt] = M::mma(ld_tr<M>(smem + DOFF + rbase, lo.tra[dt], lo.trb[dt]), pf, dv[dt]);
-          dk[dt] = M::mma(ld_tr<M>(smem + QOFF + rbase, lo.tra[dt], lo.trb[dt]), dsf, dk[dt]);
+          dv[dt] = M::mma(ld_tr<M>(dOs + rbase, lo.tra[dt], lo.trb[dt]), pf, dv[dt]);
+          dk[dt] = M::mma(ld_tr<M>(Qs + rbase, lo.tra[dt], lo.trb[dt]), dsf, dk[dt]);
         }
       }
     }
+#ifdef BWD16_SGB2
+    // Second phase: transposing reads of a slice ahead of its products,
+    // vector work of the next slice between the products.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+#pragma unroll
+    for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+      for (int i = 0; i < 4 * DVT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+#endif
   }
 };
 
-template <typename M, int D, int NW, int BMQ, int WPE>
+template <typename M, int D, int NW, int BMQ, int WPE, int ST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dkdv16_kernel(BwdArgs a) {
-  using F = Dkdv16<M, D, BMQ>;
+  using F = Dkdv16<M, D, BMQ, ST, (WPE == 1)>;
   using T = typename M::elem;
+  using DL = DmaLane<T, D, BMQ, NW>;
   constexpr int NT = NW * 64, BNK = NW * 32, DVT = F::DVT;
-  __shared__ __attribute__((aligned(1024))) T smem[4 * F::TILE];
-  __shared__ __attribute__((aligned(16))) float stats[2][2][BMQ];  // [stage][lse2, delta][row]
+  constexpr int RW = BMQ / NW;           // LSE / Delta rows each wave copies per tile
+  constexpr int VM = 2 * DL::PER + 2;    // vector-memory instructions per wave per tile
+  static_assert(BMQ % NW == 0 && RW <= 64, "stats rows");
+  // One LDS array per stage and operand, so that the compiler can tell the
+  // tiles being read from those being filled by direct loads and does not
+  // wait for those loads before every read.  Stage 2 exists only when ST = 3.
+  __shared__ __attribute__((aligned(1024))) T q_s0[F::TILE], q_s1[F::TILE], q_s2[ST > 2 ? F::TILE : 8];
+  __shared__ __attribute__((aligned(1024))) T d_s0[F::TILE], d_s1[F::TILE], d_s2[ST > 2 ? F::TILE : 8];
+  // LSE log2(e) and Delta of each stage's query rows.
+  __shared__ __attribute__((aligned(16))) float l_s0[BMQ], l_s1[BMQ], l_s2[BMQ], e_s0[BMQ], e_s1[BMQ], e_s2[BMQ];
 
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -517,7 +613,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const T* dop = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + q0 * a.dout.ss;
   T* dkp = (T*)a.dk.ptr + b * a.dk.sb + h * a.dk.sh + k0 * a.dk.ss;
   T* dvp = (T*)a.dv.ptr + b * a.dv.sb + h * a.dv.sh + k0 * a.dv.ss;
-  const float* lsep = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  const float* l2p = a.lse2 + b * P.lse_sb + h * P.lse_sh + q0;
   const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
 
   // Queries that can see the block's keys, and the tiles of this wave's keys.
@@ -555,53 +651,78 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   if (!block_empty) {
     LdsOffsets<M, D> lo;
     lo.init(lane);
-    DmaLane<T, D, BMQ, NW> qd, dd;
+    DL qd, dd;
     qd.init(a.q.ss, wave, lane);
     dd.init(a.dout.ss, wave, lane);
-    zero_unused_slots<T, D, 4 * BMQ, NT>(smem, tid);
+    T* const qs[3] = {q_s0, q_s1, q_s2};
+    T* const ds_[3] = {d_s0, d_s1, d_s2};
+#pragma unroll
+    for (int u = 0; u < ST; ++u) {
+      zero_unused_slots<T, D, BMQ, NT>(qs[u], tid);
+      zero_unused_slots<T, D, BMQ, NT>(ds_[u], tid);
+    }
     const int t0 = (int)(ilo / BMQ), t1 = (int)(ihi / BMQ);
-    auto dma = [&](int stage, int t) {
+    // One tile's loads, all direct to LDS: its Q and dO rows and, per wave,
+    // RW rows of LSE log2(e) and Delta (rows past the sequence repeat its
+    // last row and are masked).  Every wave issues exactly VM vector-memory
+    // instructions per tile, so a wait for "at most VM outstanding" retires
+    // everything issued before the latest tile.
+    float* const ls[3] = {l_s0, l_s1, l_s2};
+    float* const es[3] = {e_s0, e_s1, e_s2};
+    auto issue = [&](int stage, int t) {
       const int i0 = t * BMQ;
-      qd.issue(smem + F::qOff(stage), qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
-      dd.issue(smem + F::dOff(stage), dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, wave, lane);
-    };
-    float st_l = INFINITY, st_d = 0.f;  // this thread's LSE / Delta entry (tid < BMQ)
-    auto load_stats = [&](int t) {
-      if (tid < BMQ) {
-        const int i = t * BMQ + tid;
-        st_l = i < sq ? lsep[i] * kLog2e : INFINITY;
-        st_d = i < sq ? delp[i] : 0.f;
+      qd.issue(qs[stage], qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
+      dd.issue(ds_[stage], dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, wave, lane);
+      if (lane < RW) {
+        const int ic = min(i0 + wave * RW + lane, sq - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(l2p + ic), (lds_void*)(ls[stage] + wave * RW), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(delp + ic), (lds_void*)(es[stage] + wave * RW), 4, 0, 0);
       }
     };
-    auto store_stats = [&](int stage) {
-      if (tid < BMQ) {
-        stats[stage][0][tid] = st_l;
-        stats[stage][1][tid] = st_d;
-      }
-    };
-    dma(0, t0);
-    load_stats(t0);
-    store_stats(0);
+    issue(0, t0);
+    if (ST == 3 && t0 + 1 <= t1) issue(1, t0 + 1);
     __syncthreads();
-    // Step t: the tiles of query tile t sit in stage P = (t - t0) & 1; the
-    // copies of tile t+1 into stage P^1 fly during the step.
-    auto step = [&](auto parity, int t) {
+    // Step t: tile t sits in stage P = (t - t0) % ST; the loads of tile
+    // t+ST-1 are issued now into the stage tile t-1 used.  With three stages
+    // the barrier at the end waits only for tile t+1 (AH: the step looks
+    // ahead, known at compile time in the steady state so that the wait
+    // counts stay exact).
+    auto step = [&](auto parity, auto ahead_c, int t) {
       constexpr int Pq = decltype(parity)::value;
-      if (t + 1 <= t1) {
-        dma(Pq ^ 1, t + 1);
-        load_stats(t + 1);
-      }
+      constexpr int Pa = (Pq + ST - 1) % ST;
+      constexpr int AH = decltype(ahead_c)::value;  // 1: yes, 0: check
+      const bool ahead = AH || t + ST - 1 <= t1;
+      if (ahead) issue(Pa, t + ST - 1);
       if (tw0 <= t && t <= tw1) {
-        const bool masked = classify(w, (long long)t * BMQ, BMQ, jw0, 32, sk) == kPartial;
-        F::template tile<F::qOff(Pq), F::dOff(Pq)>(smem, lo, stats[Pq][0], stats[Pq][1], kf, vf, dk, dv, c,
-                                                  masked, w, t * BMQ, kj, g);
+        const bool masked =
+            classify(w, (long long)t * BMQ, BMQ, jw0, 32, sk) == kPartial || (t + 1) * BMQ > sq;
+        F::tile(qs[Pq], ds_[Pq], lo, ls[Pq], es[Pq], kf, vf, dk, dv, c, masked, w, t * BMQ, kj, sq, g);
       }
-      if (t + 1 <= t1) store_stats(Pq ^ 1);
-      __syncthreads();
+      if (ST == 3 && AH)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+      else
+        __syncthreads();
     };
-    for (int t = t0; t <= t1; t += 2) {
-      step(std::integral_constant<int, 0>{}, t);
-      if (t + 1 <= t1) step(std::integral_constant<int, 1>{}, t + 1);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    static_assert(ST == 2 || ST == 3, "stages");
+    int t = t0;
+    if constexpr (ST == 3) {
+      for (; t + ST + 1 <= t1; t += 3) {  // every step of the group looks ahead
+        step(I0{}, I1{}, t);
+        step(I1{}, I1{}, t + 1);
+        step(I2{}, I1{}, t + 2);
+      }
+      if (t <= t1) step(I0{}, I0{}, t);
+      if (t + 1 <= t1) step(I1{}, I0{}, t + 1);
+      if (t + 2 <= t1) step(I2{}, I0{}, t + 2);
+      if (t + 3 <= t1) step(I0{}, I0{}, t + 3);
+    } else {
+      for (; t <= t1; t += 2) {
+        step(I0{}, I0{}, t);
+        if (t + 1 <= t1) step(I1{}, I0{}, t + 1);
+      }
     }
   }
 
@@ -639,12 +760,8 @@ struct Dq16 {
   using frag = typename M::frag;
   static constexpr int KT = BN / 32, NS = D / 16, DVT = (D + 31) / 32;
   static constexpr int TILE = BN * L::PITCH;
-  // LDS, in elements: K stage 0, K stage 1, V stage 0, V stage 1.
-  static constexpr int kOff(int stage) { return stage * TILE; }
-  static constexpr int vOff(int stage) { return (2 + stage) * TILE; }
 
-  template <int KOFF, int VOFF>
-  static __device__ __forceinline__ void tile(const T* smem, const LdsOffsets<M, D>& lo,
+  static __device__ __forceinline__ void tile(const T* Ks, const T* Vs, const LdsOffsets<M, D>& lo,
                                               const RowFrags<M, D>& qf, const RowFrags<M, D>& dof, f32x16* dq,
                                               float c, float lse2, float delta, bool masked, Window w, int j0,
                                               int qi, int sk, int g) {
@@ -653,8 +770,8 @@ struct Dq16 {
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        s = M::mma(ld_row<M>(smem + KOFF + 32 * kt * L::PITCH, lo.row[st]), qf.f[st], s);
-        dp = M::mma(ld_row<M>(smem + VOFF + 32 * kt * L::PITCH, lo.row[st]), dof.f[st], dp);
+        s = M::mma(ld_row<M>(Ks + 32 * kt * L::PITCH, lo.row[st]), qf.f[st], s);
+        dp = M::mma(ld_row<M>(Vs + 32 * kt * L::PITCH, lo.row[st]), dof.f[st], dp);
       }
       if (masked) {
 #pragma unroll
@@ -675,7 +792,7 @@ struct Dq16 {
         const int rbase = (32 * kt + 16 * st) * L::PITCH;
 #pragma unroll
         for (int dt = 0; dt < DVT; ++dt)
-          dq[dt] = M::mma(ld_tr<M>(smem + KOFF + rbase, lo.tra[dt], lo.trb[dt]), dsf, dq[dt]);
+          dq[dt] = M::mma(ld_tr<M>(Ks + rbase, lo.tra[dt], lo.trb[dt]), dsf, dq[dt]);
       }
     }
   }
@@ -686,7 +803,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   using F = Dq16<M, D, BN>;
   using T = typename M::elem;
   constexpr int NT = NW * 64, BM = NW * 32, DVT = F::DVT;
-  __shared__ __attribute__((aligned(1024))) T smem[4 * F::TILE];
+  // One LDS array per stage and operand (see the dK/dV kernel).
+  __shared__ __attribute__((aligned(1024))) T k_s0[F::TILE], k_s1[F::TILE], v_s0[F::TILE], v_s1[F::TILE];
 
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -713,7 +831,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
   const T* dop = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + q0 * a.dout.ss;
   T* dqp = (T*)a.dq.ptr + b * a.dq.sb + h * a.dq.sh + q0 * a.dq.ss;
-  const float* lsep = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  const float* l2p = a.lse2 + b * P.lse_sb + h * P.lse_sh + q0;
   const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
 
   const int ilast = min(i0 + BM, sq) - 1;
@@ -738,7 +856,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   RowFrags<M, D> qf, dof;
   qf.load(qp + (long long)qi * a.q.ss, row_ok, g);
   dof.load(dop + (long long)qi * a.dout.ss, row_ok, g);
-  const float lse2 = row_ok ? lsep[qi] * kLog2e : INFINITY;
+  const float lse2 = row_ok ? l2p[qi] : INFINITY;
   const float delta = row_ok ? delp[qi] : 0.f;
   const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
   if (P.scale_log2 < 0.f) qf.negate();
@@ -753,21 +871,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     DmaLane<T, D, BN, NW> kd, vd;
     kd.init(a.k.ss, wave, lane);
     vd.init(a.v.ss, wave, lane);
-    zero_unused_slots<T, D, 4 * BN, NT>(smem, tid);
+    zero_unused_slots<T, D, BN, NT>(k_s0, tid);
+    zero_unused_slots<T, D, BN, NT>(k_s1, tid);
+    zero_unused_slots<T, D, BN, NT>(v_s0, tid);
+    zero_unused_slots<T, D, BN, NT>(v_s1, tid);
     const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
-    auto dma = [&](int stage, int t) {
-      kd.issue(smem + F::kOff(stage), kp + (long long)t * BN * a.k.ss, a.k.ss, sk - t * BN, wave, lane);
-      vd.issue(smem + F::vOff(stage), vp + (long long)t * BN * a.v.ss, a.v.ss, sk - t * BN, wave, lane);
+    auto dma = [&](T* kb, T* vb, int t) {
+      kd.issue(kb, kp + (long long)t * BN * a.k.ss, a.k.ss, sk - t * BN, wave, lane);
+      vd.issue(vb, vp + (long long)t * BN * a.v.ss, a.v.ss, sk - t * BN, wave, lane);
     };
-    dma(0, t0);
+    dma(k_s0, v_s0, t0);
     __syncthreads();
     auto step = [&](auto parity, int t) {
       constexpr int Pq = decltype(parity)::value;
-      if (t + 1 <= t1) dma(Pq ^ 1, t + 1);
+      if (t + 1 <= t1) dma(Pq ? k_s0 : k_s1, Pq ? v_s0 : v_s1, t + 1);
       if (tw0 <= t && t <= tw1) {
         const bool masked = classify(w, iw0, 32, (long long)t * BN, BN, sk) == kPartial;
-        F::template tile<F::kOff(Pq), F::vOff(Pq)>(smem, lo, qf, dof, dq, c, lse2, delta, masked, w, t * BN, qi,
-                                                  sk, g);
+        F::tile(Pq ? k_s1 : k_s0, Pq ? v_s1 : v_s0, lo, qf, dof, dq, c, lse2, delta, masked, w, t * BN, qi, sk, g);
       }
       __syncthreads();
     };
@@ -805,7 +925,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 template <typename M, int D>
 struct BwdShape {
   static constexpr bool k16 = sizeof(typename M::elem) == 2;
-  static constexpr int NW_KV = 4, BMQ = k16 ? 64 : 32, WPE_KV = D > 80 ? 1 : 2;
+#ifndef BWD16_BMQ_BIG
+#define BWD16_BMQ_BIG 64
+#endif
+#ifndef BWD16_ST_BIG
+#define BWD16_ST_BIG 2
+#endif
+  static constexpr int NW_KV = 4, BMQ = k16 ? (D > 80 ? BWD16_BMQ_BIG : 64) : 32, WPE_KV = D > 80 ? 1 : 2;
+  static constexpr int ST_KV = D > 80 ? BWD16_ST_BIG : 2;  // LDS stages of the dK/dV query tiles
   static constexpr int NW_Q = k16 ? BWD16_NWQ : 4, BN = k16 ? 64 : 32;
 };
 
@@ -841,7 +968,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
     if (nblk > 0) {
       const void* fn;
       if constexpr (S::k16)
-        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV>);
+        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV, S::ST_KV>);
       else
         fn = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>);
       err = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NW_KV * 64), kargs, 0, stream);

@@ -251,13 +251,10 @@ struct Fwd16 {
   using frag = typename M::frag;
   static constexpr int KT = BN / 32, NS = D / 16, DVT = (D + 31) / 32;
   static constexpr int TILE = BN * L::PITCH;
-  // LDS, in elements: K stage 0, K stage 1, V stage 0, V stage 1.
-  static constexpr int kOff(int stage) { return stage * TILE; }
-  static constexpr int vOff(int stage) { return (2 + stage) * TILE; }
 
-  // s[rb][kt] = (K Q^T) of one tile for every row block.
-  template <int KOFF>
-  static __device__ __forceinline__ void scores(const T* smem, const LdsOffsets<M, D>& lo,
+  // s[rb][kt] = (K Q^T) of one tile (K: the swizzled LDS tile) for every
+  // row block.
+  static __device__ __forceinline__ void scores(const T* K, const LdsOffsets<M, D>& lo,
                                                 const RowFrags<M, D>* qf, f32x16 (*s)[KT]) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -265,7 +262,7 @@ struct Fwd16 {
       for (int rb = 0; rb < RB; ++rb) s[rb][kt] = zero16();
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const frag A = ld_row<M>(smem + KOFF + 32 * kt * L::PITCH, lo.row[st]);
+        const frag A = ld_row<M>(K + 32 * kt * L::PITCH, lo.row[st]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) s[rb][kt] = M::mma(A, qf[rb].f[st], s[rb][kt]);
       }
@@ -308,8 +305,7 @@ struct Fwd16 {
 
   // P = 2^(c s - m), rounded to the working type, and O^T += V^T P^T, for
   // every row block.
-  template <int VOFF>
-  static __device__ __forceinline__ void softmax_pv(const T* smem, const LdsOffsets<M, D>& lo,
+  static __device__ __forceinline__ void softmax_pv(const T* V, const LdsOffsets<M, D>& lo,
                                                     const f32x16 (*s)[KT], f32x16 (*acc)[DVT], const float* m,
                                                     float c, float* l) {
     float nm[RB], ls[RB];
@@ -334,7 +330,7 @@ struct Fwd16 {
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const T* vb = smem + VOFF + (32 * kt + 16 * st) * L::PITCH;
+        const T* vb = V + (32 * kt + 16 * st) * L::PITCH;
 #pragma unroll
         for (int dt = 0; dt < DVT; ++dt) {
           const frag A = ld_tr<M>(vb, lo.tra[dt], lo.trb[dt]);
@@ -353,7 +349,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   using F = Fwd16<M, D, BN, RB>;
   using T = typename M::elem;
   constexpr int NT = NW * 64, WR = 32 * RB, BM = NW * WR, KT = F::KT, DVT = F::DVT;
-  __shared__ __attribute__((aligned(1024))) T smem[4 * F::TILE];
+  // One LDS array per stage and operand, so that the compiler can tell the
+  // tile being read from the tile being filled by direct loads and does not
+  // wait for those loads before every read.
+  __shared__ __attribute__((aligned(1024))) T k_s0[F::TILE], k_s1[F::TILE], v_s0[F::TILE], v_s1[F::TILE];
 
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -424,29 +423,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     DmaLane<T, D, BN, NW> kd, vd;
     kd.init(a.k.ss, wave, lane);
     vd.init(a.v.ss, wave, lane);
-    zero_unused_slots<T, D, 4 * BN, NT>(smem, tid);
+    zero_unused_slots<T, D, BN, NT>(k_s0, tid);
+    zero_unused_slots<T, D, BN, NT>(k_s1, tid);
+    zero_unused_slots<T, D, BN, NT>(v_s0, tid);
+    zero_unused_slots<T, D, BN, NT>(v_s1, tid);
     const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
-    auto dma = [&](int stage, int t) {
-      kd.issue(smem + F::kOff(stage), kp + (long long)t * BN * a.k.ss, a.k.ss, sk - t * BN, wave, lane);
-      vd.issue(smem + F::vOff(stage), vp + (long long)t * BN * a.v.ss, a.v.ss, sk - t * BN, wave, lane);
+    auto dma = [&](T* kb, T* vb, int t) {
+      kd.issue(kb, kp + (long long)t * BN * a.k.ss, a.k.ss, sk - t * BN, wave, lane);
+      vd.issue(vb, vp + (long long)t * BN * a.v.ss, a.v.ss, sk - t * BN, wave, lane);
     };
     // Step t: K_t and V_t sit in stage P = (t - t0) & 1; the copies of K_{t+1}
     // and V_{t+1} into stage P^1 fly during the step.
-    dma(0, t0);
+    dma(k_s0, v_s0, t0);
     __syncthreads();
     auto step = [&](auto parity, int t) {
       constexpr int Pq = decltype(parity)::value;
-      if (t + 1 <= t1) dma(Pq ^ 1, t + 1);
+      T* kc = Pq ? k_s1 : k_s0;
+      T* vc = Pq ? v_s1 : v_s0;
+      if (t + 1 <= t1) dma(Pq ? k_s0 : k_s1, Pq ? v_s0 : v_s1, t + 1);
       if (tw0 <= t && t <= tw1) {
         f32x16 s[RB][KT];
-        F::template scores<F::kOff(Pq)>(smem, lo, qf, s);
+        F::scores(kc, lo, qf, s);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int rb0 = iw0 + 32 * rb;
           const bool masked = classify(w, rb0, 32, (long long)t * BN, BN, sk) == kPartial;
           F::finalize(s[rb], masked, w, t * BN, rb0 + r, sk, c, m[rb], l[rb], acc[rb], g);
         }
-        F::template softmax_pv<F::vOff(Pq)>(smem, lo, s, acc, m, c, l);
+        F::softmax_pv(vc, lo, s, acc, m, c, l);
       }
       __syncthreads();
     };

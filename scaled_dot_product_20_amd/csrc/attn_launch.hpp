@@ -36,7 +36,8 @@ struct BwdArgs {
   ProblemArgs p;
   Operand q, k, v, o, dout, dq, dk, dv;
   const float* lse;
-  float* delta;
+  float* delta;  // workspace: Delta_i = sum_d dO_id O_id (written by the preprocess)
+  float* lse2;   // workspace: LSE_i * log2(e) (written by the preprocess)
 };
 
 // Steps of the backward, as a bit mask of `stages`; they run in this order.

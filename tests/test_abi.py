@@ -192,9 +192,9 @@ def test_bwd_validation_errors():
 def test_workspace_size():
     f = dense_params(B=2, H=3, S=100)
     p = bwd_params(f)
-    assert bd.lib().attn_bwd_workspace_size(ctypes.byref(p)) == ((2 * 3 * 100 * 4 + 255) // 256) * 256
+    assert bd.lib().attn_bwd_workspace_size(ctypes.byref(p)) == 2 * (((2 * 3 * 100 * 4 + 255) // 256) * 256)
     pk = bwd_params(packed_params(total_q=100, H=2))
-    assert bd.lib().attn_bwd_workspace_size(ctypes.byref(pk)) == 1024
+    assert bd.lib().attn_bwd_workspace_size(ctypes.byref(pk)) == 2 * 1024
     bad = bwd_params(dense_params())
     bad.fwd.version = 9
     assert bd.lib().attn_bwd_workspace_size(ctypes.byref(bad)) == 0
