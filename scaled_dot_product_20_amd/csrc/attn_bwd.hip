@@ -455,12 +455,8 @@ struct Dkdv16 {
           dp = M::mma(ld_row<M>(dOs + 32 * mq * L::PITCH, lo.row[st]), vf.f[st], dp);
         }
         if (masked) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int i = i0 + 32 * mq + acc_row(e, g);
-            const int diff = kj - i;
-            if (!(diff >= w.lo && diff <= w.hi && i < sq)) s[e] = -INFINITY;
-          }
+          const long long ib = (long long)i0 + 32 * mq + 4 * g;
+          mask_block(s, vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
         }
         float p[16], ds[16];
 #pragma unroll
@@ -515,14 +511,12 @@ struct Dkdv16 {
     for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #endif
     if (masked) {
+      // Query i = ib + r(e) sees key kj iff kj - hi <= i <= min(kj - lo, sq - 1).
 #pragma unroll
-      for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int i = i0 + 32 * mq + acc_row(e, g);
-          const int diff = kj - i;
-          if (!(diff >= w.lo && diff <= w.hi && i < sq)) s[mq][e] = -INFINITY;
-        }
+      for (int mq = 0; mq < MQ; ++mq) {
+        const long long ib = (long long)i0 + 32 * mq + 4 * g;
+        mask_block(s[mq], vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
+      }
     }
 #pragma unroll
     for (int mq = 0; mq < MQ; ++mq) {
@@ -774,12 +768,8 @@ struct Dq16 {
         dp = M::mma(ld_row<M>(Vs + 32 * kt * L::PITCH, lo.row[st]), dof.f[st], dp);
       }
       if (masked) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int j = j0 + 32 * kt + acc_row(e, g);
-          const int diff = j - qi;
-          if (!(diff >= w.lo && diff <= w.hi && j < sk)) s[e] = -INFINITY;
-        }
+        const long long jb = (long long)j0 + 32 * kt + 4 * g;
+        mask_block(s, vis_bits((long long)qi + w.lo - jb, min((long long)qi + w.hi, (long long)sk - 1) - jb));
       }
       float ds[16];
 #pragma unroll

@@ -457,3 +457,46 @@ struct DmaLane {
 };
 
 }  // namespace sdpa
+
+namespace sdpa {
+
+// Tiles t (of T rows or keys) whose start t*T lies in [lo, hi]: [t0, t1],
+// empty when t1 < t0.  Used for the range of tiles a window leaves whole,
+// computed once per wave so the hot loop tests two integers per tile.
+struct TileRange {
+  int t0, t1;
+};
+__host__ __device__ __forceinline__ TileRange tiles_starting_in(long long lo, long long hi, int T) {
+  const long long a = lo <= 0 ? 0 : (lo + T - 1) / T;
+  const long long b = hi < 0 ? -1 : hi / T;
+  return TileRange{(int)(a > 0x7fffffffLL ? 0x7fffffffLL : a), (int)(b > 0x7fffffffLL ? 0x7fffffffLL : b)};
+}
+
+}  // namespace sdpa
+
+namespace sdpa {
+
+// Masking of one 32 x 32 accumulator block without compares.  Element e of
+// half-wave g sits at row offset acc_row(e, g) = 8*(e/4) + 4*g + e%4 of the
+// block; with base = block row 0 + 4*g, the elements whose row offset
+// r(e) = 8*(e/4) + e%4 satisfies lo <= r(e) <= hi are visible.  vis_bits
+// turns [lo, hi] into a 32-bit mask (bit r visible); mask_block keeps the
+// visible scores and sets the others to -inf with a bit-select per element.
+__host__ __device__ __forceinline__ uint32_t vis_bits(long long lo, long long hi) {
+  const int a = (int)(lo < 0 ? 0 : (lo > 32 ? 32 : lo));
+  const int b = (int)(hi < -1 ? -1 : (hi > 31 ? 31 : hi));
+  const uint32_t below_a = a >= 32 ? 0xffffffffu : ((1u << a) - 1u);      // bits < a
+  const uint32_t upto_b = b >= 31 ? 0xffffffffu : ((1u << (b + 1)) - 1u);  // bits <= b
+  return upto_b & ~below_a;
+}
+
+__device__ __forceinline__ void mask_block(f32x16& s, uint32_t vis) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int bit = 8 * (e >> 2) + (e & 3);
+    const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)vis, bit, 1);  // all ones if visible
+    s[e] = __uint_as_float((__float_as_uint(s[e]) & keep) | (0xff800000u & ~keep));
+  }
+}
+
+}  // namespace sdpa

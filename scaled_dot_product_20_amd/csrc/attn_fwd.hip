@@ -276,14 +276,12 @@ struct Fwd16 {
   static __device__ __forceinline__ void finalize(f32x16* s, bool masked, Window w, int j0, int qi, int sk,
                                                   float c, float& m, float& l, f32x16* acc, int g) {
     if (masked) {
+      // Key j = jb + r(e) is visible iff qi + lo <= j <= min(qi + hi, sk - 1).
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int j = j0 + 32 * kt + acc_row(e, g);
-          const int diff = j - qi;
-          if (!(diff >= w.lo && diff <= w.hi && j < sk)) s[kt][e] = -INFINITY;
-        }
+      for (int kt = 0; kt < KT; ++kt) {
+        const long long jb = (long long)j0 + 32 * kt + 4 * g;
+        mask_block(s[kt], vis_bits((long long)qi + w.lo - jb, min((long long)qi + w.hi, (long long)sk - 1) - jb));
+      }
     }
     float smax = -INFINITY;
 #pragma unroll
@@ -397,6 +395,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       tw1 = (int)(a1 / BN);
     }
   }
+  // Tiles the window leaves whole for all of the wave's rows (and inside the
+  // sequence): no masking there.
+  const TileRange full = tiles_starting_in((long long)iw0 + WR - 1 + w.lo,
+                                           min((long long)iw0 + w.hi, (long long)sk - 1) - BN + 1, BN);
 
   const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
   RowFrags<M, D> qf[RB];
@@ -444,10 +446,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       if (tw0 <= t && t <= tw1) {
         f32x16 s[RB][KT];
         F::scores(kc, lo, qf, s);
+        const bool masked = t < full.t0 || t > full.t1;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int rb0 = iw0 + 32 * rb;
-          const bool masked = classify(w, rb0, 32, (long long)t * BN, BN, sk) == kPartial;
           F::finalize(s[rb], masked, w, t * BN, rb0 + r, sk, c, m[rb], l[rb], acc[rb], g);
         }
         F::softmax_pv(vc, lo, s, acc, m, c, l);

@@ -1,13 +1,27 @@
 // Host-side harness over the index helpers the kernels use (window bounds,
-// tile classification, XCD block remap, operand permutations).  Built with
-// hipcc for the host only; no kernel is launched.
+// tile classification, the per-wave range of unmasked tiles, the visibility
+// bit masks, XCD block remap, operand permutations).  Built with hipcc for
+// the host only; no kernel is launched.
+#include <algorithm>
 #include <cstdio>
+#include <cstring>
 #include <vector>
 
 #include "attn_device.hpp"
 
 int main(int argc, char** argv) {
   using namespace sdpa;
+  if (argc > 1 && strcmp(argv[1], "vis") == 0) {
+    // Lines "sq sk wl wr diag qi jb": the 32-bit mask of keys jb .. jb+31
+    // visible to query qi, as the forward and dQ kernels build it.
+    int sq, sk, wl, wr, diag, qi;
+    long long jb;
+    while (scanf("%d %d %d %d %d %d %lld", &sq, &sk, &wl, &wr, &diag, &qi, &jb) == 7) {
+      const Window w = seq_window(wl, wr, diag, sq, sk);
+      printf("%u\n", vis_bits((long long)qi + w.lo - jb, std::min((long long)qi + w.hi, (long long)sk - 1) - jb));
+    }
+    return 0;
+  }
   // 1. xcd_remap is a bijection of [0, n).
   for (int n = 1; n <= 3000; ++n) {
     std::vector<int> seen(n, 0);
@@ -28,7 +42,32 @@ int main(int argc, char** argv) {
         return 1;
       }
   printf("perm_ok\n");
-  // 3. classify rectangles read from stdin: sq sk wl wr diag i0 nr j0 nc
+  // 3. The per-wave range of unmasked tiles equals the tiles classify()
+  //    calls FULL, for waves of WR rows and tiles of BN keys.
+  {
+    const int INF = kWindowInf;
+    const int wls[] = {INF, 0, 1, 5, 37, -3, 64, 100}, wrs[] = {INF, 0, 2, 9, -2, 70};
+    for (int sq : {1, 17, 64, 65, 130, 300})
+      for (int sk : {1, 31, 64, 65, 129, 300})
+        for (int wl : wls)
+          for (int wr : wrs)
+            for (int diag = 0; diag < 2; ++diag) {
+              const Window w = seq_window(wl, wr, diag, sq, sk);
+              for (int BN : {32, 64, 128})
+                for (int WR : {32, 64})
+                  for (int iw0 = 0; iw0 < sq; iw0 += WR) {
+                    const TileRange full = tiles_starting_in(
+                        (long long)iw0 + WR - 1 + w.lo, std::min((long long)iw0 + w.hi, (long long)sk - 1) - BN + 1, BN);
+                    for (int t = 0; t * BN < sk; ++t)
+                      if ((classify(w, iw0, WR, (long long)t * BN, BN, sk) == kFull) != (t >= full.t0 && t <= full.t1)) {
+                        printf("full_fail %d %d %d %d %d %d %d %d %d\n", sq, sk, wl, wr, diag, BN, WR, iw0, t);
+                        return 1;
+                      }
+                  }
+            }
+  }
+  printf("full_ok\n");
+  // 4. classify rectangles read from stdin: sq sk wl wr diag i0 nr j0 nc
   int sq, sk, wl, wr, diag, nr, nc;
   long long i0, j0;
   while (scanf("%d %d %d %d %d %lld %d %lld %d", &sq, &sk, &wl, &wr, &diag, &i0, &nr, &j0, &nc) ==

@@ -27,9 +27,34 @@ def harness(tmp_path_factory):
     return exe
 
 
-def test_remap_and_permutation(harness):
+def test_remap_permutation_and_full_range(harness):
     out = subprocess.run([harness], input=b"", capture_output=True, check=True).stdout.decode()
-    assert "remap_ok" in out and "perm_ok" in out
+    assert "remap_ok" in out and "perm_ok" in out and "full_ok" in out
+
+
+def test_visibility_bits_against_oracle(harness):
+    """Bit r of the kernels' mask for (query qi, key block jb) is set iff key
+    jb + r is visible to qi under the oracle's predicate."""
+    rng = np.random.default_rng(5)
+    cases = []
+    for _ in range(2000):
+        sq, sk = (int(x) for x in rng.integers(1, 80, size=2))
+        wl = INF if rng.random() < 0.25 else int(rng.integers(-20, 21))
+        wr = INF if rng.random() < 0.25 else int(rng.integers(-20, 21))
+        diag = int(rng.integers(0, 2))
+        qi = int(rng.integers(0, sq))
+        jb = int(rng.integers(0, sk))
+        cases.append((sq, sk, wl, wr, diag, qi, jb))
+    text = "\n".join(" ".join(str(x) for x in c) for c in cases) + "\n"
+    out = subprocess.run([harness, "vis"], input=text.encode(), capture_output=True, check=True).stdout.decode()
+    masks = [int(x) for x in out.split()]
+    assert len(masks) == len(cases)
+    for c, mask in zip(cases, masks):
+        sq, sk, wl, wr, diag, qi, jb = c
+        d = "bottom_right" if diag else "top_left"
+        for r in range(32):
+            want = jb + r < sk and orc.visible(qi, jb + r, sq, sk, wl, wr, d)
+            assert bool(mask >> r & 1) == want, (c, r)
 
 
 def test_classify_sound_against_oracle(harness):
@@ -46,7 +71,7 @@ def test_classify_sound_against_oracle(harness):
         cases.append((sq, sk, wl, wr, diag, i0, nr, j0, nc))
     text = "\n".join(" ".join(str(x) for x in c) for c in cases) + "\n"
     out = subprocess.run([harness], input=text.encode(), capture_output=True, check=True).stdout.decode()
-    classes = [int(x) for x in out.split()[2:]]
+    classes = [int(x) for x in out.split()[3:]]
     assert len(classes) == len(cases)
     mats = {}
     for c, cls in zip(cases, classes):
