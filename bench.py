@@ -43,7 +43,8 @@ PEAK_HBM = 8000.0       # GB/s
 DEFAULT_WORKLOAD = "long_6630"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dkdv_traffic_long_6630.txt")
 KERNEL_SOURCES = ["scaled_dot_product_20_amd/csrc/attn_bwd.hip",
-                  "scaled_dot_product_20_amd/csrc/attn_device.hpp"]
+                  "scaled_dot_product_20_amd/csrc/attn_device.hpp",
+                  "scaled_dot_product_20_amd/csrc/attn_launch.hpp"]
 
 
 def log(*a):
@@ -266,13 +267,15 @@ def main():
         dk_ms = per_kernel["bwd_dkdv"]
         ach = dkdv_flop / dk_ms / 1e9
         traffic = read_traffic(W.name) if dname == "bf16" else None
-        out["roofline"] = {"kernel": "attn_bwd_dkdv_kernel", "bound": "mfma", "achieved": round(ach, 2),
+        kname = "attn_bwd_dkdv_kernel" if dtype == torch.float32 else "attn_bwd_dkdv16_kernel"
+        out["roofline"] = {"kernel": kname, "bound": "mfma", "achieved": round(ach, 2),
                            "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                            "traffic": traffic, "avg_ms": round(dk_ms, 4),
                            "algorithmic": f"8*D FLOP per visible pair x {pairs} pairs"}
     else:
         ach = fwd_flop / fwd_ms / 1e9
-        out["roofline"] = {"kernel": "attn_fwd_kernel", "bound": "mfma", "achieved": round(ach, 2),
+        kname = "attn_fwd_kernel" if dtype == torch.float32 else "attn_fwd16_kernel"
+        out["roofline"] = {"kernel": kname, "bound": "mfma", "achieved": round(ach, 2),
                            "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                            "traffic": None, "avg_ms": round(fwd_ms, 4),
                            "algorithmic": f"4*D FLOP per visible pair x {pairs} pairs"}
