@@ -35,8 +35,9 @@
  *    call (null required pointer, version or flags mismatch, negative or
  *    zero sizes where a size is needed, unit-stride or 16-byte alignment
  *    violated, workspace too small), hipErrorNotSupported for a well-formed
- *    call outside the built set (head_dim not in {64, 80, 128}), or the HIP
- *    error of the launch.  Validation makes no HIP call.  The contents of
+ *    call outside the built set (head_dim not in {64, 80, 128}; for fp16 and
+ *    bf16, a q, k, v or dout row stride so large that 63 strides plus one
+ *    row reach 2 GiB), or the HIP error of the launch.  Validation makes no HIP call.  The contents of
  *    cu_seqlens arrays are a precondition (0 first, non-decreasing, last
  *    entry equal to total_q / total_k, every length <= the seqlen_q /
  *    seqlen_k maximum) and are not checked: reading them would need a sync.
@@ -140,8 +141,8 @@ hipError_t attn_bwd(const attn_bwd_params *p, hipStream_t stream);
  * or time them one by one.  Same parameters, validation and errors as
  * attn_bwd; each enqueues one kernel on `stream`.  They must run in this
  * order on one stream (or be ordered by events): attn_bwd_dkdv and
- * attn_bwd_dq read the Delta that attn_bwd_preprocess leaves in the
- * workspace, which must not be touched in between.
+ * attn_bwd_dq read the Delta and LSE log2(e) that attn_bwd_preprocess leaves
+ * in the workspace, which must not be touched in between.
  *   attn_bwd_preprocess: Delta_i = sum_d dO_id O_id and LSE_i log2(e) into
  *                        the workspace.
  *   attn_bwd_dkdv:       dK and dV, one workgroup per block of keys.

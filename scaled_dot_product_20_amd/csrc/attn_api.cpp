@@ -41,6 +41,14 @@ bool strides_ok(const int64_t* stride, int64_t esz, bool packed) {
   return true;
 }
 
+// The 16-bit kernels copy tiles of up to 64 rows with 32-bit byte offsets
+// from the tile's lowest row: 63 row strides plus one row must stay below
+// 2^31 bytes.
+bool tile_span_ok(const int64_t* stride, int64_t esz, int64_t d) {
+  const int64_t rs = std::llabs(stride[2]);
+  return rs <= ((int64_t)1 << 31) / 64 && (63 * rs + d) * esz < ((int64_t)1 << 31);
+}
+
 // Rows of the Q side / K side of the whole tensor.
 int64_t q_rows(const attn_fwd_params* p) {
   return p->layout == ATTN_THD ? p->total_q : (int64_t)p->seqlen_q;
@@ -82,6 +90,10 @@ hipError_t check_problem(const attn_fwd_params* p) {
       !strides_ok(p->v_stride, esz, packed) || !strides_ok(p->o_stride, esz, packed))
     return hipErrorInvalidValue;
   if (!head_dim_built(p->head_dim)) return hipErrorNotSupported;
+  if (p->dtype != ATTN_FP32 &&
+      (!tile_span_ok(p->q_stride, esz, p->head_dim) || !tile_span_ok(p->k_stride, esz, p->head_dim) ||
+       !tile_span_ok(p->v_stride, esz, p->head_dim)))
+    return hipErrorNotSupported;
   return hipSuccess;
 }
 
@@ -209,6 +221,7 @@ hipError_t attn_bwd_check(const attn_bwd_params* p) {
   if (!strides_ok(p->do_stride, esz, packed) || !strides_ok(p->dq_stride, esz, packed) ||
       !strides_ok(p->dk_stride, esz, packed) || !strides_ok(p->dv_stride, esz, packed))
     return hipErrorInvalidValue;
+  if (f->dtype != ATTN_FP32 && !tile_span_ok(p->do_stride, esz, f->head_dim)) return hipErrorNotSupported;
   const int64_t B = packed ? 1 : f->batch, H = f->heads, D = f->head_dim;
   const Extent outs[4] = {
       extent_of(p->dq, p->dq_stride, B, H, q_rows(f), D, esz, packed),

@@ -10,6 +10,7 @@
 // No atomics: every output element is summed by one lane in a fixed order,
 // so results are run-to-run identical.
 #include <type_traits>
+#include <utility>
 
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
@@ -427,6 +428,136 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 //   transposing reads of the same tiles.
 // Each wave visits only the query tiles that can see its keys; tiles cut
 // by the window have their scores set to -inf where masked.
+#ifndef BWD16_PIPE
+#define BWD16_PIPE 1
+#endif
+#ifndef BWD16_PD
+#define BWD16_PD 8
+#endif
+#ifndef BWD16_VG
+#define BWD16_VG 0
+#endif
+
+// One unmasked dK/dV tile of two 32-row slices as a single ordered stream of
+// products: S and dP of slice 0, S and dP of slice 1, dV and dK of slice 0,
+// dV and dK of slice 1.  Each product's LDS operand is read PD products
+// ahead, and the vector work of slice 0 (probabilities, dS, rounding) is
+// issued between the products of slice 1's S / dP, that of slice 1 between
+// slice 0's dV / dK, so the matrix cores are fed while it runs.
+template <typename M, int D>
+struct DkdvStream {
+  using T = typename M::elem;
+  using L = Swz<D>;
+  using frag = typename M::frag;
+  static constexpr int NS = D / 16, DVT = (D + 31) / 32;
+  static constexpr int NA = 2 * NS, NB = 4 * DVT;  // products per slice: S/dP, dV/dK
+  static constexpr int N = 2 * NA + 2 * NB;
+  static constexpr int PD = BWD16_PD;
+  static constexpr bool is_a(int i) { return i < 2 * NA; }
+  static constexpr int reads(int i) { return is_a(i) ? 1 : 2; }
+
+  const T* Qs;
+  const T* dOs;
+  const LdsOffsets<M, D>& lo;
+  const float* lse2s;
+  const float* dels;
+  const RowFrags<M, D>& kf;
+  const RowFrags<M, D>& vf;
+  f32x16* dk;
+  f32x16* dv;
+  float c;
+  bool masked;  // tile cut by the window or the sequence end
+  Window w;
+  int i0, kj, sq;
+  f32x16 s[2], dp[2];
+  frag pf[2][2], dsf[2][2];
+  frag buf[PD];
+
+  __device__ __forceinline__ frag load(int i) const {
+    if (is_a(i)) {
+      const int mq = i / NA, st = (i % NA) / 2;
+      return ld_row<M>(((i & 1) ? dOs : Qs) + 32 * mq * L::PITCH, lo.row[st]);
+    }
+    const int j = i - 2 * NA, mq = j / NB, st = (j % NB) / (2 * DVT), dt = (j % (2 * DVT)) / 2;
+    return ld_tr<M>(((j & 1) ? Qs : dOs) + (32 * mq + 16 * st) * L::PITCH, lo.tra[dt], lo.trb[dt]);
+  }
+  template <int I>
+  __device__ __forceinline__ void product(const frag& A) {
+    if constexpr (is_a(I)) {
+      constexpr int mq = I / NA, st = (I % NA) / 2;
+      if constexpr (I & 1)
+        dp[mq] = M::mma(A, vf.f[st], st == 0 ? zero16() : dp[mq]);
+      else
+        s[mq] = M::mma(A, kf.f[st], st == 0 ? zero16() : s[mq]);
+    } else {
+      constexpr int j = I - 2 * NA, mq = j / NB, st = (j % NB) / (2 * DVT), dt = (j % (2 * DVT)) / 2;
+      if constexpr (j & 1)
+        dk[dt] = M::mma(A, dsf[mq][st], dk[dt]);
+      else
+        dv[dt] = M::mma(A, pf[mq][st], dv[dt]);
+    }
+  }
+  // Query i = ib + r(e) sees key kj iff kj - hi <= i <= min(kj - lo, sq - 1).
+  template <int MQ>
+  __device__ __forceinline__ void mask() {
+    if (masked) {
+      const long long ib = (long long)i0 + 32 * MQ + 4 * (threadIdx.x >> 5 & 1);
+      mask_block(s[MQ], vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
+    }
+  }
+  // P = 2^(c s - LSE log2 e), dS = P (dP - Delta) of one slice, rounded.
+  template <int MQ>
+  __device__ __forceinline__ void softmax() {
+    float p[16], ds[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int il = 32 * MQ + 8 * q4 + 4 * (threadIdx.x >> 5 & 1);
+      const float4 ll = *reinterpret_cast<const float4*>(lse2s + il);
+      const float4 dd = *reinterpret_cast<const float4*>(dels + il);
+      const float lv[4] = {ll.x, ll.y, ll.z, ll.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = 4 * q4 + u;
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[MQ][e], c, -lv[u]));
+        ds[e] = p[e] * (dp[MQ][e] - dv4[u]);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      M::pack(&p[8 * st], pf[MQ][st]);
+      M::pack(&ds[8 * st], dsf[MQ][st]);
+    }
+  }
+  template <int I>
+  __device__ __forceinline__ void step() {
+    const frag A = buf[I % PD];
+    if constexpr (I + PD < N) buf[I % PD] = load(I + PD);
+    product<I>(A);
+    if constexpr (I == NA + 1) {
+      mask<0>();
+      softmax<0>();
+    }
+    if constexpr (I == 2 * NA + 1) {
+      mask<1>();
+      softmax<1>();
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I + PD < N) __builtin_amdgcn_sched_group_barrier(0x100, reads(I + PD), 0);
+    if constexpr (BWD16_VG > 0 && ((I > NA && I < 2 * NA) || (I > 2 * NA && I < 2 * NA + NB)))
+      __builtin_amdgcn_sched_group_barrier(0x002, BWD16_VG, 0);
+  }
+  template <int... Is>
+  __device__ __forceinline__ void all(std::integer_sequence<int, Is...>) {
+    (step<Is>(), ...);
+  }
+  __device__ __forceinline__ void run() {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) buf[i] = load(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+    all(std::make_integer_sequence<int, N>{});
+  }
+};
+
 template <typename M, int D, int BMQ, int ST, bool PHASED>
 struct Dkdv16 {
   using T = typename M::elem;
@@ -485,6 +616,11 @@ struct Dkdv16 {
           }
         }
       }
+      return;
+    }
+    if constexpr (BWD16_PIPE && MQ == 2) {
+      DkdvStream<M, D> ps{Qs, dOs, lo, lse2s, dels, kf, vf, dk, dv, c, masked, w, i0, kj, sq, {}, {}, {}, {}, {}};
+      ps.run();
       return;
     }
     f32x16 s[MQ], dp[MQ];
@@ -668,9 +804,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       qd.issue(qs[stage], qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
       dd.issue(ds_[stage], dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, wave, lane);
       if (lane < RW) {
-        const int ic = min(i0 + wave * RW + lane, sq - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(l2p + ic), (lds_void*)(ls[stage] + wave * RW), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(delp + ic), (lds_void*)(es[stage] + wave * RW), 4, 0, 0);
+        const int off = 4 * (min(i0 + wave * RW + lane, sq - 1) - i0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(l2p + i0), (lds_void*)(ls[stage] + wave * RW), 4, off, 0,
+                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(delp + i0), (lds_void*)(es[stage] + wave * RW), 4, off, 0,
+                                                 0, 0);
       }
     };
     issue(0, t0);

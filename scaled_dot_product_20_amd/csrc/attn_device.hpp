@@ -305,31 +305,7 @@ struct Swz {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Copies rows [0, ROWS) of a row-major global tile into a swizzled LDS tile
-// with direct global->LDS loads (16 bytes per lane, 64 lanes filling 1 KiB of
-// consecutive slots).  Rows at or beyond `nvalid` (>= 1) repeat row
-// nvalid-1, so every loaded value is a finite input value.  The loads are
-// asynchronous: a barrier after `s_waitcnt vmcnt(0)` publishes them.
-template <typename T, int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_tile(T* lds, const T* __restrict__ g, long long row_stride, int nvalid,
-                                         int wave, int lane) {
-  using L = Swz<D>;
-  constexpr int RPI = 64 / L::SLOTS;  // rows per instruction
-  constexpr int NI = ROWS / RPI;
-  static_assert(ROWS % RPI == 0, "tile rows");
-  const int rl = lane / L::SLOTS, slot = lane % L::SLOTS;
-#pragma unroll
-  for (int i = wave; i < NI; i += NW) {
-    const int row = i * RPI + rl;
-    const int c = slot ^ L::sigma(row);
-    const int src = row < nvalid ? row : nvalid - 1;
-    if (L::CH == L::SLOTS || c < L::CH)
-      __builtin_amdgcn_global_load_lds((const void*)(g + (long long)src * row_stride + c * 8),
-                                       (lds_void*)(lds + i * RPI * L::PITCH), 16, 0, 0);
-  }
-}
-
-// Zeroes the chunk slots of a tile that dma_tile never writes (head_dim 80).
+// Zeroes the chunk slots of a tile that DmaLane never writes (head_dim 80).
 template <typename T, int D, int ROWS, int NT>
 __device__ __forceinline__ void zero_unused_slots(T* lds, int tid) {
   using L = Swz<D>;
@@ -419,37 +395,59 @@ __device__ __forceinline__ typename M::frag ld_tr(const typename M::elem* lds, i
   return __builtin_bit_cast(typename M::frag, v);
 }
 
-// One lane's share of the direct loads that fill a ROWS-row swizzled tile
-// (see dma_tile), with the source offsets of full tiles precomputed.
+// Buffer resource for direct global->LDS loads at byte offsets from `base`:
+// raw (stride 0), range 2^31 - 1 bytes (callers keep every offset below
+// it), word 3 = 32-bit data format as the gfx9 family expects.  Loads
+// through a buffer resource are tracked by the compiler as vector-memory
+// loads only, so waits on LDS reads issued after them stay partial.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+// One lane's share of copying a ROWS-row tile into a swizzled LDS tile with
+// direct loads, NW waves splitting the 1 KiB instructions (64 lanes x 16
+// bytes, RPI rows each).  Byte offsets of the lane's chunks in a full tile
+// are computed once; they are taken from the tile's lowest-addressed row, so
+// a negative row stride works too.  Rows at or beyond `nvalid` (>= 1)
+// repeat row nvalid-1, so every loaded value is a finite input value.  The
+// loads are asynchronous: a barrier after `s_waitcnt vmcnt(0)` publishes
+// them.
 template <typename T, int D, int ROWS, int NW>
 struct DmaLane {
   using L = Swz<D>;
   static constexpr int RPI = 64 / L::SLOTS, NI = ROWS / RPI, PER = (NI + NW - 1) / NW;
   static_assert(ROWS % RPI == 0, "tile rows");
-  long long goff[PER];  // element offset of the lane's chunk in a full tile
+  int boff[PER];  // byte offset of the lane's chunk in a full tile
   static __device__ __forceinline__ int row_of(int u, int wave, int lane) {
     return (wave + u * NW) * RPI + lane / L::SLOTS;
   }
   static __device__ __forceinline__ int chunk_of(int row, int lane) { return (lane % L::SLOTS) ^ L::sigma(row); }
+  static __device__ __forceinline__ long long lowest(long long row_stride) {
+    return row_stride < 0 ? (long long)(ROWS - 1) * row_stride : 0;
+  }
   __device__ __forceinline__ void init(long long row_stride, int wave, int lane) {
+    const long long lo = lowest(row_stride);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int row = row_of(u, wave, lane);
-      goff[u] = (long long)row * row_stride + chunk_of(row, lane) * 8;
+      boff[u] = (int)(((long long)row * row_stride - lo) * (long long)sizeof(T)) + chunk_of(row, lane) * 16;
     }
   }
   // Copies the tile whose first row is g (rows >= nvalid repeat row nvalid-1).
   __device__ __forceinline__ void issue(T* lds, const T* __restrict__ g, long long row_stride, int nvalid,
                                         int wave, int lane) const {
+    const long long lo = lowest(row_stride);
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(g + lo);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int i = wave + u * NW;
       if (NI % NW == 0 || i < NI) {
         const int row = row_of(u, wave, lane);
         if (L::CH == L::SLOTS || chunk_of(row, lane) < L::CH) {
-          const T* src = nvalid >= ROWS ? g + goff[u]
-                                        : g + (long long)min(row, nvalid - 1) * row_stride + chunk_of(row, lane) * 8;
-          __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds + i * RPI * L::PITCH), 16, 0, 0);
+          const int off = nvalid >= ROWS ? boff[u]
+                                         : (int)(((long long)min(row, nvalid - 1) * row_stride - lo) *
+                                                 (long long)sizeof(T)) + chunk_of(row, lane) * 16;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + i * RPI * L::PITCH), 16, off, 0, 0, 0);
         }
       }
     }

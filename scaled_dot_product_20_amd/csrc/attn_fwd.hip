@@ -24,6 +24,7 @@
 // Epilogue: O = acc / l, LSE = ln(2) * (m + log2 l); rows with no visible key
 // get O = 0 and LSE = +inf.
 #include <type_traits>
+#include <utility>
 
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
@@ -485,6 +486,300 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
 }
 
+// ------------------------------------------------ 16-bit ping-pong kernel
+//
+// Eight waves, 32 query rows each, in two groups of four; waves w and w+4
+// share a SIMD.  Per key tile k a wave runs a matrix block M_k
+// (O^T += V^T P^T of tile k-1, then S^T = K Q^T of tile k) and a vector
+// block V_k (mask, row max, rescale, exp and rounding of P).  Group B runs
+// one block behind group A and a workgroup barrier closes every block, so on
+// each SIMD one wave keeps the matrix cores busy while the other works on
+// the vector units.  Group A copies the K tiles (K_{k+1} during M_k), group
+// B the V tiles (V_{k+1} during V_k, V_0 up front); two stages each, and
+// each group waits for its own copies at the barrier one block before the
+// first reader.
+#ifndef FWDPP_PD
+#define FWDPP_PD 4
+#endif
+#ifndef FWDPP_SGB
+#define FWDPP_SGB 1
+#endif
+template <typename M, int D, int BN>
+struct FwdPP {
+  using F = Fwd16<M, D, BN, 1>;
+  using T = typename M::elem;
+  using frag = typename M::frag;
+  static constexpr int KT = F::KT, DVT = F::DVT;
+  using Dma = DmaLane<T, D, BN, 4>;
+
+  struct Ctx {
+    T* ks[2];
+    T* vs[2];
+    const T* kp;
+    const T* vp;
+    long long kss, vss;
+    int t0, nt, tw0, tw1, sk, qi, gw, lane, g;
+    TileRange full;
+    Window w;
+    float c;
+  };
+
+  static constexpr int NPV = KT * 2 * DVT, NSC = KT * F::NS;
+  template <int KS, int B, int E>
+  struct Steps {
+    static constexpr int PD = FWDPP_PD < E - B ? FWDPP_PD : E - B;
+    static constexpr int reads(int i) { return i < NPV ? 2 : 1; }  // LDS instructions of step i
+    const Ctx& x;
+    const LdsOffsets<M, D>& lo;
+    const RowFrags<M, D>& qf;
+    frag (*pf)[2];
+    f32x16* acc;
+    f32x16* s;
+    frag buf[PD];
+
+    __device__ __forceinline__ frag load(int i) const {
+      if (i < NPV) {
+        const int kt = i / (2 * DVT), st = (i / DVT) % 2, dt = i % DVT;
+        return ld_tr<M>(x.vs[KS ^ 1] + (32 * kt + 16 * st) * F::L::PITCH, lo.tra[dt], lo.trb[dt]);
+      }
+      const int j = i - NPV, kt = j / F::NS, st = j % F::NS;
+      return ld_row<M>(x.ks[KS] + 32 * kt * F::L::PITCH, lo.row[st]);
+    }
+    template <int I>
+    __device__ __forceinline__ void step() {
+      const frag A = buf[(I - B) % PD];
+      if constexpr (I + PD < E) buf[(I - B) % PD] = load(I + PD);
+      if constexpr (I < NPV) {
+        constexpr int kt = I / (2 * DVT), st = (I / DVT) % 2, dt = I % DVT;
+        acc[dt] = M::mma(A, pf[kt][st], acc[dt]);
+      } else {
+        constexpr int j = I - NPV, kt = j / F::NS, st = j % F::NS;
+        s[kt] = M::mma(A, qf.f[st], st == 0 ? zero16() : s[kt]);
+      }
+#if FWDPP_SGB
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (I + PD < E) __builtin_amdgcn_sched_group_barrier(0x100, reads(I + PD), 0);
+#endif
+    }
+    template <int... Is>
+    __device__ __forceinline__ void all(std::integer_sequence<int, Is...>) {
+      (step<B + Is>(), ...);
+    }
+    __device__ __forceinline__ void run() {
+#pragma unroll
+      for (int i = 0; i < PD; ++i) buf[i] = load(B + i);
+#if FWDPP_SGB
+      constexpr int PRO = (B + PD <= NPV ? 2 * PD : (B >= NPV ? PD : 2 * (NPV - B) + (B + PD - NPV)));
+      __builtin_amdgcn_sched_group_barrier(0x100, PRO, 0);
+#endif
+      all(std::make_integer_sequence<int, E - B>{});
+    }
+  };
+  // Matrix steps i in [B, E) of one block: steps below NPV are
+  // O^T += V^T P^T (V of the previous tile, stage KS^1), the rest
+  // S^T = K Q^T (K stage KS).  The LDS operands run PD steps ahead of the
+  // MFMAs.
+  template <int KS, int B, int E>
+  static __device__ __forceinline__ void mma_steps(const Ctx& x, const LdsOffsets<M, D>& lo, const RowFrags<M, D>& qf,
+                                                   frag (*pf)[2], f32x16* acc, f32x16* s) {
+    Steps<KS, B, E> st{x, lo, qf, pf, acc, s, {}};
+    st.run();
+  }
+
+  template <int GRP>
+  static __device__ __forceinline__ void run(const Ctx& x, const LdsOffsets<M, D>& lo, const Dma& dma,
+                                             const RowFrags<M, D>* qf, float& m, float& l, f32x16* acc) {
+    f32x16 s[1][KT];
+    frag pf[KT][2];
+    auto mine = [&](int kk) { return x.tw0 <= x.t0 + kk && x.t0 + kk <= x.tw1; };
+    auto copy = [&](T* dst, const T* base, long long ss, int kk) {
+      const int j0 = (x.t0 + kk) * BN;
+      dma.issue(dst, base + (long long)j0 * ss, ss, x.sk - j0, x.gw, x.lane);
+    };
+    // Barrier closing a block; `vm` also waits for this wave's copies.  The
+    // wait is an explicit s_waitcnt (vmcnt(0) lgkmcnt(0)) that the compiler
+    // keeps and accounts for; the asm barrier keeps memory accesses on
+    // their side of it.
+    auto barrier = [&](auto vm) {
+      if constexpr (decltype(vm)::value) {
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        asm volatile("s_barrier" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    };
+    auto mblock = [&](auto kst, int kk) {
+      constexpr int KS = decltype(kst)::value;
+      if (GRP == 0 && kk + 1 < x.nt) copy(x.ks[KS ^ 1], x.kp, x.kss, kk + 1);
+      const bool pv = kk >= 1 && mine(kk - 1), sc = kk < x.nt && mine(kk);
+      if (pv) mma_steps<KS, 0, NPV>(x, lo, qf[0], pf, acc, s[0]);
+      if (sc) mma_steps<KS, NPV, NPV + NSC>(x, lo, qf[0], pf, acc, s[0]);
+      barrier(std::integral_constant<bool, GRP == 1>{});
+    };
+    auto vblock = [&](auto kst, int kk) {
+      constexpr int KS = decltype(kst)::value;
+      if (GRP == 1 && kk + 1 < x.nt) copy(x.vs[KS ^ 1], x.vp, x.vss, kk + 1);
+      if (mine(kk)) {
+        const int t = x.t0 + kk;
+        F::finalize(s[0], t < x.full.t0 || t > x.full.t1, x.w, t * BN, x.qi, x.sk, x.c, m, l, acc, x.g);
+        const float nm = m == -INFINITY ? 0.f : -m;
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          float e2[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            e2[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][kt][e], x.c, nm));
+            ls += e2[e];
+          }
+          M::pack(&e2[0], pf[kt][0]);
+          M::pack(&e2[8], pf[kt][1]);
+        }
+        l += ls;
+      }
+      barrier(std::integral_constant<bool, GRP == 0>{});
+    };
+    if constexpr (GRP == 1) {
+      copy(x.vs[0], x.vp, x.vss, 0);
+      barrier(std::false_type{});
+    }
+    int kk = 0;
+    for (; kk + 1 < x.nt; kk += 2) {
+      mblock(std::integral_constant<int, 0>{}, kk);
+      vblock(std::integral_constant<int, 0>{}, kk);
+      mblock(std::integral_constant<int, 1>{}, kk + 1);
+      vblock(std::integral_constant<int, 1>{}, kk + 1);
+    }
+    // M_nt: O^T += V^T P^T of the last tile, then (group A) the barrier of
+    // group B's last vector block.
+    if (kk < x.nt) {
+      mblock(std::integral_constant<int, 0>{}, kk);
+      vblock(std::integral_constant<int, 0>{}, kk);
+      if (mine(kk)) mma_steps<1, 0, NPV>(x, lo, qf[0], pf, acc, s[0]);
+    } else if (mine(kk - 1)) {
+      mma_steps<0, 0, NPV>(x, lo, qf[0], pf, acc, s[0]);
+    }
+    if constexpr (GRP == 0) barrier(std::false_type{});
+  }
+};
+
+template <typename M, int D, int BN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd16pp_kernel(FwdArgs a) {
+  using PP = FwdPP<M, D, BN>;
+  using F = typename PP::F;
+  using T = typename M::elem;
+  constexpr int NT = 512, BM = 256, DVT = F::DVT;
+  __shared__ __attribute__((aligned(1024))) T k_s0[F::TILE], k_s1[F::TILE], v_s0[F::TILE], v_s1[F::TILE];
+
+  const ProblemArgs& P = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+  const int nq = (int)(gridDim.x / (P.B * P.H));
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - (blk % nq);
+
+  long long q0 = 0, k0 = 0;
+  int sq = P.Sq, sk = P.Sk;
+  if (P.varlen) {
+    q0 = P.cu_q[b];
+    sq = P.cu_q[b + 1] - (int)q0;
+    k0 = P.cu_k[b];
+    sk = P.cu_k[b + 1] - (int)k0;
+  }
+  const int i0 = qb * BM;
+  if (i0 >= sq) return;
+  const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
+
+  const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
+  T* op = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + q0 * a.o.ss;
+  float* lp = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+
+  const int ilast = min(i0 + BM, sq) - 1;
+  const long long jlo = max(0LL, (long long)i0 + w.lo);
+  const long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
+  const bool block_empty = w.lo > w.hi || jlo > jhi;
+
+  const int iw0 = i0 + 32 * wave;
+  const bool wave_live = iw0 < sq;
+  const int qi = iw0 + r;
+
+  typename PP::Ctx x;
+  x.tw0 = 0x7fffffff;
+  x.tw1 = -1;
+  if (wave_live && w.lo <= w.hi) {
+    const long long a0 = max(0LL, (long long)iw0 + w.lo);
+    const long long a1 = min((long long)sk - 1, (long long)min(iw0 + 31, sq - 1) + w.hi);
+    if (a0 <= a1) {
+      x.tw0 = (int)(a0 / BN);
+      x.tw1 = (int)(a1 / BN);
+    }
+  }
+  x.full = tiles_starting_in((long long)iw0 + 31 + w.lo, min((long long)iw0 + w.hi, (long long)sk - 1) - BN + 1, BN);
+  x.c = fmaxf(fabsf(P.scale_log2), 1e-30f);
+  x.w = w;
+  x.sk = sk;
+  x.qi = qi;
+  x.lane = lane;
+  x.g = g;
+  x.gw = wave & 3;
+
+  RowFrags<M, D> qf[1];
+  qf[0].load(qp + (long long)qi * a.q.ss, wave_live && qi < sq, g);
+  if (P.scale_log2 < 0.f) qf[0].negate();
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[DVT];
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) acc[dt] = zero16();
+
+  if (!block_empty) {
+    LdsOffsets<M, D> lo;
+    lo.init(lane);
+    typename PP::Dma dma;
+    const bool grp_b = wave >= 4;
+    dma.init(grp_b ? a.v.ss : a.k.ss, x.gw, lane);
+    zero_unused_slots<T, D, BN, NT>(k_s0, tid);
+    zero_unused_slots<T, D, BN, NT>(k_s1, tid);
+    zero_unused_slots<T, D, BN, NT>(v_s0, tid);
+    zero_unused_slots<T, D, BN, NT>(v_s1, tid);
+    x.ks[0] = k_s0;
+    x.ks[1] = k_s1;
+    x.vs[0] = v_s0;
+    x.vs[1] = v_s1;
+    x.kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
+    x.vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
+    x.kss = a.k.ss;
+    x.vss = a.v.ss;
+    x.t0 = (int)(jlo / BN);
+    x.nt = (int)(jhi / BN) - x.t0 + 1;
+    if (!grp_b) dma.issue(k_s0, x.kp + (long long)x.t0 * BN * a.k.ss, a.k.ss, sk - x.t0 * BN, x.gw, lane);
+    __syncthreads();
+    if (grp_b)
+      PP::template run<1>(x, lo, dma, qf, m, l, acc);
+    else
+      PP::template run<0>(x, lo, dma, qf, m, l, acc);
+  }
+
+  if (wave_live) {
+    const float lt = halves_sum(l);
+    if (qi < sq) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      T* orow = op + (long long)qi * a.o.ss;
+#pragma unroll
+      for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * dt + 8 * q4 + 4 * g;
+          if (d < D)
+            store4<T>(orow + d, acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv, acc[dt][4 * q4 + 2] * inv,
+                      acc[dt][4 * q4 + 3] * inv);
+        }
+      if (g == 0) lp[qi] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+    }
+  }
+}
+
 // Workgroup shapes.  fp32 (register-staged kernel, tiles twice as large):
 // 4 waves, 64-key tiles.  16-bit, 64-key tiles: head_dim <= 80, 8 waves of
 // one 32-row block (two waves per SIMD); head_dim 128, FWD16_NW_BIG waves of
@@ -495,9 +790,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #ifndef FWD16_RB_BIG
 #define FWD16_RB_BIG 1
 #endif
+#ifndef FWD16_PP
+#define FWD16_PP 1
+#endif
 template <typename M, int D>
 struct FwdShape {
   static constexpr bool k16 = sizeof(typename M::elem) == 2;
+  static constexpr bool PP = k16 && FWD16_PP;  // ping-pong kernel built (8 waves, 256 rows)
   static constexpr bool big = D > 80;
   static constexpr int RB = k16 && big ? FWD16_RB_BIG : 1;
   static constexpr int NW = k16 ? (big ? FWD16_NW_BIG : 8) : 4;
@@ -505,21 +804,36 @@ struct FwdShape {
   static constexpr int WPE = RB >= 2 ? 1 : 2;  // waves per SIMD the registers allow
 };
 
+// The ping-pong kernel walks every key tile of its 256 rows in lock step, so
+// a narrow band (both sides finite, under 1024 keys wide) goes to the
+// 128-row kernel, which visits fewer tiles outside each wave's band.
+static bool wide_window(const ProblemArgs& p) {
+  if (p.wl == kWindowInf || p.wr == kWindowInf) return true;
+  return (long long)p.wl + (long long)p.wr + 1 >= 1024;
+}
+
 template <typename M, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NW = FwdShape<M, D>::NW, BN = FwdShape<M, D>::BN, BM = NW * 32 * FwdShape<M, D>::RB;
-  const long long nq = (a.p.Sq + BM - 1) / BM;
+  using S = FwdShape<M, D>;
+  constexpr int BN = S::BN;
+  const bool pp = S::PP && wide_window(a.p);
+  const int nw = pp ? 8 : S::NW, bm = nw * 32 * (pp ? 1 : S::RB);
+  const long long nq = (a.p.Sq + bm - 1) / bm;
   const long long nblk = nq * a.p.H * a.p.B;
   if (nblk == 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
   FwdArgs args = a;
   void* kargs[] = {&args};
   const void* fn;
-  if constexpr (FwdShape<M, D>::k16)
-    fn = reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, NW, BN, FwdShape<M, D>::RB, FwdShape<M, D>::WPE>);
-  else
-    fn = reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, NW, BN>);
-  return hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NW * 64), kargs, 0, stream);
+  if constexpr (S::k16) {
+    if (pp)
+      fn = reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, BN>);
+    else
+      fn = reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, S::NW, BN, S::RB, S::WPE>);
+  } else {
+    fn = reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, S::NW, BN>);
+  }
+  return hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(nw * 64), kargs, 0, stream);
 }
 
 template <typename M>

@@ -136,3 +136,14 @@ def test_zero_length_dense():
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.all(torch.isposinf(lse))
     say("zero-length keys ok")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("window,diag", [((1100, -40), "top_left"), ((-30, 1200), "bottom_right"),
+                                         ((700, 400), "bottom_right"), ((INF, 0), "bottom_right")])
+def test_wide_windows(D, window, diag):
+    """Bands at least 1024 keys wide, which run on the 256-row forward kernel:
+    tiles cut by the band on both sides, waves whose band misses whole tiles,
+    ragged ends on both axes."""
+    Case(B=1, H=2, Sq=1300, Sk=1500, D=D, window=window, diag=diag, seed=400 + D).check()
+    Case(B=1, H=1, Sq=1700, Sk=1100, D=D, dtype=torch.float16, window=window, diag=diag, seed=500 + D).check()
