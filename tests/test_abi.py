@@ -154,6 +154,27 @@ def test_fwd_validation_strides_and_aliasing():
     assert fcheck(p) == INVALID
 
 
+def test_tile_span_limit():
+    """The 16-bit kernels address a 64-row tile with 32-bit byte offsets, so a
+    row stride whose 63 steps plus one row reach 2 GiB is not supported there;
+    fp32 takes the register-staged path and accepts it."""
+    def with_k_stride(rs, dtype, bwd=False):
+        p = dense_params(B=1, H=1, D=64, dtype=dtype)
+        p.k = addr(20)  # far from the other operands
+        p.k_stride = bd._I64x3(64 * rs, 64 * rs, rs)
+        return bcheck(bwd_params(p)) if bwd else fcheck(p)
+    below, at = 17_043_512, 17_043_520  # (63 * rs + 64) * 2 bytes: just below / at 2^31
+    for dt in (bd.BF16, bd.FP16):
+        assert with_k_stride(below, dt) == OK
+        assert with_k_stride(at, dt) == NOTSUP
+        assert with_k_stride(at, dt, bwd=True) == NOTSUP
+    assert with_k_stride(at, bd.FP32) == OK
+    p = bwd_params(dense_params(B=1, H=1, D=64))
+    p.dout = addr(20)
+    p.do_stride = bd._I64x3(64 * at, 64 * at, at)
+    assert bcheck(p) == NOTSUP
+
+
 def test_packed_validation_errors():
     p = packed_params()
     p.cu_seqlens_k = None
