@@ -437,6 +437,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 #ifndef BWD16_VG
 #define BWD16_VG 0
 #endif
+#ifndef BWD16_SL1
+#define BWD16_SL1 16  // product after which slice 1's statistics are read
+#endif
 
 // One unmasked dK/dV tile of two 32-row slices as a single ordered stream of
 // products: S and dP of slice 0, S and dP of slice 1, dV and dK of slice 0,
@@ -472,6 +475,7 @@ struct DkdvStream {
   f32x16 s[2], dp[2];
   frag pf[2][2], dsf[2][2];
   frag buf[PD];
+  float4 st_l[2][4], st_d[2][4];  // LSE log2(e) and Delta of each slice's rows
 
   __device__ __forceinline__ frag load(int i) const {
     if (is_a(i)) {
@@ -505,15 +509,24 @@ struct DkdvStream {
       mask_block(s[MQ], vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
     }
   }
+  // Reads the statistics of one slice's rows (issued well before use, so
+  // their wait does not drain the operand reads queued behind them).
+  template <int MQ>
+  __device__ __forceinline__ void load_stats() {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int il = 32 * MQ + 8 * q4 + 4 * (threadIdx.x >> 5 & 1);
+      st_l[MQ][q4] = *reinterpret_cast<const float4*>(lse2s + il);
+      st_d[MQ][q4] = *reinterpret_cast<const float4*>(dels + il);
+    }
+  }
   // P = 2^(c s - LSE log2 e), dS = P (dP - Delta) of one slice, rounded.
   template <int MQ>
   __device__ __forceinline__ void softmax() {
     float p[16], ds[16];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int il = 32 * MQ + 8 * q4 + 4 * (threadIdx.x >> 5 & 1);
-      const float4 ll = *reinterpret_cast<const float4*>(lse2s + il);
-      const float4 dd = *reinterpret_cast<const float4*>(dels + il);
+      const float4 ll = st_l[MQ][q4], dd = st_d[MQ][q4];
       const float lv[4] = {ll.x, ll.y, ll.z, ll.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -533,6 +546,7 @@ struct DkdvStream {
     const frag A = buf[I % PD];
     if constexpr (I + PD < N) buf[I % PD] = load(I + PD);
     product<I>(A);
+    if constexpr (I == BWD16_SL1) load_stats<1>();
     if constexpr (I == NA + 1) {
       mask<0>();
       softmax<0>();
@@ -542,7 +556,7 @@ struct DkdvStream {
       softmax<1>();
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (I + PD < N) __builtin_amdgcn_sched_group_barrier(0x100, reads(I + PD), 0);
+    if constexpr (I + PD < N) __builtin_amdgcn_sched_group_barrier(0x100, reads(I + PD) + (I == BWD16_SL1 ? 8 : 0), 0);
     if constexpr (BWD16_VG > 0 && ((I > NA && I < 2 * NA) || (I > 2 * NA && I < 2 * NA + NB)))
       __builtin_amdgcn_sched_group_barrier(0x002, BWD16_VG, 0);
   }
@@ -551,9 +565,10 @@ struct DkdvStream {
     (step<Is>(), ...);
   }
   __device__ __forceinline__ void run() {
+    load_stats<0>();
 #pragma unroll
     for (int i = 0; i < PD; ++i) buf[i] = load(i);
-    __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, PD + 8, 0);
     all(std::make_integer_sequence<int, N>{});
   }
 };
@@ -877,6 +892,365 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
 }
 
+// ------------------------------------- 16-bit dK/dV, producer / consumer
+//
+// Eight waves for 128 keys.  Waves w and w+4 share a SIMD and own keys
+// 32w .. 32w+31 of the block: w is the producer, w+4 the consumer.  For
+// query tile t (64 rows), in one step between two barriers:
+//   producer: S^T = K Q^T; P^T = 2^(c S^T - LSE log2 e), 0 where masked;
+//             P^T to LDS in fp16; dV += P^T dO;
+//   consumer: dS^T = P^T o (dP^T - Delta) for tile t-1 (its P^T from LDS,
+//             dP^T kept from the previous step); dK += dS^T Q; then
+//             dP^T = V dO^T of tile t.
+// The consumer's vector work runs while the producer's S products run, the
+// producer's softmax while the consumer's dK products run.  Q, dO, LSE
+// log2(e) and Delta of tile t+1 are copied during step t (three stages: the
+// consumer still reads tile t-1), P^T of each step gets its own of three
+// buffers.  Each role needs only K or V and only dV or dK, so two waves fit
+// in one SIMD's registers.
+#ifndef BWD16_PC_PD
+#define BWD16_PC_PD 4
+#endif
+
+// Calls f(integral_constant<int, I>) for I = B .. E-1 in order.
+template <int B, class Fn, int... Is>
+__device__ __forceinline__ void static_for_impl(Fn&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, B + Is>{}), ...);
+}
+template <int B, int E, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  static_for_impl<B>(f, std::make_integer_sequence<int, E - B>{});
+}
+
+// Products B .. E-1 of a sequence, each with one LDS operand: load(i) reads
+// product i's operand PD products ahead, prod(i, A) issues it, after(i) runs
+// after it (vector work placed between products).
+template <int B, int E, int PD, class Load, class Prod, class After>
+__device__ __forceinline__ void mfma_stream(Load&& load, Prod&& prod, After&& after) {
+  constexpr int D = PD < E - B ? PD : E - B;
+  using frag = decltype(load(std::integral_constant<int, B>{}));
+  frag buf[D];
+  static_for<0, D>([&](auto i) { buf[i] = load(std::integral_constant<int, B + decltype(i)::value>{}); });
+  static_for<B, E>([&](auto i) {
+    constexpr int I = decltype(i)::value;
+    const frag A = buf[(I - B) % D];
+    if constexpr (I + D < E) buf[(I - B) % D] = load(std::integral_constant<int, I + D>{});
+    prod(i, A);
+    after(i);
+  });
+}
+
+template <typename M, int D>
+struct DkdvPC {
+  using T = typename M::elem;
+  using L = Swz<D>;
+  using frag = typename M::frag;
+  static constexpr int BMQ = 64, MQ = 2, NS = D / 16, DVT = (D + 31) / 32;
+  static constexpr int TILE = BMQ * L::PITCH;              // elements of one Q or dO tile
+  static constexpr int STAGE = 2 * TILE + 4 * BMQ * 4 / (int)sizeof(T);  // Q, dO, LSE log2 e, Delta
+  static constexpr int XFR = 4 * MQ * 2 * 64;              // fp16 x8 fragments of one P buffer
+  static constexpr int NA = MQ * NS, NB = MQ * 2 * DVT;    // row-read products, transposed-read products
+  static constexpr int PD = BWD16_PC_PD;
+
+  // fp16 copy of 8 probabilities (exactly the MFMA fragment for fp16 input).
+  static __device__ __forceinline__ f16x8 half8(const float* x, const frag& f) {
+    if constexpr (std::is_same<T, _Float16>::value) {
+      return f;
+    } else {
+      f16x8 h;
+      MmaF16::pack(x, h);
+      return h;
+    }
+  }
+  // Operand of row-read product i (< NA): rows 32 (i / NS) .. +31, K step i % NS.
+  static __device__ __forceinline__ frag row_op(const T* tile, const LdsOffsets<M, D>& lo, int i) {
+    return ld_row<M>(tile + 32 * (i / NS) * L::PITCH, lo.row[i % NS]);
+  }
+  // Operand of transposed product j (< NB): rows 32 mq + 16 h .. +15 with
+  // (mq, h, dt) = (j / (2 DVT), (j / DVT) % 2, j % DVT).
+  static __device__ __forceinline__ frag tr_op(const T* tile, const LdsOffsets<M, D>& lo, int j) {
+    const int dt = j % DVT;
+    return ld_tr<M>(tile + (32 * (j / (2 * DVT)) + 16 * ((j / DVT) % 2)) * L::PITCH, lo.tra[dt], lo.trb[dt]);
+  }
+
+  // Producer: S, P (kept rounded for dV, stored in fp16 for the consumer), dV.
+  static __device__ __forceinline__ void produce(const T* st, f16x8* xb, const LdsOffsets<M, D>& lo,
+                                                 const RowFrags<M, D>& kf, f32x16* dv, float c, bool masked,
+                                                 Window w, int i0, int kj, int sq, int kw, int lane, int g) {
+    const T* Qs = st;
+    const T* dOs = st + TILE;
+    const float* l2 = reinterpret_cast<const float*>(st + 2 * TILE);
+    f32x16 s[MQ];
+    frag pf[MQ][2];
+    auto softmax = [&]() {
+      if (masked) {
+        // Query i = ib + r(e) sees key kj iff kj - hi <= i <= min(kj - lo, sq - 1).
+#pragma unroll
+        for (int mq = 0; mq < MQ; ++mq) {
+          const long long ib = (long long)i0 + 32 * mq + 4 * g;
+          mask_block(s[mq], vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
+        }
+      }
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq) {
+        float p[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 ll = *reinterpret_cast<const float4*>(l2 + 32 * mq + 8 * q4 + 4 * g);
+          const float lv[4] = {ll.x, ll.y, ll.z, ll.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            p[4 * q4 + u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mq][4 * q4 + u], c, -lv[u]));
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          M::pack(&p[8 * h], pf[mq][h]);
+          xb[((kw * MQ + mq) * 2 + h) * 64 + lane] = half8(&p[8 * h], pf[mq][h]);
+        }
+      }
+    };
+    mfma_stream<0, NA + NB, PD>(
+        [&](auto i) { return decltype(i)::value < NA ? row_op(Qs, lo, decltype(i)::value)
+                                                     : tr_op(dOs, lo, decltype(i)::value - NA); },
+        [&](auto i, const frag& A) {
+          constexpr int I = decltype(i)::value;
+          if constexpr (I < NA) {
+            constexpr int mq = I / NS, k = I % NS;
+            s[mq] = M::mma(A, kf.f[k], k == 0 ? zero16() : s[mq]);
+          } else {
+            constexpr int j = I - NA, dt = j % DVT;
+            dv[dt] = M::mma(A, pf[j / (2 * DVT)][(j / DVT) % 2], dv[dt]);
+          }
+        },
+        [&](auto i) {
+          if constexpr (decltype(i)::value == NA - 1) softmax();
+        });
+  }
+
+  // Consumer: dS of the previous tile (stage sp, P buffer xb) and
+  // dK += dS^T Q (when FIN), then dP^T = V dO^T of the current tile (stage
+  // sc, when DP).
+  template <bool FIN, bool DP>
+  static __device__ __forceinline__ void consume(const T* sp, const f16x8* xb, const T* sc,
+                                                 const LdsOffsets<M, D>& lo, const RowFrags<M, D>& vf, f32x16* dp,
+                                                 f32x16* dk, int kw, int lane, int g) {
+    const T* Qp = sp;
+    const float* del = reinterpret_cast<const float*>(sp + 2 * TILE) + BMQ;
+    const T* dOs = sc + TILE;
+    frag dsf[MQ][2];
+    auto ds_all = [&]() {
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq) {
+        const f16x8 h0 = xb[((kw * MQ + mq) * 2 + 0) * 64 + lane], h1 = xb[((kw * MQ + mq) * 2 + 1) * 64 + lane];
+        float ds[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 dd = *reinterpret_cast<const float4*>(del + 32 * mq + 8 * q4 + 4 * g);
+          const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = 4 * q4 + u;
+            ds[e] = (float)(e < 8 ? h0[e] : h1[e - 8]) * (dp[mq][e] - dv4[u]);
+          }
+        }
+        M::pack(&ds[0], dsf[mq][0]);
+        M::pack(&ds[8], dsf[mq][1]);
+      }
+    };
+    constexpr int B = FIN ? 0 : NB, E = DP ? NB + NA : NB;
+    if constexpr (FIN) ds_all();
+    mfma_stream<B, E, PD>(
+        [&](auto i) { return decltype(i)::value < NB ? tr_op(Qp, lo, decltype(i)::value)
+                                                     : row_op(dOs, lo, decltype(i)::value - NB); },
+        [&](auto i, const frag& A) {
+          constexpr int I = decltype(i)::value;
+          if constexpr (I < NB) {
+            constexpr int dt = I % DVT;
+            dk[dt] = M::mma(A, dsf[I / (2 * DVT)][(I / DVT) % 2], dk[dt]);
+          } else {
+            constexpr int j = I - NB, mq = j / NS, k = j % NS;
+            dp[mq] = M::mma(A, vf.f[k], k == 0 ? zero16() : dp[mq]);
+          }
+        },
+        [&](auto) {});
+  }
+};
+
+template <typename M, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv16pc_kernel(BwdArgs a) {
+  using F = DkdvPC<M, D>;
+  using T = typename M::elem;
+  using DL = DmaLane<T, D, F::BMQ, 8>;
+  constexpr int NT = 512, BMQ = F::BMQ, DVT = F::DVT, BNK = 128, RW = BMQ / 8;
+  // One LDS array per stage ([Q | dO | LSE log2 e | Delta]) so that the
+  // compiler tells the tile being read from the tile being filled.
+  __shared__ __attribute__((aligned(1024))) T st0[F::STAGE], st1[F::STAGE], st2[F::STAGE];
+  __shared__ __attribute__((aligned(16))) f16x8 x0[F::XFR], x1[F::XFR], x2[F::XFR];
+
+  const ProblemArgs& P = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+  const bool prod = wave < 4;
+  const int kw = wave & 3;
+  const int nkb = (int)(gridDim.x / (P.B * P.H));
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = blk / nkb, h = bh % P.H, b = bh / P.H;
+  const int kb = blk % nkb;
+
+  long long q0 = 0, k0 = 0;
+  int sq = P.Sq, sk = P.Sk;
+  if (P.varlen) {
+    q0 = P.cu_q[b];
+    sq = P.cu_q[b + 1] - (int)q0;
+    k0 = P.cu_k[b];
+    sk = P.cu_k[b + 1] - (int)k0;
+  }
+  const int j0 = kb * BNK;
+  if (j0 >= sk) return;
+  const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
+
+  const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
+  const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
+  const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
+  const T* dop = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + q0 * a.dout.ss;
+  T* dkp = (T*)a.dk.ptr + b * a.dk.sb + h * a.dk.sh + k0 * a.dk.ss;
+  T* dvp = (T*)a.dv.ptr + b * a.dv.sb + h * a.dv.sh + k0 * a.dv.ss;
+  const float* l2p = a.lse2 + b * P.lse_sb + h * P.lse_sh + q0;
+  const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
+
+  const int jlast = min(j0 + BNK, sk) - 1;
+  const long long ilo = max(0LL, (long long)j0 - w.hi);
+  const long long ihi = min((long long)sq - 1, (long long)jlast - w.lo);
+  const bool block_empty = w.lo > w.hi || ilo > ihi;
+
+  const int jw0 = j0 + 32 * kw;
+  const bool wave_live = jw0 < sk;
+  const int kj = jw0 + r;
+  int tw0 = 0x7fffffff, tw1 = -1;
+  if (wave_live && w.lo <= w.hi) {
+    const long long a0 = max(0LL, (long long)jw0 - w.hi);
+    const long long a1 = min((long long)sq - 1, (long long)min(jw0 + 31, sk - 1) - w.lo);
+    if (a0 <= a1) {
+      tw0 = (int)(a0 / BMQ);
+      tw1 = (int)(a1 / BMQ);
+    }
+  }
+
+  // The producer holds its keys' K rows, the consumer their V rows.
+  RowFrags<M, D> kv;
+  kv.load(prod ? kp + (long long)kj * a.k.ss : vp + (long long)kj * a.v.ss, wave_live && kj < sk, g);
+  const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
+  if (prod && P.scale_log2 < 0.f) kv.negate();
+
+  f32x16 acc[DVT];  // producer: dV, consumer: dK
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) acc[dt] = zero16();
+
+  if (!block_empty) {
+    LdsOffsets<M, D> lo;
+    lo.init(lane);
+    DL qd, dd;
+    qd.init(a.q.ss, wave, lane);
+    dd.init(a.dout.ss, wave, lane);
+    T* const stg[3] = {st0, st1, st2};
+    f16x8* const xs[3] = {x0, x1, x2};
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      zero_unused_slots<T, D, BMQ, NT>(stg[u], tid);
+      zero_unused_slots<T, D, BMQ, NT>(stg[u] + F::TILE, tid);
+    }
+    const int t0 = (int)(ilo / BMQ), n = (int)(ihi / BMQ) - t0 + 1;
+    // Tile copies, all direct to LDS (rows past the sequence repeat its last
+    // row and are masked); every wave copies RW rows of the statistics.
+    auto issue = [&](T* dst, int t) {
+      const int i0 = t * BMQ;
+      qd.issue(dst, qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
+      dd.issue(dst + F::TILE, dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, wave, lane);
+      if (lane < RW) {
+        float* sts = reinterpret_cast<float*>(dst + 2 * F::TILE);
+        const int off = 4 * (min(i0 + wave * RW + lane, sq - 1) - i0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(l2p + i0), (lds_void*)(sts + wave * RW), 4, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(delp + i0), (lds_void*)(sts + BMQ + wave * RW), 4, off, 0,
+                                                 0, 0);
+      }
+    };
+    // End of a step: this wave's copies and LDS traffic are complete
+    // (explicit wait the compiler accounts for), then the workgroup barrier.
+    auto barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      asm volatile("s_barrier" ::: "memory");
+    };
+    auto mine = [&](int t) { return tw0 <= t && t <= tw1; };
+    auto masked_at = [&](int t) {
+      return classify(w, (long long)t * BMQ, BMQ, jw0, 32, sk) == kPartial || (t + 1) * BMQ > sq;
+    };
+    issue(st0, t0);
+    barrier();
+    // Step it (tile t0+it in stage it % 3): copies of the next tile, this
+    // role's work, barrier.  One loop per role, so that the consumer's dP^T
+    // is not carried through the producer's code.
+    auto run = [&](auto role) {
+      constexpr bool PROD = decltype(role)::value;
+      f32x16 dp[F::MQ];  // consumer: dP^T of the last tile
+      auto step = [&](auto sc, int it) {
+        constexpr int SI = decltype(sc)::value, SN = (SI + 1) % 3, SP = (SI + 2) % 3;
+        const int t = t0 + it;
+        if (it + 1 < n) issue(stg[SN], t + 1);
+        if constexpr (PROD) {
+          if (mine(t))
+            F::produce(stg[SI], xs[SI], lo, kv, acc, c, masked_at(t), w, t * BMQ, kj, sq, kw, lane, g);
+        } else {
+          if (it >= 1 && mine(t - 1))
+            F::template consume<true, false>(stg[SP], xs[SP], stg[SI], lo, kv, dp, acc, kw, lane, g);
+          if (mine(t)) F::template consume<false, true>(stg[SP], xs[SP], stg[SI], lo, kv, dp, acc, kw, lane, g);
+        }
+        barrier();
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      int it = 0;
+      for (; it + 3 <= n; it += 3) {
+        step(I0{}, it);
+        step(I1{}, it + 1);
+        step(I2{}, it + 2);
+      }
+      if (it < n) step(I0{}, it);
+      if (it + 1 < n) step(I1{}, it + 1);
+      // The consumer's dS / dK of the last tile.
+      if constexpr (!PROD) {
+        if (mine(t0 + n - 1)) {
+          const int sl = (n - 1) % 3;
+          if (sl == 0)
+            F::template consume<true, false>(st0, x0, st0, lo, kv, dp, acc, kw, lane, g);
+          else if (sl == 1)
+            F::template consume<true, false>(st1, x1, st1, lo, kv, dp, acc, kw, lane, g);
+          else
+            F::template consume<true, false>(st2, x2, st2, lo, kv, dp, acc, kw, lane, g);
+        }
+      }
+    };
+    if (prod)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+  }
+
+  if (wave_live && kj < sk) {
+    T* row = prod ? dvp + (long long)kj * a.dv.ss : dkp + (long long)kj * a.dk.ss;
+    const float sc = prod ? 1.f : P.scale;
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * dt + 8 * q4 + 4 * g;
+        if (d < D)
+          store4b<T>(row + d, acc[dt][4 * q4] * sc, acc[dt][4 * q4 + 1] * sc, acc[dt][4 * q4 + 2] * sc,
+                     acc[dt][4 * q4 + 3] * sc);
+      }
+  }
+}
+
 // ------------------------------------------------- 16-bit dQ kernel
 //
 // One workgroup = 32*NW queries; each wave keeps its 32 queries' Q and dO
@@ -1062,6 +1436,11 @@ struct BwdShape {
   static constexpr int NW_KV = 4, BMQ = k16 ? (D > 80 ? BWD16_BMQ_BIG : 64) : 32, WPE_KV = D > 80 ? 1 : 2;
   static constexpr int ST_KV = D > 80 ? BWD16_ST_BIG : 2;  // LDS stages of the dK/dV query tiles
   static constexpr int NW_Q = k16 ? BWD16_NWQ : 4, BN = k16 ? 64 : 32;
+#ifndef BWD16_PC
+#define BWD16_PC 1
+#endif
+  // dK/dV by producer / consumer wave pairs (128 keys per workgroup, as NW_KV).
+  static constexpr bool PC = k16 && D > 80 && BWD16_PC;
 };
 
 template <typename M, int D>
@@ -1095,11 +1474,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (nblk > 0) {
       const void* fn;
-      if constexpr (S::k16)
+      int threads = NW_KV * 64;
+      if constexpr (S::PC) {
+        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16pc_kernel<M, D>);
+        threads = 512;
+      } else if constexpr (S::k16) {
         fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV, S::ST_KV>);
-      else
+      } else {
         fn = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>);
-      err = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NW_KV * 64), kargs, 0, stream);
+      }
+      err = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(threads), kargs, 0, stream);
       if (err != hipSuccess) return err;
     }
   }
