@@ -75,9 +75,29 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def dkdv_kernel_name(dname: str, head_dim: int) -> str:
+    """The dK/dV kernel the library launches for this dtype and head_dim."""
+    if dname == "fp32":
+        return "attn_bwd_dkdv_kernel"
+    return "attn_bwd_dkdv16pc_kernel" if head_dim > 80 else "attn_bwd_dkdv16_kernel"
+
+
+def fwd_kernel_name(dname: str, window) -> str:
+    """The forward kernel the library launches: the 256-row ping-pong kernel
+    for 16-bit inputs unless both window sides are finite and the band is
+    under 1024 keys wide."""
+    if dname == "fp32":
+        return "attn_fwd_kernel"
+    inf = 2147483647
+    wl, wr = window
+    wide = wl == inf or wr == inf or wl + wr + 1 >= 1024
+    return "attn_fwd16pp_kernel" if wide else "attn_fwd16_kernel"
+
+
+def read_traffic(workload: str, kernel: str):
     """HBM bytes per dK/dV launch from the committed counter summary, or None
-    when there is none for this workload or the kernel changed since."""
+    when there is none for this workload and kernel or the kernel's sources
+    changed since."""
     if workload != DEFAULT_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -86,7 +106,7 @@ def read_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("source_sha256_16") != source_hash():
+    if vals.get("source_sha256_16") != source_hash() or vals.get("kernel") != kernel:
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -266,15 +286,15 @@ def main():
                       "frac_of_peak": round(bwd_flop / bwd_ms / 1e9 / peak, 4)}
         dk_ms = per_kernel["bwd_dkdv"]
         ach = dkdv_flop / dk_ms / 1e9
-        traffic = read_traffic(W.name) if dname == "bf16" else None
-        kname = "attn_bwd_dkdv_kernel" if dtype == torch.float32 else "attn_bwd_dkdv16_kernel"
+        kname = dkdv_kernel_name(dname, D)
+        traffic = read_traffic(W.name, kname) if dname == "bf16" else None
         out["roofline"] = {"kernel": kname, "bound": "mfma", "achieved": round(ach, 2),
                            "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                            "traffic": traffic, "avg_ms": round(dk_ms, 4),
                            "algorithmic": f"8*D FLOP per visible pair x {pairs} pairs"}
     else:
         ach = fwd_flop / fwd_ms / 1e9
-        kname = "attn_fwd_kernel" if dtype == torch.float32 else "attn_fwd16_kernel"
+        kname = fwd_kernel_name(dname, W.window)
         out["roofline"] = {"kernel": kname, "bound": "mfma", "achieved": round(ach, 2),
                            "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                            "traffic": None, "avg_ms": round(fwd_ms, 4),

@@ -1219,14 +1219,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (it + 1 < n) step(I1{}, it + 1);
       // The consumer's dS / dK of the last tile.
       if constexpr (!PROD) {
+        // No copy is in flight any more, so the stage can be picked at run time.
         if (mine(t0 + n - 1)) {
           const int sl = (n - 1) % 3;
-          if (sl == 0)
-            F::template consume<true, false>(st0, x0, st0, lo, kv, dp, acc, kw, lane, g);
-          else if (sl == 1)
-            F::template consume<true, false>(st1, x1, st1, lo, kv, dp, acc, kw, lane, g);
-          else
-            F::template consume<true, false>(st2, x2, st2, lo, kv, dp, acc, kw, lane, g);
+          const T* sp = sl == 0 ? st0 : (sl == 1 ? st1 : st2);
+          const f16x8* xp = sl == 0 ? x0 : (sl == 1 ? x1 : x2);
+          F::template consume<true, false>(sp, xp, sp, lo, kv, dp, acc, kw, lane, g);
         }
       }
     };
