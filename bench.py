@@ -10,10 +10,11 @@ stream so its own average duration is known.
 
 FLOPs are counted on visible (query, key) pairs only: forward 4*D per pair
 (Q K^T and P V), backward 10*D per pair (S recomputed once, dV, dP, dK, dQ).
-The roofline object reports the dominant kernel, the dK/dV kernel, against
-its own algorithmic work of 8*D FLOPs per visible pair (S, dV, dP, dK): the
-bf16/fp16 dense MFMA peak of 2516.6 TFLOP/s (256 CUs x 2.4 GHz x 4096
-FLOP/clk/CU).
+The roofline object reports the dominant launch, attn_bwd_dkdv_dq (at
+head_dim 128 one fused dK/dV + dQ kernel where the library takes that path),
+against its own algorithmic work of 14*D FLOPs per visible pair (S, dV, dP,
+dK for dK/dV; S, dP, dQ for dQ) and the bf16/fp16 dense MFMA peak of 2516.6
+TFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP/clk/CU).
 
 The CPU baseline is the fp64 oracle timed on this host on one (sequence,
 head) slice of the same workload, scaled to the same unit.
@@ -82,16 +83,34 @@ def dkdv_kernel_name(dname: str, head_dim: int) -> str:
     return "attn_bwd_dkdv16pc_kernel" if head_dim > 80 else "attn_bwd_dkdv16_kernel"
 
 
+def wide_band(window) -> bool:
+    """A band unbounded on one side or at least 1024 keys wide."""
+    inf = 2147483647
+    wl, wr = window
+    return wl == inf or wr == inf or wl + wr + 1 >= 1024
+
+
+def bwd_main_kernels(dname: str, head_dim: int, window, seqlen_q: int, heads: int, batch: int,
+                     cus: int) -> list:
+    """The kernels attn_bwd_dkdv_dq launches: the fused dK/dV + dQ grid for
+    16-bit head_dim 128 when the band is wide and a separate dQ grid (two
+    128-row workgroups per CU) would leave its last round at most half full,
+    else the dK/dV kernel then the dQ kernel."""
+    slots = 2 * cus
+    tail = (-(-seqlen_q // 128) * heads * batch) % slots if slots else 0
+    if dname != "fp32" and head_dim > 80 and wide_band(window) and 0 < tail and 2 * tail <= slots:
+        return ["attn_bwd_fused16_kernel"]
+    dq = "attn_bwd_dq_kernel" if dname == "fp32" else "attn_bwd_dq16_kernel"
+    return [dkdv_kernel_name(dname, head_dim), dq]
+
+
 def fwd_kernel_name(dname: str, window) -> str:
     """The forward kernel the library launches: the 256-row ping-pong kernel
     for 16-bit inputs unless both window sides are finite and the band is
     under 1024 keys wide."""
     if dname == "fp32":
         return "attn_fwd_kernel"
-    inf = 2147483647
-    wl, wr = window
-    wide = wl == inf or wr == inf or wl + wr + 1 >= 1024
-    return "attn_fwd16pp_kernel" if wide else "attn_fwd16_kernel"
+    return "attn_fwd16pp_kernel" if wide_band(window) else "attn_fwd16_kernel"
 
 
 def read_traffic(workload: str, kernel: str):
@@ -222,7 +241,7 @@ def main():
     D = W.head_dim
     fwd_flop = 4.0 * D * pairs
     bwd_flop = 10.0 * D * pairs
-    dkdv_flop = 8.0 * D * pairs
+    main_flop = 14.0 * D * pairs  # dK/dV (S, dV, dP, dK) and dQ (S, dP, dQ) as executed
 
     o, lse = bd.attn_fwd(q, k, v, **kw)
     fkw = dict(cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None)
@@ -233,9 +252,8 @@ def main():
         bp, keep = bd.prepare_bwd(do, q, k, v, o, lse, **kw)
     stream = torch.cuda.current_stream(dev)
     sid = stream.cuda_stream
-    kernels = ["fwd"] + (["bwd_preprocess", "bwd_dkdv", "bwd_dq"] if do_bwd else [])
-    entry = {"fwd": "attn_fwd", "bwd_preprocess": "attn_bwd_preprocess", "bwd_dkdv": "attn_bwd_dkdv",
-             "bwd_dq": "attn_bwd_dq"}
+    kernels = ["fwd"] + (["bwd_preprocess", "bwd_dkdv_dq"] if do_bwd else [])
+    entry = {"fwd": "attn_fwd", "bwd_preprocess": "attn_bwd_preprocess", "bwd_dkdv_dq": "attn_bwd_dkdv_dq"}
 
     def step(evs=None):
         for i, kname in enumerate(kernels):
@@ -281,17 +299,19 @@ def main():
                 "frac_of_peak": round(fwd_flop / fwd_ms / 1e9 / peak, 4)},
     }
     if do_bwd:
-        bwd_ms = per_kernel["bwd_preprocess"] + per_kernel["bwd_dkdv"] + per_kernel["bwd_dq"]
+        bwd_ms = per_kernel["bwd_preprocess"] + per_kernel["bwd_dkdv_dq"]
         out["bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / bwd_ms / 1e9, 2),
                       "frac_of_peak": round(bwd_flop / bwd_ms / 1e9 / peak, 4)}
-        dk_ms = per_kernel["bwd_dkdv"]
-        ach = dkdv_flop / dk_ms / 1e9
-        kname = dkdv_kernel_name(dname, D)
+        main_ms = per_kernel["bwd_dkdv_dq"]
+        ach = main_flop / main_ms / 1e9
+        knames = bwd_main_kernels(dname, D, W.window, W.seqlen_q, W.heads, W.batch,
+                                  torch.cuda.get_device_properties(dev).multi_processor_count)
+        kname = "+".join(knames)
         traffic = read_traffic(W.name, kname) if dname == "bf16" else None
         out["roofline"] = {"kernel": kname, "bound": "mfma", "achieved": round(ach, 2),
                            "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                           "traffic": traffic, "avg_ms": round(dk_ms, 4),
-                           "algorithmic": f"8*D FLOP per visible pair x {pairs} pairs"}
+                           "traffic": traffic, "avg_ms": round(main_ms, 4),
+                           "algorithmic": f"14*D FLOP per visible pair (S, dV, dP, dK; S, dP, dQ) x {pairs} pairs"}
     else:
         ach = fwd_flop / fwd_ms / 1e9
         kname = fwd_kernel_name(dname, W.window)

@@ -132,9 +132,10 @@ hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
 /* Backward: reads q, k, v, o, lse, dout; writes dq, dk, dv.  Enqueues, in
  * stream order, the row-sum preprocess Delta_i = sum_d dO_id O_id (the
  * "bwd_preprocess" of the AOTriton 0.14b release notes) into the workspace,
- * the per-key-block dK/dV kernel and the per-query-block dQ kernel (the
- * split backward, "triton_split" in the same notes).  The dK/dV and dQ
- * sums are computed without atomics: results are run-to-run identical. */
+ * then the per-key-block dK/dV work and the per-query-block dQ work (the
+ * split backward, "triton_split" in the same notes) as attn_bwd_dkdv_dq
+ * does.  The dK/dV and dQ sums are computed without atomics: results are
+ * run-to-run identical. */
 hipError_t attn_bwd(const attn_bwd_params *p, hipStream_t stream);
 
 /* The three steps of attn_bwd as separate calls, for callers that schedule
@@ -150,6 +151,17 @@ hipError_t attn_bwd(const attn_bwd_params *p, hipStream_t stream);
 hipError_t attn_bwd_preprocess(const attn_bwd_params *p, hipStream_t stream);
 hipError_t attn_bwd_dkdv(const attn_bwd_params *p, hipStream_t stream);
 hipError_t attn_bwd_dq(const attn_bwd_params *p, hipStream_t stream);
+
+/* dK, dV and dQ after attn_bwd_preprocess (same ordering rule as the two
+ * calls above).  Where the build has it (fp16 and bf16 at head_dim 128) and
+ * the problem gains from it (a band unbounded or at least 1024 keys wide,
+ * and a separate dQ grid that would leave its last round on the device's
+ * compute units at most half full), one kernel whose workgroups are dK/dV
+ * blocks first and dQ blocks after, so that dQ blocks fill the CUs the
+ * dK/dV grid leaves idle; otherwise the two kernels in order.  Same
+ * parameters, validation and errors as attn_bwd; results equal those of
+ * attn_bwd_dkdv then attn_bwd_dq. */
+hipError_t attn_bwd_dkdv_dq(const attn_bwd_params *p, hipStream_t stream);
 
 /* Workspace bytes attn_bwd needs for this problem: two fp32 values per query
  * row and head (Delta_i and LSE_i * log2(e), written by attn_bwd_preprocess

@@ -73,7 +73,7 @@ def lib():
         l = ctypes.CDLL(LIB_PATH)
         for name, ptype in (("attn_fwd", FwdParams), ("attn_bwd", BwdParams),
                             ("attn_bwd_preprocess", BwdParams), ("attn_bwd_dkdv", BwdParams),
-                            ("attn_bwd_dq", BwdParams)):
+                            ("attn_bwd_dq", BwdParams), ("attn_bwd_dkdv_dq", BwdParams)):
             f = getattr(l, name)
             f.argtypes = [ctypes.POINTER(ptype), ctypes.c_void_p]
             f.restype = ctypes.c_int
@@ -243,8 +243,9 @@ def prepare_bwd(dout, q, k, v, o, lse, *, scale=None, window=(WINDOW_INF, WINDOW
 
 def launch(name: str, params, stream: Optional[int] = None) -> None:
     """Call one C entry point (``attn_fwd``, ``attn_bwd``,
-    ``attn_bwd_preprocess``, ``attn_bwd_dkdv`` or ``attn_bwd_dq``) with
-    filled params on ``stream`` (default: torch's current stream)."""
+    ``attn_bwd_preprocess``, ``attn_bwd_dkdv``, ``attn_bwd_dq`` or
+    ``attn_bwd_dkdv_dq``) with filled params on ``stream`` (default: torch's
+    current stream)."""
     if stream is None:
         stream = torch.cuda.current_stream().cuda_stream
     rc = getattr(lib(), name)(ctypes.byref(params), ctypes.c_void_p(stream))

@@ -291,4 +291,8 @@ hipError_t attn_bwd_dq(const attn_bwd_params* p, hipStream_t stream) {
   return bwd_stages(p, sdpa::kStageDq, stream);
 }
 
+hipError_t attn_bwd_dkdv_dq(const attn_bwd_params* p, hipStream_t stream) {
+  return bwd_stages(p, sdpa::kStageDkDv | sdpa::kStageDq, stream);
+}
+
 }  // extern "C"

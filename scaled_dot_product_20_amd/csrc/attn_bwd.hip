@@ -908,6 +908,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 // consumer still reads tile t-1), P^T of each step gets its own of three
 // buffers.  Each role needs only K or V and only dV or dK, so two waves fit
 // in one SIMD's registers.
+// LDS of the 16-bit backward kernels that run 8-wave workgroups: three
+// stages of [Q | dO | LSE log2 e | Delta] (dK/dV) or [K | V] (dQ) and three
+// fp16 P buffers.  They are named at namespace scope so that the kernel
+// bodies refer to these objects directly: the compiler then knows every
+// access is to LDS, and which stage array a direct load fills.  Sized for
+// 64-row tiles of up to 128 columns of 16-bit elements.
+constexpr int kBwdStageBytes = 2 * 64 * 128 * 2 + 4 * 64 * 4;
+constexpr int kBwdXBytes = 4 * 2 * 2 * 64 * 16;
+__shared__ __attribute__((aligned(1024))) char g_bwd_st0[kBwdStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_bwd_st1[kBwdStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_bwd_st2[kBwdStageBytes];
+__shared__ __attribute__((aligned(16))) char g_bwd_x0[kBwdXBytes];
+__shared__ __attribute__((aligned(16))) char g_bwd_x1[kBwdXBytes];
+__shared__ __attribute__((aligned(16))) char g_bwd_x2[kBwdXBytes];
+
+// The kernel's BwdArgs argument, read in place from the kernel-argument
+// segment (a kernel whose first argument is BwdArgs).  Bodies shared by
+// several kernels take it this way, so no private copy of the struct is made.
+using KBwdArgs = const __attribute__((address_space(4))) BwdArgs;
+__device__ __forceinline__ KBwdArgs& kernel_bwd_args() {
+  return *(KBwdArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
 #ifndef BWD16_PC_PD
 #define BWD16_PC_PD 4
 #endif
@@ -930,8 +953,8 @@ __device__ __forceinline__ void mfma_stream(Load&& load, Prod&& prod, After&& af
   constexpr int D = PD < E - B ? PD : E - B;
   using frag = decltype(load(std::integral_constant<int, B>{}));
   frag buf[D];
-  static_for<0, D>([&](auto i) { buf[i] = load(std::integral_constant<int, B + decltype(i)::value>{}); });
-  static_for<B, E>([&](auto i) {
+  static_for<0, D>([&](auto i) __attribute__((always_inline)) { buf[i] = load(std::integral_constant<int, B + decltype(i)::value>{}); });
+  static_for<B, E>([&](auto i) __attribute__((always_inline)) {
     constexpr int I = decltype(i)::value;
     const frag A = buf[(I - B) % D];
     if constexpr (I + D < E) buf[(I - B) % D] = load(std::integral_constant<int, I + D>{});
@@ -949,6 +972,7 @@ struct DkdvPC {
   static constexpr int TILE = BMQ * L::PITCH;              // elements of one Q or dO tile
   static constexpr int STAGE = 2 * TILE + 4 * BMQ * 4 / (int)sizeof(T);  // Q, dO, LSE log2 e, Delta
   static constexpr int XFR = 4 * MQ * 2 * 64;              // fp16 x8 fragments of one P buffer
+  static_assert(STAGE * (int)sizeof(T) <= kBwdStageBytes && XFR * 16 <= kBwdXBytes, "LDS arrays");
   static constexpr int NA = MQ * NS, NB = MQ * 2 * DVT;    // row-read products, transposed-read products
   static constexpr int PD = BWD16_PC_PD;
 
@@ -982,7 +1006,7 @@ struct DkdvPC {
     const float* l2 = reinterpret_cast<const float*>(st + 2 * TILE);
     f32x16 s[MQ];
     frag pf[MQ][2];
-    auto softmax = [&]() {
+    auto softmax = [&]() __attribute__((always_inline)) {
       if (masked) {
         // Query i = ib + r(e) sees key kj iff kj - hi <= i <= min(kj - lo, sq - 1).
 #pragma unroll
@@ -1010,9 +1034,9 @@ struct DkdvPC {
       }
     };
     mfma_stream<0, NA + NB, PD>(
-        [&](auto i) { return decltype(i)::value < NA ? row_op(Qs, lo, decltype(i)::value)
+        [&](auto i) __attribute__((always_inline)) { return decltype(i)::value < NA ? row_op(Qs, lo, decltype(i)::value)
                                                      : tr_op(dOs, lo, decltype(i)::value - NA); },
-        [&](auto i, const frag& A) {
+        [&](auto i, const frag& A) __attribute__((always_inline)) {
           constexpr int I = decltype(i)::value;
           if constexpr (I < NA) {
             constexpr int mq = I / NS, k = I % NS;
@@ -1022,7 +1046,7 @@ struct DkdvPC {
             dv[dt] = M::mma(A, pf[j / (2 * DVT)][(j / DVT) % 2], dv[dt]);
           }
         },
-        [&](auto i) {
+        [&](auto i) __attribute__((always_inline)) {
           if constexpr (decltype(i)::value == NA - 1) softmax();
         });
   }
@@ -1038,7 +1062,7 @@ struct DkdvPC {
     const float* del = reinterpret_cast<const float*>(sp + 2 * TILE) + BMQ;
     const T* dOs = sc + TILE;
     frag dsf[MQ][2];
-    auto ds_all = [&]() {
+    auto ds_all = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int mq = 0; mq < MQ; ++mq) {
         const f16x8 h0 = xb[((kw * MQ + mq) * 2 + 0) * 64 + lane], h1 = xb[((kw * MQ + mq) * 2 + 1) * 64 + lane];
@@ -1060,9 +1084,9 @@ struct DkdvPC {
     constexpr int B = FIN ? 0 : NB, E = DP ? NB + NA : NB;
     if constexpr (FIN) ds_all();
     mfma_stream<B, E, PD>(
-        [&](auto i) { return decltype(i)::value < NB ? tr_op(Qp, lo, decltype(i)::value)
+        [&](auto i) __attribute__((always_inline)) { return decltype(i)::value < NB ? tr_op(Qp, lo, decltype(i)::value)
                                                      : row_op(dOs, lo, decltype(i)::value - NB); },
-        [&](auto i, const frag& A) {
+        [&](auto i, const frag& A) __attribute__((always_inline)) {
           constexpr int I = decltype(i)::value;
           if constexpr (I < NB) {
             constexpr int dt = I % DVT;
@@ -1072,28 +1096,33 @@ struct DkdvPC {
             dp[mq] = M::mma(A, vf.f[k], k == 0 ? zero16() : dp[mq]);
           }
         },
-        [&](auto) {});
+        [&](auto) __attribute__((always_inline)) {});
   }
 };
 
+// The producer / consumer dK/dV workgroup's work: block hw of nblk, in the
+// namespace-scope LDS stages and P buffers.
 template <typename M, int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv16pc_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
   using F = DkdvPC<M, D>;
   using T = typename M::elem;
   using DL = DmaLane<T, D, F::BMQ, 8>;
   constexpr int NT = 512, BMQ = F::BMQ, DVT = F::DVT, BNK = 128, RW = BMQ / 8;
-  // One LDS array per stage ([Q | dO | LSE log2 e | Delta]) so that the
-  // compiler tells the tile being read from the tile being filled.
-  __shared__ __attribute__((aligned(1024))) T st0[F::STAGE], st1[F::STAGE], st2[F::STAGE];
-  __shared__ __attribute__((aligned(16))) f16x8 x0[F::XFR], x1[F::XFR], x2[F::XFR];
+  KBwdArgs& a = kernel_bwd_args();
+  T* const st0 = reinterpret_cast<T*>(g_bwd_st0);
+  T* const st1 = reinterpret_cast<T*>(g_bwd_st1);
+  T* const st2 = reinterpret_cast<T*>(g_bwd_st2);
+  f16x8* const x0 = reinterpret_cast<f16x8*>(g_bwd_x0);
+  f16x8* const x1 = reinterpret_cast<f16x8*>(g_bwd_x1);
+  f16x8* const x2 = reinterpret_cast<f16x8*>(g_bwd_x2);
 
-  const ProblemArgs& P = a.p;
+  const auto& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const bool prod = wave < 4;
   const int kw = wave & 3;
-  const int nkb = (int)(gridDim.x / (P.B * P.H));
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int nkb = nblk / (P.B * P.H);
+  const int blk = xcd_remap(hw, nblk);
   const int bh = blk / nkb, h = bh % P.H, b = bh / P.H;
   const int kb = blk % nkb;
 
@@ -1152,17 +1181,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     DL qd, dd;
     qd.init(a.q.ss, wave, lane);
     dd.init(a.dout.ss, wave, lane);
-    T* const stg[3] = {st0, st1, st2};
-    f16x8* const xs[3] = {x0, x1, x2};
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      zero_unused_slots<T, D, BMQ, NT>(stg[u], tid);
-      zero_unused_slots<T, D, BMQ, NT>(stg[u] + F::TILE, tid);
+    // Stage and P buffer u, chosen at compile time so that every LDS access
+    // names its own array.
+    auto stg = [&](auto u) __attribute__((always_inline)) -> T* {
+      constexpr int U = decltype(u)::value;
+      return U == 0 ? st0 : (U == 1 ? st1 : st2);
+    };
+    auto xs = [&](auto u) __attribute__((always_inline)) -> f16x8* {
+      constexpr int U = decltype(u)::value;
+      return U == 0 ? x0 : (U == 1 ? x1 : x2);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (T* st : {st0, st1, st2}) {
+      zero_unused_slots<T, D, BMQ, NT>(st, tid);
+      zero_unused_slots<T, D, BMQ, NT>(st + F::TILE, tid);
     }
     const int t0 = (int)(ilo / BMQ), n = (int)(ihi / BMQ) - t0 + 1;
     // Tile copies, all direct to LDS (rows past the sequence repeat its last
     // row and are masked); every wave copies RW rows of the statistics.
-    auto issue = [&](T* dst, int t) {
+    auto issue = [&](T* dst, int t) __attribute__((always_inline)) {
       const int i0 = t * BMQ;
       qd.issue(dst, qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
       dd.issue(dst + F::TILE, dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, wave, lane);
@@ -1176,12 +1215,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     // End of a step: this wave's copies and LDS traffic are complete
     // (explicit wait the compiler accounts for), then the workgroup barrier.
-    auto barrier = [&]() {
+    auto barrier = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(0x0070);
       asm volatile("s_barrier" ::: "memory");
     };
-    auto mine = [&](int t) { return tw0 <= t && t <= tw1; };
-    auto masked_at = [&](int t) {
+    auto mine = [&](int t) __attribute__((always_inline)) { return tw0 <= t && t <= tw1; };
+    auto masked_at = [&](int t) __attribute__((always_inline)) {
       return classify(w, (long long)t * BMQ, BMQ, jw0, 32, sk) == kPartial || (t + 1) * BMQ > sq;
     };
     issue(st0, t0);
@@ -1189,26 +1228,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // Step it (tile t0+it in stage it % 3): copies of the next tile, this
     // role's work, barrier.  One loop per role, so that the consumer's dP^T
     // is not carried through the producer's code.
-    auto run = [&](auto role) {
+    auto run = [&](auto role) __attribute__((always_inline)) {
       constexpr bool PROD = decltype(role)::value;
       f32x16 dp[F::MQ];  // consumer: dP^T of the last tile
-      auto step = [&](auto sc, int it) {
+      auto step = [&](auto sc, int it) __attribute__((always_inline)) {
         constexpr int SI = decltype(sc)::value, SN = (SI + 1) % 3, SP = (SI + 2) % 3;
+        using CI = std::integral_constant<int, SI>;
+        using CN = std::integral_constant<int, SN>;
+        using CP = std::integral_constant<int, SP>;
         const int t = t0 + it;
-        if (it + 1 < n) issue(stg[SN], t + 1);
+        if (it + 1 < n) issue(stg(CN{}), t + 1);
         if constexpr (PROD) {
           if (mine(t))
-            F::produce(stg[SI], xs[SI], lo, kv, acc, c, masked_at(t), w, t * BMQ, kj, sq, kw, lane, g);
+            F::produce(stg(CI{}), xs(CI{}), lo, kv, acc, c, masked_at(t), w, t * BMQ, kj, sq, kw, lane, g);
         } else {
           if (it >= 1 && mine(t - 1))
-            F::template consume<true, false>(stg[SP], xs[SP], stg[SI], lo, kv, dp, acc, kw, lane, g);
-          if (mine(t)) F::template consume<false, true>(stg[SP], xs[SP], stg[SI], lo, kv, dp, acc, kw, lane, g);
+            F::template consume<true, false>(stg(CP{}), xs(CP{}), stg(CI{}), lo, kv, dp, acc, kw, lane, g);
+          if (mine(t))
+            F::template consume<false, true>(stg(CP{}), xs(CP{}), stg(CI{}), lo, kv, dp, acc, kw, lane, g);
         }
         barrier();
       };
-      using I0 = std::integral_constant<int, 0>;
-      using I1 = std::integral_constant<int, 1>;
-      using I2 = std::integral_constant<int, 2>;
       int it = 0;
       for (; it + 3 <= n; it += 3) {
         step(I0{}, it);
@@ -1247,6 +1287,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                      acc[dt][4 * q4 + 3] * sc);
       }
   }
+}
+
+template <typename M, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv16pc_kernel(BwdArgs) {
+  dkdv_pc_body<M, D>(blockIdx.x, gridDim.x);
 }
 
 // ------------------------------------------------- 16-bit dQ kernel
@@ -1298,19 +1343,26 @@ struct Dq16 {
   }
 };
 
-template <typename M, int D, int NW, int BN, int WPE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dq16_kernel(BwdArgs a) {
+// The dQ workgroup's work: block hw of nblk (the block's place in its own
+// grid), K and V tiles of stage s in the first two namespace-scope LDS
+// stages ([K | V] each).
+template <typename M, int D, int NW, int BN>
+__device__ __forceinline__ void dq16_body(int hw, int nblk) {
   using F = Dq16<M, D, BN>;
   using T = typename M::elem;
   constexpr int NT = NW * 64, BM = NW * 32, DVT = F::DVT;
-  // One LDS array per stage and operand (see the dK/dV kernel).
-  __shared__ __attribute__((aligned(1024))) T k_s0[F::TILE], k_s1[F::TILE], v_s0[F::TILE], v_s1[F::TILE];
+  static_assert(2 * F::TILE * (int)sizeof(T) <= kBwdStageBytes, "K and V tiles fit a stage");
+  KBwdArgs& a = kernel_bwd_args();
+  T* const k_s0 = reinterpret_cast<T*>(g_bwd_st0);
+  T* const v_s0 = k_s0 + F::TILE;
+  T* const k_s1 = reinterpret_cast<T*>(g_bwd_st1);
+  T* const v_s1 = k_s1 + F::TILE;
 
-  const ProblemArgs& P = a.p;
+  const auto& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const int nq = (int)(gridDim.x / (P.B * P.H));
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int nq = nblk / (P.B * P.H);
+  const int blk = xcd_remap(hw, nblk);
   const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - (blk % nq);
 
@@ -1376,13 +1428,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     zero_unused_slots<T, D, BN, NT>(v_s0, tid);
     zero_unused_slots<T, D, BN, NT>(v_s1, tid);
     const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
-    auto dma = [&](T* kb, T* vb, int t) {
+    auto dma = [&](T* kb, T* vb, int t) __attribute__((always_inline)) {
       kd.issue(kb, kp + (long long)t * BN * a.k.ss, a.k.ss, sk - t * BN, wave, lane);
       vd.issue(vb, vp + (long long)t * BN * a.v.ss, a.v.ss, sk - t * BN, wave, lane);
     };
     dma(k_s0, v_s0, t0);
     __syncthreads();
-    auto step = [&](auto parity, int t) {
+    auto step = [&](auto parity, int t) __attribute__((always_inline)) {
       constexpr int Pq = decltype(parity)::value;
       if (t + 1 <= t1) dma(Pq ? k_s0 : k_s1, Pq ? v_s0 : v_s1, t + 1);
       if (tw0 <= t && t <= tw1) {
@@ -1412,6 +1464,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
 }
 
+template <typename M, int D, int NW, int BN, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dq16_kernel(BwdArgs) {
+  dq16_body<M, D, NW, BN>(blockIdx.x, gridDim.x);
+}
+
+// ------------------------------------------ 16-bit dK/dV + dQ in one grid
+//
+// Blocks [0, nkv) are producer / consumer dK/dV workgroups, the rest dQ
+// workgroups of 256 query rows (8 waves).  Both kinds need 8 waves and at
+// most the dK/dV LDS, so each CU holds one of either; with the longer dK/dV
+// blocks dispatched first, dQ blocks fill the CUs the last dK/dV round
+// leaves idle, and the dQ grid's own partial last round shrinks to a tail of
+// short blocks.  dQ's K / V stages live in the first two dK/dV stages.
+template <typename M, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_fused16_kernel(BwdArgs,
+                                                                                                        int nkv) {
+  const int hw = (int)blockIdx.x;
+  if (hw < nkv)
+    dkdv_pc_body<M, D>(hw, nkv);
+  else
+    dq16_body<M, D, 8, 64>(hw - nkv, (int)gridDim.x - nkv);
+}
+
 // ------------------------------------------------------------ launch
 
 // Workgroup shapes.  16-bit: dK/dV 4 waves (128 keys) over 64-row query
@@ -1436,6 +1511,9 @@ struct BwdShape {
   static constexpr int NW_Q = k16 ? BWD16_NWQ : 4, BN = k16 ? 64 : 32;
 #ifndef BWD16_PC
 #define BWD16_PC 1
+#endif
+#ifndef BWD16_FUSED
+#define BWD16_FUSED 1  // dK/dV and dQ requested together run as one grid
 #endif
   // dK/dV by producer / consumer wave pairs (128 keys per workgroup, as NW_KV).
   static constexpr bool PC = k16 && D > 80 && BWD16_PC;
@@ -1463,6 +1541,25 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
       err = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_pre_kernel<T, D>),
                             dim3((unsigned)nblk), dim3(256), pargs, 0, stream);
       if (err != hipSuccess) return err;
+    }
+  }
+  // 2 + 3 in one grid where the build has the fused kernel and it pays: a
+  // wide band (its dQ workgroups are 256 rows) and a separate dQ grid whose
+  // last round would be at most half full (2 workgroups of 128 rows per CU).
+  if constexpr (S::PC && BWD16_FUSED) {
+    const long long ndq4 = (a.p.Sq + NW_Q * 32 - 1) / (NW_Q * 32) * a.p.H * a.p.B;
+    const long long slots = 2LL * device_cu_count();
+    const long long tail = slots > 0 ? ndq4 % slots : 0;
+    if ((stages & kStageDkDv) && (stages & kStageDq) && wide_window(a.p) && tail > 0 && 2 * tail <= slots) {
+      const long long nkv = (a.p.Sk + 127) / 128 * a.p.H * a.p.B;
+      const long long ndq = (a.p.Sq + 255) / 256 * a.p.H * a.p.B;
+      if (nkv + ndq > 0x7fffffffLL) return hipErrorInvalidValue;
+      if (nkv > 0 && ndq > 0) {  // otherwise the separate kernels below write the zeros
+        int nk = (int)nkv;
+        void* fargs[] = {&args, &nk};
+        return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_fused16_kernel<M, D>),
+                               dim3((unsigned)(nkv + ndq)), dim3(512), fargs, 0, stream);
+      }
     }
   }
   // 2. dK, dV.

@@ -804,14 +804,6 @@ struct FwdShape {
   static constexpr int WPE = RB >= 2 ? 1 : 2;  // waves per SIMD the registers allow
 };
 
-// The ping-pong kernel walks every key tile of its 256 rows in lock step, so
-// a narrow band (both sides finite, under 1024 keys wide) goes to the
-// 128-row kernel, which visits fewer tiles outside each wave's band.
-static bool wide_window(const ProblemArgs& p) {
-  if (p.wl == kWindowInf || p.wr == kWindowInf) return true;
-  return (long long)p.wl + (long long)p.wr + 1 >= 1024;
-}
-
 template <typename M, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   using S = FwdShape<M, D>;

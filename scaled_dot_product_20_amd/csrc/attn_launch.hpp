@@ -43,6 +43,29 @@ struct BwdArgs {
 // Steps of the backward, as a bit mask of `stages`; they run in this order.
 constexpr int kStageDelta = 1, kStageDkDv = 2, kStageDq = 4, kStageAll = 7;
 
+// A band unbounded on one side or at least 1024 keys wide.  Kernels with
+// 256-row workgroups walk every key tile of their rows in lock step, so a
+// narrower band goes to kernels with smaller workgroups, which visit fewer
+// tiles outside each wave's band.
+inline bool wide_window(const ProblemArgs& p) {
+  constexpr int kInf = 2147483647;
+  if (p.wl == kInf || p.wr == kInf) return true;
+  return (long long)p.wl + (long long)p.wr + 1 >= 1024;
+}
+
+// Compute units of the current device (0 if unknown), read once per device.
+inline int device_cu_count() {
+  static int cache[64] = {};  // written once per device; racing writers store the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+  }
+  return v;
+}
+
 // dtype codes follow the C ABI: 0 fp32, 1 fp16, 2 bf16.
 hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, hipStream_t stream);

@@ -65,14 +65,14 @@ def test_full_size_sampled(name, dtype):
         okw.update(cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
     gq, gk, gv, gdo = (t.to(dev) for t in (q, k, v, do))
 
-    # The bench's launch sequence: attn_fwd, then the three backward steps.
+    # The bench's launch sequence: attn_fwd, the Delta preprocess, then dK/dV
+    # and dQ in one call (the fused grid where the library takes it).
     o, lse = bd.attn_fwd(gq, gk, gv, **kw)
     fkw = dict(cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None)
     fkw.update(kw)
     fp = bd.fwd_params(gq, gk, gv, o, lse, **fkw)
     bp, (dq, dk, dv, _ws) = bd.prepare_bwd(gdo, gq, gk, gv, o, lse, **kw)
-    for entry, params in (("attn_fwd", fp), ("attn_bwd_preprocess", bp), ("attn_bwd_dkdv", bp),
-                          ("attn_bwd_dq", bp)):
+    for entry, params in (("attn_fwd", fp), ("attn_bwd_preprocess", bp), ("attn_bwd_dkdv_dq", bp)):
         bd.launch(entry, params)
     torch.cuda.synchronize()
     for nm, t in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 from parity_util import INF, TOL, Case, max_err, say
+from scaled_dot_product_20_amd import binding as bd
 
 pytestmark = pytest.mark.gpu
 
@@ -147,3 +148,38 @@ def test_wide_windows(D, window, diag):
     ragged ends on both axes."""
     Case(B=1, H=2, Sq=1300, Sk=1500, D=D, window=window, diag=diag, seed=400 + D).check()
     Case(B=1, H=1, Sq=1700, Sk=1100, D=D, dtype=torch.float16, window=window, diag=diag, seed=500 + D).check()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("shape", ["dense", "dense_window", "packed", "d64"])
+def test_dkdv_dq_call_equals_separate_calls(dtype, shape):
+    """attn_bwd_dkdv_dq (one grid of dK/dV and dQ workgroups at head_dim 128)
+    gives exactly what attn_bwd_dkdv then attn_bwd_dq give, and matches the
+    oracle."""
+    if shape == "dense":
+        c = Case(B=2, H=3, Sq=333, Sk=290, D=128, dtype=dtype, seed=600)
+    elif shape == "dense_window":
+        c = Case(B=1, H=2, Sq=300, Sk=420, D=128, dtype=dtype, window=(70, -5), diag="bottom_right", seed=601)
+    elif shape == "packed":
+        c = Case(layout="thd", H=2, D=128, dtype=dtype, window=(INF, 0), lens_q=[37, 0, 200, 1, 65],
+                 lens_k=[50, 3, 129, 0, 64], seed=602)
+    else:
+        c = Case(B=2, H=2, Sq=200, D=64, dtype=dtype, seed=603)
+    dev = "cuda"
+    q, k, v, do = (t.to(dev) for t in c.cpu)
+    kw = c.kw_gpu(dev)
+    o, lse = bd.attn_fwd(q, k, v, **kw)
+    outs = []
+    for calls in (("attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq"),
+                  ("attn_bwd_preprocess", "attn_bwd_dkdv_dq")):
+        bp, keep = bd.prepare_bwd(do, q, k, v, o, lse, **kw)
+        for name in calls:
+            bd.launch(name, bp)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in keep[:3]])
+    for name, a, b in zip(("dq", "dk", "dv"), *outs):
+        assert torch.equal(a, b), name
+    ref = c.oracle()
+    tol = TOL[dtype] * 2 * c.tol_factor()
+    for name, got in zip(("dq", "dk", "dv"), outs[1]):
+        assert max_err(name, got, ref[name], tol) <= tol, name
