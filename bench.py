@@ -94,11 +94,11 @@ def bwd_main_kernels(dname: str, head_dim: int, window, seqlen_q: int, heads: in
                      cus: int) -> list:
     """The kernels attn_bwd_dkdv_dq launches: the fused dK/dV + dQ grid for
     16-bit head_dim 128 when the band is wide and a separate dQ grid (two
-    128-row workgroups per CU) would leave its last round at most half full,
+    128-row workgroups per CU) would leave its last round at most a quarter full,
     else the dK/dV kernel then the dQ kernel."""
     slots = 2 * cus
     tail = (-(-seqlen_q // 128) * heads * batch) % slots if slots else 0
-    if dname != "fp32" and head_dim > 80 and wide_band(window) and 0 < tail and 2 * tail <= slots:
+    if dname != "fp32" and head_dim > 80 and wide_band(window) and 0 < tail and 4 * tail <= slots:
         return ["attn_bwd_fused16_kernel"]
     dq = "attn_bwd_dq_kernel" if dname == "fp32" else "attn_bwd_dq16_kernel"
     return [dkdv_kernel_name(dname, head_dim), dq]

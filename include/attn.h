@@ -156,7 +156,7 @@ hipError_t attn_bwd_dq(const attn_bwd_params *p, hipStream_t stream);
  * calls above).  Where the build has it (fp16 and bf16 at head_dim 128) and
  * the problem gains from it (a band unbounded or at least 1024 keys wide,
  * and a separate dQ grid that would leave its last round on the device's
- * compute units at most half full), one kernel whose workgroups are dK/dV
+ * compute units at most a quarter full), one kernel whose workgroups are dK/dV
  * blocks first and dQ blocks after, so that dQ blocks fill the CUs the
  * dK/dV grid leaves idle; otherwise the two kernels in order.  Same
  * parameters, validation and errors as attn_bwd; results equal those of

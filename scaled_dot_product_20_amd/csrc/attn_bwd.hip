@@ -947,13 +947,15 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 
 // Products B .. E-1 of a sequence, each with one LDS operand: load(i) reads
 // product i's operand PD products ahead, prod(i, A) issues it, after(i) runs
-// after it (vector work placed between products).
+// after it (vector work placed between products; after(B-1) runs once the
+// first operands are requested, before the first product).
 template <int B, int E, int PD, class Load, class Prod, class After>
 __device__ __forceinline__ void mfma_stream(Load&& load, Prod&& prod, After&& after) {
   constexpr int D = PD < E - B ? PD : E - B;
   using frag = decltype(load(std::integral_constant<int, B>{}));
   frag buf[D];
   static_for<0, D>([&](auto i) __attribute__((always_inline)) { buf[i] = load(std::integral_constant<int, B + decltype(i)::value>{}); });
+  after(std::integral_constant<int, B - 1>{});  // work placed before the first product
   static_for<B, E>([&](auto i) __attribute__((always_inline)) {
     constexpr int I = decltype(i)::value;
     const frag A = buf[(I - B) % D];
@@ -1006,31 +1008,28 @@ struct DkdvPC {
     const float* l2 = reinterpret_cast<const float*>(st + 2 * TILE);
     f32x16 s[MQ];
     frag pf[MQ][2];
-    auto softmax = [&]() __attribute__((always_inline)) {
+    // Slice MQ's probabilities: masked, 2^(c s - LSE log2 e), rounded for dV
+    // and copied in fp16 for the consumer.
+    auto softmax = [&](auto mqc) __attribute__((always_inline)) {
+      constexpr int mq = decltype(mqc)::value;
       if (masked) {
         // Query i = ib + r(e) sees key kj iff kj - hi <= i <= min(kj - lo, sq - 1).
+        const long long ib = (long long)i0 + 32 * mq + 4 * g;
+        mask_block(s[mq], vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
+      }
+      float p[16];
 #pragma unroll
-        for (int mq = 0; mq < MQ; ++mq) {
-          const long long ib = (long long)i0 + 32 * mq + 4 * g;
-          mask_block(s[mq], vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
-        }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 ll = *reinterpret_cast<const float4*>(l2 + 32 * mq + 8 * q4 + 4 * g);
+        const float lv[4] = {ll.x, ll.y, ll.z, ll.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          p[4 * q4 + u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mq][4 * q4 + u], c, -lv[u]));
       }
 #pragma unroll
-      for (int mq = 0; mq < MQ; ++mq) {
-        float p[16];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 ll = *reinterpret_cast<const float4*>(l2 + 32 * mq + 8 * q4 + 4 * g);
-          const float lv[4] = {ll.x, ll.y, ll.z, ll.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            p[4 * q4 + u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mq][4 * q4 + u], c, -lv[u]));
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          M::pack(&p[8 * h], pf[mq][h]);
-          xb[((kw * MQ + mq) * 2 + h) * 64 + lane] = half8(&p[8 * h], pf[mq][h]);
-        }
+      for (int h = 0; h < 2; ++h) {
+        M::pack(&p[8 * h], pf[mq][h]);
+        xb[((kw * MQ + mq) * 2 + h) * 64 + lane] = half8(&p[8 * h], pf[mq][h]);
       }
     };
     mfma_stream<0, NA + NB, PD>(
@@ -1047,7 +1046,11 @@ struct DkdvPC {
           }
         },
         [&](auto i) __attribute__((always_inline)) {
-          if constexpr (decltype(i)::value == NA - 1) softmax();
+          // Slice 0's softmax under slice 1's S products, slice 1's under
+          // slice 0's dV products.
+          static_assert(MQ == 2, "two slices");
+          if constexpr (decltype(i)::value == NS - 1) softmax(std::integral_constant<int, 0>{});
+          if constexpr (decltype(i)::value == NA - 1) softmax(std::integral_constant<int, 1>{});
         });
   }
 
@@ -1062,27 +1065,25 @@ struct DkdvPC {
     const float* del = reinterpret_cast<const float*>(sp + 2 * TILE) + BMQ;
     const T* dOs = sc + TILE;
     frag dsf[MQ][2];
-    auto ds_all = [&]() __attribute__((always_inline)) {
+    // dS of slice MQ, rounded for dK.
+    auto ds_slice = [&](auto mqc) __attribute__((always_inline)) {
+      constexpr int mq = decltype(mqc)::value;
+      const f16x8 h0 = xb[((kw * MQ + mq) * 2 + 0) * 64 + lane], h1 = xb[((kw * MQ + mq) * 2 + 1) * 64 + lane];
+      float ds[16];
 #pragma unroll
-      for (int mq = 0; mq < MQ; ++mq) {
-        const f16x8 h0 = xb[((kw * MQ + mq) * 2 + 0) * 64 + lane], h1 = xb[((kw * MQ + mq) * 2 + 1) * 64 + lane];
-        float ds[16];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 dd = *reinterpret_cast<const float4*>(del + 32 * mq + 8 * q4 + 4 * g);
+        const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 dd = *reinterpret_cast<const float4*>(del + 32 * mq + 8 * q4 + 4 * g);
-          const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int e = 4 * q4 + u;
-            ds[e] = (float)(e < 8 ? h0[e] : h1[e - 8]) * (dp[mq][e] - dv4[u]);
-          }
+        for (int u = 0; u < 4; ++u) {
+          const int e = 4 * q4 + u;
+          ds[e] = (float)(e < 8 ? h0[e] : h1[e - 8]) * (dp[mq][e] - dv4[u]);
         }
-        M::pack(&ds[0], dsf[mq][0]);
-        M::pack(&ds[8], dsf[mq][1]);
       }
+      M::pack(&ds[0], dsf[mq][0]);
+      M::pack(&ds[8], dsf[mq][1]);
     };
     constexpr int B = FIN ? 0 : NB, E = DP ? NB + NA : NB;
-    if constexpr (FIN) ds_all();
     mfma_stream<B, E, PD>(
         [&](auto i) __attribute__((always_inline)) { return decltype(i)::value < NB ? tr_op(Qp, lo, decltype(i)::value)
                                                      : row_op(dOs, lo, decltype(i)::value - NB); },
@@ -1096,7 +1097,12 @@ struct DkdvPC {
             dp[mq] = M::mma(A, vf.f[k], k == 0 ? zero16() : dp[mq]);
           }
         },
-        [&](auto) __attribute__((always_inline)) {});
+        [&](auto i) __attribute__((always_inline)) {
+          // Slice 0's dS before the first dK product, slice 1's under slice
+          // 0's dK products.
+          if constexpr (FIN && decltype(i)::value == -1) ds_slice(std::integral_constant<int, 0>{});
+          if constexpr (FIN && decltype(i)::value == 0) ds_slice(std::integral_constant<int, 1>{});
+        });
   }
 };
 
@@ -1545,12 +1551,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
   }
   // 2 + 3 in one grid where the build has the fused kernel and it pays: a
   // wide band (its dQ workgroups are 256 rows) and a separate dQ grid whose
-  // last round would be at most half full (2 workgroups of 128 rows per CU).
+  // last round would be at most a quarter full (2 workgroups of 128 rows per
+  // CU).  At half full the filled tail no longer makes up for the 256-row
+  // dQ workgroups (1x32x15300x128: 12.47 ms fused against 11.70 ms).
   if constexpr (S::PC && BWD16_FUSED) {
     const long long ndq4 = (a.p.Sq + NW_Q * 32 - 1) / (NW_Q * 32) * a.p.H * a.p.B;
     const long long slots = 2LL * device_cu_count();
     const long long tail = slots > 0 ? ndq4 % slots : 0;
-    if ((stages & kStageDkDv) && (stages & kStageDq) && wide_window(a.p) && tail > 0 && 2 * tail <= slots) {
+    if ((stages & kStageDkDv) && (stages & kStageDq) && wide_window(a.p) && tail > 0 && 4 * tail <= slots) {
       const long long nkv = (a.p.Sk + 127) / 128 * a.p.H * a.p.B;
       const long long ndq = (a.p.Sq + 255) / 256 * a.p.H * a.p.B;
       if (nkv + ndq > 0x7fffffffLL) return hipErrorInvalidValue;
