@@ -664,7 +664,10 @@ struct FwdPP {
 };
 
 template <typename M, int D, int BN>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd16pp_kernel(FwdArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd16pp_kernel(FwdArgs a,
+                                                                                                    int nq) {
+  // The grid covers logical blocks [0, gridDim.x) of nq 256-row blocks per
+  // (batch, head); the rest, if any, go to the split tail kernel.
   using PP = FwdPP<M, D, BN>;
   using F = typename PP::F;
   using T = typename M::elem;
@@ -674,7 +677,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const int nq = (int)(gridDim.x / (P.B * P.H));
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - (blk % nq);
@@ -780,6 +782,176 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// -------------------------------------------- 16-bit forward, grid tail
+//
+// The rows of the ping-pong grid's last, partly filled round: each 256-row
+// block becomes four workgroups of 64 rows, and each workgroup splits its
+// key tiles into two halves.  Waves 0-1 take rows 0-31 / 32-63 over the
+// first half, waves 2-3 the same rows over the second half, each half with
+// its own two-stage K/V tiles; at the end the second half's (O^T, m, l)
+// pass through LDS and the first half's waves merge them:
+//   m = max(m0, m1), O^T = 2^(m0-m) O0^T + 2^(m1-m) O1^T, l likewise.
+// Four times as many workgroups with half the keys each spread the tail
+// over every CU, one wave per SIMD.
+template <typename M, int D>
+struct FwdSplit {
+  using F = Fwd16<M, D, 64, 1>;
+  using T = typename M::elem;
+  static constexpr int BN = 64, DVT = F::DVT;
+};
+
+template <typename M, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd16split_kernel(FwdArgs a,
+                                                                                                      int nq,
+                                                                                                      int lbase) {
+  using F = typename FwdSplit<M, D>::F;
+  using T = typename M::elem;
+  constexpr int BN = 64, NT = 256, DVT = F::DVT, KT = F::KT;
+  // Key half 0 and key half 1, two stages of K and V each.
+  __shared__ __attribute__((aligned(1024))) T k00[F::TILE], k01[F::TILE], v00[F::TILE], v01[F::TILE];
+  __shared__ __attribute__((aligned(1024))) T k10[F::TILE], k11[F::TILE], v10[F::TILE], v11[F::TILE];
+
+  const ProblemArgs& P = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+  const int rg = wave & 1, kh = wave >> 1;                     // row group, key half
+  const int L = lbase + (int)blockIdx.x / 4, sub = (int)blockIdx.x % 4;
+  const int bh = L / nq, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - (L % nq);
+
+  long long q0 = 0, k0 = 0;
+  int sq = P.Sq, sk = P.Sk;
+  if (P.varlen) {
+    q0 = P.cu_q[b];
+    sq = P.cu_q[b + 1] - (int)q0;
+    k0 = P.cu_k[b];
+    sk = P.cu_k[b + 1] - (int)k0;
+  }
+  const int i0 = qb * 256 + 64 * sub;
+  if (i0 >= sq) return;
+  const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
+
+  const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
+  const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
+  const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
+  T* op = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + q0 * a.o.ss;
+  float* lp = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+
+  const int ilast = min(i0 + 64, sq) - 1;
+  const long long jlo = max(0LL, (long long)i0 + w.lo);
+  const long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
+  const bool block_empty = w.lo > w.hi || jlo > jhi;
+
+  const int iw0 = i0 + 32 * rg;
+  const bool wave_live = iw0 < sq;
+  const int qi = iw0 + r;
+  int tw0 = 0x7fffffff, tw1 = -1;
+  if (wave_live && w.lo <= w.hi) {
+    const long long a0 = max(0LL, (long long)iw0 + w.lo);
+    const long long a1 = min((long long)sk - 1, (long long)min(iw0 + 31, sq - 1) + w.hi);
+    if (a0 <= a1) {
+      tw0 = (int)(a0 / BN);
+      tw1 = (int)(a1 / BN);
+    }
+  }
+  const TileRange full = tiles_starting_in((long long)iw0 + 31 + w.lo,
+                                           min((long long)iw0 + w.hi, (long long)sk - 1) - BN + 1, BN);
+  const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
+  RowFrags<M, D> qf[1];
+  qf[0].load(qp + (long long)qi * a.q.ss, wave_live && qi < sq, g);
+  if (P.scale_log2 < 0.f) qf[0].negate();
+
+  float m[1] = {-INFINITY}, l[1] = {0.f};
+  f32x16 acc[1][DVT];
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) acc[0][dt] = zero16();
+
+  // Barrier that also waits for this wave's direct loads (explicit wait the
+  // compiler accounts for).
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  const int t0 = (int)(jlo / BN), n = block_empty ? 0 : (int)(jhi / BN) - t0 + 1, n0 = (n + 1) / 2;
+  if (!block_empty) {
+    LdsOffsets<M, D> lo;
+    lo.init(lane);
+    DmaLane<T, D, BN, 2> kd, vd;
+    kd.init(a.k.ss, rg, lane);
+    vd.init(a.v.ss, rg, lane);
+    for (T* t : {k00, k01, v00, v01, k10, k11, v10, v11}) zero_unused_slots<T, D, BN, NT>(t, tid);
+    // Key half HALF: tiles [tb, tb + cnt), both halves stepping together for
+    // n0 steps (half 1 has n0 or n0 - 1 tiles).
+    auto run = [&](T* ka, T* kb, T* va, T* vb, int tb, int cnt) {
+      auto dma = [&](T* kdst, T* vdst, int t) {
+        kd.issue(kdst, kp + (long long)t * BN * a.k.ss, a.k.ss, sk - t * BN, rg, lane);
+        vd.issue(vdst, vp + (long long)t * BN * a.v.ss, a.v.ss, sk - t * BN, rg, lane);
+      };
+      if (cnt > 0) dma(ka, va, tb);
+      barrier();
+      auto step = [&](auto parity, int st) {
+        constexpr int Pq = decltype(parity)::value;
+        if (st + 1 < cnt) dma(Pq ? ka : kb, Pq ? va : vb, tb + st + 1);
+        const int t = tb + st;
+        if (st < cnt && tw0 <= t && t <= tw1) {
+          f32x16 sc[1][KT];
+          F::scores(Pq ? kb : ka, lo, qf, sc);
+          F::finalize(sc[0], t < full.t0 || t > full.t1, w, t * BN, qi, sk, c, m[0], l[0], acc[0], g);
+          F::softmax_pv(Pq ? vb : va, lo, sc, acc, m, c, l);
+        }
+        barrier();
+      };
+      for (int st = 0; st < n0; st += 2) {
+        step(std::integral_constant<int, 0>{}, st);
+        if (st + 1 < n0) step(std::integral_constant<int, 1>{}, st + 1);
+      }
+    };
+    if (kh == 0)
+      run(k00, k01, v00, v01, t0, n0);
+    else
+      run(k10, k11, v10, v11, t0 + n0, n - n0);
+  }
+
+  // Merge: the second half's waves leave O^T, m, l in LDS (half 1's K tiles
+  // hold one wave's O^T each, its V tile the row statistics); the first
+  // half's waves combine and write.
+  float* part = reinterpret_cast<float*>(rg == 0 ? k10 : k11);
+  float* stat = reinterpret_cast<float*>(v10) + rg * 128;
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(part + ((dt * 4 + q4) * 64 + lane) * 4) =
+            make_float4(acc[0][dt][4 * q4], acc[0][dt][4 * q4 + 1], acc[0][dt][4 * q4 + 2], acc[0][dt][4 * q4 + 3]);
+    stat[lane] = m[0];
+    stat[64 + lane] = l[0];
+  }
+  barrier();
+  if (kh == 1 || !wave_live) return;
+  const float m1 = stat[lane], l1 = stat[64 + lane];
+  const float mm = fmaxf(m[0], m1);
+  const float a0 = m[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[0] - mm);
+  const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+  const float lt = halves_sum(l[0] * a0 + l1 * a1);
+  if (qi < sq) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    T* orow = op + (long long)qi * a.o.ss;
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * dt + 8 * q4 + 4 * g;
+        const float4 o1 = *reinterpret_cast<const float4*>(part + ((dt * 4 + q4) * 64 + lane) * 4);
+        if (d < D)
+          store4<T>(orow + d, (acc[0][dt][4 * q4] * a0 + o1.x * a1) * inv,
+                    (acc[0][dt][4 * q4 + 1] * a0 + o1.y * a1) * inv, (acc[0][dt][4 * q4 + 2] * a0 + o1.z * a1) * inv,
+                    (acc[0][dt][4 * q4 + 3] * a0 + o1.w * a1) * inv);
+      }
+    if (g == 0) lp[qi] = lt > 0.f ? (mm + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+  }
+}
+
 // Workgroup shapes.  fp32 (register-staged kernel, tiles twice as large):
 // 4 waves, 64-key tiles.  16-bit, 64-key tiles: head_dim <= 80, 8 waves of
 // one 32-row block (two waves per SIMD); head_dim 128, FWD16_NW_BIG waves of
@@ -792,6 +964,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #endif
 #ifndef FWD16_PP
 #define FWD16_PP 1
+#endif
+#ifndef FWD16_SPLIT
+#define FWD16_SPLIT 1  // split the ping-pong grid's partly filled last round
 #endif
 template <typename M, int D>
 struct FwdShape {
@@ -818,10 +993,28 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   void* kargs[] = {&args};
   const void* fn;
   if constexpr (S::k16) {
-    if (pp)
-      fn = reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, BN>);
-    else
-      fn = reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, S::NW, BN, S::RB, S::WPE>);
+    if (pp) {
+      // Full rounds of one 256-row workgroup per CU on the ping-pong kernel.
+      // With at most three of them, a last round at most a quarter full
+      // goes to the split tail kernel, which then fills every CU once
+      // (1x32x6630x128: 0.717 ms against 0.743 ms).  With more rounds, or a
+      // fuller last round, the tail's share is too small to pay for the
+      // split kernel's one wave per SIMD (1x32x15300x128: 3.63 against 3.46).
+      long long nmain = nblk;
+      const long long cus = device_cu_count();
+      if (FWD16_SPLIT && cus > 0 && nblk >= cus && nblk < 4 * cus && 4 * (nblk % cus) <= cus)
+        nmain = nblk - nblk % cus;
+      int nqi = (int)nq;
+      void* pargs[] = {&args, &nqi};
+      hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, BN>),
+                                       dim3((unsigned)nmain), dim3(512), pargs, 0, stream);
+      if (err != hipSuccess || nmain == nblk) return err;
+      int base = (int)nmain;
+      void* sargs[] = {&args, &nqi, &base};
+      return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd16split_kernel<M, D>),
+                             dim3((unsigned)(4 * (nblk - nmain))), dim3(256), sargs, 0, stream);
+    }
+    fn = reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, S::NW, BN, S::RB, S::WPE>);
   } else {
     fn = reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, S::NW, BN>);
   }
