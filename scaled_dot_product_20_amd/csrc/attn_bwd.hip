@@ -428,152 +428,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 //   transposing reads of the same tiles.
 // Each wave visits only the query tiles that can see its keys; tiles cut
 // by the window have their scores set to -inf where masked.
-#ifndef BWD16_PIPE
-#define BWD16_PIPE 1
-#endif
-#ifndef BWD16_PD
-#define BWD16_PD 8
-#endif
-#ifndef BWD16_VG
-#define BWD16_VG 0
-#endif
-#ifndef BWD16_SL1
-#define BWD16_SL1 16  // product after which slice 1's statistics are read
-#endif
-
-// One unmasked dK/dV tile of two 32-row slices as a single ordered stream of
-// products: S and dP of slice 0, S and dP of slice 1, dV and dK of slice 0,
-// dV and dK of slice 1.  Each product's LDS operand is read PD products
-// ahead, and the vector work of slice 0 (probabilities, dS, rounding) is
-// issued between the products of slice 1's S / dP, that of slice 1 between
-// slice 0's dV / dK, so the matrix cores are fed while it runs.
-template <typename M, int D>
-struct DkdvStream {
-  using T = typename M::elem;
-  using L = Swz<D>;
-  using frag = typename M::frag;
-  static constexpr int NS = D / 16, DVT = (D + 31) / 32;
-  static constexpr int NA = 2 * NS, NB = 4 * DVT;  // products per slice: S/dP, dV/dK
-  static constexpr int N = 2 * NA + 2 * NB;
-  static constexpr int PD = BWD16_PD;
-  static constexpr bool is_a(int i) { return i < 2 * NA; }
-  static constexpr int reads(int i) { return is_a(i) ? 1 : 2; }
-
-  const T* Qs;
-  const T* dOs;
-  const LdsOffsets<M, D>& lo;
-  const float* lse2s;
-  const float* dels;
-  const RowFrags<M, D>& kf;
-  const RowFrags<M, D>& vf;
-  f32x16* dk;
-  f32x16* dv;
-  float c;
-  bool masked;  // tile cut by the window or the sequence end
-  Window w;
-  int i0, kj, sq;
-  f32x16 s[2], dp[2];
-  frag pf[2][2], dsf[2][2];
-  frag buf[PD];
-  float4 st_l[2][4], st_d[2][4];  // LSE log2(e) and Delta of each slice's rows
-
-  __device__ __forceinline__ frag load(int i) const {
-    if (is_a(i)) {
-      const int mq = i / NA, st = (i % NA) / 2;
-      return ld_row<M>(((i & 1) ? dOs : Qs) + 32 * mq * L::PITCH, lo.row[st]);
-    }
-    const int j = i - 2 * NA, mq = j / NB, st = (j % NB) / (2 * DVT), dt = (j % (2 * DVT)) / 2;
-    return ld_tr<M>(((j & 1) ? Qs : dOs) + (32 * mq + 16 * st) * L::PITCH, lo.tra[dt], lo.trb[dt]);
-  }
-  template <int I>
-  __device__ __forceinline__ void product(const frag& A) {
-    if constexpr (is_a(I)) {
-      constexpr int mq = I / NA, st = (I % NA) / 2;
-      if constexpr (I & 1)
-        dp[mq] = M::mma(A, vf.f[st], st == 0 ? zero16() : dp[mq]);
-      else
-        s[mq] = M::mma(A, kf.f[st], st == 0 ? zero16() : s[mq]);
-    } else {
-      constexpr int j = I - 2 * NA, mq = j / NB, st = (j % NB) / (2 * DVT), dt = (j % (2 * DVT)) / 2;
-      if constexpr (j & 1)
-        dk[dt] = M::mma(A, dsf[mq][st], dk[dt]);
-      else
-        dv[dt] = M::mma(A, pf[mq][st], dv[dt]);
-    }
-  }
-  // Query i = ib + r(e) sees key kj iff kj - hi <= i <= min(kj - lo, sq - 1).
-  template <int MQ>
-  __device__ __forceinline__ void mask() {
-    if (masked) {
-      const long long ib = (long long)i0 + 32 * MQ + 4 * (threadIdx.x >> 5 & 1);
-      mask_block(s[MQ], vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
-    }
-  }
-  // Reads the statistics of one slice's rows (issued well before use, so
-  // their wait does not drain the operand reads queued behind them).
-  template <int MQ>
-  __device__ __forceinline__ void load_stats() {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int il = 32 * MQ + 8 * q4 + 4 * (threadIdx.x >> 5 & 1);
-      st_l[MQ][q4] = *reinterpret_cast<const float4*>(lse2s + il);
-      st_d[MQ][q4] = *reinterpret_cast<const float4*>(dels + il);
-    }
-  }
-  // P = 2^(c s - LSE log2 e), dS = P (dP - Delta) of one slice, rounded.
-  template <int MQ>
-  __device__ __forceinline__ void softmax() {
-    float p[16], ds[16];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 ll = st_l[MQ][q4], dd = st_d[MQ][q4];
-      const float lv[4] = {ll.x, ll.y, ll.z, ll.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = 4 * q4 + u;
-        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[MQ][e], c, -lv[u]));
-        ds[e] = p[e] * (dp[MQ][e] - dv4[u]);
-      }
-    }
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      M::pack(&p[8 * st], pf[MQ][st]);
-      M::pack(&ds[8 * st], dsf[MQ][st]);
-    }
-  }
-  template <int I>
-  __device__ __forceinline__ void step() {
-    const frag A = buf[I % PD];
-    if constexpr (I + PD < N) buf[I % PD] = load(I + PD);
-    product<I>(A);
-    if constexpr (I == BWD16_SL1) load_stats<1>();
-    if constexpr (I == NA + 1) {
-      mask<0>();
-      softmax<0>();
-    }
-    if constexpr (I == 2 * NA + 1) {
-      mask<1>();
-      softmax<1>();
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (I + PD < N) __builtin_amdgcn_sched_group_barrier(0x100, reads(I + PD) + (I == BWD16_SL1 ? 8 : 0), 0);
-    if constexpr (BWD16_VG > 0 && ((I > NA && I < 2 * NA) || (I > 2 * NA && I < 2 * NA + NB)))
-      __builtin_amdgcn_sched_group_barrier(0x002, BWD16_VG, 0);
-  }
-  template <int... Is>
-  __device__ __forceinline__ void all(std::integer_sequence<int, Is...>) {
-    (step<Is>(), ...);
-  }
-  __device__ __forceinline__ void run() {
-    load_stats<0>();
-#pragma unroll
-    for (int i = 0; i < PD; ++i) buf[i] = load(i);
-    __builtin_amdgcn_sched_group_barrier(0x100, PD + 8, 0);
-    all(std::make_integer_sequence<int, N>{});
-  }
-};
-
-template <typename M, int D, int BMQ, int ST, bool PHASED>
+template <typename M, int D, int BMQ>
 struct Dkdv16 {
   using T = typename M::elem;
   using L = Swz<D>;
@@ -581,108 +436,36 @@ struct Dkdv16 {
   static constexpr int MQ = BMQ / 32, NS = D / 16, DVT = (D + 31) / 32;
   static constexpr int TILE = BMQ * L::PITCH;
 
-  // PHASED (one wave per SIMD): all S and dP products of the tile come first
-  // (one straight run of matrix work), then the masking of a tile cut by the
-  // window or the sequence end (one uniform branch), then per 32-row slice
-  // the probabilities and the dV / dK products, so one slice's vector work
-  // overlaps the next slice's products.  Otherwise slice by slice.
+  // One query tile against this wave's 32 keys, one 32-row slice at a time
+  // (two waves per SIMD; one slice at a time keeps the registers low).
   static __device__ __forceinline__ void tile(const T* Qs, const T* dOs, const LdsOffsets<M, D>& lo, const float* lse2s,
                                               const float* dels, const RowFrags<M, D>& kf,
                                               const RowFrags<M, D>& vf, f32x16* dk, f32x16* dv, float c,
                                               bool masked, Window w, int i0, int kj, int sq, int g) {
-    if constexpr (!PHASED) {
-      // Two waves per SIMD: one slice at a time keeps the registers low.
-#pragma unroll
-      for (int mq = 0; mq < MQ; ++mq) {
-        f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          s = M::mma(ld_row<M>(Qs + 32 * mq * L::PITCH, lo.row[st]), kf.f[st], s);
-          dp = M::mma(ld_row<M>(dOs + 32 * mq * L::PITCH, lo.row[st]), vf.f[st], dp);
-        }
-        if (masked) {
-          const long long ib = (long long)i0 + 32 * mq + 4 * g;
-          mask_block(s, vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
-        }
-        float p[16], ds[16];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int il = 32 * mq + 8 * q4 + 4 * g;
-          const float4 ll = *reinterpret_cast<const float4*>(lse2s + il);
-          const float4 dd = *reinterpret_cast<const float4*>(dels + il);
-          const float lv[4] = {ll.x, ll.y, ll.z, ll.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int e = 4 * q4 + u;
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
-            ds[e] = p[e] * (dp[e] - dv4[u]);
-          }
-        }
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          frag pf, dsf;
-          M::pack(&p[8 * st], pf);
-          M::pack(&ds[8 * st], dsf);
-          const int rbase = (32 * mq + 16 * st) * L::PITCH;
-#pragma unroll
-          for (int dt = 0; dt < DVT; ++dt) {
-            dv[dt] = M::mma(ld_tr<M>(dOs + rbase, lo.tra[dt], lo.trb[dt]), pf, dv[dt]);
-            dk[dt] = M::mma(ld_tr<M>(Qs + rbase, lo.tra[dt], lo.trb[dt]), dsf, dk[dt]);
-          }
-        }
-      }
-      return;
-    }
-    if constexpr (BWD16_PIPE && MQ == 2) {
-      DkdvStream<M, D> ps{Qs, dOs, lo, lse2s, dels, kf, vf, dk, dv, c, masked, w, i0, kj, sq, {}, {}, {}, {}, {}};
-      ps.run();
-      return;
-    }
-    f32x16 s[MQ], dp[MQ];
 #pragma unroll
     for (int mq = 0; mq < MQ; ++mq) {
-      s[mq] = zero16();
-      dp[mq] = zero16();
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        s[mq] = M::mma(ld_row<M>(Qs + 32 * mq * L::PITCH, lo.row[st]), kf.f[st], s[mq]);
-        dp[mq] = M::mma(ld_row<M>(dOs + 32 * mq * L::PITCH, lo.row[st]), vf.f[st], dp[mq]);
+        s = M::mma(ld_row<M>(Qs + 32 * mq * L::PITCH, lo.row[st]), kf.f[st], s);
+        dp = M::mma(ld_row<M>(dOs + 32 * mq * L::PITCH, lo.row[st]), vf.f[st], dp);
       }
-    }
-#ifdef BWD16_SGB
-    // Issue order: 8 operand reads ahead, then one product per read.
-#pragma unroll
-    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * MQ * NS - 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#endif
-    if (masked) {
-      // Query i = ib + r(e) sees key kj iff kj - hi <= i <= min(kj - lo, sq - 1).
-#pragma unroll
-      for (int mq = 0; mq < MQ; ++mq) {
+      if (masked) {
         const long long ib = (long long)i0 + 32 * mq + 4 * g;
-        mask_block(s[mq], vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
+        mask_block(s, vis_bits((long long)kj - w.hi - ib, min((long long)kj - w.lo, (long long)sq - 1) - ib));
       }
-    }
-#pragma unroll
-    for (int mq = 0; mq < MQ; ++mq) {
       float p[16], ds[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int il = 32 * mq + 8 * q4 + 4 * g;  // rows il .. il+3 of the tile
+        const int il = 32 * mq + 8 * q4 + 4 * g;
         const float4 ll = *reinterpret_cast<const float4*>(lse2s + il);
         const float4 dd = *reinterpret_cast<const float4*>(dels + il);
         const float lv[4] = {ll.x, ll.y, ll.z, ll.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int e = 4 * q4 + u;
-          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mq][e], c, -lv[u]));
-          ds[e] = p[e] * (dp[mq][e] - dv4[u]);
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
+          ds[e] = p[e] * (dp[e] - dv4[u]);
         }
       }
 #pragma unroll
@@ -698,39 +481,24 @@ struct Dkdv16 {
         }
       }
     }
-#ifdef BWD16_SGB2
-    // Second phase: transposing reads of a slice ahead of its products,
-    // vector work of the next slice between the products.
-#pragma unroll
-    for (int i = 0; i < 16; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-#pragma unroll
-    for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-      for (int i = 0; i < 4 * DVT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      }
-#endif
   }
 };
 
-template <typename M, int D, int NW, int BMQ, int WPE, int ST>
+template <typename M, int D, int NW, int BMQ, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dkdv16_kernel(BwdArgs a) {
-  using F = Dkdv16<M, D, BMQ, ST, (WPE == 1)>;
+  using F = Dkdv16<M, D, BMQ>;
   using T = typename M::elem;
   using DL = DmaLane<T, D, BMQ, NW>;
   constexpr int NT = NW * 64, BNK = NW * 32, DVT = F::DVT;
-  constexpr int RW = BMQ / NW;           // LSE / Delta rows each wave copies per tile
-  constexpr int VM = 2 * DL::PER + 2;    // vector-memory instructions per wave per tile
+  constexpr int RW = BMQ / NW;  // LSE / Delta rows each wave copies per tile
   static_assert(BMQ % NW == 0 && RW <= 64, "stats rows");
   // One LDS array per stage and operand, so that the compiler can tell the
   // tiles being read from those being filled by direct loads and does not
-  // wait for those loads before every read.  Stage 2 exists only when ST = 3.
-  __shared__ __attribute__((aligned(1024))) T q_s0[F::TILE], q_s1[F::TILE], q_s2[ST > 2 ? F::TILE : 8];
-  __shared__ __attribute__((aligned(1024))) T d_s0[F::TILE], d_s1[F::TILE], d_s2[ST > 2 ? F::TILE : 8];
+  // wait for those loads before every read.
+  __shared__ __attribute__((aligned(1024))) T q_s0[F::TILE], q_s1[F::TILE];
+  __shared__ __attribute__((aligned(1024))) T d_s0[F::TILE], d_s1[F::TILE];
   // LSE log2(e) and Delta of each stage's query rows.
-  __shared__ __attribute__((aligned(16))) float l_s0[BMQ], l_s1[BMQ], l_s2[BMQ], e_s0[BMQ], e_s1[BMQ], e_s2[BMQ];
+  __shared__ __attribute__((aligned(16))) float l_s0[BMQ], l_s1[BMQ], e_s0[BMQ], e_s1[BMQ];
 
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -799,21 +567,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     DL qd, dd;
     qd.init(a.q.ss, wave, lane);
     dd.init(a.dout.ss, wave, lane);
-    T* const qs[3] = {q_s0, q_s1, q_s2};
-    T* const ds_[3] = {d_s0, d_s1, d_s2};
+    T* const qs[2] = {q_s0, q_s1};
+    T* const ds_[2] = {d_s0, d_s1};
 #pragma unroll
-    for (int u = 0; u < ST; ++u) {
+    for (int u = 0; u < 2; ++u) {
       zero_unused_slots<T, D, BMQ, NT>(qs[u], tid);
       zero_unused_slots<T, D, BMQ, NT>(ds_[u], tid);
     }
     const int t0 = (int)(ilo / BMQ), t1 = (int)(ihi / BMQ);
     // One tile's loads, all direct to LDS: its Q and dO rows and, per wave,
     // RW rows of LSE log2(e) and Delta (rows past the sequence repeat its
-    // last row and are masked).  Every wave issues exactly VM vector-memory
-    // instructions per tile, so a wait for "at most VM outstanding" retires
-    // everything issued before the latest tile.
-    float* const ls[3] = {l_s0, l_s1, l_s2};
-    float* const es[3] = {e_s0, e_s1, e_s2};
+    // last row and are masked).
+    float* const ls[2] = {l_s0, l_s1};
+    float* const es[2] = {e_s0, e_s1};
     auto issue = [&](int stage, int t) {
       const int i0 = t * BMQ;
       qd.issue(qs[stage], qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
@@ -827,49 +593,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       }
     };
     issue(0, t0);
-    if (ST == 3 && t0 + 1 <= t1) issue(1, t0 + 1);
     __syncthreads();
-    // Step t: tile t sits in stage P = (t - t0) % ST; the loads of tile
-    // t+ST-1 are issued now into the stage tile t-1 used.  With three stages
-    // the barrier at the end waits only for tile t+1 (AH: the step looks
-    // ahead, known at compile time in the steady state so that the wait
-    // counts stay exact).
-    auto step = [&](auto parity, auto ahead_c, int t) {
+    // Step t: tile t sits in stage (t - t0) & 1; the loads of tile t+1 go
+    // into the other stage during the step.
+    auto step = [&](auto parity, int t) {
       constexpr int Pq = decltype(parity)::value;
-      constexpr int Pa = (Pq + ST - 1) % ST;
-      constexpr int AH = decltype(ahead_c)::value;  // 1: yes, 0: check
-      const bool ahead = AH || t + ST - 1 <= t1;
-      if (ahead) issue(Pa, t + ST - 1);
+      if (t + 1 <= t1) issue(Pq ^ 1, t + 1);
       if (tw0 <= t && t <= tw1) {
         const bool masked =
             classify(w, (long long)t * BMQ, BMQ, jw0, 32, sk) == kPartial || (t + 1) * BMQ > sq;
         F::tile(qs[Pq], ds_[Pq], lo, ls[Pq], es[Pq], kf, vf, dk, dv, c, masked, w, t * BMQ, kj, sq, g);
       }
-      if (ST == 3 && AH)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
-      else
-        __syncthreads();
+      __syncthreads();
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    static_assert(ST == 2 || ST == 3, "stages");
-    int t = t0;
-    if constexpr (ST == 3) {
-      for (; t + ST + 1 <= t1; t += 3) {  // every step of the group looks ahead
-        step(I0{}, I1{}, t);
-        step(I1{}, I1{}, t + 1);
-        step(I2{}, I1{}, t + 2);
-      }
-      if (t <= t1) step(I0{}, I0{}, t);
-      if (t + 1 <= t1) step(I1{}, I0{}, t + 1);
-      if (t + 2 <= t1) step(I2{}, I0{}, t + 2);
-      if (t + 3 <= t1) step(I0{}, I0{}, t + 3);
-    } else {
-      for (; t <= t1; t += 2) {
-        step(I0{}, I0{}, t);
-        if (t + 1 <= t1) step(I1{}, I0{}, t + 1);
-      }
+    for (int t = t0; t <= t1; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 <= t1) step(std::integral_constant<int, 1>{}, t + 1);
     }
   }
 
@@ -931,10 +670,6 @@ __device__ __forceinline__ KBwdArgs& kernel_bwd_args() {
   return *(KBwdArgs*)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
-#ifndef BWD16_PC_PD
-#define BWD16_PC_PD 4
-#endif
-
 // Calls f(integral_constant<int, I>) for I = B .. E-1 in order.
 template <int B, class Fn, int... Is>
 __device__ __forceinline__ void static_for_impl(Fn&& f, std::integer_sequence<int, Is...>) {
@@ -976,7 +711,7 @@ struct DkdvPC {
   static constexpr int XFR = 4 * MQ * 2 * 64;              // fp16 x8 fragments of one P buffer
   static_assert(STAGE * (int)sizeof(T) <= kBwdStageBytes && XFR * 16 <= kBwdXBytes, "LDS arrays");
   static constexpr int NA = MQ * NS, NB = MQ * 2 * DVT;    // row-read products, transposed-read products
-  static constexpr int PD = BWD16_PC_PD;
+  static constexpr int PD = 4;  // LDS operand reads ahead of the products
 
   // fp16 copy of 8 probabilities (exactly the MFMA fragment for fp16 input).
   static __device__ __forceinline__ f16x8 half8(const float* x, const frag& f) {
@@ -1496,33 +1231,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // ------------------------------------------------------------ launch
 
 // Workgroup shapes.  16-bit: dK/dV 4 waves (128 keys) over 64-row query
-// tiles, two waves per SIMD where the registers allow (head_dim <= 80), one
-// at head_dim 128; dQ 4 waves (128 queries) over 64-key tiles, two per SIMD.
-// fp32 (register-staged kernels): 4 waves each, dQ key tiles of 32 to fit
-// LDS.
-#ifndef BWD16_NWQ
-#define BWD16_NWQ 4
-#endif
+// tiles at two waves per SIMD for head_dim <= 80, producer / consumer pairs
+// (8 waves, 128 keys) at head_dim 128; dQ 4 waves (128 queries) over 64-key
+// tiles, two per SIMD.  fp32 (register-staged kernels): 4 waves each, tiles
+// of 32 to fit LDS.
 template <typename M, int D>
 struct BwdShape {
   static constexpr bool k16 = sizeof(typename M::elem) == 2;
-#ifndef BWD16_BMQ_BIG
-#define BWD16_BMQ_BIG 64
-#endif
-#ifndef BWD16_ST_BIG
-#define BWD16_ST_BIG 2
-#endif
-  static constexpr int NW_KV = 4, BMQ = k16 ? (D > 80 ? BWD16_BMQ_BIG : 64) : 32, WPE_KV = D > 80 ? 1 : 2;
-  static constexpr int ST_KV = D > 80 ? BWD16_ST_BIG : 2;  // LDS stages of the dK/dV query tiles
-  static constexpr int NW_Q = k16 ? BWD16_NWQ : 4, BN = k16 ? 64 : 32;
-#ifndef BWD16_PC
-#define BWD16_PC 1
-#endif
-#ifndef BWD16_FUSED
-#define BWD16_FUSED 1  // dK/dV and dQ requested together run as one grid
-#endif
+  static constexpr int NW_KV = 4, BMQ = k16 ? 64 : 32;
+  static constexpr int NW_Q = 4, BN = k16 ? 64 : 32;
   // dK/dV by producer / consumer wave pairs (128 keys per workgroup, as NW_KV).
-  static constexpr bool PC = k16 && D > 80 && BWD16_PC;
+  static constexpr bool PC = k16 && D > 80;
 };
 
 template <typename M, int D>
@@ -1554,7 +1273,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
   // last round would be at most a quarter full (2 workgroups of 128 rows per
   // CU).  At half full the filled tail no longer makes up for the 256-row
   // dQ workgroups (1x32x15300x128: 12.47 ms fused against 11.70 ms).
-  if constexpr (S::PC && BWD16_FUSED) {
+  if constexpr (S::PC) {
     const long long ndq4 = (a.p.Sq + NW_Q * 32 - 1) / (NW_Q * 32) * a.p.H * a.p.B;
     const long long slots = 2LL * device_cu_count();
     const long long tail = slots > 0 ? ndq4 % slots : 0;
@@ -1582,7 +1301,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
         fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16pc_kernel<M, D>);
         threads = 512;
       } else if constexpr (S::k16) {
-        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV, S::ST_KV>);
+        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, 2>);
       } else {
         fn = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>);
       }

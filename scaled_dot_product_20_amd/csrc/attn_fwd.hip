@@ -498,12 +498,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 // B the V tiles (V_{k+1} during V_k, V_0 up front); two stages each, and
 // each group waits for its own copies at the barrier one block before the
 // first reader.
-#ifndef FWDPP_PD
-#define FWDPP_PD 4
-#endif
-#ifndef FWDPP_SGB
-#define FWDPP_SGB 1
-#endif
 template <typename M, int D, int BN>
 struct FwdPP {
   using F = Fwd16<M, D, BN, 1>;
@@ -527,7 +521,7 @@ struct FwdPP {
   static constexpr int NPV = KT * 2 * DVT, NSC = KT * F::NS;
   template <int KS, int B, int E>
   struct Steps {
-    static constexpr int PD = FWDPP_PD < E - B ? FWDPP_PD : E - B;
+    static constexpr int PD = 4 < E - B ? 4 : E - B;  // LDS operand reads ahead of the products
     static constexpr int reads(int i) { return i < NPV ? 2 : 1; }  // LDS instructions of step i
     const Ctx& x;
     const LdsOffsets<M, D>& lo;
@@ -556,10 +550,8 @@ struct FwdPP {
         constexpr int j = I - NPV, kt = j / F::NS, st = j % F::NS;
         s[kt] = M::mma(A, qf.f[st], st == 0 ? zero16() : s[kt]);
       }
-#if FWDPP_SGB
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if constexpr (I + PD < E) __builtin_amdgcn_sched_group_barrier(0x100, reads(I + PD), 0);
-#endif
     }
     template <int... Is>
     __device__ __forceinline__ void all(std::integer_sequence<int, Is...>) {
@@ -568,10 +560,8 @@ struct FwdPP {
     __device__ __forceinline__ void run() {
 #pragma unroll
       for (int i = 0; i < PD; ++i) buf[i] = load(B + i);
-#if FWDPP_SGB
       constexpr int PRO = (B + PD <= NPV ? 2 * PD : (B >= NPV ? PD : 2 * (NPV - B) + (B + PD - NPV)));
       __builtin_amdgcn_sched_group_barrier(0x100, PRO, 0);
-#endif
       all(std::make_integer_sequence<int, E - B>{});
     }
   };
@@ -953,30 +943,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // Workgroup shapes.  fp32 (register-staged kernel, tiles twice as large):
-// 4 waves, 64-key tiles.  16-bit, 64-key tiles: head_dim <= 80, 8 waves of
-// one 32-row block (two waves per SIMD); head_dim 128, FWD16_NW_BIG waves of
-// FWD16_RB_BIG row blocks.
-#ifndef FWD16_NW_BIG
-#define FWD16_NW_BIG 4
-#endif
-#ifndef FWD16_RB_BIG
-#define FWD16_RB_BIG 1
-#endif
-#ifndef FWD16_PP
-#define FWD16_PP 1
-#endif
-#ifndef FWD16_SPLIT
-#define FWD16_SPLIT 1  // split the ping-pong grid's partly filled last round
-#endif
+// 4 waves, 64-key tiles.  16-bit, 64-key tiles, one 32-row block per wave,
+// two waves per SIMD: the ping-pong kernel (8 waves) for wide bands; for
+// narrower ones 8 waves at head_dim <= 80, 4 at head_dim 128.
 template <typename M, int D>
 struct FwdShape {
   static constexpr bool k16 = sizeof(typename M::elem) == 2;
-  static constexpr bool PP = k16 && FWD16_PP;  // ping-pong kernel built (8 waves, 256 rows)
-  static constexpr bool big = D > 80;
-  static constexpr int RB = k16 && big ? FWD16_RB_BIG : 1;
-  static constexpr int NW = k16 ? (big ? FWD16_NW_BIG : 8) : 4;
+  static constexpr bool PP = k16;  // ping-pong kernel built (8 waves, 256 rows)
+  static constexpr int RB = 1;
+  static constexpr int NW = k16 ? (D > 80 ? 4 : 8) : 4;
   static constexpr int BN = 64;
-  static constexpr int WPE = RB >= 2 ? 1 : 2;  // waves per SIMD the registers allow
+  static constexpr int WPE = 2;  // waves per SIMD the registers allow
 };
 
 template <typename M, int D>
@@ -1002,7 +979,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
       // split kernel's one wave per SIMD (1x32x15300x128: 3.63 against 3.46).
       long long nmain = nblk;
       const long long cus = device_cu_count();
-      if (FWD16_SPLIT && cus > 0 && nblk >= cus && nblk < 4 * cus && 4 * (nblk % cus) <= cus)
+      if (cus > 0 && nblk >= cus && nblk < 4 * cus && 4 * (nblk % cus) <= cus)
         nmain = nblk - nblk % cus;
       int nqi = (int)nq;
       void* pargs[] = {&args, &nqi};
