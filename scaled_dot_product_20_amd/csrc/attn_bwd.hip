@@ -1051,36 +1051,91 @@ struct Dq16 {
   static constexpr int KT = BN / 32, NS = D / 16, DVT = (D + 31) / 32;
   static constexpr int TILE = BN * L::PITCH;
 
+  // One key tile (KT 32-key slices) against this wave's 32 queries.
+  // Head_dim <= 80: one ordered stream of products with LDS operands read
+  // ahead (S and dP of every slice, then dQ += dS K slice by slice; slice
+  // kt's dS is computed under the next products once its S and dP are
+  // complete).  Head_dim 128: slice by slice, which keeps both slices' S and
+  // dP out of the registers at two waves per SIMD.
+  static constexpr int NA = 2 * NS, NB = 2 * DVT;  // products per slice: S and dP, dQ
   static __device__ __forceinline__ void tile(const T* Ks, const T* Vs, const LdsOffsets<M, D>& lo,
                                               const RowFrags<M, D>& qf, const RowFrags<M, D>& dof, f32x16* dq,
                                               float c, float lse2, float delta, bool masked, Window w, int j0,
                                               int qi, int sk, int g) {
+    if constexpr (D > 80) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      f32x16 s = zero16(), dp = zero16();
+      for (int kt = 0; kt < KT; ++kt) {
+        f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        s = M::mma(ld_row<M>(Ks + 32 * kt * L::PITCH, lo.row[st]), qf.f[st], s);
-        dp = M::mma(ld_row<M>(Vs + 32 * kt * L::PITCH, lo.row[st]), dof.f[st], dp);
+        for (int st = 0; st < NS; ++st) {
+          s = M::mma(ld_row<M>(Ks + 32 * kt * L::PITCH, lo.row[st]), qf.f[st], s);
+          dp = M::mma(ld_row<M>(Vs + 32 * kt * L::PITCH, lo.row[st]), dof.f[st], dp);
+        }
+        if (masked) {
+          const long long jb = (long long)j0 + 32 * kt + 4 * g;
+          mask_block(s, vis_bits((long long)qi + w.lo - jb, min((long long)qi + w.hi, (long long)sk - 1) - jb));
+        }
+        float ds[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lse2)) * (dp[e] - delta);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          frag dsf;
+          M::pack(&ds[8 * st], dsf);
+          const int rbase = (32 * kt + 16 * st) * L::PITCH;
+#pragma unroll
+          for (int dt = 0; dt < DVT; ++dt)
+            dq[dt] = M::mma(ld_tr<M>(Ks + rbase, lo.tra[dt], lo.trb[dt]), dsf, dq[dt]);
+        }
       }
+      return;
+    }
+    f32x16 s[KT], dp[KT];
+    frag dsf[KT][2];
+    auto ds_slice = [&](auto ktc) __attribute__((always_inline)) {
+      constexpr int kt = decltype(ktc)::value;
       if (masked) {
         const long long jb = (long long)j0 + 32 * kt + 4 * g;
-        mask_block(s, vis_bits((long long)qi + w.lo - jb, min((long long)qi + w.hi, (long long)sk - 1) - jb));
+        mask_block(s[kt], vis_bits((long long)qi + w.lo - jb, min((long long)qi + w.hi, (long long)sk - 1) - jb));
       }
       float ds[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lse2)) * (dp[e] - delta);
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        frag dsf;
-        M::pack(&ds[8 * st], dsf);
-        const int rbase = (32 * kt + 16 * st) * L::PITCH;
-#pragma unroll
-        for (int dt = 0; dt < DVT; ++dt)
-          dq[dt] = M::mma(ld_tr<M>(Ks + rbase, lo.tra[dt], lo.trb[dt]), dsf, dq[dt]);
-      }
-    }
+        ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, -lse2)) * (dp[kt][e] - delta);
+      M::pack(&ds[0], dsf[kt][0]);
+      M::pack(&ds[8], dsf[kt][1]);
+    };
+    mfma_stream<0, KT * (NA + NB), 4>(
+        [&](auto i) __attribute__((always_inline)) {
+          constexpr int I = decltype(i)::value;
+          if constexpr (I < KT * NA) {
+            constexpr int kt = I / NA, st = (I % NA) / 2;
+            return ld_row<M>(((I & 1) ? Vs : Ks) + 32 * kt * L::PITCH, lo.row[st]);
+          } else {
+            constexpr int j = I - KT * NA, kt = j / NB, st = (j % NB) / DVT, dt = j % DVT;
+            return ld_tr<M>(Ks + (32 * kt + 16 * st) * L::PITCH, lo.tra[dt], lo.trb[dt]);
+          }
+        },
+        [&](auto i, const frag& A) __attribute__((always_inline)) {
+          constexpr int I = decltype(i)::value;
+          if constexpr (I < KT * NA) {
+            constexpr int kt = I / NA, st = (I % NA) / 2;
+            if constexpr (I & 1)
+              dp[kt] = M::mma(A, dof.f[st], st == 0 ? zero16() : dp[kt]);
+            else
+              s[kt] = M::mma(A, qf.f[st], st == 0 ? zero16() : s[kt]);
+          } else {
+            constexpr int j = I - KT * NA, kt = j / NB, st = (j % NB) / DVT, dt = j % DVT;
+            dq[dt] = M::mma(A, dsf[kt][st], dq[dt]);
+          }
+        },
+        [&](auto i) __attribute__((always_inline)) {
+          constexpr int I = decltype(i)::value;
+          static_assert(KT == 2, "two slices");
+          if constexpr (I == NA - 1) ds_slice(std::integral_constant<int, 0>{});
+          if constexpr (I == KT * NA - 1) ds_slice(std::integral_constant<int, 1>{});
+        });
   }
 };
 
