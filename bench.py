@@ -2,8 +2,9 @@
 """Throughput of the fused attention forward + backward on one MI355X.
 
 One step = the whole path over one batch of synthetic input: attn_fwd (O,
-LSE), then the backward's three kernels (Delta preprocess, dK/dV, dQ), all
-through the C ABI on torch's current stream.  Inputs are resident in HBM
+LSE), then the backward's two calls (attn_bwd_preprocess for Delta, then
+attn_bwd_dkdv_dq, which runs dK/dV and dQ as one fused grid or as two
+kernels), all through the C ABI on torch's current stream.  Inputs are resident in HBM
 before the timed region starts; K steps are timed between a synchronize on
 each side, and every kernel is also bracketed by HIP events on the launch
 stream so its own average duration is known.
@@ -114,9 +115,9 @@ def fwd_kernel_name(dname: str, window) -> str:
 
 
 def read_traffic(workload: str, kernel: str):
-    """HBM bytes per dK/dV launch from the committed counter summary, or None
-    when there is none for this workload and kernel or the kernel's sources
-    changed since."""
+    """HBM bytes per launch of the dK/dV (+ dQ) kernel from the committed
+    counter summary, or None when there is none for this workload and kernel
+    or the kernel's sources changed since."""
     if workload != DEFAULT_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
