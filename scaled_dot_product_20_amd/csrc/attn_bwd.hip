@@ -847,8 +847,8 @@ template <typename M, int D>
 __device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
   using F = DkdvPC<M, D>;
   using T = typename M::elem;
-  using DL = DmaLane<T, D, F::BMQ, 8>;
-  constexpr int NT = 512, BMQ = F::BMQ, DVT = F::DVT, BNK = 128, RW = BMQ / 8;
+  using DL = DmaLane<T, D, F::BMQ, 4>;  // copies by the four producer waves
+  constexpr int NT = 512, BMQ = F::BMQ, DVT = F::DVT, BNK = 128, RW = BMQ / 4;
   KBwdArgs& a = kernel_bwd_args();
   T* const st0 = reinterpret_cast<T*>(g_bwd_st0);
   T* const st1 = reinterpret_cast<T*>(g_bwd_st1);
@@ -920,8 +920,8 @@ __device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
     LdsOffsets<M, D> lo;
     lo.init(lane);
     DL qd, dd;
-    qd.init(a.q.ss, wave, lane);
-    dd.init(a.dout.ss, wave, lane);
+    qd.init(a.q.ss, kw, lane);
+    dd.init(a.dout.ss, kw, lane);
     // Stage and P buffer u, chosen at compile time so that every LDS access
     // names its own array.
     auto stg = [&](auto u) __attribute__((always_inline)) -> T* {
@@ -941,17 +941,20 @@ __device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
     }
     const int t0 = (int)(ilo / BMQ), n = (int)(ihi / BMQ) - t0 + 1;
     // Tile copies, all direct to LDS (rows past the sequence repeat its last
-    // row and are masked); every wave copies RW rows of the statistics.
+    // row and are masked), issued by the producer waves only: they wait for
+    // the consumer at every barrier, while copy instructions hold up the wave
+    // that issues them, and the consumer's step is the longer one.  Every
+    // producer wave copies RW rows of the statistics.
     auto issue = [&](T* dst, int t) __attribute__((always_inline)) {
       const int i0 = t * BMQ;
-      qd.issue(dst, qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
-      dd.issue(dst + F::TILE, dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, wave, lane);
+      qd.issue(dst, qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, kw, lane);
+      dd.issue(dst + F::TILE, dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, kw, lane);
       if (lane < RW) {
         float* sts = reinterpret_cast<float*>(dst + 2 * F::TILE);
-        const int off = 4 * (min(i0 + wave * RW + lane, sq - 1) - i0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(l2p + i0), (lds_void*)(sts + wave * RW), 4, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(delp + i0), (lds_void*)(sts + BMQ + wave * RW), 4, off, 0,
-                                                 0, 0);
+        const int off = 4 * (min(i0 + kw * RW + lane, sq - 1) - i0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(l2p + i0), (lds_void*)(sts + kw * RW), 4, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(delp + i0), (lds_void*)(sts + BMQ + kw * RW), 4, off, 0, 0,
+                                                 0);
       }
     };
     // End of a step: this wave's copies and LDS traffic are complete
@@ -964,7 +967,7 @@ __device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
     auto masked_at = [&](int t) __attribute__((always_inline)) {
       return classify(w, (long long)t * BMQ, BMQ, jw0, 32, sk) == kPartial || (t + 1) * BMQ > sq;
     };
-    issue(st0, t0);
+    if (prod) issue(st0, t0);
     barrier();
     // Step it (tile t0+it in stage it % 3): copies of the next tile, this
     // role's work, barrier.  One loop per role, so that the consumer's dP^T
@@ -978,7 +981,7 @@ __device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
         using CN = std::integral_constant<int, SN>;
         using CP = std::integral_constant<int, SP>;
         const int t = t0 + it;
-        if (it + 1 < n) issue(stg(CN{}), t + 1);
+        if (PROD && it + 1 < n) issue(stg(CN{}), t + 1);
         if constexpr (PROD) {
           if (mine(t))
             F::produce(stg(CI{}), xs(CI{}), lo, kv, acc, c, masked_at(t), w, t * BMQ, kj, sq, kw, lane, g);
