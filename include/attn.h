@@ -109,7 +109,9 @@ typedef struct {
   int64_t q_stride[3];     /* element strides {batch, head, row}; the */
   int64_t k_stride[3];     /* head_dim stride is 1.  Base pointers and */
   int64_t v_stride[3];     /* strides must keep every row 16-byte */
-  int64_t o_stride[3];     /* aligned. */
+  int64_t o_stride[3];     /* aligned.  A stride may be negative: the
+                              pointer is then the address of index 0 on that
+                              axis, and the operand reaches below it. */
 } attn_fwd_params;
 
 typedef struct {

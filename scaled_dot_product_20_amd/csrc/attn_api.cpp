@@ -23,14 +23,19 @@ struct Extent {
   uintptr_t lo, hi;
 };
 
+// A negative stride reaches below the base pointer: each axis adds
+// (n - 1) * stride elements to the lower or the upper end.
 Extent extent_of(const void* ptr, const int64_t* stride, int64_t nb, int64_t nh, int64_t nrows,
                  int64_t d, int64_t esz, bool packed) {
-  int64_t span = d;  // the last row's head_dim elements
-  if (!packed && nb > 0) span += (nb - 1) * std::llabs(stride[0]);
-  if (nh > 0) span += (nh - 1) * std::llabs(stride[1]);
-  if (nrows > 0) span += (nrows - 1) * std::llabs(stride[2]);
-  const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
-  return Extent{lo, lo + (uintptr_t)(span * esz)};
+  int64_t below = 0, above = d;  // elements; the last row's head_dim elements
+  auto axis = [&](int64_t n, int64_t s) {
+    if (n > 1) (s < 0 ? below : above) += (n - 1) * std::llabs(s);
+  };
+  if (!packed) axis(nb, stride[0]);
+  axis(nh, stride[1]);
+  axis(nrows, stride[2]);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(ptr);
+  return Extent{base - (uintptr_t)(below * esz), base + (uintptr_t)(above * esz)};
 }
 
 bool overlap(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }

@@ -154,6 +154,31 @@ def test_fwd_validation_strides_and_aliasing():
     assert fcheck(p) == INVALID
 
 
+def test_negative_row_strides_validate_and_overlap():
+    """Rows stored last to first: the base pointer is row 0, the highest
+    address, and the operand reaches (S - 1) rows below it.  Such operands
+    validate, and the overlap check sees the bytes below the base."""
+    B, H, S, D = 2, 3, 64, 64
+    span = B * H * S * D * 2
+    p = dense_params(B=B, H=H, S=S, D=D)
+    top = (S - 1) * D * 2  # byte offset of row 0 from the operand's lowest address
+    for name, i in (("q", 1), ("k", 2), ("v", 3), ("o", 4)):
+        setattr(p, name, addr(i) + top)
+        setattr(p, name + "_stride", bd._I64x3(H * S * D, S * D, -D))
+    assert fcheck(p) == OK
+    assert bcheck(bwd_params(p)) == OK
+    # The output's rows lie below its base; place that range across the end of q's.
+    p.o = addr(1) + span + top - D * 2
+    assert fcheck(p) == INVALID
+    p.o = addr(1) + span + top
+    assert fcheck(p) == OK
+    # LSE right below o's base pointer falls inside o's rows.
+    p = dense_params(B=B, H=H, S=S, D=D)
+    p.o, p.o_stride = addr(4) + top, bd._I64x3(H * S * D, S * D, -D)
+    p.lse = addr(4) + 64
+    assert fcheck(p) == INVALID
+
+
 def test_tile_span_limit():
     """The 16-bit kernels address a 64-row tile with 32-bit byte offsets, so a
     row stride whose 63 steps plus one row reach 2 GiB is not supported there;

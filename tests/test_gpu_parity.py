@@ -195,3 +195,59 @@ def test_forward_grid_tail(D, window, diag):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     H = cus // 4 + 1
     Case(B=1, H=H, Sq=1000, Sk=1100, D=D, window=window, diag=diag, seed=700 + D).check(bwd=False)
+
+
+@pytest.mark.parametrize("dtype,D,sq,sk,window,diag", [
+    (torch.bfloat16, 128, 333, 333, (INF, INF), "top_left"),
+    (torch.bfloat16, 64, 200, 300, (40, 7), "bottom_right"),
+    (torch.float16, 80, 130, 130, (INF, 0), "top_left"),
+    (torch.float32, 64, 100, 100, (INF, INF), "top_left"),
+])
+def test_negative_row_strides(dtype, D, sq, sk, window, diag):
+    """Every operand stored with its rows last to first (row stride -D, base
+    pointer at row 0, the highest address): attn_fwd, attn_bwd and
+    attn_bwd_dkdv_dq give the same bits as with the rows in order, since only
+    the addressing differs."""
+    import ctypes
+    c = Case(B=2, H=3, Sq=sq, Sk=sk, D=D, dtype=dtype, window=window, diag=diag, seed=700)
+    q, k, v, do = (t.cuda() for t in c.cpu)
+    kw = c.kw_gpu("cuda")
+    o, lse = bd.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = bd.attn_bwd(do, q, k, v, o, lse, **kw)
+
+    def rev(t):  # rows-reversed storage, base pointer of logical row 0, strides
+        st = t.flip(2).contiguous()
+        B, H, S, _ = t.shape
+        return st, st.data_ptr() + (S - 1) * D * st.element_size(), bd._I64x3(H * S * D, S * D, -D)
+
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    (qs, qb, qst), (ks, kb, kst), (vs, vb, vst) = rev(q), rev(k), rev(v)
+    os_, ob, ost = rev(torch.zeros_like(o))
+    lse_n = torch.empty_like(lse)
+    p = bd.fwd_params(q, k, v, o, lse_n, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                      max_seqlen_k=None, **kw)
+    p.q, p.k, p.v, p.o = qb, kb, vb, ob
+    p.q_stride, p.k_stride, p.v_stride, p.o_stride = qst, kst, vst, ost
+    assert bd.lib().attn_fwd(ctypes.byref(p), stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(os_.flip(2), o), "o"
+    assert torch.equal(lse_n, lse), "lse"
+
+    for entry in ("attn_bwd", "attn_bwd_dkdv_dq"):
+        (dos, dob, dost) = rev(do)
+        outs = [rev(torch.zeros_like(t)) for t in (q, k, v)]
+        bp = bd.BwdParams()
+        bp.fwd = p
+        bp.dout, bp.do_stride = dob, dost
+        (bp.dq, bp.dq_stride), (bp.dk, bp.dk_stride), (bp.dv, bp.dv_stride) = ((b, st) for _, b, st in outs)
+        need = int(bd.lib().attn_bwd_workspace_size(ctypes.byref(bp)))
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        bp.workspace, bp.workspace_bytes = ws.data_ptr(), ws.numel()
+        if entry == "attn_bwd":
+            assert bd.lib().attn_bwd(ctypes.byref(bp), stream) == 0
+        else:
+            assert bd.lib().attn_bwd_preprocess(ctypes.byref(bp), stream) == 0
+            assert bd.lib().attn_bwd_dkdv_dq(ctypes.byref(bp), stream) == 0
+        torch.cuda.synchronize()
+        for name, (st, _, _), ref in zip(("dq", "dk", "dv"), outs, (dq, dk, dv)):
+            assert torch.equal(st.flip(2), ref), f"{entry} {name}"
