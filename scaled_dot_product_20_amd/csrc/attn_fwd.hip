@@ -494,10 +494,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 // block V_k (mask, row max, rescale, exp and rounding of P).  Group B runs
 // one block behind group A and a workgroup barrier closes every block, so on
 // each SIMD one wave keeps the matrix cores busy while the other works on
-// the vector units.  Group A copies the K tiles (K_{k+1} during M_k), group
-// B the V tiles (V_{k+1} during V_k, V_0 up front); two stages each, and
-// each group waits for its own copies at the barrier one block before the
-// first reader.
+// the vector units.  Group A copies the K tiles (K_{k+2} during V_k, K_0
+// and K_1 up front), group B the V tiles (V_{k+2} during V_k, V_0 and V_1
+// up front), three stages each: a copy has about three blocks to land, each
+// phase issues the copies of one tile, and each group waits only for the
+// tile its next block reads (a partial vmcnt) at the barrier one block
+// before its first reader.
 template <typename M, int D, int BN>
 struct FwdPP {
   using F = Fwd16<M, D, BN, 1>;
@@ -506,9 +508,12 @@ struct FwdPP {
   static constexpr int KT = F::KT, DVT = F::DVT;
   using Dma = DmaLane<T, D, BN, 4>;
 
+  // K stages 0-2 then V stages 0-2 in one LDS array.  Operand reads address
+  // a stage through an immediate offset from the array start (at most 64
+  // KiB), so the V reads take lane offsets biased by 3 tiles (VOff).
   struct Ctx {
-    T* ks[2];
-    T* vs[2];
+    T* ks[3];
+    T* vs[3];
     const T* kp;
     const T* vp;
     long long kss, vss;
@@ -519,12 +524,29 @@ struct FwdPP {
   };
 
   static constexpr int NPV = KT * 2 * DVT, NSC = KT * F::NS;
+  static constexpr int NSTG = 3;  // K and V stages
+  static constexpr int prev(int ks) { return (ks + NSTG - 1) % NSTG; }
+  // Transposing-read offsets of the V tiles, biased by NSTG tiles (the V
+  // region) and hidden from constant folding, so that a read of V stage p
+  // is ks[p] + an immediate.
+  struct VOff {
+    int a[DVT], b[DVT];
+    __device__ __forceinline__ void init(const LdsOffsets<M, D>& lo) {
+#pragma unroll
+      for (int dt = 0; dt < DVT; ++dt) {
+        a[dt] = lo.tra[dt] + NSTG * F::TILE;
+        b[dt] = lo.trb[dt] + NSTG * F::TILE;
+        asm volatile("" : "+v"(a[dt]), "+v"(b[dt]));
+      }
+    }
+  };
   template <int KS, int B, int E>
   struct Steps {
     static constexpr int PD = 4 < E - B ? 4 : E - B;  // LDS operand reads ahead of the products
     static constexpr int reads(int i) { return i < NPV ? 2 : 1; }  // LDS instructions of step i
     const Ctx& x;
     const LdsOffsets<M, D>& lo;
+    const VOff& vo;
     const RowFrags<M, D>& qf;
     frag (*pf)[2];
     f32x16* acc;
@@ -534,7 +556,7 @@ struct FwdPP {
     __device__ __forceinline__ frag load(int i) const {
       if (i < NPV) {
         const int kt = i / (2 * DVT), st = (i / DVT) % 2, dt = i % DVT;
-        return ld_tr<M>(x.vs[KS ^ 1] + (32 * kt + 16 * st) * F::L::PITCH, lo.tra[dt], lo.trb[dt]);
+        return ld_tr<M>(x.ks[prev(KS)] + (32 * kt + 16 * st) * F::L::PITCH, vo.a[dt], vo.b[dt]);
       }
       const int j = i - NPV, kt = j / F::NS, st = j % F::NS;
       return ld_row<M>(x.ks[KS] + 32 * kt * F::L::PITCH, lo.row[st]);
@@ -566,19 +588,20 @@ struct FwdPP {
     }
   };
   // Matrix steps i in [B, E) of one block: steps below NPV are
-  // O^T += V^T P^T (V of the previous tile, stage KS^1), the rest
+  // O^T += V^T P^T (V of the previous tile, stage prev(KS)), the rest
   // S^T = K Q^T (K stage KS).  The LDS operands run PD steps ahead of the
   // MFMAs.
   template <int KS, int B, int E>
-  static __device__ __forceinline__ void mma_steps(const Ctx& x, const LdsOffsets<M, D>& lo, const RowFrags<M, D>& qf,
-                                                   frag (*pf)[2], f32x16* acc, f32x16* s) {
-    Steps<KS, B, E> st{x, lo, qf, pf, acc, s, {}};
+  static __device__ __forceinline__ void mma_steps(const Ctx& x, const LdsOffsets<M, D>& lo, const VOff& vo,
+                                                   const RowFrags<M, D>& qf, frag (*pf)[2], f32x16* acc, f32x16* s) {
+    Steps<KS, B, E> st{x, lo, vo, qf, pf, acc, s, {}};
     st.run();
   }
 
   template <int GRP>
-  static __device__ __forceinline__ void run(const Ctx& x, const LdsOffsets<M, D>& lo, const Dma& dma,
-                                             const RowFrags<M, D>* qf, float& m, float& l, f32x16* acc) {
+  static __device__ __forceinline__ void run(const Ctx& x, const LdsOffsets<M, D>& lo, const VOff& vo,
+                                             const Dma& dma, const RowFrags<M, D>* qf, float& m, float& l,
+                                             f32x16* acc) {
     f32x16 s[1][KT];
     frag pf[KT][2];
     auto mine = [&](int kk) { return x.tw0 <= x.t0 + kk && x.t0 + kk <= x.tw1; };
@@ -586,13 +609,17 @@ struct FwdPP {
       const int j0 = (x.t0 + kk) * BN;
       dma.issue(dst, base + (long long)j0 * ss, ss, x.sk - j0, x.gw, x.lane);
     };
-    // Barrier closing a block; `vm` also waits for this wave's copies.  The
-    // wait is an explicit s_waitcnt (vmcnt(0) lgkmcnt(0)) that the compiler
-    // keeps and accounts for; the asm barrier keeps memory accesses on
-    // their side of it.
-    auto barrier = [&](auto vm) {
+    // Barrier closing a block.  With `vm` it first waits for this wave's
+    // copies except the newest tile's, or for all of them when `all` (no
+    // newer tile was issued): an explicit s_waitcnt (vmcnt(N) lgkmcnt(0);
+    // copies complete in order) that the compiler keeps and accounts for;
+    // the asm barrier keeps memory accesses on their side of it.
+    auto barrier = [&](auto vm, bool all) {
       if constexpr (decltype(vm)::value) {
-        __builtin_amdgcn_s_waitcnt(0x0070);
+        if (all)
+          __builtin_amdgcn_s_waitcnt(0x0070);
+        else
+          __builtin_amdgcn_s_waitcnt(0x0070 | Dma::PER);
         asm volatile("s_barrier" ::: "memory");
       } else {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -600,15 +627,25 @@ struct FwdPP {
     };
     auto mblock = [&](auto kst, int kk) {
       constexpr int KS = decltype(kst)::value;
-      if (GRP == 0 && kk + 1 < x.nt) copy(x.ks[KS ^ 1], x.kp, x.kss, kk + 1);
       const bool pv = kk >= 1 && mine(kk - 1), sc = kk < x.nt && mine(kk);
-      if (pv) mma_steps<KS, 0, NPV>(x, lo, qf[0], pf, acc, s[0]);
-      if (sc) mma_steps<KS, NPV, NPV + NSC>(x, lo, qf[0], pf, acc, s[0]);
-      barrier(std::integral_constant<bool, GRP == 1>{});
+      if (pv) mma_steps<KS, 0, NPV>(x, lo, vo, qf[0], pf, acc, s[0]);
+      if (sc) mma_steps<KS, NPV, NPV + NSC>(x, lo, vo, qf[0], pf, acc, s[0]);
+      // Group B: V_kk, read by the next block of group A, must have landed.
+      // M_nt (the last tile's P.V only) closes with group B's last vector
+      // block, so only group A meets a barrier there.
+      if (GRP == 0 || kk < x.nt) barrier(std::integral_constant<bool, GRP == 1>{}, kk + 1 >= x.nt);
     };
     auto vblock = [&](auto kst, int kk) {
       constexpr int KS = decltype(kst)::value;
-      if (GRP == 1 && kk + 1 < x.nt) copy(x.vs[KS ^ 1], x.vp, x.vss, kk + 1);
+      // Copies of tile kk+2: K by group A here (while group B runs M_kk), V
+      // by group B here (while group A runs M_kk+1), so each phase issues
+      // one tile of copies, from the waves that run vector work.
+      if (kk + 2 < x.nt) {
+        if constexpr (GRP == 0)
+          copy(x.ks[(KS + 2) % NSTG], x.kp, x.kss, kk + 2);
+        else
+          copy(x.vs[(KS + 2) % NSTG], x.vp, x.vss, kk + 2);
+      }
       if (mine(kk)) {
         const int t = x.t0 + kk;
         F::finalize(s[0], t < x.full.t0 || t > x.full.t1, x.w, t * BN, x.qi, x.sk, x.c, m, l, acc, x.g);
@@ -627,29 +664,29 @@ struct FwdPP {
         }
         l += ls;
       }
-      barrier(std::integral_constant<bool, GRP == 0>{});
+      // Group A: K_{kk+1}, read by its next block, must have landed.
+      barrier(std::integral_constant<bool, GRP == 0>{}, kk + 2 >= x.nt);
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
     if constexpr (GRP == 1) {
       copy(x.vs[0], x.vp, x.vss, 0);
-      barrier(std::false_type{});
+      if (x.nt > 1) copy(x.vs[1], x.vp, x.vss, 1);
+      barrier(std::false_type{}, true);
     }
-    int kk = 0;
-    for (; kk + 1 < x.nt; kk += 2) {
-      mblock(std::integral_constant<int, 0>{}, kk);
-      vblock(std::integral_constant<int, 0>{}, kk);
-      mblock(std::integral_constant<int, 1>{}, kk + 1);
-      vblock(std::integral_constant<int, 1>{}, kk + 1);
+    // Tiles 0 .. nt-1, then M_nt: O^T += V^T P^T of the last tile.
+    for (int kk = 0;; kk += 3) {
+      mblock(I0{}, kk);
+      if (kk >= x.nt) break;
+      vblock(I0{}, kk);
+      mblock(I1{}, kk + 1);
+      if (kk + 1 >= x.nt) break;
+      vblock(I1{}, kk + 1);
+      mblock(I2{}, kk + 2);
+      if (kk + 2 >= x.nt) break;
+      vblock(I2{}, kk + 2);
     }
-    // M_nt: O^T += V^T P^T of the last tile, then (group A) the barrier of
-    // group B's last vector block.
-    if (kk < x.nt) {
-      mblock(std::integral_constant<int, 0>{}, kk);
-      vblock(std::integral_constant<int, 0>{}, kk);
-      if (mine(kk)) mma_steps<1, 0, NPV>(x, lo, qf[0], pf, acc, s[0]);
-    } else if (mine(kk - 1)) {
-      mma_steps<0, 0, NPV>(x, lo, qf[0], pf, acc, s[0]);
-    }
-    if constexpr (GRP == 0) barrier(std::false_type{});
   }
 };
 
@@ -662,7 +699,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   using F = typename PP::F;
   using T = typename M::elem;
   constexpr int NT = 512, BM = 256, DVT = F::DVT;
-  __shared__ __attribute__((aligned(1024))) T k_s0[F::TILE], k_s1[F::TILE], v_s0[F::TILE], v_s1[F::TILE];
+  __shared__ __attribute__((aligned(1024))) T kv_s[2 * PP::NSTG * F::TILE];
 
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -731,26 +768,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     typename PP::Dma dma;
     const bool grp_b = wave >= 4;
     dma.init(grp_b ? a.v.ss : a.k.ss, x.gw, lane);
-    zero_unused_slots<T, D, BN, NT>(k_s0, tid);
-    zero_unused_slots<T, D, BN, NT>(k_s1, tid);
-    zero_unused_slots<T, D, BN, NT>(v_s0, tid);
-    zero_unused_slots<T, D, BN, NT>(v_s1, tid);
-    x.ks[0] = k_s0;
-    x.ks[1] = k_s1;
-    x.vs[0] = v_s0;
-    x.vs[1] = v_s1;
+#pragma unroll
+    for (int i = 0; i < PP::NSTG; ++i) {
+      x.ks[i] = kv_s + i * F::TILE;
+      x.vs[i] = kv_s + (PP::NSTG + i) * F::TILE;
+      zero_unused_slots<T, D, BN, NT>(x.ks[i], tid);
+      zero_unused_slots<T, D, BN, NT>(x.vs[i], tid);
+    }
+    typename PP::VOff vo;
+    vo.init(lo);
     x.kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
     x.vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
     x.kss = a.k.ss;
     x.vss = a.v.ss;
     x.t0 = (int)(jlo / BN);
     x.nt = (int)(jhi / BN) - x.t0 + 1;
-    if (!grp_b) dma.issue(k_s0, x.kp + (long long)x.t0 * BN * a.k.ss, a.k.ss, sk - x.t0 * BN, x.gw, lane);
+    if (!grp_b) {
+      // K_0 and K_1 up front; this wave's part of K_0 lands before the barrier.
+      dma.issue(x.ks[0], x.kp + (long long)x.t0 * BN * a.k.ss, a.k.ss, sk - x.t0 * BN, x.gw, lane);
+      if (x.nt > 1) {
+        dma.issue(x.ks[1], x.kp + (long long)(x.t0 + 1) * BN * a.k.ss, a.k.ss, sk - (x.t0 + 1) * BN, x.gw, lane);
+        __builtin_amdgcn_s_waitcnt(0x0070 | PP::Dma::PER);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0070);
+      }
+    }
     __syncthreads();
     if (grp_b)
-      PP::template run<1>(x, lo, dma, qf, m, l, acc);
+      PP::template run<1>(x, lo, vo, dma, qf, m, l, acc);
     else
-      PP::template run<0>(x, lo, dma, qf, m, l, acc);
+      PP::template run<0>(x, lo, vo, dma, qf, m, l, acc);
   }
 
   if (wave_live) {
