@@ -690,9 +690,16 @@ struct FwdPP {
   }
 };
 
+// Workgroups of the ping-pong kernel per CU: two at head_dim 64, where a
+// wave fits in 128 registers, so one workgroup's start (Q rows, first tiles)
+// and end (O rows) overlap the other's steady state (192x16x512x64 fp16:
+// 0.427 -> 0.374 ms); one otherwise.
+template <int D>
+constexpr int pp_per_cu() { return D <= 64 ? 2 : 1; }
+
 template <typename M, int D, int BN>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd16pp_kernel(FwdArgs a,
-                                                                                                    int nq) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2 * pp_per_cu<D>(), 2 * pp_per_cu<D>()))) void
+attn_fwd16pp_kernel(FwdArgs a, int nq) {
   // The grid covers logical blocks [0, gridDim.x) of nq 256-row blocks per
   // (batch, head); the rest, if any, go to the split tail kernel.
   using PP = FwdPP<M, D, BN>;
@@ -1018,14 +1025,15 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const void* fn;
   if constexpr (S::k16) {
     if (pp) {
-      // Full rounds of one 256-row workgroup per CU on the ping-pong kernel.
-      // With at most three of them, a last round at most a quarter full
-      // goes to the split tail kernel, which then fills every CU once
-      // (1x32x6630x128: 0.717 ms against 0.743 ms).  With more rounds, or a
-      // fuller last round, the tail's share is too small to pay for the
-      // split kernel's one wave per SIMD (1x32x15300x128: 3.63 against 3.46).
+      // Full rounds of 256-row workgroups (pp_per_cu per CU) on the
+      // ping-pong kernel.  With at most three of them, a last round at most
+      // a quarter full goes to the split tail kernel, which then fills every
+      // CU once (1x32x6630x128: 0.717 ms against 0.743 ms).  With more
+      // rounds, or a fuller last round, the tail's share is too small to pay
+      // for the split kernel's one wave per SIMD (1x32x15300x128: 3.63
+      // against 3.46).
       long long nmain = nblk;
-      const long long cus = device_cu_count();
+      const long long cus = device_cu_count() * pp_per_cu<D>();
       if (cus > 0 && nblk >= cus && nblk < 4 * cus && 4 * (nblk % cus) <= cus)
         nmain = nblk - nblk % cus;
       int nqi = (int)nq;

@@ -188,12 +188,13 @@ def test_dkdv_dq_call_equals_separate_calls(dtype, shape):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("window,diag", [((INF, INF), "top_left"), ((INF, 0), "bottom_right"), ((1200, 3), "top_left")])
 def test_forward_grid_tail(D, window, diag):
-    """A wide-band forward whose 256-row grid has one full round per CU plus
-    a few blocks: those rows run on the split tail kernel (64-row workgroups,
-    key tiles halved and merged).  Sq = 1000 gives 4 blocks per head; heads =
-    CUs / 4 + 1 makes CUs + 4 blocks, 4 of them in the tail (the last heads)."""
+    """A wide-band forward whose 256-row grid has one full round plus a few
+    blocks: those rows run on the split tail kernel (64-row workgroups, key
+    tiles halved and merged).  A round is one workgroup per CU, two at
+    head_dim 64.  Sq = 1000 gives 4 blocks per head; heads = round / 4 + 1
+    makes a round + 4 blocks, 4 of them in the tail (the last heads)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    H = cus // 4 + 1
+    H = cus * (2 if D <= 64 else 1) // 4 + 1
     Case(B=1, H=H, Sq=1000, Sk=1100, D=D, window=window, diag=diag, seed=700 + D).check(bwd=False)
 
 
