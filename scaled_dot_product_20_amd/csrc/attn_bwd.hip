@@ -108,9 +108,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nkb = (int)(gridDim.x / (P.B * P.H));
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = blk / nkb, h = bh % P.H, b = bh / P.H;
-  const int kb = blk % nkb;
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nkb, P.B * P.H, P.varlen);
+  const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
+  const int kb = gp.i;
 
   long long q0 = 0, k0 = 0;
   int sq = P.Sq, sk = P.Sk;
@@ -283,9 +283,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = (int)(gridDim.x / (P.B * P.H));
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
-  const int qb = nq - 1 - (blk % nq);
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.varlen);
+  const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - gp.i;
 
   long long q0 = 0, k0 = 0;
   int sq = P.Sq, sk = P.Sk;
@@ -504,9 +504,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nkb = (int)(gridDim.x / (P.B * P.H));
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = blk / nkb, h = bh % P.H, b = bh / P.H;
-  const int kb = blk % nkb;
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nkb, P.B * P.H, P.varlen);
+  const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
+  const int kb = gp.i;
 
   long long q0 = 0, k0 = 0;
   int sq = P.Sq, sk = P.Sk;
@@ -863,9 +863,9 @@ __device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
   const bool prod = wave < 4;
   const int kw = wave & 3;
   const int nkb = nblk / (P.B * P.H);
-  const int blk = xcd_remap(hw, nblk);
-  const int bh = blk / nkb, h = bh % P.H, b = bh / P.H;
-  const int kb = blk % nkb;
+  const GridPos gp = grid_pos(hw, nblk, nkb, P.B * P.H, P.varlen);
+  const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
+  const int kb = gp.i;
 
   long long q0 = 0, k0 = 0;
   int sq = P.Sq, sk = P.Sk;
@@ -1161,9 +1161,9 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = nblk / (P.B * P.H);
-  const int blk = xcd_remap(hw, nblk);
-  const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
-  const int qb = nq - 1 - (blk % nq);
+  const GridPos gp = grid_pos(hw, nblk, nq, P.B * P.H, P.varlen);
+  const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - gp.i;
 
   long long q0 = 0, k0 = 0;
   int sq = P.Sq, sk = P.Sk;

@@ -62,9 +62,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = (int)(gridDim.x / (P.B * P.H));
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
-  const int qb = nq - 1 - (blk % nq);  // longest rows (under causal) first
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.varlen);
+  const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - gp.i;  // longest rows (under causal) first
 
   long long q0 = 0, k0 = 0;
   int sq = P.Sq, sk = P.Sk;
@@ -357,9 +357,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = (int)(gridDim.x / (P.B * P.H));
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
-  const int qb = nq - 1 - (blk % nq);
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.varlen);
+  const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - gp.i;
 
   long long q0 = 0, k0 = 0;
   int sq = P.Sq, sk = P.Sk;
@@ -711,9 +711,9 @@ attn_fwd16pp_kernel(FwdArgs a, int nq) {
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = blk / nq, h = bh % P.H, b = bh / P.H;
-  const int qb = nq - 1 - (blk % nq);
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.varlen);
+  const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - gp.i;
 
   long long q0 = 0, k0 = 0;
   int sq = P.Sq, sk = P.Sk;
@@ -860,8 +860,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int rg = wave & 1, kh = wave >> 1;                     // row group, key half
   const int L = lbase + (int)blockIdx.x / 4, sub = (int)blockIdx.x % 4;
-  const int bh = L / nq, h = bh % P.H, b = bh / P.H;
-  const int qb = nq - 1 - (L % nq);
+  // Logical block L of the whole grid, in the order grid_pos gives the
+  // ping-pong kernel's blocks (which cover L < lbase).
+  const int nbh = P.B * P.H;
+  const int bh = P.varlen ? L % nbh : L / nq, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - (P.varlen ? L / nbh : L % nq);
 
   long long q0 = 0, k0 = 0;
   int sq = P.Sq, sk = P.Sk;

@@ -34,6 +34,27 @@ int main(int argc, char** argv) {
     }
   }
   printf("remap_ok\n");
+  // 1b. grid_pos maps [0, nseq * nbh) one to one onto (bh, i) pairs, dense
+  //     and packed; and for packed sequences with nbh a multiple of 8 every
+  //     XCD (hw mod 8) gets the same positions i of the same bh mod 8.
+  for (int varlen = 0; varlen < 2; ++varlen)
+    for (int nbh = 1; nbh <= 40; ++nbh)
+      for (int nseq = 1; nseq <= 40; ++nseq) {
+        const int n = nseq * nbh;
+        std::vector<int> seen(n, 0);
+        for (int hw = 0; hw < n; ++hw) {
+          const GridPos p = grid_pos(hw, n, nseq, nbh, varlen != 0);
+          if (p.bh < 0 || p.bh >= nbh || p.i < 0 || p.i >= nseq || seen[p.bh * nseq + p.i]++) {
+            printf("grid_fail %d %d %d %d\n", varlen, nbh, nseq, hw);
+            return 1;
+          }
+          if (varlen && nbh % 8 == 0 && p.bh % 8 != hw % 8) {
+            printf("grid_xcd_fail %d %d %d\n", nbh, nseq, hw);
+            return 1;
+          }
+        }
+      }
+  printf("grid_ok\n");
   // 2. perm_pos(e, g) == perm16(acc_row(e, g)) on every 32-row block.
   for (int g = 0; g < 2; ++g)
     for (int e = 0; e < 16; ++e)
