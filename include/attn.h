@@ -35,7 +35,9 @@
  *    call (null required pointer, version or flags mismatch, negative or
  *    zero sizes where a size is needed, unit-stride or 16-byte alignment
  *    violated, workspace too small), hipErrorNotSupported for a well-formed
- *    call outside the built set (head_dim not in {64, 80, 128}; for fp16 and
+ *    call outside the built set (head_dim not in {32, 48, 64, 80, 96, 128}: the
+ *    multiples of 16 up to 128 that the AOTriton pages name or test, 48 and
+ *    80 among them (0.10b "Known Problems"); for fp16 and
  *    bf16, a q, k, v or dout row stride so large that 63 strides plus one
  *    row reach 2 GiB), or the HIP error of the launch.  Validation makes no HIP call.  The contents of
  *    cu_seqlens arrays are a precondition (0 first, non-decreasing, last
@@ -87,7 +89,7 @@ typedef struct {
   int32_t layout;          /* ATTN_BHSD / ATTN_THD */
   int32_t batch;           /* BHSD: batch; THD: number of sequences (>= 1) */
   int32_t heads;           /* >= 1; Q, K and V have the same head count */
-  int32_t head_dim;        /* 64, 80 or 128; V/O share it */
+  int32_t head_dim;        /* 32, 48, 64, 80, 96 or 128; V/O share it */
   int32_t seqlen_q;        /* BHSD: Sq (>= 0); THD: max sequence length of Q */
   int32_t seqlen_k;        /* BHSD: Sk (>= 0); THD: max sequence length of K */
   int32_t window_left;     /* any int32; ATTN_WINDOW_INF = unbounded */

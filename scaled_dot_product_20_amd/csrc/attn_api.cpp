@@ -14,7 +14,7 @@ using sdpa::Operand;
 
 bool dtype_ok(int32_t d) { return d == ATTN_FP32 || d == ATTN_FP16 || d == ATTN_BF16; }
 int64_t elem_bytes(int32_t d) { return d == ATTN_FP32 ? 4 : 2; }
-bool head_dim_built(int32_t d) { return d == 64 || d == 80 || d == 128; }
+bool head_dim_built(int32_t d) { return d == 32 || d == 48 || d == 64 || d == 80 || d == 96 || d == 128; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -1388,8 +1388,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
 template <typename M>
 static hipError_t launch_bwd_d(int head_dim, const BwdArgs& a, int stages, hipStream_t stream) {
   switch (head_dim) {
+    case 32: return launch_bwd_t<M, 32>(a, stages, stream);
+    case 48: return launch_bwd_t<M, 48>(a, stages, stream);
     case 64: return launch_bwd_t<M, 64>(a, stages, stream);
     case 80: return launch_bwd_t<M, 80>(a, stages, stream);
+    case 96: return launch_bwd_t<M, 96>(a, stages, stream);
     case 128: return launch_bwd_t<M, 128>(a, stages, stream);
     default: return hipErrorNotSupported;
   }

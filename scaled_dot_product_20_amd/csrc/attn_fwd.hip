@@ -1059,8 +1059,11 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 template <typename M>
 static hipError_t launch_fwd_d(int head_dim, const FwdArgs& a, hipStream_t stream) {
   switch (head_dim) {
+    case 32: return launch_fwd_t<M, 32>(a, stream);
+    case 48: return launch_fwd_t<M, 48>(a, stream);
     case 64: return launch_fwd_t<M, 64>(a, stream);
     case 80: return launch_fwd_t<M, 80>(a, stream);
+    case 96: return launch_fwd_t<M, 96>(a, stream);
     case 128: return launch_fwd_t<M, 128>(a, stream);
     default: return hipErrorNotSupported;
   }

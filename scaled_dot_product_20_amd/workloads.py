@@ -107,7 +107,7 @@ def _varlen(name: str, head_dim: int) -> Workload:
 
 
 def workloads() -> dict:
-    """The tiny check, the pages' model shapes, and a long-sequence bwd cell."""
+    """The tiny check, the pages' model shapes, and a long-sequence bwd cell at each built head dim."""
     ws = [
         Workload("tiny_f32", "bhsd", 1, 2, 64, 128, 128, (torch.float32,), seed=1),
         Workload("bert_like", "bhsd", 192, 16, 64, 512, 512, (torch.float16, torch.bfloat16), seed=2),
@@ -118,5 +118,9 @@ def workloads() -> dict:
         _varlen("varlen_window_d80", 80),
         _varlen("varlen_window_d128", 128),
         Workload("long_4096_bwd", "bhsd", 1, 32, 128, 4096, 4096, (torch.bfloat16,), seed=6),
+        # The same cell at the other head dims the kernels are built for.
+        Workload("long_4096_d32", "bhsd", 1, 32, 32, 4096, 4096, (torch.bfloat16,), seed=7),
+        Workload("long_4096_d48", "bhsd", 1, 32, 48, 4096, 4096, (torch.bfloat16,), seed=8),
+        Workload("long_4096_d96", "bhsd", 1, 32, 96, 4096, 4096, (torch.bfloat16,), seed=9),
     ]
     return {w.name: w for w in ws}

@@ -121,8 +121,10 @@ def test_valid_calls_pass():
     assert bcheck(bwd_params(dense_params())) == OK
     assert bcheck(bwd_params(packed_params())) == OK
     for dt in (bd.FP32, bd.FP16, bd.BF16):
-        for D in (64, 80, 128):
+        for D in (32, 48, 64, 80, 96, 128):
             assert fcheck(dense_params(D=D, dtype=dt)) == OK
+        for D in (16, 40, 72, 112, 160, 256):
+            assert fcheck(dense_params(D=D, dtype=dt)) == NOTSUP
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -134,7 +136,7 @@ def test_valid_calls_pass():
     ("q", 0, INVALID), ("lse", 0, INVALID), ("o", 0, INVALID),
     ("k", BASE + 8, INVALID),               # not 16-byte aligned
     ("cu_seqlens_q", BASE, INVALID),        # dense with cu_seqlens
-    ("head_dim", 96, NOTSUP), ("head_dim", 256, NOTSUP), ("head_dim", 72, NOTSUP),
+    ("head_dim", 112, NOTSUP), ("head_dim", 256, NOTSUP), ("head_dim", 72, NOTSUP),
 ])
 def test_fwd_validation_errors(field, value, code):
     p = dense_params()
@@ -231,7 +233,7 @@ def test_bwd_validation_errors():
     p = bwd_params(dense_params())
     p.dout = None
     assert bcheck(p) == INVALID
-    p = bwd_params(dense_params(D=96))
+    p = bwd_params(dense_params(D=112))
     assert bcheck(p) == NOTSUP
 
 

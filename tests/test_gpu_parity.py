@@ -42,6 +42,21 @@ def test_dense_other_dtypes(dtype, D):
                  seed=200 + 10 * i + j).check()
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("D", [32, 48, 96])
+def test_more_head_dims(dtype, D):
+    """Head dims 32, 48 and 96: dense problems spanning several tiles with
+    ragged ends, under the no-mask, causal, numeric and empty windows, and a
+    packed one with empty sequences."""
+    for i, (sq, sk) in enumerate([(129, 127), (300, 333)]):
+        for j, (window, diag) in enumerate([((INF, INF), "top_left"), ((INF, 0), "bottom_right"),
+                                            ((40, 7), "bottom_right"), ((-3, 1), "top_left")]):
+            Case(B=2, H=2, Sq=sq, Sk=sk, D=D, dtype=dtype, window=window, diag=diag,
+                 seed=900 + 10 * i + j).check()
+    Case(layout="thd", H=2, D=D, dtype=dtype, window=(64, 0), diag="bottom_right",
+         lens_q=[100, 0, 37, 260], lens_k=[150, 10, 37, 300], seed=950).check()
+
+
 def test_tiny_fp32_config():
     """1 x 2 heads x 128 x 64, fp32, no mask, scale 1/8 (the tiny check)."""
     Case(B=1, H=2, Sq=128, D=64, dtype=torch.float32, scale=0.125, seed=1).check()
