@@ -258,16 +258,18 @@ struct Fwd16 {
   static __device__ __forceinline__ void scores(const T* K, const LdsOffsets<M, D>& lo,
                                                 const RowFrags<M, D>* qf, f32x16 (*s)[KT]) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) s[rb][kt] = zero16();
+    // K step outermost: consecutive products go to different accumulators.
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
         const frag A = ld_row<M>(K + 32 * kt * L::PITCH, lo.row[st]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) s[rb][kt] = M::mma(A, qf[rb].f[st], s[rb][kt]);
       }
-    }
   }
 
   // Masks one row block's scores of a tile cut by the window or the
@@ -558,7 +560,7 @@ struct FwdPP {
         const int kt = i / (2 * DVT), st = (i / DVT) % 2, dt = i % DVT;
         return ld_tr<M>(x.ks[prev(KS)] + (32 * kt + 16 * st) * F::L::PITCH, vo.a[dt], vo.b[dt]);
       }
-      const int j = i - NPV, kt = j / F::NS, st = j % F::NS;
+      const int j = i - NPV, kt = j % KT, st = j / KT;  // two accumulators in turn
       return ld_row<M>(x.ks[KS] + 32 * kt * F::L::PITCH, lo.row[st]);
     }
     template <int I>
@@ -569,7 +571,7 @@ struct FwdPP {
         constexpr int kt = I / (2 * DVT), st = (I / DVT) % 2, dt = I % DVT;
         acc[dt] = M::mma(A, pf[kt][st], acc[dt]);
       } else {
-        constexpr int j = I - NPV, kt = j / F::NS, st = j % F::NS;
+        constexpr int j = I - NPV, kt = j % KT, st = j / KT;
         s[kt] = M::mma(A, qf.f[st], st == 0 ? zero16() : s[kt]);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
