@@ -305,8 +305,9 @@ namespace sdpa {
 //  - a 64-bit transposing read of 4 consecutive rows (aligned to 4) x 4
 //    consecutive chunks (aligned to 4) by 32 lanes (an operand read across
 //    rows, see tr_frag)
-// both touch every bank once.  Rows are 8 chunk slots (head_dim 64) or 16
-// (head_dim 80 and 128; 80 leaves slots unused).
+// both touch every bank once.  Rows are 8 chunk slots (head_dim up to 64) or
+// 16 (head_dim 80 to 128); a head_dim below the slot count (32, 48, 80, 96)
+// leaves slots unused.
 template <int D>
 struct Swz {
   static constexpr int CH = D / 8;                // chunks holding data

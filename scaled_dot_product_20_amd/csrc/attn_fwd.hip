@@ -10,8 +10,9 @@
 // notes, "Bottom-Right Aligned Sliding Windows").
 //
 // Per key tile of BN keys:
-//   K (row-major) and V (transposed) are staged HBM -> registers -> LDS,
-//     double-buffered, the next tile's loads in flight during this tile;
+//   K and V are copied HBM -> LDS with direct loads into swizzled row-major
+//     tiles (two stages in the narrow-band kernel, three in the ping-pong
+//     kernel), the next tiles' copies in flight during this tile;
 //   S^T = K Q^T on the matrix cores (Q fragments stay in registers);
 //   online softmax in the log2 domain: x = c*s with c = |scale|*log2(e)
 //     (a negative scale is moved into Q, so c >= 0 and max_j x_j is
