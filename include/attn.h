@@ -60,6 +60,12 @@ extern "C" {
  * Changes": kVersion fields, reserved bits rejected). */
 #define ATTN_PARAMS_VERSION 1u
 
+/* Bits of attn_fwd_params.flags; every other bit must be 0.
+ * ATTN_FLAG_LSE_TH (packed layout only): lse is [total_q, heads] (the "TH"
+ *   layout of the AOTriton 0.14b VarlenBits LSE field) instead of
+ *   [heads, total_q]. */
+#define ATTN_FLAG_LSE_TH 1u
+
 /* Unbounded side of a window. */
 #define ATTN_WINDOW_INF 2147483647
 
@@ -84,7 +90,7 @@ extern "C" {
 
 typedef struct {
   uint32_t version;        /* ATTN_PARAMS_VERSION */
-  uint32_t flags;          /* reserved, must be 0 */
+  uint32_t flags;          /* 0 or ATTN_FLAG_LSE_TH (THD only) */
   int32_t dtype;           /* ATTN_FP32 / ATTN_FP16 / ATTN_BF16 */
   int32_t layout;          /* ATTN_BHSD / ATTN_THD */
   int32_t batch;           /* BHSD: batch; THD: number of sequences (>= 1) */
@@ -105,7 +111,8 @@ typedef struct {
   void *o;                 /* fwd: output; bwd: input (the forward's O) */
   float *lse;              /* fwd: output; bwd: input.  BHSD: contiguous
                               [batch, heads, seqlen_q]; THD: contiguous
-                              [heads, total_q] (the "HT" layout). */
+                              [heads, total_q] (the "HT" layout), or
+                              [total_q, heads] with ATTN_FLAG_LSE_TH. */
   const int32_t *cu_seqlens_q; /* THD: device int32[batch+1]; BHSD: NULL */
   const int32_t *cu_seqlens_k; /* THD: device int32[batch+1]; BHSD: NULL */
   int64_t q_stride[3];     /* element strides {batch, head, row}; the */

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(HERE, "libsdpa20.so")
 
 WINDOW_INF = 2147483647
 PARAMS_VERSION = 1
+FLAG_LSE_TH = 1  # ATTN_FLAG_LSE_TH: packed LSE as [T, H]
 FP32, FP16, BF16 = 0, 1, 2
 BHSD, THD = 0, 1
 TOP_LEFT, BOTTOM_RIGHT = 0, 1
@@ -115,11 +116,21 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _lse_flags(lse_layout: str, packed: bool) -> int:
+    if lse_layout == "ht":
+        return 0
+    if lse_layout == "th" and packed:
+        return FLAG_LSE_TH
+    raise ValueError("lse_layout is 'ht', or 'th' for packed [T, H, D] inputs")
+
+
 def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens_k,
-               max_seqlen_q, max_seqlen_k) -> FwdParams:
-    """Fill an attn_fwd_params from tensors (no device work)."""
+               max_seqlen_q, max_seqlen_k, lse_layout="ht") -> FwdParams:
+    """Fill an attn_fwd_params from tensors (no device work).  ``lse_layout``
+    'th' (packed inputs only) stores LSE as [T, H] instead of [H, T]."""
     p = FwdParams()
     p.version = PARAMS_VERSION
+    p.flags = _lse_flags(lse_layout, q.dim() == 3)
     if q.dtype not in _DTYPE:
         raise TypeError(f"unsupported dtype {q.dtype}")
     p.dtype = _DTYPE[q.dtype]
@@ -176,8 +187,9 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Option
              window: Tuple[int, int] = (WINDOW_INF, WINDOW_INF), diag="top_left",
              cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
              max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
-             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
-    """Forward: returns (O, LSE).  LSE is fp32 [B, H, Sq] (dense) or [H, T] (packed)."""
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, lse_layout: str = "ht"):
+    """Forward: returns (O, LSE).  LSE is fp32 [B, H, Sq] (dense), [H, T]
+    (packed) or [T, H] (packed, ``lse_layout='th'``)."""
     _check_inputs(q, k, v)
     dev = q.device
     if scale is None:
@@ -186,13 +198,14 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Option
     if q.dim() == 3:
         max_seqlen_q = _max_len(cu_q) if max_seqlen_q is None else max_seqlen_q
         max_seqlen_k = _max_len(cu_k) if max_seqlen_k is None else max_seqlen_k
-        lse_shape = (q.shape[1], q.shape[0])
+        lse_shape = (q.shape[1], q.shape[0]) if lse_layout == "ht" else (q.shape[0], q.shape[1])
     else:
         lse_shape = tuple(q.shape[:3])
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     lse = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse is None else lse
     p = fwd_params(q, k, v, o, lse, scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q,
-                   cu_seqlens_k=cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+                   cu_seqlens_k=cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                   lse_layout=lse_layout)
     rc = lib().attn_fwd(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
     if rc:
         raise AttnError("attn_fwd", rc)
@@ -213,7 +226,7 @@ def bwd_params(dout, q, k, v, o, lse, dq, dk, dv, workspace, **kw) -> BwdParams:
 
 def prepare_bwd(dout, q, k, v, o, lse, *, scale=None, window=(WINDOW_INF, WINDOW_INF), diag="top_left",
                 cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-                dq=None, dk=None, dv=None, workspace=None):
+                dq=None, dk=None, dv=None, workspace=None, lse_layout="ht"):
     """Allocate the outputs and workspace of a backward and fill its params
     once, for callers that launch it repeatedly or step by step.  Returns
     (params, (dq, dk, dv, workspace)); the tensors must outlive every launch
@@ -230,7 +243,7 @@ def prepare_bwd(dout, q, k, v, o, lse, *, scale=None, window=(WINDOW_INF, WINDOW
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     kw = dict(scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, lse_layout=lse_layout)
     p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **kw)
     if workspace is None:
         need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))
@@ -259,8 +272,10 @@ def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
              cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
              max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """Backward: returns (dQ, dK, dV) given the forward's O and LSE."""
+             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             lse_layout: str = "ht"):
+    """Backward: returns (dQ, dK, dV) given the forward's O and LSE (in the
+    layout ``lse_layout`` names, as for attn_fwd)."""
     _check_inputs(q, k, v, o, dout)
     dev = q.device
     if scale is None:
@@ -273,7 +288,7 @@ def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     kw = dict(scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, lse_layout=lse_layout)
     p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **kw)
     if workspace is None:
         need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))

@@ -64,7 +64,8 @@ int64_t k_rows(const attn_fwd_params* p) {
 
 hipError_t check_problem(const attn_fwd_params* p) {
   if (!p) return hipErrorInvalidValue;
-  if (p->version != ATTN_PARAMS_VERSION || p->flags != 0 || p->reserved0 != 0)
+  if (p->version != ATTN_PARAMS_VERSION || (p->flags & ~ATTN_FLAG_LSE_TH) != 0 || p->reserved0 != 0 ||
+      ((p->flags & ATTN_FLAG_LSE_TH) && p->layout != ATTN_THD))
     return hipErrorInvalidValue;
   if (!dtype_ok(p->dtype)) return hipErrorInvalidValue;
   if (p->layout != ATTN_BHSD && p->layout != ATTN_THD) return hipErrorInvalidValue;
@@ -138,6 +139,13 @@ sdpa::ProblemArgs problem_args(const attn_fwd_params* p) {
   } else {
     a.lse_sb = (int64_t)p->heads * p->seqlen_q;
     a.lse_sh = p->seqlen_q;
+  }
+  a.olse_sb = a.lse_sb;
+  a.olse_sh = a.lse_sh;
+  a.olse_ss = 1;
+  if (p->flags & ATTN_FLAG_LSE_TH) {  // [total_q, heads]
+    a.olse_sh = 1;
+    a.olse_ss = p->heads;
   }
   a.total_q = a.varlen ? p->total_q : 0;
   return a;

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a, long long 
   if (c == 0) {
     const long long idx = b * P.lse_sb + h * P.lse_sh + i;
     a.delta[idx] = s;
-    a.lse2[idx] = a.lse[idx] * kLog2e;  // +inf (empty row) stays +inf
+    a.lse2[idx] = a.lse[b * P.olse_sb + h * P.olse_sh + i * P.olse_ss] * kLog2e;  // +inf (empty row) stays +inf
   }
 }
 
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const T* dop = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + q0 * a.dout.ss;
   T* dkp = (T*)a.dk.ptr + b * a.dk.sb + h * a.dk.sh + k0 * a.dk.ss;
   T* dvp = (T*)a.dv.ptr + b * a.dv.sb + h * a.dv.sh + k0 * a.dv.ss;
-  const float* lsep = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  const float* lsep = a.lse + b * P.olse_sb + h * P.olse_sh + q0 * P.olse_ss;
   const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
 
   // Queries that can see the block's keys.
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
       dos.load(dop + (long long)i0 * a.dout.ss, a.dout.ss, sq - i0, tid);
       if (tid < BMQ) {
         const bool ok = i0 + tid < sq;
-        st_l = ok ? lsep[i0 + tid] * kLog2e : INFINITY;
+        st_l = ok ? lsep[(i0 + tid) * P.olse_ss] * kLog2e : INFINITY;
         st_d = ok ? delp[i0 + tid] : 0.f;
       }
     };
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
   const T* dop = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + q0 * a.dout.ss;
   T* dqp = (T*)a.dq.ptr + b * a.dq.sb + h * a.dq.sh + q0 * a.dq.ss;
-  const float* lsep = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  const float* lsep = a.lse + b * P.olse_sb + h * P.olse_sh + q0 * P.olse_ss;
   const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
 
   const int ilast = min(i0 + BM, sq) - 1;
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   RowFrags<M, D> qf, dof;
   qf.load(qp + (long long)qi * a.q.ss, row_ok, g);
   dof.load(dop + (long long)qi * a.dout.ss, row_ok, g);
-  const float lse2 = row_ok ? lsep[qi] * kLog2e : INFINITY;
+  const float lse2 = row_ok ? lsep[qi * P.olse_ss] * kLog2e : INFINITY;
   const float delta = row_ok ? delp[qi] : 0.f;
 
   if constexpr (DPAD != D) {

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
   const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
   T* op = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + q0 * a.o.ss;
-  float* lp = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  float* lp = a.lse + b * P.olse_sb + h * P.olse_sh + q0 * P.olse_ss;
 
   // Keys the block can see.
   const int ilast = min(i0 + BM, sq) - 1;
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
             store4<T>(orow + d, acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
                       acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
         }
-      if (g == 0) lp[qi] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+      if (g == 0) lp[qi * P.olse_ss] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
     }
   }
 }
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
   const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
   T* op = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + q0 * a.o.ss;
-  float* lp = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  float* lp = a.lse + b * P.olse_sb + h * P.olse_sh + q0 * P.olse_ss;
 
   // Keys the block can see, and the tiles of this wave's rows.
   const int ilast = min(i0 + BM, sq) - 1;
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
               store4<T>(orow + d, acc[rb][dt][4 * q4] * inv, acc[rb][dt][4 * q4 + 1] * inv,
                         acc[rb][dt][4 * q4 + 2] * inv, acc[rb][dt][4 * q4 + 3] * inv);
           }
-        if (g == 0) lp[qi] = lt > 0.f ? (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+        if (g == 0) lp[qi * P.olse_ss] = lt > 0.f ? (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
       }
     }
   }
@@ -732,7 +732,7 @@ attn_fwd16pp_kernel(FwdArgs a, int nq) {
 
   const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
   T* op = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + q0 * a.o.ss;
-  float* lp = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  float* lp = a.lse + b * P.olse_sb + h * P.olse_sh + q0 * P.olse_ss;
 
   const int ilast = min(i0 + BM, sq) - 1;
   const long long jlo = max(0LL, (long long)i0 + w.lo);
@@ -824,7 +824,7 @@ attn_fwd16pp_kernel(FwdArgs a, int nq) {
             store4<T>(orow + d, acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv, acc[dt][4 * q4 + 2] * inv,
                       acc[dt][4 * q4 + 3] * inv);
         }
-      if (g == 0) lp[qi] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+      if (g == 0) lp[qi * P.olse_ss] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
     }
   }
 }
@@ -885,7 +885,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
   const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
   T* op = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + q0 * a.o.ss;
-  float* lp = a.lse + b * P.lse_sb + h * P.lse_sh + q0;
+  float* lp = a.lse + b * P.olse_sb + h * P.olse_sh + q0 * P.olse_ss;
 
   const int ilast = min(i0 + 64, sq) - 1;
   const long long jlo = max(0LL, (long long)i0 + w.lo);
@@ -998,7 +998,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     (acc[0][dt][4 * q4 + 1] * a0 + o1.y * a1) * inv, (acc[0][dt][4 * q4 + 2] * a0 + o1.z * a1) * inv,
                     (acc[0][dt][4 * q4 + 3] * a0 + o1.w * a1) * inv);
       }
-    if (g == 0) lp[qi] = lt > 0.f ? (mm + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+    if (g == 0) lp[qi * P.olse_ss] = lt > 0.f ? (mm + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
   }
 }
 

@@ -22,7 +22,8 @@ struct ProblemArgs {
   int wl, wr, diag;
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
-  long long lse_sb, lse_sh;  // LSE / Delta: base + b*lse_sb + h*lse_sh + row
+  long long lse_sb, lse_sh;  // workspace (Delta, LSE log2 e): base + b*lse_sb + h*lse_sh + row
+  long long olse_sb, olse_sh, olse_ss;  // the caller's LSE: + b*sb + h*sh + row*ss
   long long total_q;         // packed layout: rows of Q
 };
 

@@ -246,3 +246,20 @@ def test_workspace_size():
     bad = bwd_params(dense_params())
     bad.fwd.version = 9
     assert bd.lib().attn_bwd_workspace_size(ctypes.byref(bad)) == 0
+
+
+def test_lse_th_flag():
+    """ATTN_FLAG_LSE_TH is accepted for the packed layout only; other flag
+    bits stay reserved.  The binding's value is the header's."""
+    hdr = open(os.path.join(ROOT, "include", "attn.h")).read()
+    assert int(re.search(r"#define ATTN_FLAG_LSE_TH (\d+)u", hdr).group(1)) == bd.FLAG_LSE_TH
+    p = packed_params()
+    p.flags = bd.FLAG_LSE_TH
+    assert fcheck(p) == OK
+    assert bcheck(bwd_params(p)) == OK
+    p.flags = 2
+    assert fcheck(p) == INVALID
+    p = dense_params()
+    p.flags = bd.FLAG_LSE_TH
+    assert fcheck(p) == INVALID
+    assert bcheck(bwd_params(p)) == INVALID

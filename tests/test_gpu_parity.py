@@ -267,3 +267,24 @@ def test_negative_row_strides(dtype, D, sq, sk, window, diag):
         torch.cuda.synchronize()
         for name, (st, _, _), ref in zip(("dq", "dk", "dv"), outs, (dq, dk, dv)):
             assert torch.equal(st.flip(2), ref), f"{entry} {name}"
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float16, 80), (torch.float32, 64)])
+def test_packed_lse_th_layout(dtype, D):
+    """Packed LSE stored [T, H] (ATTN_FLAG_LSE_TH): the forward writes the
+    transpose of its [H, T] result, the backward reads it and returns the
+    same gradients, bit for bit; the [H, T] run itself matches the oracle."""
+    c = Case(layout="thd", H=3, D=D, dtype=dtype, window=(64, 0), diag="bottom_right",
+             lens_q=[37, 0, 130, 64, 1], lens_k=[50, 3, 129, 64, 0], seed=960)
+    dev = "cuda"
+    q, k, v, do = (t.to(dev) for t in c.cpu)
+    kw = c.kw_gpu(dev)
+    o1, l1 = bd.attn_fwd(q, k, v, **kw)
+    o2, l2 = bd.attn_fwd(q, k, v, lse_layout="th", **kw)
+    assert l2.shape == (q.shape[0], q.shape[1])
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1.t(), l2)
+    g1 = bd.attn_bwd(do, q, k, v, o1, l1, **kw)
+    g2 = bd.attn_bwd(do, q, k, v, o2, l2, lse_layout="th", **kw)
+    for name, a, b in zip(("dq", "dk", "dv"), g1, g2):
+        assert torch.equal(a, b), name
+    c.check(dev=dev)
