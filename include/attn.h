@@ -58,7 +58,7 @@ extern "C" {
 /* Version of the params structs below; a mismatch is hipErrorInvalidValue
  * (the versioned-params idea of the AOTriton 0.15b release notes, "API
  * Changes": kVersion fields, reserved bits rejected). */
-#define ATTN_PARAMS_VERSION 1u
+#define ATTN_PARAMS_VERSION 2u
 
 /* Bits of attn_fwd_params.flags; every other bit must be 0.
  * ATTN_FLAG_LSE_TH (packed layout only): lse is [total_q, heads] (the "TH"
@@ -121,6 +121,17 @@ typedef struct {
   int64_t o_stride[3];     /* aligned.  A stride may be negative: the
                               pointer is then the address of index 0 on that
                               axis, and the operand reaches below it. */
+  const int32_t *seqused_q; /* optional device int32[batch]: sequence b uses
+                              only its first seqused_q[b] query rows (of
+                              seqlen_q rows, BHSD, or of its cu_seqlens_q
+                              range, THD); NULL = all rows */
+  const int32_t *seqused_k; /* optional, the same for keys ("seqused_k" of
+                              a packed KV cache, VarlenBits of the AOTriton
+                              0.14b notes).  Rows past the used ones are
+                              written as fully masked: O = 0, LSE = +inf,
+                              dQ = dK = dV = 0.  0 <= seqused[b] <= the
+                              sequence's rows is a precondition (values out
+                              of range are clamped, never read past). */
 } attn_fwd_params;
 
 typedef struct {

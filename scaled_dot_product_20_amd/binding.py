@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsdpa20.so")
 
 WINDOW_INF = 2147483647
-PARAMS_VERSION = 1
+PARAMS_VERSION = 2
 FLAG_LSE_TH = 1  # ATTN_FLAG_LSE_TH: packed LSE as [T, H]
 FP32, FP16, BF16 = 0, 1, 2
 BHSD, THD = 0, 1
@@ -48,6 +48,7 @@ class FwdParams(ctypes.Structure):
         ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
         ("q_stride", _I64x3), ("k_stride", _I64x3), ("v_stride", _I64x3), ("o_stride", _I64x3),
+        ("seqused_q", ctypes.c_void_p), ("seqused_k", ctypes.c_void_p),
     ]
 
 
@@ -124,10 +125,20 @@ def _lse_flags(lse_layout: str, packed: bool) -> int:
     raise ValueError("lse_layout is 'ht', or 'th' for packed [T, H, D] inputs")
 
 
+def _seqused(t: Optional[torch.Tensor], batch: int, dev):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.numel() != batch or not t.is_contiguous() or t.device != dev:
+        raise ValueError("seqused_q / seqused_k are contiguous int32 [batch] tensors on the inputs' device")
+    return t
+
+
 def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens_k,
-               max_seqlen_q, max_seqlen_k, lse_layout="ht") -> FwdParams:
+               max_seqlen_q, max_seqlen_k, lse_layout="ht", seqused_q=None, seqused_k=None) -> FwdParams:
     """Fill an attn_fwd_params from tensors (no device work).  ``lse_layout``
-    'th' (packed inputs only) stores LSE as [T, H] instead of [H, T]."""
+    'th' (packed inputs only) stores LSE as [T, H] instead of [H, T].
+    ``seqused_q`` / ``seqused_k`` (int32 [batch] on the device): sequence b
+    uses only its first seqused[b] rows; the rest are written as masked."""
     p = FwdParams()
     p.version = PARAMS_VERSION
     p.flags = _lse_flags(lse_layout, q.dim() == 3)
@@ -154,6 +165,8 @@ def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens
         p.cu_seqlens_q, p.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
     else:
         raise ValueError("inputs are [B, H, S, D] or [T, H, D]")
+    p.seqused_q = _ptr(_seqused(seqused_q, p.batch, q.device))
+    p.seqused_k = _ptr(_seqused(seqused_k, p.batch, q.device))
     return p
 
 
@@ -187,7 +200,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Option
              window: Tuple[int, int] = (WINDOW_INF, WINDOW_INF), diag="top_left",
              cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
              max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
-             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, lse_layout: str = "ht"):
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, lse_layout: str = "ht",
+             seqused_q: Optional[torch.Tensor] = None, seqused_k: Optional[torch.Tensor] = None):
     """Forward: returns (O, LSE).  LSE is fp32 [B, H, Sq] (dense), [H, T]
     (packed) or [T, H] (packed, ``lse_layout='th'``)."""
     _check_inputs(q, k, v)
@@ -205,7 +219,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Option
     lse = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse is None else lse
     p = fwd_params(q, k, v, o, lse, scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q,
                    cu_seqlens_k=cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
-                   lse_layout=lse_layout)
+                   lse_layout=lse_layout, seqused_q=seqused_q, seqused_k=seqused_k)
     rc = lib().attn_fwd(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
     if rc:
         raise AttnError("attn_fwd", rc)
@@ -226,7 +240,7 @@ def bwd_params(dout, q, k, v, o, lse, dq, dk, dv, workspace, **kw) -> BwdParams:
 
 def prepare_bwd(dout, q, k, v, o, lse, *, scale=None, window=(WINDOW_INF, WINDOW_INF), diag="top_left",
                 cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-                dq=None, dk=None, dv=None, workspace=None, lse_layout="ht"):
+                dq=None, dk=None, dv=None, workspace=None, lse_layout="ht", seqused_q=None, seqused_k=None):
     """Allocate the outputs and workspace of a backward and fill its params
     once, for callers that launch it repeatedly or step by step.  Returns
     (params, (dq, dk, dv, workspace)); the tensors must outlive every launch
@@ -243,7 +257,8 @@ def prepare_bwd(dout, q, k, v, o, lse, *, scale=None, window=(WINDOW_INF, WINDOW
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     kw = dict(scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, lse_layout=lse_layout)
+              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, lse_layout=lse_layout,
+              seqused_q=seqused_q, seqused_k=seqused_k)
     p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **kw)
     if workspace is None:
         need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))
@@ -273,7 +288,8 @@ def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
              max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
              dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-             lse_layout: str = "ht"):
+             lse_layout: str = "ht", seqused_q: Optional[torch.Tensor] = None,
+             seqused_k: Optional[torch.Tensor] = None):
     """Backward: returns (dQ, dK, dV) given the forward's O and LSE (in the
     layout ``lse_layout`` names, as for attn_fwd)."""
     _check_inputs(q, k, v, o, dout)
@@ -288,7 +304,8 @@ def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     kw = dict(scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, lse_layout=lse_layout)
+              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, lse_layout=lse_layout,
+              seqused_q=seqused_q, seqused_k=seqused_k)
     p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **kw)
     if workspace is None:
         need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))

@@ -148,6 +148,8 @@ sdpa::ProblemArgs problem_args(const attn_fwd_params* p) {
     a.olse_ss = p->heads;
   }
   a.total_q = a.varlen ? p->total_q : 0;
+  a.used_q = p->seqused_q;
+  a.used_k = p->seqused_k;
   return a;
 }
 

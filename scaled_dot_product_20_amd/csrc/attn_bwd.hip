@@ -112,14 +112,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int kb = gp.i;
 
-  long long q0 = 0, k0 = 0;
-  int sq = P.Sq, sk = P.Sk;
-  if (P.varlen) {
-    q0 = P.cu_q[b];
-    sq = P.cu_q[b + 1] - (int)q0;
-    k0 = P.cu_k[b];
-    sk = P.cu_k[b + 1] - (int)k0;
-  }
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
   const int j0 = kb * BNK;
   if (j0 >= sk) return;
   const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
@@ -287,14 +282,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
-  long long q0 = 0, k0 = 0;
-  int sq = P.Sq, sk = P.Sk;
-  if (P.varlen) {
-    q0 = P.cu_q[b];
-    sq = P.cu_q[b + 1] - (int)q0;
-    k0 = P.cu_k[b];
-    sk = P.cu_k[b + 1] - (int)k0;
-  }
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
   const int i0 = qb * BM;
   if (i0 >= sq) return;
   const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
@@ -508,14 +498,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int kb = gp.i;
 
-  long long q0 = 0, k0 = 0;
-  int sq = P.Sq, sk = P.Sk;
-  if (P.varlen) {
-    q0 = P.cu_q[b];
-    sq = P.cu_q[b + 1] - (int)q0;
-    k0 = P.cu_k[b];
-    sk = P.cu_k[b + 1] - (int)k0;
-  }
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
   const int j0 = kb * BNK;
   if (j0 >= sk) return;
   const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
@@ -867,14 +852,9 @@ __device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int kb = gp.i;
 
-  long long q0 = 0, k0 = 0;
-  int sq = P.Sq, sk = P.Sk;
-  if (P.varlen) {
-    q0 = P.cu_q[b];
-    sq = P.cu_q[b + 1] - (int)q0;
-    k0 = P.cu_k[b];
-    sk = P.cu_k[b + 1] - (int)k0;
-  }
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
   const int j0 = kb * BNK;
   if (j0 >= sk) return;
   const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
@@ -1165,14 +1145,9 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
-  long long q0 = 0, k0 = 0;
-  int sq = P.Sq, sk = P.Sk;
-  if (P.varlen) {
-    q0 = P.cu_q[b];
-    sq = P.cu_q[b + 1] - (int)q0;
-    k0 = P.cu_k[b];
-    sk = P.cu_k[b + 1] - (int)k0;
-  }
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
   const int i0 = qb * BM;
   if (i0 >= sq) return;
   const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
@@ -1399,12 +1374,18 @@ static hipError_t launch_bwd_d(int head_dim, const BwdArgs& a, int stages, hipSt
 }
 
 hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, hipStream_t stream) {
+  hipError_t err;
   switch (dtype) {
-    case 0: return launch_bwd_d<MmaF32>(head_dim, a, stages, stream);
-    case 1: return launch_bwd_d<MmaF16>(head_dim, a, stages, stream);
-    case 2: return launch_bwd_d<MmaBF16>(head_dim, a, stages, stream);
+    case 0: err = launch_bwd_d<MmaF32>(head_dim, a, stages, stream); break;
+    case 1: err = launch_bwd_d<MmaF16>(head_dim, a, stages, stream); break;
+    case 2: err = launch_bwd_d<MmaBF16>(head_dim, a, stages, stream); break;
     default: return hipErrorNotSupported;
   }
+  // Rows past the used ones (seqused arrays): dQ, and dK / dV, are zero.
+  const int esz = dtype == 0 ? 4 : 2, rb = head_dim * esz;
+  if (err == hipSuccess && (stages & kStageDq)) err = launch_pad_rows(a.p, a.dq, Operand{}, nullptr, 0, rb, esz, stream);
+  if (err == hipSuccess && (stages & kStageDkDv)) err = launch_pad_rows(a.p, a.dk, a.dv, nullptr, 1, rb, esz, stream);
+  return err;
 }
 
 }  // namespace sdpa

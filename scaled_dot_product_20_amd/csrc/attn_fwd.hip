@@ -67,14 +67,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;  // longest rows (under causal) first
 
-  long long q0 = 0, k0 = 0;
-  int sq = P.Sq, sk = P.Sk;
-  if (P.varlen) {
-    q0 = P.cu_q[b];
-    sq = P.cu_q[b + 1] - (int)q0;
-    k0 = P.cu_k[b];
-    sk = P.cu_k[b + 1] - (int)k0;
-  }
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
   const int i0 = qb * BM;
   if (i0 >= sq) return;
   const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
@@ -364,14 +359,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
-  long long q0 = 0, k0 = 0;
-  int sq = P.Sq, sk = P.Sk;
-  if (P.varlen) {
-    q0 = P.cu_q[b];
-    sq = P.cu_q[b + 1] - (int)q0;
-    k0 = P.cu_k[b];
-    sk = P.cu_k[b + 1] - (int)k0;
-  }
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
   const int i0 = qb * BM;
   if (i0 >= sq) return;
   const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
@@ -718,14 +708,9 @@ attn_fwd16pp_kernel(FwdArgs a, int nq) {
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
-  long long q0 = 0, k0 = 0;
-  int sq = P.Sq, sk = P.Sk;
-  if (P.varlen) {
-    q0 = P.cu_q[b];
-    sq = P.cu_q[b + 1] - (int)q0;
-    k0 = P.cu_k[b];
-    sk = P.cu_k[b + 1] - (int)k0;
-  }
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
   const int i0 = qb * BM;
   if (i0 >= sq) return;
   const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
@@ -869,14 +854,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int bh = P.varlen ? L % nbh : L / nq, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - (P.varlen ? L / nbh : L % nq);
 
-  long long q0 = 0, k0 = 0;
-  int sq = P.Sq, sk = P.Sk;
-  if (P.varlen) {
-    q0 = P.cu_q[b];
-    sq = P.cu_q[b + 1] - (int)q0;
-    k0 = P.cu_k[b];
-    sk = P.cu_k[b + 1] - (int)k0;
-  }
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
   const int i0 = qb * 256 + 64 * sub;
   if (i0 >= sq) return;
   const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
@@ -1072,13 +1052,78 @@ static hipError_t launch_fwd_d(int head_dim, const FwdArgs& a, hipStream_t strea
   }
 }
 
+// ------------------------------------------------ rows past the used ones
+//
+// With seqused arrays, the rows of a sequence past its used rows take part
+// in no attention: they are written as fully masked rows (zeros, LSE +inf).
+// One workgroup per (sequence, head); 16-byte stores.
+struct PadArgs {
+  ProblemArgs p;
+  Operand t[2];  // tensors whose padding rows are zeroed (null: none)
+  float* lse;    // LSE rows set to +inf (query side of the forward), or null
+  int side;      // 0: query rows (seqused_q), 1: key rows (seqused_k)
+  int chunks;    // 16-byte chunks per row
+  int esz;       // element size of t
+};
+
+__global__ __launch_bounds__(256) void attn_pad_rows_kernel(PadArgs a) {
+  const ProblemArgs& P = a.p;
+  const int h = (int)(blockIdx.x % P.H), b = (int)(blockIdx.x / P.H);
+  const int* used = a.side ? P.used_k : P.used_q;
+  long long r0 = 0;
+  int n = a.side ? P.Sk : P.Sq;
+  if (P.varlen) {
+    const int* cu = a.side ? P.cu_k : P.cu_q;
+    r0 = cu[b];
+    n = cu[b + 1] - (int)r0;
+  }
+  const int u = max(0, min(n, used[b]));
+  const long long work = (long long)(n - u) * a.chunks;
+  for (long long x = threadIdx.x; x < work; x += 256) {
+    const long long row = r0 + u + x / a.chunks;
+    const int c = (int)(x % a.chunks);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (a.t[i].ptr) {
+        char* p = (char*)a.t[i].ptr + (b * a.t[i].sb + h * a.t[i].sh + row * a.t[i].ss) * a.esz + 16 * c;
+        *reinterpret_cast<uint4*>(p) = make_uint4(0, 0, 0, 0);
+      }
+  }
+  if (a.lse)
+    for (int x = threadIdx.x; x < n - u; x += 256)
+      a.lse[b * P.olse_sb + h * P.olse_sh + (r0 + u + x) * P.olse_ss] = INFINITY;
+}
+
+hipError_t launch_pad_rows(const ProblemArgs& p, Operand t0, Operand t1, float* lse, int side, int row_bytes,
+                           int esz, hipStream_t stream) {
+  if ((side ? p.used_k : p.used_q) == nullptr) return hipSuccess;
+  const long long nblk = (long long)p.B * p.H;
+  if (nblk == 0) return hipSuccess;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+  PadArgs a{};
+  a.p = p;
+  a.t[0] = t0;
+  a.t[1] = t1;
+  a.lse = lse;
+  a.side = side;
+  a.chunks = row_bytes / 16;
+  a.esz = esz;
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_pad_rows_kernel), dim3((unsigned)nblk), dim3(256), args,
+                         0, stream);
+}
+
 hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, hipStream_t stream) {
+  hipError_t err;
   switch (dtype) {
-    case 0: return launch_fwd_d<MmaF32>(head_dim, a, stream);
-    case 1: return launch_fwd_d<MmaF16>(head_dim, a, stream);
-    case 2: return launch_fwd_d<MmaBF16>(head_dim, a, stream);
+    case 0: err = launch_fwd_d<MmaF32>(head_dim, a, stream); break;
+    case 1: err = launch_fwd_d<MmaF16>(head_dim, a, stream); break;
+    case 2: err = launch_fwd_d<MmaBF16>(head_dim, a, stream); break;
     default: return hipErrorNotSupported;
   }
+  if (err != hipSuccess) return err;
+  const int esz = dtype == 0 ? 4 : 2;
+  return launch_pad_rows(a.p, a.o, Operand{}, a.lse, 0, head_dim * esz, esz, stream);
 }
 
 }  // namespace sdpa

@@ -25,7 +25,29 @@ struct ProblemArgs {
   long long lse_sb, lse_sh;  // workspace (Delta, LSE log2 e): base + b*lse_sb + h*lse_sh + row
   long long olse_sb, olse_sh, olse_ss;  // the caller's LSE: + b*sb + h*sh + row*ss
   long long total_q;         // packed layout: rows of Q
+  const int* used_q;         // optional: rows of sequence b in use (seqused_q)
+  const int* used_k;
 };
+
+// Rows of sequence b: Q rows q0 .. q0+sq-1 and K rows k0 .. k0+sk-1 (packed:
+// its cu_seqlens range; dense: all rows), cut to the used rows when the
+// caller gives seqused arrays.  Every kernel computes on these rows only.
+// (A template so that P may also sit in the kernel-argument segment.)
+template <class PA>
+__device__ __forceinline__ void seq_rows(PA& P, int b, long long& q0, int& sq, long long& k0, int& sk) {
+  q0 = 0;
+  k0 = 0;
+  sq = P.Sq;
+  sk = P.Sk;
+  if (P.varlen) {
+    q0 = P.cu_q[b];
+    sq = P.cu_q[b + 1] - (int)q0;
+    k0 = P.cu_k[b];
+    sk = P.cu_k[b + 1] - (int)k0;
+  }
+  if (P.used_q) sq = max(0, min(sq, P.used_q[b]));
+  if (P.used_k) sk = max(0, min(sk, P.used_k[b]));
+}
 
 struct FwdArgs {
   ProblemArgs p;
@@ -69,6 +91,11 @@ inline int device_cu_count() {
 
 // dtype codes follow the C ABI: 0 fp32, 1 fp16, 2 bf16.
 hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, hipStream_t stream);
+// Rows past the used rows of every sequence (seqused_q for side 0, seqused_k
+// for side 1): zeros in t0 and t1 (null pointers skipped) and, when lse is
+// given, LSE = +inf.  Rows are row_bytes long (a multiple of 16).
+hipError_t launch_pad_rows(const ProblemArgs& p, Operand t0, Operand t1, float* lse, int side, int row_bytes,
+                           int esz, hipStream_t stream);
 hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, hipStream_t stream);
 
 }  // namespace sdpa

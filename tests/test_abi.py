@@ -128,7 +128,7 @@ def test_valid_calls_pass():
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("version", 2, INVALID), ("flags", 1, INVALID), ("reserved0", 3, INVALID),
+    ("version", 1, INVALID), ("version", 3, INVALID), ("flags", 1, INVALID), ("reserved0", 3, INVALID),
     ("dtype", 7, INVALID), ("layout", 5, INVALID), ("diag", 2, INVALID),
     ("heads", 0, INVALID), ("head_dim", 0, INVALID), ("seqlen_q", -1, INVALID),
     ("seqlen_k", -5, INVALID), ("batch", -1, INVALID),

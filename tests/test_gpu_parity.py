@@ -288,3 +288,90 @@ def test_packed_lse_th_layout(dtype, D):
     for name, a, b in zip(("dq", "dk", "dv"), g1, g2):
         assert torch.equal(a, b), name
     c.check(dev=dev)
+
+
+def _used_rows_case(layout, dtype, D, window, diag, seed):
+    """A packed problem of `used` rows per sequence (the oracle checks it),
+    and the same rows spread into larger per-sequence ranges (packed) or a
+    padded [B, H, S, D] tensor, with NaN in every row past the used ones."""
+    used_q, used_k = [37, 0, 130, 64, 9], [50, 3, 129, 64, 0]
+    alloc_q, alloc_k = [45, 7, 130, 100, 9], [60, 3, 200, 64, 12]
+    c = Case(layout="thd", H=2, D=D, dtype=dtype, window=window, diag=diag, lens_q=used_q, lens_k=used_k, seed=seed)
+    dev = "cuda"
+    comp = [t.to(dev) for t in c.cpu]  # q, k, v, do packed over the used rows
+    B, H = len(used_q), 2
+
+    def spread(t, used, alloc):
+        if layout == "thd":
+            out = torch.full((sum(alloc), H, D), float("nan"), dtype=dtype, device=dev)
+        else:
+            out = torch.full((B, H, max(alloc), D), float("nan"), dtype=dtype, device=dev)
+        src = dst = 0
+        for b in range(B):
+            if layout == "thd":
+                out[dst:dst + used[b]] = t[src:src + used[b]]
+                dst += alloc[b]
+            else:
+                out[b, :, :used[b]] = t[src:src + used[b]].permute(1, 0, 2)
+            src += used[b]
+        return out
+
+    full = [spread(t, used_q if i in (0, 3) else used_k, alloc_q if i in (0, 3) else alloc_k)
+            for i, t in enumerate(comp)]
+    kw = dict(scale=c.scale, window=window, diag=diag,
+              seqused_q=torch.tensor(used_q, dtype=torch.int32, device=dev),
+              seqused_k=torch.tensor(used_k, dtype=torch.int32, device=dev))
+    if layout == "thd":
+        kw.update(cu_seqlens_q=torch.from_numpy(wl_prefix(alloc_q)).to(dev),
+                  cu_seqlens_k=torch.from_numpy(wl_prefix(alloc_k)).to(dev),
+                  max_seqlen_q=max(alloc_q), max_seqlen_k=max(alloc_k))
+    return c, comp, full, kw, (used_q, used_k, alloc_q, alloc_k)
+
+
+def wl_prefix(lengths):
+    from scaled_dot_product_20_amd import workloads as wls
+    return wls.prefix(lengths)
+
+
+@pytest.mark.parametrize("layout", ["thd", "bhsd"])
+@pytest.mark.parametrize("dtype,D,window,diag", [
+    (torch.bfloat16, 128, (INF, INF), "top_left"),
+    (torch.float16, 64, (40, 0), "bottom_right"),
+    (torch.float32, 80, (INF, 0), "top_left"),
+    (torch.bfloat16, 48, (1 << 30, 3), "bottom_right"),
+])
+def test_seqused_rows(layout, dtype, D, window, diag):
+    """seqused_q / seqused_k: sequence b computes on its first used rows only
+    (bottom-right windows shift by the used lengths), bit for bit as the
+    compact packed problem of those rows, which matches the oracle; rows
+    past them (NaN in the inputs) come out as fully masked rows: O = 0,
+    LSE = +inf, dQ = dK = dV = 0."""
+    c, comp, full, kw, (uq, uk, aq, ak) = _used_rows_case(layout, dtype, D, window, diag, seed=970)
+    dev = "cuda"
+    o_c, l_c = bd.attn_fwd(*comp[:3], **c.kw_gpu(dev))
+    g_c = bd.attn_bwd(comp[3], *comp[:3], o_c, l_c, **c.kw_gpu(dev))
+    o_f, l_f = bd.attn_fwd(*full[:3], **kw)
+    g_f = bd.attn_bwd(full[3], *full[:3], o_f, l_f, **kw)
+    H = comp[0].shape[1]
+    sq_c = sk_c = sq_f = sk_f = 0
+    for b in range(len(uq)):
+        def rows_f(t, start, b, n, alloc):
+            return t[start:start + alloc] if layout == "thd" else t[b].permute(1, 0, 2)[:alloc]
+        of = rows_f(o_f, sq_f, b, uq[b], aq[b])
+        assert torch.equal(of[:uq[b]], o_c[sq_c:sq_c + uq[b]]), ("o", b)
+        assert torch.count_nonzero(of[uq[b]:]) == 0, ("o pad", b)
+        lf = l_f[:, sq_f:sq_f + aq[b]] if layout == "thd" else l_f[b, :, :aq[b]]
+        assert torch.equal(lf[:, :uq[b]], l_c[:, sq_c:sq_c + uq[b]]), ("lse", b)
+        assert bool(torch.all(lf[:, uq[b]:] == float("inf"))), ("lse pad", b)
+        dqf = rows_f(g_f[0], sq_f, b, uq[b], aq[b])
+        assert torch.equal(dqf[:uq[b]], g_c[0][sq_c:sq_c + uq[b]]), ("dq", b)
+        assert torch.count_nonzero(dqf[uq[b]:]) == 0, ("dq pad", b)
+        for name, gf, gc in (("dk", g_f[1], g_c[1]), ("dv", g_f[2], g_c[2])):
+            kf = rows_f(gf, sk_f, b, uk[b], ak[b])
+            assert torch.equal(kf[:uk[b]], gc[sk_c:sk_c + uk[b]]), (name, b)
+            assert torch.count_nonzero(kf[uk[b]:]) == 0, (name + " pad", b)
+        sq_c += uq[b]
+        sk_c += uk[b]
+        sq_f += aq[b]
+        sk_f += ak[b]
+    c.check(dev=dev)
