@@ -48,56 +48,39 @@ __device__ __forceinline__ float dot_chunk(uint4 x, uint4 y) {
 
 // Delta_i = sum_d dO_id * O_id in fp32, one group of G lanes per row, each
 // lane one 16-byte chunk; beside it LSE_i * log2(e), the form the 16-bit
-// kernels use.  Rows are (b, h, i) for the dense layout and (packed row t,
-// h) for the packed one.  A group takes kPreRows rows spaced 256 / G apart,
-// so each lane has 2 * kPreRows loads in flight.
-constexpr int kPreRows = 4;
-
+// kernels use.  Rows are (b, h, i) for the dense layout and
+// (packed row t, h) for the packed one.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a, long long nrows) {
   constexpr int CE = 16 / (int)sizeof(T), CH = D / CE;
-  constexpr int G = CH <= 8 ? 8 : (CH <= 16 ? 16 : 32), RPB = 256 / G;
+  constexpr int G = CH <= 8 ? 8 : (CH <= 16 ? 16 : 32);
   const ProblemArgs& P = a.p;
+  const long long row = (long long)blockIdx.x * (256 / G) + threadIdx.x / G;
   const int c = threadIdx.x % G;
-  const long long row0 = (long long)blockIdx.x * (RPB * kPreRows) + threadIdx.x / G;
-  float s[kPreRows];
-  long long bb[kPreRows], hh[kPreRows], ii[kPreRows];
-#pragma unroll
-  for (int u = 0; u < kPreRows; ++u) {
-    const long long row = row0 + u * RPB;
-    long long b = 0, h = 0, i = 0;
-    if (row < nrows) {
-      if (P.varlen) {
-        i = row / P.H;  // packed row
-        h = row % P.H;
-      } else {
-        const long long bh = row / P.Sq;
-        i = row % P.Sq;
-        h = bh % P.H;
-        b = bh / P.H;
-      }
-    }
-    bb[u] = b;
-    hh[u] = h;
-    ii[u] = i;
-    s[u] = 0.f;
-    if (row < nrows && c < CH) {
-      const T* op = (const T*)a.o.ptr + b * a.o.sb + h * a.o.sh + i * a.o.ss + c * CE;
-      const T* dp = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + i * a.dout.ss + c * CE;
-      s[u] = dot_chunk<T>(*reinterpret_cast<const uint4*>(op), *reinterpret_cast<const uint4*>(dp));
-    }
+  if (row >= nrows) return;  // whole groups leave together
+  long long b, h, i;
+  if (P.varlen) {
+    i = row / P.H;  // packed row
+    h = row % P.H;
+    b = 0;
+  } else {
+    const long long bh = row / P.Sq;
+    i = row % P.Sq;
+    h = bh % P.H;
+    b = bh / P.H;
+  }
+  float s = 0.f;
+  if (c < CH) {
+    const T* op = (const T*)a.o.ptr + b * a.o.sb + h * a.o.sh + i * a.o.ss + c * CE;
+    const T* dp = (const T*)a.dout.ptr + b * a.dout.sb + h * a.dout.sh + i * a.dout.ss + c * CE;
+    s = dot_chunk<T>(*reinterpret_cast<const uint4*>(op), *reinterpret_cast<const uint4*>(dp));
   }
 #pragma unroll
-  for (int u = 0; u < kPreRows; ++u) {
-#pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) s[u] += __shfl_xor(s[u], off, G);
-    const long long row = row0 + u * RPB;
-    if (c == 0 && row < nrows) {
-      const long long b = bb[u], h = hh[u], i = ii[u];
-      const long long idx = b * P.lse_sb + h * P.lse_sh + i;
-      a.delta[idx] = s[u];
-      a.lse2[idx] = a.lse[b * P.olse_sb + h * P.olse_sh + i * P.olse_ss] * kLog2e;  // +inf (empty row) stays +inf
-    }
+  for (int off = G / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, G);
+  if (c == 0) {
+    const long long idx = b * P.lse_sb + h * P.lse_sh + i;
+    a.delta[idx] = s;
+    a.lse2[idx] = a.lse[b * P.olse_sb + h * P.olse_sh + i * P.olse_ss] * kLog2e;  // +inf (empty row) stays +inf
   }
 }
 
@@ -1308,8 +1291,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
         a.p.varlen ? a.p.total_q * a.p.H : (long long)a.p.B * a.p.H * a.p.Sq;
     constexpr int CE = 16 / (int)sizeof(T), CH = D / CE;
     constexpr int G = CH <= 8 ? 8 : (CH <= 16 ? 16 : 32);
-    const long long rpb = (256 / G) * kPreRows;  // rows per block
-    const long long nblk = (nrows + rpb - 1) / rpb;
+    const long long nblk = (nrows + (256 / G) - 1) / (256 / G);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (nblk > 0) {
       long long nr = nrows;
