@@ -31,6 +31,8 @@
  *    AOTriton 0.14b release notes, "Runtime Bug Fixes").  The null stream
  *    means the current device's null stream.
  *  - Every output element is overwritten; nothing needs pre-zeroing.
+ *  - A tensor with no elements (batch 0, or no rows on its side) touches no
+ *    memory: its pointer may be NULL and takes part in no aliasing check.
  *  - Errors are returned, never printed: hipErrorInvalidValue for a malformed
  *    call (null required pointer, version or flags mismatch, negative or
  *    zero sizes where a size is needed, unit-stride or 16-byte alignment

@@ -24,9 +24,12 @@ struct Extent {
 };
 
 // A negative stride reaches below the base pointer: each axis adds
-// (n - 1) * stride elements to the lower or the upper end.
+// (n - 1) * stride elements to the lower or the upper end.  A tensor with no
+// elements touches nothing (its pointer may be NULL).
 Extent extent_of(const void* ptr, const int64_t* stride, int64_t nb, int64_t nh, int64_t nrows,
                  int64_t d, int64_t esz, bool packed) {
+  const uintptr_t base = reinterpret_cast<uintptr_t>(ptr);
+  if ((!packed && nb == 0) || nh == 0 || nrows == 0 || d == 0) return Extent{base, base};
   int64_t below = 0, above = d;  // elements; the last row's head_dim elements
   auto axis = [&](int64_t n, int64_t s) {
     if (n > 1) (s < 0 ? below : above) += (n - 1) * std::llabs(s);
@@ -34,11 +37,10 @@ Extent extent_of(const void* ptr, const int64_t* stride, int64_t nb, int64_t nh,
   if (!packed) axis(nb, stride[0]);
   axis(nh, stride[1]);
   axis(nrows, stride[2]);
-  const uintptr_t base = reinterpret_cast<uintptr_t>(ptr);
   return Extent{base - (uintptr_t)(below * esz), base + (uintptr_t)(above * esz)};
 }
 
-bool overlap(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+bool overlap(Extent a, Extent b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
 bool strides_ok(const int64_t* stride, int64_t esz, bool packed) {
   for (int i = packed ? 1 : 0; i < 3; ++i)

@@ -144,6 +144,39 @@ def test_fwd_validation_errors(field, value, code):
     assert fcheck(p) == code
 
 
+def test_empty_tensors_may_be_null():
+    """A tensor with no elements touches no memory: its pointer may be NULL,
+    and several such NULL pointers do not count as aliasing each other."""
+    cases = []
+    p = dense_params(S=0, Sk=64)               # no query rows: q, o, lse NULL
+    p.q = p.o = p.lse = 0
+    cases.append(p)
+    p = dense_params(S=0, Sk=0)                # nothing at all
+    p.q = p.o = p.lse = p.k = p.v = 0
+    cases.append(p)
+    p = dense_params(B=0)
+    p.q = p.o = p.lse = p.k = p.v = 0
+    cases.append(p)
+    p = packed_params(total_q=0, total_k=0)    # packed, every sequence empty
+    p.q = p.o = p.lse = p.k = p.v = 0
+    cases.append(p)
+    for f in cases:
+        assert fcheck(f) == OK
+        b = bwd_params(f)
+        if f.q == 0:
+            b.dout = b.dq = 0
+        if f.k == 0:
+            b.dk = b.dv = 0
+        assert bcheck(b) == OK
+    p = dense_params(S=0, Sk=64)
+    p.q = 0
+    p.k = 0                                    # k still has rows: required
+    assert fcheck(p) == INVALID
+    p = dense_params(Sk=0)
+    p.o = p.q                                  # aliasing of non-empty tensors still caught
+    assert fcheck(p) == INVALID
+
+
 def test_fwd_validation_strides_and_aliasing():
     p = dense_params()
     p.q_stride = bd._I64x3(3 * 64 * 64, 64 * 64, 60)  # row stride not 16-byte multiple

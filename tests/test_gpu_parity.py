@@ -113,6 +113,22 @@ def test_deterministic_bitwise():
             assert torch.equal(a[n], b[n]), n
 
 
+@pytest.mark.parametrize("kw", [
+    dict(B=1, H=2, Sq=0, Sk=50), dict(B=2, H=1, Sq=33, Sk=0), dict(B=2, H=1, Sq=0, Sk=0),
+    dict(B=0, H=2, Sq=10, Sk=20),
+    dict(layout="thd", H=3, lens_q=[0], lens_k=[0]),
+    dict(layout="thd", H=2, lens_q=[0, 0], lens_k=[5, 0]),
+    dict(layout="thd", H=2, lens_q=[3, 0], lens_k=[0, 0]),
+], ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_zero_size_problems(kw, dtype, D):
+    """Problems with no query rows, no keys or no elements at all (the empty
+    tensors' pointers are NULL): the calls succeed, and whatever has rows
+    comes out as the oracle's fully masked result (O = 0, LSE = +inf,
+    gradients 0)."""
+    Case(D=D, dtype=dtype, seed=16, **kw).check()
+
+
 def test_guard_memory_untouched():
     """Outputs written only inside their rows and head_dim columns (the early
     exit fix bounded by the head dim, AOTriton 0.15b), and no LSE write past
