@@ -3,22 +3,30 @@
 
 One step = the whole path over one batch of synthetic input: attn_fwd (O,
 LSE), then the backward's two calls (attn_bwd_preprocess for Delta, then
-attn_bwd_dkdv_dq, which runs dK/dV and dQ as one fused grid or as two
-kernels), all through the C ABI on torch's current stream.  Inputs are resident in HBM
-before the timed region starts; K steps are timed between a synchronize on
-each side, and every kernel is also bracketed by HIP events on the launch
-stream so its own average duration is known.
+attn_bwd_dkdv_dq for dK, dV and dQ), all through the C ABI on torch's
+current stream.  Inputs are resident in HBM before the timed region starts;
+K steps are timed between a synchronize on each side, and every call is also
+bracketed by HIP events on the launch stream so its own average duration is
+known.
 
 FLOPs are counted on visible (query, key) pairs only: forward 4*D per pair
 (Q K^T and P V), backward 10*D per pair (S recomputed once, dV, dP, dK, dQ).
-The roofline object reports the dominant launch, attn_bwd_dkdv_dq (at
-head_dim 128 one fused dK/dV + dQ kernel where the library takes that path),
-against its own algorithmic work of 14*D FLOPs per visible pair (S, dV, dP,
-dK for dK/dV; S, dP, dQ for dQ) and the bf16/fp16 dense MFMA peak of 2516.6
-TFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP/clk/CU).
+The roofline object reports the call with the largest time share against
+that algorithmic work and the bf16/fp16 dense MFMA peak of 2516.6 TFLOP/s
+(256 CUs x 2.4 GHz x 4096 FLOP/clk/CU); the backward call's executed work
+(S and dP are computed both for dK/dV and for dQ: 14*D per pair) is reported
+beside it as executed_tflops.  The kernels each call launches are the
+library's own plan (attn_fwd_plan / attn_bwd_plan).
 
-The CPU baseline is the fp64 oracle timed on this host on one (sequence,
-head) slice of the same workload, scaled to the same unit.
+Algorithmic HBM bytes: forward reads Q and the K/V rows some query sees and
+writes O and the fp32 LSE; backward reads Q, K, V, O, dO and LSE, writes dQ,
+dK and dV, and writes and reads the fp32 Delta.
+
+Besides the headline workload, the line carries `cells`: the same
+measurement (fewer steps) on every other workload of the pages' shapes.
+
+The CPU baseline is the fp64 oracle timed on this host on (sequence, head)
+slices of the headline workload, scaled to the same unit.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line on stdout; progress goes to stderr.
@@ -29,8 +37,8 @@ import argparse
 import dataclasses
 import hashlib
 import json
-import math
 import os
+import platform
 import sys
 import time
 
@@ -43,20 +51,28 @@ PEAK_MFMA_16 = 2516.6   # TFLOP/s, bf16 and fp16 dense
 PEAK_MFMA_32 = 157.3    # TFLOP/s, fp32
 PEAK_HBM = 8000.0       # GB/s
 DEFAULT_WORKLOAD = "long_6630"
+# The timed cells besides the headline: every workload of the pages' shapes
+# (tiny fp32, BERT-like in fp16 and bf16, gpt2-like causal, both long
+# sequences, packed windowed at head_dim 80 and 128, the 4096-row cell).
+CELLS = [("tiny_f32", "fp32"), ("bert_like", "fp16"), ("bert_like", "bf16"), ("gpt2_like_causal", "bf16"),
+         ("long_6630", "bf16"), ("long_15300", "bf16"), ("varlen_window_d80", "bf16"),
+         ("varlen_window_d128", "bf16"), ("long_4096_bwd", "bf16")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dkdv_traffic_long_6630.txt")
 KERNEL_SOURCES = ["scaled_dot_product_20_amd/csrc/attn_bwd.hip",
                   "scaled_dot_product_20_amd/csrc/attn_device.hpp",
                   "scaled_dot_product_20_amd/csrc/attn_launch.hpp"]
+ENTRY = {"fwd": "attn_fwd", "bwd_preprocess": "attn_bwd_preprocess", "bwd_dkdv_dq": "attn_bwd_dkdv_dq"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def visible_pairs(sq: int, sk: int, window, diag: str) -> int:
-    """Visible (i, j) pairs of one sequence, by rows: key j is visible to
-    query i iff i - L <= j <= i + R, (L, R) shifted by d = sk - sq under the
-    bottom-right diagonal when both sides are finite."""
+def row_ranges(sq: int, sk: int, window, diag: str):
+    """Per query row i, the visible keys [lo_i, hi_i] of one sequence (empty
+    when hi < lo): key j is visible to query i iff i - L <= j <= i + R, (L, R)
+    shifted by d = sk - sq under the bottom-right diagonal when both sides
+    are finite."""
     import numpy as np
     inf = 2147483647
     wl, wr = window
@@ -66,7 +82,24 @@ def visible_pairs(sq: int, sk: int, window, diag: str) -> int:
     i = np.arange(sq, dtype=np.int64)
     lo = np.zeros(sq, np.int64) if L == inf else np.maximum(0, i - L)
     hi = np.full(sq, sk - 1, np.int64) if R == inf else np.minimum(sk - 1, i + R)
+    return lo, hi
+
+
+def visible_pairs(sq: int, sk: int, window, diag: str) -> int:
+    import numpy as np
+    lo, hi = row_ranges(sq, sk, window, diag)
     return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def visible_keys(sq: int, sk: int, window, diag: str) -> int:
+    """Keys of one sequence that at least one query sees."""
+    import numpy as np
+    lo, hi = row_ranges(sq, sk, window, diag)
+    ok = hi >= lo
+    cover = np.zeros(sk + 1, np.int64)
+    np.add.at(cover, lo[ok], 1)
+    np.add.at(cover, hi[ok] + 1, -1)
+    return int((np.cumsum(cover[:sk]) > 0).sum())
 
 
 def source_hash() -> str:
@@ -77,47 +110,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def dkdv_kernel_name(dname: str, head_dim: int) -> str:
-    """The dK/dV kernel the library launches for this dtype and head_dim."""
-    if dname == "fp32":
-        return "attn_bwd_dkdv_kernel"
-    return "attn_bwd_dkdv16pc_kernel" if head_dim > 80 else "attn_bwd_dkdv16_kernel"
-
-
-def wide_band(window) -> bool:
-    """A band unbounded on one side or at least 1024 keys wide."""
-    inf = 2147483647
-    wl, wr = window
-    return wl == inf or wr == inf or wl + wr + 1 >= 1024
-
-
-def bwd_main_kernels(dname: str, head_dim: int, window, seqlen_q: int, heads: int, batch: int,
-                     cus: int) -> list:
-    """The kernels attn_bwd_dkdv_dq launches: the fused dK/dV + dQ grid for
-    16-bit head_dim 128 when the band is wide and a separate dQ grid (two
-    128-row workgroups per CU) would leave its last round at most a quarter full,
-    else the dK/dV kernel then the dQ kernel."""
-    slots = 2 * cus
-    tail = (-(-seqlen_q // 128) * heads * batch) % slots if slots else 0
-    if dname != "fp32" and head_dim > 80 and wide_band(window) and 0 < tail and 4 * tail <= slots:
-        return ["attn_bwd_fused16_kernel"]
-    dq = "attn_bwd_dq_kernel" if dname == "fp32" else "attn_bwd_dq16_kernel"
-    return [dkdv_kernel_name(dname, head_dim), dq]
-
-
-def fwd_kernel_name(dname: str, window) -> str:
-    """The forward kernel the library launches: the 256-row ping-pong kernel
-    for 16-bit inputs unless both window sides are finite and the band is
-    under 1024 keys wide."""
-    if dname == "fp32":
-        return "attn_fwd_kernel"
-    return "attn_fwd16pp_kernel" if wide_band(window) else "attn_fwd16_kernel"
-
-
 def read_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of the dK/dV (+ dQ) kernel from the committed
-    counter summary, or None when there is none for this workload and kernel
-    or the kernel's sources changed since."""
+    """HBM bytes per launch of the backward call from the committed counter
+    summary, or None when there is none for this workload and kernel or the
+    kernel's sources changed since."""
     if workload != DEFAULT_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -132,6 +128,17 @@ def read_traffic(workload: str, kernel: str):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(w, dtype, min_seconds=10.0, max_slices=32):
@@ -167,7 +174,7 @@ def cpu_baseline(w, dtype, min_seconds=10.0, max_slices=32):
         spent += time.perf_counter() - t0
         n += 1
     return {"value": round(n * flop_slice / spent / 1e12, 6), "unit": "TFLOP/s",
-            "cores": orc.num_threads(), "kind": "oracle",
+            "cores": orc.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"fp64 {'+'.join(w.passes)} of {n} slices: {what}; {spent:.1f} s",
             "seconds": round(spent, 2)}
 
@@ -190,6 +197,95 @@ def copy_probe(mib: int, steps: int) -> None:
                       "gb_s_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
+class Run:
+    """One workload on the GPU: inputs in HBM, the params of each call, the
+    library's launch plan, and timed steps."""
+
+    def __init__(self, W, dtype, passes, dev):
+        import torch
+        from scaled_dot_product_20_amd import binding as bd
+
+        self.W, self.dtype, self.passes, self.dev = W, dtype, passes, dev
+        self.dname = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[dtype]
+        q, k, v, do = (t.to(dev) for t in W.inputs(dtype))
+        kw = dict(scale=W.scale, window=W.window, diag=W.diag)
+        if W.layout == "thd":
+            cu_q, cu_k = W.cu_seqlens()
+            kw.update(cu_seqlens_q=torch.from_numpy(cu_q).to(dev), cu_seqlens_k=torch.from_numpy(cu_k).to(dev),
+                      max_seqlen_q=W.seqlen_q, max_seqlen_k=W.seqlen_k)
+            lens = list(zip(W.lens_q, W.lens_k))
+        else:
+            lens = [(W.seqlen_q, W.seqlen_k)] * W.batch
+        self.pairs = W.heads * sum(visible_pairs(a, b, W.window, W.diag) for a, b in lens)
+        kvis = W.heads * sum(visible_keys(a, b, W.window, W.diag) for a, b in lens)
+        tq, tk = W.heads * sum(a for a, _ in lens), W.heads * sum(b for _, b in lens)
+        esz, D = q.element_size(), W.head_dim
+        self.fwd_bytes = esz * D * (2 * tq + 2 * kvis) + 4 * tq
+        self.bwd_bytes = esz * D * (4 * tq + 4 * tk) + 4 * 3 * tq
+        o, lse = bd.attn_fwd(q, k, v, **kw)
+        fkw = dict(cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None)
+        fkw.update(kw)
+        self.params = {"fwd": bd.fwd_params(q, k, v, o, lse, **fkw)}
+        self.calls = ["fwd"]
+        self.keep = (q, k, v, do, o, lse, kw)
+        if "bwd" in passes:
+            bp, self.bkeep = bd.prepare_bwd(do, q, k, v, o, lse, **kw)
+            self.params["bwd_preprocess"] = self.params["bwd_dkdv_dq"] = bp
+            self.calls += ["bwd_preprocess", "bwd_dkdv_dq"]
+        self.stream = torch.cuda.current_stream(dev)
+        self.plan = {c: bd.plan(ENTRY[c], self.params[c], self.stream.cuda_stream) for c in self.calls}
+
+    def step(self, evs=None):
+        from scaled_dot_product_20_amd import binding as bd
+        sid = self.stream.cuda_stream
+        for i, c in enumerate(self.calls):
+            if evs is not None:
+                evs[i].record(self.stream)
+            bd.launch(ENTRY[c], self.params[c], sid)
+        if evs is not None:
+            evs[len(self.calls)].record(self.stream)
+
+    def time(self, steps, warmup):
+        """(wall ms per step, {call: average ms from HIP events on the launch stream})."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.calls) + 1)]
+                  for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            self.step(events[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = {c: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / steps for i, c in enumerate(self.calls)}
+        return wall * 1e3 / steps, per
+
+    def kernels(self, call):
+        return "+".join(name for name, _, _ in self.plan[call])
+
+    def summary(self, per, peak):
+        D = self.W.head_dim
+        fwd_flop, bwd_flop = 4.0 * D * self.pairs, 10.0 * D * self.pairs
+        out = {"fwd": {"ms": round(per["fwd"], 4), "tflops": round(fwd_flop / per["fwd"] / 1e9, 2),
+                       "frac_of_peak": round(fwd_flop / per["fwd"] / 1e9 / peak, 4),
+                       "gb_s": round(self.fwd_bytes / per["fwd"] / 1e6, 1),
+                       "kernels": self.kernels("fwd")}}
+        if "bwd_dkdv_dq" in per:
+            ms = per["bwd_preprocess"] + per["bwd_dkdv_dq"]
+            out["bwd"] = {"ms": round(ms, 4), "tflops": round(bwd_flop / ms / 1e9, 2),
+                          "frac_of_peak": round(bwd_flop / ms / 1e9 / peak, 4),
+                          "gb_s": round(self.bwd_bytes / ms / 1e6, 1),
+                          "kernels": self.kernels("bwd_preprocess") + "," + self.kernels("bwd_dkdv_dq")}
+        return out
+
+    def release(self):
+        import torch
+        self.keep = self.bkeep = self.params = None
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,7 +294,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--dtype", default=None, help="bf16 / fp16 / fp32 (default: the workload's first)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--passes", default=None, help="fwd or fwd,bwd (default: the workload's)")
+    ap.add_argument("--no-cells", action="store_true", help="time the headline workload only")
+    ap.add_argument("--cell-steps", type=int, default=10)
+    ap.add_argument("--cell-warmup", type=int, default=3)
+    ap.add_argument("--passes", default=None, help="fwd or fwd,bwd (default: fwd,bwd)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the attention step, run a plain device-to-device copy of MIB "
                          "MiB (the calibration kernel for HBM byte counters) and exit")
@@ -211,7 +310,6 @@ def main():
         sys.exit(2)
 
     import torch
-    from scaled_dot_product_20_amd import binding as bd
     from scaled_dot_product_20_amd import workloads as wls
 
     if not torch.cuda.is_available():
@@ -220,109 +318,80 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe, args.steps)
         return
-    W = wls.workloads()[args.workload]
     names = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+    wl_all = wls.workloads()
+    W = wl_all[args.workload]
     dtype = names[args.dtype] if args.dtype else W.dtypes[0]
-    dname = {v: k for k, v in names.items()}[dtype]
     passes = tuple(args.passes.split(",")) if args.passes else ("fwd", "bwd")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    peak_of = lambda dt: PEAK_MFMA_32 if dt == torch.float32 else PEAK_MFMA_16
 
-    log(f"[bench] workload {W.name} dtype {dname} passes {passes}: drawing inputs")
-    q, k, v, do = (t.to(dev) for t in W.inputs(dtype))
-    cu_q, cu_k = W.cu_seqlens()
-    kw = dict(scale=W.scale, window=W.window, diag=W.diag)
-    if W.layout == "thd":
-        kw.update(cu_seqlens_q=torch.from_numpy(cu_q).to(dev), cu_seqlens_k=torch.from_numpy(cu_k).to(dev),
-                  max_seqlen_q=W.seqlen_q, max_seqlen_k=W.seqlen_k)
-        lens = list(zip(W.lens_q, W.lens_k))
-    else:
-        lens = [(W.seqlen_q, W.seqlen_k)] * W.batch
-    pairs = W.heads * sum(visible_pairs(a, b, W.window, W.diag) for a, b in lens)
+    log(f"[bench] workload {W.name} dtype {dtype} passes {passes}: drawing inputs")
+    run = Run(W, dtype, passes, dev)
+    log(f"[bench] plan {json.dumps(run.plan)}")
+    log(f"[bench] warmup {args.warmup} steps, timing {args.steps} steps")
+    ms_step, per = run.time(args.steps, args.warmup)
+    log("[bench] per-call ms " + json.dumps({k: round(v, 4) for k, v in per.items()}))
+
+    peak = peak_of(dtype)
     D = W.head_dim
-    fwd_flop = 4.0 * D * pairs
-    bwd_flop = 10.0 * D * pairs
-    main_flop = 14.0 * D * pairs  # dK/dV (S, dV, dP, dK) and dQ (S, dP, dQ) as executed
-
-    o, lse = bd.attn_fwd(q, k, v, **kw)
-    fkw = dict(cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None)
-    fkw.update(kw)
-    fp = bd.fwd_params(q, k, v, o, lse, **fkw)
-    do_bwd = "bwd" in passes
-    if do_bwd:
-        bp, keep = bd.prepare_bwd(do, q, k, v, o, lse, **kw)
-    stream = torch.cuda.current_stream(dev)
-    sid = stream.cuda_stream
-    kernels = ["fwd"] + (["bwd_preprocess", "bwd_dkdv_dq"] if do_bwd else [])
-    entry = {"fwd": "attn_fwd", "bwd_preprocess": "attn_bwd_preprocess", "bwd_dkdv_dq": "attn_bwd_dkdv_dq"}
-
-    def step(evs=None):
-        for i, kname in enumerate(kernels):
-            if evs is not None:
-                evs[i].record(stream)
-            bd.launch(entry[kname], fp if kname == "fwd" else bp, sid)
-        if evs is not None:
-            evs[len(kernels)].record(stream)
-
-    log(f"[bench] warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
-              for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_kernel = {kname: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps
-                  for i, kname in enumerate(kernels)}
-    ms_step = wall * 1e3 / args.steps
-    log("[bench] per-kernel ms " + json.dumps({k: round(v, 4) for k, v in per_kernel.items()}))
-
-    peak = PEAK_MFMA_32 if dtype == torch.float32 else PEAK_MFMA_16
-    total_flop = fwd_flop + (bwd_flop if do_bwd else 0.0)
+    fwd_flop = 4.0 * D * run.pairs
+    bwd_flop = 10.0 * D * run.pairs
+    total_flop = fwd_flop + (bwd_flop if "bwd" in passes else 0.0)
     value = total_flop / (ms_step * 1e-3) / 1e12
-    fwd_ms = per_kernel["fwd"]
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dname,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": run.dname,
         "data": "synthetic: i.i.d. N(0,1) Q/K/V/dO from a seeded generator, cast RNE",
         "config": {"workload": W.name, "layout": W.layout, "batch": W.batch, "heads": W.heads,
                    "head_dim": D, "seqlen_q": W.seqlen_q, "seqlen_k": W.seqlen_k,
                    "window": list(W.window), "diag": W.diag, "passes": list(passes),
-                   "visible_pairs": pairs},
+                   "visible_pairs": run.pairs},
         "frac_of_peak": round(value / peak, 4),
-        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flop / fwd_ms / 1e9, 2),
-                "frac_of_peak": round(fwd_flop / fwd_ms / 1e9 / peak, 4)},
     }
-    if do_bwd:
-        bwd_ms = per_kernel["bwd_preprocess"] + per_kernel["bwd_dkdv_dq"]
-        out["bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / bwd_ms / 1e9, 2),
-                      "frac_of_peak": round(bwd_flop / bwd_ms / 1e9 / peak, 4)}
-        main_ms = per_kernel["bwd_dkdv_dq"]
-        ach = main_flop / main_ms / 1e9
-        knames = bwd_main_kernels(dname, D, W.window, W.seqlen_q, W.heads, W.batch,
-                                  torch.cuda.get_device_properties(dev).multi_processor_count)
-        kname = "+".join(knames)
-        traffic = read_traffic(W.name, kname) if dname == "bf16" else None
-        out["roofline"] = {"kernel": kname, "bound": "mfma", "achieved": round(ach, 2),
-                           "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                           "traffic": traffic, "avg_ms": round(main_ms, 4),
-                           "algorithmic": f"14*D FLOP per visible pair (S, dV, dP, dK; S, dP, dQ) x {pairs} pairs"}
-    else:
-        ach = fwd_flop / fwd_ms / 1e9
-        kname = fwd_kernel_name(dname, W.window)
-        out["roofline"] = {"kernel": kname, "bound": "mfma", "achieved": round(ach, 2),
-                           "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                           "traffic": None, "avg_ms": round(fwd_ms, 4),
-                           "algorithmic": f"4*D FLOP per visible pair x {pairs} pairs"}
-    out["kernels_ms"] = {k: round(v, 4) for k, v in per_kernel.items()}
+    out.update(run.summary(per, peak))
+    # Roofline of the call with the largest time share, priced at its
+    # algorithmic work; the backward call's executed work beside it.
+    dom = max(per, key=per.get)
+    kname = run.kernels(dom)
+    if dom == "bwd_dkdv_dq":
+        ach = bwd_flop / per[dom] / 1e9
+        algo = f"10*D FLOP per visible pair (S, dV, dP, dK, dQ) x {run.pairs} pairs"
+        executed = round(14.0 * D * run.pairs / per[dom] / 1e9, 2)
+        traffic = read_traffic(W.name, kname) if run.dname == "bf16" else None
+    elif dom == "fwd":
+        ach = fwd_flop / per[dom] / 1e9
+        algo = f"4*D FLOP per visible pair (S, P V) x {run.pairs} pairs"
+        executed, traffic = round(ach, 2), None
+    else:  # the preprocess dominates only for degenerate problems
+        ach, algo, executed, traffic = 0.0, "row sums only", 0.0, None
+    out["roofline"] = {"kernel": kname, "call": ENTRY[dom], "bound": "mfma", "achieved": round(ach, 2),
+                       "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
+                       "avg_ms": round(per[dom], 4), "algorithmic": algo, "executed_tflops": executed}
+    out["kernels_ms"] = {k: round(v, 4) for k, v in per.items()}
+    run.release()
+
+    if not args.no_cells:
+        cells = {}
+        for name, dn in CELLS:
+            if name == W.name and dn == run.dname:
+                cells[f"{name}:{dn}"] = {k: out[k] for k in ("fwd", "bwd") if k in out}
+                continue
+            t0 = time.perf_counter()
+            cw = wl_all[name]
+            r = Run(cw, names[dn], ("fwd", "bwd"), dev)
+            _, cper = r.time(args.cell_steps, args.cell_warmup)
+            cells[f"{name}:{dn}"] = r.summary(cper, peak_of(names[dn]))
+            cells[f"{name}:{dn}"]["visible_pairs"] = r.pairs
+            r.release()
+            c = cells[f"{name}:{dn}"]
+            log(f"[bench] cell {name}:{dn} fwd {c['fwd']['ms']} ms bwd {c['bwd']['ms']} ms "
+                f"({time.perf_counter() - t0:.1f} s)")
+        out["cells"] = cells
     if not args.no_cpu:
-        log("[bench] timing the fp64 oracle on one slice (CPU)")
+        log("[bench] timing the fp64 oracle on slices of the headline workload (CPU)")
         out["cpu_baseline"] = cpu_baseline(dataclasses.replace(W, passes=passes), dtype)
     else:
         out["cpu_baseline"] = None

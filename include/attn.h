@@ -150,7 +150,13 @@ typedef struct {
   uint64_t workspace_bytes;/* >= attn_bwd_workspace_size(this) */
 } attn_bwd_params;
 
-/* Forward: writes o and lse.  Enqueues one kernel on `stream`. */
+/* Forward: writes o and lse.  Enqueues on `stream` one forward kernel
+ * over the query blocks (for fp16 / bf16 inputs with a band unbounded or at
+ * least 1024 keys wide, the 256-row ping-pong kernel, and when its grid's
+ * last round on the device would be mostly idle, a second kernel that
+ * splits that round's blocks over the key axis and merges the halves), then,
+ * only when seqused_q is given, a small kernel that writes the rows past the
+ * used ones as masked rows.  attn_fwd_plan lists the kernels of a call. */
 hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
 
 /* Backward: reads q, k, v, o, lse, dout; writes dq, dk, dv.  Enqueues, in
@@ -158,16 +164,19 @@ hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
  * "bwd_preprocess" of the AOTriton 0.14b release notes) into the workspace,
  * then the per-key-block dK/dV work and the per-query-block dQ work (the
  * split backward, "triton_split" in the same notes) as attn_bwd_dkdv_dq
- * does.  The dK/dV and dQ sums are computed without atomics: results are
- * run-to-run identical. */
+ * does, then, only when seqused_q / seqused_k are given, the small kernels
+ * that zero the gradient rows past the used ones.  The dK/dV and dQ sums are
+ * computed without atomics: results are run-to-run identical. */
 hipError_t attn_bwd(const attn_bwd_params *p, hipStream_t stream);
 
 /* The three steps of attn_bwd as separate calls, for callers that schedule
  * or time them one by one.  Same parameters, validation and errors as
- * attn_bwd; each enqueues one kernel on `stream`.  They must run in this
- * order on one stream (or be ordered by events): attn_bwd_dkdv and
- * attn_bwd_dq read the Delta and LSE log2(e) that attn_bwd_preprocess leaves
- * in the workspace, which must not be touched in between.
+ * attn_bwd; each enqueues one kernel on `stream`, and attn_bwd_dkdv /
+ * attn_bwd_dq also the row-zeroing kernel of their outputs when seqused
+ * arrays are given.  They must run in this order on one stream (or be
+ * ordered by events): attn_bwd_dkdv and attn_bwd_dq read the Delta and LSE
+ * log2(e) that attn_bwd_preprocess leaves in the workspace, which must not
+ * be touched in between.
  *   attn_bwd_preprocess: Delta_i = sum_d dO_id O_id and LSE_i log2(e) into
  *                        the workspace.
  *   attn_bwd_dkdv:       dK and dV, one workgroup per block of keys.
@@ -201,6 +210,35 @@ hipError_t attn_bwd_check(const attn_bwd_params *p);
 
 /* ATTN_PARAMS_VERSION of the built library. */
 uint32_t attn_params_version(void);
+
+/* ------------------------------------------------------------ launch plans
+ *
+ * What a call would enqueue, for callers that label, profile or schedule its
+ * work: the kernels in launch order, by function name (static strings owned
+ * by the library, valid while it is loaded), with their workgroup counts and
+ * sizes.  The plan is made by the same code that makes the launch choice of
+ * the call, for the stream's device (its compute-unit count decides some
+ * choices).  Host-only: nothing is enqueued and no device memory is read or
+ * written.  The call's own validation runs first and its error is returned;
+ * attn_bwd_plan does not look at the workspace, which decides nothing. */
+#define ATTN_PLAN_MAX 4
+typedef struct {
+  const char *kernel[ATTN_PLAN_MAX]; /* kernel[i], i < count */
+  uint32_t grid[ATTN_PLAN_MAX];      /* workgroups of launch i */
+  uint32_t block[ATTN_PLAN_MAX];     /* threads per workgroup of launch i */
+  int32_t count;                     /* launches; 0 for a problem with no rows */
+  int32_t reserved;
+} attn_plan;
+
+/* Steps of the backward for attn_bwd_plan (bit mask, any non-empty subset):
+ * attn_bwd is ATTN_BWD_ALL, attn_bwd_dkdv_dq is ATTN_BWD_DKDV | ATTN_BWD_DQ. */
+#define ATTN_BWD_PREPROCESS 1u
+#define ATTN_BWD_DKDV 2u
+#define ATTN_BWD_DQ 4u
+#define ATTN_BWD_ALL 7u
+
+hipError_t attn_fwd_plan(const attn_fwd_params *p, hipStream_t stream, attn_plan *plan);
+hipError_t attn_bwd_plan(const attn_bwd_params *p, uint32_t steps, hipStream_t stream, attn_plan *plan);
 
 #ifdef __cplusplus
 }

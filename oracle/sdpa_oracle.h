@@ -14,9 +14,10 @@
  * definition out rather than the tiled algorithm.
  *
  * Visibility follows the generalized sliding-window rule of the AOTriton
- * 0.10b release notes ("Causal masks are implemented with Generalized sliding
- * window attention"), with the diagonal choice of the AOTriton 0.15b release
- * notes, section "Bottom-Right Aligned Sliding Windows".
+ * 0.10b release notes (section "Major Changes": causal masking expressed as a
+ * special case of the generalized window), with the diagonal choice of the
+ * AOTriton 0.15b release notes, section "Bottom-Right Aligned Sliding
+ * Windows".
  */
 #ifndef SDPA_ORACLE_H
 #define SDPA_ORACLE_H

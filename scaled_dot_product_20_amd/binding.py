@@ -29,7 +29,7 @@ BHSD, THD = 0, 1
 TOP_LEFT, BOTTOM_RIGHT = 0, 1
 
 _DTYPE = {torch.float32: FP32, torch.float16: FP16, torch.bfloat16: BF16}
-_HIP_ERRORS = {1: "hipErrorInvalidValue", 801: "hipErrorNotSupported", 98: "hipErrorInvalidDeviceFunction",
+_HIP_ERRORS = {1: "hipErrorInvalidValue", 2: "hipErrorOutOfMemory", 801: "hipErrorNotSupported", 98: "hipErrorInvalidDeviceFunction",
                209: "hipErrorNoBinaryForGpu", 200: "hipErrorInvalidImage"}
 
 _I64x3 = ctypes.c_int64 * 3
@@ -62,6 +62,20 @@ class BwdParams(ctypes.Structure):
     ]
 
 
+PLAN_MAX = 4
+BWD_PREPROCESS, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
+# Backward steps each entry point runs (attn_bwd_plan's `steps`).
+ENTRY_STEPS = {"attn_bwd": BWD_ALL, "attn_bwd_preprocess": BWD_PREPROCESS,
+               "attn_bwd_dkdv": BWD_DKDV, "attn_bwd_dq": BWD_DQ, "attn_bwd_dkdv_dq": BWD_DKDV | BWD_DQ}
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("kernel", ctypes.c_char_p * PLAN_MAX), ("grid", ctypes.c_uint32 * PLAN_MAX),
+        ("block", ctypes.c_uint32 * PLAN_MAX), ("count", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -86,6 +100,11 @@ def lib():
         l.attn_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdParams)]
         l.attn_bwd_workspace_size.restype = ctypes.c_uint64
         l.attn_params_version.restype = ctypes.c_uint32
+        l.attn_fwd_plan.argtypes = [ctypes.POINTER(FwdParams), ctypes.c_void_p, ctypes.POINTER(Plan)]
+        l.attn_fwd_plan.restype = ctypes.c_int
+        l.attn_bwd_plan.argtypes = [ctypes.POINTER(BwdParams), ctypes.c_uint32, ctypes.c_void_p,
+                                    ctypes.POINTER(Plan)]
+        l.attn_bwd_plan.restype = ctypes.c_int
         _lib = l
     return _lib
 
@@ -279,6 +298,23 @@ def launch(name: str, params, stream: Optional[int] = None) -> None:
     rc = getattr(lib(), name)(ctypes.byref(params), ctypes.c_void_p(stream))
     if rc:
         raise AttnError(name, rc)
+
+
+def plan(name: str, params, stream: Optional[int] = None):
+    """The launches entry point ``name`` would make with these params, from
+    the library's own launch choice (attn_fwd_plan / attn_bwd_plan): a list
+    of (kernel name, workgroups, threads per workgroup).  Host-only."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    pl = Plan()
+    if name == "attn_fwd":
+        rc = lib().attn_fwd_plan(ctypes.byref(params), ctypes.c_void_p(stream), ctypes.byref(pl))
+    else:
+        rc = lib().attn_bwd_plan(ctypes.byref(params), ENTRY_STEPS[name], ctypes.c_void_p(stream),
+                                 ctypes.byref(pl))
+    if rc:
+        raise AttnError(name + " plan", rc)
+    return [(pl.kernel[i].decode(), int(pl.grid[i]), int(pl.block[i])) for i in range(pl.count)]
 
 
 def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,

@@ -1,6 +1,8 @@
 // attn_api.cpp - the C ABI declared in include/attn.h: validation, argument
 // marshalling into kernel argument blocks, and the device taken from the
-// stream.  No allocation, no global mutable state, nothing printed.
+// stream.  Nothing is allocated per call and nothing is printed.  The
+// library's only state is written once per device and never changed after:
+// the compute-unit count the launchers read (attn_launch.hpp).
 #include "attn.h"
 
 #include <cmath>
@@ -159,6 +161,95 @@ Operand operand(const void* ptr, const int64_t* stride, bool packed) {
   return Operand{ptr, packed ? 0 : stride[0], stride[1], stride[2]};
 }
 
+// The checks of attn_bwd_check; the workspace is checked only when `ws`
+// (the plan query does not look at it).
+hipError_t check_bwd(const attn_bwd_params* p, bool ws) {
+  if (!p) return hipErrorInvalidValue;
+  const attn_fwd_params* f = &p->fwd;
+  hipError_t err = check_problem(f);
+  if (err != hipSuccess) return err;
+  const int64_t nb = f->layout == ATTN_THD ? 1 : f->batch;
+  const bool no_q = nb == 0 || q_rows(f) == 0, no_k = nb == 0 || k_rows(f) == 0;
+  if ((!p->dout && !no_q) || (!p->dq && !no_q) || (!p->dk && !no_k) || (!p->dv && !no_k))
+    return hipErrorInvalidValue;
+  if (ws && (!p->workspace || p->workspace_bytes < delta_bytes(f) ||
+             (reinterpret_cast<uintptr_t>(p->workspace) & 255u) != 0))
+    return hipErrorInvalidValue;
+  const bool packed = f->layout == ATTN_THD;
+  const int64_t esz = elem_bytes(f->dtype);
+  if (!aligned16(p->dout) || !aligned16(p->dq) || !aligned16(p->dk) || !aligned16(p->dv))
+    return hipErrorInvalidValue;
+  if (!strides_ok(p->do_stride, esz, packed) || !strides_ok(p->dq_stride, esz, packed) ||
+      !strides_ok(p->dk_stride, esz, packed) || !strides_ok(p->dv_stride, esz, packed))
+    return hipErrorInvalidValue;
+  if (f->dtype != ATTN_FP32 && !tile_span_ok(p->do_stride, esz, f->head_dim)) return hipErrorNotSupported;
+  const int64_t B = packed ? 1 : f->batch, H = f->heads, D = f->head_dim;
+  const Extent outs[4] = {
+      extent_of(p->dq, p->dq_stride, B, H, q_rows(f), D, esz, packed),
+      extent_of(p->dk, p->dk_stride, B, H, k_rows(f), D, esz, packed),
+      extent_of(p->dv, p->dv_stride, B, H, k_rows(f), D, esz, packed),
+      ws ? Extent{reinterpret_cast<uintptr_t>(p->workspace),
+                  reinterpret_cast<uintptr_t>(p->workspace) + (uintptr_t)delta_bytes(f)}
+         : Extent{0, 0}};
+  const Extent ins[6] = {
+      extent_of(f->q, f->q_stride, B, H, q_rows(f), D, esz, packed),
+      extent_of(f->k, f->k_stride, B, H, k_rows(f), D, esz, packed),
+      extent_of(f->v, f->v_stride, B, H, k_rows(f), D, esz, packed),
+      extent_of(f->o, f->o_stride, B, H, q_rows(f), D, esz, packed),
+      extent_of(p->dout, p->do_stride, B, H, q_rows(f), D, esz, packed),
+      lse_extent(f)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Extent& in : ins)
+      if (overlap(outs[i], in)) return hipErrorInvalidValue;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+sdpa::FwdArgs fwd_args(const attn_fwd_params* p) {
+  const bool packed = p->layout == ATTN_THD;
+  sdpa::FwdArgs a{};
+  a.p = problem_args(p);
+  a.q = operand(p->q, p->q_stride, packed);
+  a.k = operand(p->k, p->k_stride, packed);
+  a.v = operand(p->v, p->v_stride, packed);
+  a.o = operand(p->o, p->o_stride, packed);
+  a.lse = p->lse;
+  return a;
+}
+
+// Kernel arguments of a backward whose workspace (Delta, then LSE log2 e)
+// starts at `ws`.
+sdpa::BwdArgs bwd_args(const attn_bwd_params* p, void* ws) {
+  const attn_fwd_params* f = &p->fwd;
+  const bool packed = f->layout == ATTN_THD;
+  sdpa::BwdArgs a{};
+  a.p = problem_args(f);
+  a.q = operand(f->q, f->q_stride, packed);
+  a.k = operand(f->k, f->k_stride, packed);
+  a.v = operand(f->v, f->v_stride, packed);
+  a.o = operand(f->o, f->o_stride, packed);
+  a.dout = operand(p->dout, p->do_stride, packed);
+  a.dq = operand(p->dq, p->dq_stride, packed);
+  a.dk = operand(p->dk, p->dk_stride, packed);
+  a.dv = operand(p->dv, p->dv_stride, packed);
+  a.lse = f->lse;
+  a.delta = static_cast<float*>(ws);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + stat_section_bytes(f));
+  return a;
+}
+
+void plan_out(const sdpa::Plan& pl, attn_plan* out) {
+  *out = attn_plan{};
+  out->count = pl.n;
+  for (int i = 0; i < pl.n; ++i) {
+    out->kernel[i] = pl.e[i].name;
+    out->grid[i] = pl.e[i].grid;
+    out->block[i] = pl.e[i].block;
+  }
+}
+
 // Runs `launch` with the stream's device current, restoring the caller's.
 template <typename F>
 hipError_t on_stream_device(hipStream_t stream, F launch) {
@@ -203,15 +294,19 @@ hipError_t attn_fwd_check(const attn_fwd_params* p) {
 hipError_t attn_fwd(const attn_fwd_params* p, hipStream_t stream) {
   hipError_t err = attn_fwd_check(p);
   if (err != hipSuccess) return err;
-  const bool packed = p->layout == ATTN_THD;
-  sdpa::FwdArgs a{};
-  a.p = problem_args(p);
-  a.q = operand(p->q, p->q_stride, packed);
-  a.k = operand(p->k, p->k_stride, packed);
-  a.v = operand(p->v, p->v_stride, packed);
-  a.o = operand(p->o, p->o_stride, packed);
-  a.lse = p->lse;
-  return on_stream_device(stream, [&] { return sdpa::launch_fwd(p->dtype, p->head_dim, a, stream); });
+  const sdpa::FwdArgs a = fwd_args(p);
+  return on_stream_device(stream, [&] { return sdpa::launch_fwd(p->dtype, p->head_dim, a, sdpa::Enqueue{stream}); });
+}
+
+hipError_t attn_fwd_plan(const attn_fwd_params* p, hipStream_t stream, attn_plan* plan) {
+  if (!plan) return hipErrorInvalidValue;
+  hipError_t err = attn_fwd_check(p);
+  if (err != hipSuccess) return err;
+  const sdpa::FwdArgs a = fwd_args(p);
+  sdpa::Plan pl{};
+  err = on_stream_device(stream, [&] { return sdpa::launch_fwd(p->dtype, p->head_dim, a, sdpa::Record{&pl}); });
+  if (err == hipSuccess) plan_out(pl, plan);
+  return err;
 }
 
 uint64_t attn_bwd_workspace_size(const attn_bwd_params* p) {
@@ -219,48 +314,7 @@ uint64_t attn_bwd_workspace_size(const attn_bwd_params* p) {
   return delta_bytes(&p->fwd);
 }
 
-hipError_t attn_bwd_check(const attn_bwd_params* p) {
-  if (!p) return hipErrorInvalidValue;
-  const attn_fwd_params* f = &p->fwd;
-  hipError_t err = check_problem(f);
-  if (err != hipSuccess) return err;
-  const int64_t nb = f->layout == ATTN_THD ? 1 : f->batch;
-  const bool no_q = nb == 0 || q_rows(f) == 0, no_k = nb == 0 || k_rows(f) == 0;
-  if ((!p->dout && !no_q) || (!p->dq && !no_q) || (!p->dk && !no_k) || (!p->dv && !no_k) ||
-      !p->workspace)
-    return hipErrorInvalidValue;
-  if (p->workspace_bytes < delta_bytes(f)) return hipErrorInvalidValue;
-  if ((reinterpret_cast<uintptr_t>(p->workspace) & 255u) != 0) return hipErrorInvalidValue;
-  const bool packed = f->layout == ATTN_THD;
-  const int64_t esz = elem_bytes(f->dtype);
-  if (!aligned16(p->dout) || !aligned16(p->dq) || !aligned16(p->dk) || !aligned16(p->dv))
-    return hipErrorInvalidValue;
-  if (!strides_ok(p->do_stride, esz, packed) || !strides_ok(p->dq_stride, esz, packed) ||
-      !strides_ok(p->dk_stride, esz, packed) || !strides_ok(p->dv_stride, esz, packed))
-    return hipErrorInvalidValue;
-  if (f->dtype != ATTN_FP32 && !tile_span_ok(p->do_stride, esz, f->head_dim)) return hipErrorNotSupported;
-  const int64_t B = packed ? 1 : f->batch, H = f->heads, D = f->head_dim;
-  const Extent outs[4] = {
-      extent_of(p->dq, p->dq_stride, B, H, q_rows(f), D, esz, packed),
-      extent_of(p->dk, p->dk_stride, B, H, k_rows(f), D, esz, packed),
-      extent_of(p->dv, p->dv_stride, B, H, k_rows(f), D, esz, packed),
-      Extent{reinterpret_cast<uintptr_t>(p->workspace),
-             reinterpret_cast<uintptr_t>(p->workspace) + (uintptr_t)delta_bytes(f)}};
-  const Extent ins[6] = {
-      extent_of(f->q, f->q_stride, B, H, q_rows(f), D, esz, packed),
-      extent_of(f->k, f->k_stride, B, H, k_rows(f), D, esz, packed),
-      extent_of(f->v, f->v_stride, B, H, k_rows(f), D, esz, packed),
-      extent_of(f->o, f->o_stride, B, H, q_rows(f), D, esz, packed),
-      extent_of(p->dout, p->do_stride, B, H, q_rows(f), D, esz, packed),
-      lse_extent(f)};
-  for (int i = 0; i < 4; ++i) {
-    for (const Extent& in : ins)
-      if (overlap(outs[i], in)) return hipErrorInvalidValue;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outs[j])) return hipErrorInvalidValue;
-  }
-  return hipSuccess;
-}
+hipError_t attn_bwd_check(const attn_bwd_params* p) { return check_bwd(p, true); }
 
 }  // extern "C"
 
@@ -270,22 +324,9 @@ hipError_t bwd_stages(const attn_bwd_params* p, int stages, hipStream_t stream) 
   hipError_t err = attn_bwd_check(p);
   if (err != hipSuccess) return err;
   const attn_fwd_params* f = &p->fwd;
-  const bool packed = f->layout == ATTN_THD;
-  sdpa::BwdArgs a{};
-  a.p = problem_args(f);
-  a.q = operand(f->q, f->q_stride, packed);
-  a.k = operand(f->k, f->k_stride, packed);
-  a.v = operand(f->v, f->v_stride, packed);
-  a.o = operand(f->o, f->o_stride, packed);
-  a.dout = operand(p->dout, p->do_stride, packed);
-  a.dq = operand(p->dq, p->dq_stride, packed);
-  a.dk = operand(p->dk, p->dk_stride, packed);
-  a.dv = operand(p->dv, p->dv_stride, packed);
-  a.lse = f->lse;
-  a.delta = static_cast<float*>(p->workspace);
-  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(p->workspace) + stat_section_bytes(f));
-  return on_stream_device(stream,
-                          [&] { return sdpa::launch_bwd(f->dtype, f->head_dim, a, stages, stream); });
+  const sdpa::BwdArgs a = bwd_args(p, p->workspace);
+  return on_stream_device(
+      stream, [&] { return sdpa::launch_bwd(f->dtype, f->head_dim, a, stages, sdpa::Enqueue{stream}); });
 }
 
 }  // namespace
@@ -310,6 +351,19 @@ hipError_t attn_bwd_dq(const attn_bwd_params* p, hipStream_t stream) {
 
 hipError_t attn_bwd_dkdv_dq(const attn_bwd_params* p, hipStream_t stream) {
   return bwd_stages(p, sdpa::kStageDkDv | sdpa::kStageDq, stream);
+}
+
+hipError_t attn_bwd_plan(const attn_bwd_params* p, uint32_t steps, hipStream_t stream, attn_plan* plan) {
+  if (!plan || steps == 0 || (steps & ~(uint32_t)ATTN_BWD_ALL) != 0) return hipErrorInvalidValue;
+  hipError_t err = check_bwd(p, false);
+  if (err != hipSuccess) return err;
+  const attn_fwd_params* f = &p->fwd;
+  const sdpa::BwdArgs a = bwd_args(p, nullptr);
+  sdpa::Plan pl{};
+  err = on_stream_device(
+      stream, [&] { return sdpa::launch_bwd(f->dtype, f->head_dim, a, (int)steps, sdpa::Record{&pl}); });
+  if (err == hipSuccess) plan_out(pl, plan);
+  return err;
 }
 
 }  // extern "C"

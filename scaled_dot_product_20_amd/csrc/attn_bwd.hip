@@ -409,15 +409,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 // wave keeps its 32 keys' K and V rows in registers (B operands).  Query
 // tiles of BMQ rows of Q and dO are copied HBM -> LDS with direct loads into
 // swizzled row-major tiles, two stages deep, with the tile's LSE (as log2)
-// and Delta beside them; query rows past the sequence get LSE = +inf, so
-// their P is exactly 0.  Per 32-query slice:
+// and Delta beside them; tile rows past the sequence repeat its last row
+// (every loaded value is a finite input) and are masked out: the tile is
+// treated as cut, and those rows' scores are set to -inf, so their P is
+// exactly 0.  Per 32-query slice:
 //   S = Q K^T and dP = dO V^T from 128-bit row reads of the Q and dO tiles;
 //   P = 2^(c S - LSE log2(e)) with c = |scale| log2(e) (a negative scale is
 //   moved into the K operand), dS = P o (dP - Delta);
 //   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T taken by
 //   transposing reads of the same tiles.
 // Each wave visits only the query tiles that can see its keys; tiles cut
-// by the window have their scores set to -inf where masked.
+// by the window or the sequence end have their scores set to -inf where
+// masked.
 template <typename M, int D, int BMQ>
 struct Dkdv16 {
   using T = typename M::elem;
@@ -1277,13 +1280,11 @@ struct BwdShape {
   static constexpr bool PC = k16 && D > 80;
 };
 
-template <typename M, int D>
-static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
+template <typename M, int D, class Ex>
+static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
   using T = typename M::elem;
   using S = BwdShape<M, D>;
   constexpr int NW_KV = S::NW_KV, BMQ = S::BMQ, NW_Q = S::NW_Q, BN = S::BN;
-  BwdArgs args = a;
-  void* kargs[] = {&args};
   hipError_t err;
   // 1. Delta.
   if (stages & kStageDelta) {
@@ -1294,10 +1295,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
     const long long nblk = (nrows + (256 / G) - 1) / (256 / G);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (nblk > 0) {
-      long long nr = nrows;
-      void* pargs[] = {&args, &nr};
-      err = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_pre_kernel<T, D>),
-                            dim3((unsigned)nblk), dim3(256), pargs, 0, stream);
+      err = ex(reinterpret_cast<const void*>(&attn_bwd_pre_kernel<T, D>), "attn_bwd_pre_kernel", (unsigned)nblk,
+               256u, a, nrows);
       if (err != hipSuccess) return err;
     }
   }
@@ -1314,12 +1313,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
       const long long nkv = (a.p.Sk + 127) / 128 * a.p.H * a.p.B;
       const long long ndq = (a.p.Sq + 255) / 256 * a.p.H * a.p.B;
       if (nkv + ndq > 0x7fffffffLL) return hipErrorInvalidValue;
-      if (nkv > 0 && ndq > 0) {  // otherwise the separate kernels below write the zeros
-        int nk = (int)nkv;
-        void* fargs[] = {&args, &nk};
-        return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_fused16_kernel<M, D>),
-                               dim3((unsigned)(nkv + ndq)), dim3(512), fargs, 0, stream);
-      }
+      if (nkv > 0 && ndq > 0)  // otherwise the separate kernels below write the zeros
+        return ex(reinterpret_cast<const void*>(&attn_bwd_fused16_kernel<M, D>), "attn_bwd_fused16_kernel",
+                  (unsigned)(nkv + ndq), 512u, a, (int)nkv);
     }
   }
   // 2. dK, dV.
@@ -1328,17 +1324,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
     const long long nblk = nkb * a.p.H * a.p.B;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (nblk > 0) {
-      const void* fn;
-      int threads = NW_KV * 64;
-      if constexpr (S::PC) {
-        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16pc_kernel<M, D>);
-        threads = 512;
-      } else if constexpr (S::k16) {
-        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, 2>);
-      } else {
-        fn = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>);
-      }
-      err = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(threads), kargs, 0, stream);
+      if constexpr (S::PC)
+        err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16pc_kernel<M, D>), "attn_bwd_dkdv16pc_kernel",
+                 (unsigned)nblk, 512u, a);
+      else if constexpr (S::k16)
+        err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, 2>),
+                 "attn_bwd_dkdv16_kernel", (unsigned)nblk, (unsigned)(NW_KV * 64), a);
+      else
+        err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>), "attn_bwd_dkdv_kernel",
+                 (unsigned)nblk, (unsigned)(NW_KV * 64), a);
       if (err != hipSuccess) return err;
     }
   }
@@ -1348,44 +1342,52 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream)
     const long long nblk = nq * a.p.H * a.p.B;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (nblk > 0) {
-      const void* fn;
       if constexpr (S::k16)
-        fn = reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, 2>);
+        err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, 2>), "attn_bwd_dq16_kernel",
+                 (unsigned)nblk, (unsigned)(NW_Q * 64), a);
       else
-        fn = reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN>);
-      err = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NW_Q * 64), kargs, 0, stream);
+        err = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN>), "attn_bwd_dq_kernel",
+                 (unsigned)nblk, (unsigned)(NW_Q * 64), a);
       if (err != hipSuccess) return err;
     }
   }
   return hipSuccess;
 }
 
-template <typename M>
-static hipError_t launch_bwd_d(int head_dim, const BwdArgs& a, int stages, hipStream_t stream) {
+template <typename M, class Ex>
+static hipError_t launch_bwd_d(int head_dim, const BwdArgs& a, int stages, const Ex& ex) {
   switch (head_dim) {
-    case 32: return launch_bwd_t<M, 32>(a, stages, stream);
-    case 48: return launch_bwd_t<M, 48>(a, stages, stream);
-    case 64: return launch_bwd_t<M, 64>(a, stages, stream);
-    case 80: return launch_bwd_t<M, 80>(a, stages, stream);
-    case 96: return launch_bwd_t<M, 96>(a, stages, stream);
-    case 128: return launch_bwd_t<M, 128>(a, stages, stream);
+    case 32: return launch_bwd_t<M, 32>(a, stages, ex);
+    case 48: return launch_bwd_t<M, 48>(a, stages, ex);
+    case 64: return launch_bwd_t<M, 64>(a, stages, ex);
+    case 80: return launch_bwd_t<M, 80>(a, stages, ex);
+    case 96: return launch_bwd_t<M, 96>(a, stages, ex);
+    case 128: return launch_bwd_t<M, 128>(a, stages, ex);
     default: return hipErrorNotSupported;
   }
 }
 
-hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, hipStream_t stream) {
+template <class Ex>
+static hipError_t launch_bwd_any(int dtype, int head_dim, const BwdArgs& a, int stages, const Ex& ex) {
   hipError_t err;
   switch (dtype) {
-    case 0: err = launch_bwd_d<MmaF32>(head_dim, a, stages, stream); break;
-    case 1: err = launch_bwd_d<MmaF16>(head_dim, a, stages, stream); break;
-    case 2: err = launch_bwd_d<MmaBF16>(head_dim, a, stages, stream); break;
+    case 0: err = launch_bwd_d<MmaF32>(head_dim, a, stages, ex); break;
+    case 1: err = launch_bwd_d<MmaF16>(head_dim, a, stages, ex); break;
+    case 2: err = launch_bwd_d<MmaBF16>(head_dim, a, stages, ex); break;
     default: return hipErrorNotSupported;
   }
   // Rows past the used ones (seqused arrays): dQ, and dK / dV, are zero.
   const int esz = dtype == 0 ? 4 : 2, rb = head_dim * esz;
-  if (err == hipSuccess && (stages & kStageDq)) err = launch_pad_rows(a.p, a.dq, Operand{}, nullptr, 0, rb, esz, stream);
-  if (err == hipSuccess && (stages & kStageDkDv)) err = launch_pad_rows(a.p, a.dk, a.dv, nullptr, 1, rb, esz, stream);
+  if (err == hipSuccess && (stages & kStageDq)) err = launch_pad_rows(a.p, a.dq, Operand{}, nullptr, 0, rb, esz, ex);
+  if (err == hipSuccess && (stages & kStageDkDv)) err = launch_pad_rows(a.p, a.dk, a.dv, nullptr, 1, rb, esz, ex);
   return err;
+}
+
+hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, const Enqueue& ex) {
+  return launch_bwd_any(dtype, head_dim, a, stages, ex);
+}
+hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, const Record& ex) {
+  return launch_bwd_any(dtype, head_dim, a, stages, ex);
 }
 
 }  // namespace sdpa

@@ -996,8 +996,8 @@ struct FwdShape {
   static constexpr int WPE = 2;  // waves per SIMD the registers allow
 };
 
-template <typename M, int D>
-static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+template <typename M, int D, class Ex>
+static hipError_t launch_fwd_t(const FwdArgs& a, const Ex& ex) {
   using S = FwdShape<M, D>;
   constexpr int BN = S::BN;
   const bool pp = S::PP && wide_window(a.p);
@@ -1006,9 +1006,6 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const long long nblk = nq * a.p.H * a.p.B;
   if (nblk == 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-  FwdArgs args = a;
-  void* kargs[] = {&args};
-  const void* fn;
   if constexpr (S::k16) {
     if (pp) {
       // Full rounds of 256-row workgroups (pp_per_cu per CU) on the
@@ -1022,32 +1019,30 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
       const long long cus = device_cu_count() * pp_per_cu<D>();
       if (cus > 0 && nblk >= cus && nblk < 4 * cus && 4 * (nblk % cus) <= cus)
         nmain = nblk - nblk % cus;
-      int nqi = (int)nq;
-      void* pargs[] = {&args, &nqi};
-      hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, BN>),
-                                       dim3((unsigned)nmain), dim3(512), pargs, 0, stream);
+      const int nqi = (int)nq;
+      hipError_t err = ex(reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, BN>), "attn_fwd16pp_kernel",
+                          (unsigned)nmain, 512u, a, nqi);
       if (err != hipSuccess || nmain == nblk) return err;
-      int base = (int)nmain;
-      void* sargs[] = {&args, &nqi, &base};
-      return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd16split_kernel<M, D>),
-                             dim3((unsigned)(4 * (nblk - nmain))), dim3(256), sargs, 0, stream);
+      return ex(reinterpret_cast<const void*>(&attn_fwd16split_kernel<M, D>), "attn_fwd16split_kernel",
+                (unsigned)(4 * (nblk - nmain)), 256u, a, nqi, (int)nmain);
     }
-    fn = reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, S::NW, BN, S::RB, S::WPE>);
+    return ex(reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, S::NW, BN, S::RB, S::WPE>),
+              "attn_fwd16_kernel", (unsigned)nblk, (unsigned)(nw * 64), a);
   } else {
-    fn = reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, S::NW, BN>);
+    return ex(reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, S::NW, BN>), "attn_fwd_kernel", (unsigned)nblk,
+              (unsigned)(nw * 64), a);
   }
-  return hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(nw * 64), kargs, 0, stream);
 }
 
-template <typename M>
-static hipError_t launch_fwd_d(int head_dim, const FwdArgs& a, hipStream_t stream) {
+template <typename M, class Ex>
+static hipError_t launch_fwd_d(int head_dim, const FwdArgs& a, const Ex& ex) {
   switch (head_dim) {
-    case 32: return launch_fwd_t<M, 32>(a, stream);
-    case 48: return launch_fwd_t<M, 48>(a, stream);
-    case 64: return launch_fwd_t<M, 64>(a, stream);
-    case 80: return launch_fwd_t<M, 80>(a, stream);
-    case 96: return launch_fwd_t<M, 96>(a, stream);
-    case 128: return launch_fwd_t<M, 128>(a, stream);
+    case 32: return launch_fwd_t<M, 32>(a, ex);
+    case 48: return launch_fwd_t<M, 48>(a, ex);
+    case 64: return launch_fwd_t<M, 64>(a, ex);
+    case 80: return launch_fwd_t<M, 80>(a, ex);
+    case 96: return launch_fwd_t<M, 96>(a, ex);
+    case 128: return launch_fwd_t<M, 128>(a, ex);
     default: return hipErrorNotSupported;
   }
 }
@@ -1094,8 +1089,9 @@ __global__ __launch_bounds__(256) void attn_pad_rows_kernel(PadArgs a) {
       a.lse[b * P.olse_sb + h * P.olse_sh + (r0 + u + x) * P.olse_ss] = INFINITY;
 }
 
+template <class Ex>
 hipError_t launch_pad_rows(const ProblemArgs& p, Operand t0, Operand t1, float* lse, int side, int row_bytes,
-                           int esz, hipStream_t stream) {
+                           int esz, const Ex& ex) {
   if ((side ? p.used_k : p.used_q) == nullptr) return hipSuccess;
   const long long nblk = (long long)p.B * p.H;
   if (nblk == 0) return hipSuccess;
@@ -1108,22 +1104,32 @@ hipError_t launch_pad_rows(const ProblemArgs& p, Operand t0, Operand t1, float* 
   a.side = side;
   a.chunks = row_bytes / 16;
   a.esz = esz;
-  void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_pad_rows_kernel), dim3((unsigned)nblk), dim3(256), args,
-                         0, stream);
+  return ex(reinterpret_cast<const void*>(&attn_pad_rows_kernel), "attn_pad_rows_kernel", (unsigned)nblk, 256u, a);
 }
+template hipError_t launch_pad_rows<Enqueue>(const ProblemArgs&, Operand, Operand, float*, int, int, int,
+                                             const Enqueue&);
+template hipError_t launch_pad_rows<Record>(const ProblemArgs&, Operand, Operand, float*, int, int, int,
+                                            const Record&);
 
-hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, hipStream_t stream) {
+template <class Ex>
+static hipError_t launch_fwd_any(int dtype, int head_dim, const FwdArgs& a, const Ex& ex) {
   hipError_t err;
   switch (dtype) {
-    case 0: err = launch_fwd_d<MmaF32>(head_dim, a, stream); break;
-    case 1: err = launch_fwd_d<MmaF16>(head_dim, a, stream); break;
-    case 2: err = launch_fwd_d<MmaBF16>(head_dim, a, stream); break;
+    case 0: err = launch_fwd_d<MmaF32>(head_dim, a, ex); break;
+    case 1: err = launch_fwd_d<MmaF16>(head_dim, a, ex); break;
+    case 2: err = launch_fwd_d<MmaBF16>(head_dim, a, ex); break;
     default: return hipErrorNotSupported;
   }
   if (err != hipSuccess) return err;
   const int esz = dtype == 0 ? 4 : 2;
-  return launch_pad_rows(a.p, a.o, Operand{}, a.lse, 0, head_dim * esz, esz, stream);
+  return launch_pad_rows(a.p, a.o, Operand{}, a.lse, 0, head_dim * esz, esz, ex);
+}
+
+hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, const Enqueue& ex) {
+  return launch_fwd_any(dtype, head_dim, a, ex);
+}
+hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, const Record& ex) {
+  return launch_fwd_any(dtype, head_dim, a, ex);
 }
 
 }  // namespace sdpa

@@ -76,9 +76,12 @@ inline bool wide_window(const ProblemArgs& p) {
   return (long long)p.wl + (long long)p.wr + 1 >= 1024;
 }
 
-// Compute units of the current device (0 if unknown), read once per device.
+// Compute units of the current device (0 if unknown).  The library keeps
+// one value per device, read from the runtime on first use and never changed
+// after (racing first readers store the same value); the split forward tail
+// and the fused dK/dV + dQ grid are chosen from it.
 inline int device_cu_count() {
-  static int cache[64] = {};  // written once per device; racing writers store the same value
+  static int cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
@@ -89,13 +92,50 @@ inline int device_cu_count() {
   return v;
 }
 
+// The launches of one call, as the C ABI's plan queries report them.
+constexpr int kPlanMax = 4;
+struct PlanEntry {
+  const char* name;  // kernel function name (without template arguments)
+  unsigned grid, block;
+};
+struct Plan {
+  int n;
+  PlanEntry e[kPlanMax];
+};
+
+// A launcher decides which kernels a call runs and hands each launch to an
+// executor: Enqueue launches it on a stream, Record only lists it.  Both go
+// through the same decision code, so a plan lists exactly what the call
+// enqueues.  Kernel arguments are passed by value and referenced only for
+// the duration of the launch call.
+struct Enqueue {
+  hipStream_t stream;
+  template <class... A>
+  hipError_t operator()(const void* fn, const char*, unsigned grid, unsigned block, A... args) const {
+    void* ptrs[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(fn, dim3(grid), dim3(block), ptrs, 0, stream);
+  }
+};
+struct Record {
+  Plan* plan;
+  template <class... A>
+  hipError_t operator()(const void*, const char* name, unsigned grid, unsigned block, A...) const {
+    if (plan->n >= kPlanMax) return hipErrorUnknown;
+    plan->e[plan->n++] = PlanEntry{name, grid, block};
+    return hipSuccess;
+  }
+};
+
 // dtype codes follow the C ABI: 0 fp32, 1 fp16, 2 bf16.
-hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, const Enqueue& ex);
+hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, const Record& ex);
+hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, const Enqueue& ex);
+hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, const Record& ex);
 // Rows past the used rows of every sequence (seqused_q for side 0, seqused_k
 // for side 1): zeros in t0 and t1 (null pointers skipped) and, when lse is
 // given, LSE = +inf.  Rows are row_bytes long (a multiple of 16).
+template <class Ex>
 hipError_t launch_pad_rows(const ProblemArgs& p, Operand t0, Operand t1, float* lse, int side, int row_bytes,
-                           int esz, hipStream_t stream);
-hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, hipStream_t stream);
+                           int esz, const Ex& ex);
 
 }  // namespace sdpa

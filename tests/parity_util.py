@@ -34,15 +34,33 @@ def ulp(x, dtype):
     return np.ldexp(1.0, e - _SIG_BITS[dtype])
 
 
-def max_err(name, got, ref, tol, inf_exact=False):
-    """Max |got - ref| over all elements; +inf in ref must be matched exactly.
+def half_ulp_bound(got, ref, tol, dtype):
+    """Per-element bound on |got - ref|: tol, plus half the output type's
+    spacing wherever that spacing exceeds tol.  A result computed within tol
+    of ref and then rounded to the output type lies within tol + 1/2 ulp of
+    ref; below that spacing the absolute bound alone decides.  The spacing is
+    taken at the larger of |got| and |ref|, so a value rounded across a power
+    of two is held to the coarser side's spacing."""
+    if dtype not in _SIG_BITS:
+        return np.full(np.shape(ref), tol, dtype=np.float64)
+    u = ulp(np.maximum(np.abs(got), np.abs(ref)), dtype)
+    return np.where(u > tol, tol + 0.5 * u, tol)
 
-    Each element is held to max(tol, one ulp of the output type at ref): no
-    value of that type lies closer to ref than half an ulp, so where the
-    type's spacing exceeds the absolute bound (bf16 values of magnitude 8 and
-    up against the 4e-2 gradient bound, e.g. dV of one key summed over a
-    hundred queries) the bound is the output's own rounding plus the
-    accumulation error that may carry a value across a rounding midpoint."""
+
+# Elements (per comparison name) that exceeded the absolute bound and were
+# admitted only by the output type's half ulp; printed by every comparison
+# and summed here for a test run.
+HALF_ULP_ADMITTED = {}
+
+
+def max_err(name, got, ref, tol, inf_exact=False):
+    """Max |got - ref| over all elements; +inf in ref must be matched
+    exactly, and any NaN fails.  Each element is held to half_ulp_bound:
+    where the output type's spacing exceeds the absolute bound (bf16 values
+    of magnitude 8 and up against the 4e-2 gradient bound, e.g. dV of one key
+    summed over a hundred queries) the bound is the output's own rounding
+    plus tol.  The elements admitted only by that half ulp are counted and
+    printed."""
     dtype = got.dtype if isinstance(got, torch.Tensor) else torch.float64
     g = got.detach().double().cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
     r = np.asarray(ref, np.float64)
@@ -55,11 +73,15 @@ def max_err(name, got, ref, tol, inf_exact=False):
         g, r = g[~inf], r[~inf]
     d = np.abs(g - r)
     err = float(d.max()) if g.size else 0.0
-    bound = np.maximum(tol, ulp(r, dtype)) if dtype in _SIG_BITS else np.full_like(r, tol)
+    bound = half_ulp_bound(g, r, tol, dtype)
     if g.size and not np.all(d <= bound):
         i = int(np.argmax(d - bound))
-        raise AssertionError(f"{name}: abs err {d.flat[i]:.3e} > {bound.flat[i]:.1e} at ref {r.flat[i]:.4g} "
+        raise AssertionError(f"{name}: abs err {d.flat[i]:.3e} > {bound.flat[i]:.3e} at ref {r.flat[i]:.4g} "
                              f"(max abs err {err:.3e}, tol {tol:.1e})")
+    admitted = int(np.count_nonzero(d > tol))
+    if admitted:
+        HALF_ULP_ADMITTED[name] = HALF_ULP_ADMITTED.get(name, 0) + admitted
+        say(f"  {name}: {admitted} of {g.size} elements beyond {tol:.1e}, within tol + 1/2 ulp of the output type")
     return err
 
 
@@ -89,11 +111,20 @@ class Case:
         self.cpu = (q, k, v, do)
 
     def tol_factor(self):
-        """1 at the configs' scale 1/sqrt(D).  Off that scale the logits, the
-        exponent errors and the gradient magnitudes all grow with
-        |scale| * sqrt(D) (the logit standard deviation for N(0,1) inputs), so
-        the absolute bound grows with it."""
+        """Factor on the bounds of LSE and the gradients (and of O in fp32):
+        1 at the configs' scale 1/sqrt(D).  Off that scale the logits grow
+        with |scale| * sqrt(D) (the logit standard deviation for N(0,1)
+        inputs), and with them the absolute error of LSE (a logit plus a
+        log), of dS = P (dP - Delta) times scale in dQ and dK, and of the
+        fp32-rounded exponents c * s, whose relative error carries into every
+        P.  That last error is what bounds O in fp32; in fp16 / bf16 the
+        rounding of P to the 16-bit type (a relative 2^-11 / 2^-8, whatever
+        the logits) dominates, and O's bound there stays unscaled."""
         return max(1.0, abs(self.scale) * math.sqrt(self.D))
+
+    def o_tol(self):
+        base = TOL[self.dtype]
+        return base * self.tol_factor() if self.dtype == torch.float32 else base
 
     def kw_oracle(self):
         kw = dict(scale=self.scale, window=self.window, diag=self.diag)
@@ -135,8 +166,9 @@ class Case:
             f"dtype={self.dtype} window={self.window} diag={self.diag} scale={self.scale} seed={self.seed}")
         got = self.gpu(dev, bwd)
         ref = self.oracle(bwd)
-        tol = TOL[self.dtype] * self.tol_factor()
-        errs = {"o": max_err("O", got["o"], ref["o"], tol),
+        base = TOL[self.dtype]
+        tol = base * self.tol_factor()
+        errs = {"o": max_err("O", got["o"], ref["o"], self.o_tol()),
                 "lse": max_err("LSE", got["lse"], ref["lse"], tol, inf_exact=True)}
         if bwd:
             for n in ("dq", "dk", "dv"):

@@ -296,3 +296,46 @@ def test_lse_th_flag():
     p.flags = bd.FLAG_LSE_TH
     assert fcheck(p) == INVALID
     assert bcheck(bwd_params(p)) == INVALID
+
+
+def test_plan_struct_and_constants_match_header(tmp_path):
+    """attn_plan's layout and the backward step bits are the header's."""
+    src = tmp_path / "plan.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "attn.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %d %u %u %u %u\n", sizeof(attn_plan), offsetof(attn_plan, kernel),
+         offsetof(attn_plan, grid), offsetof(attn_plan, block), offsetof(attn_plan, count), ATTN_PLAN_MAX,
+         ATTN_BWD_PREPROCESS, ATTN_BWD_DKDV, ATTN_BWD_DQ, ATTN_BWD_ALL);
+  return 0;
+}
+""")
+    exe = tmp_path / "plan"
+    subprocess.check_call(["gcc", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                           "-I" + os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    want = [ctypes.sizeof(bd.Plan), bd.Plan.kernel.offset, bd.Plan.grid.offset, bd.Plan.block.offset,
+            bd.Plan.count.offset, bd.PLAN_MAX, bd.BWD_PREPROCESS, bd.BWD_DKDV, bd.BWD_DQ, bd.BWD_ALL]
+    assert got == want
+
+
+def test_plan_validation_errors():
+    """The plan queries run the call's own validation first (no HIP call is
+    reached for a malformed call); attn_bwd_plan takes any non-empty subset of
+    the three steps and ignores the workspace."""
+    lib = bd.lib()
+    pl = bd.Plan()
+    bad = dense_params()
+    bad.version = 9
+    assert lib.attn_fwd_plan(ctypes.byref(bad), None, ctypes.byref(pl)) == INVALID
+    assert lib.attn_fwd_plan(ctypes.byref(dense_params(D=112)), None, ctypes.byref(pl)) == NOTSUP
+    assert lib.attn_fwd_plan(ctypes.byref(dense_params()), None, None) == INVALID
+    bp = bwd_params(dense_params())
+    for steps in (0, 8, 9, 15):
+        assert lib.attn_bwd_plan(ctypes.byref(bp), steps, None, ctypes.byref(pl)) == INVALID
+    bad = bwd_params(dense_params())
+    bad.dq = bad.fwd.q
+    assert lib.attn_bwd_plan(ctypes.byref(bad), bd.BWD_ALL, None, ctypes.byref(pl)) == INVALID
+
