@@ -240,6 +240,27 @@ typedef struct {
 hipError_t attn_fwd_plan(const attn_fwd_params *p, hipStream_t stream, attn_plan *plan);
 hipError_t attn_bwd_plan(const attn_bwd_params *p, uint32_t steps, hipStream_t stream, attn_plan *plan);
 
+/* ------------------------------------------------- no-allocation backward
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same work and results as attn_bwd (same kernels, bit for
+ * bit), with the workspace taken from a static array of
+ * ATTN_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on until the process ends.  p->workspace and p->workspace_bytes are
+ * ignored.  Allocates nothing, on the host or the device.
+ *  - Limit: problems whose workspace (attn_bwd_workspace_size) exceeds
+ *    ATTN_NOALLOC_SCRATCH_BYTES, i.e. more than about two million (head,
+ *    query row) pairs, return hipErrorOutOfMemory before enqueuing anything.
+ *  - Every call on one device shares that device's array: calls that may
+ *    overlap in time on one device (different streams, or other threads)
+ *    race and must be ordered by the caller.  Nothing in it needs clearing:
+ *    each call writes the part it reads before reading it.
+ *  - The array's device address is looked up on the first call on each
+ *    device; that call must not be made under stream capture. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+hipError_t attn_bwd_noalloc(const attn_bwd_params *p, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,8 +64,10 @@ class BwdParams(ctypes.Structure):
 
 PLAN_MAX = 4
 BWD_PREPROCESS, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
+# ATTN_NOALLOC_SCRATCH_BYTES: the workspace limit of attn_bwd_noalloc.
+NOALLOC_SCRATCH_BYTES = 16 << 20
 # Backward steps each entry point runs (attn_bwd_plan's `steps`).
-ENTRY_STEPS = {"attn_bwd": BWD_ALL, "attn_bwd_preprocess": BWD_PREPROCESS,
+ENTRY_STEPS = {"attn_bwd": BWD_ALL, "attn_bwd_noalloc": BWD_ALL, "attn_bwd_preprocess": BWD_PREPROCESS,
                "attn_bwd_dkdv": BWD_DKDV, "attn_bwd_dq": BWD_DQ, "attn_bwd_dkdv_dq": BWD_DKDV | BWD_DQ}
 
 
@@ -89,7 +91,8 @@ def lib():
         l = ctypes.CDLL(LIB_PATH)
         for name, ptype in (("attn_fwd", FwdParams), ("attn_bwd", BwdParams),
                             ("attn_bwd_preprocess", BwdParams), ("attn_bwd_dkdv", BwdParams),
-                            ("attn_bwd_dq", BwdParams), ("attn_bwd_dkdv_dq", BwdParams)):
+                            ("attn_bwd_dq", BwdParams), ("attn_bwd_dkdv_dq", BwdParams),
+                            ("attn_bwd_noalloc", BwdParams)):
             f = getattr(l, name)
             f.argtypes = [ctypes.POINTER(ptype), ctypes.c_void_p]
             f.restype = ctypes.c_int
@@ -315,6 +318,33 @@ def plan(name: str, params, stream: Optional[int] = None):
     if rc:
         raise AttnError(name + " plan", rc)
     return [(pl.kernel[i].decode(), int(pl.grid[i]), int(pl.block[i])) for i in range(pl.count)]
+
+
+def attn_bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                     lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, *, scale=None,
+                     window=(WINDOW_INF, WINDOW_INF), diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None,
+                     max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                     lse_layout: str = "ht", seqused_q=None, seqused_k=None):
+    """attn_bwd_noalloc: the backward into caller-given dq, dk, dv, with its
+    workspace in the library's per-device static array (nothing allocated).
+    Raises when the problem's workspace exceeds NOALLOC_SCRATCH_BYTES."""
+    _check_inputs(q, k, v, o, dout)
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if q.dim() == 3 and (max_seqlen_q is None or max_seqlen_k is None):
+        raise ValueError("packed inputs need max_seqlen_q and max_seqlen_k (no device read-back here)")
+    kw = dict(scale=scale, window=window, diag=diag, cu_seqlens_q=_cu(cu_seqlens_q, dev),
+              cu_seqlens_k=_cu(cu_seqlens_k, dev), max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+              lse_layout=lse_layout, seqused_q=seqused_q, seqused_k=seqused_k)
+    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **kw)
+    rc = lib().attn_bwd_noalloc(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
+    if rc == 2:  # hipErrorOutOfMemory
+        need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))
+        raise AttnError(f"attn_bwd_noalloc (workspace {need} B > limit {NOALLOC_SCRATCH_BYTES} B)", rc)
+    if rc:
+        raise AttnError("attn_bwd_noalloc", rc)
+    return dq, dk, dv
 
 
 def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,

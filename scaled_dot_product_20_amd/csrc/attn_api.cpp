@@ -2,11 +2,13 @@
 // marshalling into kernel argument blocks, and the device taken from the
 // stream.  Nothing is allocated per call and nothing is printed.  The
 // library's only state is written once per device and never changed after:
-// the compute-unit count the launchers read (attn_launch.hpp).
+// the compute-unit count the launchers read (attn_launch.hpp), and the device
+// address of the no-allocation backward's scratch array (below).
 #include "attn.h"
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "attn_launch.hpp"
 
@@ -250,6 +252,42 @@ void plan_out(const sdpa::Plan& pl, attn_plan* out) {
   }
 }
 
+}  // namespace
+
+// ------------------------------------------------ no-allocation backward
+//
+// The workspace of attn_bwd_noalloc: one array per device, in the library's
+// code object, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it names a stand-in, not device
+// memory): the device address is looked up once per device, with that
+// device current, and kept.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array.
+hipError_t scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+
 // Runs `launch` with the stream's device current, restoring the caller's.
 template <typename F>
 hipError_t on_stream_device(hipStream_t stream, F launch) {
@@ -364,6 +402,20 @@ hipError_t attn_bwd_plan(const attn_bwd_params* p, uint32_t steps, hipStream_t s
       stream, [&] { return sdpa::launch_bwd(f->dtype, f->head_dim, a, (int)steps, sdpa::Record{&pl}); });
   if (err == hipSuccess) plan_out(pl, plan);
   return err;
+}
+
+hipError_t attn_bwd_noalloc(const attn_bwd_params* p, hipStream_t stream) {
+  hipError_t err = check_bwd(p, false);
+  if (err != hipSuccess) return err;
+  const attn_fwd_params* f = &p->fwd;
+  if (delta_bytes(f) > (uint64_t)ATTN_NOALLOC_SCRATCH_BYTES) return hipErrorOutOfMemory;
+  return on_stream_device(stream, [&] {
+    void* ws = nullptr;
+    const hipError_t serr = scratch_ptr(&ws);
+    if (serr != hipSuccess) return serr;
+    const sdpa::BwdArgs a = bwd_args(p, ws);
+    return sdpa::launch_bwd(f->dtype, f->head_dim, a, sdpa::kStageAll, sdpa::Enqueue{stream});
+  });
 }
 
 }  // extern "C"

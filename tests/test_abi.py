@@ -299,16 +299,17 @@ def test_lse_th_flag():
 
 
 def test_plan_struct_and_constants_match_header(tmp_path):
-    """attn_plan's layout and the backward step bits are the header's."""
+    """attn_plan's layout, the backward step bits and the no-allocation limit
+    are the header's."""
     src = tmp_path / "plan.c"
     src.write_text(r"""
 #include <stdio.h>
 #include <stddef.h>
 #include "attn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %d %u %u %u %u\n", sizeof(attn_plan), offsetof(attn_plan, kernel),
+  printf("%zu %zu %zu %zu %zu %d %u %u %u %u %u\n", sizeof(attn_plan), offsetof(attn_plan, kernel),
          offsetof(attn_plan, grid), offsetof(attn_plan, block), offsetof(attn_plan, count), ATTN_PLAN_MAX,
-         ATTN_BWD_PREPROCESS, ATTN_BWD_DKDV, ATTN_BWD_DQ, ATTN_BWD_ALL);
+         ATTN_BWD_PREPROCESS, ATTN_BWD_DKDV, ATTN_BWD_DQ, ATTN_BWD_ALL, ATTN_NOALLOC_SCRATCH_BYTES);
   return 0;
 }
 """)
@@ -317,7 +318,8 @@ int main(void) {
                            "-I" + os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
     got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
     want = [ctypes.sizeof(bd.Plan), bd.Plan.kernel.offset, bd.Plan.grid.offset, bd.Plan.block.offset,
-            bd.Plan.count.offset, bd.PLAN_MAX, bd.BWD_PREPROCESS, bd.BWD_DKDV, bd.BWD_DQ, bd.BWD_ALL]
+            bd.Plan.count.offset, bd.PLAN_MAX, bd.BWD_PREPROCESS, bd.BWD_DKDV, bd.BWD_DQ, bd.BWD_ALL,
+            bd.NOALLOC_SCRATCH_BYTES]
     assert got == want
 
 
@@ -339,3 +341,20 @@ def test_plan_validation_errors():
     bad.dq = bad.fwd.q
     assert lib.attn_bwd_plan(ctypes.byref(bad), bd.BWD_ALL, None, ctypes.byref(pl)) == INVALID
 
+
+def test_noalloc_validation_and_limit():
+    """attn_bwd_noalloc checks the call as attn_bwd does except for the
+    workspace, which it ignores, and refuses a problem whose workspace exceeds
+    its static array (hipErrorOutOfMemory) before any HIP call."""
+    lib = bd.lib()
+    p = bwd_params(dense_params())
+    p.dq = p.fwd.q
+    assert lib.attn_bwd_noalloc(ctypes.byref(p), None) == INVALID
+    p = bwd_params(dense_params(D=112))
+    assert lib.attn_bwd_noalloc(ctypes.byref(p), None) == NOTSUP
+    # 3 x 16 x 87382 query rows: 2 x 16 MiB of workspace > the 16 MiB limit.
+    f = dense_params(B=3, H=16, S=87382)
+    big = bwd_params(f)
+    need = lib.attn_bwd_workspace_size(ctypes.byref(big))
+    assert need > bd.NOALLOC_SCRATCH_BYTES
+    assert lib.attn_bwd_noalloc(ctypes.byref(big), None) == 2
