@@ -57,10 +57,14 @@
 extern "C" {
 #endif
 
-/* Version of the params structs below; a mismatch is hipErrorInvalidValue
- * (the versioned-params idea of the AOTriton 0.15b release notes, "API
- * Changes": kVersion fields, reserved bits rejected). */
-#define ATTN_PARAMS_VERSION 2u
+/* Version of the params structs below (the versioned-params idea of the
+ * AOTriton 0.15b release notes, "API Changes": kVersion fields, reserved bits
+ * rejected).  Version 3 adds the per-side addressing fields at the end of
+ * attn_fwd_params.  Structs of version 2 (the same layout without those
+ * fields, and attn_bwd_params embedding that shorter struct) are still
+ * accepted and translated, as the AOTriton 0.14b notes do for older params
+ * ("ABI backward compatibility"); any other version is hipErrorInvalidValue. */
+#define ATTN_PARAMS_VERSION 3u
 
 /* Bits of attn_fwd_params.flags; every other bit must be 0.
  * ATTN_FLAG_LSE_TH (packed layout only): lse is [total_q, heads] (the "TH"
@@ -77,14 +81,56 @@ extern "C" {
 #define ATTN_FP16 1
 #define ATTN_BF16 2
 
-/* ATTN_BHSD: dense [batch, heads, seq, head_dim] addressed with strides
- *            {batch, head, row}.
- * ATTN_THD:  packed [total, heads, head_dim]; sequence b owns rows
- *            cu_seqlens[b] .. cu_seqlens[b+1]-1 ("stacked" varlen of the
- *            AOTriton 0.14b release notes, "VarlenBits supersedes
- *            VarlenType"); strides {ignored, head, row}. */
+/* ATTN_BHSD:   dense [batch, heads, seq, head_dim] addressed with strides
+ *              {batch, head, row}.
+ * ATTN_THD:    packed [total, heads, head_dim]; sequence b owns rows
+ *              cu_seqlens[b] .. cu_seqlens[b+1]-1 ("stacked" varlen of the
+ *              AOTriton 0.14b release notes, "VarlenBits supersedes
+ *              VarlenType"); strides {ignored, head, row}.
+ * ATTN_VARLEN: each side addressed on its own by the mode byte of its side
+ *              in `varlen` (below).  ATTN_BHSD is the mode 0 on both sides
+ *              (plus ATTN_SEQ_LEN_ARRAY where seqused is given), ATTN_THD the
+ *              mode ATTN_SEQ_STACKED | ATTN_SEQ_LEN_CUMSUM |
+ *              ATTN_SEQ_POS_CUMSUM (LEN_ARRAY with seqused). */
 #define ATTN_BHSD 0
 #define ATTN_THD 1
+#define ATTN_VARLEN 2
+
+/* Mode byte of one side (VarlenMode of the AOTriton 0.14b VarlenBits: Q and
+ * K decode independently along three axes).  Bit 0, storage:
+ *   0 padded:  sequence b's rows start at b * stride[0] (a [batch, heads,
+ *              seqlen, head_dim]-style tensor; seqlen rows of room each);
+ *   ATTN_SEQ_STACKED: rows of every sequence in one [total, heads,
+ *              head_dim] tensor (stride[0] ignored).
+ * Bits 2:1, lengths:
+ *   ATTN_SEQ_LEN_UNIFORM: every sequence has seqlen_q / seqlen_k rows;
+ *   ATTN_SEQ_LEN_CUMSUM:  cu_seqlens[b+1] - cu_seqlens[b];
+ *   ATTN_SEQ_LEN_ARRAY:   seqused[b] (seqused_q / seqused_k).
+ * Bits 4:3, start row of sequence b in a stacked tensor (padded: 0):
+ *   ATTN_SEQ_POS_UNIFORM: b * seqlen;
+ *   ATTN_SEQ_POS_CUMSUM:  cu_seqlens[b];
+ *   ATTN_SEQ_POS_ARRAY:   seqstart[b] (seqstart_q / seqstart_k).
+ * A sequence's room is seqlen rows (padded, or stacked with POS_UNIFORM) or
+ * its cu_seqlens range (stacked with POS_CUMSUM); with POS_ARRAY it is not
+ * known.  LEN_ARRAY lengths are clamped to the room, or to seqlen when the
+ * room is not known; rows of the room past the length are written as fully
+ * masked rows (O = 0, LSE = +inf, gradients 0), rows outside every sequence
+ * are never touched.  The sequences of one side must not overlap (outputs
+ * are written per sequence).  Every row a mode addresses must lie in the
+ * tensor: total rows (stacked) or batch * seqlen rows (padded).  The LSE
+ * (and the backward's workspace) follows the Q side: [batch, heads,
+ * seqlen_q] padded, [heads, total_q] (or [total_q, heads] with
+ * ATTN_FLAG_LSE_TH) stacked. */
+#define ATTN_SEQ_STACKED 0x01u
+#define ATTN_SEQ_LEN_UNIFORM 0x00u
+#define ATTN_SEQ_LEN_CUMSUM 0x02u
+#define ATTN_SEQ_LEN_ARRAY 0x04u
+#define ATTN_SEQ_POS_UNIFORM 0x00u
+#define ATTN_SEQ_POS_CUMSUM 0x08u
+#define ATTN_SEQ_POS_ARRAY 0x10u
+/* `varlen` field of attn_fwd_params (ATTN_VARLEN only; 0 otherwise): Q's
+ * mode byte in bits 7:0, K's in bits 15:8, the rest 0. */
+#define ATTN_VARLEN_BITS(qmode, kmode) ((uint32_t)(qmode) | ((uint32_t)(kmode) << 8))
 
 /* Principal diagonal (AOTriton 0.15b, VarlenPrincipalDiagonal). */
 #define ATTN_TOP_LEFT 0
@@ -94,19 +140,24 @@ typedef struct {
   uint32_t version;        /* ATTN_PARAMS_VERSION */
   uint32_t flags;          /* 0 or ATTN_FLAG_LSE_TH (THD only) */
   int32_t dtype;           /* ATTN_FP32 / ATTN_FP16 / ATTN_BF16 */
-  int32_t layout;          /* ATTN_BHSD / ATTN_THD */
-  int32_t batch;           /* BHSD: batch; THD: number of sequences (>= 1) */
+  int32_t layout;          /* ATTN_BHSD / ATTN_THD / ATTN_VARLEN */
+  int32_t batch;           /* BHSD: batch; THD: number of sequences (>= 1);
+                              VARLEN: number of sequences (>= 1 if a side
+                              is stacked) */
   int32_t heads;           /* >= 1; Q, K and V have the same head count */
   int32_t head_dim;        /* 32, 48, 64, 80, 96 or 128; V/O share it */
-  int32_t seqlen_q;        /* BHSD: Sq (>= 0); THD: max sequence length of Q */
-  int32_t seqlen_k;        /* BHSD: Sk (>= 0); THD: max sequence length of K */
+  int32_t seqlen_q;        /* BHSD: Sq (>= 0); THD: max sequence length of Q;
+                              VARLEN: the Q side's uniform length / room,
+                              and the largest length (>= 0) */
+  int32_t seqlen_k;        /* the same for K */
   int32_t window_left;     /* any int32; ATTN_WINDOW_INF = unbounded */
   int32_t window_right;    /* any int32; ATTN_WINDOW_INF = unbounded */
   int32_t diag;            /* ATTN_TOP_LEFT / ATTN_BOTTOM_RIGHT */
   float scale;             /* any finite value, 0 and negatives included */
   int32_t reserved0;       /* must be 0 */
-  int64_t total_q;         /* THD: rows of Q/O/dO (= cu_seqlens_q[batch]) */
-  int64_t total_k;         /* THD: rows of K/V (= cu_seqlens_k[batch]) */
+  int64_t total_q;         /* stacked Q side: rows of Q/O/dO (THD:
+                              = cu_seqlens_q[batch]) */
+  int64_t total_k;         /* stacked K side: rows of K/V */
   const void *q;           /* input */
   const void *k;           /* input */
   const void *v;           /* input */
@@ -115,8 +166,9 @@ typedef struct {
                               [batch, heads, seqlen_q]; THD: contiguous
                               [heads, total_q] (the "HT" layout), or
                               [total_q, heads] with ATTN_FLAG_LSE_TH. */
-  const int32_t *cu_seqlens_q; /* THD: device int32[batch+1]; BHSD: NULL */
-  const int32_t *cu_seqlens_k; /* THD: device int32[batch+1]; BHSD: NULL */
+  const int32_t *cu_seqlens_q; /* device int32[batch+1]: THD, and VARLEN
+                              with LEN_CUMSUM or POS_CUMSUM on Q; else NULL */
+  const int32_t *cu_seqlens_k; /* the same for K */
   int64_t q_stride[3];     /* element strides {batch, head, row}; the */
   int64_t k_stride[3];     /* head_dim stride is 1.  Base pointers and */
   int64_t v_stride[3];     /* strides must keep every row 16-byte */
@@ -133,7 +185,17 @@ typedef struct {
                               written as fully masked: O = 0, LSE = +inf,
                               dQ = dK = dV = 0.  0 <= seqused[b] <= the
                               sequence's rows is a precondition (values out
-                              of range are clamped, never read past). */
+                              of range are clamped, never read past).  With
+                              ATTN_VARLEN: the lengths of LEN_ARRAY, required
+                              there and NULL otherwise. */
+  /* Version 3. */
+  uint32_t varlen;          /* ATTN_VARLEN: ATTN_VARLEN_BITS(qmode, kmode);
+                              other layouts: 0 */
+  int32_t reserved1;        /* must be 0 */
+  const int32_t *seqstart_q; /* ATTN_VARLEN with POS_ARRAY on Q: device
+                              int32[batch], start row of each sequence in
+                              the stacked tensor; NULL otherwise */
+  const int32_t *seqstart_k; /* the same for K */
 } attn_fwd_params;
 
 typedef struct {

@@ -22,10 +22,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsdpa20.so")
 
 WINDOW_INF = 2147483647
-PARAMS_VERSION = 2
+PARAMS_VERSION = 3
 FLAG_LSE_TH = 1  # ATTN_FLAG_LSE_TH: packed LSE as [T, H]
 FP32, FP16, BF16 = 0, 1, 2
-BHSD, THD = 0, 1
+BHSD, THD, VARLEN = 0, 1, 2
+# Mode byte of one side under VARLEN (ATTN_SEQ_* in include/attn.h).
+SEQ_STACKED = 0x01
+SEQ_LEN_UNIFORM, SEQ_LEN_CUMSUM, SEQ_LEN_ARRAY = 0x00, 0x02, 0x04
+SEQ_POS_UNIFORM, SEQ_POS_CUMSUM, SEQ_POS_ARRAY = 0x00, 0x08, 0x10
 TOP_LEFT, BOTTOM_RIGHT = 0, 1
 
 _DTYPE = {torch.float32: FP32, torch.float16: FP16, torch.bfloat16: BF16}
@@ -49,6 +53,8 @@ class FwdParams(ctypes.Structure):
         ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
         ("q_stride", _I64x3), ("k_stride", _I64x3), ("v_stride", _I64x3), ("o_stride", _I64x3),
         ("seqused_q", ctypes.c_void_p), ("seqused_k", ctypes.c_void_p),
+        ("varlen", ctypes.c_uint32), ("reserved1", ctypes.c_int32),
+        ("seqstart_q", ctypes.c_void_p), ("seqstart_k", ctypes.c_void_p),
     ]
 
 
@@ -155,15 +161,41 @@ def _seqused(t: Optional[torch.Tensor], batch: int, dev):
     return t
 
 
+def _int_array(t: Optional[torch.Tensor], n: int, dev, what: str):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.numel() != n or not t.is_contiguous() or t.device != dev:
+        raise ValueError(f"{what} must be a contiguous int32 tensor of {n} entries on the inputs' device")
+    return t
+
+
+def _side(t: torch.Tensor, mode: int, cu, max_seqlen, name: str):
+    """(stacked, rows or None, seqlen) of one side under an explicit mode."""
+    if mode & SEQ_STACKED:
+        if t.dim() != 3:
+            raise ValueError(f"{name}: a stacked side is [T, H, D]")
+        if max_seqlen is None:
+            raise ValueError(f"{name}: a stacked side needs its max_seqlen (its uniform length for "
+                             "SEQ_POS_UNIFORM)")
+        return True, t.shape[0], int(max_seqlen)
+    if t.dim() != 4:
+        raise ValueError(f"{name}: a padded side is [B, H, S, D]")
+    return False, None, t.shape[2]
+
+
 def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens_k,
-               max_seqlen_q, max_seqlen_k, lse_layout="ht", seqused_q=None, seqused_k=None) -> FwdParams:
+               max_seqlen_q, max_seqlen_k, lse_layout="ht", seqused_q=None, seqused_k=None,
+               q_mode=None, k_mode=None, seqstart_q=None, seqstart_k=None, batch=None) -> FwdParams:
     """Fill an attn_fwd_params from tensors (no device work).  ``lse_layout``
-    'th' (packed inputs only) stores LSE as [T, H] instead of [H, T].
+    'th' (a stacked Q side only) stores LSE as [T, H] instead of [H, T].
     ``seqused_q`` / ``seqused_k`` (int32 [batch] on the device): sequence b
-    uses only its first seqused[b] rows; the rest are written as masked."""
+    uses only its first seqused[b] rows; the rest of its room are written as
+    masked.  ``q_mode`` / ``k_mode`` (SEQ_* bits) select the ATTN_VARLEN
+    layout, each side addressed on its own: a stacked side is [T, H, D], a
+    padded one [B, H, S, D]; ``seqstart_q`` / ``seqstart_k`` are the start
+    rows of SEQ_POS_ARRAY; ``batch`` is required when no array gives it."""
     p = FwdParams()
     p.version = PARAMS_VERSION
-    p.flags = _lse_flags(lse_layout, q.dim() == 3)
     if q.dtype not in _DTYPE:
         raise TypeError(f"unsupported dtype {q.dtype}")
     p.dtype = _DTYPE[q.dtype]
@@ -172,11 +204,36 @@ def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens
     p.scale = float(scale)
     p.q, p.k, p.v, p.o, p.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)
     p.q_stride, p.k_stride, p.v_stride, p.o_stride = _strides(q), _strides(k), _strides(v), _strides(o)
-    if q.dim() == 4:
+    if q_mode is not None or k_mode is not None:
+        if q_mode is None or k_mode is None:
+            raise ValueError("q_mode and k_mode go together")
+        p.layout = VARLEN
+        p.varlen = (int(q_mode) & 0xFF) | ((int(k_mode) & 0xFF) << 8)
+        qst, tq, p.seqlen_q = _side(q, q_mode, cu_seqlens_q, max_seqlen_q, "q")
+        kst, tk, p.seqlen_k = _side(k, k_mode, cu_seqlens_k, max_seqlen_k, "k")
+        p.heads, p.head_dim = q.shape[-2] if qst else q.shape[1], q.shape[-1]
+        p.total_q, p.total_k = tq or 0, tk or 0
+        nb = [x.numel() - 1 for x in (cu_seqlens_q, cu_seqlens_k) if x is not None]
+        nb += [x.numel() for x in (seqused_q, seqused_k, seqstart_q, seqstart_k) if x is not None]
+        nb += [t.shape[0] for t, st in ((q, qst), (k, kst)) if not st]
+        if batch is not None:
+            nb.append(int(batch))
+        if not nb or any(n != nb[0] for n in nb):
+            raise ValueError(f"the sides disagree on the number of sequences: {nb}")
+        p.batch = nb[0]
+        p.flags = FLAG_LSE_TH if lse_layout == "th" and qst else 0
+        if lse_layout not in ("ht", "th") or (lse_layout == "th" and not qst):
+            raise ValueError("lse_layout is 'ht', or 'th' for a stacked Q side")
+        p.cu_seqlens_q, p.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
+        p.seqstart_q = _ptr(_int_array(seqstart_q, p.batch, q.device, "seqstart_q"))
+        p.seqstart_k = _ptr(_int_array(seqstart_k, p.batch, q.device, "seqstart_k"))
+    elif q.dim() == 4:
+        p.flags = _lse_flags(lse_layout, False)
         p.layout = BHSD
         p.batch, p.heads, p.seqlen_q, p.head_dim = q.shape
         p.seqlen_k = k.shape[2]
     elif q.dim() == 3:
+        p.flags = _lse_flags(lse_layout, True)
         if cu_seqlens_q is None or cu_seqlens_k is None:
             raise ValueError("packed [T, H, D] inputs need cu_seqlens_q and cu_seqlens_k")
         p.layout = THD
@@ -218,30 +275,51 @@ def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
-             window: Tuple[int, int] = (WINDOW_INF, WINDOW_INF), diag="top_left",
-             cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
-             max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
-             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, lse_layout: str = "ht",
-             seqused_q: Optional[torch.Tensor] = None, seqused_k: Optional[torch.Tensor] = None):
-    """Forward: returns (O, LSE).  LSE is fp32 [B, H, Sq] (dense), [H, T]
-    (packed) or [T, H] (packed, ``lse_layout='th'``)."""
-    _check_inputs(q, k, v)
+def _problem(q, *, scale=None, window=(WINDOW_INF, WINDOW_INF), diag="top_left", cu_seqlens_q=None,
+             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, lse_layout="ht", seqused_q=None,
+             seqused_k=None, q_mode=None, k_mode=None, seqstart_q=None, seqstart_k=None, batch=None,
+             read_back=True):
+    """The keyword arguments of fwd_params for a call: default scale,
+    cu_seqlens checked, and (packed [T, H, D] inputs without modes) the max
+    lengths read back from cu_seqlens when not given and `read_back`."""
     dev = q.device
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     cu_q, cu_k = _cu(cu_seqlens_q, dev), _cu(cu_seqlens_k, dev)
-    if q.dim() == 3:
+    if q_mode is None and q.dim() == 3:
+        if not read_back and (max_seqlen_q is None or max_seqlen_k is None):
+            raise ValueError("packed inputs need max_seqlen_q and max_seqlen_k (no device read-back here)")
         max_seqlen_q = _max_len(cu_q) if max_seqlen_q is None else max_seqlen_q
         max_seqlen_k = _max_len(cu_k) if max_seqlen_k is None else max_seqlen_k
-        lse_shape = (q.shape[1], q.shape[0]) if lse_layout == "ht" else (q.shape[0], q.shape[1])
-    else:
-        lse_shape = tuple(q.shape[:3])
+    return dict(scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+                max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, lse_layout=lse_layout,
+                seqused_q=seqused_q, seqused_k=seqused_k, q_mode=q_mode, k_mode=k_mode,
+                seqstart_q=seqstart_q, seqstart_k=seqstart_k, batch=batch)
+
+
+def lse_shape(q: torch.Tensor, lse_layout="ht", q_mode=None):
+    """Shape of the LSE a forward writes: [B, H, S] for a padded Q side,
+    [H, T] or [T, H] ('th') for a stacked one."""
+    stacked = q.dim() == 3 if q_mode is None else bool(q_mode & SEQ_STACKED)
+    if not stacked:
+        return tuple(q.shape[:3])
+    return (q.shape[1], q.shape[0]) if lse_layout == "ht" else (q.shape[0], q.shape[1])
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None, **kw):
+    """Forward: returns (O, LSE).  Keywords: scale (default 1/sqrt(D)),
+    window, diag, cu_seqlens_q/k, max_seqlen_q/k, lse_layout, seqused_q/k,
+    and for the ATTN_VARLEN layout q_mode, k_mode, seqstart_q/k, batch (see
+    fwd_params).  LSE is fp32 [B, H, Sq] (padded Q), [H, T] (stacked Q) or
+    [T, H] (stacked Q, ``lse_layout='th'``)."""
+    _check_inputs(q, k, v)
+    dev = q.device
+    pk = _problem(q, **kw)
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
-    lse = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse is None else lse
-    p = fwd_params(q, k, v, o, lse, scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q,
-                   cu_seqlens_k=cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
-                   lse_layout=lse_layout, seqused_q=seqused_q, seqused_k=seqused_k)
+    if lse is None:
+        lse = torch.empty(lse_shape(q, pk["lse_layout"], pk["q_mode"]), dtype=torch.float32, device=dev)
+    p = fwd_params(q, k, v, o, lse, **pk)
     rc = lib().attn_fwd(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
     if rc:
         raise AttnError("attn_fwd", rc)
@@ -260,34 +338,29 @@ def bwd_params(dout, q, k, v, o, lse, dq, dk, dv, workspace, **kw) -> BwdParams:
     return p
 
 
-def prepare_bwd(dout, q, k, v, o, lse, *, scale=None, window=(WINDOW_INF, WINDOW_INF), diag="top_left",
-                cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-                dq=None, dk=None, dv=None, workspace=None, lse_layout="ht", seqused_q=None, seqused_k=None):
-    """Allocate the outputs and workspace of a backward and fill its params
-    once, for callers that launch it repeatedly or step by step.  Returns
-    (params, (dq, dk, dv, workspace)); the tensors must outlive every launch
-    made with the params."""
-    _check_inputs(q, k, v, o, dout)
-    dev = q.device
-    if scale is None:
-        scale = 1.0 / math.sqrt(q.shape[-1])
-    cu_q, cu_k = _cu(cu_seqlens_q, dev), _cu(cu_seqlens_k, dev)
-    if q.dim() == 3:
-        max_seqlen_q = _max_len(cu_q) if max_seqlen_q is None else max_seqlen_q
-        max_seqlen_k = _max_len(cu_k) if max_seqlen_k is None else max_seqlen_k
+def _bwd_outputs(q, k, v, dq, dk, dv):
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
-    kw = dict(scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, lse_layout=lse_layout,
-              seqused_q=seqused_q, seqused_k=seqused_k)
-    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **kw)
+    return dq, dk, dv
+
+
+def prepare_bwd(dout, q, k, v, o, lse, *, dq=None, dk=None, dv=None, workspace=None, **kw):
+    """Allocate the outputs and workspace of a backward and fill its params
+    once, for callers that launch it repeatedly or step by step (keywords as
+    for attn_fwd).  Returns (params, (dq, dk, dv, workspace)); the tensors
+    must outlive every launch made with the params."""
+    _check_inputs(q, k, v, o, dout)
+    dev = q.device
+    pk = _problem(q, **kw)
+    dq, dk, dv = _bwd_outputs(q, k, v, dq, dk, dv)
+    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **pk)
     if workspace is None:
         need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     p.workspace = _ptr(workspace)
     p.workspace_bytes = workspace.numel() * workspace.element_size()
-    p._keep = (cu_q, cu_k)  # device cu_seqlens referenced by the params
+    p._keep = (pk["cu_seqlens_q"], pk["cu_seqlens_k"])  # device cu_seqlens referenced by the params
     return p, (dq, dk, dv, workspace)
 
 
@@ -321,23 +394,15 @@ def plan(name: str, params, stream: Optional[int] = None):
 
 
 def attn_bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-                     lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, *, scale=None,
-                     window=(WINDOW_INF, WINDOW_INF), diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None,
-                     max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
-                     lse_layout: str = "ht", seqused_q=None, seqused_k=None):
+                     lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, **kw):
     """attn_bwd_noalloc: the backward into caller-given dq, dk, dv, with its
-    workspace in the library's per-device static array (nothing allocated).
+    workspace in the library's per-device static array (nothing allocated;
+    keywords as for attn_fwd, packed inputs with their max_seqlen given).
     Raises when the problem's workspace exceeds NOALLOC_SCRATCH_BYTES."""
     _check_inputs(q, k, v, o, dout)
     dev = q.device
-    if scale is None:
-        scale = 1.0 / math.sqrt(q.shape[-1])
-    if q.dim() == 3 and (max_seqlen_q is None or max_seqlen_k is None):
-        raise ValueError("packed inputs need max_seqlen_q and max_seqlen_k (no device read-back here)")
-    kw = dict(scale=scale, window=window, diag=diag, cu_seqlens_q=_cu(cu_seqlens_q, dev),
-              cu_seqlens_k=_cu(cu_seqlens_k, dev), max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
-              lse_layout=lse_layout, seqused_q=seqused_q, seqused_k=seqused_k)
-    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **kw)
+    pk = _problem(q, read_back=False, **kw)
+    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **pk)
     rc = lib().attn_bwd_noalloc(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
     if rc == 2:  # hipErrorOutOfMemory
         need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))
@@ -348,37 +413,13 @@ def attn_bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: to
 
 
 def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-             lse: torch.Tensor, *, scale: Optional[float] = None,
-             window: Tuple[int, int] = (WINDOW_INF, WINDOW_INF), diag="top_left",
-             cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
-             max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
-             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-             lse_layout: str = "ht", seqused_q: Optional[torch.Tensor] = None,
-             seqused_k: Optional[torch.Tensor] = None):
+             lse: torch.Tensor, *, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, **kw):
     """Backward: returns (dQ, dK, dV) given the forward's O and LSE (in the
-    layout ``lse_layout`` names, as for attn_fwd)."""
-    _check_inputs(q, k, v, o, dout)
-    dev = q.device
-    if scale is None:
-        scale = 1.0 / math.sqrt(q.shape[-1])
-    cu_q, cu_k = _cu(cu_seqlens_q, dev), _cu(cu_seqlens_k, dev)
-    if q.dim() == 3:
-        max_seqlen_q = _max_len(cu_q) if max_seqlen_q is None else max_seqlen_q
-        max_seqlen_k = _max_len(cu_k) if max_seqlen_k is None else max_seqlen_k
-    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
-    kw = dict(scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-              max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, lse_layout=lse_layout,
-              seqused_q=seqused_q, seqused_k=seqused_k)
-    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **kw)
-    if workspace is None:
-        need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    p.workspace = _ptr(workspace)
-    p.workspace_bytes = workspace.numel() * workspace.element_size()
-    rc = lib().attn_bwd(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
+    layout ``lse_layout`` names; keywords as for attn_fwd)."""
+    p, (dq, dk, dv, workspace) = prepare_bwd(dout, q, k, v, o, lse, dq=dq, dk=dk, dv=dv, workspace=workspace,
+                                             **kw)
+    rc = lib().attn_bwd(ctypes.byref(p), ctypes.c_void_p(_stream(q.device)))
     if rc:
         raise AttnError("attn_bwd", rc)
     return dq, dk, dv

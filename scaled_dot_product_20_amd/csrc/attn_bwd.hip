@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a, long long 
   const int c = threadIdx.x % G;
   if (row >= nrows) return;  // whole groups leave together
   long long b, h, i;
-  if (P.varlen) {
-    i = row / P.H;  // packed row
+  if (P.qs.mode & kSeqStacked) {
+    i = row / P.H;  // stacked row
     h = row % P.H;
     b = 0;
   } else {
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nkb = (int)(gridDim.x / (P.B * P.H));
-  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nkb, P.B * P.H, P.varlen);
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nkb, P.B * P.H, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int kb = gp.i;
 
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = (int)(gridDim.x / (P.B * P.H));
-  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.varlen);
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nkb = (int)(gridDim.x / (P.B * P.H));
-  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nkb, P.B * P.H, P.varlen);
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nkb, P.B * P.H, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int kb = gp.i;
 
@@ -851,7 +851,7 @@ __device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
   const bool prod = wave < 4;
   const int kw = wave & 3;
   const int nkb = nblk / (P.B * P.H);
-  const GridPos gp = grid_pos(hw, nblk, nkb, P.B * P.H, P.varlen);
+  const GridPos gp = grid_pos(hw, nblk, nkb, P.B * P.H, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int kb = gp.i;
 
@@ -1144,7 +1144,7 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = nblk / (P.B * P.H);
-  const GridPos gp = grid_pos(hw, nblk, nq, P.B * P.H, P.varlen);
+  const GridPos gp = grid_pos(hw, nblk, nq, P.B * P.H, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
@@ -1289,7 +1289,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
   // 1. Delta.
   if (stages & kStageDelta) {
     const long long nrows =
-        a.p.varlen ? a.p.total_q * a.p.H : (long long)a.p.B * a.p.H * a.p.Sq;
+        (a.p.qs.mode & kSeqStacked) ? a.p.total_q * a.p.H : (long long)a.p.B * a.p.H * a.p.Sq;
     constexpr int CE = 16 / (int)sizeof(T), CH = D / CE;
     constexpr int G = CH <= 8 ? 8 : (CH <= 16 ? 16 : 32);
     const long long nblk = (nrows + (256 / G) - 1) / (256 / G);
@@ -1376,7 +1376,7 @@ static hipError_t launch_bwd_any(int dtype, int head_dim, const BwdArgs& a, int 
     case 2: err = launch_bwd_d<MmaBF16>(head_dim, a, stages, ex); break;
     default: return hipErrorNotSupported;
   }
-  // Rows past the used ones (seqused arrays): dQ, and dK / dV, are zero.
+  // Rows of a sequence's room past its length: dQ, and dK / dV, are zero.
   const int esz = dtype == 0 ? 4 : 2, rb = head_dim * esz;
   if (err == hipSuccess && (stages & kStageDq)) err = launch_pad_rows(a.p, a.dq, Operand{}, nullptr, 0, rb, esz, ex);
   if (err == hipSuccess && (stages & kStageDkDv)) err = launch_pad_rows(a.p, a.dk, a.dv, nullptr, 1, rb, esz, ex);

@@ -167,8 +167,8 @@ __host__ __device__ __forceinline__ int xcd_remap(int hw, int n) {
 // Position of hardware block hw in a grid of n = nseq * nbh workgroups:
 // (sequence-head index bh, block index i along the sequence).  Dense
 // problems: xcd_remap hands each XCD a contiguous range, so the blocks of
-// one head share its K/V in that XCD's L2.  Packed sequences of different
-// lengths: bh runs fastest, so each XCD (hardware blocks are dealt to the
+// one head share its K/V in that XCD's L2.  Sequences of different
+// lengths (`ragged`): bh runs fastest, so each XCD (hardware blocks are dealt to the
 // XCDs round-robin) gets the same heads of every sequence at every position
 // along it.  A contiguous range would give whole sequences to one XCD (24
 // sequences of 64..2048 rows, 128-row blocks: the busiest XCD had 1.43x the
@@ -176,8 +176,8 @@ __host__ __device__ __forceinline__ int xcd_remap(int hw, int n) {
 struct GridPos {
   int bh, i;
 };
-__host__ __device__ __forceinline__ GridPos grid_pos(int hw, int n, int nseq, int nbh, bool varlen) {
-  if (varlen) return GridPos{hw % nbh, hw / nbh};
+__host__ __device__ __forceinline__ GridPos grid_pos(int hw, int n, int nseq, int nbh, bool ragged) {
+  if (ragged) return GridPos{hw % nbh, hw / nbh};
   const int blk = xcd_remap(hw, n);
   return GridPos{blk / nseq, blk % nseq};
 }

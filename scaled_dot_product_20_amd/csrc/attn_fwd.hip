@@ -63,7 +63,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = (int)(gridDim.x / (P.B * P.H));
-  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.varlen);
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;  // longest rows (under causal) first
 
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nq = (int)(gridDim.x / (P.B * P.H));
-  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.varlen);
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
@@ -704,7 +704,7 @@ attn_fwd16pp_kernel(FwdArgs a, int nq) {
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.varlen);
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
@@ -851,8 +851,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Logical block L of the whole grid, in the order grid_pos gives the
   // ping-pong kernel's blocks (which cover L < lbase).
   const int nbh = P.B * P.H;
-  const int bh = P.varlen ? L % nbh : L / nq, h = bh % P.H, b = bh / P.H;
-  const int qb = nq - 1 - (P.varlen ? L / nbh : L % nq);
+  const int bh = P.ragged ? L % nbh : L / nq, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - (P.ragged ? L / nbh : L % nq);
 
   long long q0, k0;
   int sq, sk;
@@ -1049,14 +1049,15 @@ static hipError_t launch_fwd_d(int head_dim, const FwdArgs& a, const Ex& ex) {
 
 // ------------------------------------------------ rows past the used ones
 //
-// With seqused arrays, the rows of a sequence past its used rows take part
-// in no attention: they are written as fully masked rows (zeros, LSE +inf).
-// One workgroup per (sequence, head); 16-byte stores.
+// Rows of a sequence's room past its length (lengths from seqused arrays,
+// or cumulative lengths inside uniform rooms) take part in no attention:
+// they are written as fully masked rows (zeros, LSE +inf).  One workgroup
+// per (sequence, head); 16-byte stores.
 struct PadArgs {
   ProblemArgs p;
   Operand t[2];  // tensors whose padding rows are zeroed (null: none)
   float* lse;    // LSE rows set to +inf (query side of the forward), or null
-  int side;      // 0: query rows (seqused_q), 1: key rows (seqused_k)
+  int side;      // 0: query rows, 1: key rows
   int chunks;    // 16-byte chunks per row
   int esz;       // element size of t
 };
@@ -1064,18 +1065,11 @@ struct PadArgs {
 __global__ __launch_bounds__(256) void attn_pad_rows_kernel(PadArgs a) {
   const ProblemArgs& P = a.p;
   const int h = (int)(blockIdx.x % P.H), b = (int)(blockIdx.x / P.H);
-  const int* used = a.side ? P.used_k : P.used_q;
-  long long r0 = 0;
-  int n = a.side ? P.Sk : P.Sq;
-  if (P.varlen) {
-    const int* cu = a.side ? P.cu_k : P.cu_q;
-    r0 = cu[b];
-    n = cu[b + 1] - (int)r0;
-  }
-  const int u = max(0, min(n, used[b]));
-  const long long work = (long long)(n - u) * a.chunks;
+  const SideRows r = side_rows(a.side ? P.ks : P.qs, b);
+  if (r.room < 0) return;
+  const long long work = (long long)(r.room - r.n) * a.chunks;
   for (long long x = threadIdx.x; x < work; x += 256) {
-    const long long row = r0 + u + x / a.chunks;
+    const long long row = r.r0 + r.n + x / a.chunks;
     const int c = (int)(x % a.chunks);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1085,14 +1079,14 @@ __global__ __launch_bounds__(256) void attn_pad_rows_kernel(PadArgs a) {
       }
   }
   if (a.lse)
-    for (int x = threadIdx.x; x < n - u; x += 256)
-      a.lse[b * P.olse_sb + h * P.olse_sh + (r0 + u + x) * P.olse_ss] = INFINITY;
+    for (int x = threadIdx.x; x < r.room - r.n; x += 256)
+      a.lse[b * P.olse_sb + h * P.olse_sh + (r.r0 + r.n + x) * P.olse_ss] = INFINITY;
 }
 
 template <class Ex>
 hipError_t launch_pad_rows(const ProblemArgs& p, Operand t0, Operand t1, float* lse, int side, int row_bytes,
                            int esz, const Ex& ex) {
-  if ((side ? p.used_k : p.used_q) == nullptr) return hipSuccess;
+  if (!side_may_pad(side ? p.ks.mode : p.qs.mode)) return hipSuccess;
   const long long nblk = (long long)p.B * p.H;
   if (nblk == 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;

@@ -13,40 +13,82 @@ struct Operand {
   long long sb, sh, ss;
 };
 
+// Addressing of one side (Q or K) of the problem: the mode byte of the C
+// ABI (bit 0 stacked; bits 2:1 length source uniform / cumulative / array;
+// bits 4:3 start source uniform / cumulative / array) and its arrays.
+struct SideArgs {
+  const int* cu;     // cumulative lengths [B+1] (length or start source 1)
+  const int* len;    // lengths [B] (length source 2)
+  const int* start;  // start rows [B] (start source 2)
+  int mode;
+  int S;             // uniform length and room; the largest length otherwise
+};
+constexpr int kSeqStacked = 1;
+__host__ __device__ __forceinline__ int side_len_src(int mode) { return (mode >> 1) & 3; }
+__host__ __device__ __forceinline__ int side_pos_src(int mode) { return (mode >> 3) & 3; }
+// Whether a sequence of this side can have fewer rows than its room (the
+// rows in between are written as masked rows).
+__host__ __device__ __forceinline__ bool side_may_pad(int mode) {
+  const int ls = side_len_src(mode), ps = side_pos_src(mode);
+  if (!(mode & kSeqStacked) || ps == 0) return ls != 0;
+  return ps == 1 && ls != 1;
+}
+
+// Rows of sequence b on one side: start row r0 (stacked tensors; 0 for a
+// padded side, whose sequences start at b * stride[0]), length n, and room
+// (rows the sequence owns; -1 when not known).  Lengths are clamped to
+// [0, room], or to [0, S] when the room is not known.
+struct SideRows {
+  long long r0;
+  int n, room;
+};
+template <class SA>
+__device__ __forceinline__ SideRows side_rows(const SA& s, int b) {
+  const int ls = side_len_src(s.mode), ps = side_pos_src(s.mode);
+  SideRows r{0, s.S, s.S};
+  if (s.mode & kSeqStacked) {
+    if (ps == 0) {
+      r.r0 = (long long)b * s.S;
+    } else if (ps == 1) {
+      r.r0 = s.cu[b];
+      r.room = s.cu[b + 1] - s.cu[b];
+    } else {
+      r.r0 = s.start[b];
+      r.room = -1;
+    }
+  }
+  const int cap = r.room >= 0 ? r.room : s.S;
+  int n = s.S;
+  if (ls == 1) n = s.cu[b + 1] - s.cu[b];
+  if (ls == 2) n = s.len[b];
+  r.n = max(0, min(cap, n));
+  return r;
+}
+
 struct ProblemArgs {
-  const int* cu_q;   // packed layout only
-  const int* cu_k;
-  int varlen;
+  SideArgs qs, ks;
+  int ragged;        // sequences may differ in length: blocks run (sequence, head) fastest
   int B, H;
-  int Sq, Sk;        // dense: exact lengths; packed: maxima
+  int Sq, Sk;        // the sides' uniform lengths / rooms, else the largest lengths
   int wl, wr, diag;
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   long long lse_sb, lse_sh;  // workspace (Delta, LSE log2 e): base + b*lse_sb + h*lse_sh + row
   long long olse_sb, olse_sh, olse_ss;  // the caller's LSE: + b*sb + h*sh + row*ss
-  long long total_q;         // packed layout: rows of Q
-  const int* used_q;         // optional: rows of sequence b in use (seqused_q)
-  const int* used_k;
+  long long total_q;         // stacked Q side: rows of Q
 };
 
-// Rows of sequence b: Q rows q0 .. q0+sq-1 and K rows k0 .. k0+sk-1 (packed:
-// its cu_seqlens range; dense: all rows), cut to the used rows when the
-// caller gives seqused arrays.  Every kernel computes on these rows only.
-// (A template so that P may also sit in the kernel-argument segment.)
+// Rows of sequence b: Q rows q0 .. q0+sq-1 and K rows k0 .. k0+sk-1 (start
+// rows in stacked tensors, 0 for padded sides) as the sides' modes resolve
+// them.  Every kernel computes on these rows only.  (A template so that P
+// may also sit in the kernel-argument segment.)
 template <class PA>
 __device__ __forceinline__ void seq_rows(PA& P, int b, long long& q0, int& sq, long long& k0, int& sk) {
-  q0 = 0;
-  k0 = 0;
-  sq = P.Sq;
-  sk = P.Sk;
-  if (P.varlen) {
-    q0 = P.cu_q[b];
-    sq = P.cu_q[b + 1] - (int)q0;
-    k0 = P.cu_k[b];
-    sk = P.cu_k[b + 1] - (int)k0;
-  }
-  if (P.used_q) sq = max(0, min(sq, P.used_q[b]));
-  if (P.used_k) sk = max(0, min(sk, P.used_k[b]));
+  const SideRows q = side_rows(P.qs, b), k = side_rows(P.ks, b);
+  q0 = q.r0;
+  sq = q.n;
+  k0 = k.r0;
+  sk = k.n;
 }
 
 struct FwdArgs {
@@ -131,9 +173,10 @@ hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, const Enqueue& 
 hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, const Record& ex);
 hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, const Enqueue& ex);
 hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, const Record& ex);
-// Rows past the used rows of every sequence (seqused_q for side 0, seqused_k
-// for side 1): zeros in t0 and t1 (null pointers skipped) and, when lse is
-// given, LSE = +inf.  Rows are row_bytes long (a multiple of 16).
+// Rows of each sequence's room past its length (side 0: Q, side 1: K): zeros
+// in t0 and t1 (null pointers skipped) and, when lse is given, LSE = +inf.
+// Rows are row_bytes long (a multiple of 16).  Launches nothing for a side
+// whose lengths always fill their rooms.
 template <class Ex>
 hipError_t launch_pad_rows(const ProblemArgs& p, Operand t0, Operand t1, float* lse, int side, int row_bytes,
                            int esz, const Ex& ex);

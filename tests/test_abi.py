@@ -44,10 +44,12 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "attn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(attn_fwd_params), sizeof(attn_bwd_params),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(attn_fwd_params), sizeof(attn_bwd_params),
          offsetof(attn_fwd_params, total_q), offsetof(attn_fwd_params, q),
          offsetof(attn_fwd_params, o_stride), offsetof(attn_bwd_params, dout),
-         offsetof(attn_bwd_params, workspace), offsetof(attn_bwd_params, workspace_bytes));
+         offsetof(attn_bwd_params, workspace), offsetof(attn_bwd_params, workspace_bytes),
+         offsetof(attn_fwd_params, varlen), offsetof(attn_fwd_params, seqstart_q),
+         offsetof(attn_fwd_params, seqstart_k));
   return 0;
 }
 """)
@@ -57,7 +59,8 @@ int main(void) {
     got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
     want = [ctypes.sizeof(bd.FwdParams), ctypes.sizeof(bd.BwdParams),
             bd.FwdParams.total_q.offset, bd.FwdParams.q.offset, bd.FwdParams.o_stride.offset,
-            bd.BwdParams.dout.offset, bd.BwdParams.workspace.offset, bd.BwdParams.workspace_bytes.offset]
+            bd.BwdParams.dout.offset, bd.BwdParams.workspace.offset, bd.BwdParams.workspace_bytes.offset,
+            bd.FwdParams.varlen.offset, bd.FwdParams.seqstart_q.offset, bd.FwdParams.seqstart_k.offset]
     assert got == want
 
 
@@ -128,7 +131,8 @@ def test_valid_calls_pass():
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("version", 1, INVALID), ("version", 3, INVALID), ("flags", 1, INVALID), ("reserved0", 3, INVALID),
+    ("version", 1, INVALID), ("version", 4, INVALID), ("flags", 1, INVALID), ("reserved0", 3, INVALID),
+    ("reserved1", 1, INVALID), ("varlen", 1, INVALID), ("seqstart_q", BASE, INVALID),
     ("dtype", 7, INVALID), ("layout", 5, INVALID), ("diag", 2, INVALID),
     ("heads", 0, INVALID), ("head_dim", 0, INVALID), ("seqlen_q", -1, INVALID),
     ("seqlen_k", -5, INVALID), ("batch", -1, INVALID),
@@ -358,3 +362,151 @@ def test_noalloc_validation_and_limit():
     need = lib.attn_bwd_workspace_size(ctypes.byref(big))
     assert need > bd.NOALLOC_SCRATCH_BYTES
     assert lib.attn_bwd_noalloc(ctypes.byref(big), None) == 2
+
+
+# ----------------------------------------------------------- version 2 structs
+
+class FwdParamsV2(ctypes.Structure):
+    """attn_fwd_params as version 2 laid it out (no per-side addressing)."""
+    _fields_ = [f for f in bd.FwdParams._fields_ if f[0] not in ("varlen", "reserved1", "seqstart_q", "seqstart_k")]
+
+
+class BwdParamsV2(ctypes.Structure):
+    _fields_ = [("fwd", FwdParamsV2)] + [f for f in bd.BwdParams._fields_ if f[0] != "fwd"]
+
+
+def to_v2(p, cls):
+    out = cls()
+    for name, _ in cls._fields_:
+        if name == "fwd":
+            out.fwd = to_v2(p.fwd, FwdParamsV2)
+        else:
+            setattr(out, name, getattr(p, name))
+    out_ver = out.fwd if cls is BwdParamsV2 else out
+    out_ver.version = 2
+    return out
+
+
+def test_version2_structs_are_translated():
+    """A version-2 struct (shorter, no addressing fields) is accepted and
+    validated like its version-3 equivalent; the library reads nothing past
+    its end."""
+    lib = bd.lib()
+    assert ctypes.sizeof(FwdParamsV2) == bd.FwdParams.varlen.offset
+    for f in (dense_params(), packed_params()):
+        v2 = to_v2(f, FwdParamsV2)
+        assert lib.attn_fwd_check(ctypes.cast(ctypes.byref(v2), ctypes.POINTER(bd.FwdParams))) == OK
+        b2 = to_v2(bwd_params(f), BwdParamsV2)
+        bp = ctypes.cast(ctypes.byref(b2), ctypes.POINTER(bd.BwdParams))
+        assert lib.attn_bwd_check(bp) == OK
+        assert lib.attn_bwd_workspace_size(bp) == lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f)))
+    # Version-2 errors stay errors.
+    bad = to_v2(dense_params(D=112), FwdParamsV2)
+    assert lib.attn_fwd_check(ctypes.cast(ctypes.byref(bad), ctypes.POINTER(bd.FwdParams))) == NOTSUP
+    b2 = to_v2(bwd_params(dense_params()), BwdParamsV2)
+    b2.dq = b2.fwd.q
+    assert lib.attn_bwd_check(ctypes.cast(ctypes.byref(b2), ctypes.POINTER(bd.BwdParams))) == INVALID
+
+
+# ------------------------------------------------------ per-side addressing
+
+def varlen_params(qmode, kmode, B=3, H=2, D=64, Sq=40, Sk=50, total_q=120, total_k=150):
+    """An ATTN_VARLEN call with the arrays each mode reads (fake addresses)."""
+    p = bd.FwdParams()
+    p.version = bd.PARAMS_VERSION
+    p.dtype, p.layout = bd.BF16, bd.VARLEN
+    p.varlen = qmode | (kmode << 8)
+    p.batch, p.heads, p.head_dim, p.seqlen_q, p.seqlen_k = B, H, D, Sq, Sk
+    p.window_left, p.window_right, p.diag, p.scale = INF, INF, bd.TOP_LEFT, 0.125
+    p.q, p.k, p.v, p.o, p.lse = addr(1), addr(2), addr(3), addr(4), addr(5)
+    for side, mode, S, T, base in (("q", qmode, Sq, total_q, 20), ("k", kmode, Sk, total_k, 30)):
+        stacked = mode & bd.SEQ_STACKED
+        if stacked:
+            setattr(p, "total_" + side, T)
+        ls, ps = (mode >> 1) & 3, (mode >> 3) & 3
+        if ls == 1 or ps == 1:
+            setattr(p, "cu_seqlens_" + side, addr(base))
+        if ls == 2:
+            setattr(p, "seqused_" + side, addr(base + 1))
+        if ps == 2:
+            setattr(p, "seqstart_" + side, addr(base + 2))
+        for name in ((side + "_stride",) + (("o_stride",) if side == "q" else ("v_stride",))):
+            setattr(p, name, bd._I64x3(0, D, H * D) if stacked else bd._I64x3(H * S * D, S * D, D))
+    return p
+
+
+ST, LU, LC, LA, PU, PC, PA = (bd.SEQ_STACKED, bd.SEQ_LEN_UNIFORM, bd.SEQ_LEN_CUMSUM, bd.SEQ_LEN_ARRAY,
+                              bd.SEQ_POS_UNIFORM, bd.SEQ_POS_CUMSUM, bd.SEQ_POS_ARRAY)
+GOOD_MODES = [LU, LA, LC, ST | LC | PC, ST | LA | PC, ST | LU | PU, ST | LA | PU, ST | LA | PA, ST | LC | PA,
+              ST | LU | PA, ST | LU | PC, ST | LC | PU]
+
+
+@pytest.mark.parametrize("qmode", GOOD_MODES)
+@pytest.mark.parametrize("kmode", [LU, ST | LC | PC, ST | LA | PA])
+def test_varlen_modes_validate(qmode, kmode):
+    """Every combination of storage, length and start sources validates when
+    exactly the arrays it reads are given, forward and backward."""
+    p = varlen_params(qmode, kmode)
+    assert fcheck(p) == OK
+    assert bcheck(bwd_params(p)) == OK
+    # The LSE and the workspace follow the Q side.
+    n = 2 * p.total_q if qmode & ST else 3 * 2 * p.seqlen_q
+    ws = bd.lib().attn_bwd_workspace_size(ctypes.byref(bwd_params(p)))
+    assert ws == 2 * ((n * 4 + 255) // 256 * 256)
+
+
+@pytest.mark.parametrize("mode", [PC, PA, PC | LC, 6, 3 << 3, 0x20, 0x80])
+def test_varlen_bad_modes(mode):
+    """Padded sides take no start source; length / start value 3 and the
+    three reserved bits are invalid."""
+    assert fcheck(varlen_params(mode, LU)) == INVALID
+    assert fcheck(varlen_params(LU, mode)) == INVALID
+
+
+def test_varlen_arrays_match_modes():
+    """An array the mode does not read, or a missing one, is invalid; so are
+    bits above the two mode bytes, the [T, H] LSE for a padded Q side, and no
+    sequences with a stacked side."""
+    p = varlen_params(ST | LA | PA, LU)
+    p.seqstart_q = None
+    assert fcheck(p) == INVALID
+    p = varlen_params(ST | LA | PA, LU)
+    p.cu_seqlens_q = addr(40)
+    assert fcheck(p) == INVALID
+    p = varlen_params(LU, ST | LC | PC)
+    p.seqused_k = addr(41)
+    assert fcheck(p) == INVALID
+    p = varlen_params(LU, ST | LC | PC)
+    p.cu_seqlens_k = None
+    assert fcheck(p) == INVALID
+    p = varlen_params(LU, LU)
+    p.varlen |= 1 << 16
+    assert fcheck(p) == INVALID
+    p = varlen_params(LU, ST | LC | PC)
+    p.flags = bd.FLAG_LSE_TH
+    assert fcheck(p) == INVALID
+    p = varlen_params(ST | LC | PC, LU)
+    p.flags = bd.FLAG_LSE_TH
+    assert fcheck(p) == OK
+    p = varlen_params(ST | LC | PC, LU, B=0)
+    assert fcheck(p) == INVALID
+    p = varlen_params(LU, LU, B=0)
+    assert fcheck(p) == OK
+    # BHSD / THD take no addressing fields.
+    p = dense_params()
+    p.seqstart_k = addr(9)
+    assert fcheck(p) == INVALID
+
+
+def test_varlen_mixed_extents():
+    """Extents follow each side's storage: a padded Q tensor and a stacked K
+    tensor that would overlap only under the other reading validate, and a
+    stacked output that reaches into a padded input does not."""
+    p = varlen_params(LU, ST | LC | PC, B=2, H=1, D=64, Sq=10, total_k=30)
+    # Q padded: 2 x 1 x 10 rows of 64 -> 2560 bytes; put K right after it.
+    p.q = BASE
+    p.k = BASE + 2 * 10 * 64 * 2
+    p.q_stride = bd._I64x3(10 * 64, 10 * 64, 64)
+    assert fcheck(p) == OK
+    p.o = BASE + 2 * 10 * 64 * 2 + 29 * 64 * 2  # O starts inside K's last row
+    assert fcheck(p) == INVALID
