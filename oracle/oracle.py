@@ -61,6 +61,14 @@ class _Problem(ctypes.Structure):
         ("window_right", ctypes.c_int),
         ("diag", ctypes.c_int),
         ("scale", ctypes.c_double),
+        ("bias", ctypes.c_void_p),
+        ("bias_stride", ctypes.c_int64 * 3),
+        ("alibi_slopes", ctypes.POINTER(ctypes.c_double)),
+        ("dropout_p", ctypes.c_double),
+        ("philox_seed", ctypes.c_uint64),
+        ("philox_offset", ctypes.c_uint64),
+        ("max_seqlen_q", ctypes.c_int),
+        ("max_seqlen_k", ctypes.c_int),
     ]
 
 
@@ -81,13 +89,22 @@ def _load():
         lib.oracle_decode_bf16.restype = ctypes.c_double
         lib.oracle_fwd.argtypes = [pp, vp, vp, vp, dp, dp]
         lib.oracle_bwd.argtypes = [pp, vp, vp, vp, vp, dp, dp, dp, dp, dp]
+        lib.oracle_bwd_dbias.argtypes = [pp, vp, vp, vp, vp, dp, dp, dp, dp, dp, dp]
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        lib.oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_dropout_keep.argtypes = [pp, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
+        lib.oracle_dropout_keep.restype = ctypes.c_int
+        lib.oracle_dropout_mask.argtypes = [pp, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.POINTER(ctypes.c_uint8)]
+        lib.oracle_dropout_mask.restype = None
         lib.oracle_fwd_rows.argtypes = [pp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ip, dp, dp]
         lib.oracle_bwd_dq_rows.argtypes = [pp, vp, vp, vp, vp, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ip, dp]
         lib.oracle_bwd_dkdv_cols.argtypes = [pp, vp, vp, vp, vp, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_int, ip, dp, dp]
-        for f in ("oracle_fwd", "oracle_bwd", "oracle_fwd_rows",
+        for f in ("oracle_fwd", "oracle_bwd", "oracle_bwd_dbias", "oracle_fwd_rows",
                   "oracle_bwd_dq_rows", "oracle_bwd_dkdv_cols"):
             getattr(lib, f).restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -104,9 +121,18 @@ def _diag_code(diag) -> int:
 
 
 class _Call:
-    """Keeps the marshalled inputs alive for the duration of one C call."""
+    """Keeps the marshalled inputs alive for the duration of one C call.
 
-    def __init__(self, q, k, v, dout, window, diag, scale, cu_seqlens_q, cu_seqlens_k):
+    Optional features (keyword arguments of every entry below): ``bias`` (a
+    CPU tensor in the inputs' dtype, indexed [b, h, i, j] with local
+    indices, broadcast strides allowed, unit stride on j), ``alibi_slopes``
+    (one per head), ``dropout_p`` with ``philox_seed`` / ``philox_offset``,
+    and ``max_seqlen_q`` / ``max_seqlen_k`` (the row length of the dropout
+    counters and of dBias; default the largest lengths)."""
+
+    def __init__(self, q, k, v, dout, window, diag, scale, cu_seqlens_q, cu_seqlens_k, bias=None,
+                 alibi_slopes=None, dropout_p=0.0, philox_seed=0, philox_offset=0, max_seqlen_q=None,
+                 max_seqlen_k=None):
         tensors = [q, k, v] + ([dout] if dout is not None else [])
         dt = q.dtype
         if dt not in _DTYPE_CODE or any(t.dtype != dt for t in tensors):
@@ -141,6 +167,31 @@ class _Call:
             p.batch, p.heads, p.seqlen_q, p.head_dim = q.shape
             p.seqlen_k = k.shape[2]
             self.lse_shape = (p.batch, p.heads, p.seqlen_q)
+        if bias is not None:
+            if bias.dtype != dt or bias.device.type != "cpu" or bias.dim() != 4:
+                raise TypeError("bias is a 4-d CPU tensor in the inputs' dtype")
+            if bias.stride(-1) != 1:
+                bias = bias.contiguous()
+            self.bias = bias
+            p.bias = ctypes.c_void_p(bias.data_ptr())
+            for t in range(3):
+                p.bias_stride[t] = bias.stride(t) if bias.shape[t] > 1 else 0
+        if alibi_slopes is not None:
+            self.slopes = np.ascontiguousarray(np.asarray(alibi_slopes, dtype=np.float64))
+            if self.slopes.shape != (p.heads,):
+                raise ValueError("one ALiBi slope per head")
+            p.alibi_slopes = self.slopes.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+        p.dropout_p = float(dropout_p)
+        p.philox_seed = int(philox_seed) & (2**64 - 1)
+        p.philox_offset = int(philox_offset) & (2**64 - 1)
+        if packed:
+            lq = np.diff(self.cuq) if len(self.cuq) > 1 else np.zeros(1, np.int32)
+            lk = np.diff(self.cuk) if len(self.cuk) > 1 else np.zeros(1, np.int32)
+            p.max_seqlen_q = int(lq.max()) if max_seqlen_q is None else int(max_seqlen_q)
+            p.max_seqlen_k = int(lk.max()) if max_seqlen_k is None else int(max_seqlen_k)
+        else:
+            p.max_seqlen_q = p.seqlen_q if max_seqlen_q is None else int(max_seqlen_q)
+            p.max_seqlen_k = p.seqlen_k if max_seqlen_k is None else int(max_seqlen_k)
         self.p = p
         self.D = p.head_dim
 
@@ -157,9 +208,9 @@ def _iptr(a):
 
 
 def fwd(q, k, v, *, scale, window=(WINDOW_INF, WINDOW_INF), diag="top_left",
-        cu_seqlens_q=None, cu_seqlens_k=None):
+        cu_seqlens_q=None, cu_seqlens_k=None, **feat):
     """O and LSE of the whole problem (float64)."""
-    c = _Call(q, k, v, None, window, diag, scale, cu_seqlens_q, cu_seqlens_k)
+    c = _Call(q, k, v, None, window, diag, scale, cu_seqlens_q, cu_seqlens_k, **feat)
     o = np.zeros(tuple(q.shape), dtype=np.float64)
     lse = np.zeros(c.lse_shape, dtype=np.float64)
     rc = _load().oracle_fwd(ctypes.byref(c.p), c.ptr(0), c.ptr(1), c.ptr(2), _dptr(o), _dptr(lse))
@@ -169,25 +220,30 @@ def fwd(q, k, v, *, scale, window=(WINDOW_INF, WINDOW_INF), diag="top_left",
 
 
 def bwd(q, k, v, dout, *, scale, window=(WINDOW_INF, WINDOW_INF), diag="top_left",
-        cu_seqlens_q=None, cu_seqlens_k=None):
-    """(O, LSE, dQ, dK, dV) of the whole problem (float64)."""
-    c = _Call(q, k, v, dout, window, diag, scale, cu_seqlens_q, cu_seqlens_k)
+        cu_seqlens_q=None, cu_seqlens_k=None, want_dbias=False, **feat):
+    """(O, LSE, dQ, dK, dV) of the whole problem (float64); with
+    ``want_dbias`` also dBias = d loss / d logits, [B, H, max_seqlen_q,
+    max_seqlen_k] (0 where the sequence has no pair)."""
+    c = _Call(q, k, v, dout, window, diag, scale, cu_seqlens_q, cu_seqlens_k, **feat)
     o = np.zeros(tuple(q.shape), dtype=np.float64)
     lse = np.zeros(c.lse_shape, dtype=np.float64)
     dq = np.zeros(tuple(q.shape), dtype=np.float64)
     dk = np.zeros(tuple(k.shape), dtype=np.float64)
     dv = np.zeros(tuple(v.shape), dtype=np.float64)
-    rc = _load().oracle_bwd(ctypes.byref(c.p), c.ptr(0), c.ptr(1), c.ptr(2), c.ptr(3),
-                            _dptr(o), _dptr(lse), _dptr(dq), _dptr(dk), _dptr(dv))
+    db = np.zeros((c.p.batch, c.p.heads, c.p.max_seqlen_q, c.p.max_seqlen_k), dtype=np.float64) \
+        if want_dbias else None
+    rc = _load().oracle_bwd_dbias(ctypes.byref(c.p), c.ptr(0), c.ptr(1), c.ptr(2), c.ptr(3),
+                                  _dptr(o), _dptr(lse), _dptr(dq), _dptr(dk), _dptr(dv),
+                                  _dptr(db) if db is not None else None)
     if rc:
         raise ValueError("oracle_bwd rejected the problem")
-    return o, lse, dq, dk, dv
+    return (o, lse, dq, dk, dv, db) if want_dbias else (o, lse, dq, dk, dv)
 
 
 def fwd_rows(q, k, v, b, h, rows, *, scale, window=(WINDOW_INF, WINDOW_INF),
-             diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None):
+             diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None, **feat):
     """O rows [n, D] and LSE [n] for sequence-local query rows of (b, h)."""
-    c = _Call(q, k, v, None, window, diag, scale, cu_seqlens_q, cu_seqlens_k)
+    c = _Call(q, k, v, None, window, diag, scale, cu_seqlens_q, cu_seqlens_k, **feat)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
     o = np.zeros((len(rows), c.D), dtype=np.float64)
     lse = np.zeros(len(rows), dtype=np.float64)
@@ -199,9 +255,9 @@ def fwd_rows(q, k, v, b, h, rows, *, scale, window=(WINDOW_INF, WINDOW_INF),
 
 
 def bwd_dq_rows(q, k, v, dout, b, h, rows, *, scale, window=(WINDOW_INF, WINDOW_INF),
-                diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None):
+                diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None, **feat):
     """dQ rows [n, D] for sequence-local query rows of (b, h)."""
-    c = _Call(q, k, v, dout, window, diag, scale, cu_seqlens_q, cu_seqlens_k)
+    c = _Call(q, k, v, dout, window, diag, scale, cu_seqlens_q, cu_seqlens_k, **feat)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
     dq = np.zeros((len(rows), c.D), dtype=np.float64)
     rc = _load().oracle_bwd_dq_rows(ctypes.byref(c.p), c.ptr(0), c.ptr(1), c.ptr(2), c.ptr(3),
@@ -212,9 +268,9 @@ def bwd_dq_rows(q, k, v, dout, b, h, rows, *, scale, window=(WINDOW_INF, WINDOW_
 
 
 def bwd_dkdv_cols(q, k, v, dout, b, h, cols, *, scale, window=(WINDOW_INF, WINDOW_INF),
-                  diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None):
+                  diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None, **feat):
     """dK and dV rows [n, D] for sequence-local key rows of (b, h)."""
-    c = _Call(q, k, v, dout, window, diag, scale, cu_seqlens_q, cu_seqlens_k)
+    c = _Call(q, k, v, dout, window, diag, scale, cu_seqlens_q, cu_seqlens_k, **feat)
     cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int32))
     dk = np.zeros((len(cols), c.D), dtype=np.float64)
     dv = np.zeros((len(cols), c.D), dtype=np.float64)
@@ -251,3 +307,29 @@ def decode_bf16(bits: int) -> float:
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def philox4x32_10(ctr, key):
+    """The four 32-bit output words of Philox4x32-10 at counter ctr[4] under
+    key key[2]."""
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+    k = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    out = (ctypes.c_uint32 * 4)()
+    _load().oracle_philox4x32_10(c, k, out)
+    return [int(x) for x in out]
+
+
+def dropout_keep(q, k, v, b, h, i, j, *, cu_seqlens_q=None, cu_seqlens_k=None, **feat):
+    """1 when the dropout of the problem keeps pair (i, j) of (b, h)."""
+    c = _Call(q, k, v, None, (WINDOW_INF, WINDOW_INF), "top_left", 1.0, cu_seqlens_q, cu_seqlens_k, **feat)
+    return int(_load().oracle_dropout_keep(ctypes.byref(c.p), int(b), int(h), int(i), int(j)))
+
+
+def dropout_mask(q, k, v, b, h, nq, nk, *, cu_seqlens_q=None, cu_seqlens_k=None, **feat):
+    """bool [nq, nk]: the keep decisions of rows [0, nq) and keys [0, nk) of
+    (b, h) for the problem's dropout."""
+    c = _Call(q, k, v, None, (WINDOW_INF, WINDOW_INF), "top_left", 1.0, cu_seqlens_q, cu_seqlens_k, **feat)
+    out = np.zeros((int(nq), int(nk)), dtype=np.uint8)
+    _load().oracle_dropout_mask(ctypes.byref(c.p), int(b), int(h), int(nq), int(nk),
+                                out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    return out.astype(bool)

@@ -65,6 +65,81 @@ static double decode_at(int dtype, const void *base, int64_t idx) {
   return dtype == ORACLE_F16 ? oracle_decode_f16(b) : oracle_decode_bf16(b);
 }
 
+/* ------------------------------------------------------------- Philox */
+
+/*
+ * Philox4x32-10 as published (Salmon et al., SC 2011): ten rounds of
+ *   (hi0, lo0) = M0 * c0, (hi1, lo1) = M1 * c2   (32 x 32 -> 64-bit products)
+ *   c = (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0)
+ * with the key bumped by the Weyl constants (W0, W1) before every round but
+ * the first.
+ */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t p0 = (uint64_t)M0 * c[0], p1 = (uint64_t)M1 * c[2];
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+  for (int t = 0; t < 4; ++t) out[t] = c[t];
+}
+
+/* Largest sequence length of one side (the counters' and bias rows'
+ * stride), from the fields or, when they are 0, from the problem. */
+static int64_t max_len(const oracle_problem *p, int q) {
+  int64_t m = q ? p->max_seqlen_q : p->max_seqlen_k;
+  if (m > 0) return m;
+  if (p->layout == ORACLE_DENSE) return q ? p->seqlen_q : p->seqlen_k;
+  const int32_t *cu = q ? p->cu_seqlens_q : p->cu_seqlens_k;
+  m = 0;
+  for (int b = 0; b < p->batch; ++b)
+    if (cu[b + 1] - cu[b] > m) m = cu[b + 1] - cu[b];
+  return m;
+}
+
+/* Threshold of the keep decision: floor(p * 2^32), in [0, 2^32). */
+static uint32_t dropout_threshold(double pdrop) {
+  double t = floor(pdrop * 4294967296.0);
+  if (t < 0.0) t = 0.0;
+  if (t > 4294967295.0) t = 4294967295.0;
+  return (uint32_t)t;
+}
+
+int oracle_dropout_keep(const oracle_problem *p, int b, int h, int64_t i, int64_t j) {
+  if (!(p->dropout_p > 0.0)) return 1;
+  const int64_t sqm = max_len(p, 1), skm = max_len(p, 0);
+  const uint64_t groups = (uint64_t)((skm + 3) / 4);
+  const uint64_t row = ((uint64_t)b * (uint64_t)p->heads + (uint64_t)h) * (uint64_t)sqm + (uint64_t)i;
+  const uint64_t n = p->philox_offset + row * groups + (uint64_t)(j / 4);
+  const uint32_t ctr[4] = {(uint32_t)n, (uint32_t)(n >> 32), 0u, 0u};
+  const uint32_t key[2] = {(uint32_t)p->philox_seed, (uint32_t)(p->philox_seed >> 32)};
+  uint32_t out[4];
+  oracle_philox4x32_10(ctr, key, out);
+  return out[j % 4] >= dropout_threshold(p->dropout_p);
+}
+
+void oracle_dropout_mask(const oracle_problem *p, int b, int h, int64_t nq, int64_t nk, uint8_t *keep) {
+  for (int64_t i = 0; i < nq; ++i)
+    for (int64_t j = 0; j < nk; ++j) keep[i * nk + j] = (uint8_t)oracle_dropout_keep(p, b, h, i, j);
+}
+
+/* Multiplier of P_ij after dropout: keep / (1 - p). */
+static double dropout_scale(const oracle_problem *p, int b, int h, int64_t i, int64_t j) {
+  if (!(p->dropout_p > 0.0)) return 1.0;
+  return oracle_dropout_keep(p, b, h, i, j) ? 1.0 / (1.0 - p->dropout_p) : 0.0;
+}
+
 /* -------------------------------------------------------------- visibility */
 
 /*
@@ -102,6 +177,8 @@ static int check_problem(const oracle_problem *p) {
   if (!p || p->batch < 0 || p->heads <= 0 || p->head_dim <= 0) return -1;
   if (p->dtype < ORACLE_F32 || p->dtype > ORACLE_BF16) return -1;
   if (p->diag != ORACLE_TOP_LEFT && p->diag != ORACLE_BOTTOM_RIGHT) return -1;
+  if (!(p->dropout_p >= 0.0 && p->dropout_p < 1.0)) return -1;
+  if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0) return -1;
   if (p->layout == ORACLE_DENSE) {
     if (p->seqlen_q < 0 || p->seqlen_k < 0) return -1;
     return 0;
@@ -109,10 +186,14 @@ static int check_problem(const oracle_problem *p) {
   if (p->layout != ORACLE_PACKED) return -1;
   if (!p->cu_seqlens_q || !p->cu_seqlens_k) return -1;
   if (p->cu_seqlens_q[0] != 0 || p->cu_seqlens_k[0] != 0) return -1;
-  for (int b = 0; b < p->batch; ++b)
+  for (int b = 0; b < p->batch; ++b) {
     if (p->cu_seqlens_q[b + 1] < p->cu_seqlens_q[b] ||
         p->cu_seqlens_k[b + 1] < p->cu_seqlens_k[b])
       return -1;
+    if ((p->max_seqlen_q && p->cu_seqlens_q[b + 1] - p->cu_seqlens_q[b] > p->max_seqlen_q) ||
+        (p->max_seqlen_k && p->cu_seqlens_k[b + 1] - p->cu_seqlens_k[b] > p->max_seqlen_k))
+      return -1;
+  }
   return 0;
 }
 
@@ -160,76 +241,91 @@ static double dot(const double *a, const double *b, int n) {
   return s;
 }
 
+/* ------------------------------------------------------------ logits */
+
+typedef struct {
+  seq_span sp;
+  int b, h;
+  double *Q, *K, *V, *dO; /* decoded slice */
+} slice;
+
+/* Logit of the visible pair (i, j) of a slice: scale q_i.k_j, plus the
+ * bias entry (decoded from its stored encoding) and the ALiBi term when the
+ * problem has them. */
+static double logit(const oracle_problem *p, const slice *sl, int64_t i, int64_t j) {
+  int D = p->head_dim;
+  double x = p->scale * dot(sl->Q + i * D, sl->K + j * D, D);
+  if (p->bias)
+    x += decode_at(p->dtype, p->bias,
+                   sl->b * p->bias_stride[0] + sl->h * p->bias_stride[1] + i * p->bias_stride[2] + j);
+  if (p->alibi_slopes) {
+    const int64_t shift = sl->sp.sk - sl->sp.sq;
+    x -= p->alibi_slopes[sl->h] * fabs((double)(i + shift - j));
+  }
+  return x;
+}
+
+static int visible_in(const oracle_problem *p, const slice *sl, int64_t i, int64_t j) {
+  return oracle_visible(i, j, sl->sp.sq, sl->sp.sk, p->window_left, p->window_right, p->diag);
+}
+
 /* ------------------------------------------------------------ one row, fwd */
 
 /*
  * Row i of the forward pass, two passes over the visible keys:
- *   m = max_j S_ij, l = sum_j exp(S_ij - m), LSE = m + ln l (natural log),
- *   O_i = sum_j exp(S_ij - LSE) v_j.
+ *   m = max_j X_ij, l = sum_j exp(X_ij - m), LSE = m + ln l (natural log),
+ *   O_i = sum_j exp(X_ij - LSE) M_ij v_j,
+ * X the logits above and M_ij the dropout multiplier (1 without dropout).
  * A row with no visible key gets O_i = 0 and LSE_i = +inf, the early-exit
  * convention of the AOTriton 0.15b and 0.14b release notes ("Kernel Bug
  * Fixes": the early-exit zero store and the +inf LSE of fully masked rows).
- * s must hold sk doubles.
+ * So does a row whose every visible logit is -inf (a bias of -inf masks
+ * like the window).  s must hold sk doubles.
  */
-static void row_forward(const oracle_problem *p, const double *Q,
-                        const double *K, const double *V, int64_t i,
-                        int64_t sq, int64_t sk, double *s, double *o_row,
+static void row_forward(const oracle_problem *p, const slice *sl, int64_t i, double *s, double *o_row,
                         double *lse_out) {
   int D = p->head_dim;
-  int any = 0;
+  int64_t sk = sl->sp.sk;
   double m = -INFINITY;
   for (int64_t j = 0; j < sk; ++j) {
-    if (!oracle_visible(i, j, sq, sk, p->window_left, p->window_right,
-                        p->diag))
-      continue;
-    s[j] = p->scale * dot(Q + i * D, K + j * D, D);
+    if (!visible_in(p, sl, i, j)) continue;
+    s[j] = logit(p, sl, i, j);
     if (s[j] > m) m = s[j];
-    any = 1;
   }
   for (int d = 0; d < D; ++d) o_row[d] = 0.0;
-  if (!any) {
+  if (m == -INFINITY) {
     *lse_out = INFINITY;
     return;
   }
   double l = 0.0;
   for (int64_t j = 0; j < sk; ++j)
-    if (oracle_visible(i, j, sq, sk, p->window_left, p->window_right,
-                       p->diag))
-      l += exp(s[j] - m);
+    if (visible_in(p, sl, i, j)) l += exp(s[j] - m);
   double lse = m + log(l);
   for (int64_t j = 0; j < sk; ++j) {
-    if (!oracle_visible(i, j, sq, sk, p->window_left, p->window_right,
-                        p->diag))
-      continue;
-    double pij = exp(s[j] - lse);
-    for (int d = 0; d < D; ++d) o_row[d] += pij * V[j * D + d];
+    if (!visible_in(p, sl, i, j)) continue;
+    double w = exp(s[j] - lse) * dropout_scale(p, sl->b, sl->h, i, j);
+    for (int d = 0; d < D; ++d) o_row[d] += w * sl->V[j * D + d];
   }
   *lse_out = lse;
 }
 
-/* P_ij recomputed from the row's LSE; 0 when j is not visible to i or the
- * row is empty (LSE = +inf). */
-static double prob(const oracle_problem *p, const double *Q, const double *K,
-                   int64_t i, int64_t j, int64_t sq, int64_t sk, double lse) {
-  if (!oracle_visible(i, j, sq, sk, p->window_left, p->window_right, p->diag))
-    return 0.0;
+/* P_ij recomputed from the row's LSE (the softmax before dropout); 0 when j
+ * is not visible to i or the row is empty (LSE = +inf). */
+static double prob(const oracle_problem *p, const slice *sl, int64_t i, int64_t j, double lse) {
+  if (!visible_in(p, sl, i, j)) return 0.0;
   if (isinf(lse)) return 0.0;
-  int D = p->head_dim;
-  return exp(p->scale * dot(Q + i * D, K + j * D, D) - lse);
+  return exp(logit(p, sl, i, j) - lse);
 }
 
 /* ------------------------------------------------------------ slice helper */
-
-typedef struct {
-  seq_span sp;
-  double *Q, *K, *V, *dO; /* decoded slice */
-} slice;
 
 static int slice_load(const oracle_problem *p, const void *q, const void *k,
                       const void *v, const void *dout, int b, int h,
                       slice *sl) {
   int D = p->head_dim;
   sl->sp = span_of(p, b);
+  sl->b = b;
+  sl->h = h;
   int64_t sq = sl->sp.sq, sk = sl->sp.sk;
   sl->Q = (double *)malloc(sizeof(double) * (size_t)(sq * D + 1));
   sl->K = (double *)malloc(sizeof(double) * (size_t)(sk * D + 1));
@@ -263,8 +359,7 @@ static int slice_forward(const oracle_problem *p, const slice *sl,
 #pragma omp for schedule(dynamic, 8)
     for (int64_t i = 0; i < sq; ++i)
       if (s)
-        row_forward(p, sl->Q, sl->K, sl->V, i, sq, sk, s,
-                    O + i * p->head_dim, lse + i);
+        row_forward(p, sl, i, s, O + i * p->head_dim, lse + i);
     free(s);
   }
   return fail ? -1 : 0;
@@ -314,8 +409,7 @@ int oracle_fwd_rows(const oracle_problem *p, const void *q, const void *k,
 #pragma omp for schedule(dynamic, 1)
       for (int r = 0; r < nrows; ++r)
         if (s)
-          row_forward(p, sl.Q, sl.K, sl.V, rows[r], sq, sk, s,
-                      o_rows + (int64_t)r * p->head_dim, lse_rows + r);
+          row_forward(p, &sl, rows[r], s, o_rows + (int64_t)r * p->head_dim, lse_rows + r);
       if (!s) {
 #pragma omp atomic write
         bad = 1;
@@ -330,25 +424,32 @@ int oracle_fwd_rows(const oracle_problem *p, const void *q, const void *k,
 /* ------------------------------------------------------------ backward */
 
 /*
- * Explicit gradients of the scalar <dO, O>:
- *   dP_ij = <dO_i, v_j>,  Delta_i = <dO_i, O_i>  (the oracle's own fp64 O),
- *   dS_ij = P_ij (dP_ij - Delta_i),
+ * Explicit gradients of the scalar <dO, O>, with M_ij the dropout
+ * multiplier and P the softmax before dropout:
+ *   G_ij = <dO_i, v_j>,  Delta_i = <dO_i, O_i>  (the oracle's own fp64 O),
+ *   dS_ij = P_ij (M_ij G_ij - Delta_i)   (= d loss / d logit_ij),
  *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
- *   dV_j = sum_i P_ij dO_i.
+ *   dV_j = sum_i P_ij M_ij dO_i.
  * Delta is the row-sum term of the backward preprocess named in the AOTriton
- * 0.14b release notes ("bwd_preprocess").  Empty rows have P = 0 and so
+ * 0.14b release notes ("bwd_preprocess"); with dropout, sum_j P_ij M_ij G_ij
+ * equals <dO_i, O_i>, so it stays that term.  Empty rows have P = 0 and so
  * contribute nothing; keys seen by no row get dK = dV = 0.
  */
+static double dlogit(const oracle_problem *p, const slice *sl, int64_t i, int64_t j, double pij, double delta_i) {
+  int D = p->head_dim;
+  double g = dot(sl->dO + i * D, sl->V + j * D, D);
+  return pij * (dropout_scale(p, sl->b, sl->h, i, j) * g - delta_i);
+}
+
 static void row_dq(const oracle_problem *p, const slice *sl, int64_t i,
                    double lse_i, double delta_i, double *dq_row) {
   int D = p->head_dim;
-  int64_t sq = sl->sp.sq, sk = sl->sp.sk;
+  int64_t sk = sl->sp.sk;
   for (int d = 0; d < D; ++d) dq_row[d] = 0.0;
   for (int64_t j = 0; j < sk; ++j) {
-    double pij = prob(p, sl->Q, sl->K, i, j, sq, sk, lse_i);
+    double pij = prob(p, sl, i, j, lse_i);
     if (pij == 0.0) continue;
-    double dpij = dot(sl->dO + i * D, sl->V + j * D, D);
-    double ds = pij * (dpij - delta_i);
+    double ds = dlogit(p, sl, i, j, pij, delta_i);
     for (int d = 0; d < D; ++d) dq_row[d] += p->scale * ds * sl->K[j * D + d];
   }
 }
@@ -357,16 +458,16 @@ static void col_dkdv(const oracle_problem *p, const slice *sl, int64_t j,
                      const double *lse, const double *delta, double *dk_row,
                      double *dv_row) {
   int D = p->head_dim;
-  int64_t sq = sl->sp.sq, sk = sl->sp.sk;
+  int64_t sq = sl->sp.sq;
   for (int d = 0; d < D; ++d) dk_row[d] = dv_row[d] = 0.0;
   for (int64_t i = 0; i < sq; ++i) {
-    double pij = prob(p, sl->Q, sl->K, i, j, sq, sk, lse[i]);
+    double pij = prob(p, sl, i, j, lse[i]);
     if (pij == 0.0) continue;
-    double dpij = dot(sl->dO + i * D, sl->V + j * D, D);
-    double ds = pij * (dpij - delta[i]);
+    double ds = dlogit(p, sl, i, j, pij, delta[i]);
+    double pm = pij * dropout_scale(p, sl->b, sl->h, i, j);
     for (int d = 0; d < D; ++d) {
       dk_row[d] += p->scale * ds * sl->Q[i * D + d];
-      dv_row[d] += pij * sl->dO[i * D + d];
+      dv_row[d] += pm * sl->dO[i * D + d];
     }
   }
 }
@@ -384,8 +485,15 @@ static int slice_stats(const oracle_problem *p, const slice *sl, double *O,
 int oracle_bwd(const oracle_problem *p, const void *q, const void *k,
                const void *v, const void *dout, double *o, double *lse,
                double *dq, double *dk, double *dv) {
+  return oracle_bwd_dbias(p, q, k, v, dout, o, lse, dq, dk, dv, NULL);
+}
+
+int oracle_bwd_dbias(const oracle_problem *p, const void *q, const void *k,
+                     const void *v, const void *dout, double *o, double *lse,
+                     double *dq, double *dk, double *dv, double *dbias) {
   if (check_problem(p)) return -1;
   int D = p->head_dim;
+  const int64_t sqm = max_len(p, 1), skm = max_len(p, 0);
   for (int b = 0; b < p->batch; ++b)
     for (int h = 0; h < p->heads; ++h) {
       slice sl;
@@ -419,6 +527,15 @@ int oracle_bwd(const oracle_problem *p, const void *q, const void *k,
             dk[e] = dK[j * D + d];
             dv[e] = dV[j * D + d];
           }
+        if (dbias) {
+          double *row0 = dbias + ((int64_t)b * p->heads + h) * sqm * skm;
+#pragma omp parallel for schedule(dynamic, 8)
+          for (int64_t i = 0; i < sq; ++i)
+            for (int64_t j = 0; j < sk; ++j) {
+              double pij = prob(p, &sl, i, j, L[i]);
+              row0[i * skm + j] = pij == 0.0 ? 0.0 : dlogit(p, &sl, i, j, pij, De[i]);
+            }
+        }
       }
       free(O); free(L); free(De); free(dQ); free(dK); free(dV);
       slice_free(&sl);
@@ -449,7 +566,7 @@ int oracle_bwd_dq_rows(const oracle_problem *p, const void *q, const void *k,
         if (!s || !orow) continue;
         double lse_i;
         int64_t i = rows[r];
-        row_forward(p, sl.Q, sl.K, sl.V, i, sq, sk, s, orow, &lse_i);
+        row_forward(p, &sl, i, s, orow, &lse_i);
         double delta_i = dot(sl.dO + i * D, orow, D);
         row_dq(p, &sl, i, lse_i, delta_i, dq_rows + (int64_t)r * D);
       }

@@ -49,7 +49,45 @@ typedef struct {
   int window_right;
   int diag;          /* ORACLE_TOP_LEFT / ORACLE_BOTTOM_RIGHT */
   double scale;
+  /* Additive bias on the logits (NULL: none): logit_ij = scale q_i.k_j +
+   * bias[b*bias_stride[0] + h*bias_stride[1] + i*bias_stride[2] + j], local
+   * indices, stored in the inputs' encoding (dtype) and decoded exactly. */
+  const void *bias;
+  int64_t bias_stride[3];
+  /* ALiBi (NULL: none): logit_ij gains -alibi_slopes[h] * |i + sk - sq - j|
+   * with the sequence's own sq, sk (query i sits at key position
+   * i + sk - sq, the bottom-right alignment of a query block that ends
+   * where the keys end). */
+  const double *alibi_slopes;
+  /* Dropout (dropout_p = 0: none).  After the softmax, P_ij is multiplied by
+   * keep_ij / (1 - dropout_p), keep_ij from oracle_dropout_keep below. */
+  double dropout_p;
+  uint64_t philox_seed;
+  uint64_t philox_offset;
+  /* Row length of the dropout counters and of the bias / dBias arrays: the
+   * largest Sq / Sk (packed; the dense seqlen_q / seqlen_k otherwise). */
+  int max_seqlen_q;
+  int max_seqlen_k;
 } oracle_problem;
+
+/* Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel
+ * random numbers: as easy as 1, 2, 3", SC 2011): the four output words of
+ * counter ctr[4] under key key[2]; the generator the AOTriton 0.10b notes
+ * name for dropout ("Philox32x4"). */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+
+/* Dropout decision for (sequence b, head h, local row i, local key j):
+ * word j % 4 of Philox4x32-10 at counter (lo, hi 32 bits of
+ * philox_offset + ((b*heads + h)*max_seqlen_q + i)*ceil(max_seqlen_k/4) +
+ * j/4, 0, 0) and key (lo, hi 32 bits of philox_seed); the element is kept
+ * iff that word is >= floor(dropout_p * 2^32).  The four words of one
+ * counter serve four consecutive keys in generation order (the word order
+ * fix of the AOTriton 0.14b notes, "Minor Changes"). */
+int oracle_dropout_keep(const oracle_problem *p, int b, int h, int64_t i, int64_t j);
+
+/* The keep decisions of rows [0, nq) and keys [0, nk) of (b, h) into
+ * keep[nq][nk] (1 kept, 0 dropped). */
+void oracle_dropout_mask(const oracle_problem *p, int b, int h, int64_t nq, int64_t nk, uint8_t *keep);
 
 /* 1 if key j is visible to query i in a sequence of sq queries, sk keys. */
 int oracle_visible(int64_t i, int64_t j, int64_t sq, int64_t sk,
@@ -70,6 +108,13 @@ int oracle_fwd(const oracle_problem *p, const void *q, const void *k,
 int oracle_bwd(const oracle_problem *p, const void *q, const void *k,
                const void *v, const void *dout, double *o, double *lse,
                double *dq, double *dk, double *dv);
+
+/* The same, with the gradient of the logits dS_ij (= d loss / d bias_ij)
+ * into dbias [B][H][max_seqlen_q][max_seqlen_k] (fp64, 0 where no pair of
+ * the sequence sits); dbias may be NULL. */
+int oracle_bwd_dbias(const oracle_problem *p, const void *q, const void *k,
+                     const void *v, const void *dout, double *o, double *lse,
+                     double *dq, double *dk, double *dv, double *dbias);
 
 /* Forward for selected query rows of one (sequence b, head h): rows[] are
  * sequence-local indices; o_rows is [nrows][D], lse_rows [nrows]. */
