@@ -196,6 +196,36 @@ typedef struct {
                               int32[batch], start row of each sequence in
                               the stacked tensor; NULL otherwise */
   const int32_t *seqstart_k; /* the same for K */
+  /* Optional features (version 3; a NULL pointer / 0 disables each).  The
+   * logits become scale q_i.k_j + bias_ij + alibi_ij, and dropout scales the
+   * softmax after it; a call with any of them runs on kernels built for
+   * them (the plain kernels are unchanged).  Indices i, j are local to the
+   * sequence (i < its Q length, j < its K length). */
+  const void *bias;         /* additive bias in the dtype of q: element
+                              (b, h, i, j) at b*bias_stride[0] +
+                              h*bias_stride[1] + i*bias_stride[2] + j
+                              (strides may be 0 to broadcast); converted to
+                              fp32 before use (the AOTriton 0.14b notes,
+                              "Kernel Bug Fixes"); -inf masks the pair */
+  int64_t bias_stride[3];
+  const float *alibi_slopes; /* device fp32[heads]: ALiBi adds
+                              -slope_h * |i + sk - sq - j| with the
+                              sequence's lengths sq, sk (query i at key
+                              position i + sk - sq) */
+  float dropout_p;          /* 0 (none) <= p < 1: pair (i, j) is kept iff word
+                              j % 4 of Philox4x32-10 (the generator of the
+                              AOTriton 0.10b notes) at counter (lo, hi 32 bits
+                              of philox_offset + ((b*heads + h)*seqlen_q + i)
+                              * ceil(seqlen_k / 4) + j / 4, 0, 0) and key
+                              (lo, hi 32 bits of philox_seed) is >=
+                              floor(p * 2^32) -- one counter for four
+                              consecutive keys, words in generation order
+                              (0.14b "Minor Changes"); kept probabilities are
+                              scaled by 1 / (1 - p).  LSE is the softmax's,
+                              before dropout. */
+  int32_t reserved2;        /* must be 0 */
+  uint64_t philox_seed;
+  uint64_t philox_offset;
 } attn_fwd_params;
 
 typedef struct {
@@ -210,6 +240,13 @@ typedef struct {
   int64_t dv_stride[3];
   void *workspace;         /* device, caller-owned, 256-byte aligned */
   uint64_t workspace_bytes;/* >= attn_bwd_workspace_size(this) */
+  /* Version 3: optional output, fp32, the gradient of the loss with respect
+   * to the logits (= d loss / d bias_ij): element (b, h, i, j) at
+   * b*dbias_stride[0] + h*dbias_stride[1] + i*dbias_stride[2] + j, written
+   * for every i < the sequence's Q length and j < its K length (0 where the
+   * pair is masked), untouched elsewhere.  NULL: not computed. */
+  float *dbias;
+  int64_t dbias_stride[3];
 } attn_bwd_params;
 
 /* Forward: writes o and lse.  Enqueues on `stream` one forward kernel

@@ -55,6 +55,9 @@ class FwdParams(ctypes.Structure):
         ("seqused_q", ctypes.c_void_p), ("seqused_k", ctypes.c_void_p),
         ("varlen", ctypes.c_uint32), ("reserved1", ctypes.c_int32),
         ("seqstart_q", ctypes.c_void_p), ("seqstart_k", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p), ("bias_stride", _I64x3), ("alibi_slopes", ctypes.c_void_p),
+        ("dropout_p", ctypes.c_float), ("reserved2", ctypes.c_int32),
+        ("philox_seed", ctypes.c_uint64), ("philox_offset", ctypes.c_uint64),
     ]
 
 
@@ -65,6 +68,7 @@ class BwdParams(ctypes.Structure):
         ("dv", ctypes.c_void_p),
         ("do_stride", _I64x3), ("dq_stride", _I64x3), ("dk_stride", _I64x3), ("dv_stride", _I64x3),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
+        ("dbias", ctypes.c_void_p), ("dbias_stride", _I64x3),
     ]
 
 
@@ -185,7 +189,8 @@ def _side(t: torch.Tensor, mode: int, cu, max_seqlen, name: str):
 
 def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens_k,
                max_seqlen_q, max_seqlen_k, lse_layout="ht", seqused_q=None, seqused_k=None,
-               q_mode=None, k_mode=None, seqstart_q=None, seqstart_k=None, batch=None) -> FwdParams:
+               q_mode=None, k_mode=None, seqstart_q=None, seqstart_k=None, batch=None, bias=None,
+               alibi_slopes=None, dropout_p=0.0, philox_seed=0, philox_offset=0) -> FwdParams:
     """Fill an attn_fwd_params from tensors (no device work).  ``lse_layout``
     'th' (a stacked Q side only) stores LSE as [T, H] instead of [H, T].
     ``seqused_q`` / ``seqused_k`` (int32 [batch] on the device): sequence b
@@ -193,7 +198,11 @@ def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens
     masked.  ``q_mode`` / ``k_mode`` (SEQ_* bits) select the ATTN_VARLEN
     layout, each side addressed on its own: a stacked side is [T, H, D], a
     padded one [B, H, S, D]; ``seqstart_q`` / ``seqstart_k`` are the start
-    rows of SEQ_POS_ARRAY; ``batch`` is required when no array gives it."""
+    rows of SEQ_POS_ARRAY; ``batch`` is required when no array gives it.
+    Optional features: ``bias`` (inputs' dtype, indexable [B, H, seqlen_q,
+    seqlen_k] with sequence-local query / key indices; size-1 axes
+    broadcast; unit stride on the key axis), ``alibi_slopes`` (fp32 [H]),
+    ``dropout_p`` with ``philox_seed`` / ``philox_offset``."""
     p = FwdParams()
     p.version = PARAMS_VERSION
     if q.dtype not in _DTYPE:
@@ -246,7 +255,28 @@ def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens
         raise ValueError("inputs are [B, H, S, D] or [T, H, D]")
     p.seqused_q = _ptr(_seqused(seqused_q, p.batch, q.device))
     p.seqused_k = _ptr(_seqused(seqused_k, p.batch, q.device))
+    if bias is not None:
+        p.bias, p.bias_stride = _ptr(bias), _bias_strides(bias, q, "bias")
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.device != q.device or \
+                alibi_slopes.shape != (p.heads,) or alibi_slopes.stride(0) != 1:
+            raise ValueError("alibi_slopes: contiguous fp32 [heads] on the inputs' device")
+        p.alibi_slopes = _ptr(alibi_slopes)
+    p.dropout_p = float(dropout_p)
+    p.philox_seed = int(philox_seed) & (2**64 - 1)
+    p.philox_offset = int(philox_offset) & (2**64 - 1)
     return p
+
+
+def _bias_strides(t, q, name, dtype=None):
+    """[b, h, i] element strides of a 4-d bias-shaped tensor (0 on size-1
+    axes: broadcast)."""
+    if t.dim() != 4 or t.device != q.device or t.dtype != (q.dtype if dtype is None else dtype):
+        raise ValueError(f"{name}: a 4-d tensor [B, H, Sq, Sk] on the inputs' device, "
+                         f"dtype {q.dtype if dtype is None else dtype}")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: unit stride on the key axis")
+    return _I64x3(*[t.stride(i) if t.shape[i] > 1 else 0 for i in range(3)])
 
 
 def _max_len(cu: torch.Tensor) -> int:
@@ -278,7 +308,7 @@ def _stream(dev) -> int:
 def _problem(q, *, scale=None, window=(WINDOW_INF, WINDOW_INF), diag="top_left", cu_seqlens_q=None,
              cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, lse_layout="ht", seqused_q=None,
              seqused_k=None, q_mode=None, k_mode=None, seqstart_q=None, seqstart_k=None, batch=None,
-             read_back=True):
+             bias=None, alibi_slopes=None, dropout_p=0.0, philox_seed=0, philox_offset=0, read_back=True):
     """The keyword arguments of fwd_params for a call: default scale,
     cu_seqlens checked, and (packed [T, H, D] inputs without modes) the max
     lengths read back from cu_seqlens when not given and `read_back`."""
@@ -294,7 +324,9 @@ def _problem(q, *, scale=None, window=(WINDOW_INF, WINDOW_INF), diag="top_left",
     return dict(scale=scale, window=window, diag=diag, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
                 max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, lse_layout=lse_layout,
                 seqused_q=seqused_q, seqused_k=seqused_k, q_mode=q_mode, k_mode=k_mode,
-                seqstart_q=seqstart_q, seqstart_k=seqstart_k, batch=batch)
+                seqstart_q=seqstart_q, seqstart_k=seqstart_k, batch=batch, bias=bias,
+                alibi_slopes=alibi_slopes, dropout_p=dropout_p, philox_seed=philox_seed,
+                philox_offset=philox_offset)
 
 
 def lse_shape(q: torch.Tensor, lse_layout="ht", q_mode=None):
@@ -326,9 +358,13 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: Optional
     return o, lse
 
 
-def bwd_params(dout, q, k, v, o, lse, dq, dk, dv, workspace, **kw) -> BwdParams:
+def bwd_params(dout, q, k, v, o, lse, dq, dk, dv, workspace, dbias=None, **kw) -> BwdParams:
+    """Fill an attn_bwd_params (keywords as for fwd_params); ``dbias``: the
+    optional fp32 output d loss / d logits, [B, H, seqlen_q, seqlen_k]."""
     p = BwdParams()
     p.fwd = fwd_params(q, k, v, o, lse, **kw)
+    if dbias is not None:
+        p.dbias, p.dbias_stride = _ptr(dbias), _bias_strides(dbias, q, "dbias", torch.float32)
     p.dout, p.dq, p.dk, p.dv = _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv)
     p.do_stride, p.dq_stride = _strides(dout), _strides(dq)
     p.dk_stride, p.dv_stride = _strides(dk), _strides(dv)
@@ -345,7 +381,7 @@ def _bwd_outputs(q, k, v, dq, dk, dv):
     return dq, dk, dv
 
 
-def prepare_bwd(dout, q, k, v, o, lse, *, dq=None, dk=None, dv=None, workspace=None, **kw):
+def prepare_bwd(dout, q, k, v, o, lse, *, dq=None, dk=None, dv=None, workspace=None, dbias=None, **kw):
     """Allocate the outputs and workspace of a backward and fill its params
     once, for callers that launch it repeatedly or step by step (keywords as
     for attn_fwd).  Returns (params, (dq, dk, dv, workspace)); the tensors
@@ -354,7 +390,7 @@ def prepare_bwd(dout, q, k, v, o, lse, *, dq=None, dk=None, dv=None, workspace=N
     dev = q.device
     pk = _problem(q, **kw)
     dq, dk, dv = _bwd_outputs(q, k, v, dq, dk, dv)
-    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **pk)
+    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, dbias=dbias, **pk)
     if workspace is None:
         need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -394,7 +430,8 @@ def plan(name: str, params, stream: Optional[int] = None):
 
 
 def attn_bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-                     lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, **kw):
+                     lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, dbias=None,
+                     **kw):
     """attn_bwd_noalloc: the backward into caller-given dq, dk, dv, with its
     workspace in the library's per-device static array (nothing allocated;
     keywords as for attn_fwd, packed inputs with their max_seqlen given).
@@ -402,7 +439,7 @@ def attn_bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: to
     _check_inputs(q, k, v, o, dout)
     dev = q.device
     pk = _problem(q, read_back=False, **kw)
-    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, **pk)
+    p = bwd_params(dout, q, k, v, o, lse, dq, dk, dv, None, dbias=dbias, **pk)
     rc = lib().attn_bwd_noalloc(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
     if rc == 2:  # hipErrorOutOfMemory
         need = int(lib().attn_bwd_workspace_size(ctypes.byref(p)))
@@ -414,11 +451,15 @@ def attn_bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: to
 
 def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              lse: torch.Tensor, *, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, **kw):
+             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             dbias: Optional[torch.Tensor] = None, **kw):
     """Backward: returns (dQ, dK, dV) given the forward's O and LSE (in the
-    layout ``lse_layout`` names; keywords as for attn_fwd)."""
+    layout ``lse_layout`` names; keywords as for attn_fwd, with the same
+    bias / alibi / dropout arguments as the forward).  ``dbias`` (fp32,
+    [B, H, seqlen_q, seqlen_k]) receives d loss / d logits for every pair of
+    each sequence (0 where masked)."""
     p, (dq, dk, dv, workspace) = prepare_bwd(dout, q, k, v, o, lse, dq=dq, dk=dk, dv=dv, workspace=workspace,
-                                             **kw)
+                                             dbias=dbias, **kw)
     rc = lib().attn_bwd(ctypes.byref(p), ctypes.c_void_p(_stream(q.device)))
     if rc:
         raise AttnError("attn_bwd", rc)

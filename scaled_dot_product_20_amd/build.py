@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libsdpa20.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_api.cpp"]
-HEADERS = ["attn_device.hpp", "attn_launch.hpp"]
+HEADERS = ["attn_device.hpp", "attn_launch.hpp", "attn_feat.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [

@@ -6,6 +6,7 @@
 // address of the no-allocation backward's scratch array (below).
 #include "attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -170,6 +171,51 @@ bool tile_span_ok(const int64_t* stride, int64_t esz, int64_t d) {
   return rs <= ((int64_t)1 << 31) / 64 && (63 * rs + d) * esz < ((int64_t)1 << 31);
 }
 
+// ------------------------------------------------------ optional features
+
+bool feat_on(const attn_fwd_params* p) { return p->bias || p->alibi_slopes || p->dropout_p != 0.f; }
+
+// Bias / dbias element ranges: [batch, heads, seqlen_q, seqlen_k] with the
+// given strides (0 broadcasts) and unit stride on the last axis.
+Extent extent4(const void* ptr, const int64_t* stride, const attn_fwd_params* p, int64_t esz) {
+  const uintptr_t base = reinterpret_cast<uintptr_t>(ptr);
+  if (!ptr || p->batch == 0 || p->seqlen_q == 0 || p->seqlen_k == 0) return Extent{base, base};
+  int64_t below = 0, above = p->seqlen_k;
+  const int64_t n[3] = {p->batch, p->heads, p->seqlen_q};
+  for (int t = 0; t < 3; ++t)
+    if (n[t] > 1) (stride[t] < 0 ? below : above) += (n[t] - 1) * std::llabs(stride[t]);
+  return Extent{base - (uintptr_t)(below * esz), base + (uintptr_t)(above * esz)};
+}
+
+hipError_t check_feat(const attn_fwd_params* p) {
+  if (p->reserved2 != 0) return hipErrorInvalidValue;
+  if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f)) return hipErrorInvalidValue;  // also NaN
+  if (p->bias && (reinterpret_cast<uintptr_t>(p->bias) % (uintptr_t)elem_bytes(p->dtype)) != 0)
+    return hipErrorInvalidValue;
+  if (p->alibi_slopes && (reinterpret_cast<uintptr_t>(p->alibi_slopes) & 3u) != 0) return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+sdpa::FeatArgs feat_args(const attn_fwd_params* p) {
+  sdpa::FeatArgs f{};
+  f.bias = p->bias;
+  if (p->bias) {
+    f.bsb = p->bias_stride[0];
+    f.bsh = p->bias_stride[1];
+    f.bss = p->bias_stride[2];
+  }
+  f.alibi = p->alibi_slopes;
+  if (p->dropout_p > 0.f) {
+    const double t = std::floor((double)p->dropout_p * 4294967296.0);
+    f.drop_thresh = (unsigned)std::min(t, 4294967295.0);
+    f.drop_scale = (float)(1.0 / (1.0 - (double)p->dropout_p));
+    f.seed_lo = (unsigned)p->philox_seed;
+    f.seed_hi = (unsigned)(p->philox_seed >> 32);
+    f.offset = p->philox_offset;
+  }
+  return f;
+}
+
 hipError_t check_problem(const attn_fwd_params* p) {
   if (!p) return hipErrorInvalidValue;
   if (p->version != ATTN_PARAMS_VERSION || p->reserved0 != 0 || p->reserved1 != 0) return hipErrorInvalidValue;
@@ -196,6 +242,7 @@ hipError_t check_problem(const attn_fwd_params* p) {
   if (!strides_ok(p->q_stride, esz, qs.stacked()) || !strides_ok(p->k_stride, esz, ks.stacked()) ||
       !strides_ok(p->v_stride, esz, ks.stacked()) || !strides_ok(p->o_stride, esz, qs.stacked()))
     return hipErrorInvalidValue;
+  if (check_feat(p) != hipSuccess) return hipErrorInvalidValue;
   if (!head_dim_built(p->head_dim)) return hipErrorNotSupported;
   if (p->dtype != ATTN_FP32 &&
       (!tile_span_ok(p->q_stride, esz, p->head_dim) || !tile_span_ok(p->k_stride, esz, p->head_dim) ||
@@ -268,6 +315,11 @@ Operand operand(const void* ptr, const int64_t* stride, bool stacked) {
   return Operand{ptr, stacked ? 0 : stride[0], stride[1], stride[2]};
 }
 
+Extent alibi_extent(const attn_fwd_params* p) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p->alibi_slopes);
+  return Extent{lo, p->alibi_slopes ? lo + (uintptr_t)p->heads * 4 : lo};
+}
+
 hipError_t check_fwd(const attn_fwd_params* p) {
   hipError_t err = check_problem(p);
   if (err != hipSuccess) return err;
@@ -281,6 +333,9 @@ hipError_t check_fwd(const attn_fwd_params* p) {
   for (const Extent& in : ins)
     if (overlap(o, in) || overlap(l, in)) return hipErrorInvalidValue;
   if (overlap(o, l)) return hipErrorInvalidValue;
+  const Extent fin[2] = {extent4(p->bias, p->bias_stride, p, esz), alibi_extent(p)};
+  for (const Extent& in : fin)
+    if (overlap(o, in) || overlap(l, in)) return hipErrorInvalidValue;
   return hipSuccess;
 }
 
@@ -306,23 +361,27 @@ hipError_t check_bwd(const attn_bwd_params* p, bool ws) {
       !strides_ok(p->dk_stride, esz, ks.stacked()) || !strides_ok(p->dv_stride, esz, ks.stacked()))
     return hipErrorInvalidValue;
   if (f->dtype != ATTN_FP32 && !tile_span_ok(p->do_stride, esz, f->head_dim)) return hipErrorNotSupported;
+  if (p->dbias && (reinterpret_cast<uintptr_t>(p->dbias) & 3u) != 0) return hipErrorInvalidValue;
   const int64_t B = f->batch, H = f->heads, D = f->head_dim;
-  const Extent outs[4] = {
+  const Extent outs[5] = {
       extent_of(p->dq, p->dq_stride, B, H, qs, D, esz), extent_of(p->dk, p->dk_stride, B, H, ks, D, esz),
       extent_of(p->dv, p->dv_stride, B, H, ks, D, esz),
       ws ? Extent{reinterpret_cast<uintptr_t>(p->workspace),
                   reinterpret_cast<uintptr_t>(p->workspace) + (uintptr_t)delta_bytes(f)}
-         : Extent{0, 0}};
-  const Extent ins[6] = {extent_of(f->q, f->q_stride, B, H, qs, D, esz),
+         : Extent{0, 0},
+      extent4(p->dbias, p->dbias_stride, f, 4)};
+  const Extent ins[8] = {extent_of(f->q, f->q_stride, B, H, qs, D, esz),
                          extent_of(f->k, f->k_stride, B, H, ks, D, esz),
                          extent_of(f->v, f->v_stride, B, H, ks, D, esz),
                          extent_of(f->o, f->o_stride, B, H, qs, D, esz),
                          extent_of(p->dout, p->do_stride, B, H, qs, D, esz),
-                         lse_extent(f)};
-  for (int i = 0; i < 4; ++i) {
+                         lse_extent(f),
+                         extent4(f->bias, f->bias_stride, f, esz),
+                         alibi_extent(f)};
+  for (int i = 0; i < 5; ++i) {
     for (const Extent& in : ins)
       if (overlap(outs[i], in)) return hipErrorInvalidValue;
-    for (int j = i + 1; j < 4; ++j)
+    for (int j = i + 1; j < 5; ++j)
       if (overlap(outs[i], outs[j])) return hipErrorInvalidValue;
   }
   return hipSuccess;
@@ -337,6 +396,8 @@ sdpa::FwdArgs fwd_args(const attn_fwd_params* p) {
   a.v = operand(p->v, p->v_stride, kst);
   a.o = operand(p->o, p->o_stride, qst);
   a.lse = p->lse;
+  a.f = feat_args(p);
+  a.feat = feat_on(p);
   return a;
 }
 
@@ -358,6 +419,14 @@ sdpa::BwdArgs bwd_args(const attn_bwd_params* p, void* ws) {
   a.lse = f->lse;
   a.delta = static_cast<float*>(ws);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + stat_section_bytes(f));
+  a.f = feat_args(f);
+  a.f.dbias = p->dbias;
+  if (p->dbias) {
+    a.f.dsb = p->dbias_stride[0];
+    a.f.dsh = p->dbias_stride[1];
+    a.f.dss = p->dbias_stride[2];
+  }
+  a.feat = feat_on(f) || p->dbias != nullptr;
   return a;
 }
 

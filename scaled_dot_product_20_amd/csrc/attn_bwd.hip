@@ -91,7 +91,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a, long long 
 // (BMQ rows) that can see its keys.  Per tile, Q and dO are staged both
 // row-major (A operands of S = Q K^T and dP = dO V^T) and transposed (A
 // operands of dK^T += Q^T dS and dV^T += dO^T P), with LSE and Delta.
-template <typename M, int D, int NW, int BMQ>
+// With FEAT the logits carry the bias / ALiBi terms and dropout multiplies
+// P (in dV) and dP (in dS) by keep / (1 - p).
+template <typename M, int D, int NW, int BMQ, bool FEAT = false>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   using T = typename M::elem;
   constexpr int NT = NW * 64, BNK = NW * 32, KPL = M::KPL;
@@ -210,13 +212,23 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int il = 32 * mq + acc_row(e, g);
-            float pe = __builtin_amdgcn_exp2f(s[e] * P.scale_log2 - stats[bf][0][il]);
+            float x = s[e] * P.scale_log2;
+            if constexpr (FEAT) x = __builtin_fmaf(s[e], P.scale_log2, extra_log2<T>(a.f, b, h, i0 + il, kj, sq, sk));
+            float pe = __builtin_amdgcn_exp2f(x - stats[bf][0][il]);
             if (cls == kPartial) {
               const int diff = kj - (i0 + il);
               if (!(diff >= w.lo && diff <= w.hi && kj < sk)) pe = 0.f;
             }
-            p[e] = pe;
-            ds[e] = pe * (dp[e] - stats[bf][1][il]);
+            float pv = pe, dpe = dp[e];
+            if constexpr (FEAT) {
+              if (a.f.drop_thresh) {
+                const bool kp = keep1(a.f, b, h, P.H, i0 + il, kj, P.Sq, P.Sk);
+                pv = kp ? pe * a.f.drop_scale : 0.f;
+                dpe = kp ? dp[e] * a.f.drop_scale : 0.f;
+              }
+            }
+            p[e] = pv;
+            ds[e] = pe * (dpe - stats[bf][1][il]);
           }
           // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end).
 #pragma unroll
@@ -262,7 +274,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
 // One workgroup = 32*NW queries, each wave 32 queries with its Q and dO rows,
 // LSE and Delta in registers; the workgroup walks the key tiles its window
 // can see, staging K (row-major and transposed) and V (row-major).
-template <typename M, int D, int NW, int BN>
+// With FEAT the logits carry the bias / ALiBi terms, dropout multiplies dP
+// by keep / (1 - p), and with a dbias output every key tile is visited and
+// dS is stored (zeros where masked).
+template <typename M, int D, int NW, int BN, bool FEAT = false>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   using T = typename M::elem;
   constexpr int NT = NW * 64, BM = NW * 32, KPL = M::KPL;
@@ -297,10 +312,16 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const float* lsep = a.lse + b * P.olse_sb + h * P.olse_sh + q0 * P.olse_ss;
   const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
 
+  const bool all_tiles = FEAT && a.f.dbias != nullptr;
   const int ilast = min(i0 + BM, sq) - 1;
-  const long long jlo = max(0LL, (long long)i0 + w.lo);
-  const long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
-  const bool block_empty = w.lo > w.hi || jlo > jhi;
+  long long jlo = max(0LL, (long long)i0 + w.lo);
+  long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
+  bool block_empty = w.lo > w.hi || jlo > jhi;
+  if (all_tiles) {
+    jlo = 0;
+    jhi = (long long)sk - 1;
+    block_empty = sk == 0;
+  }
 
   const int iw0 = i0 + 32 * wave;
   const bool wave_live = iw0 < sq;
@@ -348,7 +369,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
       const T* Ks = smem + bf * STAGE;
       const T* Vs = Ks + BN * RLD;
       const T* Kt = Ks + 2 * BN * RLD;
-      const int cls = wave_live ? classify(w, iw0, 32, j0, BN, sk) : kEmpty;
+      int cls = wave_live ? classify(w, iw0, 32, j0, BN, sk) : kEmpty;
+      if (all_tiles && wave_live && cls == kEmpty) cls = kPartial;  // its dS is stored: zeros
       if (cls != kEmpty) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
@@ -361,15 +383,40 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
             dp = M::mma(load_frag<M>(Vs + off), dof.f[st], dp);
           }
           float ds[16];
+          uint32_t keep = 0xffffu;
+          if constexpr (FEAT) {
+            if (a.f.drop_thresh) {
+              keep = 0;
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd)
+                keep |= keep4(a.f, b, h, P.H, qi, j0 + 32 * kt + 8 * qd + 4 * g, P.Sq, P.Sk) << (4 * qd);
+            }
+          }
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            float pe = __builtin_amdgcn_exp2f(s[e] * P.scale_log2 - lse2);
+            const int j = j0 + 32 * kt + acc_row(e, g);
+            float x = s[e] * P.scale_log2;
+            if constexpr (FEAT) x = __builtin_fmaf(s[e], P.scale_log2, extra_log2<T>(a.f, b, h, qi, j, sq, sk));
+            float pe = __builtin_amdgcn_exp2f(x - lse2);
             if (cls == kPartial) {
-              const int j = j0 + 32 * kt + acc_row(e, g);
               const int diff = j - qi;
               if (!(diff >= w.lo && diff <= w.hi && j < sk)) pe = 0.f;
             }
-            ds[e] = pe * (dp[e] - delta);
+            float dpe = dp[e];
+            if constexpr (FEAT) {
+              if (a.f.drop_thresh) dpe = ((keep >> e) & 1u) ? dp[e] * a.f.drop_scale : 0.f;
+            }
+            ds[e] = pe * (dpe - delta);
+          }
+          if constexpr (FEAT) {
+            if (all_tiles && row_ok) {
+              float* drow = a.f.dbias + b * a.f.dsb + h * a.f.dsh + (long long)qi * a.f.dss;
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const int j = j0 + 32 * kt + acc_row(e, g);
+                if (j < sk) drow[j] = ds[e];
+              }
+            }
           }
           // dQ^T += K^T dS^T (scale applied at the end).
 #pragma unroll
@@ -477,7 +524,71 @@ struct Dkdv16 {
   }
 };
 
-template <typename M, int D, int NW, int BMQ, int WPE>
+// The dK/dV tile with the optional features: logits x = c s + log2(e)
+// (bias + alibi), P = 2^(x - LSE log2 e), and with dropout M = keep / (1 -
+// p): dV^T += dO^T (P o M), dS = P o (M o dP - Delta).  Each lane holds one
+// key, so every element needs its own dropout counter.
+template <typename M, int D, int BMQ>
+struct Dkdv16Feat {
+  using F = Dkdv16<M, D, BMQ>;
+  using T = typename M::elem;
+  using L = Swz<D>;
+  using frag = typename M::frag;
+  static constexpr int MQ = F::MQ, NS = F::NS, DVT = F::DVT;
+
+  static __device__ __forceinline__ void tile(const T* Qs, const T* dOs, const LdsOffsets<M, D>& lo, const float* lse2s,
+                                              const float* dels, const RowFrags<M, D>& kf,
+                                              const RowFrags<M, D>& vf, f32x16* dk, f32x16* dv, float c,
+                                              bool masked, Window w, int i0, int kj, int sq, int sk, int g,
+                                              const BwdArgs& a, int b, int h) {
+    const FeatArgs& f = a.f;
+#pragma unroll
+    for (int mq = 0; mq < MQ; ++mq) {
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s = M::mma(ld_row<M>(Qs + 32 * mq * L::PITCH, lo.row[st]), kf.f[st], s);
+        dp = M::mma(ld_row<M>(dOs + 32 * mq * L::PITCH, lo.row[st]), vf.f[st], dp);
+      }
+      const int ib = i0 + 32 * mq;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        s[e] = __builtin_fmaf(s[e], c, extra_log2<T>(f, b, h, ib + acc_row(e, g), kj, sq, sk));
+      if (masked) {
+        const long long ibg = (long long)ib + 4 * g;
+        mask_block(s, vis_bits((long long)kj - w.hi - ibg, min((long long)kj - w.lo, (long long)sq - 1) - ibg));
+      }
+      float p[16], ds[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int il = 32 * mq + acc_row(e, g);
+        const float pe = __builtin_amdgcn_exp2f(s[e] - lse2s[il]);
+        float mdp = dp[e], pm = pe;
+        if (f.drop_thresh) {
+          const bool kp = pe != 0.f && keep1(f, b, h, a.p.H, ib + acc_row(e, g), kj, a.p.Sq, a.p.Sk);
+          mdp = kp ? dp[e] * f.drop_scale : 0.f;
+          pm = kp ? pe * f.drop_scale : 0.f;
+        }
+        p[e] = pm;
+        ds[e] = pe * (mdp - dels[il]);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        frag pf, dsf;
+        M::pack(&p[8 * st], pf);
+        M::pack(&ds[8 * st], dsf);
+        const int rbase = (32 * mq + 16 * st) * L::PITCH;
+#pragma unroll
+        for (int dt = 0; dt < DVT; ++dt) {
+          dv[dt] = M::mma(ld_tr<M>(dOs + rbase, lo.tra[dt], lo.trb[dt]), pf, dv[dt]);
+          dk[dt] = M::mma(ld_tr<M>(Qs + rbase, lo.tra[dt], lo.trb[dt]), dsf, dk[dt]);
+        }
+      }
+    }
+  }
+};
+
+template <typename M, int D, int NW, int BMQ, int WPE, bool FEAT = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dkdv16_kernel(BwdArgs a) {
   using F = Dkdv16<M, D, BMQ>;
   using T = typename M::elem;
@@ -590,7 +701,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       if (tw0 <= t && t <= tw1) {
         const bool masked =
             classify(w, (long long)t * BMQ, BMQ, jw0, 32, sk) == kPartial || (t + 1) * BMQ > sq;
-        F::tile(qs[Pq], ds_[Pq], lo, ls[Pq], es[Pq], kf, vf, dk, dv, c, masked, w, t * BMQ, kj, sq, g);
+        if constexpr (FEAT)
+          Dkdv16Feat<M, D, BMQ>::tile(qs[Pq], ds_[Pq], lo, ls[Pq], es[Pq], kf, vf, dk, dv, c, masked, w, t * BMQ, kj,
+                                      sq, sk, g, a, b, h);
+        else
+          F::tile(qs[Pq], ds_[Pq], lo, ls[Pq], es[Pq], kf, vf, dk, dv, c, masked, w, t * BMQ, kj, sq, g);
       }
       __syncthreads();
     };
@@ -656,6 +771,27 @@ __shared__ __attribute__((aligned(16))) char g_bwd_x2[kBwdXBytes];
 using KBwdArgs = const __attribute__((address_space(4))) BwdArgs;
 __device__ __forceinline__ KBwdArgs& kernel_bwd_args() {
   return *(KBwdArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+// A private copy of the feature arguments (field by field: the implicit
+// copy constructor does not take the kernel-argument address space).
+__device__ __forceinline__ FeatArgs feat_args(KBwdArgs& a) {
+  FeatArgs f;
+  f.bias = a.f.bias;
+  f.bsb = a.f.bsb;
+  f.bsh = a.f.bsh;
+  f.bss = a.f.bss;
+  f.alibi = a.f.alibi;
+  f.offset = a.f.offset;
+  f.seed_lo = a.f.seed_lo;
+  f.seed_hi = a.f.seed_hi;
+  f.drop_thresh = a.f.drop_thresh;
+  f.drop_scale = a.f.drop_scale;
+  f.dbias = a.f.dbias;
+  f.dsb = a.f.dsb;
+  f.dsh = a.f.dsh;
+  f.dss = a.f.dss;
+  return f;
 }
 
 // Calls f(integral_constant<int, I>) for I = B .. E-1 in order.
@@ -1125,10 +1261,77 @@ struct Dq16 {
   }
 };
 
+// The dQ tile with the optional features: logits x = c s + log2(e)
+// (bias + alibi), P = 2^(x - LSE log2 e), with dropout M = keep / (1 - p):
+// dS = P o (M o dP - Delta), dQ^T += K^T dS^T; dS is also d loss / d logit,
+// stored to dbias when asked for.  One counter serves the lane's four
+// consecutive keys.
+template <typename M, int D, int BN>
+struct Dq16Feat {
+  using F = Dq16<M, D, BN>;
+  using T = typename M::elem;
+  using L = Swz<D>;
+  using frag = typename M::frag;
+  static constexpr int KT = F::KT, NS = F::NS, DVT = F::DVT;
+
+  static __device__ __forceinline__ void tile(const T* Ks, const T* Vs, const LdsOffsets<M, D>& lo,
+                                              const RowFrags<M, D>& qf, const RowFrags<M, D>& dof, f32x16* dq,
+                                              float c, float lse2, float delta, bool masked, Window w, int j0, int qi,
+                                              int sq, int sk, int g, const FeatArgs& f, int b, int h, int H, int Sq,
+                                              int Sk, bool row_ok) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s = M::mma(ld_row<M>(Ks + 32 * kt * L::PITCH, lo.row[st]), qf.f[st], s);
+        dp = M::mma(ld_row<M>(Vs + 32 * kt * L::PITCH, lo.row[st]), dof.f[st], dp);
+      }
+      const int jb = j0 + 32 * kt;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = __builtin_fmaf(s[e], c, extra_log2<T>(f, b, h, qi, jb + acc_row(e, g), sq, sk));
+      if (masked) {
+        const long long jbg = (long long)jb + 4 * g;
+        mask_block(s, vis_bits((long long)qi + w.lo - jbg, min((long long)qi + w.hi, (long long)sk - 1) - jbg));
+      }
+      uint32_t keep = 0xffffu;
+      if (f.drop_thresh) {
+        keep = 0;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) keep |= keep4(f, b, h, H, qi, jb + 8 * qd + 4 * g, Sq, Sk) << (4 * qd);
+      }
+      float ds[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(s[e] - lse2);
+        const float mdp = f.drop_thresh ? (((keep >> e) & 1u) ? dp[e] * f.drop_scale : 0.f) : dp[e];
+        ds[e] = pe * (mdp - delta);
+      }
+      if (f.dbias && row_ok) {
+        float* drow = f.dbias + b * f.dsb + h * f.dsh + (long long)qi * f.dss;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = jb + acc_row(e, g);
+          if (j < sk) drow[j] = ds[e];
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        frag dsf;
+        M::pack(&ds[8 * st], dsf);
+        const int rbase = (32 * kt + 16 * st) * L::PITCH;
+#pragma unroll
+        for (int dt = 0; dt < DVT; ++dt) dq[dt] = M::mma(ld_tr<M>(Ks + rbase, lo.tra[dt], lo.trb[dt]), dsf, dq[dt]);
+      }
+    }
+  }
+};
+
 // The dQ workgroup's work: block hw of nblk (the block's place in its own
 // grid), K and V tiles of stage s in the first two namespace-scope LDS
-// stages ([K | V] each).
-template <typename M, int D, int NW, int BN>
+// stages ([K | V] each).  With FEAT and a dbias output, every key tile of
+// the sequence is visited (tiles the window leaves empty write their zeros).
+template <typename M, int D, int NW, int BN, bool FEAT = false>
 __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   using F = Dq16<M, D, BN>;
   using T = typename M::elem;
@@ -1163,10 +1366,16 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   const float* l2p = a.lse2 + b * P.lse_sb + h * P.lse_sh + q0;
   const float* delp = a.delta + b * P.lse_sb + h * P.lse_sh + q0;
 
+  const bool all_tiles = FEAT && a.f.dbias != nullptr;
   const int ilast = min(i0 + BM, sq) - 1;
-  const long long jlo = max(0LL, (long long)i0 + w.lo);
-  const long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
-  const bool block_empty = w.lo > w.hi || jlo > jhi;
+  long long jlo = max(0LL, (long long)i0 + w.lo);
+  long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
+  bool block_empty = w.lo > w.hi || jlo > jhi;
+  if (all_tiles) {
+    jlo = 0;
+    jhi = (long long)sk - 1;
+    block_empty = sk == 0;
+  }
 
   const int iw0 = i0 + 32 * wave;
   const bool wave_live = iw0 < sq;
@@ -1180,6 +1389,10 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
       tw0 = (int)(a0 / BN);
       tw1 = (int)(a1 / BN);
     }
+  }
+  if (all_tiles && wave_live && sk > 0) {
+    tw0 = 0;
+    tw1 = (sk - 1) / BN;
   }
 
   RowFrags<M, D> qf, dof;
@@ -1215,8 +1428,15 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
       constexpr int Pq = decltype(parity)::value;
       if (t + 1 <= t1) dma(Pq ? k_s0 : k_s1, Pq ? v_s0 : v_s1, t + 1);
       if (tw0 <= t && t <= tw1) {
-        const bool masked = classify(w, iw0, 32, (long long)t * BN, BN, sk) == kPartial;
-        F::tile(Pq ? k_s1 : k_s0, Pq ? v_s1 : v_s0, lo, qf, dof, dq, c, lse2, delta, masked, w, t * BN, qi, sk, g);
+        if constexpr (FEAT) {
+          const FeatArgs f = feat_args(a);
+          const bool masked = classify(w, iw0, 32, (long long)t * BN, BN, sk) != kFull;
+          Dq16Feat<M, D, BN>::tile(Pq ? k_s1 : k_s0, Pq ? v_s1 : v_s0, lo, qf, dof, dq, c, lse2, delta, masked, w,
+                                   t * BN, qi, sq, sk, g, f, b, h, P.H, P.Sq, P.Sk, row_ok);
+        } else {
+          const bool masked = classify(w, iw0, 32, (long long)t * BN, BN, sk) == kPartial;
+          F::tile(Pq ? k_s1 : k_s0, Pq ? v_s1 : v_s0, lo, qf, dof, dq, c, lse2, delta, masked, w, t * BN, qi, sk, g);
+        }
       }
       __syncthreads();
     };
@@ -1241,9 +1461,9 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   }
 }
 
-template <typename M, int D, int NW, int BN, int WPE>
+template <typename M, int D, int NW, int BN, int WPE, bool FEAT = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dq16_kernel(BwdArgs) {
-  dq16_body<M, D, NW, BN>(blockIdx.x, gridDim.x);
+  dq16_body<M, D, NW, BN, FEAT>(blockIdx.x, gridDim.x);
 }
 
 // ------------------------------------------ 16-bit dK/dV + dQ in one grid
@@ -1299,6 +1519,38 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
                256u, a, nrows);
       if (err != hipSuccess) return err;
     }
+  }
+  // Bias, ALiBi, dropout or dbias: the kernels built with them (16-bit dK/dV
+  // one wave per SIMD above head_dim 64, where their registers do not fit
+  // two), never the fused or producer / consumer ones.
+  if (a.feat) {
+    if (stages & kStageDkDv) {
+      const long long nblk = (a.p.Sk + NW_KV * 32 - 1) / (NW_KV * 32) * a.p.H * a.p.B;
+      if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+      if (nblk > 0) {
+        if constexpr (S::k16)
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, (D > 64 ? 1 : 2), true>),
+                   "attn_bwd_dkdv16_kernel", (unsigned)nblk, (unsigned)(NW_KV * 64), a);
+        else
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ, true>),
+                   "attn_bwd_dkdv_kernel", (unsigned)nblk, (unsigned)(NW_KV * 64), a);
+        if (err != hipSuccess) return err;
+      }
+    }
+    if (stages & kStageDq) {
+      const long long nblk = (a.p.Sq + NW_Q * 32 - 1) / (NW_Q * 32) * a.p.H * a.p.B;
+      if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+      if (nblk > 0) {
+        if constexpr (S::k16)
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, (D > 80 ? 1 : 2), true>),
+                   "attn_bwd_dq16_kernel", (unsigned)nblk, (unsigned)(NW_Q * 64), a);
+        else
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN, true>), "attn_bwd_dq_kernel",
+                   (unsigned)nblk, (unsigned)(NW_Q * 64), a);
+        if (err != hipSuccess) return err;
+      }
+    }
+    return hipSuccess;
   }
   // 2 + 3 in one grid where the build has the fused kernel and it pays: a
   // wide band (its dQ workgroups are 256 rows) and a separate dQ grid whose

@@ -47,7 +47,7 @@ __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d)
   }
 }
 
-template <typename M, int D, int NW, int BN>
+template <typename M, int D, int NW, int BN, bool FEAT = false>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   using T = typename M::elem;
   constexpr int NT = NW * 64, BM = NW * 32, KPL = M::KPL;
@@ -143,6 +143,27 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
           }
         }
         const bool partial = cls == kPartial;
+        float cc = c;
+        uint32_t keep[KT];
+        if constexpr (FEAT) {
+          // Logits in the log2 domain with the additive terms, and the
+          // dropout bits of every element (4 consecutive keys per counter).
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            const int jb = j0 + 32 * kt;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              s[kt][e] = __builtin_fmaf(s[kt][e], c, extra_log2<T>(a.f, b, h, qi, jb + acc_row(e, g), sq, sk));
+            keep[kt] = 0xffffu;
+            if (a.f.drop_thresh) {
+              keep[kt] = 0;
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd)
+                keep[kt] |= keep4(a.f, b, h, P.H, qi, jb + 8 * qd + 4 * g, P.Sq, P.Sk) << (4 * qd);
+            }
+          }
+          cc = 1.f;
+        }
         if (partial) {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
@@ -160,7 +181,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
           for (int e = 0; e < 16; ++e) smax = fmaxf(smax, s[kt][e]);
         smax = halves_max(smax);
         // Max of x = c*s over the row's visible keys of this tile.
-        const float mx = smax == -INFINITY ? -INFINITY : smax * c;
+        const float mx = smax == -INFINITY ? -INFINITY : smax * cc;
         const bool raise = mx > m + kRescaleSlack;  // also when m is still -inf
         if (__builtin_amdgcn_ballot_w64(raise)) {
           const float alpha = raise ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
@@ -179,10 +200,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, nm));
-            if (partial && s[kt][e] == -INFINITY) pe = 0.f;
-            x[kt][e] = pe;
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], cc, nm));
+            if ((partial || FEAT) && s[kt][e] == -INFINITY) pe = 0.f;
             ls += pe;
+            if constexpr (FEAT) pe = ((keep[kt] >> e) & 1u) ? pe : 0.f;
+            x[kt][e] = pe;
           }
         l += ls;
         // O^T += V^T P^T
@@ -212,7 +234,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   if (wave_live) {
     const float lt = halves_sum(l);
     if (qi < sq) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float inv = lt > 0.f ? (FEAT && a.f.drop_thresh ? a.f.drop_scale : 1.f) / lt : 0.f;
       T* orow = op + (long long)qi * a.o.ss;
 #pragma unroll
       for (int dt = 0; dt < DVT; ++dt)
@@ -301,10 +323,12 @@ struct Fwd16 {
   }
 
   // P = 2^(c s - m), rounded to the working type, and O^T += V^T P^T, for
-  // every row block.
+  // every row block.  With DROP, element e of block (rb, kt) enters the row
+  // sum and then the product only when bit e of keep[rb][kt] is set.
+  template <bool DROP = false>
   static __device__ __forceinline__ void softmax_pv(const T* V, const LdsOffsets<M, D>& lo,
                                                     const f32x16 (*s)[KT], f32x16 (*acc)[DVT], const float* m,
-                                                    float c, float* l) {
+                                                    float c, float* l, const uint32_t (*keep)[KT] = nullptr) {
     float nm[RB], ls[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -321,6 +345,7 @@ struct Fwd16 {
         for (int e = 0; e < 16; ++e) {
           x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][kt][e], c, nm[rb]));
           ls[rb] += x[e];
+          if constexpr (DROP) x[e] = ((keep[rb][kt] >> e) & 1u) ? x[e] : 0.f;
         }
         M::pack(&x[0], pf[rb][0]);
         M::pack(&x[8], pf[rb][1]);
@@ -341,7 +366,7 @@ struct Fwd16 {
   }
 };
 
-template <typename M, int D, int NW, int BN, int RB, int WPE>
+template <typename M, int D, int NW, int BN, int RB, int WPE, bool FEAT = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_fwd16_kernel(FwdArgs a) {
   using F = Fwd16<M, D, BN, RB>;
   using T = typename M::elem;
@@ -441,12 +466,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         f32x16 s[RB][KT];
         F::scores(kc, lo, qf, s);
         const bool masked = t < full.t0 || t > full.t1;
+        float cc = c;
+        uint32_t keep[RB][KT];
+        if constexpr (FEAT) {
+          // Logits in the log2 domain with the additive terms, and the
+          // dropout bits of every element (4 consecutive keys per counter).
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+              const int qi = iw0 + 32 * rb + r, jb = t * BN + 32 * kt;
+              keep[rb][kt] = 0xffffu;
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                s[rb][kt][e] = __builtin_fmaf(s[rb][kt][e], c, extra_log2<T>(a.f, b, h, qi, jb + acc_row(e, g), sq, sk));
+              if (a.f.drop_thresh) {
+                keep[rb][kt] = 0;
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd)
+                  keep[rb][kt] |= keep4(a.f, b, h, P.H, qi, jb + 8 * qd + 4 * g, P.Sq, P.Sk) << (4 * qd);
+              }
+            }
+          cc = 1.f;
+        }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int rb0 = iw0 + 32 * rb;
-          F::finalize(s[rb], masked, w, t * BN, rb0 + r, sk, c, m[rb], l[rb], acc[rb], g);
+          F::finalize(s[rb], masked, w, t * BN, rb0 + r, sk, cc, m[rb], l[rb], acc[rb], g);
         }
-        F::softmax_pv(vc, lo, s, acc, m, c, l);
+        if (FEAT && a.f.drop_thresh)
+          F::template softmax_pv<true>(vc, lo, s, acc, m, cc, l, keep);
+        else
+          F::softmax_pv(vc, lo, s, acc, m, cc, l);
       }
       __syncthreads();
     };
@@ -462,7 +513,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       const int qi = iw0 + 32 * rb + r;
       const float lt = halves_sum(l[rb]);
       if (qi < sq) {
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const float inv = lt > 0.f ? (FEAT && a.f.drop_thresh ? a.f.drop_scale : 1.f) / lt : 0.f;
         T* orow = op + (long long)qi * a.o.ss;
 #pragma unroll
         for (int dt = 0; dt < DVT; ++dt)
@@ -1000,6 +1051,20 @@ template <typename M, int D, class Ex>
 static hipError_t launch_fwd_t(const FwdArgs& a, const Ex& ex) {
   using S = FwdShape<M, D>;
   constexpr int BN = S::BN;
+  if (a.feat) {
+    // Bias, ALiBi or dropout: the narrow kernel built with them (one wave
+    // per SIMD above head_dim 80, where their registers do not fit two).
+    const long long nq = (a.p.Sq + S::NW * 32 - 1) / (S::NW * 32);
+    const long long nblk = nq * a.p.H * a.p.B;
+    if (nblk == 0) return hipSuccess;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+    if constexpr (S::k16)
+      return ex(reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, S::NW, BN, 1, (D > 80 ? 1 : 2), true>),
+                "attn_fwd16_kernel", (unsigned)nblk, (unsigned)(S::NW * 64), a);
+    else
+      return ex(reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, S::NW, BN, true>), "attn_fwd_kernel",
+                (unsigned)nblk, (unsigned)(S::NW * 64), a);
+  }
   const bool pp = S::PP && wide_window(a.p);
   const int nw = pp ? 8 : S::NW, bm = nw * 32 * (pp ? 1 : S::RB);
   const long long nq = (a.p.Sq + bm - 1) / bm;

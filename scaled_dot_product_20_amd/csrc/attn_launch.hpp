@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_feat.hpp"
+
 namespace sdpa {
 
 // Element strides of one operand: base + b*sb + h*sh + row*ss + d.  For the
@@ -95,6 +97,8 @@ struct FwdArgs {
   ProblemArgs p;
   Operand q, k, v, o;
   float* lse;
+  FeatArgs f;  // optional features (read by the FEAT kernels only)
+  int feat;    // any feature present: the FEAT kernels run
 };
 
 struct BwdArgs {
@@ -103,6 +107,8 @@ struct BwdArgs {
   const float* lse;
   float* delta;  // workspace: Delta_i = sum_d dO_id O_id (written by the preprocess)
   float* lse2;   // workspace: LSE_i * log2(e) (written by the preprocess)
+  FeatArgs f;
+  int feat;
 };
 
 // Steps of the backward, as a bit mask of `stages`; they run in this order.

@@ -44,12 +44,17 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "attn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(attn_fwd_params), sizeof(attn_bwd_params),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n",
+         sizeof(attn_fwd_params), sizeof(attn_bwd_params),
          offsetof(attn_fwd_params, total_q), offsetof(attn_fwd_params, q),
          offsetof(attn_fwd_params, o_stride), offsetof(attn_bwd_params, dout),
          offsetof(attn_bwd_params, workspace), offsetof(attn_bwd_params, workspace_bytes),
          offsetof(attn_fwd_params, varlen), offsetof(attn_fwd_params, seqstart_q),
-         offsetof(attn_fwd_params, seqstart_k));
+         offsetof(attn_fwd_params, seqstart_k), offsetof(attn_fwd_params, bias),
+         offsetof(attn_fwd_params, bias_stride), offsetof(attn_fwd_params, alibi_slopes),
+         offsetof(attn_fwd_params, dropout_p), offsetof(attn_fwd_params, reserved2),
+         offsetof(attn_fwd_params, philox_seed), offsetof(attn_fwd_params, philox_offset),
+         offsetof(attn_bwd_params, dbias), offsetof(attn_bwd_params, dbias_stride));
   return 0;
 }
 """)
@@ -60,7 +65,10 @@ int main(void) {
     want = [ctypes.sizeof(bd.FwdParams), ctypes.sizeof(bd.BwdParams),
             bd.FwdParams.total_q.offset, bd.FwdParams.q.offset, bd.FwdParams.o_stride.offset,
             bd.BwdParams.dout.offset, bd.BwdParams.workspace.offset, bd.BwdParams.workspace_bytes.offset,
-            bd.FwdParams.varlen.offset, bd.FwdParams.seqstart_q.offset, bd.FwdParams.seqstart_k.offset]
+            bd.FwdParams.varlen.offset, bd.FwdParams.seqstart_q.offset, bd.FwdParams.seqstart_k.offset,
+            bd.FwdParams.bias.offset, bd.FwdParams.bias_stride.offset, bd.FwdParams.alibi_slopes.offset,
+            bd.FwdParams.dropout_p.offset, bd.FwdParams.reserved2.offset, bd.FwdParams.philox_seed.offset,
+            bd.FwdParams.philox_offset.offset, bd.BwdParams.dbias.offset, bd.BwdParams.dbias_stride.offset]
     assert got == want
 
 
@@ -367,12 +375,14 @@ def test_noalloc_validation_and_limit():
 # ----------------------------------------------------------- version 2 structs
 
 class FwdParamsV2(ctypes.Structure):
-    """attn_fwd_params as version 2 laid it out (no per-side addressing)."""
-    _fields_ = [f for f in bd.FwdParams._fields_ if f[0] not in ("varlen", "reserved1", "seqstart_q", "seqstart_k")]
+    """attn_fwd_params as version 2 laid it out: every field before the
+    version-3 ones (per-side addressing, then the optional features)."""
+    _fields_ = bd.FwdParams._fields_[:[f[0] for f in bd.FwdParams._fields_].index("varlen")]
 
 
 class BwdParamsV2(ctypes.Structure):
-    _fields_ = [("fwd", FwdParamsV2)] + [f for f in bd.BwdParams._fields_ if f[0] != "fwd"]
+    _fields_ = [("fwd", FwdParamsV2)] + [f for f in bd.BwdParams._fields_
+                                         if f[0] not in ("fwd", "dbias", "dbias_stride")]
 
 
 def to_v2(p, cls):
@@ -510,3 +520,82 @@ def test_varlen_mixed_extents():
     assert fcheck(p) == OK
     p.o = BASE + 2 * 10 * 64 * 2 + 29 * 64 * 2  # O starts inside K's last row
     assert fcheck(p) == INVALID
+
+
+def test_feature_fields_validate():
+    """Bias, ALiBi, dropout and dbias: well-formed values pass; a set
+    reserved2, a dropout probability outside [0, 1) or NaN, misaligned
+    pointers, and outputs overlapping the bias, the slopes or each other are
+    rejected before any HIP call."""
+    B, H, S, D = 2, 3, 64, 64
+
+    def feat(**kw):
+        p = dense_params(B=B, H=H, S=S, D=D)
+        p.bias = kw.get("bias", addr(20))
+        p.bias_stride = bd._I64x3(*kw.get("bias_stride", (H * S * S, S * S, S)))
+        p.alibi_slopes = kw.get("alibi", addr(21))
+        p.dropout_p = kw.get("dropout_p", 0.25)
+        p.philox_seed, p.philox_offset = 2**64 - 1, 12345
+        return p
+
+    assert fcheck(feat()) == OK
+    assert fcheck(feat(bias_stride=(0, 0, S))) == OK        # one [Sq, Sk] bias for all
+    assert fcheck(feat(bias_stride=(0, 0, 0))) == OK        # one row for every query
+    assert fcheck(feat(dropout_p=0.0)) == OK
+    p = feat()
+    p.reserved2 = 1
+    assert fcheck(p) == INVALID
+    for dp in (1.0, 1.5, -0.1, float("nan")):
+        assert fcheck(feat(dropout_p=dp)) == INVALID, dp
+    assert fcheck(feat(bias=addr(20) + 1)) == INVALID       # not element-aligned
+    assert fcheck(feat(alibi=addr(21) + 2)) == INVALID
+    p = feat()
+    p.o = p.bias                                           # output over the bias
+    assert fcheck(p) == INVALID
+    p = feat()
+    p.lse = p.alibi_slopes
+    assert fcheck(p) == INVALID
+
+    b = bwd_params(feat())
+    b.dbias = addr(22)
+    b.dbias_stride = bd._I64x3(H * S * S, S * S, S)
+    assert bcheck(b) == OK
+    b.dbias = addr(22) + 2                                 # fp32 output: 4-byte aligned
+    assert bcheck(b) == INVALID
+    for other in ("dq", "dk", "workspace"):
+        b = bwd_params(feat())
+        b.dbias_stride = bd._I64x3(H * S * S, S * S, S)
+        b.dbias = getattr(b, other)
+        assert bcheck(b) == INVALID, other
+    b = bwd_params(feat())
+    b.dbias_stride = bd._I64x3(H * S * S, S * S, S)
+    b.dbias = b.fwd.bias
+    assert bcheck(b) == INVALID
+    b = bwd_params(dense_params())                         # dbias alone is a valid request
+    b.dbias = addr(22)
+    b.dbias_stride = bd._I64x3(H * S * S, S * S, S)
+    assert bcheck(b) == OK
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,D", [(bd.BF16, 128), (bd.FP16, 64), (bd.FP32, 96)])
+def test_feature_calls_plan_feature_kernels(dtype, D):
+    """A call with any feature runs the kernels built for them: the narrow
+    forward, and the separate dK/dV and dQ kernels (never the fused or the
+    producer / consumer backward)."""
+    lib = bd.lib()
+    p = dense_params(B=2, H=4, S=1024, D=D, dtype=dtype)
+    p.dropout_p = 0.1
+    pl = bd.Plan()
+    assert lib.attn_fwd_plan(ctypes.byref(p), None, ctypes.byref(pl)) == OK
+    want_fwd = "attn_fwd16_kernel" if dtype != bd.FP32 else "attn_fwd_kernel"
+    assert [pl.kernel[i].decode() for i in range(pl.count)][0] == want_fwd
+    for name, field in (("dropout", None), ("dbias", "dbias")):
+        b = bwd_params(p if field is None else dense_params(B=2, H=4, S=1024, D=D, dtype=dtype))
+        if field:
+            b.dbias = addr(22)
+            b.dbias_stride = bd._I64x3(4 * 1024 * 1024, 1024 * 1024, 1024)
+        assert lib.attn_bwd_plan(ctypes.byref(b), bd.BWD_ALL, None, ctypes.byref(pl)) == OK
+        names = [pl.kernel[i].decode() for i in range(pl.count)]
+        sfx = "16" if dtype != bd.FP32 else ""
+        assert names == ["attn_bwd_pre_kernel", f"attn_bwd_dkdv{sfx}_kernel", f"attn_bwd_dq{sfx}_kernel"], names
