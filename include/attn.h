@@ -71,6 +71,10 @@ extern "C" {
  *   layout of the AOTriton 0.14b VarlenBits LSE field) instead of
  *   [heads, total_q]. */
 #define ATTN_FLAG_LSE_TH 1u
+/* ATTN_FLAG_NO_SPLIT (backward only, ignored by the forward): never use the
+ *   split mode of attn_bwd_workspace_size / attn_bwd below, which small
+ *   problems otherwise take; the workspace then holds only Delta and LSE. */
+#define ATTN_FLAG_NO_SPLIT 2u
 
 /* Unbounded side of a window. */
 #define ATTN_WINDOW_INF 2147483647
@@ -138,7 +142,8 @@ extern "C" {
 
 typedef struct {
   uint32_t version;        /* ATTN_PARAMS_VERSION */
-  uint32_t flags;          /* 0 or ATTN_FLAG_LSE_TH (THD only) */
+  uint32_t flags;          /* ATTN_FLAG_LSE_TH (stacked Q only) and / or
+                              ATTN_FLAG_NO_SPLIT, else 0 */
   int32_t dtype;           /* ATTN_FP32 / ATTN_FP16 / ATTN_BF16 */
   int32_t layout;          /* ATTN_BHSD / ATTN_THD / ATTN_VARLEN */
   int32_t batch;           /* BHSD: batch; THD: number of sequences (>= 1);
@@ -265,14 +270,27 @@ hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
  * split backward, "triton_split" in the same notes) as attn_bwd_dkdv_dq
  * does, then, only when seqused_q / seqused_k are given, the small kernels
  * that zero the gradient rows past the used ones.  The dK/dV and dQ sums are
- * computed without atomics: results are run-to-run identical. */
+ * computed without atomics: results are run-to-run identical.
+ *
+ * Split mode (small problems, unless ATTN_FLAG_NO_SPLIT): when the dK/dV or
+ * the dQ grid (128 keys or queries per workgroup) would have fewer than 64
+ * workgroups, and the call has no bias, ALiBi, dropout or dbias, each grid
+ * is repeated so that copy g of n walks the g-th of n contiguous shares of
+ * the tiles it would visit (query tiles for dK/dV, key tiles for dQ), about
+ * 256 workgroups in all (at most 8 copies, one per tile, fp32 partial sums
+ * of at most 8 MiB); the copies store fp32 partial sums in the workspace,
+ * and a last kernel adds them in copy order, scales, rounds, and writes the
+ * rows past each length.  The sums then group the tiles differently from
+ * the unsplit path (results differ in rounding only, and stay run-to-run
+ * identical). */
 hipError_t attn_bwd(const attn_bwd_params *p, hipStream_t stream);
 
 /* The three steps of attn_bwd as separate calls, for callers that schedule
  * or time them one by one.  Same parameters, validation and errors as
  * attn_bwd; each enqueues one kernel on `stream`, and attn_bwd_dkdv /
  * attn_bwd_dq also the row-zeroing kernel of their outputs when seqused
- * arrays are given.  They must run in this order on one stream (or be
+ * arrays are given (in split mode: their split grid and the reduction of
+ * their outputs).  They must run in this order on one stream (or be
  * ordered by events): attn_bwd_dkdv and attn_bwd_dq read the Delta and LSE
  * log2(e) that attn_bwd_preprocess leaves in the workspace, which must not
  * be touched in between.
@@ -297,8 +315,11 @@ hipError_t attn_bwd_dkdv_dq(const attn_bwd_params *p, hipStream_t stream);
 
 /* Workspace bytes attn_bwd needs for this problem: two fp32 values per query
  * row and head (Delta_i and LSE_i * log2(e), written by attn_bwd_preprocess
- * and read by the other two steps), each array rounded up to 256 bytes;
- * 0 when the problem is malformed. */
+ * and read by the other two steps), each array rounded up to 256 bytes,
+ * then, in split mode, the fp32 partial sums (head_dim floats per copy, head
+ * and row: dK and dV per key-side copy, dQ per query-side copy; rows are the
+ * stacked tensor's rows, or batch * seqlen for a padded side), rounded up to
+ * 256 bytes; 0 when the problem is malformed. */
 uint64_t attn_bwd_workspace_size(const attn_bwd_params *p);
 
 /* Host-only validation of a call, the same checks attn_fwd / attn_bwd make

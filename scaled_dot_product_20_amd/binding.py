@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(HERE, "libsdpa20.so")
 WINDOW_INF = 2147483647
 PARAMS_VERSION = 3
 FLAG_LSE_TH = 1  # ATTN_FLAG_LSE_TH: packed LSE as [T, H]
+FLAG_NO_SPLIT = 2  # ATTN_FLAG_NO_SPLIT: the backward never takes its split mode
 FP32, FP16, BF16 = 0, 1, 2
 BHSD, THD, VARLEN = 0, 1, 2
 # Mode byte of one side under VARLEN (ATTN_SEQ_* in include/attn.h).
@@ -190,7 +191,7 @@ def _side(t: torch.Tensor, mode: int, cu, max_seqlen, name: str):
 def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens_k,
                max_seqlen_q, max_seqlen_k, lse_layout="ht", seqused_q=None, seqused_k=None,
                q_mode=None, k_mode=None, seqstart_q=None, seqstart_k=None, batch=None, bias=None,
-               alibi_slopes=None, dropout_p=0.0, philox_seed=0, philox_offset=0) -> FwdParams:
+               alibi_slopes=None, dropout_p=0.0, philox_seed=0, philox_offset=0, split=True) -> FwdParams:
     """Fill an attn_fwd_params from tensors (no device work).  ``lse_layout``
     'th' (a stacked Q side only) stores LSE as [T, H] instead of [H, T].
     ``seqused_q`` / ``seqused_k`` (int32 [batch] on the device): sequence b
@@ -202,7 +203,8 @@ def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens
     Optional features: ``bias`` (inputs' dtype, indexable [B, H, seqlen_q,
     seqlen_k] with sequence-local query / key indices; size-1 axes
     broadcast; unit stride on the key axis), ``alibi_slopes`` (fp32 [H]),
-    ``dropout_p`` with ``philox_seed`` / ``philox_offset``."""
+    ``dropout_p`` with ``philox_seed`` / ``philox_offset``.  ``split=False``
+    keeps the backward out of its split mode (ATTN_FLAG_NO_SPLIT)."""
     p = FwdParams()
     p.version = PARAMS_VERSION
     if q.dtype not in _DTYPE:
@@ -262,6 +264,8 @@ def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens
                 alibi_slopes.shape != (p.heads,) or alibi_slopes.stride(0) != 1:
             raise ValueError("alibi_slopes: contiguous fp32 [heads] on the inputs' device")
         p.alibi_slopes = _ptr(alibi_slopes)
+    if not split:
+        p.flags |= FLAG_NO_SPLIT
     p.dropout_p = float(dropout_p)
     p.philox_seed = int(philox_seed) & (2**64 - 1)
     p.philox_offset = int(philox_offset) & (2**64 - 1)
@@ -308,7 +312,8 @@ def _stream(dev) -> int:
 def _problem(q, *, scale=None, window=(WINDOW_INF, WINDOW_INF), diag="top_left", cu_seqlens_q=None,
              cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, lse_layout="ht", seqused_q=None,
              seqused_k=None, q_mode=None, k_mode=None, seqstart_q=None, seqstart_k=None, batch=None,
-             bias=None, alibi_slopes=None, dropout_p=0.0, philox_seed=0, philox_offset=0, read_back=True):
+             bias=None, alibi_slopes=None, dropout_p=0.0, philox_seed=0, philox_offset=0, split=True,
+             read_back=True):
     """The keyword arguments of fwd_params for a call: default scale,
     cu_seqlens checked, and (packed [T, H, D] inputs without modes) the max
     lengths read back from cu_seqlens when not given and `read_back`."""
@@ -326,7 +331,7 @@ def _problem(q, *, scale=None, window=(WINDOW_INF, WINDOW_INF), diag="top_left",
                 seqused_q=seqused_q, seqused_k=seqused_k, q_mode=q_mode, k_mode=k_mode,
                 seqstart_q=seqstart_q, seqstart_k=seqstart_k, batch=batch, bias=bias,
                 alibi_slopes=alibi_slopes, dropout_p=dropout_p, philox_seed=philox_seed,
-                philox_offset=philox_offset)
+                philox_offset=philox_offset, split=split)
 
 
 def lse_shape(q: torch.Tensor, lse_layout="ht", q_mode=None):
@@ -466,7 +471,8 @@ def attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
     return dq, dk, dv
 
 
-def workspace_size(dout, q, k, v, o, lse, **kw) -> int:
-    """Bytes attn_bwd needs for its Delta workspace."""
-    p = bwd_params(dout, q, k, v, o, lse, dout, dout, dout, None, **kw)
+def workspace_size(dout, q, k, v, o, lse, dbias=None, **kw) -> int:
+    """Bytes attn_bwd needs for its workspace (Delta and LSE, and the split
+    mode's partial sums when it takes it; keywords as for attn_bwd)."""
+    p = bwd_params(dout, q, k, v, o, lse, dout, dout, dout, None, dbias=dbias, **_problem(q, **kw))
     return int(lib().attn_bwd_workspace_size(ctypes.byref(p)))

@@ -228,7 +228,7 @@ hipError_t check_problem(const attn_fwd_params* p) {
   if (!std::isfinite(p->scale)) return hipErrorInvalidValue;
   const Side qs = side_of(p, true), ks = side_of(p, false);
   if (!side_ok(qs) || !side_ok(ks)) return hipErrorInvalidValue;
-  if ((p->flags & ~ATTN_FLAG_LSE_TH) != 0 || ((p->flags & ATTN_FLAG_LSE_TH) && !qs.stacked()))
+  if ((p->flags & ~(ATTN_FLAG_LSE_TH | ATTN_FLAG_NO_SPLIT)) != 0 || ((p->flags & ATTN_FLAG_LSE_TH) && !qs.stacked()))
     return hipErrorInvalidValue;
   if (p->batch < ((qs.stacked() || ks.stacked()) ? 1 : 0)) return hipErrorInvalidValue;
   // A pointer may be NULL only when its tensor has no elements.
@@ -267,6 +267,47 @@ Extent lse_extent(const attn_fwd_params* p) {
 // bytes.
 uint64_t stat_section_bytes(const attn_fwd_params* p) { return ((uint64_t)lse_count(p) * 4 + 255) / 256 * 256; }
 uint64_t delta_bytes(const attn_fwd_params* p) { return 2 * stat_section_bytes(p); }
+
+// Split mode of the backward (the launch rules in attn_bwd.hip): taken for
+// calls without optional features whose dK/dV or dQ grid (128 keys or
+// queries per workgroup) has fewer than 64 workgroups, i.e. would leave at
+// least three quarters of a 256-CU GPU idle.  Each grid is repeated to reach
+// about 256 workgroups, at most 8 times and at most once per tile of the
+// axis it splits; the fp32 partial sums are capped at 8 MiB (fewer copies,
+// or no split, beyond that).  Depends on the call only, so the workspace
+// size and the launch agree.
+struct Split {
+  int gkv = 1, gq = 1;
+  int64_t rows_q = 0, rows_k = 0;
+  uint64_t bytes = 0;  // 0: no split
+};
+
+Split split_of(const attn_bwd_params* p) {
+  Split sp;
+  const attn_fwd_params* f = &p->fwd;
+  if (feat_on(f) || p->dbias || (f->flags & ATTN_FLAG_NO_SPLIT)) return sp;
+  const Side qs = side_of(f, true), ks = side_of(f, false);
+  const int64_t B = f->batch, H = f->heads, D = f->head_dim, Sq = f->seqlen_q, Sk = f->seqlen_k;
+  const int64_t nkv = B * H * ((Sk + 127) / 128), nq = B * H * ((Sq + 127) / 128);
+  if (nkv == 0 || nq == 0 || (nkv >= 64 && nq >= 64)) return sp;
+  const int64_t tile = f->dtype == ATTN_FP32 ? 32 : 64;  // query tile of dK/dV, key tile of dQ
+  auto groups = [](int64_t nblk, int64_t ntiles) {
+    return (int)std::max<int64_t>(1, std::min<int64_t>({(256 + nblk - 1) / nblk, 8, ntiles}));
+  };
+  sp.gkv = groups(nkv, (Sq + tile - 1) / tile);
+  sp.gq = groups(nq, (Sk + tile - 1) / tile);
+  sp.rows_q = qs.stacked() ? f->total_q : B * Sq;
+  sp.rows_k = ks.stacked() ? f->total_k : B * Sk;
+  auto bytes = [&] { return (uint64_t)(4 * D * H * (2 * sp.gkv * sp.rows_k + sp.gq * sp.rows_q)); };
+  constexpr uint64_t kCap = 8u << 20;
+  while (bytes() > kCap && (sp.gkv > 1 || sp.gq > 1)) (sp.gkv >= sp.gq ? sp.gkv : sp.gq) -= 1;
+  if (bytes() > kCap || (sp.gkv == 1 && sp.gq == 1)) return Split{};
+  sp.bytes = (bytes() + 255) / 256 * 256;
+  return sp;
+}
+
+// Workspace of a backward: Delta and LSE log2(e), then the split partials.
+uint64_t bwd_ws_bytes(const attn_bwd_params* p) { return delta_bytes(&p->fwd) + split_of(p).bytes; }
 
 sdpa::SideArgs side_args(const Side& s) {
   sdpa::SideArgs a{};
@@ -351,7 +392,7 @@ hipError_t check_bwd(const attn_bwd_params* p, bool ws) {
   const bool no_q = empty_side(f, qs), no_k = empty_side(f, ks);
   if ((!p->dout && !no_q) || (!p->dq && !no_q) || (!p->dk && !no_k) || (!p->dv && !no_k))
     return hipErrorInvalidValue;
-  if (ws && (!p->workspace || p->workspace_bytes < delta_bytes(f) ||
+  if (ws && (!p->workspace || p->workspace_bytes < bwd_ws_bytes(p) ||
              (reinterpret_cast<uintptr_t>(p->workspace) & 255u) != 0))
     return hipErrorInvalidValue;
   const int64_t esz = elem_bytes(f->dtype);
@@ -367,7 +408,7 @@ hipError_t check_bwd(const attn_bwd_params* p, bool ws) {
       extent_of(p->dq, p->dq_stride, B, H, qs, D, esz), extent_of(p->dk, p->dk_stride, B, H, ks, D, esz),
       extent_of(p->dv, p->dv_stride, B, H, ks, D, esz),
       ws ? Extent{reinterpret_cast<uintptr_t>(p->workspace),
-                  reinterpret_cast<uintptr_t>(p->workspace) + (uintptr_t)delta_bytes(f)}
+                  reinterpret_cast<uintptr_t>(p->workspace) + (uintptr_t)bwd_ws_bytes(p)}
          : Extent{0, 0},
       extent4(p->dbias, p->dbias_stride, f, 4)};
   const Extent ins[8] = {extent_of(f->q, f->q_stride, B, H, qs, D, esz),
@@ -427,6 +468,16 @@ sdpa::BwdArgs bwd_args(const attn_bwd_params* p, void* ws) {
     a.f.dss = p->dbias_stride[2];
   }
   a.feat = feat_on(f) || p->dbias != nullptr;
+  a.split_kv = a.split_q = 1;
+  const Split sp = split_of(p);
+  if (sp.bytes) {
+    // Integer arithmetic: the plan query passes no workspace.
+    a.part = reinterpret_cast<float*>(reinterpret_cast<uintptr_t>(ws) + (uintptr_t)delta_bytes(f));
+    a.rows_q = sp.rows_q;
+    a.rows_k = sp.rows_k;
+    a.split_kv = sp.gkv;
+    a.split_q = sp.gq;
+  }
   return a;
 }
 
@@ -538,7 +589,7 @@ uint64_t attn_bwd_workspace_size(const attn_bwd_params* p_in) {
   attn_bwd_params tmp;
   const attn_bwd_params* p = bwd_v3(p_in, &tmp);
   if (!p || check_problem(&p->fwd) != hipSuccess) return 0;
-  return delta_bytes(&p->fwd);
+  return bwd_ws_bytes(p);
 }
 
 hipError_t attn_bwd_check(const attn_bwd_params* p_in) {
@@ -592,7 +643,7 @@ hipError_t attn_bwd_noalloc(const attn_bwd_params* p_in, hipStream_t stream) {
   hipError_t err = check_bwd(p, false);
   if (err != hipSuccess) return err;
   const attn_fwd_params* f = &p->fwd;
-  if (delta_bytes(f) > (uint64_t)ATTN_NOALLOC_SCRATCH_BYTES) return hipErrorOutOfMemory;
+  if (bwd_ws_bytes(p) > (uint64_t)ATTN_NOALLOC_SCRATCH_BYTES) return hipErrorOutOfMemory;
   return on_stream_device(stream, [&] {
     void* ws = nullptr;
     const hipError_t serr = scratch_ptr(&ws);

@@ -29,6 +29,58 @@ __device__ __forceinline__ void store4b(T* p, float a, float b, float c, float d
   }
 }
 
+// ------------------------------------------------------------ split mode
+
+// Copy sg of n takes the sg-th of n contiguous, nearly equal shares of the
+// tile range [t0, t1] (an empty range when there are more copies than
+// tiles).
+__device__ __forceinline__ void split_share(int& t0, int& t1, int sg, int n) {
+  if (n <= 1) return;
+  const int len = t1 - t0 + 1, per = (len + n - 1) / n;
+  t0 += sg * per;
+  t1 = min(t1, t0 + per - 1);
+}
+
+// Unscaled fp32 dK and dV sums of this lane's key (partial-sum row prow of
+// copy sg): the accumulator layout of the dK/dV kernels (lane half g holds
+// columns 32 dt + 8 q4 + 4 g .. + 3).
+template <int D>
+__device__ __forceinline__ void store_partial_kv(float* part, long long rows_k, int split_kv, int H, int sg, int h,
+                                                 long long prow, const f32x16* dk, const f32x16* dv, int g) {
+  constexpr int DVT = (D + 31) / 32;
+  float* pk = part + ((long long)(sg * H + h) * rows_k + prow) * D;
+  float* pv = pk + (long long)split_kv * H * rows_k * D;
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * dt + 8 * q4 + 4 * g;
+      if (d < D) {
+        *reinterpret_cast<float4*>(pk + d) =
+            make_float4(dk[dt][4 * q4], dk[dt][4 * q4 + 1], dk[dt][4 * q4 + 2], dk[dt][4 * q4 + 3]);
+        *reinterpret_cast<float4*>(pv + d) =
+            make_float4(dv[dt][4 * q4], dv[dt][4 * q4 + 1], dv[dt][4 * q4 + 2], dv[dt][4 * q4 + 3]);
+      }
+    }
+}
+
+// The same for dQ (part_q: the dQ section).
+template <int D>
+__device__ __forceinline__ void store_partial_q(float* part_q, long long rows_q, int H, int sg, int h, long long prow,
+                                                const f32x16* dq, int g) {
+  constexpr int DVT = (D + 31) / 32;
+  float* pq = part_q + ((long long)(sg * H + h) * rows_q + prow) * D;
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * dt + 8 * q4 + 4 * g;
+      if (d < D)
+        *reinterpret_cast<float4*>(pq + d) =
+            make_float4(dq[dt][4 * q4], dq[dt][4 * q4 + 1], dq[dt][4 * q4 + 2], dq[dt][4 * q4 + 3]);
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ float dot_chunk(uint4 x, uint4 y) {
   if constexpr (sizeof(T) == 4) {
@@ -109,8 +161,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const int nkb = (int)(gridDim.x / (P.B * P.H));
-  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nkb, P.B * P.H, P.ragged);
+  const int nbh = P.B * P.H;
+  const int nkb = (int)(gridDim.x / ((unsigned)nbh * a.split_kv));
+  const int sg = (int)(blockIdx.x / (unsigned)(nkb * nbh));  // split copy (0 without split)
+  const GridPos gp = grid_pos((int)(blockIdx.x % (unsigned)(nkb * nbh)), nkb * nbh, nkb, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int kb = gp.i;
 
@@ -134,7 +188,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int jlast = min(j0 + BNK, sk) - 1;
   const long long ilo = max(0LL, (long long)j0 - w.hi);
   const long long ihi = min((long long)sq - 1, (long long)jlast - w.lo);
-  const bool block_empty = w.lo > w.hi || ilo > ihi;
+  int t0 = 0, t1 = -1;
+  if (w.lo <= w.hi && ilo <= ihi) {
+    t0 = (int)(ilo / BMQ);
+    t1 = (int)(ihi / BMQ);
+    split_share(t0, t1, sg, a.split_kv);
+  }
+  const bool block_empty = t0 > t1;
 
   const int jw0 = j0 + 32 * wave;
   const bool wave_live = jw0 < sk;
@@ -161,7 +221,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
 
   if (!block_empty) {
-    const int t0 = (int)(ilo / BMQ), t1 = (int)(ihi / BMQ);
     TileStage<T, BMQ, D, NT> qs, dos;
     float st_l = INFINITY, st_d = 0.f;  // this thread's LSE/Delta entry (tid < BMQ)
     auto load_tile = [&](int i0) {
@@ -250,7 +309,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  if (wave_live && kj < sk) {
+  if (wave_live && kj < sk && a.part) {
+    store_partial_kv<D>(a.part, a.rows_k, a.split_kv, P.H, sg, h, part_row(P.ks.mode, P.Sk, b, k0, kj), dk, dv, g);
+  } else if (wave_live && kj < sk) {
     T* dkrow = dkp + (long long)kj * a.dk.ss;
     T* dvrow = dvp + (long long)kj * a.dv.ss;
     const float sc = P.scale;
@@ -292,8 +353,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const int nq = (int)(gridDim.x / (P.B * P.H));
-  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.ragged);
+  const int nbh = P.B * P.H;
+  const int nq = (int)(gridDim.x / ((unsigned)nbh * a.split_q));
+  const int sg = (int)(blockIdx.x / (unsigned)(nq * nbh));  // split copy (0 without split)
+  const GridPos gp = grid_pos((int)(blockIdx.x % (unsigned)(nq * nbh)), nq * nbh, nq, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
@@ -322,6 +385,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     jhi = (long long)sk - 1;
     block_empty = sk == 0;
   }
+  int t0 = 0, t1 = -1;
+  if (!block_empty) {
+    t0 = (int)(jlo / BN);
+    t1 = (int)(jhi / BN);
+    split_share(t0, t1, sg, a.split_q);
+  }
+  block_empty = t0 > t1;
 
   const int iw0 = i0 + 32 * wave;
   const bool wave_live = iw0 < sq;
@@ -346,7 +416,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   for (int dt = 0; dt < DVT; ++dt) dq[dt] = zero16();
 
   if (!block_empty) {
-    const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
     TileStage<T, BN, D, NT> ks, vs;
     auto load_tile = [&](int j0) {
       ks.load(kp + (long long)j0 * a.k.ss, a.k.ss, sk - j0, tid);
@@ -435,7 +504,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  if (row_ok) {
+  if (row_ok && a.part) {
+    store_partial_q<D>(a.part + 2LL * a.split_kv * P.H * a.rows_k * D, a.rows_q, P.H, sg, h,
+                       part_row(P.qs.mode, P.Sq, b, q0, qi), dq, g);
+  } else if (row_ok) {
     T* dqrow = dqp + (long long)qi * a.dq.ss;
     const float sc = P.scale;
 #pragma unroll
@@ -607,8 +679,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const int nkb = (int)(gridDim.x / (P.B * P.H));
-  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nkb, P.B * P.H, P.ragged);
+  const int nbh = P.B * P.H;
+  const int nkb = (int)(gridDim.x / ((unsigned)nbh * a.split_kv));
+  const int sg = (int)(blockIdx.x / (unsigned)(nkb * nbh));  // split copy (0 without split)
+  const GridPos gp = grid_pos((int)(blockIdx.x % (unsigned)(nkb * nbh)), nkb * nbh, nkb, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int kb = gp.i;
 
@@ -632,7 +706,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int jlast = min(j0 + BNK, sk) - 1;
   const long long ilo = max(0LL, (long long)j0 - w.hi);
   const long long ihi = min((long long)sq - 1, (long long)jlast - w.lo);
-  const bool block_empty = w.lo > w.hi || ilo > ihi;
+  int t0 = 0, t1 = -1;
+  if (w.lo <= w.hi && ilo <= ihi) {
+    t0 = (int)(ilo / BMQ);
+    t1 = (int)(ihi / BMQ);
+    split_share(t0, t1, sg, a.split_kv);
+  }
+  const bool block_empty = t0 > t1;
 
   const int jw0 = j0 + 32 * wave;
   const bool wave_live = jw0 < sk;
@@ -673,7 +753,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       zero_unused_slots<T, D, BMQ, NT>(qs[u], tid);
       zero_unused_slots<T, D, BMQ, NT>(ds_[u], tid);
     }
-    const int t0 = (int)(ilo / BMQ), t1 = (int)(ihi / BMQ);
     // One tile's loads, all direct to LDS: its Q and dO rows and, per wave,
     // RW rows of LSE log2(e) and Delta (rows past the sequence repeat its
     // last row and are masked).
@@ -715,7 +794,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     }
   }
 
-  if (wave_live && kj < sk) {
+  if (wave_live && kj < sk && a.part) {
+    store_partial_kv<D>(a.part, a.rows_k, a.split_kv, P.H, sg, h, part_row(P.ks.mode, P.Sk, b, k0, kj), dk, dv, g);
+  } else if (wave_live && kj < sk) {
     T* dkrow = dkp + (long long)kj * a.dk.ss;
     T* dvrow = dvp + (long long)kj * a.dv.ss;
     const float sc = P.scale;
@@ -1346,8 +1427,10 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   const auto& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const int nq = nblk / (P.B * P.H);
-  const GridPos gp = grid_pos(hw, nblk, nq, P.B * P.H, P.ragged);
+  const int nbh = P.B * P.H;
+  const int nq = nblk / (nbh * a.split_q);
+  const int sg = hw / (nq * nbh);  // split copy (0 without split)
+  const GridPos gp = grid_pos(hw % (nq * nbh), nq * nbh, nq, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
@@ -1376,6 +1459,13 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
     jhi = (long long)sk - 1;
     block_empty = sk == 0;
   }
+  int t0 = 0, t1 = -1;
+  if (!block_empty) {
+    t0 = (int)(jlo / BN);
+    t1 = (int)(jhi / BN);
+    split_share(t0, t1, sg, a.split_q);
+  }
+  block_empty = t0 > t1;
 
   const int iw0 = i0 + 32 * wave;
   const bool wave_live = iw0 < sq;
@@ -1417,7 +1507,6 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
     zero_unused_slots<T, D, BN, NT>(k_s1, tid);
     zero_unused_slots<T, D, BN, NT>(v_s0, tid);
     zero_unused_slots<T, D, BN, NT>(v_s1, tid);
-    const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
     auto dma = [&](T* kb, T* vb, int t) __attribute__((always_inline)) {
       kd.issue(kb, kp + (long long)t * BN * a.k.ss, a.k.ss, sk - t * BN, wave, lane);
       vd.issue(vb, vp + (long long)t * BN * a.v.ss, a.v.ss, sk - t * BN, wave, lane);
@@ -1446,7 +1535,10 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
     }
   }
 
-  if (row_ok) {
+  if (row_ok && a.part) {
+    store_partial_q<D>(a.part + 2LL * a.split_kv * P.H * a.rows_k * D, a.rows_q, P.H, sg, h,
+                       part_row(P.qs.mode, P.Sq, b, q0, qi), dq, g);
+  } else if (row_ok) {
     T* dqrow = dqp + (long long)qi * a.dq.ss;
     const float sc = P.scale;
 #pragma unroll
@@ -1484,6 +1576,59 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     dq16_body<M, D, 8, 64>(hw - nkv, (int)gridDim.x - nkv);
 }
 
+// ------------------------------------------------------------ split reduce
+
+// Split-mode epilogue, one workgroup per (side, sequence, head, row slice):
+// each row of a sequence's length gets the sum of its partial rows in copy
+// order (so the result does not depend on the schedule), times the scale
+// for dQ and dK, rounded to the output type; rows of the sequence's room
+// past its length get zeros (as the padding kernel writes without split).
+// sides: 1 Q (dQ), 2 K (dK, dV), 3 both; the grid is
+// nsides * B * H * slices, Q side first.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, int sides, int slices) {
+  constexpr int V4 = D / 4, RPP = 256 / V4;  // float4 columns per row, rows per pass
+  static_assert(D % 4 == 0 && RPP >= 1, "row shape");
+  const int tid = threadIdx.x, ri = tid / V4, d = 4 * (tid % V4);
+  if (ri >= RPP) return;  // threads past the last whole row of a pass
+  const ProblemArgs& P = a.p;
+  const int nbh = P.B * P.H;
+  int blk = (int)blockIdx.x;
+  const int sl = blk % slices;
+  blk /= slices;
+  const int bh = blk % nbh;
+  const int side = (sides == 3) ? blk / nbh : (sides == 2 ? 1 : 0);  // 0: Q, 1: K
+  const int h = bh % P.H, b = bh / P.H;
+  const SideArgs& S = side ? P.ks : P.qs;
+  const SideRows r = side_rows(S, b);
+  const long long limit = r.room > r.n ? r.room : r.n;
+  const long long rows = side ? a.rows_k : a.rows_q;
+  const int groups = side ? a.split_kv : a.split_q;
+  const float* p0 = side ? a.part : a.part + 2LL * a.split_kv * P.H * a.rows_k * D;  // dK or dQ
+  const float* p1 = a.part + (long long)a.split_kv * P.H * a.rows_k * D;             // dV
+  const long long gstride = (long long)P.H * rows * D;
+  const Operand o0 = side ? a.dk : a.dq;
+  const float sc = P.scale;
+  for (long long i = (long long)sl * RPP + ri; i < limit; i += (long long)slices * RPP) {
+    float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+    if (i < r.n) {
+      const long long off = ((long long)h * rows + part_row(S.mode, S.S, b, r.r0, (int)i)) * D + d;
+      for (int g = 0; g < groups; ++g) {
+        const float4 x = *reinterpret_cast<const float4*>(p0 + g * gstride + off);
+        s0.x += x.x; s0.y += x.y; s0.z += x.z; s0.w += x.w;
+        if (side) {
+          const float4 y = *reinterpret_cast<const float4*>(p1 + g * gstride + off);
+          s1.x += y.x; s1.y += y.y; s1.z += y.z; s1.w += y.w;
+        }
+      }
+    }
+    const long long row = r.r0 + i;
+    store4b<T>((T*)o0.ptr + b * o0.sb + h * o0.sh + row * o0.ss + d, s0.x * sc, s0.y * sc, s0.z * sc, s0.w * sc);
+    if (side)
+      store4b<T>((T*)a.dv.ptr + b * a.dv.sb + h * a.dv.sh + row * a.dv.ss + d, s1.x, s1.y, s1.z, s1.w);
+  }
+}
+
 // ------------------------------------------------------------ launch
 
 // Workgroup shapes.  16-bit: dK/dV 4 waves (128 keys) over 64-row query
@@ -1519,6 +1664,49 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
                256u, a, nrows);
       if (err != hipSuccess) return err;
     }
+  }
+  // Split mode (the call's grids would leave most of the GPU idle): the
+  // plain dK/dV and dQ kernels over split copies of their grids, then one
+  // reduction, which also writes the rows past each length.
+  if (a.part) {
+    if (stages & kStageDkDv) {
+      const long long nblk = (a.p.Sk + NW_KV * 32 - 1) / (NW_KV * 32) * a.p.H * a.p.B * a.split_kv;
+      if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+      if (nblk > 0) {
+        if constexpr (S::k16)
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, (D > 80 ? 1 : 2)>),
+                   "attn_bwd_dkdv16_kernel", (unsigned)nblk, (unsigned)(NW_KV * 64), a);
+        else
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>), "attn_bwd_dkdv_kernel",
+                   (unsigned)nblk, (unsigned)(NW_KV * 64), a);
+        if (err != hipSuccess) return err;
+      }
+    }
+    if (stages & kStageDq) {
+      const long long nblk = (a.p.Sq + NW_Q * 32 - 1) / (NW_Q * 32) * a.p.H * a.p.B * a.split_q;
+      if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+      if (nblk > 0) {
+        if constexpr (S::k16)
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, 2>), "attn_bwd_dq16_kernel",
+                   (unsigned)nblk, (unsigned)(NW_Q * 64), a);
+        else
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN>), "attn_bwd_dq_kernel",
+                   (unsigned)nblk, (unsigned)(NW_Q * 64), a);
+        if (err != hipSuccess) return err;
+      }
+    }
+    const int sides = ((stages & kStageDq) ? 1 : 0) | ((stages & kStageDkDv) ? 2 : 0);
+    if (sides) {
+      constexpr int RPP = 256 / (D / 4);
+      const int rows = sides == 1 ? a.p.Sq : (sides == 2 ? a.p.Sk : max(a.p.Sq, a.p.Sk));
+      const int slices = max(1, min(64, (rows + RPP - 1) / RPP));
+      const long long nblk = (long long)(sides == 3 ? 2 : 1) * a.p.B * a.p.H * slices;
+      if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+      if (nblk > 0)
+        return ex(reinterpret_cast<const void*>(&attn_bwd_reduce_kernel<T, D>), "attn_bwd_reduce_kernel",
+                  (unsigned)nblk, 256u, a, sides, slices);
+    }
+    return hipSuccess;
   }
   // Bias, ALiBi, dropout or dbias: the kernels built with them (16-bit dK/dV
   // one wave per SIMD above head_dim 64, where their registers do not fit
@@ -1628,8 +1816,10 @@ static hipError_t launch_bwd_any(int dtype, int head_dim, const BwdArgs& a, int 
     case 2: err = launch_bwd_d<MmaBF16>(head_dim, a, stages, ex); break;
     default: return hipErrorNotSupported;
   }
-  // Rows of a sequence's room past its length: dQ, and dK / dV, are zero.
+  // Rows of a sequence's room past its length: dQ, and dK / dV, are zero
+  // (written by the reduction in split mode).
   const int esz = dtype == 0 ? 4 : 2, rb = head_dim * esz;
+  if (a.part) return err;
   if (err == hipSuccess && (stages & kStageDq)) err = launch_pad_rows(a.p, a.dq, Operand{}, nullptr, 0, rb, esz, ex);
   if (err == hipSuccess && (stages & kStageDkDv)) err = launch_pad_rows(a.p, a.dk, a.dv, nullptr, 1, rb, esz, ex);
   return err;

@@ -109,7 +109,23 @@ struct BwdArgs {
   float* lse2;   // workspace: LSE_i * log2(e) (written by the preprocess)
   FeatArgs f;
   int feat;
+  // Split mode (null part: off).  The dK/dV grid is repeated split_kv times,
+  // copy g walking its g-th share of the query tiles, and the dQ grid
+  // split_q times over the key tiles; each copy stores unscaled fp32 sums
+  // into part, and a reduction kernel adds them in copy order.  Layout, in
+  // rows of head_dim floats: dK [split_kv][H][rows_k], then dV likewise,
+  // then dQ [split_q][H][rows_q]; a row's index is its storage row (stacked
+  // side) or b * seqlen + local row (padded side).
+  float* part;
+  long long rows_q, rows_k;
+  int split_kv, split_q;
 };
+
+// Partial-sum row of local row i of sequence b on a side of the given mode
+// and seqlen S whose sequence starts at storage row r0.
+__host__ __device__ __forceinline__ long long part_row(int mode, int S, int b, long long r0, int i) {
+  return (mode & kSeqStacked) ? r0 + i : (long long)b * S + i;
+}
 
 // Steps of the backward, as a bit mask of `stages`; they run in this order.
 constexpr int kStageDelta = 1, kStageDkDv = 2, kStageDq = 4, kStageAll = 7;

@@ -90,12 +90,12 @@ class Case:
 
     def __init__(self, *, layout="bhsd", B=1, H=2, Sq=64, Sk=None, D=64, dtype=torch.bfloat16,
                  window=(INF, INF), diag="top_left", scale=None, seed=0, lens_q=None, lens_k=None,
-                 bshd=False):
+                 bshd=False, split=True):
         self.layout, self.B, self.H, self.D, self.dtype = layout, B, H, D, dtype
         self.Sq, self.Sk = Sq, (Sq if Sk is None else Sk)
         self.window, self.diag = window, diag
         self.scale = 1.0 / math.sqrt(D) if scale is None else scale
-        self.seed, self.bshd = seed, bshd
+        self.seed, self.bshd, self.split = seed, bshd, split
         if layout == "thd":
             self.lens_q, self.lens_k = list(lens_q), list(lens_k)
             self.cu_q, self.cu_k = wl.prefix(self.lens_q), wl.prefix(self.lens_k)
@@ -133,7 +133,7 @@ class Case:
         return kw
 
     def kw_gpu(self, dev):
-        kw = dict(scale=self.scale, window=self.window, diag=self.diag)
+        kw = dict(scale=self.scale, window=self.window, diag=self.diag, split=self.split)
         if self.layout == "thd":
             kw.update(cu_seqlens_q=torch.from_numpy(self.cu_q).to(dev),
                       cu_seqlens_k=torch.from_numpy(self.cu_k).to(dev),
@@ -163,7 +163,8 @@ class Case:
 
     def check(self, bwd=True, dev="cuda"):
         say(f"case layout={self.layout} B={self.B} H={self.H} Sq={self.Sq} Sk={self.Sk} D={self.D} "
-            f"dtype={self.dtype} window={self.window} diag={self.diag} scale={self.scale} seed={self.seed}")
+            f"dtype={self.dtype} window={self.window} diag={self.diag} scale={self.scale} seed={self.seed} "
+            f"split={self.split}")
         got = self.gpu(dev, bwd)
         ref = self.oracle(bwd)
         base = TOL[self.dtype]

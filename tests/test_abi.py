@@ -139,7 +139,8 @@ def test_valid_calls_pass():
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("version", 1, INVALID), ("version", 4, INVALID), ("flags", 1, INVALID), ("reserved0", 3, INVALID),
+    ("version", 1, INVALID), ("version", 4, INVALID), ("flags", 1, INVALID), ("flags", 4, INVALID),
+    ("flags", 3, INVALID), ("reserved0", 3, INVALID),
     ("reserved1", 1, INVALID), ("varlen", 1, INVALID), ("seqstart_q", BASE, INVALID),
     ("dtype", 7, INVALID), ("layout", 5, INVALID), ("diag", 2, INVALID),
     ("heads", 0, INVALID), ("head_dim", 0, INVALID), ("seqlen_q", -1, INVALID),
@@ -282,28 +283,81 @@ def test_bwd_validation_errors():
     assert bcheck(p) == NOTSUP
 
 
+def split_bytes(f):
+    """Partial-sum bytes of the backward's split mode, from its documented
+    rule: split when the dK/dV or the dQ grid (128 rows per workgroup) has
+    fewer than 64 workgroups; copies = min(ceil(256 / workgroups), 8, tiles
+    of the split axis (64 rows, 32 in fp32)); fp32 partials of dK, dV (per
+    key copy) and dQ (per query copy), capped at 8 MiB by dropping copies
+    from the larger count; 0 when no copy is left to split."""
+    if f.flags & bd.FLAG_NO_SPLIT:
+        return 0
+    B, H, D, Sq, Sk = f.batch, f.heads, f.head_dim, f.seqlen_q, f.seqlen_k
+    nkv, nq = B * H * -(-Sk // 128), B * H * -(-Sq // 128)
+    if nkv == 0 or nq == 0 or (nkv >= 64 and nq >= 64):
+        return 0
+    tile = 32 if f.dtype == bd.FP32 else 64
+    gkv = max(1, min(-(-256 // nkv), 8, -(-Sq // tile)))
+    gq = max(1, min(-(-256 // nq), 8, -(-Sk // tile)))
+    rq = f.total_q if f.layout == bd.THD else B * Sq
+    rk = f.total_k if f.layout == bd.THD else B * Sk
+    nbytes = lambda: 4 * D * H * (2 * gkv * rk + gq * rq)
+    while nbytes() > 8 << 20 and (gkv > 1 or gq > 1):
+        if gkv >= gq:
+            gkv -= 1
+        else:
+            gq -= 1
+    if nbytes() > 8 << 20 or (gkv == 1 and gq == 1):
+        return 0
+    return -(-nbytes() // 256) * 256
+
+
 def test_workspace_size():
+    """Delta and LSE log2(e) (one fp32 section each, 256-byte rounded), plus
+    the split mode's partial sums where the call takes it."""
+    lib = bd.lib()
     f = dense_params(B=2, H=3, S=100)
-    p = bwd_params(f)
-    assert bd.lib().attn_bwd_workspace_size(ctypes.byref(p)) == 2 * (((2 * 3 * 100 * 4 + 255) // 256) * 256)
-    pk = bwd_params(packed_params(total_q=100, H=2))
-    assert bd.lib().attn_bwd_workspace_size(ctypes.byref(pk)) == 2 * 1024
+    delta = 2 * (((2 * 3 * 100 * 4 + 255) // 256) * 256)
+    assert split_bytes(f) == 4 * 64 * 3 * (2 * 2 * 200 + 2 * 200)
+    assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f))) == delta + split_bytes(f)
+    f.flags = bd.FLAG_NO_SPLIT
+    assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f))) == delta
+    fk = packed_params(total_q=100, H=2)
+    assert split_bytes(fk) > 0
+    assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(fk))) == 2 * 1024 + split_bytes(fk)
+    big = dense_params(B=8, H=16, S=1024)                  # grids fill the GPU: no split
+    assert split_bytes(big) == 0
+    assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(big))) == 2 * 8 * 16 * 1024 * 4
+    for B, H, S, D, dt in ((1, 2, 128, 64, bd.FP32), (1, 1, 4000, 128, bd.BF16), (3, 5, 700, 80, bd.FP16),
+                           (1, 8, 1023, 128, bd.BF16), (2, 1, 8000, 64, bd.FP32)):
+        f = dense_params(B=B, H=H, S=S, D=D, dtype=dt)
+        stat = ((B * H * S * 4 + 255) // 256) * 256
+        assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f))) == 2 * stat + split_bytes(f), (B, H, S, D)
+    feat = dense_params(B=1, H=2, S=128)
+    feat.dropout_p = 0.5                                   # optional features: never split
+    assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(feat))) == 2 * (((2 * 128 * 4 + 255) // 256) * 256)
     bad = bwd_params(dense_params())
     bad.fwd.version = 9
-    assert bd.lib().attn_bwd_workspace_size(ctypes.byref(bad)) == 0
+    assert lib.attn_bwd_workspace_size(ctypes.byref(bad)) == 0
 
 
 def test_lse_th_flag():
-    """ATTN_FLAG_LSE_TH is accepted for the packed layout only; other flag
-    bits stay reserved.  The binding's value is the header's."""
+    """ATTN_FLAG_LSE_TH is accepted for the packed layout only,
+    ATTN_FLAG_NO_SPLIT for any; other flag bits stay reserved.  The
+    binding's values are the header's."""
     hdr = open(os.path.join(ROOT, "include", "attn.h")).read()
     assert int(re.search(r"#define ATTN_FLAG_LSE_TH (\d+)u", hdr).group(1)) == bd.FLAG_LSE_TH
+    assert int(re.search(r"#define ATTN_FLAG_NO_SPLIT (\d+)u", hdr).group(1)) == bd.FLAG_NO_SPLIT
     p = packed_params()
     p.flags = bd.FLAG_LSE_TH
     assert fcheck(p) == OK
     assert bcheck(bwd_params(p)) == OK
-    p.flags = 2
-    assert fcheck(p) == INVALID
+    p.flags = bd.FLAG_LSE_TH | bd.FLAG_NO_SPLIT
+    assert fcheck(p) == OK
+    assert bcheck(bwd_params(p)) == OK
+    for bit in range(2, 32):
+        p.flags = 1 << bit
+        assert fcheck(p) == INVALID
     p = dense_params()
     p.flags = bd.FLAG_LSE_TH
     assert fcheck(p) == INVALID

@@ -26,25 +26,33 @@ WINDOWS = [
 SHAPES = [(1, 1), (17, 17), (63, 65), (64, 64), (127, 129), (129, 127), (300, 200), (200, 300)]
 
 
+# Small problems take the backward's split mode by default; each of these
+# sweeps also runs with it switched off, so both paths see every window.
+SPLIT = [True, False]
+
+
+@pytest.mark.parametrize("split", SPLIT)
 @pytest.mark.parametrize("D", [64, 80, 128])
 @pytest.mark.parametrize("sq,sk", SHAPES)
-def test_dense_bf16_windows(D, sq, sk):
+def test_dense_bf16_windows(D, sq, sk, split):
     for i, (window, diag) in enumerate(WINDOWS):
-        Case(B=2, H=2, Sq=sq, Sk=sk, D=D, window=window, diag=diag, seed=100 + i).check()
+        Case(B=2, H=2, Sq=sq, Sk=sk, D=D, window=window, diag=diag, seed=100 + i, split=split).check()
 
 
+@pytest.mark.parametrize("split", SPLIT)
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
 @pytest.mark.parametrize("D", [64, 80, 128])
-def test_dense_other_dtypes(dtype, D):
+def test_dense_other_dtypes(dtype, D, split):
     for i, (sq, sk) in enumerate([(65, 65), (130, 97)]):
         for j, (window, diag) in enumerate(WINDOWS[:5]):
             Case(B=1, H=3, Sq=sq, Sk=sk, D=D, dtype=dtype, window=window, diag=diag,
-                 seed=200 + 10 * i + j).check()
+                 seed=200 + 10 * i + j, split=split).check()
 
 
+@pytest.mark.parametrize("split", SPLIT)
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("D", [32, 48, 96])
-def test_more_head_dims(dtype, D):
+def test_more_head_dims(dtype, D, split):
     """Head dims 32, 48 and 96: dense problems spanning several tiles with
     ragged ends, under the no-mask, causal, numeric and empty windows, and a
     packed one with empty sequences."""
@@ -52,9 +60,9 @@ def test_more_head_dims(dtype, D):
         for j, (window, diag) in enumerate([((INF, INF), "top_left"), ((INF, 0), "bottom_right"),
                                             ((40, 7), "bottom_right"), ((-3, 1), "top_left")]):
             Case(B=2, H=2, Sq=sq, Sk=sk, D=D, dtype=dtype, window=window, diag=diag,
-                 seed=900 + 10 * i + j).check()
+                 seed=900 + 10 * i + j, split=split).check()
     Case(layout="thd", H=2, D=D, dtype=dtype, window=(64, 0), diag="bottom_right",
-         lens_q=[100, 0, 37, 260], lens_k=[150, 10, 37, 300], seed=950).check()
+         lens_q=[100, 0, 37, 260], lens_k=[150, 10, 37, 300], seed=950, split=split).check()
 
 
 def test_tiny_fp32_config():
@@ -62,14 +70,43 @@ def test_tiny_fp32_config():
     Case(B=1, H=2, Sq=128, D=64, dtype=torch.float32, scale=0.125, seed=1).check()
 
 
+@pytest.mark.parametrize("dtype,D,B,H,S", [(torch.float32, 64, 1, 2, 128), (torch.bfloat16, 128, 1, 4, 1000),
+                                           (torch.float16, 80, 2, 3, 300)])
+def test_split_mode_plan_and_bits(dtype, D, B, H, S):
+    """Small problems run the backward in split mode: the plan lists the
+    split grids and the reduction, the workspace holds the partial sums, and
+    the results are run-to-run identical and within the oracle's bounds,
+    next to the unsplit path's."""
+    c = Case(B=B, H=H, Sq=S, D=D, dtype=dtype, seed=15)
+    q, k, v, do = (t.cuda() for t in c.cpu)
+    o, lse = bd.attn_fwd(q, k, v, scale=c.scale)
+    p, _ = bd.prepare_bwd(do, q, k, v, o, lse, scale=c.scale)
+    names = [n for n, _, _ in bd.plan("attn_bwd", p)]
+    assert names[-1] == "attn_bwd_reduce_kernel" and len(names) == 4, names
+    p0, _ = bd.prepare_bwd(do, q, k, v, o, lse, scale=c.scale, split=False)
+    assert "attn_bwd_reduce_kernel" not in [n for n, _, _ in bd.plan("attn_bwd", p0)]
+    ws = bd.workspace_size(do, q, k, v, o, lse, scale=c.scale)
+    ws0 = bd.workspace_size(do, q, k, v, o, lse, scale=c.scale, split=False)
+    assert ws > ws0
+    a = bd.attn_bwd(do, q, k, v, o, lse, scale=c.scale)
+    b = bd.attn_bwd(do, q, k, v, o, lse, scale=c.scale)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    c.check()
+    Case(B=B, H=H, Sq=S, D=D, dtype=dtype, seed=15, split=False).check()
+
+
 @pytest.mark.parametrize("D", [80, 128])
 @pytest.mark.parametrize("window,diag", [((5, 0), "bottom_right"), ((INF, 0), "top_left"),
                                          ((INF, INF), "top_left"), ((1 << 30, 0), "bottom_right"),
                                          ((0, 0), "top_left")])
-def test_packed_varlen(D, window, diag):
+@pytest.mark.parametrize("split", SPLIT)
+def test_packed_varlen(D, window, diag, split):
     lens_q = [37, 0, 130, 1, 64, 5, 200]
     lens_k = [50, 3, 129, 0, 64, 70, 260]
-    Case(layout="thd", H=3, D=D, window=window, diag=diag, lens_q=lens_q, lens_k=lens_k, seed=7).check()
+    Case(layout="thd", H=3, D=D, window=window, diag=diag, lens_q=lens_q, lens_k=lens_k, seed=7,
+         split=split).check()
 
 
 def test_packed_varlen_fp16():
@@ -356,18 +393,30 @@ def wl_prefix(lengths):
     (torch.float32, 80, (INF, 0), "top_left"),
     (torch.bfloat16, 48, (1 << 30, 3), "bottom_right"),
 ])
-def test_seqused_rows(layout, dtype, D, window, diag):
+@pytest.mark.parametrize("split", SPLIT)
+def test_seqused_rows(layout, dtype, D, window, diag, split):
     """seqused_q / seqused_k: sequence b computes on its first used rows only
-    (bottom-right windows shift by the used lengths), bit for bit as the
-    compact packed problem of those rows, which matches the oracle; rows
-    past them (NaN in the inputs) come out as fully masked rows: O = 0,
-    LSE = +inf, dQ = dK = dV = 0."""
+    (bottom-right windows shift by the used lengths), as the compact packed
+    problem of those rows, which matches the oracle: bit for bit, except for
+    the gradients in the backward's split mode, whose partial sums group the
+    tiles by the grid (which differs between the two layouts) and so are
+    held to the gradients' bound instead.  Rows past the used ones (NaN in
+    the inputs) come out as fully masked rows: O = 0, LSE = +inf, dQ = dK =
+    dV = 0."""
     c, comp, full, kw, (uq, uk, aq, ak) = _used_rows_case(layout, dtype, D, window, diag, seed=970)
+    c.split = split
+    kw["split"] = split
     dev = "cuda"
     o_c, l_c = bd.attn_fwd(*comp[:3], **c.kw_gpu(dev))
     g_c = bd.attn_bwd(comp[3], *comp[:3], o_c, l_c, **c.kw_gpu(dev))
     o_f, l_f = bd.attn_fwd(*full[:3], **kw)
     g_f = bd.attn_bwd(full[3], *full[:3], o_f, l_f, **kw)
+
+    def same_grad(name, got, want):
+        if split:
+            max_err(name, got, want.double().cpu().numpy(), 2 * TOL[dtype] * c.tol_factor())
+        else:
+            assert torch.equal(got, want), name
     H = comp[0].shape[1]
     sq_c = sk_c = sq_f = sk_f = 0
     for b in range(len(uq)):
@@ -380,11 +429,11 @@ def test_seqused_rows(layout, dtype, D, window, diag):
         assert torch.equal(lf[:, :uq[b]], l_c[:, sq_c:sq_c + uq[b]]), ("lse", b)
         assert bool(torch.all(lf[:, uq[b]:] == float("inf"))), ("lse pad", b)
         dqf = rows_f(g_f[0], sq_f, b, uq[b], aq[b])
-        assert torch.equal(dqf[:uq[b]], g_c[0][sq_c:sq_c + uq[b]]), ("dq", b)
+        same_grad(f"dq {b}", dqf[:uq[b]], g_c[0][sq_c:sq_c + uq[b]])
         assert torch.count_nonzero(dqf[uq[b]:]) == 0, ("dq pad", b)
         for name, gf, gc in (("dk", g_f[1], g_c[1]), ("dv", g_f[2], g_c[2])):
             kf = rows_f(gf, sk_f, b, uk[b], ak[b])
-            assert torch.equal(kf[:uk[b]], gc[sk_c:sk_c + uk[b]]), (name, b)
+            same_grad(f"{name} {b}", kf[:uk[b]], gc[sk_c:sk_c + uk[b]])
             assert torch.count_nonzero(kf[uk[b]:]) == 0, (name + " pad", b)
         sq_c += uq[b]
         sk_c += uk[b]
