@@ -69,6 +69,7 @@ class _Problem(ctypes.Structure):
         ("philox_offset", ctypes.c_uint64),
         ("max_seqlen_q", ctypes.c_int),
         ("max_seqlen_k", ctypes.c_int),
+        ("head_dim_v", ctypes.c_int),
     ]
 
 
@@ -192,8 +193,14 @@ class _Call:
         else:
             p.max_seqlen_q = p.seqlen_q if max_seqlen_q is None else int(max_seqlen_q)
             p.max_seqlen_k = p.seqlen_k if max_seqlen_k is None else int(max_seqlen_k)
+        if v.shape[:-1] != k.shape[:-1] or (dout is not None and dout.shape[:-1] != q.shape[:-1]):
+            raise ValueError("v must match k, and dout q, in every dim but the last")
+        if dout is not None and dout.shape[-1] != v.shape[-1]:
+            raise ValueError("dout has v's head dim")
+        p.head_dim_v = v.shape[-1]
         self.p = p
-        self.D = p.head_dim
+        self.D, self.DV = p.head_dim, p.head_dim_v
+        self.o_shape = tuple(q.shape[:-1]) + (self.DV,)
 
     def ptr(self, i):
         return ctypes.c_void_p(self.keep[i].data_ptr())
@@ -211,7 +218,7 @@ def fwd(q, k, v, *, scale, window=(WINDOW_INF, WINDOW_INF), diag="top_left",
         cu_seqlens_q=None, cu_seqlens_k=None, **feat):
     """O and LSE of the whole problem (float64)."""
     c = _Call(q, k, v, None, window, diag, scale, cu_seqlens_q, cu_seqlens_k, **feat)
-    o = np.zeros(tuple(q.shape), dtype=np.float64)
+    o = np.zeros(c.o_shape, dtype=np.float64)
     lse = np.zeros(c.lse_shape, dtype=np.float64)
     rc = _load().oracle_fwd(ctypes.byref(c.p), c.ptr(0), c.ptr(1), c.ptr(2), _dptr(o), _dptr(lse))
     if rc:
@@ -225,7 +232,7 @@ def bwd(q, k, v, dout, *, scale, window=(WINDOW_INF, WINDOW_INF), diag="top_left
     ``want_dbias`` also dBias = d loss / d logits, [B, H, max_seqlen_q,
     max_seqlen_k] (0 where the sequence has no pair)."""
     c = _Call(q, k, v, dout, window, diag, scale, cu_seqlens_q, cu_seqlens_k, **feat)
-    o = np.zeros(tuple(q.shape), dtype=np.float64)
+    o = np.zeros(c.o_shape, dtype=np.float64)
     lse = np.zeros(c.lse_shape, dtype=np.float64)
     dq = np.zeros(tuple(q.shape), dtype=np.float64)
     dk = np.zeros(tuple(k.shape), dtype=np.float64)
@@ -242,10 +249,11 @@ def bwd(q, k, v, dout, *, scale, window=(WINDOW_INF, WINDOW_INF), diag="top_left
 
 def fwd_rows(q, k, v, b, h, rows, *, scale, window=(WINDOW_INF, WINDOW_INF),
              diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None, **feat):
-    """O rows [n, D] and LSE [n] for sequence-local query rows of (b, h)."""
+    """O rows [n, DV] (V's head dim) and LSE [n] for sequence-local query
+    rows of (b, h)."""
     c = _Call(q, k, v, None, window, diag, scale, cu_seqlens_q, cu_seqlens_k, **feat)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
-    o = np.zeros((len(rows), c.D), dtype=np.float64)
+    o = np.zeros((len(rows), c.DV), dtype=np.float64)
     lse = np.zeros(len(rows), dtype=np.float64)
     rc = _load().oracle_fwd_rows(ctypes.byref(c.p), c.ptr(0), c.ptr(1), c.ptr(2), int(b), int(h),
                                  len(rows), _iptr(rows), _dptr(o), _dptr(lse))
@@ -269,11 +277,12 @@ def bwd_dq_rows(q, k, v, dout, b, h, rows, *, scale, window=(WINDOW_INF, WINDOW_
 
 def bwd_dkdv_cols(q, k, v, dout, b, h, cols, *, scale, window=(WINDOW_INF, WINDOW_INF),
                   diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None, **feat):
-    """dK and dV rows [n, D] for sequence-local key rows of (b, h)."""
+    """dK rows [n, D] and dV rows [n, DV] for sequence-local key rows of
+    (b, h)."""
     c = _Call(q, k, v, dout, window, diag, scale, cu_seqlens_q, cu_seqlens_k, **feat)
     cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int32))
     dk = np.zeros((len(cols), c.D), dtype=np.float64)
-    dv = np.zeros((len(cols), c.D), dtype=np.float64)
+    dv = np.zeros((len(cols), c.DV), dtype=np.float64)
     rc = _load().oracle_bwd_dkdv_cols(ctypes.byref(c.p), c.ptr(0), c.ptr(1), c.ptr(2), c.ptr(3),
                                       int(b), int(h), len(cols), _iptr(cols), _dptr(dk), _dptr(dv))
     if rc:

@@ -174,7 +174,7 @@ typedef struct {
 } seq_span;
 
 static int check_problem(const oracle_problem *p) {
-  if (!p || p->batch < 0 || p->heads <= 0 || p->head_dim <= 0) return -1;
+  if (!p || p->batch < 0 || p->heads <= 0 || p->head_dim <= 0 || p->head_dim_v < 0) return -1;
   if (p->dtype < ORACLE_F32 || p->dtype > ORACLE_BF16) return -1;
   if (p->diag != ORACLE_TOP_LEFT && p->diag != ORACLE_BOTTOM_RIGHT) return -1;
   if (!(p->dropout_p >= 0.0 && p->dropout_p < 1.0)) return -1;
@@ -209,10 +209,14 @@ static seq_span span_of(const oracle_problem *p, int b) {
   return s;
 }
 
-/* Flat element index of (sequence b, head h, local row r, dim d). */
+/* Head dim of V, O, dO and dV: head_dim_v, or head_dim when it is 0. */
+static int dim_v(const oracle_problem *p) { return p->head_dim_v > 0 ? p->head_dim_v : p->head_dim; }
+
+/* Flat element index of (sequence b, head h, local row r, dim d) in a
+ * tensor whose rows hold D values. */
 static int64_t elem_index(const oracle_problem *p, int b, int h, int64_t row0,
-                          int64_t r, int64_t seqlen, int d) {
-  int64_t H = p->heads, D = p->head_dim;
+                          int64_t r, int64_t seqlen, int64_t D, int d) {
+  int64_t H = p->heads;
   if (p->layout == ORACLE_DENSE)
     return (((int64_t)b * H + h) * seqlen + r) * D + d;
   return ((row0 + r) * H + h) * D + d;
@@ -225,14 +229,14 @@ static int64_t lse_index(const oracle_problem *p, int b, int h, int64_t i) {
   return (int64_t)h * p->cu_seqlens_q[p->batch] + p->cu_seqlens_q[b] + i;
 }
 
-/* Decode rows [0, n) of one (b, h) slice into a dense fp64 [n][D] array. */
+/* Decode rows [0, n) of one (b, h) slice of a tensor with D values per row
+ * into a dense fp64 [n][D] array. */
 static void load_slice(const oracle_problem *p, const void *src, int b, int h,
-                       int64_t row0, int64_t n, double *dst) {
-  int D = p->head_dim;
+                       int64_t row0, int64_t n, int D, double *dst) {
   for (int64_t r = 0; r < n; ++r)
     for (int d = 0; d < D; ++d)
       dst[r * D + d] =
-          decode_at(p->dtype, src, elem_index(p, b, h, row0, r, n, d));
+          decode_at(p->dtype, src, elem_index(p, b, h, row0, r, n, D, d));
 }
 
 static double dot(const double *a, const double *b, int n) {
@@ -284,7 +288,7 @@ static int visible_in(const oracle_problem *p, const slice *sl, int64_t i, int64
  */
 static void row_forward(const oracle_problem *p, const slice *sl, int64_t i, double *s, double *o_row,
                         double *lse_out) {
-  int D = p->head_dim;
+  int D = dim_v(p);
   int64_t sk = sl->sp.sk;
   double m = -INFINITY;
   for (int64_t j = 0; j < sk; ++j) {
@@ -322,21 +326,21 @@ static double prob(const oracle_problem *p, const slice *sl, int64_t i, int64_t 
 static int slice_load(const oracle_problem *p, const void *q, const void *k,
                       const void *v, const void *dout, int b, int h,
                       slice *sl) {
-  int D = p->head_dim;
+  int D = p->head_dim, DV = dim_v(p);
   sl->sp = span_of(p, b);
   sl->b = b;
   sl->h = h;
   int64_t sq = sl->sp.sq, sk = sl->sp.sk;
   sl->Q = (double *)malloc(sizeof(double) * (size_t)(sq * D + 1));
   sl->K = (double *)malloc(sizeof(double) * (size_t)(sk * D + 1));
-  sl->V = (double *)malloc(sizeof(double) * (size_t)(sk * D + 1));
-  sl->dO = dout ? (double *)malloc(sizeof(double) * (size_t)(sq * D + 1))
+  sl->V = (double *)malloc(sizeof(double) * (size_t)(sk * DV + 1));
+  sl->dO = dout ? (double *)malloc(sizeof(double) * (size_t)(sq * DV + 1))
                 : NULL;
   if (!sl->Q || !sl->K || !sl->V || (dout && !sl->dO)) return -1;
-  load_slice(p, q, b, h, sl->sp.q0, sq, sl->Q);
-  load_slice(p, k, b, h, sl->sp.k0, sk, sl->K);
-  load_slice(p, v, b, h, sl->sp.k0, sk, sl->V);
-  if (dout) load_slice(p, dout, b, h, sl->sp.q0, sq, sl->dO);
+  load_slice(p, q, b, h, sl->sp.q0, sq, D, sl->Q);
+  load_slice(p, k, b, h, sl->sp.k0, sk, D, sl->K);
+  load_slice(p, v, b, h, sl->sp.k0, sk, DV, sl->V);
+  if (dout) load_slice(p, dout, b, h, sl->sp.q0, sq, DV, sl->dO);
   return 0;
 }
 
@@ -344,7 +348,7 @@ static void slice_free(slice *sl) {
   free(sl->Q); free(sl->K); free(sl->V); free(sl->dO);
 }
 
-/* Forward over all rows of a slice into dense [sq][D] / [sq] fp64 arrays. */
+/* Forward over all rows of a slice into dense [sq][DV] / [sq] fp64 arrays. */
 static int slice_forward(const oracle_problem *p, const slice *sl,
                          double *O, double *lse) {
   int64_t sq = sl->sp.sq, sk = sl->sp.sk;
@@ -359,7 +363,7 @@ static int slice_forward(const oracle_problem *p, const slice *sl,
 #pragma omp for schedule(dynamic, 8)
     for (int64_t i = 0; i < sq; ++i)
       if (s)
-        row_forward(p, sl, i, s, O + i * p->head_dim, lse + i);
+        row_forward(p, sl, i, s, O + i * dim_v(p), lse + i);
     free(s);
   }
   return fail ? -1 : 0;
@@ -370,19 +374,19 @@ static int slice_forward(const oracle_problem *p, const slice *sl,
 int oracle_fwd(const oracle_problem *p, const void *q, const void *k,
                const void *v, double *o, double *lse) {
   if (check_problem(p)) return -1;
-  int D = p->head_dim;
+  int DV = dim_v(p);
   for (int b = 0; b < p->batch; ++b)
     for (int h = 0; h < p->heads; ++h) {
       slice sl;
       if (slice_load(p, q, k, v, NULL, b, h, &sl)) { slice_free(&sl); return -1; }
       int64_t sq = sl.sp.sq;
-      double *O = (double *)malloc(sizeof(double) * (size_t)(sq * D + 1));
+      double *O = (double *)malloc(sizeof(double) * (size_t)(sq * DV + 1));
       double *L = (double *)malloc(sizeof(double) * (size_t)(sq + 1));
       int rc = (O && L) ? slice_forward(p, &sl, O, L) : -1;
       if (!rc)
         for (int64_t i = 0; i < sq; ++i) {
-          for (int d = 0; d < D; ++d)
-            o[elem_index(p, b, h, sl.sp.q0, i, sq, d)] = O[i * D + d];
+          for (int d = 0; d < DV; ++d)
+            o[elem_index(p, b, h, sl.sp.q0, i, sq, DV, d)] = O[i * DV + d];
           lse[lse_index(p, b, h, i)] = L[i];
         }
       free(O); free(L); slice_free(&sl);
@@ -409,7 +413,7 @@ int oracle_fwd_rows(const oracle_problem *p, const void *q, const void *k,
 #pragma omp for schedule(dynamic, 1)
       for (int r = 0; r < nrows; ++r)
         if (s)
-          row_forward(p, &sl, rows[r], s, o_rows + (int64_t)r * p->head_dim, lse_rows + r);
+          row_forward(p, &sl, rows[r], s, o_rows + (int64_t)r * dim_v(p), lse_rows + r);
       if (!s) {
 #pragma omp atomic write
         bad = 1;
@@ -436,8 +440,8 @@ int oracle_fwd_rows(const oracle_problem *p, const void *q, const void *k,
  * contribute nothing; keys seen by no row get dK = dV = 0.
  */
 static double dlogit(const oracle_problem *p, const slice *sl, int64_t i, int64_t j, double pij, double delta_i) {
-  int D = p->head_dim;
-  double g = dot(sl->dO + i * D, sl->V + j * D, D);
+  int DV = dim_v(p);
+  double g = dot(sl->dO + i * DV, sl->V + j * DV, DV);
   return pij * (dropout_scale(p, sl->b, sl->h, i, j) * g - delta_i);
 }
 
@@ -457,28 +461,27 @@ static void row_dq(const oracle_problem *p, const slice *sl, int64_t i,
 static void col_dkdv(const oracle_problem *p, const slice *sl, int64_t j,
                      const double *lse, const double *delta, double *dk_row,
                      double *dv_row) {
-  int D = p->head_dim;
+  int D = p->head_dim, DV = dim_v(p);
   int64_t sq = sl->sp.sq;
-  for (int d = 0; d < D; ++d) dk_row[d] = dv_row[d] = 0.0;
+  for (int d = 0; d < D; ++d) dk_row[d] = 0.0;
+  for (int d = 0; d < DV; ++d) dv_row[d] = 0.0;
   for (int64_t i = 0; i < sq; ++i) {
     double pij = prob(p, sl, i, j, lse[i]);
     if (pij == 0.0) continue;
     double ds = dlogit(p, sl, i, j, pij, delta[i]);
     double pm = pij * dropout_scale(p, sl->b, sl->h, i, j);
-    for (int d = 0; d < D; ++d) {
-      dk_row[d] += p->scale * ds * sl->Q[i * D + d];
-      dv_row[d] += pm * sl->dO[i * D + d];
-    }
+    for (int d = 0; d < D; ++d) dk_row[d] += p->scale * ds * sl->Q[i * D + d];
+    for (int d = 0; d < DV; ++d) dv_row[d] += pm * sl->dO[i * DV + d];
   }
 }
 
 /* Row statistics (O, LSE, Delta) of a whole slice. */
 static int slice_stats(const oracle_problem *p, const slice *sl, double *O,
                        double *lse, double *delta) {
-  int D = p->head_dim;
+  int DV = dim_v(p);
   if (slice_forward(p, sl, O, lse)) return -1;
   for (int64_t i = 0; i < sl->sp.sq; ++i)
-    delta[i] = dot(sl->dO + i * D, O + i * D, D);
+    delta[i] = dot(sl->dO + i * DV, O + i * DV, DV);
   return 0;
 }
 
@@ -492,19 +495,19 @@ int oracle_bwd_dbias(const oracle_problem *p, const void *q, const void *k,
                      const void *v, const void *dout, double *o, double *lse,
                      double *dq, double *dk, double *dv, double *dbias) {
   if (check_problem(p)) return -1;
-  int D = p->head_dim;
+  int D = p->head_dim, DV = dim_v(p);
   const int64_t sqm = max_len(p, 1), skm = max_len(p, 0);
   for (int b = 0; b < p->batch; ++b)
     for (int h = 0; h < p->heads; ++h) {
       slice sl;
       if (slice_load(p, q, k, v, dout, b, h, &sl)) { slice_free(&sl); return -1; }
       int64_t sq = sl.sp.sq, sk = sl.sp.sk;
-      double *O = (double *)malloc(sizeof(double) * (size_t)(sq * D + 1));
+      double *O = (double *)malloc(sizeof(double) * (size_t)(sq * DV + 1));
       double *L = (double *)malloc(sizeof(double) * (size_t)(sq + 1));
       double *De = (double *)malloc(sizeof(double) * (size_t)(sq + 1));
       double *dQ = (double *)malloc(sizeof(double) * (size_t)(sq * D + 1));
       double *dK = (double *)malloc(sizeof(double) * (size_t)(sk * D + 1));
-      double *dV = (double *)malloc(sizeof(double) * (size_t)(sk * D + 1));
+      double *dV = (double *)malloc(sizeof(double) * (size_t)(sk * DV + 1));
       int rc = (O && L && De && dQ && dK && dV) ? slice_stats(p, &sl, O, L, De)
                                                  : -1;
       if (!rc) {
@@ -512,21 +515,17 @@ int oracle_bwd_dbias(const oracle_problem *p, const void *q, const void *k,
         for (int64_t i = 0; i < sq; ++i) row_dq(p, &sl, i, L[i], De[i], dQ + i * D);
 #pragma omp parallel for schedule(dynamic, 8)
         for (int64_t j = 0; j < sk; ++j)
-          col_dkdv(p, &sl, j, L, De, dK + j * D, dV + j * D);
+          col_dkdv(p, &sl, j, L, De, dK + j * D, dV + j * DV);
         for (int64_t i = 0; i < sq; ++i) {
-          for (int d = 0; d < D; ++d) {
-            int64_t e = elem_index(p, b, h, sl.sp.q0, i, sq, d);
-            dq[e] = dQ[i * D + d];
-            if (o) o[e] = O[i * D + d];
-          }
+          for (int d = 0; d < D; ++d) dq[elem_index(p, b, h, sl.sp.q0, i, sq, D, d)] = dQ[i * D + d];
+          if (o)
+            for (int d = 0; d < DV; ++d) o[elem_index(p, b, h, sl.sp.q0, i, sq, DV, d)] = O[i * DV + d];
           if (lse) lse[lse_index(p, b, h, i)] = L[i];
         }
-        for (int64_t j = 0; j < sk; ++j)
-          for (int d = 0; d < D; ++d) {
-            int64_t e = elem_index(p, b, h, sl.sp.k0, j, sk, d);
-            dk[e] = dK[j * D + d];
-            dv[e] = dV[j * D + d];
-          }
+        for (int64_t j = 0; j < sk; ++j) {
+          for (int d = 0; d < D; ++d) dk[elem_index(p, b, h, sl.sp.k0, j, sk, D, d)] = dK[j * D + d];
+          for (int d = 0; d < DV; ++d) dv[elem_index(p, b, h, sl.sp.k0, j, sk, DV, d)] = dV[j * DV + d];
+        }
         if (dbias) {
           double *row0 = dbias + ((int64_t)b * p->heads + h) * sqm * skm;
 #pragma omp parallel for schedule(dynamic, 8)
@@ -551,7 +550,7 @@ int oracle_bwd_dq_rows(const oracle_problem *p, const void *q, const void *k,
     return -1;
   slice sl;
   if (slice_load(p, q, k, v, dout, b, h, &sl)) { slice_free(&sl); return -1; }
-  int D = p->head_dim;
+  int D = p->head_dim, DV = dim_v(p);
   int64_t sq = sl.sp.sq, sk = sl.sp.sk;
   int bad = 0;
   for (int r = 0; r < nrows; ++r)
@@ -560,14 +559,14 @@ int oracle_bwd_dq_rows(const oracle_problem *p, const void *q, const void *k,
 #pragma omp parallel
     {
       double *s = (double *)malloc(sizeof(double) * (size_t)(sk + 1));
-      double *orow = (double *)malloc(sizeof(double) * (size_t)D);
+      double *orow = (double *)malloc(sizeof(double) * (size_t)DV);
 #pragma omp for schedule(dynamic, 1)
       for (int r = 0; r < nrows; ++r) {
         if (!s || !orow) continue;
         double lse_i;
         int64_t i = rows[r];
         row_forward(p, &sl, i, s, orow, &lse_i);
-        double delta_i = dot(sl.dO + i * D, orow, D);
+        double delta_i = dot(sl.dO + i * DV, orow, DV);
         row_dq(p, &sl, i, lse_i, delta_i, dq_rows + (int64_t)r * D);
       }
       if (!s || !orow) {
@@ -589,12 +588,12 @@ int oracle_bwd_dkdv_cols(const oracle_problem *p, const void *q,
     return -1;
   slice sl;
   if (slice_load(p, q, k, v, dout, b, h, &sl)) { slice_free(&sl); return -1; }
-  int D = p->head_dim;
+  int D = p->head_dim, DV = dim_v(p);
   int64_t sq = sl.sp.sq, sk = sl.sp.sk;
   int bad = 0;
   for (int c = 0; c < ncols; ++c)
     if (cols[c] < 0 || cols[c] >= sk) bad = 1;
-  double *O = (double *)malloc(sizeof(double) * (size_t)(sq * D + 1));
+  double *O = (double *)malloc(sizeof(double) * (size_t)(sq * DV + 1));
   double *L = (double *)malloc(sizeof(double) * (size_t)(sq + 1));
   double *De = (double *)malloc(sizeof(double) * (size_t)(sq + 1));
   if (!O || !L || !De) bad = 1;
@@ -603,7 +602,7 @@ int oracle_bwd_dkdv_cols(const oracle_problem *p, const void *q,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int c = 0; c < ncols; ++c)
       col_dkdv(p, &sl, cols[c], L, De, dk_cols + (int64_t)c * D,
-               dv_cols + (int64_t)c * D);
+               dv_cols + (int64_t)c * DV);
   }
   free(O); free(L); free(De);
   slice_free(&sl);

@@ -68,6 +68,10 @@ typedef struct {
    * largest Sq / Sk (packed; the dense seqlen_q / seqlen_k otherwise). */
   int max_seqlen_q;
   int max_seqlen_k;
+  /* Head dim of V (and so of O, dO and dV); 0 means head_dim.  Q and K
+   * rows hold head_dim values, the scores use those; V rows hold
+   * head_dim_v. */
+  int head_dim_v;
 } oracle_problem;
 
 /* Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel
