@@ -35,13 +35,11 @@
  *    memory: its pointer may be NULL and takes part in no aliasing check.
  *  - Errors are returned, never printed: hipErrorInvalidValue for a malformed
  *    call (null required pointer, version or flags mismatch, negative or
- *    zero sizes where a size is needed, unit-stride or 16-byte alignment
- *    violated, workspace too small), hipErrorNotSupported for a well-formed
- *    call outside the built set (head_dim not in {32, 48, 64, 80, 96, 128}: the
- *    multiples of 16 up to 128 that the AOTriton pages name or test, 48 and
- *    80 among them (0.10b "Known Problems"); for fp16 and
- *    bf16, a q, k, v or dout row stride so large that 63 strides plus one
- *    row reach 2 GiB), or the HIP error of the launch.  Validation makes no HIP call.  The contents of
+ *    zero sizes where a size is needed, a pointer not aligned to its element
+ *    size, workspace too small), hipErrorNotSupported for a well-formed call
+ *    outside the built set (head_dim or head_dim_v above 128; for fp16 and
+ *    bf16 run in place, a q, k, v or dout row stride so large that 63
+ *    strides plus one row reach 2 GiB), or the HIP error of the launch.  Validation makes no HIP call.  The contents of
  *    cu_seqlens arrays are a precondition (0 first, non-decreasing, last
  *    entry equal to total_q / total_k, every length <= the seqlen_q /
  *    seqlen_k maximum) and are not checked: reading them would need a sync.
@@ -150,7 +148,12 @@ typedef struct {
                               VARLEN: number of sequences (>= 1 if a side
                               is stacked) */
   int32_t heads;           /* >= 1; Q, K and V have the same head count */
-  int32_t head_dim;        /* 32, 48, 64, 80, 96 or 128; V/O share it */
+  int32_t head_dim;        /* 1..128, of Q and K (and of V, O, dO, dV when
+                              head_dim_v is 0).  32, 48, 64, 80, 96 and 128
+                              (the multiples of 16 up to 128 the AOTriton
+                              pages name or test, 48 and 80 among them, 0.10b
+                              "Known Problems") run in place; see "Repacked
+                              calls" for the others */
   int32_t seqlen_q;        /* BHSD: Sq (>= 0); THD: max sequence length of Q;
                               VARLEN: the Q side's uniform length / room,
                               and the largest length (>= 0) */
@@ -175,11 +178,12 @@ typedef struct {
                               with LEN_CUMSUM or POS_CUMSUM on Q; else NULL */
   const int32_t *cu_seqlens_k; /* the same for K */
   int64_t q_stride[3];     /* element strides {batch, head, row}; the */
-  int64_t k_stride[3];     /* head_dim stride is 1.  Base pointers and */
-  int64_t v_stride[3];     /* strides must keep every row 16-byte */
-  int64_t o_stride[3];     /* aligned.  A stride may be negative: the
-                              pointer is then the address of index 0 on that
-                              axis, and the operand reaches below it. */
+  int64_t k_stride[3];     /* head_dim stride is 1.  A call whose base */
+  int64_t v_stride[3];     /* pointers and strides keep every row 16-byte */
+  int64_t o_stride[3];     /* aligned runs in place, any other is repacked.
+                              A stride may be negative: the pointer is then
+                              the address of index 0 on that axis, and the
+                              operand reaches below it. */
   const int32_t *seqused_q; /* optional device int32[batch]: sequence b uses
                               only its first seqused_q[b] query rows (of
                               seqlen_q rows, BHSD, or of its cu_seqlens_q
@@ -228,10 +232,38 @@ typedef struct {
                               (0.14b "Minor Changes"); kept probabilities are
                               scaled by 1 / (1 - p).  LSE is the softmax's,
                               before dropout. */
-  int32_t reserved2;        /* must be 0 */
+  int32_t head_dim_v;       /* head dim of V, O, dO and dV, 1..128 (Hdim_vo
+                              of the AOTriton 0.15b notes, "Kernel Bug
+                              Fixes"); 0 = head_dim.  A value other than
+                              head_dim makes the call a repacked one. */
   uint64_t philox_seed;
   uint64_t philox_offset;
+  void *workspace;          /* forward of a repacked call: device,
+                              caller-owned, 256-byte aligned, >=
+                              attn_fwd_workspace_size(this) bytes; ignored
+                              otherwise, and by the backward calls (which
+                              take attn_bwd_params.workspace) */
+  uint64_t workspace_bytes;
 } attn_fwd_params;
+
+/* Repacked calls.  A call runs in place when head_dim is one of the built
+ * dims (32, 48, 64, 80, 96, 128), head_dim_v equals it, and every operand
+ * row is 16-byte aligned (base pointers and strides).  Any other call with
+ * head dims up to 128 is repacked: the library first copies its inputs,
+ * each row zero-padded to Dp columns (the smallest built dim >= both head
+ * dims), into the workspace, runs the in-place kernels there at head dim Dp
+ * (zero columns add nothing to Q K^T, and give zero columns of O, dQ, dK
+ * and dV), and copies the outputs' first head_dim (head_dim_v) columns
+ * back, over the rows the in-place call would write.  LSE and dbias are
+ * written directly.  The copies cost one read and one write of each
+ * operand; the results equal those of the same problem zero-padded to Dp
+ * by the caller. */
+
+/* Forward workspace bytes of a call: 0 when it runs in place; for a
+ * repacked call, padded copies of q, k, v and o (rows of Dp elements; a
+ * stacked side's rows are total_q / total_k, a padded side's batch *
+ * seqlen), each rounded up to 256 bytes; 0 when the problem is malformed. */
+uint64_t attn_fwd_workspace_size(const attn_fwd_params *p);
 
 typedef struct {
   attn_fwd_params fwd;     /* problem, inputs q/k/v and the forward's o/lse */
@@ -319,7 +351,12 @@ hipError_t attn_bwd_dkdv_dq(const attn_bwd_params *p, hipStream_t stream);
  * then, in split mode, the fp32 partial sums (head_dim floats per copy, head
  * and row: dK and dV per key-side copy, dQ per query-side copy; rows are the
  * stacked tensor's rows, or batch * seqlen for a padded side), rounded up to
- * 256 bytes; 0 when the problem is malformed. */
+ * 256 bytes; 0 when the problem is malformed.  A repacked call (see above)
+ * needs, before those (sized for head dim Dp), padded copies of q, k, v, o,
+ * dout, dq, dk and dv, each rounded up to 256 bytes.  Repacked, the three
+ * step calls share the copies through the workspace: attn_bwd_preprocess
+ * makes the input copies, attn_bwd_dkdv / attn_bwd_dq copy their outputs
+ * back. */
 uint64_t attn_bwd_workspace_size(const attn_bwd_params *p);
 
 /* Host-only validation of a call, the same checks attn_fwd / attn_bwd make
@@ -341,7 +378,7 @@ uint32_t attn_params_version(void);
  * choices).  Host-only: nothing is enqueued and no device memory is read or
  * written.  The call's own validation runs first and its error is returned;
  * attn_bwd_plan does not look at the workspace, which decides nothing. */
-#define ATTN_PLAN_MAX 4
+#define ATTN_PLAN_MAX 8
 typedef struct {
   const char *kernel[ATTN_PLAN_MAX]; /* kernel[i], i < count */
   uint32_t grid[ATTN_PLAN_MAX];      /* workgroups of launch i */

@@ -57,8 +57,9 @@ class FwdParams(ctypes.Structure):
         ("varlen", ctypes.c_uint32), ("reserved1", ctypes.c_int32),
         ("seqstart_q", ctypes.c_void_p), ("seqstart_k", ctypes.c_void_p),
         ("bias", ctypes.c_void_p), ("bias_stride", _I64x3), ("alibi_slopes", ctypes.c_void_p),
-        ("dropout_p", ctypes.c_float), ("reserved2", ctypes.c_int32),
+        ("dropout_p", ctypes.c_float), ("head_dim_v", ctypes.c_int32),
         ("philox_seed", ctypes.c_uint64), ("philox_offset", ctypes.c_uint64),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
     ]
 
 
@@ -73,7 +74,7 @@ class BwdParams(ctypes.Structure):
     ]
 
 
-PLAN_MAX = 4
+PLAN_MAX = 8
 BWD_PREPROCESS, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 # ATTN_NOALLOC_SCRATCH_BYTES: the workspace limit of attn_bwd_noalloc.
 NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -113,6 +114,8 @@ def lib():
         l.attn_bwd_check.restype = ctypes.c_int
         l.attn_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdParams)]
         l.attn_bwd_workspace_size.restype = ctypes.c_uint64
+        l.attn_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdParams)]
+        l.attn_fwd_workspace_size.restype = ctypes.c_uint64
         l.attn_params_version.restype = ctypes.c_uint32
         l.attn_fwd_plan.argtypes = [ctypes.POINTER(FwdParams), ctypes.c_void_p, ctypes.POINTER(Plan)]
         l.attn_fwd_plan.restype = ctypes.c_int
@@ -257,6 +260,8 @@ def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens
         raise ValueError("inputs are [B, H, S, D] or [T, H, D]")
     p.seqused_q = _ptr(_seqused(seqused_q, p.batch, q.device))
     p.seqused_k = _ptr(_seqused(seqused_k, p.batch, q.device))
+    if v.shape[-1] != q.shape[-1]:
+        p.head_dim_v = v.shape[-1]
     if bias is not None:
         p.bias, p.bias_stride = _ptr(bias), _bias_strides(bias, q, "bias")
     if alibi_slopes is not None:
@@ -353,10 +358,18 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: Optional
     _check_inputs(q, k, v)
     dev = q.device
     pk = _problem(q, **kw)
-    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    if out is None:
+        o = torch.empty(tuple(q.shape[:-1]) + (v.shape[-1],), dtype=q.dtype, device=dev)
+    else:
+        o = out
     if lse is None:
         lse = torch.empty(lse_shape(q, pk["lse_layout"], pk["q_mode"]), dtype=torch.float32, device=dev)
     p = fwd_params(q, k, v, o, lse, **pk)
+    need = int(lib().attn_fwd_workspace_size(ctypes.byref(p)))
+    ws = None
+    if need:  # a repacked call: zero-padded copies of its operands
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        p.workspace, p.workspace_bytes = ws.data_ptr(), need
     rc = lib().attn_fwd(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
     if rc:
         raise AttnError("attn_fwd", rc)

@@ -77,8 +77,20 @@ const attn_bwd_params* bwd_v3(const attn_bwd_params* p, attn_bwd_params* tmp) {
 bool dtype_ok(int32_t d) { return d == ATTN_FP32 || d == ATTN_FP16 || d == ATTN_BF16; }
 int64_t elem_bytes(int32_t d) { return d == ATTN_FP32 ? 4 : 2; }
 bool head_dim_built(int32_t d) { return d == 32 || d == 48 || d == 64 || d == 80 || d == 96 || d == 128; }
+constexpr int kMaxDim = 128;  // largest built head dim
+
+// Smallest built head dim >= d (d <= kMaxDim).
+int padded_dim(int d) {
+  for (int b : {32, 48, 64, 80, 96, 128})
+    if (d <= b) return b;
+  return 0;
+}
+
+// Head dim of V, O, dO and dV.
+int dim_v(const attn_fwd_params* p) { return p->head_dim_v ? p->head_dim_v : p->head_dim; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool elem_aligned(const void* p, int64_t esz) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)esz) == 0; }
 
 // ------------------------------------------------------ per-side addressing
 
@@ -188,7 +200,6 @@ Extent extent4(const void* ptr, const int64_t* stride, const attn_fwd_params* p,
 }
 
 hipError_t check_feat(const attn_fwd_params* p) {
-  if (p->reserved2 != 0) return hipErrorInvalidValue;
   if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f)) return hipErrorInvalidValue;  // also NaN
   if (p->bias && (reinterpret_cast<uintptr_t>(p->bias) % (uintptr_t)elem_bytes(p->dtype)) != 0)
     return hipErrorInvalidValue;
@@ -224,7 +235,8 @@ hipError_t check_problem(const attn_fwd_params* p) {
   if (p->layout != ATTN_VARLEN && (p->varlen != 0 || p->seqstart_q || p->seqstart_k)) return hipErrorInvalidValue;
   if (p->layout == ATTN_VARLEN && (p->varlen >> 16) != 0) return hipErrorInvalidValue;
   if (p->diag != ATTN_TOP_LEFT && p->diag != ATTN_BOTTOM_RIGHT) return hipErrorInvalidValue;
-  if (p->heads < 1 || p->head_dim < 1 || p->seqlen_q < 0 || p->seqlen_k < 0) return hipErrorInvalidValue;
+  if (p->heads < 1 || p->head_dim < 1 || p->head_dim_v < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
+    return hipErrorInvalidValue;
   if (!std::isfinite(p->scale)) return hipErrorInvalidValue;
   const Side qs = side_of(p, true), ks = side_of(p, false);
   if (!side_ok(qs) || !side_ok(ks)) return hipErrorInvalidValue;
@@ -237,17 +249,11 @@ hipError_t check_problem(const attn_fwd_params* p) {
       (!p->v && !no_k))
     return hipErrorInvalidValue;
   const int64_t esz = elem_bytes(p->dtype);
-  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
-    return hipErrorInvalidValue;
-  if (!strides_ok(p->q_stride, esz, qs.stacked()) || !strides_ok(p->k_stride, esz, ks.stacked()) ||
-      !strides_ok(p->v_stride, esz, ks.stacked()) || !strides_ok(p->o_stride, esz, qs.stacked()))
+  if (!elem_aligned(p->q, esz) || !elem_aligned(p->k, esz) || !elem_aligned(p->v, esz) ||
+      !elem_aligned(p->o, esz))
     return hipErrorInvalidValue;
   if (check_feat(p) != hipSuccess) return hipErrorInvalidValue;
-  if (!head_dim_built(p->head_dim)) return hipErrorNotSupported;
-  if (p->dtype != ATTN_FP32 &&
-      (!tile_span_ok(p->q_stride, esz, p->head_dim) || !tile_span_ok(p->k_stride, esz, p->head_dim) ||
-       !tile_span_ok(p->v_stride, esz, p->head_dim)))
-    return hipErrorNotSupported;
+  if (p->head_dim > kMaxDim || dim_v(p) > kMaxDim) return hipErrorNotSupported;
   return hipSuccess;
 }
 
@@ -306,8 +312,119 @@ Split split_of(const attn_bwd_params* p) {
   return sp;
 }
 
-// Workspace of a backward: Delta and LSE log2(e), then the split partials.
-uint64_t bwd_ws_bytes(const attn_bwd_params* p) { return delta_bytes(&p->fwd) + split_of(p).bytes; }
+// Workspace of an in-place backward: Delta and LSE log2(e), then the split
+// partials.
+uint64_t inner_ws_bytes(const attn_bwd_params* p) { return delta_bytes(&p->fwd) + split_of(p).bytes; }
+
+// ------------------------------------------------------------- repacking
+
+// A call runs in place when its head dims are one built dim and every row
+// it addresses is 16-byte aligned (and, for the 16-bit kernels' tile copies,
+// within the 2 GiB span); any other call runs on zero-padded copies.
+bool in_place_fwd(const attn_fwd_params* p) {
+  if (!head_dim_built(p->head_dim) || dim_v(p) != p->head_dim) return false;
+  const Side qs = side_of(p, true), ks = side_of(p, false);
+  const int64_t esz = elem_bytes(p->dtype), D = p->head_dim;
+  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o)) return false;
+  if (!strides_ok(p->q_stride, esz, qs.stacked()) || !strides_ok(p->k_stride, esz, ks.stacked()) ||
+      !strides_ok(p->v_stride, esz, ks.stacked()) || !strides_ok(p->o_stride, esz, qs.stacked()))
+    return false;
+  if (p->dtype != ATTN_FP32 && (!tile_span_ok(p->q_stride, esz, D) || !tile_span_ok(p->k_stride, esz, D) ||
+                                !tile_span_ok(p->v_stride, esz, D)))
+    return false;
+  return true;
+}
+
+bool in_place_bwd(const attn_bwd_params* p) {
+  const attn_fwd_params* f = &p->fwd;
+  if (!in_place_fwd(f)) return false;
+  const Side qs = side_of(f, true), ks = side_of(f, false);
+  const int64_t esz = elem_bytes(f->dtype);
+  if (!aligned16(p->dout) || !aligned16(p->dq) || !aligned16(p->dk) || !aligned16(p->dv)) return false;
+  if (!strides_ok(p->do_stride, esz, qs.stacked()) || !strides_ok(p->dq_stride, esz, qs.stacked()) ||
+      !strides_ok(p->dk_stride, esz, ks.stacked()) || !strides_ok(p->dv_stride, esz, ks.stacked()))
+    return false;
+  return f->dtype == ATTN_FP32 || tile_span_ok(p->do_stride, esz, f->head_dim);
+}
+
+// Padded copies of a repacked call in its workspace: q, k, v, o (and for
+// the backward dout, dq, dk, dv), rows of Dp elements, each section
+// rounded up to 256 bytes.
+enum { kPQ, kPK, kPV, kPO, kPdO, kPdQ, kPdK, kPdV, kPN };
+struct Pack {
+  int Dp = 0;
+  uint64_t off[kPN] = {};
+  uint64_t bytes = 0;  // all sections of the call
+};
+
+Pack pack_of(const attn_fwd_params* f, bool bwd) {
+  Pack pk;
+  pk.Dp = padded_dim(std::max(f->head_dim, dim_v(f)));
+  const Side qs = side_of(f, true), ks = side_of(f, false);
+  const uint64_t esz = (uint64_t)elem_bytes(f->dtype), row = (uint64_t)f->heads * pk.Dp * esz;
+  const uint64_t rq = (uint64_t)(qs.stacked() ? f->total_q : (int64_t)f->batch * f->seqlen_q);
+  const uint64_t rk = (uint64_t)(ks.stacked() ? f->total_k : (int64_t)f->batch * f->seqlen_k);
+  const uint64_t sq = (rq * row + 255) / 256 * 256, sk = (rk * row + 255) / 256 * 256;
+  const bool q_side[kPN] = {true, false, false, true, true, true, false, false};
+  for (int t = 0; t < (bwd ? kPN : kPdO); ++t) {
+    pk.off[t] = pk.bytes;
+    pk.bytes += q_side[t] ? sq : sk;
+  }
+  return pk;
+}
+
+// Strides of a padded copy: stacked [rows, heads, Dp], padded [batch,
+// heads, seqlen, Dp].
+void copy_strides(const Side& s, int H, int Dp, int64_t* st) {
+  st[0] = s.stacked() ? 0 : (int64_t)H * s.S * Dp;
+  st[1] = s.stacked() ? Dp : (int64_t)s.S * Dp;
+  st[2] = s.stacked() ? (int64_t)H * Dp : Dp;
+}
+
+// The in-place call on the copies (ws: the workspace's address).
+attn_fwd_params inner_fwd(const attn_fwd_params* p, uintptr_t ws, const Pack& pk) {
+  attn_fwd_params in = *p;
+  const Side qs = side_of(p, true), ks = side_of(p, false);
+  in.head_dim = pk.Dp;
+  in.head_dim_v = 0;
+  in.q = reinterpret_cast<const void*>(ws + pk.off[kPQ]);
+  in.k = reinterpret_cast<const void*>(ws + pk.off[kPK]);
+  in.v = reinterpret_cast<const void*>(ws + pk.off[kPV]);
+  in.o = reinterpret_cast<void*>(ws + pk.off[kPO]);
+  copy_strides(qs, p->heads, pk.Dp, in.q_stride);
+  copy_strides(ks, p->heads, pk.Dp, in.k_stride);
+  copy_strides(ks, p->heads, pk.Dp, in.v_stride);
+  copy_strides(qs, p->heads, pk.Dp, in.o_stride);
+  in.workspace = nullptr;
+  in.workspace_bytes = 0;
+  return in;
+}
+
+attn_bwd_params inner_bwd(const attn_bwd_params* p, uintptr_t ws, const Pack& pk) {
+  attn_bwd_params in = *p;
+  in.fwd = inner_fwd(&p->fwd, ws, pk);
+  const Side qs = side_of(&p->fwd, true), ks = side_of(&p->fwd, false);
+  in.dout = reinterpret_cast<const void*>(ws + pk.off[kPdO]);
+  in.dq = reinterpret_cast<void*>(ws + pk.off[kPdQ]);
+  in.dk = reinterpret_cast<void*>(ws + pk.off[kPdK]);
+  in.dv = reinterpret_cast<void*>(ws + pk.off[kPdV]);
+  copy_strides(qs, p->fwd.heads, pk.Dp, in.do_stride);
+  copy_strides(qs, p->fwd.heads, pk.Dp, in.dq_stride);
+  copy_strides(ks, p->fwd.heads, pk.Dp, in.dk_stride);
+  copy_strides(ks, p->fwd.heads, pk.Dp, in.dv_stride);
+  in.workspace = reinterpret_cast<void*>(ws + pk.bytes);
+  in.workspace_bytes = p->workspace_bytes > pk.bytes ? p->workspace_bytes - pk.bytes : 0;
+  return in;
+}
+
+uint64_t fwd_ws_bytes(const attn_fwd_params* p) { return in_place_fwd(p) ? 0 : pack_of(p, false).bytes; }
+
+uint64_t bwd_ws_bytes(const attn_bwd_params* p) {
+  if (in_place_bwd(p)) return inner_ws_bytes(p);
+  const Pack pk = pack_of(&p->fwd, true);
+  const attn_bwd_params in = inner_bwd(p, 0, pk);
+  return pk.bytes + inner_ws_bytes(&in);
+}
 
 sdpa::SideArgs side_args(const Side& s) {
   sdpa::SideArgs a{};
@@ -361,22 +478,29 @@ Extent alibi_extent(const attn_fwd_params* p) {
   return Extent{lo, p->alibi_slopes ? lo + (uintptr_t)p->heads * 4 : lo};
 }
 
-hipError_t check_fwd(const attn_fwd_params* p) {
+// The checks of attn_fwd_check; the workspace (of a repacked call) is
+// checked only when `ws` (the plan query does not look at it).
+hipError_t check_fwd(const attn_fwd_params* p, bool ws = true) {
   hipError_t err = check_problem(p);
   if (err != hipSuccess) return err;
   const Side qs = side_of(p, true), ks = side_of(p, false);
-  const int64_t esz = elem_bytes(p->dtype), B = p->batch, H = p->heads, D = p->head_dim;
-  const Extent o = extent_of(p->o, p->o_stride, B, H, qs, D, esz);
-  const Extent ins[3] = {extent_of(p->q, p->q_stride, B, H, qs, D, esz),
+  const int64_t esz = elem_bytes(p->dtype), B = p->batch, H = p->heads, D = p->head_dim, DV = dim_v(p);
+  const uint64_t need = ws ? fwd_ws_bytes(p) : 0;
+  if (need && (!p->workspace || p->workspace_bytes < need || (reinterpret_cast<uintptr_t>(p->workspace) & 255u)))
+    return hipErrorInvalidValue;
+  const uintptr_t w0 = reinterpret_cast<uintptr_t>(p->workspace);
+  const Extent outs[3] = {extent_of(p->o, p->o_stride, B, H, qs, DV, esz), lse_extent(p),
+                          need ? Extent{w0, w0 + (uintptr_t)need} : Extent{0, 0}};
+  const Extent ins[5] = {extent_of(p->q, p->q_stride, B, H, qs, D, esz),
                          extent_of(p->k, p->k_stride, B, H, ks, D, esz),
-                         extent_of(p->v, p->v_stride, B, H, ks, D, esz)};
-  const Extent l = lse_extent(p);
-  for (const Extent& in : ins)
-    if (overlap(o, in) || overlap(l, in)) return hipErrorInvalidValue;
-  if (overlap(o, l)) return hipErrorInvalidValue;
-  const Extent fin[2] = {extent4(p->bias, p->bias_stride, p, esz), alibi_extent(p)};
-  for (const Extent& in : fin)
-    if (overlap(o, in) || overlap(l, in)) return hipErrorInvalidValue;
+                         extent_of(p->v, p->v_stride, B, H, ks, DV, esz), extent4(p->bias, p->bias_stride, p, esz),
+                         alibi_extent(p)};
+  for (int i = 0; i < 3; ++i) {
+    for (const Extent& in : ins)
+      if (overlap(outs[i], in)) return hipErrorInvalidValue;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return hipErrorInvalidValue;
+  }
   return hipSuccess;
 }
 
@@ -396,26 +520,23 @@ hipError_t check_bwd(const attn_bwd_params* p, bool ws) {
              (reinterpret_cast<uintptr_t>(p->workspace) & 255u) != 0))
     return hipErrorInvalidValue;
   const int64_t esz = elem_bytes(f->dtype);
-  if (!aligned16(p->dout) || !aligned16(p->dq) || !aligned16(p->dk) || !aligned16(p->dv))
+  if (!elem_aligned(p->dout, esz) || !elem_aligned(p->dq, esz) || !elem_aligned(p->dk, esz) ||
+      !elem_aligned(p->dv, esz))
     return hipErrorInvalidValue;
-  if (!strides_ok(p->do_stride, esz, qs.stacked()) || !strides_ok(p->dq_stride, esz, qs.stacked()) ||
-      !strides_ok(p->dk_stride, esz, ks.stacked()) || !strides_ok(p->dv_stride, esz, ks.stacked()))
-    return hipErrorInvalidValue;
-  if (f->dtype != ATTN_FP32 && !tile_span_ok(p->do_stride, esz, f->head_dim)) return hipErrorNotSupported;
   if (p->dbias && (reinterpret_cast<uintptr_t>(p->dbias) & 3u) != 0) return hipErrorInvalidValue;
-  const int64_t B = f->batch, H = f->heads, D = f->head_dim;
+  const int64_t B = f->batch, H = f->heads, D = f->head_dim, DV = dim_v(f);
   const Extent outs[5] = {
       extent_of(p->dq, p->dq_stride, B, H, qs, D, esz), extent_of(p->dk, p->dk_stride, B, H, ks, D, esz),
-      extent_of(p->dv, p->dv_stride, B, H, ks, D, esz),
+      extent_of(p->dv, p->dv_stride, B, H, ks, DV, esz),
       ws ? Extent{reinterpret_cast<uintptr_t>(p->workspace),
                   reinterpret_cast<uintptr_t>(p->workspace) + (uintptr_t)bwd_ws_bytes(p)}
          : Extent{0, 0},
       extent4(p->dbias, p->dbias_stride, f, 4)};
   const Extent ins[8] = {extent_of(f->q, f->q_stride, B, H, qs, D, esz),
                          extent_of(f->k, f->k_stride, B, H, ks, D, esz),
-                         extent_of(f->v, f->v_stride, B, H, ks, D, esz),
-                         extent_of(f->o, f->o_stride, B, H, qs, D, esz),
-                         extent_of(p->dout, p->do_stride, B, H, qs, D, esz),
+                         extent_of(f->v, f->v_stride, B, H, ks, DV, esz),
+                         extent_of(f->o, f->o_stride, B, H, qs, DV, esz),
+                         extent_of(p->dout, p->do_stride, B, H, qs, DV, esz),
                          lse_extent(f),
                          extent4(f->bias, f->bias_stride, f, esz),
                          alibi_extent(f)};
@@ -479,6 +600,83 @@ sdpa::BwdArgs bwd_args(const attn_bwd_params* p, void* ws) {
     a.split_q = sp.gq;
   }
   return a;
+}
+
+// One repack launch: tensors (caller operand, copy operand, side, columns)
+// in the given direction.
+struct RepackList {
+  sdpa::RepackArgs a{};
+  void add(const void* caller, const int64_t* cs, const void* copy, const int64_t* ps, const Side& s, int side,
+           int cols) {
+    sdpa::RepackT& t = a.t[a.n++];
+    const Operand user = operand(caller, cs, s.stacked()), pad = operand(copy, ps, s.stacked());
+    t.src = a.out ? pad : user;
+    t.dst = a.out ? user : pad;
+    t.side = side;
+    t.cols = cols;
+  }
+};
+
+RepackList repack_list(const attn_fwd_params* p, int Dp, int out) {
+  RepackList l;
+  l.a.p = problem_args(p);
+  l.a.out = out;
+  l.a.pad = Dp;
+  l.a.esz = (int)elem_bytes(p->dtype);
+  return l;
+}
+
+// The forward of any call on executor ex: in place, or repacked through
+// the workspace at ws (an address; the plan passes the caller's, maybe 0).
+template <class Ex>
+hipError_t run_fwd(const attn_fwd_params* p, uintptr_t ws, const Ex& ex) {
+  if (in_place_fwd(p)) return sdpa::launch_fwd(p->dtype, p->head_dim, fwd_args(p), ex);
+  const Pack pk = pack_of(p, false);
+  const attn_fwd_params in = inner_fwd(p, ws, pk);
+  const Side qs = side_of(p, true), ks = side_of(p, false);
+  RepackList ci = repack_list(p, pk.Dp, 0);
+  ci.add(p->q, p->q_stride, in.q, in.q_stride, qs, 0, p->head_dim);
+  ci.add(p->k, p->k_stride, in.k, in.k_stride, ks, 1, p->head_dim);
+  ci.add(p->v, p->v_stride, in.v, in.v_stride, ks, 1, dim_v(p));
+  hipError_t err = sdpa::launch_repack(ci.a, ex);
+  if (err == hipSuccess) err = sdpa::launch_fwd(in.dtype, in.head_dim, fwd_args(&in), ex);
+  if (err != hipSuccess) return err;
+  RepackList co = repack_list(p, pk.Dp, 1);
+  co.add(p->o, p->o_stride, in.o, in.o_stride, qs, 0, dim_v(p));
+  return sdpa::launch_repack(co.a, ex);
+}
+
+// The backward steps `stages` of any call (workspace at ws).  Repacked: the
+// Delta step makes the input copies first; the dK/dV and dQ steps copy
+// their outputs back after.
+template <class Ex>
+hipError_t run_bwd(const attn_bwd_params* p, uintptr_t ws, int stages, const Ex& ex) {
+  const attn_fwd_params* f = &p->fwd;
+  if (in_place_bwd(p))
+    return sdpa::launch_bwd(f->dtype, f->head_dim, bwd_args(p, reinterpret_cast<void*>(ws)), stages, ex);
+  const Pack pk = pack_of(f, true);
+  const attn_bwd_params in = inner_bwd(p, ws, pk);
+  const Side qs = side_of(f, true), ks = side_of(f, false);
+  const int D = f->head_dim, DV = dim_v(f);
+  hipError_t err = hipSuccess;
+  if (stages & sdpa::kStageDelta) {
+    RepackList ci = repack_list(f, pk.Dp, 0);
+    ci.add(f->q, f->q_stride, in.fwd.q, in.fwd.q_stride, qs, 0, D);
+    ci.add(f->k, f->k_stride, in.fwd.k, in.fwd.k_stride, ks, 1, D);
+    ci.add(f->v, f->v_stride, in.fwd.v, in.fwd.v_stride, ks, 1, DV);
+    ci.add(f->o, f->o_stride, in.fwd.o, in.fwd.o_stride, qs, 0, DV);
+    ci.add(p->dout, p->do_stride, in.dout, in.do_stride, qs, 0, DV);
+    err = sdpa::launch_repack(ci.a, ex);
+  }
+  if (err == hipSuccess) err = sdpa::launch_bwd(f->dtype, pk.Dp, bwd_args(&in, in.workspace), stages, ex);
+  if (err != hipSuccess) return err;
+  RepackList co = repack_list(f, pk.Dp, 1);
+  if (stages & sdpa::kStageDq) co.add(p->dq, p->dq_stride, in.dq, in.dq_stride, qs, 0, D);
+  if (stages & sdpa::kStageDkDv) {
+    co.add(p->dk, p->dk_stride, in.dk, in.dk_stride, ks, 1, D);
+    co.add(p->dv, p->dv_stride, in.dv, in.dv_stride, ks, 1, DV);
+  }
+  return sdpa::launch_repack(co.a, ex);
 }
 
 void plan_out(const sdpa::Plan& pl, attn_plan* out) {
@@ -546,10 +744,8 @@ hipError_t on_stream_device(hipStream_t stream, F launch) {
 hipError_t bwd_stages(const attn_bwd_params* p, int stages, hipStream_t stream) {
   hipError_t err = check_bwd(p, true);
   if (err != hipSuccess) return err;
-  const attn_fwd_params* f = &p->fwd;
-  const sdpa::BwdArgs a = bwd_args(p, p->workspace);
-  return on_stream_device(
-      stream, [&] { return sdpa::launch_bwd(f->dtype, f->head_dim, a, stages, sdpa::Enqueue{stream}); });
+  const uintptr_t ws = reinterpret_cast<uintptr_t>(p->workspace);
+  return on_stream_device(stream, [&] { return run_bwd(p, ws, stages, sdpa::Enqueue{stream}); });
 }
 
 }  // namespace
@@ -568,19 +764,26 @@ hipError_t attn_fwd(const attn_fwd_params* p_in, hipStream_t stream) {
   const attn_fwd_params* p = fwd_v3(p_in, &tmp);
   hipError_t err = check_fwd(p);
   if (err != hipSuccess) return err;
-  const sdpa::FwdArgs a = fwd_args(p);
-  return on_stream_device(stream, [&] { return sdpa::launch_fwd(p->dtype, p->head_dim, a, sdpa::Enqueue{stream}); });
+  const uintptr_t ws = reinterpret_cast<uintptr_t>(p->workspace);
+  return on_stream_device(stream, [&] { return run_fwd(p, ws, sdpa::Enqueue{stream}); });
+}
+
+uint64_t attn_fwd_workspace_size(const attn_fwd_params* p_in) {
+  attn_fwd_params tmp;
+  const attn_fwd_params* p = fwd_v3(p_in, &tmp);
+  if (!p || check_problem(p) != hipSuccess) return 0;
+  return fwd_ws_bytes(p);
 }
 
 hipError_t attn_fwd_plan(const attn_fwd_params* p_in, hipStream_t stream, attn_plan* plan) {
   if (!plan) return hipErrorInvalidValue;
   attn_fwd_params tmp;
   const attn_fwd_params* p = fwd_v3(p_in, &tmp);
-  hipError_t err = check_fwd(p);
+  hipError_t err = check_fwd(p, false);
   if (err != hipSuccess) return err;
-  const sdpa::FwdArgs a = fwd_args(p);
+  const uintptr_t ws = reinterpret_cast<uintptr_t>(p->workspace);
   sdpa::Plan pl{};
-  err = on_stream_device(stream, [&] { return sdpa::launch_fwd(p->dtype, p->head_dim, a, sdpa::Record{&pl}); });
+  err = on_stream_device(stream, [&] { return run_fwd(p, ws, sdpa::Record{&pl}); });
   if (err == hipSuccess) plan_out(pl, plan);
   return err;
 }
@@ -628,11 +831,8 @@ hipError_t attn_bwd_plan(const attn_bwd_params* p_in, uint32_t steps, hipStream_
   const attn_bwd_params* p = bwd_v3(p_in, &tmp);
   hipError_t err = check_bwd(p, false);
   if (err != hipSuccess) return err;
-  const attn_fwd_params* f = &p->fwd;
-  const sdpa::BwdArgs a = bwd_args(p, nullptr);
   sdpa::Plan pl{};
-  err = on_stream_device(
-      stream, [&] { return sdpa::launch_bwd(f->dtype, f->head_dim, a, (int)steps, sdpa::Record{&pl}); });
+  err = on_stream_device(stream, [&] { return run_bwd(p, 0, (int)steps, sdpa::Record{&pl}); });
   if (err == hipSuccess) plan_out(pl, plan);
   return err;
 }
@@ -642,14 +842,16 @@ hipError_t attn_bwd_noalloc(const attn_bwd_params* p_in, hipStream_t stream) {
   const attn_bwd_params* p = bwd_v3(p_in, &tmp);
   hipError_t err = check_bwd(p, false);
   if (err != hipSuccess) return err;
-  const attn_fwd_params* f = &p->fwd;
-  if (bwd_ws_bytes(p) > (uint64_t)ATTN_NOALLOC_SCRATCH_BYTES) return hipErrorOutOfMemory;
+  const uint64_t need = bwd_ws_bytes(p);
+  if (need > (uint64_t)ATTN_NOALLOC_SCRATCH_BYTES) return hipErrorOutOfMemory;
   return on_stream_device(stream, [&] {
     void* ws = nullptr;
     const hipError_t serr = scratch_ptr(&ws);
     if (serr != hipSuccess) return serr;
-    const sdpa::BwdArgs a = bwd_args(p, ws);
-    return sdpa::launch_bwd(f->dtype, f->head_dim, a, sdpa::kStageAll, sdpa::Enqueue{stream});
+    attn_bwd_params q = *p;  // the scratch array as the workspace
+    q.workspace = ws;
+    q.workspace_bytes = need;
+    return run_bwd(&q, reinterpret_cast<uintptr_t>(ws), sdpa::kStageAll, sdpa::Enqueue{stream});
   });
 }
 

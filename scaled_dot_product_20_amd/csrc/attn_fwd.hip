@@ -1170,6 +1170,52 @@ template hipError_t launch_pad_rows<Enqueue>(const ProblemArgs&, Operand, Operan
 template hipError_t launch_pad_rows<Record>(const ProblemArgs&, Operand, Operand, float*, int, int, int,
                                             const Record&);
 
+// One workgroup per (sequence, head) and slice of its rows; half a
+// workgroup per row (128 columns at most), element by element, so rows of
+// any alignment and width are copied.
+__global__ __launch_bounds__(256) void attn_repack_kernel(RepackArgs a, int slices) {
+  const ProblemArgs& P = a.p;
+  const int sl = (int)(blockIdx.x % (unsigned)slices), bh = (int)(blockIdx.x / (unsigned)slices);
+  const int h = bh % P.H, b = bh / P.H;
+  const int half = threadIdx.x >> 7, col = threadIdx.x & 127;
+#pragma unroll
+  for (int t = 0; t < kRepackMax; ++t) {
+    if (t >= a.n) break;
+    const RepackT x = a.t[t];
+    const SideRows r = side_rows(x.side ? P.ks : P.qs, b);
+    const long long rows = a.out ? (r.room > r.n ? r.room : r.n) : r.n;
+    const int w = a.out ? x.cols : a.pad;  // columns written
+    if (col >= w) continue;
+    for (long long i = 2LL * sl + half; i < rows; i += 2LL * slices) {
+      const long long row = r.r0 + i;
+      const long long so = b * x.src.sb + h * x.src.sh + row * x.src.ss + col;
+      const long long d = b * x.dst.sb + h * x.dst.sh + row * x.dst.ss + col;
+      const bool have = a.out || col < x.cols;
+      if (a.esz == 2) {
+        const uint16_t v = have ? ((const uint16_t*)x.src.ptr)[so] : (uint16_t)0;
+        ((uint16_t*)x.dst.ptr)[d] = v;
+      } else {
+        const uint32_t v = have ? ((const uint32_t*)x.src.ptr)[so] : 0u;
+        ((uint32_t*)x.dst.ptr)[d] = v;
+      }
+    }
+  }
+}
+
+template <class Ex>
+hipError_t launch_repack(const RepackArgs& a, const Ex& ex) {
+  if (a.n == 0 || a.pad > 128) return a.n == 0 ? hipSuccess : hipErrorInvalidValue;
+  const long long nbh = (long long)a.p.B * a.p.H;
+  if (nbh == 0) return hipSuccess;
+  const int rows = a.p.Sq > a.p.Sk ? a.p.Sq : a.p.Sk;
+  const int slices = rows < 2 ? 1 : (rows / 2 < 64 ? rows / 2 : 64);
+  if (nbh * slices > 0x7fffffffLL) return hipErrorInvalidValue;
+  return ex(reinterpret_cast<const void*>(&attn_repack_kernel), "attn_repack_kernel", (unsigned)(nbh * slices), 256u,
+            a, slices);
+}
+template hipError_t launch_repack<Enqueue>(const RepackArgs&, const Enqueue&);
+template hipError_t launch_repack<Record>(const RepackArgs&, const Record&);
+
 template <class Ex>
 static hipError_t launch_fwd_any(int dtype, int head_dim, const FwdArgs& a, const Ex& ex) {
   hipError_t err;

@@ -157,7 +157,7 @@ inline int device_cu_count() {
 }
 
 // The launches of one call, as the C ABI's plan queries report them.
-constexpr int kPlanMax = 4;
+constexpr int kPlanMax = 8;
 struct PlanEntry {
   const char* name;  // kernel function name (without template arguments)
   unsigned grid, block;
@@ -202,5 +202,29 @@ hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, con
 template <class Ex>
 hipError_t launch_pad_rows(const ProblemArgs& p, Operand t0, Operand t1, float* lse, int side, int row_bytes,
                            int esz, const Ex& ex);
+
+// Copies between a caller's tensor and its zero-padded copy (repacked
+// calls).  Inward (out = 0): each sequence's rows (its length) of src, cols
+// columns, into dst with columns [cols, pad) zeroed.  Outward (out = 1):
+// the first cols columns of each sequence's rows up to its room (the rows
+// the kernels write: lengths, then masked padding rows) from the copy src
+// back to the caller's dst.  Rows are addressed as the kernels address
+// them (storage row r0 + i of sequence b), in both tensors.
+struct RepackT {
+  Operand src, dst;
+  int side;  // 0: query rows, 1: key rows
+  int cols;  // the caller's columns
+};
+constexpr int kRepackMax = 5;
+struct RepackArgs {
+  ProblemArgs p;
+  RepackT t[kRepackMax];
+  int n;    // tensors used
+  int out;  // direction
+  int pad;  // columns of the copies (<= 128)
+  int esz;  // element size
+};
+template <class Ex>
+hipError_t launch_repack(const RepackArgs& a, const Ex& ex);
 
 }  // namespace sdpa

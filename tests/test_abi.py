@@ -44,7 +44,7 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "attn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n",
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n",
          sizeof(attn_fwd_params), sizeof(attn_bwd_params),
          offsetof(attn_fwd_params, total_q), offsetof(attn_fwd_params, q),
          offsetof(attn_fwd_params, o_stride), offsetof(attn_bwd_params, dout),
@@ -52,9 +52,10 @@ int main(void) {
          offsetof(attn_fwd_params, varlen), offsetof(attn_fwd_params, seqstart_q),
          offsetof(attn_fwd_params, seqstart_k), offsetof(attn_fwd_params, bias),
          offsetof(attn_fwd_params, bias_stride), offsetof(attn_fwd_params, alibi_slopes),
-         offsetof(attn_fwd_params, dropout_p), offsetof(attn_fwd_params, reserved2),
+         offsetof(attn_fwd_params, dropout_p), offsetof(attn_fwd_params, head_dim_v),
          offsetof(attn_fwd_params, philox_seed), offsetof(attn_fwd_params, philox_offset),
-         offsetof(attn_bwd_params, dbias), offsetof(attn_bwd_params, dbias_stride));
+         offsetof(attn_bwd_params, dbias), offsetof(attn_bwd_params, dbias_stride),
+         offsetof(attn_fwd_params, workspace), offsetof(attn_fwd_params, workspace_bytes));
   return 0;
 }
 """)
@@ -67,8 +68,9 @@ int main(void) {
             bd.BwdParams.dout.offset, bd.BwdParams.workspace.offset, bd.BwdParams.workspace_bytes.offset,
             bd.FwdParams.varlen.offset, bd.FwdParams.seqstart_q.offset, bd.FwdParams.seqstart_k.offset,
             bd.FwdParams.bias.offset, bd.FwdParams.bias_stride.offset, bd.FwdParams.alibi_slopes.offset,
-            bd.FwdParams.dropout_p.offset, bd.FwdParams.reserved2.offset, bd.FwdParams.philox_seed.offset,
-            bd.FwdParams.philox_offset.offset, bd.BwdParams.dbias.offset, bd.BwdParams.dbias_stride.offset]
+            bd.FwdParams.dropout_p.offset, bd.FwdParams.head_dim_v.offset, bd.FwdParams.philox_seed.offset,
+            bd.FwdParams.philox_offset.offset, bd.BwdParams.dbias.offset, bd.BwdParams.dbias_stride.offset,
+            bd.FwdParams.workspace.offset, bd.FwdParams.workspace_bytes.offset]
     assert got == want
 
 
@@ -134,7 +136,13 @@ def test_valid_calls_pass():
     for dt in (bd.FP32, bd.FP16, bd.BF16):
         for D in (32, 48, 64, 80, 96, 128):
             assert fcheck(dense_params(D=D, dtype=dt)) == OK
-        for D in (16, 40, 72, 112, 160, 256):
+        for D in (1, 16, 40, 72, 112, 127):          # repacked: a workspace is required
+            p = dense_params(D=D, dtype=dt)
+            assert fcheck(p) == INVALID
+            p.workspace, p.workspace_bytes = addr(30), 1 << 30
+            assert fcheck(p) == OK
+            assert bcheck(bwd_params(dense_params(D=D, dtype=dt))) == OK
+        for D in (129, 160, 256):
             assert fcheck(dense_params(D=D, dtype=dt)) == NOTSUP
 
 
@@ -147,9 +155,13 @@ def test_valid_calls_pass():
     ("seqlen_k", -5, INVALID), ("batch", -1, INVALID),
     ("scale", float("inf"), INVALID), ("scale", float("nan"), INVALID),
     ("q", 0, INVALID), ("lse", 0, INVALID), ("o", 0, INVALID),
-    ("k", BASE + 8, INVALID),               # not 16-byte aligned
+    ("k", BASE + 8, INVALID),               # not 16-byte aligned: repacked, and no workspace
+    ("k", BASE + 1, INVALID),               # not element-aligned
     ("cu_seqlens_q", BASE, INVALID),        # dense with cu_seqlens
-    ("head_dim", 112, NOTSUP), ("head_dim", 256, NOTSUP), ("head_dim", 72, NOTSUP),
+    ("head_dim", 112, INVALID), ("head_dim", 72, INVALID),   # repacked, and no workspace
+    ("head_dim_v", 32, INVALID),            # likewise
+    ("head_dim", 256, NOTSUP), ("head_dim", 129, NOTSUP), ("head_dim_v", 200, NOTSUP),
+    ("head_dim_v", -1, INVALID),
 ])
 def test_fwd_validation_errors(field, value, code):
     p = dense_params()
@@ -229,23 +241,31 @@ def test_negative_row_strides_validate_and_overlap():
 
 def test_tile_span_limit():
     """The 16-bit kernels address a 64-row tile with 32-bit byte offsets, so a
-    row stride whose 63 steps plus one row reach 2 GiB is not supported there;
-    fp32 takes the register-staged path and accepts it."""
+    call with a row stride whose 63 steps plus one row reach 2 GiB runs
+    repacked (a forward without workspace is then invalid); fp32 takes the
+    register-staged path in place."""
     def with_k_stride(rs, dtype, bwd=False):
         p = dense_params(B=1, H=1, D=64, dtype=dtype)
         p.k = addr(20)  # far from the other operands
         p.k_stride = bd._I64x3(64 * rs, 64 * rs, rs)
         return bcheck(bwd_params(p)) if bwd else fcheck(p)
     below, at = 17_043_512, 17_043_520  # (63 * rs + 64) * 2 bytes: just below / at 2^31
+    lib = bd.lib()
     for dt in (bd.BF16, bd.FP16):
         assert with_k_stride(below, dt) == OK
-        assert with_k_stride(at, dt) == NOTSUP
-        assert with_k_stride(at, dt, bwd=True) == NOTSUP
+        assert with_k_stride(at, dt) == INVALID
+        assert with_k_stride(at, dt, bwd=True) == OK
     assert with_k_stride(at, bd.FP32) == OK
+    p = dense_params(B=1, H=1, D=64)
+    assert lib.attn_fwd_workspace_size(ctypes.byref(p)) == 0
+    p.k, p.k_stride = addr(20), bd._I64x3(64 * at, 64 * at, at)
+    assert lib.attn_fwd_workspace_size(ctypes.byref(p)) > 0
     p = bwd_params(dense_params(B=1, H=1, D=64))
+    ws0 = lib.attn_bwd_workspace_size(ctypes.byref(p))
     p.dout = addr(20)
     p.do_stride = bd._I64x3(64 * at, 64 * at, at)
-    assert bcheck(p) == NOTSUP
+    assert bcheck(p) == OK
+    assert lib.attn_bwd_workspace_size(ctypes.byref(p)) > ws0
 
 
 def test_packed_validation_errors():
@@ -279,8 +299,16 @@ def test_bwd_validation_errors():
     p = bwd_params(dense_params())
     p.dout = None
     assert bcheck(p) == INVALID
-    p = bwd_params(dense_params(D=112))
+    p = bwd_params(dense_params(D=160))
     assert bcheck(p) == NOTSUP
+    p = bwd_params(dense_params(D=112))                  # repacked
+    assert bcheck(p) == OK
+    p.workspace_bytes = lib_ws(p) - 1
+    assert bcheck(p) == INVALID
+
+
+def lib_ws(p):
+    return bd.lib().attn_bwd_workspace_size(ctypes.byref(p))
 
 
 def split_bytes(f):
@@ -398,7 +426,7 @@ def test_plan_validation_errors():
     bad = dense_params()
     bad.version = 9
     assert lib.attn_fwd_plan(ctypes.byref(bad), None, ctypes.byref(pl)) == INVALID
-    assert lib.attn_fwd_plan(ctypes.byref(dense_params(D=112)), None, ctypes.byref(pl)) == NOTSUP
+    assert lib.attn_fwd_plan(ctypes.byref(dense_params(D=160)), None, ctypes.byref(pl)) == NOTSUP
     assert lib.attn_fwd_plan(ctypes.byref(dense_params()), None, None) == INVALID
     bp = bwd_params(dense_params())
     for steps in (0, 8, 9, 15):
@@ -416,7 +444,7 @@ def test_noalloc_validation_and_limit():
     p = bwd_params(dense_params())
     p.dq = p.fwd.q
     assert lib.attn_bwd_noalloc(ctypes.byref(p), None) == INVALID
-    p = bwd_params(dense_params(D=112))
+    p = bwd_params(dense_params(D=160))
     assert lib.attn_bwd_noalloc(ctypes.byref(p), None) == NOTSUP
     # 3 x 16 x 87382 query rows: 2 x 16 MiB of workspace > the 16 MiB limit.
     f = dense_params(B=3, H=16, S=87382)
@@ -465,7 +493,7 @@ def test_version2_structs_are_translated():
         assert lib.attn_bwd_check(bp) == OK
         assert lib.attn_bwd_workspace_size(bp) == lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f)))
     # Version-2 errors stay errors.
-    bad = to_v2(dense_params(D=112), FwdParamsV2)
+    bad = to_v2(dense_params(D=160), FwdParamsV2)
     assert lib.attn_fwd_check(ctypes.cast(ctypes.byref(bad), ctypes.POINTER(bd.FwdParams))) == NOTSUP
     b2 = to_v2(bwd_params(dense_params()), BwdParamsV2)
     b2.dq = b2.fwd.q
@@ -577,8 +605,8 @@ def test_varlen_mixed_extents():
 
 
 def test_feature_fields_validate():
-    """Bias, ALiBi, dropout and dbias: well-formed values pass; a set
-    reserved2, a dropout probability outside [0, 1) or NaN, misaligned
+    """Bias, ALiBi, dropout and dbias: well-formed values pass; a dropout
+    probability outside [0, 1) or NaN, misaligned
     pointers, and outputs overlapping the bias, the slopes or each other are
     rejected before any HIP call."""
     B, H, S, D = 2, 3, 64, 64
@@ -596,9 +624,6 @@ def test_feature_fields_validate():
     assert fcheck(feat(bias_stride=(0, 0, S))) == OK        # one [Sq, Sk] bias for all
     assert fcheck(feat(bias_stride=(0, 0, 0))) == OK        # one row for every query
     assert fcheck(feat(dropout_p=0.0)) == OK
-    p = feat()
-    p.reserved2 = 1
-    assert fcheck(p) == INVALID
     for dp in (1.0, 1.5, -0.1, float("nan")):
         assert fcheck(feat(dropout_p=dp)) == INVALID, dp
     assert fcheck(feat(bias=addr(20) + 1)) == INVALID       # not element-aligned
@@ -653,3 +678,29 @@ def test_feature_calls_plan_feature_kernels(dtype, D):
         names = [pl.kernel[i].decode() for i in range(pl.count)]
         sfx = "16" if dtype != bd.FP32 else ""
         assert names == ["attn_bwd_pre_kernel", f"attn_bwd_dkdv{sfx}_kernel", f"attn_bwd_dq{sfx}_kernel"], names
+
+
+def test_repacked_workspace_sizes():
+    """Workspace of a repacked call (head dims outside the built set, a
+    value head dim of its own, or rows not 16-byte aligned): padded copies
+    with rows of Dp elements (Dp the smallest built dim >= both head dims),
+    each rounded up to 256 bytes; forward q, k, v, o; backward also dout, dq,
+    dk, dv, then the in-place workspace of the problem at Dp."""
+    lib = bd.lib()
+    r256 = lambda n: -(-n // 256) * 256
+    for D, DV, Dp, dt, esz in ((67, 67, 80, bd.BF16, 2), (64, 128, 128, bd.FP16, 2), (13, 7, 32, bd.FP32, 4),
+                               (96, 48, 96, bd.BF16, 2)):
+        B, H, Sq, Sk = 2, 3, 100, 70
+        f = dense_params(B=B, H=H, S=Sq, Sk=Sk, D=D, dtype=dt)
+        f.head_dim_v = DV
+        sq, sk = r256(B * Sq * H * Dp * esz), r256(B * Sk * H * Dp * esz)
+        assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == 2 * sq + 2 * sk, (D, DV)
+        inner = dense_params(B=B, H=H, S=Sq, Sk=Sk, D=Dp, dtype=dt)
+        inner_ws = lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(inner)))
+        assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f))) == 4 * sq + 4 * sk + inner_ws, (D, DV)
+    f = dense_params(D=64)
+    assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == 0
+    f.q_stride = bd._I64x3(3 * 64 * 65, 64 * 65, 65)       # rows 130 bytes apart: repacked
+    assert lib.attn_fwd_workspace_size(ctypes.byref(f)) > 0
+    f.head_dim = 200
+    assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == 0  # malformed (not built)

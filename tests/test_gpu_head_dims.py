@@ -1,0 +1,213 @@
+"""Head dims outside the built set and a value head dim different from the
+query/key one (Hdim_vo != Hdim_qk, the AOTriton 0.15b release notes,
+"Kernel Bug Fixes"; prime head dims, the 0.14b notes, "Minor Changes"),
+run as repacked calls: the operands are copied into zero-padded rows of
+the next built dim, the built kernels run there, and the outputs are copied
+back.  Checked against the oracle (forward and backward, dense and packed,
+with windows and with the optional features), and for rows that are merely
+misaligned, bit for bit against the in-place call on aligned copies of the
+same values (same kernels, same arithmetic)."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from parity_util import INF, TOL, max_err, say
+from scaled_dot_product_20_amd import binding as bd
+from scaled_dot_product_20_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _draw(layout, B, H, Sq, Sk, D, DV, dtype, seed, lens=None):
+    if layout == "thd":
+        lq, lk = lens
+        tq, tk = sum(lq), sum(lk)
+        return wl.draw([(tq, H, D), (tk, H, D), (tk, H, DV), (tq, H, DV)], seed, dtype)
+    return wl.draw([(B, H, Sq, D), (B, H, Sk, D), (B, H, Sk, DV), (B, H, Sq, DV)], seed, dtype)
+
+
+def _run(q, k, v, do, kw):
+    gq, gk, gv, gdo = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = bd.attn_fwd(gq, gk, gv, **kw)
+    dq, dk, dv = bd.attn_bwd(gdo, gq, gk, gv, o, lse, **kw)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+def _check(name, got, ref, dtype, D, scale):
+    tol = TOL[dtype] * max(1.0, abs(scale) * math.sqrt(D))
+    o_tol = tol if dtype == torch.float32 else TOL[dtype]
+    errs = {"O": max_err(f"{name} O", got[0], ref[0], o_tol),
+            "LSE": max_err(f"{name} LSE", got[1], ref[1], tol, inf_exact=True)}
+    for n, g, r in zip(("dQ", "dK", "dV"), got[2:], ref[2:]):
+        errs[n] = max_err(f"{name} {n}", g, r, 2 * tol)
+    say("  errs", {k: f"{e:.2e}" for k, e in errs.items()})
+
+
+# (layout, B, H, Sq, Sk, D, DV, dtype, window, diag, lens)
+CASES = [
+    ("bhsd", 2, 2, 77, 130, 7, 7, torch.bfloat16, (INF, INF), "top_left", None),
+    ("bhsd", 1, 3, 129, 65, 13, 13, torch.float16, (INF, 0), "bottom_right", None),
+    ("bhsd", 2, 1, 100, 100, 67, 67, torch.bfloat16, (30, 5), "top_left", None),
+    ("bhsd", 1, 2, 70, 140, 113, 113, torch.float32, (INF, INF), "top_left", None),
+    ("bhsd", 1, 2, 65, 65, 127, 127, torch.bfloat16, (INF, 0), "top_left", None),
+    ("bhsd", 2, 2, 90, 120, 1, 1, torch.float16, (INF, INF), "top_left", None),
+    ("bhsd", 2, 2, 130, 97, 64, 128, torch.bfloat16, (INF, INF), "top_left", None),
+    ("bhsd", 1, 3, 97, 200, 128, 64, torch.float16, (INF, 0), "bottom_right", None),
+    ("bhsd", 2, 2, 64, 64, 96, 48, torch.float32, (16, 16), "top_left", None),
+    ("bhsd", 1, 2, 150, 70, 32, 80, torch.bfloat16, (INF, 0), "top_left", None),
+    ("bhsd", 1, 2, 33, 47, 13, 7, torch.float32, (INF, INF), "top_left", None),
+    ("thd", None, 2, None, None, 72, 40, torch.bfloat16, (64, 0), "bottom_right", ([70, 0, 130], [90, 5, 129])),
+    ("thd", None, 3, None, None, 19, 19, torch.float16, (INF, INF), "top_left", ([33, 1, 65], [40, 64, 2])),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_head_dims_match_oracle(case):
+    layout, B, H, Sq, Sk, D, DV, dtype, window, diag, lens = CASES[case]
+    seed = 1100 + case
+    say(f"head-dim case {case}: layout={layout} B={B} H={H} Sq={Sq} Sk={Sk} D={D} DV={DV} dtype={dtype} "
+        f"window={window} diag={diag} lens={lens} seed={seed}")
+    q, k, v, do = _draw(layout, B, H, Sq, Sk, D, DV, dtype, seed, lens)
+    scale = 1.0 / math.sqrt(D)
+    kwo = dict(scale=scale, window=window, diag=diag)
+    kwg = dict(kwo)
+    if layout == "thd":
+        cuq, cuk = wl.prefix(lens[0]), wl.prefix(lens[1])
+        kwo.update(cu_seqlens_q=cuq, cu_seqlens_k=cuk)
+        kwg.update(cu_seqlens_q=torch.from_numpy(cuq).to(DEV), cu_seqlens_k=torch.from_numpy(cuk).to(DEV),
+                   max_seqlen_q=max(lens[0]), max_seqlen_k=max(lens[1]))
+    got = _run(q, k, v, do, kwg)
+    assert got[0].shape[-1] == DV and got[4].shape[-1] == DV and got[2].shape[-1] == D
+    ref = orc.bwd(q, k, v, do, **kwo)
+    _check(f"case {case}", got, ref, dtype, D, scale)
+
+
+def test_repacked_plan_and_workspace():
+    """A repacked call's plan starts with the copy-in and ends with the
+    copy-back kernel around the built kernels at the padded dim; both
+    workspace sizes are positive, and zero for the in-place call."""
+    q, k, v, do = (t.to(DEV) for t in _draw("bhsd", 1, 2, 64, 64, 67, 40, torch.bfloat16, 5))
+    o = torch.empty(1, 2, 64, 40, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(1, 2, 64, dtype=torch.float32, device=DEV)
+    kw = bd._problem(q, scale=0.2)
+    p = bd.fwd_params(q, k, v, o, lse, **kw)
+    assert p.head_dim == 67 and p.head_dim_v == 40
+    assert bd.lib().attn_fwd_workspace_size(ctypes.byref(p)) > 0
+    names = [n for n, _, _ in bd.plan("attn_fwd", p)]
+    assert names[0] == "attn_repack_kernel" and names[-1] == "attn_repack_kernel", names
+    bp, _ = bd.prepare_bwd(do, q, k, v, o, lse, scale=0.2)
+    names = [n for n, _, _ in bd.plan("attn_bwd", bp)]
+    assert names[0] == "attn_repack_kernel" and names[-1] == "attn_repack_kernel", names
+    q2, k2, v2 = (t.to(DEV) for t in _draw("bhsd", 1, 2, 64, 64, 64, 64, torch.bfloat16, 5)[:3])
+    p2 = bd.fwd_params(q2, k2, v2, torch.empty_like(q2), lse, **bd._problem(q2, scale=0.2))
+    assert bd.lib().attn_fwd_workspace_size(ctypes.byref(p2)) == 0
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 64), (torch.float16, 128), (torch.float32, 80)])
+def test_misaligned_rows_equal_aligned_bits(dtype, D):
+    """Operands whose rows start one element past a 16-byte boundary (views
+    into a buffer at offset 1) run repacked, at the same built dim: the
+    results equal the in-place call's on aligned copies bit for bit."""
+    B, H, S = 2, 3, 97
+    q, k, v, do = (t.to(DEV) for t in wl.draw([(B, H, S, D)] * 4, 77, dtype))
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
+        x = buf[1:].view(t.shape)
+        x.copy_(t)
+        return x
+    kw = dict(scale=1.0 / math.sqrt(D), window=(40, 3), diag="bottom_right")
+    ref = [t.clone() for t in (*bd.attn_fwd(q, k, v, **kw), )]
+    ref += list(bd.attn_bwd(do, q, k, v, ref[0], ref[1], **kw))
+    qs, ks, vs, dos = (shifted(t) for t in (q, k, v, do))
+    os_ = shifted(torch.zeros_like(q))
+    lse = torch.empty_like(ref[1])
+    bd.attn_fwd(qs, ks, vs, out=os_, lse=lse, **kw)
+    dq, dk, dv = (shifted(torch.zeros_like(t)) for t in (q, k, v))
+    bd.attn_bwd(dos, qs, ks, vs, os_, lse, dq=dq, dk=dk, dv=dv, **kw)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), ref, (os_, lse, dq, dk, dv)):
+        assert torch.equal(a, b), name
+
+
+def test_repacked_stage_calls_and_noalloc_equal_attn_bwd():
+    """The step calls of a repacked backward (preprocess makes the copies,
+    dK/dV and dQ copy back) and the no-allocation call give attn_bwd's bits."""
+    q, k, v, do = (t.to(DEV) for t in _draw("bhsd", 2, 2, 90, 70, 24, 40, torch.bfloat16, 9))
+    kw = dict(scale=0.25, window=(INF, 0), diag="bottom_right")
+    o, lse = bd.attn_fwd(q, k, v, **kw)
+    ref = bd.attn_bwd(do, q, k, v, o, lse, **kw)
+    for calls in (("attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq"),
+                  ("attn_bwd_preprocess", "attn_bwd_dkdv_dq")):
+        bp, keep = bd.prepare_bwd(do, q, k, v, o, lse, **kw)
+        for name in calls:
+            bd.launch(name, bp)
+        torch.cuda.synchronize()
+        for n, a, b in zip(("dq", "dk", "dv"), ref, keep[:3]):
+            assert torch.equal(a, b), (calls, n)
+    outs = [torch.full_like(t, 5.0) for t in (q, k, v)]
+    bd.attn_bwd_noalloc(do, q, k, v, o, lse, *outs, **kw)
+    torch.cuda.synchronize()
+    for n, a, b in zip(("dq", "dk", "dv"), ref, outs):
+        assert torch.equal(a, b), ("noalloc", n)
+
+
+def test_repacked_with_features_and_gapped_rows():
+    """Repacked calls keep the optional features (bias, dropout, dbias) and
+    per-side addressing: a stacked K side whose sequences sit at array start
+    rows with gaps keeps the gap rows untouched after the copy back."""
+    H, D, DV, dtype = 2, 21, 34, torch.float16
+    lq, lk = [40, 3, 66], [50, 20, 77]
+    cuq = wl.prefix(lq)
+    q, k, v, do = wl.draw([(sum(lq), H, D), (sum(lk), H, D), (sum(lk), H, DV), (sum(lq), H, DV)], 31, dtype)
+    # K side stored in reverse order with 2-row gaps (start array), V alike.
+    starts, row = [0] * 3, 2
+    for b in reversed(range(3)):
+        starts[b] = row
+        row += lk[b] + 2
+    total_k = row
+    cuk = wl.prefix(lk)
+
+    def place(t):
+        out = torch.full((total_k,) + tuple(t.shape[1:]), 9.0, dtype=t.dtype)
+        for b in range(3):
+            out[starts[b]:starts[b] + lk[b]] = t[int(cuk[b]):int(cuk[b + 1])]
+        return out
+    ks, vs = place(k), place(v)
+    bias = wl.draw([(3, H, max(lq), max(lk))], 32, dtype)[0]
+    feat = dict(bias=bias, dropout_p=0.2, philox_seed=77, philox_offset=5)
+    ST, LC, PC, LA, PA = bd.SEQ_STACKED, bd.SEQ_LEN_CUMSUM, bd.SEQ_POS_CUMSUM, bd.SEQ_LEN_ARRAY, bd.SEQ_POS_ARRAY
+    kw = dict(scale=0.3, window=(INF, 0), diag="bottom_right", q_mode=ST | LC | PC, k_mode=ST | LA | PA,
+              cu_seqlens_q=torch.from_numpy(cuq).to(DEV), seqused_k=torch.tensor(lk, dtype=torch.int32, device=DEV),
+              seqstart_k=torch.tensor(starts, dtype=torch.int32, device=DEV), max_seqlen_q=max(lq),
+              max_seqlen_k=max(lk), batch=3, bias=bias.to(DEV), dropout_p=0.2, philox_seed=77, philox_offset=5)
+    gq, gk, gv, gdo = (t.to(DEV) for t in (q, ks, vs, do))
+    o, lse = bd.attn_fwd(gq, gk, gv, **kw)
+    dbias = torch.zeros(3, H, max(lq), max(lk), dtype=torch.float32, device=DEV)
+    dk = torch.full_like(gk, 9.0)
+    dv = torch.full_like(gv, 9.0)
+    dq, dk, dv = bd.attn_bwd(gdo, gq, gk, gv, o, lse, dk=dk, dv=dv, dbias=dbias, **kw)
+    torch.cuda.synchronize()
+    ref = orc.bwd(q, k, v, do, scale=0.3, window=(INF, 0), diag="bottom_right", cu_seqlens_q=cuq,
+                  cu_seqlens_k=cuk, want_dbias=True, max_seqlen_q=max(lq), max_seqlen_k=max(lk), **feat)
+
+    def gather(t):
+        return torch.cat([t[starts[b]:starts[b] + lk[b]] for b in range(3)]).cpu()
+    tol = TOL[dtype] * max(1.0, 0.3 * math.sqrt(D)) * math.sqrt(2.0) / 0.8
+    max_err("O", o, ref[0], TOL[dtype] / 0.8)
+    max_err("LSE", lse, ref[1], tol, inf_exact=True)
+    max_err("dQ", dq, ref[2], 2 * tol)
+    max_err("dK", gather(dk), ref[3], 2 * tol)
+    max_err("dV", gather(dv), ref[4], 2 * tol)
+    max_err("dBias", dbias, ref[5], 2 * tol)
+    covered = np.zeros(total_k, dtype=bool)
+    for b in range(3):
+        covered[starts[b]:starts[b] + lk[b]] = True
+    gap = torch.from_numpy(~covered)
+    assert torch.all(dk.cpu()[gap] == 9.0) and torch.all(dv.cpu()[gap] == 9.0), "gap rows written"
