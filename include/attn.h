@@ -37,9 +37,8 @@
  *    call (null required pointer, version or flags mismatch, negative or
  *    zero sizes where a size is needed, a pointer not aligned to its element
  *    size, workspace too small), hipErrorNotSupported for a well-formed call
- *    outside the built set (head_dim or head_dim_v above 128; for fp16 and
- *    bf16 run in place, a q, k, v or dout row stride so large that 63
- *    strides plus one row reach 2 GiB), or the HIP error of the launch.  Validation makes no HIP call.  The contents of
+ *    outside the built set (head_dim or head_dim_v above 256 for fp16 and
+ *    bf16, above 128 for fp32), or the HIP error of the launch.  Validation makes no HIP call.  The contents of
  *    cu_seqlens arrays are a precondition (0 first, non-decreasing, last
  *    entry equal to total_q / total_k, every length <= the seqlen_q /
  *    seqlen_k maximum) and are not checked: reading them would need a sync.
@@ -148,12 +147,15 @@ typedef struct {
                               VARLEN: number of sequences (>= 1 if a side
                               is stacked) */
   int32_t heads;           /* >= 1; Q, K and V have the same head count */
-  int32_t head_dim;        /* 1..128, of Q and K (and of V, O, dO, dV when
-                              head_dim_v is 0).  32, 48, 64, 80, 96 and 128
+  int32_t head_dim;        /* of Q and K (and of V, O, dO, dV when
+                              head_dim_v is 0): 1..256 for fp16 / bf16,
+                              1..128 for fp32.  32, 48, 64, 80, 96 and 128
                               (the multiples of 16 up to 128 the AOTriton
                               pages name or test, 48 and 80 among them, 0.10b
-                              "Known Problems") run in place; see "Repacked
-                              calls" for the others */
+                              "Known Problems"), and 192 and 256 for fp16 /
+                              bf16 (toward the larger heads of the 0.14b
+                              notes, "Gfx950 Performance Boost"), run in
+                              place; see "Repacked calls" for the others */
   int32_t seqlen_q;        /* BHSD: Sq (>= 0); THD: max sequence length of Q;
                               VARLEN: the Q side's uniform length / room,
                               and the largest length (>= 0) */
@@ -232,7 +234,7 @@ typedef struct {
                               (0.14b "Minor Changes"); kept probabilities are
                               scaled by 1 / (1 - p).  LSE is the softmax's,
                               before dropout. */
-  int32_t head_dim_v;       /* head dim of V, O, dO and dV, 1..128 (Hdim_vo
+  int32_t head_dim_v;       /* head dim of V, O, dO and dV, as head_dim (Hdim_vo
                               of the AOTriton 0.15b notes, "Kernel Bug
                               Fixes"); 0 = head_dim.  A value other than
                               head_dim makes the call a repacked one. */
@@ -247,9 +249,11 @@ typedef struct {
 } attn_fwd_params;
 
 /* Repacked calls.  A call runs in place when head_dim is one of the built
- * dims (32, 48, 64, 80, 96, 128), head_dim_v equals it, and every operand
- * row is 16-byte aligned (base pointers and strides).  Any other call with
- * head dims up to 128 is repacked: the library first copies its inputs,
+ * dims (32, 48, 64, 80, 96, 128; 192 and 256 for fp16 / bf16), head_dim_v
+ * equals it, and every operand row is 16-byte aligned (base pointers and
+ * strides; for fp16 / bf16 also within the tile copies' 2 GiB span: 63 row
+ * strides plus one row).  Any other call with supported head dims is
+ * repacked: the library first copies its inputs,
  * each row zero-padded to Dp columns (the smallest built dim >= both head
  * dims), into the workspace, runs the in-place kernels there at head dim Dp
  * (zero columns add nothing to Q K^T, and give zero columns of O, dQ, dK

@@ -76,13 +76,18 @@ const attn_bwd_params* bwd_v3(const attn_bwd_params* p, attn_bwd_params* tmp) {
 
 bool dtype_ok(int32_t d) { return d == ATTN_FP32 || d == ATTN_FP16 || d == ATTN_BF16; }
 int64_t elem_bytes(int32_t d) { return d == ATTN_FP32 ? 4 : 2; }
-bool head_dim_built(int32_t d) { return d == 32 || d == 48 || d == 64 || d == 80 || d == 96 || d == 128; }
-constexpr int kMaxDim = 128;  // largest built head dim
+// Head dims with kernels built: 32 .. 128 for every dtype, 192 and 256 for
+// fp16 / bf16 (whose accumulators and tiles fit there).
+bool head_dim_built(int32_t d, int32_t dtype) {
+  return d == 32 || d == 48 || d == 64 || d == 80 || d == 96 || d == 128 ||
+         (dtype != ATTN_FP32 && (d == 192 || d == 256));
+}
+int max_dim(int32_t dtype) { return dtype == ATTN_FP32 ? 128 : 256; }
 
-// Smallest built head dim >= d (d <= kMaxDim).
-int padded_dim(int d) {
-  for (int b : {32, 48, 64, 80, 96, 128})
-    if (d <= b) return b;
+// Smallest built head dim >= d (d <= max_dim(dtype)).
+int padded_dim(int d, int32_t dtype) {
+  for (int b : {32, 48, 64, 80, 96, 128, 192, 256})
+    if (d <= b && head_dim_built(b, dtype)) return b;
   return 0;
 }
 
@@ -253,7 +258,7 @@ hipError_t check_problem(const attn_fwd_params* p) {
       !elem_aligned(p->o, esz))
     return hipErrorInvalidValue;
   if (check_feat(p) != hipSuccess) return hipErrorInvalidValue;
-  if (p->head_dim > kMaxDim || dim_v(p) > kMaxDim) return hipErrorNotSupported;
+  if (p->head_dim > max_dim(p->dtype) || dim_v(p) > max_dim(p->dtype)) return hipErrorNotSupported;
   return hipSuccess;
 }
 
@@ -322,7 +327,7 @@ uint64_t inner_ws_bytes(const attn_bwd_params* p) { return delta_bytes(&p->fwd) 
 // it addresses is 16-byte aligned (and, for the 16-bit kernels' tile copies,
 // within the 2 GiB span); any other call runs on zero-padded copies.
 bool in_place_fwd(const attn_fwd_params* p) {
-  if (!head_dim_built(p->head_dim) || dim_v(p) != p->head_dim) return false;
+  if (!head_dim_built(p->head_dim, p->dtype) || dim_v(p) != p->head_dim) return false;
   const Side qs = side_of(p, true), ks = side_of(p, false);
   const int64_t esz = elem_bytes(p->dtype), D = p->head_dim;
   if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o)) return false;
@@ -359,7 +364,7 @@ struct Pack {
 
 Pack pack_of(const attn_fwd_params* f, bool bwd) {
   Pack pk;
-  pk.Dp = padded_dim(std::max(f->head_dim, dim_v(f)));
+  pk.Dp = padded_dim(std::max(f->head_dim, dim_v(f)), f->dtype);
   const Side qs = side_of(f, true), ks = side_of(f, false);
   const uint64_t esz = (uint64_t)elem_bytes(f->dtype), row = (uint64_t)f->heads * pk.Dp * esz;
   const uint64_t rq = (uint64_t)(qs.stacked() ? f->total_q : (int64_t)f->batch * f->seqlen_q);

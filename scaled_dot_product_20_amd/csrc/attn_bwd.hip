@@ -1292,8 +1292,7 @@ struct Dq16 {
             dq[dt] = M::mma(ld_tr<M>(Ks + rbase, lo.tra[dt], lo.trb[dt]), dsf, dq[dt]);
         }
       }
-      return;
-    }
+    } else {
     f32x16 s[KT], dp[KT];
     frag dsf[KT][2];
     auto ds_slice = [&](auto ktc) __attribute__((always_inline)) {
@@ -1339,6 +1338,7 @@ struct Dq16 {
           if constexpr (I == NA - 1) ds_slice(std::integral_constant<int, 0>{});
           if constexpr (I == KT * NA - 1) ds_slice(std::integral_constant<int, 1>{});
         });
+    }
   }
 };
 
@@ -1640,9 +1640,13 @@ template <typename M, int D>
 struct BwdShape {
   static constexpr bool k16 = sizeof(typename M::elem) == 2;
   static constexpr int NW_KV = 4, BMQ = k16 ? 64 : 32;
-  static constexpr int NW_Q = 4, BN = k16 ? 64 : 32;
+  // dQ key tiles: 32 keys above head_dim 128 (K and V tiles of 64 keys would
+  // not fit a stage).
+  static constexpr int NW_Q = 4, BN = k16 ? (D > 128 ? 32 : 64) : 32;
   // dK/dV by producer / consumer wave pairs (128 keys per workgroup, as NW_KV).
-  static constexpr bool PC = k16 && D > 80;
+  static constexpr bool PC = k16 && D > 80 && D <= 128;
+  // Waves per SIMD the registers allow: dK/dV (plain kernel) and dQ.
+  static constexpr int WPE_KV = D > 80 ? 1 : 2, WPE_Q = D > 128 ? 1 : 2;
 };
 
 template <typename M, int D, class Ex>
@@ -1674,7 +1678,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
       if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
       if (nblk > 0) {
         if constexpr (S::k16)
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, (D > 80 ? 1 : 2)>),
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV>),
                    "attn_bwd_dkdv16_kernel", (unsigned)nblk, (unsigned)(NW_KV * 64), a);
         else
           err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>), "attn_bwd_dkdv_kernel",
@@ -1687,8 +1691,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
       if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
       if (nblk > 0) {
         if constexpr (S::k16)
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, 2>), "attn_bwd_dq16_kernel",
-                   (unsigned)nblk, (unsigned)(NW_Q * 64), a);
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, S::WPE_Q>),
+                   "attn_bwd_dq16_kernel", (unsigned)nblk, (unsigned)(NW_Q * 64), a);
         else
           err = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN>), "attn_bwd_dq_kernel",
                    (unsigned)nblk, (unsigned)(NW_Q * 64), a);
@@ -1768,7 +1772,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
         err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16pc_kernel<M, D>), "attn_bwd_dkdv16pc_kernel",
                  (unsigned)nblk, 512u, a);
       else if constexpr (S::k16)
-        err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, 2>),
+        err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV>),
                  "attn_bwd_dkdv16_kernel", (unsigned)nblk, (unsigned)(NW_KV * 64), a);
       else
         err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>), "attn_bwd_dkdv_kernel",
@@ -1783,8 +1787,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (nblk > 0) {
       if constexpr (S::k16)
-        err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, 2>), "attn_bwd_dq16_kernel",
-                 (unsigned)nblk, (unsigned)(NW_Q * 64), a);
+        err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, S::WPE_Q>),
+                 "attn_bwd_dq16_kernel", (unsigned)nblk, (unsigned)(NW_Q * 64), a);
       else
         err = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN>), "attn_bwd_dq_kernel",
                  (unsigned)nblk, (unsigned)(NW_Q * 64), a);
@@ -1803,6 +1807,12 @@ static hipError_t launch_bwd_d(int head_dim, const BwdArgs& a, int stages, const
     case 80: return launch_bwd_t<M, 80>(a, stages, ex);
     case 96: return launch_bwd_t<M, 96>(a, stages, ex);
     case 128: return launch_bwd_t<M, 128>(a, stages, ex);
+    case 192:
+      if constexpr (sizeof(typename M::elem) == 2) return launch_bwd_t<M, 192>(a, stages, ex);
+      return hipErrorNotSupported;
+    case 256:
+      if constexpr (sizeof(typename M::elem) == 2) return launch_bwd_t<M, 256>(a, stages, ex);
+      return hipErrorNotSupported;
     default: return hipErrorNotSupported;
   }
 }

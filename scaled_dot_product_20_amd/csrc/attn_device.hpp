@@ -310,12 +310,14 @@ namespace sdpa {
 // leaves slots unused.
 template <int D>
 struct Swz {
-  static constexpr int CH = D / 8;                // chunks holding data
-  static constexpr int SLOTS = D <= 64 ? 8 : 16;  // chunk slots per row
-  static constexpr int PITCH = SLOTS * 8;         // elements per row
-  static_assert(D % 16 == 0 && D <= 128, "head_dim must be a multiple of 16, at most 128");
+  static constexpr int CH = D / 8;                                   // chunks holding data
+  static constexpr int SLOTS = D <= 64 ? 8 : (D <= 128 ? 16 : 32);  // chunk slots per row
+  static constexpr int PITCH = SLOTS * 8;                            // elements per row
+  static_assert(D % 16 == 0 && D <= 256, "head_dim must be a multiple of 16, at most 256");
+  // Rows of 32 slots (512 bytes) start on the same bank as rows of 16; the
+  // same 16 XOR patterns spread a column over every bank.
   __host__ __device__ static constexpr int sigma(int r) {
-    return SLOTS == 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    return SLOTS >= 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
   }
   // Element offset of chunk c of row r.
   __host__ __device__ static constexpr int off(int r, int c) { return r * PITCH + ((c ^ sigma(r)) << 3); }

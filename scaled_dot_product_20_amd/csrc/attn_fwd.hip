@@ -1040,11 +1040,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <typename M, int D>
 struct FwdShape {
   static constexpr bool k16 = sizeof(typename M::elem) == 2;
-  static constexpr bool PP = k16;  // ping-pong kernel built (8 waves, 256 rows)
+  static constexpr bool PP = k16 && D <= 128;  // ping-pong kernel built (8 waves, 256 rows)
   static constexpr int RB = 1;
   static constexpr int NW = k16 ? (D > 80 ? 4 : 8) : 4;
   static constexpr int BN = 64;
-  static constexpr int WPE = 2;  // waves per SIMD the registers allow
+  static constexpr int WPE = D > 128 ? 1 : 2;  // waves per SIMD the registers allow
 };
 
 template <typename M, int D, class Ex>
@@ -1072,7 +1072,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, const Ex& ex) {
   if (nblk == 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
   if constexpr (S::k16) {
-    if (pp) {
+    if constexpr (S::PP) if (pp) {
       // Full rounds of 256-row workgroups (pp_per_cu per CU) on the
       // ping-pong kernel.  With at most three of them, a last round at most
       // a quarter full goes to the split tail kernel, which then fills every
@@ -1108,6 +1108,12 @@ static hipError_t launch_fwd_d(int head_dim, const FwdArgs& a, const Ex& ex) {
     case 80: return launch_fwd_t<M, 80>(a, ex);
     case 96: return launch_fwd_t<M, 96>(a, ex);
     case 128: return launch_fwd_t<M, 128>(a, ex);
+    case 192:
+      if constexpr (sizeof(typename M::elem) == 2) return launch_fwd_t<M, 192>(a, ex);
+      return hipErrorNotSupported;
+    case 256:
+      if constexpr (sizeof(typename M::elem) == 2) return launch_fwd_t<M, 256>(a, ex);
+      return hipErrorNotSupported;
     default: return hipErrorNotSupported;
   }
 }
@@ -1171,7 +1177,7 @@ template hipError_t launch_pad_rows<Record>(const ProblemArgs&, Operand, Operand
                                             const Record&);
 
 // One workgroup per (sequence, head) and slice of its rows; half a
-// workgroup per row (128 columns at most), element by element, so rows of
+// workgroup per row (128 columns per pass), element by element, so rows of
 // any alignment and width are copied.
 __global__ __launch_bounds__(256) void attn_repack_kernel(RepackArgs a, int slices) {
   const ProblemArgs& P = a.p;
@@ -1185,18 +1191,19 @@ __global__ __launch_bounds__(256) void attn_repack_kernel(RepackArgs a, int slic
     const SideRows r = side_rows(x.side ? P.ks : P.qs, b);
     const long long rows = a.out ? (r.room > r.n ? r.room : r.n) : r.n;
     const int w = a.out ? x.cols : a.pad;  // columns written
-    if (col >= w) continue;
     for (long long i = 2LL * sl + half; i < rows; i += 2LL * slices) {
       const long long row = r.r0 + i;
-      const long long so = b * x.src.sb + h * x.src.sh + row * x.src.ss + col;
-      const long long d = b * x.dst.sb + h * x.dst.sh + row * x.dst.ss + col;
-      const bool have = a.out || col < x.cols;
-      if (a.esz == 2) {
-        const uint16_t v = have ? ((const uint16_t*)x.src.ptr)[so] : (uint16_t)0;
-        ((uint16_t*)x.dst.ptr)[d] = v;
-      } else {
-        const uint32_t v = have ? ((const uint32_t*)x.src.ptr)[so] : 0u;
-        ((uint32_t*)x.dst.ptr)[d] = v;
+      for (int c = col; c < w; c += 128) {
+        const long long so = b * x.src.sb + h * x.src.sh + row * x.src.ss + c;
+        const long long d = b * x.dst.sb + h * x.dst.sh + row * x.dst.ss + c;
+        const bool have = a.out || c < x.cols;
+        if (a.esz == 2) {
+          const uint16_t v = have ? ((const uint16_t*)x.src.ptr)[so] : (uint16_t)0;
+          ((uint16_t*)x.dst.ptr)[d] = v;
+        } else {
+          const uint32_t v = have ? ((const uint32_t*)x.src.ptr)[so] : 0u;
+          ((uint32_t*)x.dst.ptr)[d] = v;
+        }
       }
     }
   }
@@ -1204,7 +1211,7 @@ __global__ __launch_bounds__(256) void attn_repack_kernel(RepackArgs a, int slic
 
 template <class Ex>
 hipError_t launch_repack(const RepackArgs& a, const Ex& ex) {
-  if (a.n == 0 || a.pad > 128) return a.n == 0 ? hipSuccess : hipErrorInvalidValue;
+  if (a.n == 0 || a.pad > 256) return a.n == 0 ? hipSuccess : hipErrorInvalidValue;
   const long long nbh = (long long)a.p.B * a.p.H;
   if (nbh == 0) return hipSuccess;
   const int rows = a.p.Sq > a.p.Sk ? a.p.Sq : a.p.Sk;

@@ -221,7 +221,7 @@ struct RepackArgs {
   RepackT t[kRepackMax];
   int n;    // tensors used
   int out;  // direction
-  int pad;  // columns of the copies (<= 128)
+  int pad;  // columns of the copies (<= 256)
   int esz;  // element size
 };
 template <class Ex>

@@ -142,7 +142,13 @@ def test_valid_calls_pass():
             p.workspace, p.workspace_bytes = addr(30), 1 << 30
             assert fcheck(p) == OK
             assert bcheck(bwd_params(dense_params(D=D, dtype=dt))) == OK
-        for D in (129, 160, 256):
+        for D in (192, 256):
+            assert fcheck(dense_params(D=D, dtype=dt)) == (NOTSUP if dt == bd.FP32 else OK)
+        for D in (129, 160):
+            p = dense_params(D=D, dtype=dt)
+            p.workspace, p.workspace_bytes = addr(30), 1 << 30
+            assert fcheck(p) == (NOTSUP if dt == bd.FP32 else OK)
+        for D in (257, 512):
             assert fcheck(dense_params(D=D, dtype=dt)) == NOTSUP
 
 
@@ -160,7 +166,8 @@ def test_valid_calls_pass():
     ("cu_seqlens_q", BASE, INVALID),        # dense with cu_seqlens
     ("head_dim", 112, INVALID), ("head_dim", 72, INVALID),   # repacked, and no workspace
     ("head_dim_v", 32, INVALID),            # likewise
-    ("head_dim", 256, NOTSUP), ("head_dim", 129, NOTSUP), ("head_dim_v", 200, NOTSUP),
+    ("head_dim", 129, INVALID), ("head_dim_v", 200, INVALID),  # repacked, and no workspace
+    ("head_dim", 257, NOTSUP), ("head_dim_v", 300, NOTSUP),
     ("head_dim_v", -1, INVALID),
 ])
 def test_fwd_validation_errors(field, value, code):
@@ -299,8 +306,9 @@ def test_bwd_validation_errors():
     p = bwd_params(dense_params())
     p.dout = None
     assert bcheck(p) == INVALID
-    p = bwd_params(dense_params(D=160))
+    p = bwd_params(dense_params(D=300))
     assert bcheck(p) == NOTSUP
+    assert bcheck(bwd_params(dense_params(D=160, dtype=bd.FP32))) == NOTSUP
     p = bwd_params(dense_params(D=112))                  # repacked
     assert bcheck(p) == OK
     p.workspace_bytes = lib_ws(p) - 1
@@ -426,7 +434,7 @@ def test_plan_validation_errors():
     bad = dense_params()
     bad.version = 9
     assert lib.attn_fwd_plan(ctypes.byref(bad), None, ctypes.byref(pl)) == INVALID
-    assert lib.attn_fwd_plan(ctypes.byref(dense_params(D=160)), None, ctypes.byref(pl)) == NOTSUP
+    assert lib.attn_fwd_plan(ctypes.byref(dense_params(D=300)), None, ctypes.byref(pl)) == NOTSUP
     assert lib.attn_fwd_plan(ctypes.byref(dense_params()), None, None) == INVALID
     bp = bwd_params(dense_params())
     for steps in (0, 8, 9, 15):
@@ -444,7 +452,7 @@ def test_noalloc_validation_and_limit():
     p = bwd_params(dense_params())
     p.dq = p.fwd.q
     assert lib.attn_bwd_noalloc(ctypes.byref(p), None) == INVALID
-    p = bwd_params(dense_params(D=160))
+    p = bwd_params(dense_params(D=300))
     assert lib.attn_bwd_noalloc(ctypes.byref(p), None) == NOTSUP
     # 3 x 16 x 87382 query rows: 2 x 16 MiB of workspace > the 16 MiB limit.
     f = dense_params(B=3, H=16, S=87382)
@@ -493,7 +501,7 @@ def test_version2_structs_are_translated():
         assert lib.attn_bwd_check(bp) == OK
         assert lib.attn_bwd_workspace_size(bp) == lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f)))
     # Version-2 errors stay errors.
-    bad = to_v2(dense_params(D=160), FwdParamsV2)
+    bad = to_v2(dense_params(D=300), FwdParamsV2)
     assert lib.attn_fwd_check(ctypes.cast(ctypes.byref(bad), ctypes.POINTER(bd.FwdParams))) == NOTSUP
     b2 = to_v2(bwd_params(dense_params()), BwdParamsV2)
     b2.dq = b2.fwd.q
@@ -689,7 +697,7 @@ def test_repacked_workspace_sizes():
     lib = bd.lib()
     r256 = lambda n: -(-n // 256) * 256
     for D, DV, Dp, dt, esz in ((67, 67, 80, bd.BF16, 2), (64, 128, 128, bd.FP16, 2), (13, 7, 32, bd.FP32, 4),
-                               (96, 48, 96, bd.BF16, 2)):
+                               (96, 48, 96, bd.BF16, 2), (160, 64, 192, bd.BF16, 2), (200, 256, 256, bd.FP16, 2)):
         B, H, Sq, Sk = 2, 3, 100, 70
         f = dense_params(B=B, H=H, S=Sq, Sk=Sk, D=D, dtype=dt)
         f.head_dim_v = DV
@@ -702,5 +710,5 @@ def test_repacked_workspace_sizes():
     assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == 0
     f.q_stride = bd._I64x3(3 * 64 * 65, 64 * 65, 65)       # rows 130 bytes apart: repacked
     assert lib.attn_fwd_workspace_size(ctypes.byref(f)) > 0
-    f.head_dim = 200
-    assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == 0  # malformed (not built)
+    f.head_dim = 300
+    assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == 0  # malformed (above the largest built dim)

@@ -1,7 +1,8 @@
-"""Head dims outside the built set and a value head dim different from the
-query/key one (Hdim_vo != Hdim_qk, the AOTriton 0.15b release notes,
-"Kernel Bug Fixes"; prime head dims, the 0.14b notes, "Minor Changes"),
-run as repacked calls: the operands are copied into zero-padded rows of
+"""Head dims outside the 32..128 set and a value head dim different from
+the query/key one (Hdim_vo != Hdim_qk, the AOTriton 0.15b release notes,
+"Kernel Bug Fixes"; prime head dims, the 0.14b notes, "Minor Changes").
+192 and 256 are built for fp16 / bf16 and run in place; the others run as
+repacked calls: the operands are copied into zero-padded rows of
 the next built dim, the built kernels run there, and the outputs are copied
 back.  Checked against the oracle (forward and backward, dense and packed,
 with windows and with the optional features), and for rows that are merely
@@ -64,6 +65,13 @@ CASES = [
     ("bhsd", 1, 2, 33, 47, 13, 7, torch.float32, (INF, INF), "top_left", None),
     ("thd", None, 2, None, None, 72, 40, torch.bfloat16, (64, 0), "bottom_right", ([70, 0, 130], [90, 5, 129])),
     ("thd", None, 3, None, None, 19, 19, torch.float16, (INF, INF), "top_left", ([33, 1, 65], [40, 64, 2])),
+    # Built above 128 for fp16 / bf16, in place and repacked onto them.
+    ("bhsd", 2, 2, 130, 97, 192, 192, torch.bfloat16, (INF, INF), "top_left", None),
+    ("bhsd", 1, 2, 100, 150, 256, 256, torch.float16, (INF, 0), "bottom_right", None),
+    ("bhsd", 1, 2, 129, 129, 256, 256, torch.bfloat16, (40, 0), "top_left", None),
+    ("bhsd", 1, 2, 70, 90, 160, 160, torch.bfloat16, (INF, INF), "top_left", None),
+    ("bhsd", 1, 2, 64, 64, 200, 72, torch.float16, (INF, 0), "top_left", None),
+    ("thd", None, 2, None, None, 128, 256, torch.bfloat16, (INF, 0), "bottom_right", ([50, 3, 129], [64, 20, 100])),
 ]
 
 
