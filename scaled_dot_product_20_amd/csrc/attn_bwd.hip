@@ -32,13 +32,19 @@ __device__ __forceinline__ void store4b(T* p, float a, float b, float c, float d
 // ------------------------------------------------------------ split mode
 
 // Copy sg of n takes the sg-th of n contiguous, nearly equal shares of the
-// tile range [t0, t1] (an empty range when there are more copies than
-// tiles).
-__device__ __forceinline__ void split_share(int& t0, int& t1, int sg, int n) {
-  if (n <= 1) return;
-  const int len = t1 - t0 + 1, per = (len + n - 1) / n;
-  t0 += sg * per;
-  t1 = min(t1, t0 + per - 1);
+// tiles (of T rows) that rows [lo, hi] touch, and narrows [lo, hi] to the
+// rows of its share (lo > hi: no tile, when there are more copies than
+// tiles or the range is empty).
+__device__ __forceinline__ void split_rows(long long& lo, long long& hi, int T, int sg, int n) {
+  if (n <= 1 || lo > hi) return;
+  const long long t0 = lo / T, t1 = hi / T, per = (t1 - t0 + n) / n;
+  const long long s0 = t0 + sg * per, s1 = min(t1, s0 + per - 1);
+  if (s0 > s1) {
+    hi = lo - 1;
+    return;
+  }
+  lo = max(lo, s0 * T);
+  hi = min(hi, s1 * T + T - 1);
 }
 
 // Unscaled fp32 dK and dV sums of this lane's key (partial-sum row prow of
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a, long long 
 // operands of dK^T += Q^T dS and dV^T += dO^T P), with LSE and Delta.
 // With FEAT the logits carry the bias / ALiBi terms and dropout multiplies
 // P (in dV) and dP (in dS) by keep / (1 - p).
-template <typename M, int D, int NW, int BMQ, bool FEAT = false>
+template <typename M, int D, int NW, int BMQ, bool FEAT = false, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   using T = typename M::elem;
   constexpr int NT = NW * 64, BNK = NW * 32, KPL = M::KPL;
@@ -162,7 +168,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nbh = P.B * P.H;
-  const int nkb = (int)(gridDim.x / ((unsigned)nbh * a.split_kv));
+  const int nsplit = SPLIT ? a.split_kv : 1;
+  const int nkb = (int)(gridDim.x / ((unsigned)nbh * nsplit));
   const int sg = (int)(blockIdx.x / (unsigned)(nkb * nbh));  // split copy (0 without split)
   const GridPos gp = grid_pos((int)(blockIdx.x % (unsigned)(nkb * nbh)), nkb * nbh, nkb, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
@@ -186,15 +193,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
 
   // Queries that can see the block's keys.
   const int jlast = min(j0 + BNK, sk) - 1;
-  const long long ilo = max(0LL, (long long)j0 - w.hi);
-  const long long ihi = min((long long)sq - 1, (long long)jlast - w.lo);
-  int t0 = 0, t1 = -1;
-  if (w.lo <= w.hi && ilo <= ihi) {
-    t0 = (int)(ilo / BMQ);
-    t1 = (int)(ihi / BMQ);
-    split_share(t0, t1, sg, a.split_kv);
-  }
-  const bool block_empty = t0 > t1;
+  long long ilo = max(0LL, (long long)j0 - w.hi);
+  long long ihi = min((long long)sq - 1, (long long)jlast - w.lo);
+  if constexpr (SPLIT) split_rows(ilo, ihi, BMQ, sg, nsplit);
+  const bool block_empty = w.lo > w.hi || ilo > ihi;
 
   const int jw0 = j0 + 32 * wave;
   const bool wave_live = jw0 < sk;
@@ -221,6 +223,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
 
   if (!block_empty) {
+    const int t0 = (int)(ilo / BMQ), t1 = (int)(ihi / BMQ);
     TileStage<T, BMQ, D, NT> qs, dos;
     float st_l = INFINITY, st_d = 0.f;  // this thread's LSE/Delta entry (tid < BMQ)
     auto load_tile = [&](int i0) {
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  if (wave_live && kj < sk && a.part) {
+  if (SPLIT && wave_live && kj < sk) {
     store_partial_kv<D>(a.part, a.rows_k, a.split_kv, P.H, sg, h, part_row(P.ks.mode, P.Sk, b, k0, kj), dk, dv, g);
   } else if (wave_live && kj < sk) {
     T* dkrow = dkp + (long long)kj * a.dk.ss;
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
 // With FEAT the logits carry the bias / ALiBi terms, dropout multiplies dP
 // by keep / (1 - p), and with a dbias output every key tile is visited and
 // dS is stored (zeros where masked).
-template <typename M, int D, int NW, int BN, bool FEAT = false>
+template <typename M, int D, int NW, int BN, bool FEAT = false, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   using T = typename M::elem;
   constexpr int NT = NW * 64, BM = NW * 32, KPL = M::KPL;
@@ -354,7 +357,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nbh = P.B * P.H;
-  const int nq = (int)(gridDim.x / ((unsigned)nbh * a.split_q));
+  const int nsplit = SPLIT ? a.split_q : 1;
+  const int nq = (int)(gridDim.x / ((unsigned)nbh * nsplit));
   const int sg = (int)(blockIdx.x / (unsigned)(nq * nbh));  // split copy (0 without split)
   const GridPos gp = grid_pos((int)(blockIdx.x % (unsigned)(nq * nbh)), nq * nbh, nq, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
@@ -385,13 +389,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     jhi = (long long)sk - 1;
     block_empty = sk == 0;
   }
-  int t0 = 0, t1 = -1;
-  if (!block_empty) {
-    t0 = (int)(jlo / BN);
-    t1 = (int)(jhi / BN);
-    split_share(t0, t1, sg, a.split_q);
+  if constexpr (SPLIT) {
+    split_rows(jlo, jhi, BN, sg, nsplit);
+    block_empty = block_empty || jlo > jhi;
   }
-  block_empty = t0 > t1;
 
   const int iw0 = i0 + 32 * wave;
   const bool wave_live = iw0 < sq;
@@ -416,6 +417,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   for (int dt = 0; dt < DVT; ++dt) dq[dt] = zero16();
 
   if (!block_empty) {
+    const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
     TileStage<T, BN, D, NT> ks, vs;
     auto load_tile = [&](int j0) {
       ks.load(kp + (long long)j0 * a.k.ss, a.k.ss, sk - j0, tid);
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  if (row_ok && a.part) {
+  if (SPLIT && row_ok) {
     store_partial_q<D>(a.part + 2LL * a.split_kv * P.H * a.rows_k * D, a.rows_q, P.H, sg, h,
                        part_row(P.qs.mode, P.Sq, b, q0, qi), dq, g);
   } else if (row_ok) {
@@ -660,7 +662,7 @@ struct Dkdv16Feat {
   }
 };
 
-template <typename M, int D, int NW, int BMQ, int WPE, bool FEAT = false>
+template <typename M, int D, int NW, int BMQ, int WPE, bool FEAT = false, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dkdv16_kernel(BwdArgs a) {
   using F = Dkdv16<M, D, BMQ>;
   using T = typename M::elem;
@@ -680,7 +682,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nbh = P.B * P.H;
-  const int nkb = (int)(gridDim.x / ((unsigned)nbh * a.split_kv));
+  const int nsplit = SPLIT ? a.split_kv : 1;
+  const int nkb = (int)(gridDim.x / ((unsigned)nbh * nsplit));
   const int sg = (int)(blockIdx.x / (unsigned)(nkb * nbh));  // split copy (0 without split)
   const GridPos gp = grid_pos((int)(blockIdx.x % (unsigned)(nkb * nbh)), nkb * nbh, nkb, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
@@ -704,15 +707,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 
   // Queries that can see the block's keys, and the tiles of this wave's keys.
   const int jlast = min(j0 + BNK, sk) - 1;
-  const long long ilo = max(0LL, (long long)j0 - w.hi);
-  const long long ihi = min((long long)sq - 1, (long long)jlast - w.lo);
-  int t0 = 0, t1 = -1;
-  if (w.lo <= w.hi && ilo <= ihi) {
-    t0 = (int)(ilo / BMQ);
-    t1 = (int)(ihi / BMQ);
-    split_share(t0, t1, sg, a.split_kv);
-  }
-  const bool block_empty = t0 > t1;
+  long long ilo = max(0LL, (long long)j0 - w.hi);
+  long long ihi = min((long long)sq - 1, (long long)jlast - w.lo);
+  if constexpr (SPLIT) split_rows(ilo, ihi, BMQ, sg, nsplit);
+  const bool block_empty = w.lo > w.hi || ilo > ihi;
 
   const int jw0 = j0 + 32 * wave;
   const bool wave_live = jw0 < sk;
@@ -753,6 +751,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       zero_unused_slots<T, D, BMQ, NT>(qs[u], tid);
       zero_unused_slots<T, D, BMQ, NT>(ds_[u], tid);
     }
+    const int t0 = (int)(ilo / BMQ), t1 = (int)(ihi / BMQ);
     // One tile's loads, all direct to LDS: its Q and dO rows and, per wave,
     // RW rows of LSE log2(e) and Delta (rows past the sequence repeat its
     // last row and are masked).
@@ -794,7 +793,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     }
   }
 
-  if (wave_live && kj < sk && a.part) {
+  if (SPLIT && wave_live && kj < sk) {
     store_partial_kv<D>(a.part, a.rows_k, a.split_kv, P.H, sg, h, part_row(P.ks.mode, P.Sk, b, k0, kj), dk, dv, g);
   } else if (wave_live && kj < sk) {
     T* dkrow = dkp + (long long)kj * a.dk.ss;
@@ -1412,7 +1411,7 @@ struct Dq16Feat {
 // grid), K and V tiles of stage s in the first two namespace-scope LDS
 // stages ([K | V] each).  With FEAT and a dbias output, every key tile of
 // the sequence is visited (tiles the window leaves empty write their zeros).
-template <typename M, int D, int NW, int BN, bool FEAT = false>
+template <typename M, int D, int NW, int BN, bool FEAT = false, bool SPLIT = false>
 __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   using F = Dq16<M, D, BN>;
   using T = typename M::elem;
@@ -1428,7 +1427,8 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nbh = P.B * P.H;
-  const int nq = nblk / (nbh * a.split_q);
+  const int nsplit = SPLIT ? a.split_q : 1;
+  const int nq = nblk / (nbh * nsplit);
   const int sg = hw / (nq * nbh);  // split copy (0 without split)
   const GridPos gp = grid_pos(hw % (nq * nbh), nq * nbh, nq, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
@@ -1459,13 +1459,10 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
     jhi = (long long)sk - 1;
     block_empty = sk == 0;
   }
-  int t0 = 0, t1 = -1;
-  if (!block_empty) {
-    t0 = (int)(jlo / BN);
-    t1 = (int)(jhi / BN);
-    split_share(t0, t1, sg, a.split_q);
+  if constexpr (SPLIT) {
+    split_rows(jlo, jhi, BN, sg, nsplit);
+    block_empty = block_empty || jlo > jhi;
   }
-  block_empty = t0 > t1;
 
   const int iw0 = i0 + 32 * wave;
   const bool wave_live = iw0 < sq;
@@ -1507,6 +1504,7 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
     zero_unused_slots<T, D, BN, NT>(k_s1, tid);
     zero_unused_slots<T, D, BN, NT>(v_s0, tid);
     zero_unused_slots<T, D, BN, NT>(v_s1, tid);
+    const int t0 = (int)(jlo / BN), t1 = (int)(jhi / BN);
     auto dma = [&](T* kb, T* vb, int t) __attribute__((always_inline)) {
       kd.issue(kb, kp + (long long)t * BN * a.k.ss, a.k.ss, sk - t * BN, wave, lane);
       vd.issue(vb, vp + (long long)t * BN * a.v.ss, a.v.ss, sk - t * BN, wave, lane);
@@ -1535,7 +1533,7 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
     }
   }
 
-  if (row_ok && a.part) {
+  if (SPLIT && row_ok) {
     store_partial_q<D>(a.part + 2LL * a.split_kv * P.H * a.rows_k * D, a.rows_q, P.H, sg, h,
                        part_row(P.qs.mode, P.Sq, b, q0, qi), dq, g);
   } else if (row_ok) {
@@ -1553,9 +1551,9 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   }
 }
 
-template <typename M, int D, int NW, int BN, int WPE, bool FEAT = false>
+template <typename M, int D, int NW, int BN, int WPE, bool FEAT = false, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dq16_kernel(BwdArgs) {
-  dq16_body<M, D, NW, BN, FEAT>(blockIdx.x, gridDim.x);
+  dq16_body<M, D, NW, BN, FEAT, SPLIT>(blockIdx.x, gridDim.x);
 }
 
 // ------------------------------------------ 16-bit dK/dV + dQ in one grid
@@ -1678,10 +1676,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
       if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
       if (nblk > 0) {
         if constexpr (S::k16)
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV>),
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV, false, true>),
                    "attn_bwd_dkdv16_kernel", (unsigned)nblk, (unsigned)(NW_KV * 64), a);
         else
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ>), "attn_bwd_dkdv_kernel",
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ, false, true>), "attn_bwd_dkdv_kernel",
                    (unsigned)nblk, (unsigned)(NW_KV * 64), a);
         if (err != hipSuccess) return err;
       }
@@ -1691,10 +1689,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
       if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
       if (nblk > 0) {
         if constexpr (S::k16)
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, S::WPE_Q>),
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, S::WPE_Q, false, true>),
                    "attn_bwd_dq16_kernel", (unsigned)nblk, (unsigned)(NW_Q * 64), a);
         else
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN>), "attn_bwd_dq_kernel",
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN, false, true>), "attn_bwd_dq_kernel",
                    (unsigned)nblk, (unsigned)(NW_Q * 64), a);
         if (err != hipSuccess) return err;
       }
