@@ -197,6 +197,28 @@ def copy_probe(mib: int, steps: int) -> None:
                       "gb_s_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
+def mfma_probe(n: int, steps: int) -> None:
+    """A plain bf16 GEMM (torch.matmul, n x n x n), `steps` times: a matrix-
+    core-bound library kernel whose FLOP rate is known from its time, the
+    reference against which an MFMA-busy counter's reading is scaled."""
+    import torch
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        c = torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"mfma_probe_n": n, "launches": steps + 1, "ms": round(ms, 4), "tflops": round(tf, 1),
+                      "frac_of_bf16_peak": round(tf / PEAK_MFMA_16, 4)}), flush=True)
+
+
 class Run:
     """One workload on the GPU: inputs in HBM, the params of each call, the
     library's launch plan, and timed steps."""
@@ -301,6 +323,9 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the attention step, run a plain device-to-device copy of MIB "
                          "MiB (the calibration kernel for HBM byte counters) and exit")
+    ap.add_argument("--mfma-probe", type=int, default=0, metavar="N",
+                    help="instead of the attention step, run an N x N x N bf16 GEMM (the reference for "
+                         "MFMA-busy counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -317,6 +342,9 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe(args.copy_probe, args.steps)
+        return
+    if args.mfma_probe:
+        mfma_probe(args.mfma_probe, args.steps)
         return
     names = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
     wl_all = wls.workloads()
