@@ -314,19 +314,27 @@ hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
  * is repeated so that copy g of n walks the g-th of n contiguous shares of
  * the tiles it would visit (query tiles for dK/dV, key tiles for dQ), about
  * 256 workgroups in all (at most 8 copies, one per tile, fp32 partial sums
- * of at most 8 MiB); the copies store fp32 partial sums in the workspace,
- * and a last kernel adds them in copy order, scales, rounds, and writes the
- * rows past each length.  The sums then group the tiles differently from
- * the unsplit path (results differ in rounding only, and stay run-to-run
- * identical). */
+ * of at most 8 MiB); the copies store fp32 partial sums in the workspace
+ * and count themselves in on an arrival counter per block there, and the
+ * last copy of a block to arrive adds the block's partials in copy order,
+ * scales, rounds and writes them (so the result does not depend on which
+ * copy is last), and resets the counter.  No workgroup waits for another.
+ * The dK/dV and dQ copies run as one grid where both kinds fit one
+ * workgroup's LDS (fp16 / bf16 up to head_dim 128, fp32 up to 64).  The sums
+ * then group the tiles differently from the unsplit path (results differ in
+ * rounding only, and stay run-to-run identical).  attn_bwd_preprocess
+ * zeroes the counters, so the step calls below need it first, as they do
+ * anyway for Delta; repeated dK/dV or dQ calls on one workspace are fine.
+ * Split calls that overlap on one workspace race, as any calls that share a
+ * workspace do. */
 hipError_t attn_bwd(const attn_bwd_params *p, hipStream_t stream);
 
 /* The three steps of attn_bwd as separate calls, for callers that schedule
  * or time them one by one.  Same parameters, validation and errors as
  * attn_bwd; each enqueues one kernel on `stream`, and attn_bwd_dkdv /
  * attn_bwd_dq also the row-zeroing kernel of their outputs when seqused
- * arrays are given (in split mode: their split grid and the reduction of
- * their outputs).  They must run in this order on one stream (or be
+ * arrays are given (in split mode: their split grid, whose last copies
+ * write the outputs).  They must run in this order on one stream (or be
  * ordered by events): attn_bwd_dkdv and attn_bwd_dq read the Delta and LSE
  * log2(e) that attn_bwd_preprocess leaves in the workspace, which must not
  * be touched in between.
@@ -355,7 +363,9 @@ hipError_t attn_bwd_dkdv_dq(const attn_bwd_params *p, hipStream_t stream);
  * then, in split mode, the fp32 partial sums (head_dim floats per copy, head
  * and row: dK and dV per key-side copy, dQ per query-side copy; rows are the
  * stacked tensor's rows, or batch * seqlen for a padded side), rounded up to
- * 256 bytes; 0 when the problem is malformed.  A repacked call (see above)
+ * 256 bytes, and a 4-byte arrival counter per dK/dV and per dQ workgroup of
+ * the unsplit grids (B H ceil(seqlen_k / 128) + B H ceil(seqlen_q / 128)),
+ * rounded up to 256 bytes; 0 when the problem is malformed.  A repacked call (see above)
  * needs, before those (sized for head dim Dp), padded copies of q, k, v, o,
  * dout, dq, dk and dv, each rounded up to 256 bytes.  Repacked, the three
  * step calls share the copies through the workspace: attn_bwd_preprocess
@@ -415,8 +425,9 @@ hipError_t attn_bwd_plan(const attn_bwd_params *p, uint32_t steps, hipStream_t s
  *    query row) pairs, return hipErrorOutOfMemory before enqueuing anything.
  *  - Every call on one device shares that device's array: calls that may
  *    overlap in time on one device (different streams, or other threads)
- *    race and must be ordered by the caller.  Nothing in it needs clearing:
- *    each call writes the part it reads before reading it.
+ *    race and must be ordered by the caller.  Nothing in it needs clearing
+ *    by the caller: each call writes the part it reads before reading it
+ *    (its preprocess kernel zeroes the split mode's arrival counters).
  *  - The array's device address is looked up on the first call on each
  *    device; that call must not be made under stream capture. */
 #define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)

@@ -282,14 +282,18 @@ uint64_t delta_bytes(const attn_fwd_params* p) { return 2 * stat_section_bytes(p
 // Split mode of the backward (the launch rules in attn_bwd.hip): taken for
 // calls without optional features whose dK/dV or dQ grid (128 keys or
 // queries per workgroup) has fewer than 64 workgroups, i.e. would leave at
-// least three quarters of a 256-CU GPU idle.  Each grid is repeated to reach
+// least three quarters of a 256-CU GPU idle (at fp16 / bf16 head dims 96
+// and 128, only up to 16 dK/dV workgroups).  Each grid is repeated to reach
 // about 256 workgroups, at most 8 times and at most once per tile of the
 // axis it splits; the fp32 partial sums are capped at 8 MiB (fewer copies,
-// or no split, beyond that).  Depends on the call only, so the workspace
-// size and the launch agree.
+// or no split, beyond that).  After the partials come the arrival counters,
+// one 4-byte word per dK/dV and per dQ block.  Depends on the call only, so
+// the workspace size and the launch agree.
 struct Split {
   int gkv = 1, gq = 1;
   int64_t rows_q = 0, rows_k = 0;
+  int64_t nkv = 0, nq = 0;  // blocks of 128 rows: counters
+  uint64_t part_bytes = 0;
   uint64_t bytes = 0;  // 0: no split
 };
 
@@ -301,6 +305,10 @@ Split split_of(const attn_bwd_params* p) {
   const int64_t B = f->batch, H = f->heads, D = f->head_dim, Sq = f->seqlen_q, Sk = f->seqlen_k;
   const int64_t nkv = B * H * ((Sk + 127) / 128), nq = B * H * ((Sq + 127) / 128);
   if (nkv == 0 || nq == 0 || (nkv >= 64 && nq >= 64)) return sp;
+  // fp16 / bf16 at head dims 96 and 128: the unsplit dK/dV runs producer /
+  // consumer workgroups, which the split copies cannot use; past 16 dK/dV
+  // blocks the unsplit path is as fast or faster.
+  if (f->dtype != ATTN_FP32 && (D == 96 || D == 128) && nkv > 16) return sp;
   const int64_t tile = f->dtype == ATTN_FP32 ? 32 : 64;  // query tile of dK/dV, key tile of dQ
   auto groups = [](int64_t nblk, int64_t ntiles) {
     return (int)std::max<int64_t>(1, std::min<int64_t>({(256 + nblk - 1) / nblk, 8, ntiles}));
@@ -313,7 +321,10 @@ Split split_of(const attn_bwd_params* p) {
   constexpr uint64_t kCap = 8u << 20;
   while (bytes() > kCap && (sp.gkv > 1 || sp.gq > 1)) (sp.gkv >= sp.gq ? sp.gkv : sp.gq) -= 1;
   if (bytes() > kCap || (sp.gkv == 1 && sp.gq == 1)) return Split{};
-  sp.bytes = (bytes() + 255) / 256 * 256;
+  sp.nkv = nkv;
+  sp.nq = nq;
+  sp.part_bytes = (bytes() + 255) / 256 * 256;
+  sp.bytes = sp.part_bytes + ((uint64_t)(4 * (nkv + nq)) + 255) / 256 * 256;
   return sp;
 }
 
@@ -603,6 +614,9 @@ sdpa::BwdArgs bwd_args(const attn_bwd_params* p, void* ws) {
     a.rows_k = sp.rows_k;
     a.split_kv = sp.gkv;
     a.split_q = sp.gq;
+    a.cnt_kv = reinterpret_cast<unsigned*>(reinterpret_cast<uintptr_t>(a.part) + (uintptr_t)sp.part_bytes);
+    a.cnt_q = a.cnt_kv + sp.nkv;
+    a.ncnt = sp.nkv + sp.nq;
   }
   return a;
 }

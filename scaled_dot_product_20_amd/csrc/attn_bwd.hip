@@ -87,6 +87,100 @@ __device__ __forceinline__ void store_partial_q(float* part_q, long long rows_q,
     }
 }
 
+// Arrival of a split copy at its block: after a barrier (the workgroup's
+// partial stores happen before it), lane 0 counts the workgroup in with one
+// release / acquire add, so the fence work is paid once per workgroup, not
+// per wave; the workgroup that brings the count to n resets the counter
+// (for the next call on the workspace), acquires the other copies' stores
+// and returns true: it sums the partials.  No workgroup waits for another,
+// so the grid drains in any schedule.
+__device__ __forceinline__ bool last_arrival(unsigned* cnt, int n) {
+  __shared__ int s_last;
+  __syncthreads();  // the workgroup's partial stores happen before lane 0's release
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev + 1u == (unsigned)n;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = s_last != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+// The last copy's epilogue for one block: rows [lo, hi) of sequence b, head
+// h (partial row part_row(mode, S, b, r0, i)) get the sum of their G partial
+// rows in copy order (so the result does not depend on which copy is last),
+// times sc, rounded into o0; with KV the second section (dV, one section of
+// G H rows further on) goes unscaled into o1.  One workgroup reads all of
+// it, so each thread keeps the loads of two float4 columns of every copy in
+// flight at once.
+template <typename T, int D, int NT, bool KV, int G>
+__device__ __forceinline__ void sum_partials_g(const float* part, long long rows, int H, int h, int mode, int S,
+                                               int b, long long r0, int lo, int hi, T* o0, long long ss0, T* o1,
+                                               long long ss1, float sc, int tid) {
+  constexpr int V4 = D / 4, U = 2;
+  static_assert(D % 4 == 0, "row shape");
+  const long long gstride = (long long)H * rows * D;
+  const float* p1 = part + G * gstride;
+  const int total = (hi - lo) * V4;
+  for (int x0 = tid; x0 < total; x0 += U * NT) {
+    float4 u[U][G], v[U][KV ? G : 1];
+    long long off[U];
+#pragma unroll
+    for (int e = 0; e < U; ++e) {
+      const int x = min(x0 + e * NT, total - 1);
+      const int i = lo + x / V4, d = 4 * (x % V4);
+      off[e] = ((long long)h * rows + part_row(mode, S, b, r0, i)) * D + d;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        u[e][g] = *reinterpret_cast<const float4*>(part + g * gstride + off[e]);
+        if constexpr (KV) v[e][g] = *reinterpret_cast<const float4*>(p1 + g * gstride + off[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < U; ++e) {
+      const int x = x0 + e * NT;
+      if (x >= total) break;
+      const int i = lo + x / V4, d = 4 * (x % V4);
+      float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        s0.x += u[e][g].x; s0.y += u[e][g].y; s0.z += u[e][g].z; s0.w += u[e][g].w;
+        if constexpr (KV) {
+          s1.x += v[e][g].x; s1.y += v[e][g].y; s1.z += v[e][g].z; s1.w += v[e][g].w;
+        }
+      }
+      store4b<T>(o0 + (long long)i * ss0 + d, s0.x * sc, s0.y * sc, s0.z * sc, s0.w * sc);
+      if constexpr (KV) store4b<T>(o1 + (long long)i * ss1 + d, s1.x, s1.y, s1.z, s1.w);
+    }
+  }
+}
+
+// The same for n copies (2 <= n <= 8, the split rule's range).
+template <typename T, int D, int NT, bool KV>
+__device__ __forceinline__ void sum_partials(const float* part, long long rows, int H, int n, int h, int mode, int S,
+                                             int b, long long r0, int lo, int hi, T* o0, long long ss0, T* o1,
+                                             long long ss1, float sc, int tid) {
+#define SDPA_SUM_CASE(G)                                                                                        \
+  case G:                                                                                                       \
+    sum_partials_g<T, D, NT, KV, G>(part, rows, H, h, mode, S, b, r0, lo, hi, o0, ss0, o1, ss1, sc, tid);       \
+    break;
+  switch (n) {
+    SDPA_SUM_CASE(1)
+    SDPA_SUM_CASE(2)
+    SDPA_SUM_CASE(3)
+    SDPA_SUM_CASE(4)
+    SDPA_SUM_CASE(5)
+    SDPA_SUM_CASE(6)
+    SDPA_SUM_CASE(7)
+    SDPA_SUM_CASE(8)
+    default: break;
+  }
+#undef SDPA_SUM_CASE
+}
+
 template <typename T>
 __device__ __forceinline__ float dot_chunk(uint4 x, uint4 y) {
   if constexpr (sizeof(T) == 4) {
@@ -113,6 +207,8 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a, long long 
   constexpr int CE = 16 / (int)sizeof(T), CH = D / CE;
   constexpr int G = CH <= 8 ? 8 : (CH <= 16 ? 16 : 32);
   const ProblemArgs& P = a.p;
+  for (long long x = (long long)blockIdx.x * 256 + threadIdx.x; x < a.ncnt; x += (long long)gridDim.x * 256)
+    a.cnt_kv[x] = 0u;
   const long long row = (long long)blockIdx.x * (256 / G) + threadIdx.x / G;
   const int c = threadIdx.x % G;
   if (row >= nrows) return;  // whole groups leave together
@@ -151,8 +247,8 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a, long long 
 // operands of dK^T += Q^T dS and dV^T += dO^T P), with LSE and Delta.
 // With FEAT the logits carry the bias / ALiBi terms and dropout multiplies
 // P (in dV) and dP (in dS) by keep / (1 - p).
-template <typename M, int D, int NW, int BMQ, bool FEAT = false, bool SPLIT = false>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
+template <typename M, int D, int NW, int BMQ, bool FEAT, bool SPLIT>
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a, unsigned hw, unsigned nblk) {
   using T = typename M::elem;
   constexpr int NT = NW * 64, BNK = NW * 32, KPL = M::KPL;
   constexpr int DVT = (D + 31) / 32, DPAD = DVT * 32;
@@ -169,9 +265,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nbh = P.B * P.H;
   const int nsplit = SPLIT ? a.split_kv : 1;
-  const int nkb = (int)(gridDim.x / ((unsigned)nbh * nsplit));
-  const int sg = (int)(blockIdx.x / (unsigned)(nkb * nbh));  // split copy (0 without split)
-  const GridPos gp = grid_pos((int)(blockIdx.x % (unsigned)(nkb * nbh)), nkb * nbh, nkb, nbh, P.ragged);
+  const int nkb = (int)(nblk / ((unsigned)nbh * nsplit));
+  const int sg = (int)(hw / (unsigned)(nkb * nbh));  // split copy (0 without split)
+  const GridPos gp = grid_pos((int)(hw % (unsigned)(nkb * nbh)), nkb * nbh, nkb, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int kb = gp.i;
 
@@ -312,8 +408,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  if (SPLIT && wave_live && kj < sk) {
-    store_partial_kv<D>(a.part, a.rows_k, a.split_kv, P.H, sg, h, part_row(P.ks.mode, P.Sk, b, k0, kj), dk, dv, g);
+  if constexpr (SPLIT) {
+    if (wave_live && kj < sk)
+      store_partial_kv<D>(a.part, a.rows_k, a.split_kv, P.H, sg, h, part_row(P.ks.mode, P.Sk, b, k0, kj), dk, dv, g);
+    if (a.cnt_kv != nullptr && last_arrival(a.cnt_kv + (long long)bh * nkb + kb, nsplit))
+      sum_partials<T, D, NT, true>(a.part, a.rows_k, P.H, nsplit, h, P.ks.mode, P.Sk, b, k0, j0, jlast + 1, dkp,
+                                   a.dk.ss, dvp, a.dv.ss, P.scale, tid);
   } else if (wave_live && kj < sk) {
     T* dkrow = dkp + (long long)kj * a.dk.ss;
     T* dvrow = dvp + (long long)kj * a.dv.ss;
@@ -333,6 +433,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+template <typename M, int D, int NW, int BMQ, bool FEAT = false, bool SPLIT = false>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
+  dkdv_body<M, D, NW, BMQ, FEAT, SPLIT>(a, blockIdx.x, gridDim.x);
+}
+
 // ------------------------------------------------------------ dQ
 
 // One workgroup = 32*NW queries, each wave 32 queries with its Q and dO rows,
@@ -341,8 +446,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
 // With FEAT the logits carry the bias / ALiBi terms, dropout multiplies dP
 // by keep / (1 - p), and with a dbias output every key tile is visited and
 // dS is stored (zeros where masked).
-template <typename M, int D, int NW, int BN, bool FEAT = false, bool SPLIT = false>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
+template <typename M, int D, int NW, int BN, bool FEAT, bool SPLIT>
+__device__ __forceinline__ void dq_body(const BwdArgs& a, unsigned hw, unsigned nblk) {
   using T = typename M::elem;
   constexpr int NT = NW * 64, BM = NW * 32, KPL = M::KPL;
   constexpr int DVT = (D + 31) / 32, DPAD = DVT * 32;
@@ -358,9 +463,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nbh = P.B * P.H;
   const int nsplit = SPLIT ? a.split_q : 1;
-  const int nq = (int)(gridDim.x / ((unsigned)nbh * nsplit));
-  const int sg = (int)(blockIdx.x / (unsigned)(nq * nbh));  // split copy (0 without split)
-  const GridPos gp = grid_pos((int)(blockIdx.x % (unsigned)(nq * nbh)), nq * nbh, nq, nbh, P.ragged);
+  const int nq = (int)(nblk / ((unsigned)nbh * nsplit));
+  const int sg = (int)(hw / (unsigned)(nq * nbh));  // split copy (0 without split)
+  const GridPos gp = grid_pos((int)(hw % (unsigned)(nq * nbh)), nq * nbh, nq, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int qb = nq - 1 - gp.i;
 
@@ -506,9 +611,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  if (SPLIT && row_ok) {
-    store_partial_q<D>(a.part + 2LL * a.split_kv * P.H * a.rows_k * D, a.rows_q, P.H, sg, h,
-                       part_row(P.qs.mode, P.Sq, b, q0, qi), dq, g);
+  if constexpr (SPLIT) {
+    float* const part_q = a.part + 2LL * a.split_kv * P.H * a.rows_k * D;
+    if (row_ok) store_partial_q<D>(part_q, a.rows_q, P.H, sg, h, part_row(P.qs.mode, P.Sq, b, q0, qi), dq, g);
+    if (a.cnt_q != nullptr && last_arrival(a.cnt_q + (long long)bh * nq + qb, nsplit))
+      sum_partials<T, D, NT, false>(part_q, a.rows_q, P.H, nsplit, h, P.qs.mode, P.Sq, b, q0, i0, ilast + 1, dqp,
+                                    a.dq.ss, nullptr, 0, P.scale, tid);
   } else if (row_ok) {
     T* dqrow = dqp + (long long)qi * a.dq.ss;
     const float sc = P.scale;
@@ -523,6 +631,26 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
       }
   }
 }
+
+template <typename M, int D, int NW, int BN, bool FEAT = false, bool SPLIT = false>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
+  dq_body<M, D, NW, BN, FEAT, SPLIT>(a, blockIdx.x, gridDim.x);
+}
+
+// LDS of the 16-bit backward kernels that run 8-wave workgroups, and of the
+// split grid: three stages of [Q | dO | LSE log2 e | Delta] (dK/dV) or
+// [K | V] (dQ) and three fp16 P buffers.  They are named at namespace scope so that the kernel
+// bodies refer to these objects directly: the compiler then knows every
+// access is to LDS, and which stage array a direct load fills.  Sized for
+// 64-row tiles of up to 128 columns of 16-bit elements.
+constexpr int kBwdStageBytes = 2 * 64 * 128 * 2 + 4 * 64 * 4;
+constexpr int kBwdXBytes = 4 * 2 * 2 * 64 * 16;
+__shared__ __attribute__((aligned(1024))) char g_bwd_st0[kBwdStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_bwd_st1[kBwdStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_bwd_st2[kBwdStageBytes];
+__shared__ __attribute__((aligned(16))) char g_bwd_x0[kBwdXBytes];
+__shared__ __attribute__((aligned(16))) char g_bwd_x1[kBwdXBytes];
+__shared__ __attribute__((aligned(16))) char g_bwd_x2[kBwdXBytes];
 
 // ------------------------------------------------- 16-bit dK / dV kernel
 //
@@ -662,30 +790,63 @@ struct Dkdv16Feat {
   }
 };
 
-template <typename M, int D, int NW, int BMQ, int WPE, bool FEAT = false, bool SPLIT = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dkdv16_kernel(BwdArgs a) {
+// LDS of the 16-bit dK/dV workgroup: per stage its Q and dO tiles and the
+// LSE log2(e) and Delta of its query rows.  Own arrays, one per stage and
+// operand, so that the compiler can tell the tiles being read from those
+// being filled by direct loads and does not wait for those loads before
+// every read; with EXT the two namespace-scope stages, one array per stage
+// (the split grid, whose dQ workgroups use the same two).
+template <typename T, int TILE, int BMQ, bool EXT>
+struct Dkdv16Lds {
+  T* q[2];
+  T* d[2];
+  float* l[2];
+  float* e[2];
+  __device__ __forceinline__ Dkdv16Lds() {
+    if constexpr (EXT) {
+      static_assert(2 * TILE * (int)sizeof(T) + 2 * BMQ * 4 <= kBwdStageBytes, "tiles fit a stage");
+      char* const st[2] = {g_bwd_st0, g_bwd_st1};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        q[u] = reinterpret_cast<T*>(st[u]);
+        d[u] = q[u] + TILE;
+        l[u] = reinterpret_cast<float*>(d[u] + TILE);
+        e[u] = l[u] + BMQ;
+      }
+    } else {
+      __shared__ __attribute__((aligned(1024))) T q_s0[TILE], q_s1[TILE];
+      __shared__ __attribute__((aligned(1024))) T d_s0[TILE], d_s1[TILE];
+      __shared__ __attribute__((aligned(16))) float l_s0[BMQ], l_s1[BMQ], e_s0[BMQ], e_s1[BMQ];
+      q[0] = q_s0;
+      q[1] = q_s1;
+      d[0] = d_s0;
+      d[1] = d_s1;
+      l[0] = l_s0;
+      l[1] = l_s1;
+      e[0] = e_s0;
+      e[1] = e_s1;
+    }
+  }
+};
+
+template <typename M, int D, int NW, int BMQ, bool FEAT, bool SPLIT, bool EXT = false>
+__device__ __forceinline__ void dkdv16_body(const BwdArgs& a, unsigned hw, unsigned nblk) {
   using F = Dkdv16<M, D, BMQ>;
   using T = typename M::elem;
   using DL = DmaLane<T, D, BMQ, NW>;
   constexpr int NT = NW * 64, BNK = NW * 32, DVT = F::DVT;
   constexpr int RW = BMQ / NW;  // LSE / Delta rows each wave copies per tile
   static_assert(BMQ % NW == 0 && RW <= 64, "stats rows");
-  // One LDS array per stage and operand, so that the compiler can tell the
-  // tiles being read from those being filled by direct loads and does not
-  // wait for those loads before every read.
-  __shared__ __attribute__((aligned(1024))) T q_s0[F::TILE], q_s1[F::TILE];
-  __shared__ __attribute__((aligned(1024))) T d_s0[F::TILE], d_s1[F::TILE];
-  // LSE log2(e) and Delta of each stage's query rows.
-  __shared__ __attribute__((aligned(16))) float l_s0[BMQ], l_s1[BMQ], e_s0[BMQ], e_s1[BMQ];
+  const Dkdv16Lds<T, F::TILE, BMQ, EXT> lds;
 
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int nbh = P.B * P.H;
   const int nsplit = SPLIT ? a.split_kv : 1;
-  const int nkb = (int)(gridDim.x / ((unsigned)nbh * nsplit));
-  const int sg = (int)(blockIdx.x / (unsigned)(nkb * nbh));  // split copy (0 without split)
-  const GridPos gp = grid_pos((int)(blockIdx.x % (unsigned)(nkb * nbh)), nkb * nbh, nkb, nbh, P.ragged);
+  const int nkb = (int)(nblk / ((unsigned)nbh * nsplit));
+  const int sg = (int)(hw / (unsigned)(nkb * nbh));  // split copy (0 without split)
+  const GridPos gp = grid_pos((int)(hw % (unsigned)(nkb * nbh)), nkb * nbh, nkb, nbh, P.ragged);
   const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
   const int kb = gp.i;
 
@@ -744,8 +905,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     DL qd, dd;
     qd.init(a.q.ss, wave, lane);
     dd.init(a.dout.ss, wave, lane);
-    T* const qs[2] = {q_s0, q_s1};
-    T* const ds_[2] = {d_s0, d_s1};
+    T* const qs[2] = {lds.q[0], lds.q[1]};
+    T* const ds_[2] = {lds.d[0], lds.d[1]};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       zero_unused_slots<T, D, BMQ, NT>(qs[u], tid);
@@ -755,8 +916,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     // One tile's loads, all direct to LDS: its Q and dO rows and, per wave,
     // RW rows of LSE log2(e) and Delta (rows past the sequence repeat its
     // last row and are masked).
-    float* const ls[2] = {l_s0, l_s1};
-    float* const es[2] = {e_s0, e_s1};
+    float* const ls[2] = {lds.l[0], lds.l[1]};
+    float* const es[2] = {lds.e[0], lds.e[1]};
     auto issue = [&](int stage, int t) {
       const int i0 = t * BMQ;
       qd.issue(qs[stage], qp + (long long)i0 * a.q.ss, a.q.ss, sq - i0, wave, lane);
@@ -793,8 +954,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     }
   }
 
-  if (SPLIT && wave_live && kj < sk) {
-    store_partial_kv<D>(a.part, a.rows_k, a.split_kv, P.H, sg, h, part_row(P.ks.mode, P.Sk, b, k0, kj), dk, dv, g);
+  if constexpr (SPLIT) {
+    if (wave_live && kj < sk)
+      store_partial_kv<D>(a.part, a.rows_k, a.split_kv, P.H, sg, h, part_row(P.ks.mode, P.Sk, b, k0, kj), dk, dv, g);
+    if (a.cnt_kv != nullptr && last_arrival(a.cnt_kv + (long long)bh * nkb + kb, nsplit))
+      sum_partials<T, D, NT, true>(a.part, a.rows_k, P.H, nsplit, h, P.ks.mode, P.Sk, b, k0, j0, jlast + 1, dkp,
+                                   a.dk.ss, dvp, a.dv.ss, P.scale, tid);
   } else if (wave_live && kj < sk) {
     T* dkrow = dkp + (long long)kj * a.dk.ss;
     T* dvrow = dvp + (long long)kj * a.dv.ss;
@@ -814,6 +979,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
 }
 
+template <typename M, int D, int NW, int BMQ, int WPE, bool FEAT = false, bool SPLIT = false>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_dkdv16_kernel(BwdArgs a) {
+  dkdv16_body<M, D, NW, BMQ, FEAT, SPLIT>(a, blockIdx.x, gridDim.x);
+}
+
 // ------------------------------------- 16-bit dK/dV, producer / consumer
 //
 // Eight waves for 128 keys.  Waves w and w+4 share a SIMD and own keys
@@ -830,20 +1000,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 // consumer still reads tile t-1), P^T of each step gets its own of three
 // buffers.  Each role needs only K or V and only dV or dK, so two waves fit
 // in one SIMD's registers.
-// LDS of the 16-bit backward kernels that run 8-wave workgroups: three
-// stages of [Q | dO | LSE log2 e | Delta] (dK/dV) or [K | V] (dQ) and three
-// fp16 P buffers.  They are named at namespace scope so that the kernel
-// bodies refer to these objects directly: the compiler then knows every
-// access is to LDS, and which stage array a direct load fills.  Sized for
-// 64-row tiles of up to 128 columns of 16-bit elements.
-constexpr int kBwdStageBytes = 2 * 64 * 128 * 2 + 4 * 64 * 4;
-constexpr int kBwdXBytes = 4 * 2 * 2 * 64 * 16;
-__shared__ __attribute__((aligned(1024))) char g_bwd_st0[kBwdStageBytes];
-__shared__ __attribute__((aligned(1024))) char g_bwd_st1[kBwdStageBytes];
-__shared__ __attribute__((aligned(1024))) char g_bwd_st2[kBwdStageBytes];
-__shared__ __attribute__((aligned(16))) char g_bwd_x0[kBwdXBytes];
-__shared__ __attribute__((aligned(16))) char g_bwd_x1[kBwdXBytes];
-__shared__ __attribute__((aligned(16))) char g_bwd_x2[kBwdXBytes];
 
 // The kernel's BwdArgs argument, read in place from the kernel-argument
 // segment (a kernel whose first argument is BwdArgs).  Bodies shared by
@@ -1533,9 +1689,12 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
     }
   }
 
-  if (SPLIT && row_ok) {
-    store_partial_q<D>(a.part + 2LL * a.split_kv * P.H * a.rows_k * D, a.rows_q, P.H, sg, h,
-                       part_row(P.qs.mode, P.Sq, b, q0, qi), dq, g);
+  if constexpr (SPLIT) {
+    float* const part_q = a.part + 2LL * a.split_kv * P.H * a.rows_k * D;
+    if (row_ok) store_partial_q<D>(part_q, a.rows_q, P.H, sg, h, part_row(P.qs.mode, P.Sq, b, q0, qi), dq, g);
+    if (a.cnt_q != nullptr && last_arrival(a.cnt_q + (long long)bh * nq + qb, nsplit))
+      sum_partials<T, D, NT, false>(part_q, a.rows_q, P.H, nsplit, h, P.qs.mode, P.Sq, b, q0, i0, ilast + 1, dqp,
+                                    a.dq.ss, nullptr, 0, P.scale, tid);
   } else if (row_ok) {
     T* dqrow = dqp + (long long)qi * a.dq.ss;
     const float sc = P.scale;
@@ -1574,14 +1733,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     dq16_body<M, D, 8, 64>(hw - nkv, (int)gridDim.x - nkv);
 }
 
+// ------------------------------------------------ split mode, one grid
+//
+// Blocks [0, nkv) are split dK/dV copies, the rest split dQ copies: the two
+// run side by side rather than one grid after the other.  Split mode is for
+// calls whose grids leave most of the GPU idle, where a kernel takes about
+// as long as its longest workgroup.
+template <typename M, int D, int NW_KV, int BMQ, int NW_Q, int BN, int WPE>
+__global__ __launch_bounds__(NW_KV * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_bwd_split16_kernel(
+    BwdArgs a, int nkv) {
+  static_assert(NW_KV == NW_Q, "one workgroup size");
+  const int hw = (int)blockIdx.x;
+  if (hw < nkv)
+    dkdv16_body<M, D, NW_KV, BMQ, false, true, true>(a, (unsigned)hw, (unsigned)nkv);
+  else
+    dq16_body<M, D, NW_Q, BN, false, true>(hw - nkv, (int)gridDim.x - nkv);
+}
+
+// The same for fp32.
+template <typename M, int D, int NW_KV, int BMQ, int NW_Q, int BN>
+__global__ __launch_bounds__(NW_KV * 64) void attn_bwd_split_kernel(BwdArgs a, int nkv) {
+  static_assert(NW_KV == NW_Q, "one workgroup size");
+  const unsigned hw = blockIdx.x;
+  if (hw < (unsigned)nkv)
+    dkdv_body<M, D, NW_KV, BMQ, false, true>(a, hw, (unsigned)nkv);
+  else
+    dq_body<M, D, NW_Q, BN, false, true>(a, hw - (unsigned)nkv, gridDim.x - (unsigned)nkv);
+}
+
 // ------------------------------------------------------------ split reduce
 
-// Split-mode epilogue, one workgroup per (side, sequence, head, row slice):
-// each row of a sequence's length gets the sum of its partial rows in copy
-// order (so the result does not depend on the schedule), times the scale
-// for dQ and dK, rounded to the output type; rows of the sequence's room
-// past its length get zeros (as the padding kernel writes without split).
-// sides: 1 Q (dQ), 2 K (dK, dV), 3 both; the grid is
+// Split-mode epilogue as its own grid, where the partials are too large for
+// one workgroup per block to sum them fast: one workgroup per (side,
+// sequence, head, row slice); each row of a sequence's length gets the sum
+// of its partial rows in copy order, times the scale for dQ and dK, rounded
+// to the output type.  sides: 1 Q (dQ), 2 K (dK, dV), 3 both; the grid is
 // nsides * B * H * slices, Q side first.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, int sides, int slices) {
@@ -1599,7 +1785,6 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, int sid
   const int h = bh % P.H, b = bh / P.H;
   const SideArgs& S = side ? P.ks : P.qs;
   const SideRows r = side_rows(S, b);
-  const long long limit = r.room > r.n ? r.room : r.n;
   const long long rows = side ? a.rows_k : a.rows_q;
   const int groups = side ? a.split_kv : a.split_q;
   const float* p0 = side ? a.part : a.part + 2LL * a.split_kv * P.H * a.rows_k * D;  // dK or dQ
@@ -1607,17 +1792,15 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, int sid
   const long long gstride = (long long)P.H * rows * D;
   const Operand o0 = side ? a.dk : a.dq;
   const float sc = P.scale;
-  for (long long i = (long long)sl * RPP + ri; i < limit; i += (long long)slices * RPP) {
+  for (long long i = (long long)sl * RPP + ri; i < r.n; i += (long long)slices * RPP) {
     float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
-    if (i < r.n) {
-      const long long off = ((long long)h * rows + part_row(S.mode, S.S, b, r.r0, (int)i)) * D + d;
-      for (int g = 0; g < groups; ++g) {
-        const float4 x = *reinterpret_cast<const float4*>(p0 + g * gstride + off);
-        s0.x += x.x; s0.y += x.y; s0.z += x.z; s0.w += x.w;
-        if (side) {
-          const float4 y = *reinterpret_cast<const float4*>(p1 + g * gstride + off);
-          s1.x += y.x; s1.y += y.y; s1.z += y.z; s1.w += y.w;
-        }
+    const long long off = ((long long)h * rows + part_row(S.mode, S.S, b, r.r0, (int)i)) * D + d;
+    for (int g = 0; g < groups; ++g) {
+      const float4 x = *reinterpret_cast<const float4*>(p0 + g * gstride + off);
+      s0.x += x.x; s0.y += x.y; s0.z += x.z; s0.w += x.w;
+      if (side) {
+        const float4 y = *reinterpret_cast<const float4*>(p1 + g * gstride + off);
+        s1.x += y.x; s1.y += y.y; s1.z += y.z; s1.w += y.w;
       }
     }
     const long long row = r.r0 + i;
@@ -1659,7 +1842,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
         (a.p.qs.mode & kSeqStacked) ? a.p.total_q * a.p.H : (long long)a.p.B * a.p.H * a.p.Sq;
     constexpr int CE = 16 / (int)sizeof(T), CH = D / CE;
     constexpr int G = CH <= 8 ? 8 : (CH <= 16 ? 16 : 32);
-    const long long nblk = (nrows + (256 / G) - 1) / (256 / G);
+    long long nblk = (nrows + (256 / G) - 1) / (256 / G);
+    if (a.ncnt > 0 && nblk < 1) nblk = 1;  // it also zeroes the split counters
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (nblk > 0) {
       err = ex(reinterpret_cast<const void*>(&attn_bwd_pre_kernel<T, D>), "attn_bwd_pre_kernel", (unsigned)nblk,
@@ -1667,38 +1851,55 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
       if (err != hipSuccess) return err;
     }
   }
-  // Split mode (the call's grids would leave most of the GPU idle): the
-  // plain dK/dV and dQ kernels over split copies of their grids, then one
-  // reduction, which also writes the rows past each length.
+  // Split mode (the call's grids would leave most of the GPU idle): split
+  // copies of the dK/dV and dQ grids, both in one launch where the two
+  // kinds' LDS fits one workgroup.  In fp32, whose products are slow enough
+  // that the copies' partials are small next to their work, the last copy
+  // of each block sums them; in fp16 / bf16 a reduction grid does, spread
+  // over the whole GPU.
   if (a.part) {
-    if (stages & kStageDkDv) {
-      const long long nblk = (a.p.Sk + NW_KV * 32 - 1) / (NW_KV * 32) * a.p.H * a.p.B * a.split_kv;
-      if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-      if (nblk > 0) {
+    if (a.split_kv < 1 || a.split_kv > 8 || a.split_q < 1 || a.split_q > 8) return hipErrorInvalidValue;
+    constexpr bool kLastCopySums = !S::k16;
+    BwdArgs sa = a;
+    if (!kLastCopySums) sa.cnt_kv = sa.cnt_q = nullptr;
+    const long long nkv =
+        (stages & kStageDkDv) ? (a.p.Sk + NW_KV * 32 - 1) / (NW_KV * 32) * a.p.H * a.p.B * a.split_kv : 0;
+    const long long nq = (stages & kStageDq) ? (a.p.Sq + NW_Q * 32 - 1) / (NW_Q * 32) * a.p.H * a.p.B * a.split_q : 0;
+    if (nkv + nq > 0x7fffffffLL) return hipErrorInvalidValue;
+    bool one = false;
+    if constexpr (S::k16 ? D <= 128 : D <= 64) one = nkv > 0 && nq > 0;
+    if (one) {
+      if constexpr (S::k16 ? D <= 128 : D <= 64) {
+        if constexpr (S::k16)
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_split16_kernel<M, D, NW_KV, BMQ, NW_Q, BN, S::WPE_KV>),
+                   "attn_bwd_split16_kernel", (unsigned)(nkv + nq), (unsigned)(NW_KV * 64), sa, (int)nkv);
+        else
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_split_kernel<M, D, NW_KV, BMQ, NW_Q, BN>),
+                   "attn_bwd_split_kernel", (unsigned)(nkv + nq), (unsigned)(NW_KV * 64), sa, (int)nkv);
+        if (err != hipSuccess) return err;
+      }
+    } else {
+      if (nkv > 0) {
         if constexpr (S::k16)
           err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV, false, true>),
-                   "attn_bwd_dkdv16_kernel", (unsigned)nblk, (unsigned)(NW_KV * 64), a);
+                   "attn_bwd_dkdv16_kernel", (unsigned)nkv, (unsigned)(NW_KV * 64), sa);
         else
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ, false, true>), "attn_bwd_dkdv_kernel",
-                   (unsigned)nblk, (unsigned)(NW_KV * 64), a);
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ, false, true>),
+                   "attn_bwd_dkdv_kernel", (unsigned)nkv, (unsigned)(NW_KV * 64), sa);
         if (err != hipSuccess) return err;
       }
-    }
-    if (stages & kStageDq) {
-      const long long nblk = (a.p.Sq + NW_Q * 32 - 1) / (NW_Q * 32) * a.p.H * a.p.B * a.split_q;
-      if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-      if (nblk > 0) {
+      if (nq > 0) {
         if constexpr (S::k16)
           err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, S::WPE_Q, false, true>),
-                   "attn_bwd_dq16_kernel", (unsigned)nblk, (unsigned)(NW_Q * 64), a);
+                   "attn_bwd_dq16_kernel", (unsigned)nq, (unsigned)(NW_Q * 64), sa);
         else
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN, false, true>), "attn_bwd_dq_kernel",
-                   (unsigned)nblk, (unsigned)(NW_Q * 64), a);
+          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN, false, true>),
+                   "attn_bwd_dq_kernel", (unsigned)nq, (unsigned)(NW_Q * 64), sa);
         if (err != hipSuccess) return err;
       }
     }
-    const int sides = ((stages & kStageDq) ? 1 : 0) | ((stages & kStageDkDv) ? 2 : 0);
-    if (sides) {
+    const int sides = (nq > 0 ? 1 : 0) | (nkv > 0 ? 2 : 0);
+    if (!kLastCopySums && sides) {
       constexpr int RPP = 256 / (D / 4);
       const int rows = sides == 1 ? a.p.Sq : (sides == 2 ? a.p.Sk : max(a.p.Sq, a.p.Sk));
       const int slices = max(1, min(64, (rows + RPP - 1) / RPP));
@@ -1824,10 +2025,8 @@ static hipError_t launch_bwd_any(int dtype, int head_dim, const BwdArgs& a, int 
     case 2: err = launch_bwd_d<MmaBF16>(head_dim, a, stages, ex); break;
     default: return hipErrorNotSupported;
   }
-  // Rows of a sequence's room past its length: dQ, and dK / dV, are zero
-  // (written by the reduction in split mode).
+  // Rows of a sequence's room past its length: dQ, and dK / dV, are zero.
   const int esz = dtype == 0 ? 4 : 2, rb = head_dim * esz;
-  if (a.part) return err;
   if (err == hipSuccess && (stages & kStageDq)) err = launch_pad_rows(a.p, a.dq, Operand{}, nullptr, 0, rb, esz, ex);
   if (err == hipSuccess && (stages & kStageDkDv)) err = launch_pad_rows(a.p, a.dk, a.dv, nullptr, 1, rb, esz, ex);
   return err;

@@ -112,13 +112,20 @@ struct BwdArgs {
   // Split mode (null part: off).  The dK/dV grid is repeated split_kv times,
   // copy g walking its g-th share of the query tiles, and the dQ grid
   // split_q times over the key tiles; each copy stores unscaled fp32 sums
-  // into part, and a reduction kernel adds them in copy order.  Layout, in
-  // rows of head_dim floats: dK [split_kv][H][rows_k], then dV likewise,
-  // then dQ [split_q][H][rows_q]; a row's index is its storage row (stacked
-  // side) or b * seqlen + local row (padded side).
+  // into part, and the last copy of a block to finish adds them in copy
+  // order.  Layout, in rows of head_dim floats: dK [split_kv][H][rows_k],
+  // then dV likewise, then dQ [split_q][H][rows_q]; a row's index is its
+  // storage row (stacked side) or b * seqlen + local row (padded side).
+  // Arrival counters, one per block of 128 rows: cnt_kv[(b H + h) nkb + kb]
+  // for the dK/dV blocks, cnt_q[(b H + h) nqb + qb] for the dQ blocks
+  // (cnt_q = cnt_kv + B H nkb); the preprocess zeroes all ncnt of them and
+  // the last arrival at a block resets its counter.
   float* part;
   long long rows_q, rows_k;
   int split_kv, split_q;
+  unsigned* cnt_kv;
+  unsigned* cnt_q;
+  long long ncnt;
 };
 
 // Partial-sum row of local row i of sequence b on a side of the given mode

@@ -322,15 +322,19 @@ def lib_ws(p):
 def split_bytes(f):
     """Partial-sum bytes of the backward's split mode, from its documented
     rule: split when the dK/dV or the dQ grid (128 rows per workgroup) has
-    fewer than 64 workgroups; copies = min(ceil(256 / workgroups), 8, tiles
+    fewer than 64 workgroups (at fp16 / bf16 head dims 96 and 128, only up
+    to 16 dK/dV workgroups); copies = min(ceil(256 / workgroups), 8, tiles
     of the split axis (64 rows, 32 in fp32)); fp32 partials of dK, dV (per
     key copy) and dQ (per query copy), capped at 8 MiB by dropping copies
-    from the larger count; 0 when no copy is left to split."""
+    from the larger count; then one 4-byte arrival counter per dK/dV and
+    per dQ workgroup of the unsplit grids; 0 when no copy is left to split."""
     if f.flags & bd.FLAG_NO_SPLIT:
         return 0
     B, H, D, Sq, Sk = f.batch, f.heads, f.head_dim, f.seqlen_q, f.seqlen_k
     nkv, nq = B * H * -(-Sk // 128), B * H * -(-Sq // 128)
     if nkv == 0 or nq == 0 or (nkv >= 64 and nq >= 64):
+        return 0
+    if f.dtype != bd.FP32 and D in (96, 128) and nkv > 16:
         return 0
     tile = 32 if f.dtype == bd.FP32 else 64
     gkv = max(1, min(-(-256 // nkv), 8, -(-Sq // tile)))
@@ -345,7 +349,7 @@ def split_bytes(f):
             gq -= 1
     if nbytes() > 8 << 20 or (gkv == 1 and gq == 1):
         return 0
-    return -(-nbytes() // 256) * 256
+    return -(-nbytes() // 256) * 256 + -(-4 * (nkv + nq) // 256) * 256
 
 
 def test_workspace_size():
@@ -354,7 +358,7 @@ def test_workspace_size():
     lib = bd.lib()
     f = dense_params(B=2, H=3, S=100)
     delta = 2 * (((2 * 3 * 100 * 4 + 255) // 256) * 256)
-    assert split_bytes(f) == 4 * 64 * 3 * (2 * 2 * 200 + 2 * 200)
+    assert split_bytes(f) == 4 * 64 * 3 * (2 * 2 * 200 + 2 * 200) + 256
     assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f))) == delta + split_bytes(f)
     f.flags = bd.FLAG_NO_SPLIT
     assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f))) == delta
@@ -364,7 +368,7 @@ def test_workspace_size():
     big = dense_params(B=8, H=16, S=1024)                  # grids fill the GPU: no split
     assert split_bytes(big) == 0
     assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(big))) == 2 * 8 * 16 * 1024 * 4
-    for B, H, S, D, dt in ((1, 2, 128, 64, bd.FP32), (1, 1, 4000, 128, bd.BF16), (3, 5, 700, 80, bd.FP16),
+    for B, H, S, D, dt in ((1, 2, 128, 64, bd.FP32), (1, 1, 4000, 128, bd.BF16), (1, 2, 700, 128, bd.BF16), (3, 5, 700, 80, bd.FP16),
                            (1, 8, 1023, 128, bd.BF16), (2, 1, 8000, 64, bd.FP32)):
         f = dense_params(B=B, H=H, S=S, D=D, dtype=dt)
         stat = ((B * H * S * 4 + 255) // 256) * 256

@@ -70,21 +70,45 @@ def test_tiny_fp32_config():
     Case(B=1, H=2, Sq=128, D=64, dtype=torch.float32, scale=0.125, seed=1).check()
 
 
-@pytest.mark.parametrize("dtype,D,B,H,S", [(torch.float32, 64, 1, 2, 128), (torch.bfloat16, 128, 1, 4, 1000),
+@pytest.mark.parametrize("dtype,D,B,H,S", [(torch.float32, 64, 1, 2, 128), (torch.bfloat16, 128, 1, 2, 1000),
                                            (torch.float16, 80, 2, 3, 300)])
 def test_split_mode_plan_and_bits(dtype, D, B, H, S):
     """Small problems run the backward in split mode: the plan lists the
-    split grids and the reduction, the workspace holds the partial sums, and
-    the results are run-to-run identical and within the oracle's bounds,
-    next to the unsplit path's."""
+    preprocess and one grid of split dK/dV and dQ copies (in fp32 each
+    block's last copy sums the partials, in fp16 / bf16 a reduction grid
+    follows), the workspace holds the partial sums and the arrival counters,
+    and the results are run-to-run identical (also on a reused workspace,
+    whose counters the last arrivals reset, and by stage calls) and within
+    the oracle's bounds, next to the unsplit path's."""
     c = Case(B=B, H=H, Sq=S, D=D, dtype=dtype, seed=15)
     q, k, v, do = (t.cuda() for t in c.cpu)
     o, lse = bd.attn_fwd(q, k, v, scale=c.scale)
-    p, _ = bd.prepare_bwd(do, q, k, v, o, lse, scale=c.scale)
+    p, ws_t = bd.prepare_bwd(do, q, k, v, o, lse, scale=c.scale)
     names = [n for n, _, _ in bd.plan("attn_bwd", p)]
-    assert names[-1] == "attn_bwd_reduce_kernel" and len(names) == 4, names
+    if dtype == torch.float32:
+        one, want = "attn_bwd_split_kernel", ["attn_bwd_pre_kernel", "attn_bwd_split_kernel"]
+    else:
+        one = "attn_bwd_split16_kernel"
+        want = ["attn_bwd_pre_kernel", one, "attn_bwd_reduce_kernel"]
+    assert names == want, names
     p0, _ = bd.prepare_bwd(do, q, k, v, o, lse, scale=c.scale, split=False)
-    assert "attn_bwd_reduce_kernel" not in [n for n, _, _ in bd.plan("attn_bwd", p0)]
+    assert one not in [n for n, _, _ in bd.plan("attn_bwd", p0)]
+    outs = ws_t[:3]
+    bd.launch("attn_bwd", p)
+    first = [t.clone() for t in outs]
+    # The same workspace again, by stages: separate split dK/dV and dQ
+    # grids, then both in one grid.
+    for t in outs:
+        t.fill_(7)
+    bd.launch("attn_bwd_dkdv", p)
+    bd.launch("attn_bwd_dq", p)
+    second = [t.clone() for t in outs]
+    for t in outs:
+        t.fill_(7)
+    bd.launch("attn_bwd_dkdv_dq", p)
+    torch.cuda.synchronize()
+    for x, y, z in zip(first, second, outs):
+        assert torch.equal(x, y) and torch.equal(x, z)
     ws = bd.workspace_size(do, q, k, v, o, lse, scale=c.scale)
     ws0 = bd.workspace_size(do, q, k, v, o, lse, scale=c.scale, split=False)
     assert ws > ws0
