@@ -314,27 +314,29 @@ hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
  * is repeated so that copy g of n walks the g-th of n contiguous shares of
  * the tiles it would visit (query tiles for dK/dV, key tiles for dQ), about
  * 256 workgroups in all (at most 8 copies, one per tile, fp32 partial sums
- * of at most 8 MiB); the copies store fp32 partial sums in the workspace
- * and count themselves in on an arrival counter per block there, and the
- * last copy of a block to arrive adds the block's partials in copy order,
- * scales, rounds and writes them (so the result does not depend on which
- * copy is last), and resets the counter.  No workgroup waits for another.
- * The dK/dV and dQ copies run as one grid where both kinds fit one
- * workgroup's LDS (fp16 / bf16 up to head_dim 128, fp32 up to 64).  The sums
- * then group the tiles differently from the unsplit path (results differ in
- * rounding only, and stay run-to-run identical).  attn_bwd_preprocess
- * zeroes the counters, so the step calls below need it first, as they do
- * anyway for Delta; repeated dK/dV or dQ calls on one workspace are fine.
- * Split calls that overlap on one workspace race, as any calls that share a
- * workspace do. */
+ * of at most 8 MiB; at fp16 / bf16 head dims 96 and 128 only while the
+ * dK/dV grid has at most 16 workgroups); the copies store fp32 partial sums
+ * in the workspace.  In fp32 each copy then counts itself in on an arrival
+ * counter per block there, and the last copy of a block to arrive adds the
+ * block's partials in copy order, scales, rounds and writes them (so the
+ * result does not depend on which copy is last), and resets the counter; no
+ * workgroup waits for another.  In fp16 / bf16 a last kernel does that sum
+ * over the whole GPU.  The dK/dV and dQ copies run as one grid where both
+ * kinds fit one workgroup's LDS (fp16 / bf16 up to head_dim 128, fp32 up to
+ * 64).  The sums then group the tiles differently from the unsplit path
+ * (results differ in rounding only, and stay run-to-run identical).
+ * attn_bwd_preprocess zeroes the counters, so the step calls below need it
+ * first, as they do anyway for Delta; repeated dK/dV or dQ calls on one
+ * workspace are fine.  Split calls that overlap on one workspace race, as
+ * any calls that share a workspace do. */
 hipError_t attn_bwd(const attn_bwd_params *p, hipStream_t stream);
 
 /* The three steps of attn_bwd as separate calls, for callers that schedule
  * or time them one by one.  Same parameters, validation and errors as
  * attn_bwd; each enqueues one kernel on `stream`, and attn_bwd_dkdv /
  * attn_bwd_dq also the row-zeroing kernel of their outputs when seqused
- * arrays are given (in split mode: their split grid, whose last copies
- * write the outputs).  They must run in this order on one stream (or be
+ * arrays are given (in split mode: their split grid, and in fp16 / bf16
+ * the reduction of their outputs).  They must run in this order on one stream (or be
  * ordered by events): attn_bwd_dkdv and attn_bwd_dq read the Delta and LSE
  * log2(e) that attn_bwd_preprocess leaves in the workspace, which must not
  * be touched in between.
