@@ -23,7 +23,12 @@ writes O and the fp32 LSE; backward reads Q, K, V, O, dO and LSE, writes dQ,
 dK and dV, and writes and reads the fp32 Delta.
 
 Besides the headline workload, the line carries `cells`: the same
-measurement (fewer steps) on every other workload of the pages' shapes.
+measurement (fewer steps) on every other workload of the pages' shapes, with
+two differences that matter only for calls of tens of microseconds: the
+backward's two calls are timed together by one event pair (an event between
+two launches costs a few microseconds of device time), and a short spin
+kernel queued first lets the host enqueue every timed step before the device
+reaches them, so the events see device time, not the host's launch rate.
 
 The CPU baseline is the fp64 oracle timed on this host on (sequence, head)
 slices of the headline workload, scaled to the same unit.
@@ -219,6 +224,25 @@ def mfma_probe(n: int, steps: int) -> None:
                       "frac_of_bf16_peak": round(tf / PEAK_MFMA_16, 4)}), flush=True)
 
 
+_SPIN = {}
+
+
+def spin_cycles(ms):
+    """Cycles of torch.cuda._sleep that last about ms milliseconds on this
+    device (calibrated once with HIP events)."""
+    import torch
+    if "per_ms" not in _SPIN:
+        n = 1 << 20
+        torch.cuda._sleep(n)  # first call loads the kernel
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        torch.cuda.synchronize()
+        _SPIN["per_ms"] = n / max(e0.elapsed_time(e1), 1e-3)
+    return int(_SPIN["per_ms"] * ms) + 1
+
+
 class Run:
     """One workload on the GPU: inputs in HBM, the params of each call, the
     library's launch plan, and timed steps."""
@@ -257,31 +281,49 @@ class Run:
         self.stream = torch.cuda.current_stream(dev)
         self.plan = {c: bd.plan(ENTRY[c], self.params[c], self.stream.cuda_stream) for c in self.calls}
 
-    def step(self, evs=None):
+    def step(self, evs=None, marks=None):
+        """One step: every call in order, with an event before the calls
+        listed in marks (default: all) and one at the end."""
         from scaled_dot_product_20_amd import binding as bd
         sid = self.stream.cuda_stream
-        for i, c in enumerate(self.calls):
-            if evs is not None:
-                evs[i].record(self.stream)
+        marks = self.calls if marks is None else marks
+        n = 0
+        for c in self.calls:
+            if evs is not None and c in marks:
+                evs[n].record(self.stream)
+                n += 1
             bd.launch(ENTRY[c], self.params[c], sid)
         if evs is not None:
-            evs[len(self.calls)].record(self.stream)
+            evs[n].record(self.stream)
 
-    def time(self, steps, warmup):
-        """(wall ms per step, {call: average ms from HIP events on the launch stream})."""
+    def time(self, steps, warmup, prefill=False, per_call=True):
+        """(wall ms per step, {call: average ms from HIP events on the launch stream}).
+
+        per_call: an event between every two calls; otherwise only between
+        the forward and the backward, whose two calls (preprocess, dK/dV +
+        dQ) then run back to back and are reported together as "bwd" (an
+        event between two launches costs a few microseconds of device time,
+        which matters for calls of tens of microseconds).
+        prefill: first queue a short spin kernel on the stream, long enough
+        for the host to enqueue every timed step behind it, so that the
+        events measure the calls' device time and not the host's launch
+        rate.  The wall time then includes the spin and is not meaningful."""
         import torch
+        marks = self.calls if per_call else [c for c in self.calls if c != "bwd_dkdv_dq"]
+        names = list(marks) if per_call else ["bwd" if c == "bwd_preprocess" else c for c in marks]
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.calls) + 1)]
-                  for _ in range(steps)]
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 1)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        if prefill:
+            torch.cuda._sleep(spin_cycles(0.25 * steps))
         for s in range(steps):
-            self.step(events[s])
+            self.step(events[s], marks)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = {c: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / steps for i, c in enumerate(self.calls)}
+        per = {c: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / steps for i, c in enumerate(names)}
         return wall * 1e3 / steps, per
 
     def kernels(self, call):
@@ -294,8 +336,8 @@ class Run:
                        "frac_of_peak": round(fwd_flop / per["fwd"] / 1e9 / peak, 4),
                        "gb_s": round(self.fwd_bytes / per["fwd"] / 1e6, 1),
                        "kernels": self.kernels("fwd")}}
-        if "bwd_dkdv_dq" in per:
-            ms = per["bwd_preprocess"] + per["bwd_dkdv_dq"]
+        if "bwd_dkdv_dq" in per or "bwd" in per:
+            ms = per["bwd"] if "bwd" in per else per["bwd_preprocess"] + per["bwd_dkdv_dq"]
             out["bwd"] = {"ms": round(ms, 4), "tflops": round(bwd_flop / ms / 1e9, 2),
                           "frac_of_peak": round(bwd_flop / ms / 1e9 / peak, 4),
                           "gb_s": round(self.bwd_bytes / ms / 1e6, 1),
@@ -410,7 +452,7 @@ def main():
             t0 = time.perf_counter()
             cw = wl_all[name]
             r = Run(cw, names[dn], ("fwd", "bwd"), dev)
-            _, cper = r.time(args.cell_steps, args.cell_warmup)
+            _, cper = r.time(args.cell_steps, args.cell_warmup, prefill=True, per_call=False)
             cells[f"{name}:{dn}"] = r.summary(cper, peak_of(names[dn]))
             cells[f"{name}:{dn}"]["visible_pairs"] = r.pairs
             r.release()
