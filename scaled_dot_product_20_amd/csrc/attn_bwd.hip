@@ -114,13 +114,13 @@ __device__ __forceinline__ bool last_arrival(unsigned* cnt, int n) {
 // rows in copy order (so the result does not depend on which copy is last),
 // times sc, rounded into o0; with KV the second section (dV, one section of
 // G H rows further on) goes unscaled into o1.  One workgroup reads all of
-// it, so each thread keeps the loads of two float4 columns of every copy in
-// flight at once.
+// it, so each thread keeps 32 float4 loads (U columns of every copy and
+// section) in flight at once.
 template <typename T, int D, int NT, bool KV, int G>
 __device__ __forceinline__ void sum_partials_g(const float* part, long long rows, int H, int h, int mode, int S,
                                                int b, long long r0, int lo, int hi, T* o0, long long ss0, T* o1,
                                                long long ss1, float sc, int tid) {
-  constexpr int V4 = D / 4, U = 2;
+  constexpr int V4 = D / 4, U = (KV ? 16 : 32) / G > 1 ? (KV ? 16 : 32) / G : 1;
   static_assert(D % 4 == 0, "row shape");
   const long long gstride = (long long)H * rows * D;
   const float* p1 = part + G * gstride;
