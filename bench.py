@@ -22,13 +22,13 @@ Algorithmic HBM bytes: forward reads Q and the K/V rows some query sees and
 writes O and the fp32 LSE; backward reads Q, K, V, O, dO and LSE, writes dQ,
 dK and dV, and writes and reads the fp32 Delta.
 
-Besides the headline workload, the line carries `cells`: the same
-measurement (fewer steps) on every other workload of the pages' shapes, with
-two differences that matter only for calls of tens of microseconds: the
-backward's two calls are timed together by one event pair (an event between
-two launches costs a few microseconds of device time), and a short spin
-kernel queued first lets the host enqueue every timed step before the device
-reaches them, so the events see device time, not the host's launch rate.
+Besides the headline workload, the line carries `cells`: every workload of
+the pages' shapes, each pass timed as a run of back-to-back calls (the
+backward's two calls together) between two events, behind a short spin
+kernel that lets the host enqueue the run first.  For calls of tens of
+microseconds this keeps per-call events (a few microseconds of device time
+each) and the host's launch rate out of the numbers; for the rest it equals
+the per-call timing.
 
 The CPU baseline is the fp64 oracle timed on this host on (sequence, head)
 slices of the headline workload, scaled to the same unit.
@@ -281,50 +281,59 @@ class Run:
         self.stream = torch.cuda.current_stream(dev)
         self.plan = {c: bd.plan(ENTRY[c], self.params[c], self.stream.cuda_stream) for c in self.calls}
 
-    def step(self, evs=None, marks=None):
-        """One step: every call in order, with an event before the calls
-        listed in marks (default: all) and one at the end."""
+    def step(self, evs=None):
         from scaled_dot_product_20_amd import binding as bd
         sid = self.stream.cuda_stream
-        marks = self.calls if marks is None else marks
-        n = 0
-        for c in self.calls:
-            if evs is not None and c in marks:
-                evs[n].record(self.stream)
-                n += 1
+        for i, c in enumerate(self.calls):
+            if evs is not None:
+                evs[i].record(self.stream)
             bd.launch(ENTRY[c], self.params[c], sid)
         if evs is not None:
-            evs[n].record(self.stream)
+            evs[len(self.calls)].record(self.stream)
 
-    def time(self, steps, warmup, prefill=False, per_call=True):
-        """(wall ms per step, {call: average ms from HIP events on the launch stream}).
-
-        per_call: an event between every two calls; otherwise only between
-        the forward and the backward, whose two calls (preprocess, dK/dV +
-        dQ) then run back to back and are reported together as "bwd" (an
-        event between two launches costs a few microseconds of device time,
-        which matters for calls of tens of microseconds).
-        prefill: first queue a short spin kernel on the stream, long enough
-        for the host to enqueue every timed step behind it, so that the
-        events measure the calls' device time and not the host's launch
-        rate.  The wall time then includes the spin and is not meaningful."""
+    def time(self, steps, warmup):
+        """(wall ms per step, {call: average ms from HIP events on the launch stream})."""
         import torch
-        marks = self.calls if per_call else [c for c in self.calls if c != "bwd_dkdv_dq"]
-        names = list(marks) if per_call else ["bwd" if c == "bwd_preprocess" else c for c in marks]
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 1)] for _ in range(steps)]
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.calls) + 1)]
+                  for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        if prefill:
-            torch.cuda._sleep(spin_cycles(0.25 * steps))
         for s in range(steps):
-            self.step(events[s], marks)
+            self.step(events[s])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = {c: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / steps for i, c in enumerate(names)}
+        per = {c: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / steps for i, c in enumerate(self.calls)}
         return wall * 1e3 / steps, per
+
+    def time_runs(self, steps, warmup):
+        """{"fwd": ms, "bwd": ms}: each pass as a run of `steps` back-to-back
+        calls (the backward: preprocess, then dK/dV + dQ) between two HIP
+        events, behind a short spin kernel that lets the host enqueue the
+        whole run before the device reaches it.  For calls of tens of
+        microseconds an event between two launches, or a host slower than
+        the device, would otherwise show up in the time."""
+        import torch
+        from scaled_dot_product_20_amd import binding as bd
+        sid = self.stream.cuda_stream
+        runs = [("fwd", ["fwd"])] + ([("bwd", ["bwd_preprocess", "bwd_dkdv_dq"])] if "bwd_dkdv_dq" in self.calls else [])
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        per = {}
+        for name, calls in runs:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(spin_cycles(0.25 * steps))
+            e0.record(self.stream)
+            for _ in range(steps):
+                for c in calls:
+                    bd.launch(ENTRY[c], self.params[c], sid)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            per[name] = e0.elapsed_time(e1) / steps
+        return per
 
     def kernels(self, call):
         return "+".join(name for name, _, _ in self.plan[call])
@@ -452,7 +461,7 @@ def main():
             t0 = time.perf_counter()
             cw = wl_all[name]
             r = Run(cw, names[dn], ("fwd", "bwd"), dev)
-            _, cper = r.time(args.cell_steps, args.cell_warmup, prefill=True, per_call=False)
+            cper = r.time_runs(args.cell_steps, args.cell_warmup)
             cells[f"{name}:{dn}"] = r.summary(cper, peak_of(names[dn]))
             cells[f"{name}:{dn}"]["visible_pairs"] = r.pairs
             r.release()
