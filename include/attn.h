@@ -365,9 +365,10 @@ hipError_t attn_bwd_dkdv_dq(const attn_bwd_params *p, hipStream_t stream);
  * then, in split mode, the fp32 partial sums (head_dim floats per copy, head
  * and row: dK and dV per key-side copy, dQ per query-side copy; rows are the
  * stacked tensor's rows, or batch * seqlen for a padded side), rounded up to
- * 256 bytes, and a 4-byte arrival counter per dK/dV and per dQ workgroup of
- * the unsplit grids (B H ceil(seqlen_k / 128) + B H ceil(seqlen_q / 128)),
- * rounded up to 256 bytes; 0 when the problem is malformed.  A repacked call (see above)
+ * 256 bytes, and a 4-byte arrival counter per block of R rows of the dK/dV
+ * and dQ grids (B H ceil(seqlen_k / R) + B H ceil(seqlen_q / R); R = 64 in
+ * fp32, 128 in fp16 / bf16), rounded up to 256 bytes; 0 when the problem is
+ * malformed.  A repacked call (see above)
  * needs, before those (sized for head dim Dp), padded copies of q, k, v, o,
  * dout, dq, dk and dv, each rounded up to 256 bytes.  Repacked, the three
  * step calls share the copies through the workspace: attn_bwd_preprocess

@@ -287,12 +287,13 @@ uint64_t delta_bytes(const attn_fwd_params* p) { return 2 * stat_section_bytes(p
 // about 256 workgroups, at most 8 times and at most once per tile of the
 // axis it splits; the fp32 partial sums are capped at 8 MiB (fewer copies,
 // or no split, beyond that).  After the partials come the arrival counters,
-// one 4-byte word per dK/dV and per dQ block.  Depends on the call only, so
-// the workspace size and the launch agree.
+// one 4-byte word per dK/dV and per dQ block of the finest grid the launch
+// may pick.  Depends on the call only, so the workspace size and the launch
+// agree.
 struct Split {
   int gkv = 1, gq = 1;
   int64_t rows_q = 0, rows_k = 0;
-  int64_t nkv = 0, nq = 0;  // blocks of 128 rows: counters
+  int64_t nkv = 0, nq = 0;  // counters: dK/dV and dQ blocks
   uint64_t part_bytes = 0;
   uint64_t bytes = 0;  // 0: no split
 };
@@ -321,8 +322,11 @@ Split split_of(const attn_bwd_params* p) {
   constexpr uint64_t kCap = 8u << 20;
   while (bytes() > kCap && (sp.gkv > 1 || sp.gq > 1)) (sp.gkv >= sp.gq ? sp.gkv : sp.gq) -= 1;
   if (bytes() > kCap || (sp.gkv == 1 && sp.gq == 1)) return Split{};
-  sp.nkv = nkv;
-  sp.nq = nq;
+  // Counters per block of the finest split grid: 64 rows in fp32 (two-wave
+  // workgroups), 128 in fp16 / bf16.
+  const int64_t crow = f->dtype == ATTN_FP32 ? 64 : 128;
+  sp.nkv = B * H * ((Sk + crow - 1) / crow);
+  sp.nq = B * H * ((Sq + crow - 1) / crow);
   sp.part_bytes = (bytes() + 255) / 256 * 256;
   sp.bytes = sp.part_bytes + ((uint64_t)(4 * (nkv + nq)) + 255) / 256 * 256;
   return sp;

@@ -1855,49 +1855,74 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int stages, const Ex& ex) {
   // copies of the dK/dV and dQ grids, both in one launch where the two
   // kinds' LDS fits one workgroup.  In fp32, whose products are slow enough
   // that the copies' partials are small next to their work, the last copy
-  // of each block sums them; in fp16 / bf16 a reduction grid does, spread
-  // over the whole GPU.
+  // of each block sums them, and workgroups of 64 rows (two waves) spread
+  // the copies over twice the CUs whenever that grid fits the device at one
+  // workgroup per CU; in fp16 / bf16 a reduction grid sums the partials,
+  // spread over the whole GPU.
   if (a.part) {
     if (a.split_kv < 1 || a.split_kv > 8 || a.split_q < 1 || a.split_q > 8) return hipErrorInvalidValue;
     constexpr bool kLastCopySums = !S::k16;
     BwdArgs sa = a;
     if (!kLastCopySums) sa.cnt_kv = sa.cnt_q = nullptr;
-    const long long nkv =
-        (stages & kStageDkDv) ? (a.p.Sk + NW_KV * 32 - 1) / (NW_KV * 32) * a.p.H * a.p.B * a.split_kv : 0;
-    const long long nq = (stages & kStageDq) ? (a.p.Sq + NW_Q * 32 - 1) / (NW_Q * 32) * a.p.H * a.p.B * a.split_q : 0;
-    if (nkv + nq > 0x7fffffffLL) return hipErrorInvalidValue;
-    bool one = false;
-    if constexpr (S::k16 ? D <= 128 : D <= 64) one = nkv > 0 && nq > 0;
-    if (one) {
-      if constexpr (S::k16 ? D <= 128 : D <= 64) {
-        if constexpr (S::k16)
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_split16_kernel<M, D, NW_KV, BMQ, NW_Q, BN, S::WPE_KV>),
-                   "attn_bwd_split16_kernel", (unsigned)(nkv + nq), (unsigned)(NW_KV * 64), sa, (int)nkv);
-        else
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_split_kernel<M, D, NW_KV, BMQ, NW_Q, BN>),
-                   "attn_bwd_split_kernel", (unsigned)(nkv + nq), (unsigned)(NW_KV * 64), sa, (int)nkv);
-        if (err != hipSuccess) return err;
+    auto grids = [&](int nw, long long& nkv, long long& nq) {
+      nkv = (stages & kStageDkDv) ? (a.p.Sk + nw * 32 - 1) / (nw * 32) * a.p.H * a.p.B * a.split_kv : 0;
+      nq = (stages & kStageDq) ? (a.p.Sq + nw * 32 - 1) / (nw * 32) * a.p.H * a.p.B * a.split_q : 0;
+    };
+    long long nkv, nq;
+    grids(NW_KV, nkv, nq);
+    bool two = false;
+    if constexpr (!S::k16) {
+      long long nkv2, nq2;
+      grids(2, nkv2, nq2);
+      const long long cus = device_cu_count();
+      two = cus > 0 && nkv2 + nq2 <= cus;
+      if (two) {
+        nkv = nkv2;
+        nq = nq2;
       }
-    } else {
+    }
+    if (nkv + nq > 0x7fffffffLL) return hipErrorInvalidValue;
+    // The copies with SNW waves per workgroup.
+    auto copies = [&](auto snw) -> hipError_t {
+      constexpr int SNW = decltype(snw)::value;
+      hipError_t e = hipSuccess;
+      bool one = false;
+      if constexpr (S::k16 ? D <= 128 : D <= 64) one = nkv > 0 && nq > 0;
+      if (one) {
+        if constexpr (S::k16 ? D <= 128 : D <= 64) {
+          if constexpr (S::k16)
+            return ex(reinterpret_cast<const void*>(&attn_bwd_split16_kernel<M, D, SNW, BMQ, SNW, BN, S::WPE_KV>),
+                      "attn_bwd_split16_kernel", (unsigned)(nkv + nq), (unsigned)(SNW * 64), sa, (int)nkv);
+          else
+            return ex(reinterpret_cast<const void*>(&attn_bwd_split_kernel<M, D, SNW, BMQ, SNW, BN>),
+                      "attn_bwd_split_kernel", (unsigned)(nkv + nq), (unsigned)(SNW * 64), sa, (int)nkv);
+        }
+      }
       if (nkv > 0) {
         if constexpr (S::k16)
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, NW_KV, BMQ, S::WPE_KV, false, true>),
-                   "attn_bwd_dkdv16_kernel", (unsigned)nkv, (unsigned)(NW_KV * 64), sa);
+          e = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv16_kernel<M, D, SNW, BMQ, S::WPE_KV, false, true>),
+                 "attn_bwd_dkdv16_kernel", (unsigned)nkv, (unsigned)(SNW * 64), sa);
         else
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, NW_KV, BMQ, false, true>),
-                   "attn_bwd_dkdv_kernel", (unsigned)nkv, (unsigned)(NW_KV * 64), sa);
-        if (err != hipSuccess) return err;
+          e = ex(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<M, D, SNW, BMQ, false, true>),
+                 "attn_bwd_dkdv_kernel", (unsigned)nkv, (unsigned)(SNW * 64), sa);
+        if (e != hipSuccess) return e;
       }
       if (nq > 0) {
         if constexpr (S::k16)
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, NW_Q, BN, S::WPE_Q, false, true>),
-                   "attn_bwd_dq16_kernel", (unsigned)nq, (unsigned)(NW_Q * 64), sa);
+          e = ex(reinterpret_cast<const void*>(&attn_bwd_dq16_kernel<M, D, SNW, BN, S::WPE_Q, false, true>),
+                 "attn_bwd_dq16_kernel", (unsigned)nq, (unsigned)(SNW * 64), sa);
         else
-          err = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, NW_Q, BN, false, true>),
-                   "attn_bwd_dq_kernel", (unsigned)nq, (unsigned)(NW_Q * 64), sa);
-        if (err != hipSuccess) return err;
+          e = ex(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<M, D, SNW, BN, false, true>),
+                 "attn_bwd_dq_kernel", (unsigned)nq, (unsigned)(SNW * 64), sa);
       }
-    }
+      return e;
+    };
+    static_assert(NW_KV == NW_Q, "split copies share one workgroup size");
+    if constexpr (!S::k16)
+      err = two ? copies(std::integral_constant<int, 2>{}) : copies(std::integral_constant<int, NW_KV>{});
+    else
+      err = copies(std::integral_constant<int, NW_KV>{});
+    if (err != hipSuccess) return err;
     const int sides = (nq > 0 ? 1 : 0) | (nkv > 0 ? 2 : 0);
     if (!kLastCopySums && sides) {
       constexpr int RPP = 256 / (D / 4);

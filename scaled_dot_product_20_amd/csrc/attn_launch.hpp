@@ -116,10 +116,11 @@ struct BwdArgs {
   // order.  Layout, in rows of head_dim floats: dK [split_kv][H][rows_k],
   // then dV likewise, then dQ [split_q][H][rows_q]; a row's index is its
   // storage row (stacked side) or b * seqlen + local row (padded side).
-  // Arrival counters, one per block of 128 rows: cnt_kv[(b H + h) nkb + kb]
-  // for the dK/dV blocks, cnt_q[(b H + h) nqb + qb] for the dQ blocks
-  // (cnt_q = cnt_kv + B H nkb); the preprocess zeroes all ncnt of them and
-  // the last arrival at a block resets its counter.
+  // Arrival counters, one per block of the split grid (128 or 64 rows):
+  // cnt_kv[(b H + h) nkb + kb] for the dK/dV blocks, cnt_q[(b H + h) nqb +
+  // qb] for the dQ blocks (cnt_q past room for the finest dK/dV grid); the
+  // preprocess zeroes all ncnt of them and the last arrival at a block
+  // resets its counter.  Null: a reduction kernel sums the partials.
   float* part;
   long long rows_q, rows_k;
   int split_kv, split_q;

@@ -327,7 +327,8 @@ def split_bytes(f):
     of the split axis (64 rows, 32 in fp32)); fp32 partials of dK, dV (per
     key copy) and dQ (per query copy), capped at 8 MiB by dropping copies
     from the larger count; then one 4-byte arrival counter per dK/dV and
-    per dQ workgroup of the unsplit grids; 0 when no copy is left to split."""
+    per dQ block of 64 rows (fp32) or 128 (fp16 / bf16); 0 when no copy is
+    left to split."""
     if f.flags & bd.FLAG_NO_SPLIT:
         return 0
     B, H, D, Sq, Sk = f.batch, f.heads, f.head_dim, f.seqlen_q, f.seqlen_k
@@ -349,7 +350,9 @@ def split_bytes(f):
             gq -= 1
     if nbytes() > 8 << 20 or (gkv == 1 and gq == 1):
         return 0
-    return -(-nbytes() // 256) * 256 + -(-4 * (nkv + nq) // 256) * 256
+    crow = 64 if f.dtype == bd.FP32 else 128
+    ncnt = B * H * (-(-Sk // crow) + -(-Sq // crow))
+    return -(-nbytes() // 256) * 256 + -(-4 * ncnt // 256) * 256
 
 
 def test_workspace_size():
