@@ -224,6 +224,46 @@ def mfma_probe(n: int, steps: int) -> None:
                       "frac_of_bf16_peak": round(tf / PEAK_MFMA_16, 4)}), flush=True)
 
 
+# Small problems the backward's split mode is for: (dtype, B, H, S, D), no
+# mask, scale 1/sqrt(D).
+SPLIT_SHAPES = [("fp32", 1, 2, 128, 64), ("fp32", 1, 4, 512, 64), ("fp16", 2, 3, 300, 80),
+                ("bf16", 1, 2, 512, 64), ("bf16", 1, 8, 512, 64), ("bf16", 1, 1, 256, 128),
+                ("bf16", 1, 2, 1000, 128), ("bf16", 1, 4, 1000, 128), ("bf16", 1, 1, 4000, 64)]
+
+
+def split_probe(steps: int) -> None:
+    """The backward (attn_bwd: preprocess, then dK/dV and dQ) of each small
+    shape with the library's choice and with the split mode off
+    (ATTN_FLAG_NO_SPLIT): microseconds per call over `steps` back-to-back
+    calls between two HIP events, behind a spin kernel that lets the host
+    enqueue them all first.  One JSON line per shape."""
+    import torch
+    from scaled_dot_product_20_amd import binding as bd
+    names = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+    sid = torch.cuda.current_stream().cuda_stream
+    for dn, B, H, S, D in SPLIT_SHAPES:
+        g = torch.Generator(device="cuda:0").manual_seed(S * D + H)
+        q, k, v, do = (torch.randn(B, H, S, D, device="cuda:0", dtype=names[dn], generator=g) for _ in range(4))
+        o, lse = bd.attn_fwd(q, k, v, scale=D ** -0.5)
+        res = {}
+        for split in (True, False):
+            p, keep = bd.prepare_bwd(do, q, k, v, o, lse, scale=D ** -0.5, split=split)
+            kernels = [n for n, _, _ in bd.plan("attn_bwd", p)]
+            for _ in range(5):
+                bd.launch("attn_bwd", p, sid)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(spin_cycles(0.1 * steps))
+            e0.record()
+            for _ in range(steps):
+                bd.launch("attn_bwd", p, sid)
+            e1.record()
+            torch.cuda.synchronize()
+            res["split" if split else "unsplit"] = {"us": round(e0.elapsed_time(e1) * 1e3 / steps, 1),
+                                                    "kernels": kernels}
+        print(json.dumps({"shape": f"{B}x{H}x{S}x{D}", "dtype": dn, **res}), flush=True)
+
+
 _SPIN = {}
 
 
@@ -377,6 +417,8 @@ def main():
     ap.add_argument("--mfma-probe", type=int, default=0, metavar="N",
                     help="instead of the attention step, run an N x N x N bf16 GEMM (the reference for "
                          "MFMA-busy counters) and exit")
+    ap.add_argument("--split-probe", action="store_true",
+                    help="time the backward of small shapes with and without its split mode (JSON lines)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -396,6 +438,9 @@ def main():
         return
     if args.mfma_probe:
         mfma_probe(args.mfma_probe, args.steps)
+        return
+    if args.split_probe:
+        split_probe(args.steps)
         return
     names = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
     wl_all = wls.workloads()
