@@ -306,7 +306,8 @@ hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
  * split backward, "triton_split" in the same notes) as attn_bwd_dkdv_dq
  * does, then, only when seqused_q / seqused_k are given, the small kernels
  * that zero the gradient rows past the used ones.  The dK/dV and dQ sums are
- * computed without atomics: results are run-to-run identical.
+ * computed without floating-point atomics: results are run-to-run
+ * identical.
  *
  * Split mode (small problems, unless ATTN_FLAG_NO_SPLIT): when the dK/dV or
  * the dQ grid (128 keys or queries per workgroup) would have fewer than 64

@@ -7,8 +7,9 @@
 // dS = P o (dP - Delta):
 //   dV = P^T dO,  dK = scale dS^T Q   (per key block, kernel 2)
 //   dQ = scale dS K                   (per query block, kernel 3)
-// No atomics: every output element is summed by one lane in a fixed order,
-// so results are run-to-run identical.
+// No floating-point atomics: every output element is summed by one lane in
+// a fixed order, so results are run-to-run identical (the split mode's only
+// atomics are integer arrival counts, which decide who sums, not the order).
 #include <type_traits>
 #include <utility>
 
