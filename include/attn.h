@@ -68,9 +68,11 @@ extern "C" {
  *   layout of the AOTriton 0.14b VarlenBits LSE field) instead of
  *   [heads, total_q]. */
 #define ATTN_FLAG_LSE_TH 1u
-/* ATTN_FLAG_NO_SPLIT (backward only, ignored by the forward): never use the
- *   split mode of attn_bwd_workspace_size / attn_bwd below, which small
- *   problems otherwise take; the workspace then holds only Delta and LSE. */
+/* ATTN_FLAG_NO_SPLIT: never use the split paths that small grids otherwise
+ *   take: the split mode of attn_bwd_workspace_size / attn_bwd below (the
+ *   workspace then holds only Delta and LSE), and the forward's key-split
+ *   workgroups (for a small grid, or for the last round of a grid of a few
+ *   rounds); the forward then runs its plain grid. */
 #define ATTN_FLAG_NO_SPLIT 2u
 
 /* Unbounded side of a window. */
@@ -294,9 +296,12 @@ typedef struct {
  * over the query blocks (for fp16 / bf16 inputs with a band unbounded or at
  * least 1024 keys wide, the 256-row ping-pong kernel, and when its grid's
  * last round on the device would be mostly idle, a second kernel that
- * splits that round's blocks over the key axis and merges the halves), then,
- * only when seqused_q is given, a small kernel that writes the rows past the
- * used ones as masked rows.  attn_fwd_plan lists the kernels of a call. */
+ * splits that round's blocks over the key axis and merges the halves; a
+ * grid of at most a quarter as many blocks as the device has CUs goes to
+ * that second kernel whole), then, only when seqused_q is given, a small
+ * kernel that writes the rows past the used ones as masked rows.
+ * ATTN_FLAG_NO_SPLIT keeps the ping-pong grid whole.  attn_fwd_plan lists
+ * the kernels of a call. */
 hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
 
 /* Backward: reads q, k, v, o, lse, dout; writes dq, dk, dv.  Enqueues, in

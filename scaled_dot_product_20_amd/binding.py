@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libsdpa20.so")
 WINDOW_INF = 2147483647
 PARAMS_VERSION = 3
 FLAG_LSE_TH = 1  # ATTN_FLAG_LSE_TH: packed LSE as [T, H]
-FLAG_NO_SPLIT = 2  # ATTN_FLAG_NO_SPLIT: the backward never takes its split mode
+FLAG_NO_SPLIT = 2  # ATTN_FLAG_NO_SPLIT: no split mode (backward), no key-split workgroups (forward)
 FP32, FP16, BF16 = 0, 1, 2
 BHSD, THD, VARLEN = 0, 1, 2
 # Mode byte of one side under VARLEN (ATTN_SEQ_* in include/attn.h).
@@ -207,7 +207,8 @@ def fwd_params(q, k, v, o, lse, *, scale, window, diag, cu_seqlens_q, cu_seqlens
     seqlen_k] with sequence-local query / key indices; size-1 axes
     broadcast; unit stride on the key axis), ``alibi_slopes`` (fp32 [H]),
     ``dropout_p`` with ``philox_seed`` / ``philox_offset``.  ``split=False``
-    keeps the backward out of its split mode (ATTN_FLAG_NO_SPLIT)."""
+    keeps the backward out of its split mode and the forward on its plain
+    grid (ATTN_FLAG_NO_SPLIT)."""
     p = FwdParams()
     p.version = PARAMS_VERSION
     if q.dtype not in _DTYPE:

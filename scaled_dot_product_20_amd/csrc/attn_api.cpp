@@ -580,6 +580,7 @@ sdpa::FwdArgs fwd_args(const attn_fwd_params* p) {
   a.lse = p->lse;
   a.f = feat_args(p);
   a.feat = feat_on(p);
+  a.no_split = (p->flags & ATTN_FLAG_NO_SPLIT) ? 1 : 0;
   return a;
 }
 

@@ -1079,14 +1079,24 @@ static hipError_t launch_fwd_t(const FwdArgs& a, const Ex& ex) {
       // CU once (1x32x6630x128: 0.717 ms against 0.743 ms).  With more
       // rounds, or a fuller last round, the tail's share is too small to pay
       // for the split kernel's one wave per SIMD (1x32x15300x128: 3.63
-      // against 3.46).
+      // against 3.46).  A grid of at most a quarter as many blocks as CUs
+      // goes to the split kernel whole: four workgroups per block, each over
+      // half the keys, still fit one round (1x2x512x64: 8.9 against 15.7
+      // us; 1x8x2048x128: 40.4 against 51.3 us), where a grid of half the
+      // CUs would take two (4x8x1024x128: 46.8 against 33.0 us).
       long long nmain = nblk;
-      const long long cus = device_cu_count() * pp_per_cu<D>();
-      if (cus > 0 && nblk >= cus && nblk < 4 * cus && 4 * (nblk % cus) <= cus)
-        nmain = nblk - nblk % cus;
+      const long long cu = device_cu_count(), cus = cu * pp_per_cu<D>();
+      if (!a.no_split) {
+        if (cus > 0 && nblk >= cus && nblk < 4 * cus && 4 * (nblk % cus) <= cus)
+          nmain = nblk - nblk % cus;
+        else if (cu > 0 && 4 * nblk <= cu)
+          nmain = 0;
+      }
       const int nqi = (int)nq;
-      hipError_t err = ex(reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, BN>), "attn_fwd16pp_kernel",
-                          (unsigned)nmain, 512u, a, nqi);
+      hipError_t err = hipSuccess;
+      if (nmain > 0)
+        err = ex(reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, BN>), "attn_fwd16pp_kernel",
+                 (unsigned)nmain, 512u, a, nqi);
       if (err != hipSuccess || nmain == nblk) return err;
       return ex(reinterpret_cast<const void*>(&attn_fwd16split_kernel<M, D>), "attn_fwd16split_kernel",
                 (unsigned)(4 * (nblk - nmain)), 256u, a, nqi, (int)nmain);

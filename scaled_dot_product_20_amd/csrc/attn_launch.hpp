@@ -97,8 +97,9 @@ struct FwdArgs {
   ProblemArgs p;
   Operand q, k, v, o;
   float* lse;
-  FeatArgs f;  // optional features (read by the FEAT kernels only)
-  int feat;    // any feature present: the FEAT kernels run
+  FeatArgs f;    // optional features (read by the FEAT kernels only)
+  int feat;      // any feature present: the FEAT kernels run
+  int no_split;  // the ping-pong grid alone, no key-split workgroups
 };
 
 struct BwdArgs {

@@ -121,6 +121,32 @@ def test_split_mode_plan_and_bits(dtype, D, B, H, S):
     Case(B=B, H=H, Sq=S, D=D, dtype=dtype, seed=15, split=False).check()
 
 
+@pytest.mark.parametrize("dtype,D,B,H,S,window", [(torch.bfloat16, 128, 1, 2, 700, (INF, INF)),
+                                                  (torch.float16, 64, 1, 3, 513, (INF, 0)),
+                                                  (torch.bfloat16, 96, 2, 1, 300, (2000, 3000))])
+def test_small_forward_split_grid(dtype, D, B, H, S, window):
+    """A forward grid of at most a quarter as many 256-row blocks as CUs runs
+    whole on the key-split kernel (ATTN_FLAG_NO_SPLIT keeps it on the
+    ping-pong grid): plans, run-to-run bits, and both paths against the
+    oracle."""
+    c = Case(B=B, H=H, Sq=S, D=D, dtype=dtype, window=window, seed=16)
+    q, k, v, _ = (t.cuda() for t in c.cpu)
+    kw = dict(scale=c.scale, window=window, diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None,
+              max_seqlen_q=None, max_seqlen_k=None)
+    o, lse = bd.attn_fwd(q, k, v, scale=c.scale, window=window)
+    plans = {}
+    for split in (True, False):
+        p = bd.fwd_params(q, k, v, o, lse, split=split, **kw)
+        plans[split] = [n for n, _, _ in bd.plan("attn_fwd", p)]
+    assert plans[True] == ["attn_fwd16split_kernel"], plans
+    assert plans[False] == ["attn_fwd16pp_kernel"], plans
+    o2, lse2 = bd.attn_fwd(q, k, v, scale=c.scale, window=window)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    c.check(bwd=False)
+    Case(B=B, H=H, Sq=S, D=D, dtype=dtype, window=window, seed=16, split=False).check(bwd=False)
+
+
 @pytest.mark.parametrize("D", [80, 128])
 @pytest.mark.parametrize("window,diag", [((5, 0), "bottom_right"), ((INF, 0), "top_left"),
                                          ((INF, INF), "top_left"), ((1 << 30, 0), "bottom_right"),
