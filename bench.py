@@ -55,6 +55,7 @@ METRIC = "attn fwd/bwd TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, hdim 128"
 PEAK_MFMA_16 = 2516.6   # TFLOP/s, bf16 and fp16 dense
 PEAK_MFMA_32 = 157.3    # TFLOP/s, fp32
 PEAK_HBM = 8000.0       # GB/s
+WINDOW_INF = 2147483647  # unbounded window side
 DEFAULT_WORKLOAD = "long_6630"
 # The timed cells besides the headline: every workload of the pages' shapes
 # (tiny fp32, BERT-like in fp16 and bf16, gpt2-like causal, both long
@@ -228,39 +229,48 @@ def mfma_probe(n: int, steps: int) -> None:
 # mask, scale 1/sqrt(D).
 SPLIT_SHAPES = [("fp32", 1, 2, 128, 64), ("fp32", 1, 4, 512, 64), ("fp16", 2, 3, 300, 80),
                 ("bf16", 1, 2, 512, 64), ("bf16", 1, 8, 512, 64), ("bf16", 1, 1, 256, 128),
-                ("bf16", 1, 2, 1000, 128), ("bf16", 1, 4, 1000, 128), ("bf16", 1, 1, 4000, 64)]
+                ("bf16", 1, 2, 1000, 128), ("bf16", 1, 4, 1000, 128), ("bf16", 1, 1, 4000, 64),
+                ("bf16", 1, 8, 2048, 128), ("bf16", 4, 8, 1024, 128)]
 
 
 def split_probe(steps: int) -> None:
-    """The backward (attn_bwd: preprocess, then dK/dV and dQ) of each small
-    shape with the library's choice and with the split mode off
-    (ATTN_FLAG_NO_SPLIT): microseconds per call over `steps` back-to-back
-    calls between two HIP events, behind a spin kernel that lets the host
-    enqueue them all first.  One JSON line per shape."""
+    """The forward (attn_fwd) and the backward (attn_bwd: preprocess, then
+    dK/dV and dQ) of each small shape with the library's choice and with
+    its split paths off (ATTN_FLAG_NO_SPLIT): microseconds per call over
+    `steps` back-to-back calls between two HIP events, behind a spin kernel
+    that lets the host enqueue them all first.  One JSON line per shape."""
     import torch
     from scaled_dot_product_20_amd import binding as bd
     names = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
     sid = torch.cuda.current_stream().cuda_stream
+
+    def per_call(entry, p):
+        for _ in range(5):
+            bd.launch(entry, p, sid)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(spin_cycles(0.1 * steps))
+        e0.record()
+        for _ in range(steps):
+            bd.launch(entry, p, sid)
+        e1.record()
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) * 1e3 / steps, 1)
+
+    fkw = dict(window=(WINDOW_INF, WINDOW_INF), diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None,
+               max_seqlen_q=None, max_seqlen_k=None)
     for dn, B, H, S, D in SPLIT_SHAPES:
         g = torch.Generator(device="cuda:0").manual_seed(S * D + H)
         q, k, v, do = (torch.randn(B, H, S, D, device="cuda:0", dtype=names[dn], generator=g) for _ in range(4))
         o, lse = bd.attn_fwd(q, k, v, scale=D ** -0.5)
         res = {}
         for split in (True, False):
-            p, keep = bd.prepare_bwd(do, q, k, v, o, lse, scale=D ** -0.5, split=split)
-            kernels = [n for n, _, _ in bd.plan("attn_bwd", p)]
-            for _ in range(5):
-                bd.launch("attn_bwd", p, sid)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda._sleep(spin_cycles(0.1 * steps))
-            e0.record()
-            for _ in range(steps):
-                bd.launch("attn_bwd", p, sid)
-            e1.record()
-            torch.cuda.synchronize()
-            res["split" if split else "unsplit"] = {"us": round(e0.elapsed_time(e1) * 1e3 / steps, 1),
-                                                    "kernels": kernels}
+            key = "split" if split else "unsplit"
+            fp = bd.fwd_params(q, k, v, torch.empty_like(o), torch.empty_like(lse), scale=D ** -0.5, split=split,
+                               **fkw)
+            bp, keep = bd.prepare_bwd(do, q, k, v, o, lse, scale=D ** -0.5, split=split)
+            res[key] = {"fwd_us": per_call("attn_fwd", fp), "fwd_kernels": [n for n, _, _ in bd.plan("attn_fwd", fp)],
+                        "bwd_us": per_call("attn_bwd", bp), "bwd_kernels": [n for n, _, _ in bd.plan("attn_bwd", bp)]}
         print(json.dumps({"shape": f"{B}x{H}x{S}x{D}", "dtype": dn, **res}), flush=True)
 
 
