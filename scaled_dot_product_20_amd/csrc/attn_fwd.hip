@@ -250,6 +250,212 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// fp32 forward of small grids: one workgroup = 64 query rows (two 32-row
+// groups) x two key halves.  Waves 0-1 take the rows over the first half of
+// the block's key tiles, waves 2-3 over the second half, each half staging
+// its own tiles (both halves step together, one barrier per step); at the
+// end the second half's (O^T, m, l) pass through LDS and the first half's
+// waves merge them: m = max(m0, m1), O = 2^(m0-m) O0 + 2^(m1-m) O1, l
+// likewise.  Each wave's chain of fp32 products covers half the keys.
+template <typename M, int D, int BN>
+__global__ __launch_bounds__(256) void attn_fwd_ks_kernel(FwdArgs a) {
+  using T = typename M::elem;
+  constexpr int HT = 128, BM = 64, KPL = M::KPL;  // threads per key half, rows per workgroup
+  constexpr int DVT = (D + 31) / 32, DPAD = DVT * 32;
+  constexpr int PAD = 16 / (int)sizeof(T);
+  constexpr int KLD = D + PAD, VLD = BN + PAD;
+  constexpr int KT = BN / 32;
+  constexpr int NS = D / (2 * KPL);
+  constexpr int STAGE = BN * KLD + DPAD * VLD;
+  static_assert(2 * (DVT * 16 * 64 + 128) <= 2 * STAGE, "merge area fits the first half's stages");
+  __shared__ __attribute__((aligned(16))) T smem[4 * STAGE];  // [key half][stage]
+
+  const ProblemArgs& P = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+  const int rg = wave & 1, kh = wave >> 1, htid = tid & (HT - 1);
+  const int nq = (int)(gridDim.x / (P.B * P.H));
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.ragged);
+  const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
+  const int qb = nq - 1 - gp.i;
+
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
+  const int i0 = qb * BM;
+  if (i0 >= sq) return;
+  const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
+
+  const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
+  const T* kp = (const T*)a.k.ptr + b * a.k.sb + h * a.k.sh + k0 * a.k.ss;
+  const T* vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
+  T* op = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + q0 * a.o.ss;
+  float* lp = a.lse + b * P.olse_sb + h * P.olse_sh + q0 * P.olse_ss;
+
+  const int ilast = min(i0 + BM, sq) - 1;
+  const long long jlo = max(0LL, (long long)i0 + w.lo);
+  const long long jhi = min((long long)sk - 1, (long long)ilast + w.hi);
+  const bool block_empty = w.lo > w.hi || jlo > jhi;
+
+  const int iw0 = i0 + 32 * rg;
+  const bool wave_live = iw0 < sq;
+  const int qi = iw0 + r;
+
+  RowFrags<M, D> qf;
+  qf.load(qp + (long long)qi * a.q.ss, wave_live && qi < sq, g);
+  const float c = fabsf(P.scale_log2);
+  if (P.scale_log2 < 0.f) qf.negate();
+
+  T* const hs = smem + kh * 2 * STAGE;  // this half's two stages
+  if constexpr (DPAD != D) {  // padding rows of the transposed V tiles
+    for (int x = htid; x < (DPAD - D) * VLD; x += HT) {
+      hs[BN * KLD + D * VLD + x] = (T)0.f;
+      hs[STAGE + BN * KLD + D * VLD + x] = (T)0.f;
+    }
+  }
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[DVT];
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) acc[dt] = zero16();
+
+  if (!block_empty) {
+    const int t0 = (int)(jlo / BN), n = (int)(jhi / BN) - t0 + 1, n0 = (n + 1) / 2;
+    const int tb = kh ? t0 + n0 : t0, cnt = kh ? n - n0 : n0;  // this half's tiles
+    TileStage<T, BN, D, HT> ks, vs;
+    if (cnt > 0) {
+      const int j0 = tb * BN;
+      ks.load(kp + (long long)j0 * a.k.ss, a.k.ss, sk - j0, htid);
+      vs.load(vp + (long long)j0 * a.v.ss, a.v.ss, sk - j0, htid);
+      ks.store_rows(hs, KLD, htid);
+      vs.store_transposed(hs + BN * KLD, VLD, htid);
+    }
+    __syncthreads();
+    for (int st = 0; st < n0; ++st) {  // both halves step together
+      const int buf = st & 1, t = tb + st, j0 = t * BN;
+      if (st + 1 < cnt) {
+        const int jn = j0 + BN;
+        ks.load(kp + (long long)jn * a.k.ss, a.k.ss, sk - jn, htid);
+        vs.load(vp + (long long)jn * a.v.ss, a.v.ss, sk - jn, htid);
+      }
+      const T* Ks = hs + buf * STAGE;
+      const T* Vt = Ks + BN * KLD;
+      const int cls = (wave_live && st < cnt) ? classify(w, iw0, 32, j0, BN, sk) : kEmpty;
+      if (cls != kEmpty) {
+        // S^T = K Q^T, 32 keys per sub-tile.
+        f32x16 s[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          s[kt] = zero16();
+#pragma unroll
+          for (int ss = 0; ss < NS; ++ss) {
+            const auto A = load_frag<M>(Ks + (32 * kt + r) * KLD + 2 * KPL * ss + KPL * g);
+            s[kt] = M::mma(A, qf.f[ss], s[kt]);
+          }
+        }
+        const bool partial = cls == kPartial;
+        if (partial) {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int j = j0 + 32 * kt + acc_row(e, g);
+              const int diff = j - qi;
+              if (!(diff >= w.lo && diff <= w.hi && j < sk)) s[kt][e] = -INFINITY;
+            }
+        }
+        float smax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) smax = fmaxf(smax, s[kt][e]);
+        smax = halves_max(smax);
+        const float mx = smax == -INFINITY ? -INFINITY : smax * c;
+        const bool raise = mx > m + kRescaleSlack;  // also when m is still -inf
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+          const float alpha = raise ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+          if (raise) m = mx;
+          l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+        }
+        const float nm = m == -INFINITY ? 0.f : -m;
+        float x[KT][16];
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, nm));
+            if (partial && s[kt][e] == -INFINITY) pe = 0.f;
+            ls += pe;
+            x[kt][e] = pe;
+          }
+        l += ls;
+        // O^T += V^T P^T
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int ss = 0; ss < 16 / KPL; ++ss) {
+            typename M::frag pf;
+            M::pack(&x[kt][KPL * ss], pf);
+            const int pos = 32 * kt + perm_pos(KPL * ss, g);
+#pragma unroll
+            for (int dt = 0; dt < DVT; ++dt) {
+              const auto A = load_frag<M>(Vt + (32 * dt + r) * VLD + pos);
+              acc[dt] = M::mma(A, pf, acc[dt]);
+            }
+          }
+      }
+      if (st + 1 < cnt) {
+        T* nb = hs + (buf ^ 1) * STAGE;
+        ks.store_rows(nb, KLD, htid);
+        vs.store_transposed(nb + BN * KLD, VLD, htid);
+      }
+      __syncthreads();
+    }
+  }
+
+  // Merge: the second half's waves leave O^T, m, l in the first half's
+  // stages (free after the last barrier); the first half's waves combine.
+  float* part = reinterpret_cast<float*>(smem) + rg * (DVT * 16 * 64 + 128);
+  float* stat = part + DVT * 16 * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(part + ((dt * 4 + q4) * 64 + lane) * 4) =
+            make_float4(acc[dt][4 * q4], acc[dt][4 * q4 + 1], acc[dt][4 * q4 + 2], acc[dt][4 * q4 + 3]);
+    stat[lane] = m;
+    stat[64 + lane] = l;
+  }
+  __syncthreads();
+  if (kh == 1 || !wave_live) return;
+  const float m1 = stat[lane], l1 = stat[64 + lane];
+  const float mm = fmaxf(m, m1);
+  const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+  const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+  const float lt = halves_sum(l * a0 + l1 * a1);
+  if (qi < sq) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    T* orow = op + (long long)qi * a.o.ss;
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * dt + 8 * q4 + 4 * g;
+        const float4 o1 = *reinterpret_cast<const float4*>(part + ((dt * 4 + q4) * 64 + lane) * 4);
+        if (d < D)
+          store4<T>(orow + d, (acc[dt][4 * q4] * a0 + o1.x * a1) * inv, (acc[dt][4 * q4 + 1] * a0 + o1.y * a1) * inv,
+                    (acc[dt][4 * q4 + 2] * a0 + o1.z * a1) * inv, (acc[dt][4 * q4 + 3] * a0 + o1.w * a1) * inv);
+      }
+    if (g == 0) lp[qi * P.olse_ss] = lt > 0.f ? (mm + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+  }
+}
+
 // ------------------------------------------------------ 16-bit kernel
 //
 // The bf16 / fp16 forward.  K and V tiles are copied HBM -> LDS with direct
@@ -1104,6 +1310,14 @@ static hipError_t launch_fwd_t(const FwdArgs& a, const Ex& ex) {
     return ex(reinterpret_cast<const void*>(&attn_fwd16_kernel<M, D, S::NW, BN, S::RB, S::WPE>),
               "attn_fwd16_kernel", (unsigned)nblk, (unsigned)(nw * 64), a);
   } else {
+    // Small grids at head_dim <= 64 (where two halves' stages fit LDS): 64-
+    // row workgroups over two key halves, when at most half as many as CUs.
+    if constexpr (D <= 64) {
+      const long long nks = (a.p.Sq + 63) / 64 * a.p.H * a.p.B, cu = device_cu_count();
+      if (!a.no_split && cu > 0 && 2 * nks <= cu)
+        return ex(reinterpret_cast<const void*>(&attn_fwd_ks_kernel<M, D, BN>), "attn_fwd_ks_kernel",
+                  (unsigned)nks, 256u, a);
+    }
     return ex(reinterpret_cast<const void*>(&attn_fwd_kernel<M, D, S::NW, BN>), "attn_fwd_kernel", (unsigned)nblk,
               (unsigned)(nw * 64), a);
   }

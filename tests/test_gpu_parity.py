@@ -123,12 +123,17 @@ def test_split_mode_plan_and_bits(dtype, D, B, H, S):
 
 @pytest.mark.parametrize("dtype,D,B,H,S,window", [(torch.bfloat16, 128, 1, 2, 700, (INF, INF)),
                                                   (torch.float16, 64, 1, 3, 513, (INF, 0)),
-                                                  (torch.bfloat16, 96, 2, 1, 300, (2000, 3000))])
+                                                  (torch.bfloat16, 96, 2, 1, 300, (2000, 3000)),
+                                                  (torch.float32, 64, 1, 2, 128, (INF, INF)),
+                                                  (torch.float32, 48, 2, 1, 300, (INF, 0)),
+                                                  (torch.float32, 32, 1, 2, 77, (5, 9))])
 def test_small_forward_split_grid(dtype, D, B, H, S, window):
-    """A forward grid of at most a quarter as many 256-row blocks as CUs runs
-    whole on the key-split kernel (ATTN_FLAG_NO_SPLIT keeps it on the
-    ping-pong grid): plans, run-to-run bits, and both paths against the
-    oracle."""
+    """A small forward grid runs on key-split workgroups (fp16 / bf16: the
+    whole ping-pong grid on the split kernel when it has at most a quarter
+    as many 256-row blocks as CUs; fp32 at head_dim <= 64: 64-row workgroups
+    over two key halves when at most half as many as CUs), and
+    ATTN_FLAG_NO_SPLIT keeps the plain grid: plans, run-to-run bits, and
+    both paths against the oracle."""
     c = Case(B=B, H=H, Sq=S, D=D, dtype=dtype, window=window, seed=16)
     q, k, v, _ = (t.cuda() for t in c.cpu)
     kw = dict(scale=c.scale, window=window, diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None,
@@ -138,8 +143,10 @@ def test_small_forward_split_grid(dtype, D, B, H, S, window):
     for split in (True, False):
         p = bd.fwd_params(q, k, v, o, lse, split=split, **kw)
         plans[split] = [n for n, _, _ in bd.plan("attn_fwd", p)]
-    assert plans[True] == ["attn_fwd16split_kernel"], plans
-    assert plans[False] == ["attn_fwd16pp_kernel"], plans
+    if dtype == torch.float32:
+        assert plans[True] == ["attn_fwd_ks_kernel"] and plans[False] == ["attn_fwd_kernel"], plans
+    else:
+        assert plans[True] == ["attn_fwd16split_kernel"] and plans[False] == ["attn_fwd16pp_kernel"], plans
     o2, lse2 = bd.attn_fwd(q, k, v, scale=c.scale, window=window)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
