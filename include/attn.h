@@ -298,10 +298,11 @@ typedef struct {
  * last round on the device would be mostly idle, a second kernel that
  * splits that round's blocks over the key axis and merges the halves; a
  * grid of at most a quarter as many blocks as the device has CUs goes to
- * that second kernel whole), then, only when seqused_q is given, a small
- * kernel that writes the rows past the used ones as masked rows.
- * ATTN_FLAG_NO_SPLIT keeps the ping-pong grid whole.  attn_fwd_plan lists
- * the kernels of a call. */
+ * that second kernel whole; in fp32 at head_dim <= 64, a grid of at most
+ * half as many 64-row blocks as CUs runs on workgroups that split the keys
+ * in two halves), then, only when seqused_q is given, a small kernel that
+ * writes the rows past the used ones as masked rows.  ATTN_FLAG_NO_SPLIT
+ * keeps the plain grids.  attn_fwd_plan lists the kernels of a call. */
 hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
 
 /* Backward: reads q, k, v, o, lse, dout; writes dq, dk, dv.  Enqueues, in
