@@ -17,7 +17,7 @@ from scaled_dot_product_20_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
 
 
 def draw_case(n: int) -> Case:
