@@ -64,7 +64,7 @@ CELLS = [("tiny_f32", "fp32"), ("bert_like", "fp16"), ("bert_like", "bf16"), ("g
          ("long_6630", "bf16"), ("long_15300", "bf16"), ("varlen_window_d80", "bf16"),
          ("varlen_window_d128", "bf16"), ("long_4096_bwd", "bf16")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dkdv_traffic_long_6630.txt")
-KERNEL_SOURCES = ["scaled_dot_product_20_amd/csrc/attn_bwd.hip",
+KERNEL_SOURCES = ["scaled_dot_product_20_amd/csrc/attn_bwd_kernels.hpp",
                   "scaled_dot_product_20_amd/csrc/attn_device.hpp",
                   "scaled_dot_product_20_amd/csrc/attn_launch.hpp"]
 ENTRY = {"fwd": "attn_fwd", "bwd_preprocess": "attn_bwd_preprocess", "bwd_dkdv_dq": "attn_bwd_dkdv_dq"}

@@ -20,8 +20,9 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsdpa20.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_api.cpp"]
-HEADERS = ["attn_device.hpp", "attn_launch.hpp", "attn_feat.hpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_f32.hip", "attn_bwd_f16.hip", "attn_bwd_bf16.hip",
+           "attn_api.cpp"]
+HEADERS = ["attn_device.hpp", "attn_launch.hpp", "attn_feat.hpp", "attn_bwd_kernels.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [

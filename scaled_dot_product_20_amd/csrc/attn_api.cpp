@@ -279,7 +279,7 @@ Extent lse_extent(const attn_fwd_params* p) {
 uint64_t stat_section_bytes(const attn_fwd_params* p) { return ((uint64_t)lse_count(p) * 4 + 255) / 256 * 256; }
 uint64_t delta_bytes(const attn_fwd_params* p) { return 2 * stat_section_bytes(p); }
 
-// Split mode of the backward (the launch rules in attn_bwd.hip): taken for
+// Split mode of the backward (the launch rules in attn_bwd_kernels.hpp): taken for
 // calls without optional features whose dK/dV or dQ grid (128 keys or
 // queries per workgroup) has fewer than 64 workgroups, i.e. would leave at
 // least three quarters of a 256-CU GPU idle (at fp16 / bf16 head dims 96

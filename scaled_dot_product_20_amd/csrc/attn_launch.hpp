@@ -204,6 +204,13 @@ hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, const Enqueue& 
 hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs& a, const Record& ex);
 hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, const Enqueue& ex);
 hipError_t launch_bwd(int dtype, int head_dim, const BwdArgs& a, int stages, const Record& ex);
+// One dtype's backward kernels (built in attn_bwd_<dtype>.hip).
+hipError_t launch_bwd_f32(int head_dim, const BwdArgs& a, int stages, const Enqueue& ex);
+hipError_t launch_bwd_f32(int head_dim, const BwdArgs& a, int stages, const Record& ex);
+hipError_t launch_bwd_f16(int head_dim, const BwdArgs& a, int stages, const Enqueue& ex);
+hipError_t launch_bwd_f16(int head_dim, const BwdArgs& a, int stages, const Record& ex);
+hipError_t launch_bwd_bf16(int head_dim, const BwdArgs& a, int stages, const Enqueue& ex);
+hipError_t launch_bwd_bf16(int head_dim, const BwdArgs& a, int stages, const Record& ex);
 // Rows of each sequence's room past its length (side 0: Q, side 1: K): zeros
 // in t0 and t1 (null pointers skipped) and, when lse is given, LSE = +inf.
 // Rows are row_bytes long (a multiple of 16).  Launches nothing for a side
