@@ -1299,9 +1299,14 @@ static hipError_t launch_fwd_t(const FwdArgs& a, const Ex& ex) {
           nmain = 0;
       }
       const int nqi = (int)nq;
+      // Key tiles of 32 at head_dim <= 64: four waves per SIMD leave 128
+      // registers, which the 64-key tile's scores overran (spilled to
+      // scratch in the loop); the halved tile fits (BERT-like 192x16x512x64
+      // bf16: 380 against 404 us).
+      constexpr int PBN = D <= 64 ? 32 : BN;
       hipError_t err = hipSuccess;
       if (nmain > 0)
-        err = ex(reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, BN>), "attn_fwd16pp_kernel",
+        err = ex(reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, PBN>), "attn_fwd16pp_kernel",
                  (unsigned)nmain, 512u, a, nqi);
       if (err != hipSuccess || nmain == nblk) return err;
       return ex(reinterpret_cast<const void*>(&attn_fwd16split_kernel<M, D>), "attn_fwd16split_kernel",
