@@ -1819,14 +1819,19 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, int sid
 // ------------------------------------------------------------ launch
 
 // Workgroup shapes.  16-bit: dK/dV 4 waves (128 keys) over 64-row query
-// tiles at two waves per SIMD for head_dim <= 80, producer / consumer pairs
+// tiles (32 at head_dim 80) at two waves per SIMD for head_dim <= 80,
+// producer / consumer pairs
 // (8 waves, 128 keys) at head_dim 128; dQ 4 waves (128 queries) over 64-key
 // tiles, two per SIMD.  fp32 (register-staged kernels): 4 waves each, tiles
 // of 32 to fit LDS.
 template <typename M, int D>
 struct BwdShape {
   static constexpr bool k16 = sizeof(typename M::elem) == 2;
-  static constexpr int NW_KV = 4, BMQ = k16 ? 64 : 32;
+  // Query tiles of 32 rows at head_dim 80: the 64-row tile's slices spilled
+  // registers at two waves per SIMD (1x32x4096x80 bf16 backward 777 ->
+  // 753 us; the (256, 0) window at 2048 rows 216 -> 198 us).  At 64 the
+  // 64-row tile stays faster (BERT-like 1119 against 1153 us).
+  static constexpr int NW_KV = 4, BMQ = k16 ? (D == 80 ? 32 : 64) : 32;
   // dQ key tiles: 32 keys above head_dim 128 (K and V tiles of 64 keys would
   // not fit a stage).
   static constexpr int NW_Q = 4, BN = k16 ? (D > 128 ? 32 : 64) : 32;
