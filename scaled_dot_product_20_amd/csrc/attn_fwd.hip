@@ -1242,13 +1242,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // Workgroup shapes.  fp32 (register-staged kernel, tiles twice as large):
 // 4 waves, 64-key tiles.  16-bit, 64-key tiles, one 32-row block per wave,
 // two waves per SIMD: the ping-pong kernel (8 waves) for wide bands; for
-// narrower ones 8 waves at head_dim <= 80, 4 at head_dim 128.
+// narrower ones 4 waves (128-row blocks: under a band the finer blocks
+// visit fewer keys; 8x16x2048x64 bf16 with a (256, 0) window 53.8 against
+// 66.3 us at 8 waves, 8x16x2048x80 63.2 against 75.6 us).
 template <typename M, int D>
 struct FwdShape {
   static constexpr bool k16 = sizeof(typename M::elem) == 2;
   static constexpr bool PP = k16 && D <= 128;  // ping-pong kernel built (8 waves, 256 rows)
   static constexpr int RB = 1;
-  static constexpr int NW = k16 ? (D > 80 ? 4 : 8) : 4;
+  static constexpr int NW = 4;
   static constexpr int BN = 64;
   static constexpr int WPE = D > 128 ? 1 : 2;  // waves per SIMD the registers allow
 };
