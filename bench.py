@@ -266,8 +266,8 @@ def split_probe(steps: int) -> None:
         res = {}
         for split in (True, False):
             key = "split" if split else "unsplit"
-            fp = bd.fwd_params(q, k, v, torch.empty_like(o), torch.empty_like(lse), scale=D ** -0.5, split=split,
-                               **fkw)
+            fp, fws = bd.prepare_fwd(q, k, v, torch.empty_like(o), torch.empty_like(lse), scale=D ** -0.5,
+                                     split=split, **fkw)
             bp, keep = bd.prepare_bwd(do, q, k, v, o, lse, scale=D ** -0.5, split=split)
             res[key] = {"fwd_us": per_call("attn_fwd", fp), "fwd_kernels": [n for n, _, _ in bd.plan("attn_fwd", fp)],
                         "bwd_us": per_call("attn_bwd", bp), "bwd_kernels": [n for n, _, _ in bd.plan("attn_bwd", bp)]}
@@ -321,9 +321,10 @@ class Run:
         o, lse = bd.attn_fwd(q, k, v, **kw)
         fkw = dict(cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None)
         fkw.update(kw)
-        self.params = {"fwd": bd.fwd_params(q, k, v, o, lse, **fkw)}
+        fp, fws = bd.prepare_fwd(q, k, v, o, lse, **fkw)
+        self.params = {"fwd": fp}
         self.calls = ["fwd"]
-        self.keep = (q, k, v, do, o, lse, kw)
+        self.keep = (q, k, v, do, o, lse, kw, fws)
         if "bwd" in passes:
             bp, self.bkeep = bd.prepare_bwd(do, q, k, v, o, lse, **kw)
             self.params["bwd_preprocess"] = self.params["bwd_dkdv_dq"] = bp

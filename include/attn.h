@@ -242,11 +242,13 @@ typedef struct {
                               head_dim makes the call a repacked one. */
   uint64_t philox_seed;
   uint64_t philox_offset;
-  void *workspace;          /* forward of a repacked call: device,
-                              caller-owned, 256-byte aligned, >=
-                              attn_fwd_workspace_size(this) bytes; ignored
-                              otherwise, and by the backward calls (which
-                              take attn_bwd_params.workspace) */
+  void *workspace;          /* forward: device, caller-owned, 256-byte
+                              aligned; needed by a repacked call, used by
+                              the key-split tail when it holds
+                              attn_fwd_workspace_size(this) bytes, NULL
+                              allowed otherwise; ignored by the backward
+                              calls (which take attn_bwd_params.workspace).
+                              Calls that overlap on one workspace race. */
   uint64_t workspace_bytes;
 } attn_fwd_params;
 
@@ -265,10 +267,23 @@ typedef struct {
  * operand; the results equal those of the same problem zero-padded to Dp
  * by the caller. */
 
-/* Forward workspace bytes of a call: 0 when it runs in place; for a
- * repacked call, padded copies of q, k, v and o (rows of Dp elements; a
- * stacked side's rows are total_q / total_k, a padded side's batch *
- * seqlen), each rounded up to 256 bytes; 0 when the problem is malformed. */
+/* Forward workspace bytes a call can use; 0 when the problem is malformed.
+ * Two parts, in this order:
+ *  - needed (attn_fwd and attn_fwd_check reject a smaller workspace): for a
+ *    repacked call, padded copies of q, k, v and o (rows of Dp elements; a
+ *    stacked side's rows are total_q / total_k, a padded side's batch *
+ *    seqlen), each rounded up to 256 bytes; nothing for an in-place call;
+ *  - optional: the key-split tail's partial sums, for the in-place call it
+ *    runs (at Dp when repacked) when that call is fp16 / bf16 at head_dim
+ *    <= 128, has no optional feature and no ATTN_FLAG_NO_SPLIT, and its
+ *    band is unbounded on a side or at least 1024 keys wide and spans at
+ *    least 2048 keys (seqlen_k, or the band width + 255 if smaller):
+ *    256 * (2 if head_dim <= 64 else 1) slots of 8 * 64 * (4 * ceil(
+ *    head_dim / 32) + 1) float4 (about 35 MiB at head_dim 128).
+ * A workspace that holds both parts (and is 256-byte aligned) lets the
+ * forward split the key axis of its grid's last, partly filled round over
+ * more workgroups; without the second part it runs without that split.
+ * The result differs between the two only by rounding. */
 uint64_t attn_fwd_workspace_size(const attn_fwd_params *p);
 
 typedef struct {
@@ -294,15 +309,22 @@ typedef struct {
 
 /* Forward: writes o and lse.  Enqueues on `stream` one forward kernel
  * over the query blocks (for fp16 / bf16 inputs with a band unbounded or at
- * least 1024 keys wide, the 256-row ping-pong kernel, and when its grid's
- * last round on the device would be mostly idle, a second kernel that
- * splits that round's blocks over the key axis and merges the halves; a
- * grid of at most a quarter as many blocks as the device has CUs goes to
- * that second kernel whole; in fp32 at head_dim <= 64, a grid of at most
- * half as many 64-row blocks as CUs runs on workgroups that split the keys
- * in two halves), then, only when seqused_q is given, a small kernel that
- * writes the rows past the used ones as masked rows.  ATTN_FLAG_NO_SPLIT
- * keeps the plain grids.  attn_fwd_plan lists the kernels of a call. */
+ * least 1024 keys wide, the 256-row ping-pong kernel; in fp32 at head_dim
+ * <= 64, a grid of at most half as many 64-row blocks as CUs runs on
+ * workgroups that split the keys in two halves), then, only when seqused_q
+ * is given, a small kernel that writes the rows past the used ones as
+ * masked rows.  The ping-pong grid's last round, when partly filled:
+ *  - with the key-split part of the workspace (attn_fwd_workspace_size),
+ *    r blocks each run as np = min(8, round / r, band keys / 1024) >= 2
+ *    ping-pong workgroups over near-equal runs of the block's key tiles,
+ *    which store fp32 partials to the workspace, and a merge kernel
+ *    combines each block's partials in a fixed order and writes its rows;
+ *  - otherwise, with at most three full rounds and a last round at most a
+ *    quarter full, a kernel that splits that round's blocks over four
+ *    64-row workgroups, each over two key halves merged in LDS.
+ * A grid of at most a quarter as many blocks as the device has CUs goes to
+ * that last kernel whole.  ATTN_FLAG_NO_SPLIT keeps the plain grids.
+ * attn_fwd_plan lists the kernels of a call. */
 hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
 
 /* Backward: reads q, k, v, o, lse, dout; writes dq, dk, dv.  Enqueues, in

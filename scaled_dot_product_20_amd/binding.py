@@ -365,16 +365,27 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: Optional
         o = out
     if lse is None:
         lse = torch.empty(lse_shape(q, pk["lse_layout"], pk["q_mode"]), dtype=torch.float32, device=dev)
-    p = fwd_params(q, k, v, o, lse, **pk)
-    need = int(lib().attn_fwd_workspace_size(ctypes.byref(p)))
-    ws = None
-    if need:  # a repacked call: zero-padded copies of its operands
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        p.workspace, p.workspace_bytes = ws.data_ptr(), need
+    p, _ws = prepare_fwd(q, k, v, o, lse, **pk)
     rc = lib().attn_fwd(ctypes.byref(p), ctypes.c_void_p(_stream(dev)))
     if rc:
         raise AttnError("attn_fwd", rc)
     return o, lse
+
+
+def prepare_fwd(q, k, v, o, lse, *, workspace=None, **kw):
+    """Params of a forward (keywords as fwd_params) with its workspace:
+    attn_fwd_workspace_size bytes (the zero-padded copies of a repacked
+    call, and the key-split tail's partial sums for large fp16 / bf16
+    forwards), allocated when ``workspace`` is None.  Returns (params,
+    workspace or None); the tensor must outlive the launches."""
+    p = fwd_params(q, k, v, o, lse, **kw)
+    need = int(lib().attn_fwd_workspace_size(ctypes.byref(p)))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        p.workspace = _ptr(workspace)
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    return p, workspace
 
 
 def bwd_params(dout, q, k, v, o, lse, dq, dk, dv, workspace, dbias=None, **kw) -> BwdParams:

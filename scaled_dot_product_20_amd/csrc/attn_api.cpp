@@ -328,7 +328,7 @@ Split split_of(const attn_bwd_params* p) {
   sp.nkv = B * H * ((Sk + crow - 1) / crow);
   sp.nq = B * H * ((Sq + crow - 1) / crow);
   sp.part_bytes = (bytes() + 255) / 256 * 256;
-  sp.bytes = sp.part_bytes + ((uint64_t)(4 * (nkv + nq)) + 255) / 256 * 256;
+  sp.bytes = sp.part_bytes + ((uint64_t)(4 * (sp.nkv + sp.nq)) + 255) / 256 * 256;
   return sp;
 }
 
@@ -415,8 +415,10 @@ attn_fwd_params inner_fwd(const attn_fwd_params* p, uintptr_t ws, const Pack& pk
   copy_strides(ks, p->heads, pk.Dp, in.k_stride);
   copy_strides(ks, p->heads, pk.Dp, in.v_stride);
   copy_strides(qs, p->heads, pk.Dp, in.o_stride);
-  in.workspace = nullptr;
-  in.workspace_bytes = 0;
+  // The rest of the caller's workspace, after the copies (the key-split
+  // tail's, when large enough).
+  in.workspace = ws ? reinterpret_cast<void*>(ws + pk.bytes) : nullptr;
+  in.workspace_bytes = p->workspace_bytes > pk.bytes ? p->workspace_bytes - pk.bytes : 0;
   return in;
 }
 
@@ -437,7 +439,41 @@ attn_bwd_params inner_bwd(const attn_bwd_params* p, uintptr_t ws, const Pack& pk
   return in;
 }
 
-uint64_t fwd_ws_bytes(const attn_fwd_params* p) { return in_place_fwd(p) ? 0 : pack_of(p, false).bytes; }
+// Key-split tail workspace of an in-place forward (the ping-pong launch in
+// attn_fwd.hip): fp16 / bf16 at head dims up to 128 without optional
+// features or ATTN_FLAG_NO_SPLIT, a band the ping-pong kernel takes (at
+// least 1024 keys wide, or unbounded on a side) spanning at least two parts
+// of kKsMinKeys keys.  Sized for one full round of a 256-CU device, so it
+// depends on the call only; whether the launch splits a tail depends on the
+// device and the grid.
+uint64_t ks_bytes(const attn_fwd_params* p) {
+  if (p->dtype == ATTN_FP32 || p->head_dim > 128 || feat_on(p) || (p->flags & ATTN_FLAG_NO_SPLIT)) return 0;
+  const bool inf = p->window_left == ATTN_WINDOW_INF || p->window_right == ATTN_WINDOW_INF;
+  const int64_t width = (int64_t)p->window_left + p->window_right + 1;
+  if (!inf && width < 1024) return 0;
+  const int64_t kb = inf ? p->seqlen_k : std::min<int64_t>(p->seqlen_k, width + 255);
+  return kb >= 2 * sdpa::kKsMinKeys ? sdpa::ks_ws_bytes(p->head_dim) : 0;
+}
+
+// Workspace a forward needs: a repacked call's padded copies (0 in place).
+uint64_t fwd_req_bytes(const attn_fwd_params* p) { return in_place_fwd(p) ? 0 : pack_of(p, false).bytes; }
+
+// Workspace a forward can use: what it needs, then the key-split tail's
+// (of the in-place call it runs).
+uint64_t fwd_ws_bytes(const attn_fwd_params* p) {
+  if (in_place_fwd(p)) return ks_bytes(p);
+  const Pack pk = pack_of(p, false);
+  const attn_fwd_params in = inner_fwd(p, 0, pk);
+  return pk.bytes + ks_bytes(&in);
+}
+
+// Workspace bytes the forward uses of a caller's workspace: the key-split
+// part only when all of it is there (and 256-byte aligned).
+uint64_t fwd_used_bytes(const attn_fwd_params* p) {
+  const uint64_t req = fwd_req_bytes(p), all = fwd_ws_bytes(p);
+  const bool ok = p->workspace && (reinterpret_cast<uintptr_t>(p->workspace) & 255u) == 0 && p->workspace_bytes >= all;
+  return ok ? all : req;
+}
 
 uint64_t bwd_ws_bytes(const attn_bwd_params* p) {
   if (in_place_bwd(p)) return inner_ws_bytes(p);
@@ -505,9 +541,10 @@ hipError_t check_fwd(const attn_fwd_params* p, bool ws = true) {
   if (err != hipSuccess) return err;
   const Side qs = side_of(p, true), ks = side_of(p, false);
   const int64_t esz = elem_bytes(p->dtype), B = p->batch, H = p->heads, D = p->head_dim, DV = dim_v(p);
-  const uint64_t need = ws ? fwd_ws_bytes(p) : 0;
-  if (need && (!p->workspace || p->workspace_bytes < need || (reinterpret_cast<uintptr_t>(p->workspace) & 255u)))
+  const uint64_t req = ws ? fwd_req_bytes(p) : 0;
+  if (req && (!p->workspace || p->workspace_bytes < req || (reinterpret_cast<uintptr_t>(p->workspace) & 255u)))
     return hipErrorInvalidValue;
+  const uint64_t need = ws ? fwd_used_bytes(p) : 0;
   const uintptr_t w0 = reinterpret_cast<uintptr_t>(p->workspace);
   const Extent outs[3] = {extent_of(p->o, p->o_stride, B, H, qs, DV, esz), lse_extent(p),
                           need ? Extent{w0, w0 + (uintptr_t)need} : Extent{0, 0}};
@@ -581,6 +618,14 @@ sdpa::FwdArgs fwd_args(const attn_fwd_params* p) {
   a.f = feat_args(p);
   a.feat = feat_on(p);
   a.no_split = (p->flags & ATTN_FLAG_NO_SPLIT) ? 1 : 0;
+  // The key-split tail's partials, when the caller's workspace holds them
+  // (the launch may still not split: it depends on the grid).
+  const uint64_t kb = ks_bytes(p);
+  const uintptr_t ws = reinterpret_cast<uintptr_t>(p->workspace);
+  if (kb && ws && (ws & 255u) == 0 && p->workspace_bytes >= kb) {
+    a.ks_part = reinterpret_cast<float*>(ws);
+    a.ks_units = (int)sdpa::ks_units(p->head_dim);
+  }
   return a;
 }
 

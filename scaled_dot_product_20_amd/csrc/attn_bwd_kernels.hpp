@@ -93,28 +93,6 @@ __device__ __forceinline__ void store_partial_q(float* part_q, long long rows_q,
     }
 }
 
-// Arrival of a split copy at its block: after a barrier (the workgroup's
-// partial stores happen before it), lane 0 counts the workgroup in with one
-// release / acquire add, so the fence work is paid once per workgroup, not
-// per wave; the workgroup that brings the count to n resets the counter
-// (for the next call on the workspace), acquires the other copies' stores
-// and returns true: it sums the partials.  No workgroup waits for another,
-// so the grid drains in any schedule.
-__device__ __forceinline__ bool last_arrival(unsigned* cnt, int n) {
-  __shared__ int s_last;
-  __syncthreads();  // the workgroup's partial stores happen before lane 0's release
-  if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev + 1u == (unsigned)n;
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
-}
-
 // The last copy's epilogue for one block: rows [lo, hi) of sequence b, head
 // h (partial row part_row(mode, S, b, r0, i)) get the sum of their G partial
 // rows in copy order (so the result does not depend on which copy is last),

@@ -118,6 +118,32 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Arrival of a workgroup that has stored its partial results for a block
+// shared by n workgroups.  Every wave first waits until its own stores have
+// completed (are in its XCD's L2; a workgroup barrier alone does not wait
+// for other waves' global stores), then, after a barrier, lane 0 counts the
+// workgroup in with one agent-scope release / acquire add, whose release
+// writes the L2 back for the other XCDs: the fence work is paid once per
+// workgroup, not per wave.  The workgroup that brings the count to n resets
+// the counter (for the next call on the buffer), acquires the others'
+// stores and returns true: it combines the partials.  No workgroup waits
+// for another, so the grid drains in any schedule.
+__device__ __forceinline__ bool last_arrival(unsigned* cnt, int n) {
+  __shared__ int s_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev + 1u == (unsigned)n;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = s_last != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
 // ------------------------------------------------------------------- window
 
 // Bounds lo <= j - i <= hi of one sequence (0-based local indices), clamped

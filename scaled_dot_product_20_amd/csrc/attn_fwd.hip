@@ -24,6 +24,7 @@
 //     AOTriton 0.15b notes) and O^T += V^T P^T on the matrix cores.
 // Epilogue: O = acc / l, LSE = ln(2) * (m + log2 l); rows with no visible key
 // get O = 0 and LSE = +inf.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -940,36 +941,35 @@ struct FwdPP {
   }
 };
 
-// Workgroups of the ping-pong kernel per CU: two at head_dim 64, where a
-// wave fits in 128 registers, so one workgroup's start (Q rows, first tiles)
-// and end (O rows) overlap the other's steady state (192x16x512x64 fp16:
-// 0.427 -> 0.374 ms); one otherwise.
+// Workgroups of the ping-pong kernel per CU (pp_wg_per_cu): two at
+// head_dim 64, where a wave fits in 128 registers, so one workgroup's start
+// (Q rows, first tiles) and end (O rows) overlap the other's steady state
+// (192x16x512x64 fp16: 0.427 -> 0.374 ms); one otherwise.
 template <int D>
-constexpr int pp_per_cu() { return D <= 64 ? 2 : 1; }
+constexpr int pp_per_cu() { return pp_wg_per_cu(D); }
 
-template <typename M, int D, int BN>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2 * pp_per_cu<D>(), 2 * pp_per_cu<D>()))) void
-attn_fwd16pp_kernel(FwdArgs a, int nq) {
-  // The grid covers logical blocks [0, gridDim.x) of nq 256-row blocks per
-  // (batch, head); the rest, if any, go to the split tail kernel.
+// One 256-row block (bh, qb) of the ping-pong kernel.  With KS the
+// workgroup is part `part` of `np` over the block's key tiles and stores
+// its partial into slot `slot` of the key-split partials instead of O and
+// LSE.
+template <typename M, int D, int BN, bool KS>
+__device__ __forceinline__ void fwd16pp_block(const FwdArgs& a, typename M::elem* kv_s, int bh, int qb, int part,
+                                              int np, int slot) {
   using PP = FwdPP<M, D, BN>;
   using F = typename PP::F;
   using T = typename M::elem;
-  constexpr int NT = 512, BM = 256, DVT = F::DVT;
-  __shared__ __attribute__((aligned(1024))) T kv_s[2 * PP::NSTG * F::TILE];
+  constexpr int BM = 256, DVT = F::DVT;
 
   const ProblemArgs& P = a.p;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, P.B * P.H, P.ragged);
-  const int bh = gp.bh, h = bh % P.H, b = bh / P.H;
-  const int qb = nq - 1 - gp.i;
+  const int h = bh % P.H, b = bh / P.H;
 
   long long q0, k0;
   int sq, sk;
   seq_rows(P, b, q0, sq, k0, sk);
   const int i0 = qb * BM;
-  if (i0 >= sq) return;
+  if (i0 >= sq) return;  // every part of the block (and its merge) returns here
   const Window w = seq_window(P.wl, P.wr, P.diag, sq, sk);
 
   const T* qp = (const T*)a.q.ptr + b * a.q.sb + h * a.q.sh + q0 * a.q.ss;
@@ -1014,7 +1014,15 @@ attn_fwd16pp_kernel(FwdArgs a, int nq) {
 #pragma unroll
   for (int dt = 0; dt < DVT; ++dt) acc[dt] = zero16();
 
-  if (!block_empty) {
+  x.t0 = (int)(jlo / BN);
+  x.nt = block_empty ? 0 : (int)(jhi / BN) - x.t0 + 1;
+  if constexpr (KS) {
+    // Part `part` takes tiles [nt part / np, nt (part + 1) / np) of the block's.
+    const int s0 = (int)((long long)x.nt * part / np), s1 = (int)((long long)x.nt * (part + 1) / np);
+    x.t0 += s0;
+    x.nt = s1 - s0;
+  }
+  if (x.nt > 0) {
     LdsOffsets<M, D> lo;
     lo.init(lane);
     typename PP::Dma dma;
@@ -1024,8 +1032,8 @@ attn_fwd16pp_kernel(FwdArgs a, int nq) {
     for (int i = 0; i < PP::NSTG; ++i) {
       x.ks[i] = kv_s + i * F::TILE;
       x.vs[i] = kv_s + (PP::NSTG + i) * F::TILE;
-      zero_unused_slots<T, D, BN, NT>(x.ks[i], tid);
-      zero_unused_slots<T, D, BN, NT>(x.vs[i], tid);
+      zero_unused_slots<T, D, BN, 512>(x.ks[i], tid);
+      zero_unused_slots<T, D, BN, 512>(x.vs[i], tid);
     }
     typename PP::VOff vo;
     vo.init(lo);
@@ -1033,8 +1041,6 @@ attn_fwd16pp_kernel(FwdArgs a, int nq) {
     x.vp = (const T*)a.v.ptr + b * a.v.sb + h * a.v.sh + k0 * a.v.ss;
     x.kss = a.k.ss;
     x.vss = a.v.ss;
-    x.t0 = (int)(jlo / BN);
-    x.nt = (int)(jhi / BN) - x.t0 + 1;
     if (!grp_b) {
       // K_0 and K_1 up front; this wave's part of K_0 lands before the barrier.
       dma.issue(x.ks[0], x.kp + (long long)x.t0 * BN * a.k.ss, a.k.ss, sk - x.t0 * BN, x.gw, lane);
@@ -1050,6 +1056,21 @@ attn_fwd16pp_kernel(FwdArgs a, int nq) {
       PP::template run<1>(x, lo, vo, dma, qf, m, l, acc);
     else
       PP::template run<0>(x, lo, vo, dma, qf, m, l, acc);
+  }
+
+  if constexpr (KS) {
+    // This part's unnormalised (O^T, m, l) per lane (l: the lane's half of
+    // the row sum); the merge kernel combines the block's parts.
+    constexpr int NC = ks_chunks(D);
+    float4* pw = reinterpret_cast<float4*>(a.ks_part) + ((long long)slot * 8 + wave) * NC * 64 + lane;
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        pw[(4 * dt + q4) * 64] = make_float4(acc[dt][4 * q4], acc[dt][4 * q4 + 1], acc[dt][4 * q4 + 2],
+                                             acc[dt][4 * q4 + 3]);
+    pw[(NC - 1) * 64] = make_float4(m, l, 0.f, 0.f);
+    return;
   }
 
   if (wave_live) {
@@ -1069,6 +1090,96 @@ attn_fwd16pp_kernel(FwdArgs a, int nq) {
       if (g == 0) lp[qi * P.olse_ss] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
     }
   }
+}
+
+// The ping-pong grid: logical blocks [0, gridDim.x) of nq 256-row blocks per
+// (batch, head), in grid_pos order; the rest, if any, go to a tail kernel.
+template <typename M, int D, int BN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2 * pp_per_cu<D>(), 2 * pp_per_cu<D>()))) void
+attn_fwd16pp_kernel(FwdArgs a, int nq) {
+  using PP = FwdPP<M, D, BN>;
+  using T = typename M::elem;
+  __shared__ __attribute__((aligned(1024))) T kv_s[2 * PP::NSTG * PP::F::TILE];
+  const GridPos gp = grid_pos(blockIdx.x, gridDim.x, nq, a.p.B * a.p.H, a.p.ragged);
+  fwd16pp_block<M, D, BN, false>(a, kv_s, gp.bh, nq - 1 - gp.i, 0, 1, 0);
+}
+
+// (batch, head) and block index along the sequence of logical block L of a
+// grid of nq blocks per (batch, head), in grid_pos's logical order.
+__device__ __forceinline__ GridPos logical_pos(const ProblemArgs& P, int L, int nq) {
+  const int nbh = P.B * P.H;
+  return P.ragged ? GridPos{L % nbh, L / nbh} : GridPos{L / nq, L % nq};
+}
+
+// The key-split tail: np workgroups per logical block lbase + blockIdx.x /
+// np (the blocks after the ping-pong grid's, in the same order), part
+// blockIdx.x % np of its key tiles, into partial slot blockIdx.x.
+template <typename M, int D, int BN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2 * pp_per_cu<D>(), 2 * pp_per_cu<D>()))) void
+attn_fwd16ppks_kernel(FwdArgs a, int nq, int lbase, int np) {
+  using PP = FwdPP<M, D, BN>;
+  using T = typename M::elem;
+  __shared__ __attribute__((aligned(1024))) T kv_s[2 * PP::NSTG * PP::F::TILE];
+  const GridPos gp = logical_pos(a.p, lbase + (int)blockIdx.x / np, nq);
+  fwd16pp_block<M, D, BN, true>(a, kv_s, gp.bh, nq - 1 - gp.i, (int)blockIdx.x % np, np, (int)blockIdx.x);
+}
+
+// The key-split tail's merge: one wave per workgroup, wave w (rows 32 w ..
+// 32 w + 31) of tail block blockIdx.x / 8, which combines the block's np
+// slots in slot order, m = max_s m_s, O^T = sum_s 2^(m_s - m) O_s^T, l
+// likewise, and writes O = O^T / l and LSE as the ping-pong epilogue does.
+// The kernel boundary orders the tail grid's stores before these loads.
+template <typename M, int D>
+__global__ __launch_bounds__(64) void attn_fwd16ksmerge_kernel(FwdArgs a, int nq, int lbase, int np) {
+  using T = typename M::elem;
+  constexpr int DVT = (D + 31) / 32, NC = ks_chunks(D);
+  const ProblemArgs& P = a.p;
+  const int tb = (int)blockIdx.x / 8, wave = (int)blockIdx.x % 8, lane = threadIdx.x, r = lane & 31, g = lane >> 5;
+  const GridPos gp = logical_pos(P, lbase + tb, nq);
+  const int h = gp.bh % P.H, b = gp.bh / P.H, qb = nq - 1 - gp.i;
+  long long q0, k0;
+  int sq, sk;
+  seq_rows(P, b, q0, sq, k0, sk);
+  const int iw0 = qb * 256 + 32 * wave, qi = iw0 + r;
+  if (iw0 >= sq) return;  // whole wave: no partial was stored for these rows' block, or they are past the end
+  const float4* pb = reinterpret_cast<const float4*>(a.ks_part) + ((long long)tb * np * 8 + wave) * NC * 64 + lane;
+  const long long SLOT = 8LL * NC * 64;
+  float mx = -INFINITY;
+  for (int s = 0; s < np; ++s) mx = fmaxf(mx, pb[s * SLOT + (NC - 1) * 64].x);
+  float l = 0.f;
+  f32x16 acc[DVT];
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt) acc[dt] = zero16();
+  for (int s = 0; s < np; ++s) {
+    const float4 ml = pb[s * SLOT + (NC - 1) * 64];
+    const float f = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - mx);
+    l = __builtin_fmaf(f, ml.y, l);
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 o = pb[s * SLOT + (4 * dt + q4) * 64];
+        acc[dt][4 * q4] = __builtin_fmaf(f, o.x, acc[dt][4 * q4]);
+        acc[dt][4 * q4 + 1] = __builtin_fmaf(f, o.y, acc[dt][4 * q4 + 1]);
+        acc[dt][4 * q4 + 2] = __builtin_fmaf(f, o.z, acc[dt][4 * q4 + 2]);
+        acc[dt][4 * q4 + 3] = __builtin_fmaf(f, o.w, acc[dt][4 * q4 + 3]);
+      }
+  }
+  const float lt = halves_sum(l);
+  if (qi >= sq) return;
+  T* orow = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + (q0 + qi) * a.o.ss;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DVT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * dt + 8 * q4 + 4 * g;
+      if (d < D)
+        store4<T>(orow + d, acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv, acc[dt][4 * q4 + 2] * inv,
+                  acc[dt][4 * q4 + 3] * inv);
+    }
+  float* lp = a.lse + b * P.olse_sb + h * P.olse_sh + q0 * P.olse_ss;
+  if (g == 0) lp[qi * P.olse_ss] = lt > 0.f ? (mx + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
 }
 
 // -------------------------------------------- 16-bit forward, grid tail
@@ -1282,24 +1393,13 @@ static hipError_t launch_fwd_t(const FwdArgs& a, const Ex& ex) {
   if constexpr (S::k16) {
     if constexpr (S::PP) if (pp) {
       // Full rounds of 256-row workgroups (pp_per_cu per CU) on the
-      // ping-pong kernel.  With at most three of them, a last round at most
-      // a quarter full goes to the split tail kernel, which then fills every
-      // CU once (1x32x6630x128: 0.717 ms against 0.743 ms).  With more
-      // rounds, or a fuller last round, the tail's share is too small to pay
-      // for the split kernel's one wave per SIMD (1x32x15300x128: 3.63
-      // against 3.46).  A grid of at most a quarter as many blocks as CUs
+      // ping-pong kernel.  A grid of at most a quarter as many blocks as CUs
       // goes to the split kernel whole: four workgroups per block, each over
       // half the keys, still fit one round (1x2x512x64: 8.9 against 15.7
       // us; 1x8x2048x128: 40.4 against 51.3 us), where a grid of half the
       // CUs would take two (4x8x1024x128: 46.8 against 33.0 us).
       long long nmain = nblk;
       const long long cu = device_cu_count(), cus = cu * pp_per_cu<D>();
-      if (!a.no_split) {
-        if (cus > 0 && nblk >= cus && nblk < 4 * cus && 4 * (nblk % cus) <= cus)
-          nmain = nblk - nblk % cus;
-        else if (cu > 0 && 4 * nblk <= cu)
-          nmain = 0;
-      }
       const int nqi = (int)nq;
       // Key tiles of 32 at head_dim <= 64: four waves per SIMD leave 128
       // registers, which the 64-key tile's scores overran (spilled to
@@ -1307,6 +1407,39 @@ static hipError_t launch_fwd_t(const FwdArgs& a, const Ex& ex) {
       // bf16: 380 against 404 us).
       constexpr int PBN = D <= 64 ? 32 : BN;
       hipError_t err = hipSuccess;
+      if (!a.no_split && cu > 0 && 4 * nblk > cu && a.ks_part != nullptr) {
+        // With a key-split workspace, the r blocks of a last, partly filled
+        // round run as np = min(8, cus / r) ping-pong workgroups each, every
+        // part over at least kKsMinKeys keys of the block's band, so the
+        // tail fills the round (1x32x6630x128: 64 tail blocks as 256 parts).
+        const long long r = nblk % cus, nm = nblk - r;
+        long long kb = a.p.Sk;
+        if (a.p.wl != kWindowInf && a.p.wr != kWindowInf) kb = std::min(kb, (long long)a.p.wl + a.p.wr + 256);
+        const long long np = r > 0 ? std::min(std::min(8LL, cus / r), kb / kKsMinKeys) : 0;
+        if (np >= 2 && r * np <= a.ks_units) {
+          if (nm > 0)
+            err = ex(reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, PBN>), "attn_fwd16pp_kernel",
+                     (unsigned)nm, 512u, a, nqi);
+          if (err == hipSuccess)
+            err = ex(reinterpret_cast<const void*>(&attn_fwd16ppks_kernel<M, D, PBN>), "attn_fwd16ppks_kernel",
+                     (unsigned)(r * np), 512u, a, nqi, (int)nm, (int)np);
+          if (err != hipSuccess) return err;
+          return ex(reinterpret_cast<const void*>(&attn_fwd16ksmerge_kernel<M, D>), "attn_fwd16ksmerge_kernel",
+                    (unsigned)(8 * r), 64u, a, nqi, (int)nm, (int)np);
+        }
+      }
+      // Without it: with at most three full rounds, a last round at most a
+      // quarter full goes to the split tail kernel, which then fills every
+      // CU once (1x32x6630x128: 0.717 ms against 0.743 ms).  With more
+      // rounds, or a fuller last round, the tail's share is too small to pay
+      // for the split kernel's one wave per SIMD (1x32x15300x128: 3.63
+      // against 3.46).
+      if (!a.no_split) {
+        if (cus > 0 && nblk >= cus && nblk < 4 * cus && 4 * (nblk % cus) <= cus)
+          nmain = nblk - nblk % cus;
+        else if (cu > 0 && 4 * nblk <= cu)
+          nmain = 0;
+      }
       if (nmain > 0)
         err = ex(reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, PBN>), "attn_fwd16pp_kernel",
                  (unsigned)nmain, 512u, a, nqi);

@@ -100,7 +100,30 @@ struct FwdArgs {
   FeatArgs f;    // optional features (read by the FEAT kernels only)
   int feat;      // any feature present: the FEAT kernels run
   int no_split;  // the ping-pong grid alone, no key-split workgroups
+  // Key-split tail of the 16-bit ping-pong forward (null ks_part: off).
+  // The blocks of the grid's last, partly filled round run as np workgroups
+  // each, workgroup s of a block over the s-th of np near-equal runs of its
+  // key tiles; each stores its unnormalised (O^T, m, l) per wave and lane
+  // into slot blockIdx.x of ks_part (ks_chunks(D) float4 per lane, chunk-
+  // major, 8 waves x 64 lanes per slot), and a merge grid then combines each
+  // block's np slots in slot order.  ks_units: slots ks_part holds.
+  float* ks_part;
+  int ks_units;
 };
+
+// Ping-pong forward workgroups per CU: two at head dims up to 64, where a
+// wave fits in 128 registers; one otherwise.
+__host__ __device__ constexpr int pp_wg_per_cu(int D) { return D <= 64 ? 2 : 1; }
+// float4 chunks of one lane's key-split partial: O^T accumulators of
+// ceil(D / 32) 32-column blocks (4 chunks each), then (m, l, 0, 0).
+__host__ __device__ constexpr int ks_chunks(int D) { return 4 * ((D + 31) / 32) + 1; }
+// Key-split workspace: one full round of slots on a 256-CU device.
+constexpr long long kKsRoundCu = 256;
+inline long long ks_units(int D) { return kKsRoundCu * pp_wg_per_cu(D); }
+inline unsigned long long ks_ws_bytes(int D) { return (unsigned long long)ks_units(D) * 8 * 64 * ks_chunks(D) * 16; }
+// Fewest keys of a block's band per key-split part: below this, the parts'
+// start and end (Q rows, first tiles, partial stores) outweigh the split.
+constexpr long long kKsMinKeys = 1024;
 
 struct BwdArgs {
   ProblemArgs p;

@@ -372,7 +372,8 @@ def test_workspace_size():
     assert split_bytes(big) == 0
     assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(big))) == 2 * 8 * 16 * 1024 * 4
     for B, H, S, D, dt in ((1, 2, 128, 64, bd.FP32), (1, 1, 4000, 128, bd.BF16), (1, 2, 700, 128, bd.BF16), (3, 5, 700, 80, bd.FP16),
-                           (1, 8, 1023, 128, bd.BF16), (2, 1, 8000, 64, bd.FP32)):
+                           (1, 8, 1023, 128, bd.BF16), (2, 1, 8000, 64, bd.FP32),
+                           (1, 31, 200, 64, bd.FP32)):  # fp32 counters: twice the 128-row blocks
         f = dense_params(B=B, H=H, S=S, D=D, dtype=dt)
         stat = ((B * H * S * 4 + 255) // 256) * 256
         assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f))) == 2 * stat + split_bytes(f), (B, H, S, D)
@@ -719,3 +720,63 @@ def test_repacked_workspace_sizes():
     assert lib.attn_fwd_workspace_size(ctypes.byref(f)) > 0
     f.head_dim = 300
     assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == 0  # malformed (above the largest built dim)
+
+
+def ks_bytes(f):
+    """Key-split tail workspace of an in-place forward, from its documented
+    rule: fp16 / bf16 at head dims up to 128, no optional features and no
+    ATTN_FLAG_NO_SPLIT, a band at least 1024 keys wide (or unbounded on a
+    side) spanning at least 2048 keys of seqlen_k (a band of width w spans
+    up to w + 255 keys of a 256-row block); then one full round of
+    workgroup slots of a 256-CU device (two per CU at head dims up to 64),
+    each 8 waves x 64 lanes x (4 ceil(D / 32) + 1) float4."""
+    if f.dtype == bd.FP32 or f.head_dim > 128 or f.flags & bd.FLAG_NO_SPLIT:
+        return 0
+    if f.bias or f.alibi_slopes or f.dropout_p:
+        return 0
+    inf = INF in (f.window_left, f.window_right)
+    width = f.window_left + f.window_right + 1
+    if not inf and width < 1024:
+        return 0
+    kb = f.seqlen_k if inf else min(f.seqlen_k, width + 255)
+    if kb < 2048:
+        return 0
+    units = 256 * (2 if f.head_dim <= 64 else 1)
+    chunks = 4 * -(-f.head_dim // 32) + 1
+    return units * 8 * 64 * chunks * 16
+
+
+def test_forward_key_split_workspace():
+    """attn_fwd_workspace_size adds the key-split tail's partials to what a
+    call needs (nothing in place, the padded copies when repacked); the
+    forward runs without them (attn_fwd_check accepts no workspace for an
+    in-place call), and a repacked call needs only its copies."""
+    lib = bd.lib()
+    cases = [  # (dtype, D, S, window, expect key-split bytes)
+        (bd.BF16, 128, 6630, (INF, INF), True), (bd.FP16, 64, 2048, (INF, 0), True),
+        (bd.BF16, 80, 4096, (1500, 1500), True), (bd.BF16, 96, 2047, (INF, INF), False),
+        (bd.BF16, 128, 4096, (1200, 3), False), (bd.BF16, 128, 4096, (500, 300), False),
+        (bd.FP32, 64, 8192, (INF, INF), False), (bd.BF16, 192, 8192, (INF, INF), False),
+        (bd.FP16, 32, 3000, (-1, 2000), True)]
+    for dt, D, S, (wl, wr), expect in cases:
+        f = dense_params(B=1, H=4, S=S, D=D, dtype=dt)
+        f.window_left, f.window_right = wl, wr
+        n = ks_bytes(f)
+        assert (n > 0) == expect, (dt, D, S, wl, wr)
+        assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == n, (dt, D, S, wl, wr)
+        assert fcheck(f) == OK
+        f.flags = bd.FLAG_NO_SPLIT
+        assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == 0
+        f.flags = 0
+        f.dropout_p = 0.25
+        assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == 0
+    # Repacked (head dim 100 runs at 128): copies, then the inner call's share.
+    f = dense_params(B=1, H=2, S=4096, D=100, dtype=bd.BF16)
+    r256 = lambda n: -(-n // 256) * 256
+    copies = 4 * r256(4096 * 2 * 128 * 2)
+    inner = dense_params(B=1, H=2, S=4096, D=128, dtype=bd.BF16)
+    assert lib.attn_fwd_workspace_size(ctypes.byref(f)) == copies + ks_bytes(inner)
+    f.workspace, f.workspace_bytes = addr(12), copies           # the copies alone suffice
+    assert fcheck(f) == OK
+    f.workspace_bytes = copies - 256
+    assert fcheck(f) == INVALID

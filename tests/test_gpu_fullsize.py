@@ -70,14 +70,14 @@ def launch_bench_sequence(w, dtype, dev, q, k, v, do):
     o, lse = bd.attn_fwd(q, k, v, **kw)
     fkw = dict(cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None)
     fkw.update(kw)
-    fp = bd.fwd_params(q, k, v, o, lse, **fkw)
+    fp, fws = bd.prepare_fwd(q, k, v, o, lse, **fkw)
     bp, (dq, dk, dv, _ws) = bd.prepare_bwd(do, q, k, v, o, lse, **kw)
     calls = (("attn_fwd", fp), ("attn_bwd_preprocess", bp), ("attn_bwd_dkdv_dq", bp))
     plan = {name: bd.plan(name, params) for name, params in calls}
     for name, params in calls:
         bd.launch(name, params)
     torch.cuda.synchronize()
-    return (o, lse, dq, dk, dv), plan, _ws
+    return (o, lse, dq, dk, dv), plan, (_ws, fws)
 
 
 FULL = [(name, dt) for name, w in wls.workloads().items() if name != "tiny_f32" for dt in w.dtypes]

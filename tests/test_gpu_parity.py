@@ -8,6 +8,8 @@ import pytest
 import torch
 
 from parity_util import INF, TOL, Case, max_err, say
+from oracle import oracle as orc
+from scaled_dot_product_20_amd import workloads as wl
 from scaled_dot_product_20_amd import binding as bd
 
 pytestmark = pytest.mark.gpu
@@ -321,6 +323,110 @@ def test_forward_grid_tail(D, window, diag):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     H = cus * (2 if D <= 64 else 1) // 4 + 1
     Case(B=1, H=H, Sq=1000, Sk=1100, D=D, window=window, diag=diag, seed=700 + D).check(bwd=False)
+
+
+def ks_rule(nblk, D, Sk, window):
+    """The key-split tail the forward's launch takes with a workspace, from
+    its documented rule: (ping-pong blocks, tail blocks r, parts np) when a
+    grid of nblk 256-row blocks has more than a quarter as many blocks as
+    CUs and its last round (pp = 1 workgroup per CU, 2 at head_dim <= 64) is
+    partly filled with r blocks, np = min(8, round / r, band keys / 1024) is
+    at least 2 and r np fits the slots (one round of a 256-CU device);
+    else None."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    ppc = 2 if D <= 64 else 1
+    cus = cu * ppc
+    kb = Sk if INF in window else min(Sk, window[0] + window[1] + 256)
+    r = nblk % cus
+    npart = min(8, cus // r, kb // 1024) if r else 0
+    if 4 * nblk > cu and npart >= 2 and r * npart <= 256 * ppc:
+        return nblk - r, r, npart
+    return None
+
+
+@pytest.mark.parametrize("dtype,D,H,Sq,Sk,window,diag,tail_heads", [
+    (torch.bfloat16, 128, 5, 4096, 4096, (INF, INF), "top_left", False),
+    (torch.bfloat16, 128, 5, 4096, 4096, (INF, 0), "top_left", False),
+    (torch.float16, 128, 5, 4096, 4096, (1500, 1500), "bottom_right", False),
+    (torch.float16, 64, 560, 256, 2048, (INF, INF), "top_left", True),
+    (torch.bfloat16, 128, 300, 256, 4096, (INF, INF), "top_left", True),
+    (torch.bfloat16, 96, 300, 256, 4096, (INF, 0), "bottom_right", True)])
+def test_forward_key_split_tail(dtype, D, H, Sq, Sk, window, diag, tail_heads):
+    """With a workspace, the blocks of a partly filled last round of the
+    ping-pong forward run as np key-split workgroups each (after the
+    ping-pong grid, if any), whose partials a merge grid combines; without
+    one, the earlier tail.
+    Plans and grid sizes, run-to-run bits, and both paths against the
+    oracle: every head, or (tail_heads, one 256-row block per head) the
+    tail's heads and the ping-pong grid's first and last."""
+    nq = -(-Sq // 256)
+    nblk = nq * H
+    rule = ks_rule(nblk, D, Sk, window)
+    say(f"case key-split tail dtype={dtype} D={D} H={H} Sq={Sq} Sk={Sk} window={window} diag={diag} rule={rule}")
+    if rule is None:
+        pytest.skip("this device's CU count gives no key-split tail for the shape")
+    nm, r, npart = rule
+    q, k, v = wl.draw([(1, H, Sq, D), (1, H, Sk, D), (1, H, Sk, D)], 900 + D + H, dtype)
+    gq, gk, gv = (t.cuda() for t in (q, k, v))
+    kw = dict(scale=D ** -0.5, window=window, diag=diag, cu_seqlens_q=None, cu_seqlens_k=None,
+              max_seqlen_q=None, max_seqlen_k=None)
+    outs = {}
+    for use_ws in (True, False):
+        o = torch.empty_like(gq)
+        lse = torch.empty(1, H, Sq, dtype=torch.float32, device="cuda")
+        if use_ws:
+            p, ws = bd.prepare_fwd(gq, gk, gv, o, lse, **kw)
+            assert ws is not None
+        else:
+            p, ws = bd.fwd_params(gq, gk, gv, o, lse, **kw), None
+        pl = bd.plan("attn_fwd", p)
+        names = [n for n, _, _ in pl]
+        say(f"  workspace={use_ws} plan {pl}")
+        if use_ws:
+            assert names == ["attn_fwd16pp_kernel"] * (nm > 0) + ["attn_fwd16ppks_kernel", "attn_fwd16ksmerge_kernel"]
+            assert pl[-2][1] == r * npart and pl[-1][1] == 8 * r and (nm == 0 or pl[0][1] == nm), pl
+        else:
+            assert "attn_fwd16ppks_kernel" not in names
+        bd.launch("attn_fwd", p)
+        torch.cuda.synchronize()
+        o1, lse1 = o.clone(), lse.clone()
+        bd.launch("attn_fwd", p)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o1) and torch.equal(lse, lse1), "two runs differ"
+        outs[use_ws] = (o1, lse1)
+        del ws
+    if tail_heads:
+        assert nq == 1
+        hs = sorted({0, nm - 1} | set(range(nm, nblk)))
+    else:
+        hs = list(range(H))
+    ro, rl = orc.fwd(q[:, hs].contiguous(), k[:, hs].contiguous(), v[:, hs].contiguous(), scale=D ** -0.5,
+                     window=window, diag=diag)
+    for use_ws, (o, lse) in outs.items():
+        eo = max_err("O", o[:, hs], ro, TOL[dtype])
+        el = max_err("LSE", lse[:, hs], rl, TOL[dtype], inf_exact=True)
+        say(f"  workspace={use_ws} heads {len(hs)}: O {eo:.2e} LSE {el:.2e}")
+
+
+def test_forward_key_split_tail_varlen():
+    """Packed sequences of lengths 4096, 3000, 70, 0 and 2500 (one head,
+    head_dim 80): 80 ragged 256-row blocks, all in the key-split tail on a
+    256-CU device; the 70-row sequence's block has two key tiles, so one of
+    its three parts has none.  Plan, then both runs against the oracle."""
+    lens = [4096, 3000, 70, 0, 2500]
+    c = Case(layout="thd", B=len(lens), H=1, D=80, lens_q=lens, lens_k=lens, seed=910)
+    rule = ks_rule(len(lens) * 16, 80, max(lens), (INF, INF))
+    if rule is None:
+        pytest.skip("this device's CU count gives no key-split tail for the shape")
+    q, k, v, _ = (t.cuda() for t in c.cpu)
+    o = torch.empty_like(q)
+    lse = torch.empty(1, q.shape[0], dtype=torch.float32, device="cuda")
+    p, ws = bd.prepare_fwd(q, k, v, o, lse, **{kk: vv for kk, vv in c.kw_gpu("cuda").items() if kk != "split"})
+    pl = bd.plan("attn_fwd", p)
+    say(f"  plan {pl}")
+    assert [n for n, _, _ in pl] == ["attn_fwd16ppks_kernel", "attn_fwd16ksmerge_kernel"], pl
+    assert pl[0][1] == rule[1] * rule[2] and pl[1][1] == 8 * rule[1], pl
+    c.check(bwd=False)
 
 
 @pytest.mark.parametrize("dtype,D,sq,sk,window,diag", [
