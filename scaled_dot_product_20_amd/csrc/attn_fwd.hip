@@ -1124,17 +1124,21 @@ attn_fwd16ppks_kernel(FwdArgs a, int nq, int lbase, int np) {
   fwd16pp_block<M, D, BN, true>(a, kv_s, gp.bh, nq - 1 - gp.i, (int)blockIdx.x % np, np, (int)blockIdx.x);
 }
 
-// The key-split tail's merge: one wave per workgroup, wave w (rows 32 w ..
-// 32 w + 31) of tail block blockIdx.x / 8, which combines the block's np
+// The key-split tail's merge: one wave per workgroup, for rows 32 w .. 32 w
+// + 31 (wave w's) and columns 32 c .. 32 c + 31 of tail block blockIdx.x /
+// (8 C) (C = ceil(D / 32) column blocks), which combines the block's np
 // slots in slot order, m = max_s m_s, O^T = sum_s 2^(m_s - m) O_s^T, l
-// likewise, and writes O = O^T / l and LSE as the ping-pong epilogue does.
-// The kernel boundary orders the tail grid's stores before these loads.
+// likewise, and writes O = O^T / l (and, for c = 0, LSE) as the ping-pong
+// epilogue does.  Each part's loads are issued before the previous part's
+// products.  The kernel boundary orders the tail grid's stores before
+// these loads.
 template <typename M, int D>
 __global__ __launch_bounds__(64) void attn_fwd16ksmerge_kernel(FwdArgs a, int nq, int lbase, int np) {
   using T = typename M::elem;
   constexpr int DVT = (D + 31) / 32, NC = ks_chunks(D);
   const ProblemArgs& P = a.p;
-  const int tb = (int)blockIdx.x / 8, wave = (int)blockIdx.x % 8, lane = threadIdx.x, r = lane & 31, g = lane >> 5;
+  const int bid = (int)blockIdx.x, dt = bid % DVT, wave = (bid / DVT) % 8, tb = bid / (8 * DVT);
+  const int lane = threadIdx.x, r = lane & 31, g = lane >> 5;
   const GridPos gp = logical_pos(P, lbase + tb, nq);
   const int h = gp.bh % P.H, b = gp.bh / P.H, qb = nq - 1 - gp.i;
   long long q0, k0;
@@ -1142,44 +1146,48 @@ __global__ __launch_bounds__(64) void attn_fwd16ksmerge_kernel(FwdArgs a, int nq
   seq_rows(P, b, q0, sq, k0, sk);
   const int iw0 = qb * 256 + 32 * wave, qi = iw0 + r;
   if (iw0 >= sq) return;  // whole wave: no partial was stored for these rows' block, or they are past the end
-  const float4* pb = reinterpret_cast<const float4*>(a.ks_part) + ((long long)tb * np * 8 + wave) * NC * 64 + lane;
   const long long SLOT = 8LL * NC * 64;
+  const float4* pb = reinterpret_cast<const float4*>(a.ks_part) + ((long long)tb * np * 8 + wave) * NC * 64 + lane;
   float mx = -INFINITY;
   for (int s = 0; s < np; ++s) mx = fmaxf(mx, pb[s * SLOT + (NC - 1) * 64].x);
+  // Chunks 4 dt .. 4 dt + 3 (this column block) and NC - 1 (m, l) of a slot.
+  auto load = [&](int s, float4* c) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) c[q4] = pb[s * SLOT + (4 * dt + q4) * 64];
+    c[4] = pb[s * SLOT + (NC - 1) * 64];
+  };
+  float4 cur[5], nxt[5];
+  load(0, cur);
   float l = 0.f;
-  f32x16 acc[DVT];
+  float4 o[4];
 #pragma unroll
-  for (int dt = 0; dt < DVT; ++dt) acc[dt] = zero16();
+  for (int q4 = 0; q4 < 4; ++q4) o[q4] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < np; ++s) {
-    const float4 ml = pb[s * SLOT + (NC - 1) * 64];
-    const float f = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - mx);
-    l = __builtin_fmaf(f, ml.y, l);
+    if (s + 1 < np) load(s + 1, nxt);
+    const float f = cur[4].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(cur[4].x - mx);
+    l = __builtin_fmaf(f, cur[4].y, l);
 #pragma unroll
-    for (int dt = 0; dt < DVT; ++dt)
+    for (int q4 = 0; q4 < 4; ++q4) {
+      o[q4].x = __builtin_fmaf(f, cur[q4].x, o[q4].x);
+      o[q4].y = __builtin_fmaf(f, cur[q4].y, o[q4].y);
+      o[q4].z = __builtin_fmaf(f, cur[q4].z, o[q4].z);
+      o[q4].w = __builtin_fmaf(f, cur[q4].w, o[q4].w);
+    }
+    if (s + 1 < np)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 o = pb[s * SLOT + (4 * dt + q4) * 64];
-        acc[dt][4 * q4] = __builtin_fmaf(f, o.x, acc[dt][4 * q4]);
-        acc[dt][4 * q4 + 1] = __builtin_fmaf(f, o.y, acc[dt][4 * q4 + 1]);
-        acc[dt][4 * q4 + 2] = __builtin_fmaf(f, o.z, acc[dt][4 * q4 + 2]);
-        acc[dt][4 * q4 + 3] = __builtin_fmaf(f, o.w, acc[dt][4 * q4 + 3]);
-      }
+      for (int q4 = 0; q4 < 5; ++q4) cur[q4] = nxt[q4];
   }
   const float lt = halves_sum(l);
   if (qi >= sq) return;
   T* orow = (T*)a.o.ptr + b * a.o.sb + h * a.o.sh + (q0 + qi) * a.o.ss;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
-  for (int dt = 0; dt < DVT; ++dt)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 32 * dt + 8 * q4 + 4 * g;
-      if (d < D)
-        store4<T>(orow + d, acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv, acc[dt][4 * q4 + 2] * inv,
-                  acc[dt][4 * q4 + 3] * inv);
-    }
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int d = 32 * dt + 8 * q4 + 4 * g;
+    if (d < D) store4<T>(orow + d, o[q4].x * inv, o[q4].y * inv, o[q4].z * inv, o[q4].w * inv);
+  }
   float* lp = a.lse + b * P.olse_sb + h * P.olse_sh + q0 * P.olse_ss;
-  if (g == 0) lp[qi * P.olse_ss] = lt > 0.f ? (mx + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
+  if (dt == 0 && g == 0) lp[qi * P.olse_ss] = lt > 0.f ? (mx + __builtin_amdgcn_logf(lt)) * kLn2 : INFINITY;
 }
 
 // -------------------------------------------- 16-bit forward, grid tail
@@ -1425,7 +1433,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, const Ex& ex) {
                      (unsigned)(r * np), 512u, a, nqi, (int)nm, (int)np);
           if (err != hipSuccess) return err;
           return ex(reinterpret_cast<const void*>(&attn_fwd16ksmerge_kernel<M, D>), "attn_fwd16ksmerge_kernel",
-                    (unsigned)(8 * r), 64u, a, nqi, (int)nm, (int)np);
+                    (unsigned)(8 * ((D + 31) / 32) * r), 64u, a, nqi, (int)nm, (int)np);
         }
       }
       // Without it: with at most three full rounds, a last round at most a
