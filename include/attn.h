@@ -277,7 +277,8 @@ typedef struct {
  *    runs (at Dp when repacked) when that call is fp16 / bf16 at head_dim
  *    <= 128, has no optional feature and no ATTN_FLAG_NO_SPLIT, and its
  *    band is unbounded on a side or at least 1024 keys wide and spans at
- *    least 2048 keys (seqlen_k, or the band width + 255 if smaller):
+ *    least 2 F keys (seqlen_k, or the band width + 255 if smaller; F = 512
+ *    at head_dim <= 64, else 1024):
  *    256 * (2 if head_dim <= 64 else 1) slots of 8 * 64 * (4 * ceil(
  *    head_dim / 32) + 1) float4 (about 35 MiB at head_dim 128).
  * A workspace that holds both parts (and is 256-byte aligned) lets the
@@ -315,10 +316,12 @@ typedef struct {
  * is given, a small kernel that writes the rows past the used ones as
  * masked rows.  The ping-pong grid's last round, when partly filled:
  *  - with the key-split part of the workspace (attn_fwd_workspace_size),
- *    r blocks each run as np = min(8, round / r, band keys / 1024) >= 2
+ *    r blocks each run as np = min(8, round / r, band keys / F) >= 2
  *    ping-pong workgroups over near-equal runs of the block's key tiles,
  *    which store fp32 partials to the workspace, and a merge kernel
- *    combines each block's partials in a fixed order and writes its rows;
+ *    combines each block's partials in a fixed order and writes its rows
+ *    (a grid of fewer blocks than a round is all last round; one of at most
+ *    a quarter as many blocks as CUs only when r np >= the CU count);
  *  - otherwise, with at most three full rounds and a last round at most a
  *    quarter full, a kernel that splits that round's blocks over four
  *    64-row workgroups, each over two key halves merged in LDS.

@@ -443,7 +443,7 @@ attn_bwd_params inner_bwd(const attn_bwd_params* p, uintptr_t ws, const Pack& pk
 // attn_fwd.hip): fp16 / bf16 at head dims up to 128 without optional
 // features or ATTN_FLAG_NO_SPLIT, a band the ping-pong kernel takes (at
 // least 1024 keys wide, or unbounded on a side) spanning at least two parts
-// of kKsMinKeys keys.  Sized for one full round of a 256-CU device, so it
+// of ks_min_keys keys.  Sized for one full round of a 256-CU device, so it
 // depends on the call only; whether the launch splits a tail depends on the
 // device and the grid.
 uint64_t ks_bytes(const attn_fwd_params* p) {
@@ -452,7 +452,7 @@ uint64_t ks_bytes(const attn_fwd_params* p) {
   const int64_t width = (int64_t)p->window_left + p->window_right + 1;
   if (!inf && width < 1024) return 0;
   const int64_t kb = inf ? p->seqlen_k : std::min<int64_t>(p->seqlen_k, width + 255);
-  return kb >= 2 * sdpa::kKsMinKeys ? sdpa::ks_ws_bytes(p->head_dim) : 0;
+  return kb >= 2 * sdpa::ks_min_keys(p->head_dim) ? sdpa::ks_ws_bytes(p->head_dim) : 0;
 }
 
 // Workspace a forward needs: a repacked call's padded copies (0 in place).

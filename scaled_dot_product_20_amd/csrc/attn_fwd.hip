@@ -1415,16 +1415,22 @@ static hipError_t launch_fwd_t(const FwdArgs& a, const Ex& ex) {
       // bf16: 380 against 404 us).
       constexpr int PBN = D <= 64 ? 32 : BN;
       hipError_t err = hipSuccess;
-      if (!a.no_split && cu > 0 && 4 * nblk > cu && a.ks_part != nullptr) {
-        // With a key-split workspace, the r blocks of a last, partly filled
-        // round run as np = min(8, cus / r) ping-pong workgroups each, every
-        // part over at least kKsMinKeys keys of the block's band, so the
-        // tail fills the round (1x32x6630x128: 64 tail blocks as 256 parts).
+      if (!a.no_split && cu > 0 && a.ks_part != nullptr) {
+        // With a key-split workspace, the r blocks of a partly filled last
+        // round (the whole grid when it has fewer blocks than a round) run
+        // as np = min(8, cus / r) ping-pong workgroups each, every part over
+        // at least ks_min_keys(D) keys of the block's band, so the tail
+        // fills the round (1x32x6630x128: 64 tail blocks as 256 parts).  A
+        // grid of at most a quarter as many blocks as CUs takes this only
+        // when its parts cover every CU; else the split kernel below, whose
+        // 64-row workgroups spread a small grid further (1x2x2048x64: 22.0
+        // against 23.4 us; but 1x2x8192x128: 77 against 132 us, 1x1x16384x128:
+        // 133 against 255 us, 1x4x4096x128: 48.8 against 69.7 us).
         const long long r = nblk % cus, nm = nblk - r;
         long long kb = a.p.Sk;
         if (a.p.wl != kWindowInf && a.p.wr != kWindowInf) kb = std::min(kb, (long long)a.p.wl + a.p.wr + 256);
-        const long long np = r > 0 ? std::min(std::min(8LL, cus / r), kb / kKsMinKeys) : 0;
-        if (np >= 2 && r * np <= a.ks_units) {
+        const long long np = r > 0 ? std::min(std::min(8LL, cus / r), kb / ks_min_keys(D)) : 0;
+        if (np >= 2 && r * np <= a.ks_units && (4 * nblk > cu || r * np >= cu)) {
           if (nm > 0)
             err = ex(reinterpret_cast<const void*>(&attn_fwd16pp_kernel<M, D, PBN>), "attn_fwd16pp_kernel",
                      (unsigned)nm, 512u, a, nqi);

@@ -122,8 +122,10 @@ constexpr long long kKsRoundCu = 256;
 inline long long ks_units(int D) { return kKsRoundCu * pp_wg_per_cu(D); }
 inline unsigned long long ks_ws_bytes(int D) { return (unsigned long long)ks_units(D) * 8 * 64 * ks_chunks(D) * 16; }
 // Fewest keys of a block's band per key-split part: below this, the parts'
-// start and end (Q rows, first tiles, partial stores) outweigh the split.
-constexpr long long kKsMinKeys = 1024;
+// start and end (Q rows, first tiles, partial stores of 8 x 64 x ks_chunks
+// float4) outweigh the split (2x16x1024x64 bf16 in two parts of 512 keys:
+// 28.3 against 31.8 us; 4x8x1024x128: 36.4 against 33.4 us).
+__host__ __device__ constexpr long long ks_min_keys(int D) { return D <= 64 ? 512 : 1024; }
 
 struct BwdArgs {
   ProblemArgs p;

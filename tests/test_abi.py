@@ -726,8 +726,9 @@ def ks_bytes(f):
     """Key-split tail workspace of an in-place forward, from its documented
     rule: fp16 / bf16 at head dims up to 128, no optional features and no
     ATTN_FLAG_NO_SPLIT, a band at least 1024 keys wide (or unbounded on a
-    side) spanning at least 2048 keys of seqlen_k (a band of width w spans
-    up to w + 255 keys of a 256-row block); then one full round of
+    side) spanning at least 2 F keys of seqlen_k (a band of width w spans
+    up to w + 255 keys of a 256-row block; F = 512 at head dims up to 64,
+    else 1024); then one full round of
     workgroup slots of a 256-CU device (two per CU at head dims up to 64),
     each 8 waves x 64 lanes x (4 ceil(D / 32) + 1) float4."""
     if f.dtype == bd.FP32 or f.head_dim > 128 or f.flags & bd.FLAG_NO_SPLIT:
@@ -739,7 +740,7 @@ def ks_bytes(f):
     if not inf and width < 1024:
         return 0
     kb = f.seqlen_k if inf else min(f.seqlen_k, width + 255)
-    if kb < 2048:
+    if kb < 2 * (512 if f.head_dim <= 64 else 1024):
         return 0
     units = 256 * (2 if f.head_dim <= 64 else 1)
     chunks = 4 * -(-f.head_dim // 32) + 1
@@ -757,7 +758,8 @@ def test_forward_key_split_workspace():
         (bd.BF16, 80, 4096, (1500, 1500), True), (bd.BF16, 96, 2047, (INF, INF), False),
         (bd.BF16, 128, 4096, (1200, 3), False), (bd.BF16, 128, 4096, (500, 300), False),
         (bd.FP32, 64, 8192, (INF, INF), False), (bd.BF16, 192, 8192, (INF, INF), False),
-        (bd.FP16, 32, 3000, (-1, 2000), True)]
+        (bd.FP16, 32, 3000, (-1, 2000), True), (bd.BF16, 64, 1024, (INF, INF), True),
+        (bd.BF16, 64, 1023, (INF, INF), False), (bd.BF16, 80, 1024, (INF, INF), False)]
     for dt, D, S, (wl, wr), expect in cases:
         f = dense_params(B=1, H=4, S=S, D=D, dtype=dt)
         f.window_left, f.window_right = wl, wr

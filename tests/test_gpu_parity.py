@@ -327,19 +327,20 @@ def test_forward_grid_tail(D, window, diag):
 
 def ks_rule(nblk, D, Sk, window):
     """The key-split tail the forward's launch takes with a workspace, from
-    its documented rule: (ping-pong blocks, tail blocks r, parts np) when a
-    grid of nblk 256-row blocks has more than a quarter as many blocks as
-    CUs and its last round (pp = 1 workgroup per CU, 2 at head_dim <= 64) is
-    partly filled with r blocks, np = min(8, round / r, band keys / 1024) is
-    at least 2 and r np fits the slots (one round of a 256-CU device);
+    its documented rule: (ping-pong blocks, tail blocks r, parts np) when
+    the last round (pp = 1 workgroup per CU, 2 at head_dim <= 64) of a grid
+    of nblk 256-row blocks is partly filled with r blocks, np = min(8, round
+    / r, band keys / F) is at least 2 (F = 512 at head_dim <= 64, else
+    1024), r np fits the slots (one round of a 256-CU device), and the grid
+    has more than a quarter as many blocks as CUs or r np covers the CUs;
     else None."""
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     ppc = 2 if D <= 64 else 1
     cus = cu * ppc
     kb = Sk if INF in window else min(Sk, window[0] + window[1] + 256)
     r = nblk % cus
-    npart = min(8, cus // r, kb // 1024) if r else 0
-    if 4 * nblk > cu and npart >= 2 and r * npart <= 256 * ppc:
+    npart = min(8, cus // r, kb // (512 if D <= 64 else 1024)) if r else 0
+    if npart >= 2 and r * npart <= 256 * ppc and (4 * nblk > cu or r * npart >= cu):
         return nblk - r, r, npart
     return None
 
@@ -350,7 +351,9 @@ def ks_rule(nblk, D, Sk, window):
     (torch.float16, 128, 5, 4096, 4096, (1500, 1500), "bottom_right", False),
     (torch.float16, 64, 560, 256, 2048, (INF, INF), "top_left", True),
     (torch.bfloat16, 128, 300, 256, 4096, (INF, INF), "top_left", True),
-    (torch.bfloat16, 96, 300, 256, 4096, (INF, 0), "bottom_right", True)])
+    (torch.bfloat16, 96, 300, 256, 4096, (INF, 0), "bottom_right", True),
+    (torch.bfloat16, 128, 2, 8192, 8192, (INF, INF), "top_left", False),   # small grid, parts cover the CUs
+    (torch.float16, 64, 32, 1024, 1024, (INF, 0), "top_left", False)])      # two parts of 512 keys
 def test_forward_key_split_tail(dtype, D, H, Sq, Sk, window, diag, tail_heads):
     """With a workspace, the blocks of a partly filled last round of the
     ping-pong forward run as np key-split workgroups each (after the
