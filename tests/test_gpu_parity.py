@@ -606,3 +606,31 @@ def test_seqused_rows(layout, dtype, D, window, diag, split):
         sq_f += aq[b]
         sk_f += ak[b]
     c.check(dev=dev)
+
+
+def test_forward_key_split_tail_repacked():
+    """A repacked call (head_dim 100, run at 128 on zero-padded copies) with
+    the key-split part of its workspace after the copies: the plan is the
+    copy-in, the key-split grid and its merge, the copy-out; O and LSE
+    against the oracle at head_dim 100."""
+    H, S, D = 5, 4096, 100
+    rule = ks_rule(H * S // 256, 128, S, (INF, INF))
+    say(f"case key-split tail repacked H={H} S={S} D={D} rule={rule}")
+    if rule is None:
+        pytest.skip("this device's CU count gives no key-split tail for the shape")
+    q, k, v = wl.draw([(1, H, S, D)] * 3, 920, torch.bfloat16)
+    gq, gk, gv = (t.cuda() for t in (q, k, v))
+    o = torch.empty_like(gq)
+    lse = torch.empty(1, H, S, dtype=torch.float32, device="cuda")
+    kw = dict(scale=D ** -0.5, window=(INF, INF), diag="top_left", cu_seqlens_q=None, cu_seqlens_k=None,
+              max_seqlen_q=None, max_seqlen_k=None)
+    p, ws = bd.prepare_fwd(gq, gk, gv, o, lse, **kw)
+    pl = bd.plan("attn_fwd", p)
+    say(f"  plan {pl}")
+    assert [n for n, _, _ in pl] == ["attn_repack_kernel", "attn_fwd16ppks_kernel", "attn_fwd16ksmerge_kernel",
+                                     "attn_repack_kernel"], pl
+    bd.launch("attn_fwd", p)
+    torch.cuda.synchronize()
+    ro, rl = orc.fwd(q, k, v, scale=D ** -0.5)
+    say(f"  O {max_err('O', o, ro, TOL[torch.bfloat16]):.2e} "
+        f"LSE {max_err('LSE', lse, rl, TOL[torch.bfloat16], inf_exact=True):.2e}")
