@@ -340,15 +340,17 @@ hipError_t attn_fwd(const attn_fwd_params *p, hipStream_t stream);
  * computed without floating-point atomics: results are run-to-run
  * identical.
  *
- * Split mode (small problems, unless ATTN_FLAG_NO_SPLIT): when the dK/dV or
- * the dQ grid (128 keys or queries per workgroup) would have fewer than 64
- * workgroups, and the call has no bias, ALiBi, dropout or dbias, each grid
- * is repeated so that copy g of n walks the g-th of n contiguous shares of
+ * Split mode (small and mid-size problems, unless ATTN_FLAG_NO_SPLIT): when
+ * the call has no bias, ALiBi, dropout or dbias and the dK/dV or the dQ
+ * grid (128 keys or queries per workgroup) would have fewer than 64
+ * workgroups (at fp16 / bf16 head dims 96 and 128: a dK/dV grid of at most
+ * 16), or, with seqlen_q and seqlen_k both at least 1024 (2048 at those
+ * head dims), fewer than 200 (65 at those head dims), each grid is
+ * repeated so that copy g of n walks the g-th of n contiguous shares of
  * the tiles it would visit (query tiles for dK/dV, key tiles for dQ), about
  * 256 workgroups in all (at most 8 copies, one per tile, fp32 partial sums
- * of at most 8 MiB; at fp16 / bf16 head dims 96 and 128 only while the
- * dK/dV grid has at most 16 workgroups); the copies store fp32 partial sums
- * in the workspace.  In fp32 each copy then counts itself in on an arrival
+ * of at most 64 MiB); the copies store fp32 partial sums in the
+ * workspace.  In fp32 each copy then counts itself in on an arrival
  * counter per block there, and the last copy of a block to arrive adds the
  * block's partials in copy order, scales, rounds and writes them (so the
  * result does not depend on which copy is last), and resets the counter; no
@@ -451,13 +453,16 @@ hipError_t attn_bwd_plan(const attn_bwd_params *p, uint32_t steps, hipStream_t s
  * For callers that cannot allocate device memory or pass a workspace: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  The same work and results as attn_bwd (same kernels, bit for
- * bit), with the workspace taken from a static array of
+ * bit; see the limit below), with the workspace taken from a static array of
  * ATTN_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
  * on until the process ends.  p->workspace and p->workspace_bytes are
  * ignored.  Allocates nothing, on the host or the device.
- *  - Limit: problems whose workspace (attn_bwd_workspace_size) exceeds
- *    ATTN_NOALLOC_SCRATCH_BYTES, i.e. more than about two million (head,
- *    query row) pairs, return hipErrorOutOfMemory before enqueuing anything.
+ *  - Limit: a call whose split-mode partial sums would make its workspace
+ *    (attn_bwd_workspace_size) exceed ATTN_NOALLOC_SCRATCH_BYTES runs
+ *    without split mode (its results are then those of attn_bwd with
+ *    ATTN_FLAG_NO_SPLIT); problems whose workspace exceeds the array even
+ *    so, i.e. more than about two million (head, query row) pairs, return
+ *    hipErrorOutOfMemory before enqueuing anything.
  *  - Every call on one device shares that device's array: calls that may
  *    overlap in time on one device (different streams, or other threads)
  *    race and must be ordered by the caller.  Nothing in it needs clearing

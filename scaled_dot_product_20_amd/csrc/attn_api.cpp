@@ -281,15 +281,24 @@ uint64_t delta_bytes(const attn_fwd_params* p) { return 2 * stat_section_bytes(p
 
 // Split mode of the backward (the launch rules in attn_bwd_kernels.hpp): taken for
 // calls without optional features whose dK/dV or dQ grid (128 keys or
-// queries per workgroup) has fewer than 64 workgroups, i.e. would leave at
-// least three quarters of a 256-CU GPU idle (at fp16 / bf16 head dims 96
-// and 128, only up to 16 dK/dV workgroups).  Each grid is repeated to reach
-// about 256 workgroups, at most 8 times and at most once per tile of the
-// axis it splits; the fp32 partial sums are capped at 8 MiB (fewer copies,
-// or no split, beyond that).  After the partials come the arrival counters,
-// one 4-byte word per dK/dV and per dQ block of the finest grid the launch
-// may pick.  Depends on the call only, so the workspace size and the launch
-// agree.
+// queries per workgroup) leaves most of the GPU idle:
+//  - fewer than 64 workgroups (at fp16 / bf16 head dims 96 and 128, whose
+//    unsplit dK/dV is the producer / consumer kernel the copies cannot use,
+//    only up to 16 dK/dV workgroups: 1x4x1000x128 bf16 45 us unsplit
+//    against 66 split);
+//  - else, over axes of at least 1024 rows (2048 at head dims 96 and 128),
+//    fewer than 200 workgroups (65 at head dims 96 and 128): 1x2x8192x64
+//    bf16 161 against 320 us unsplit, fp16 1x4x4096x80 121 against 241,
+//    fp32 1x8x2048x64 390 against 648, 1x12x2048x64 83 against 95, but
+//    1x30x1024x64 (240 workgroups) 62.7 against 58.1 and 2x16x512x64 34.5
+//    against 33.7; 1x2x4096x96 103 against 125, 1x4x2048x128 75 against 83,
+//    but 1x4x4096x128 (128 workgroups) 201 against 166.
+// Each grid is repeated to reach about 256 workgroups, at most 8 times and
+// at most once per tile of the axis it splits; the fp32 partial sums are
+// capped at 64 MiB (fewer copies, or no split, beyond that).  After the
+// partials come the arrival counters, one 4-byte word per dK/dV and per dQ
+// block of the finest grid the launch may pick.  Depends on the call only,
+// so the workspace size and the launch agree.
 struct Split {
   int gkv = 1, gq = 1;
   int64_t rows_q = 0, rows_k = 0;
@@ -305,11 +314,11 @@ Split split_of(const attn_bwd_params* p) {
   const Side qs = side_of(f, true), ks = side_of(f, false);
   const int64_t B = f->batch, H = f->heads, D = f->head_dim, Sq = f->seqlen_q, Sk = f->seqlen_k;
   const int64_t nkv = B * H * ((Sk + 127) / 128), nq = B * H * ((Sq + 127) / 128);
-  if (nkv == 0 || nq == 0 || (nkv >= 64 && nq >= 64)) return sp;
-  // fp16 / bf16 at head dims 96 and 128: the unsplit dK/dV runs producer /
-  // consumer workgroups, which the split copies cannot use; past 16 dK/dV
-  // blocks the unsplit path is as fast or faster.
-  if (f->dtype != ATTN_FP32 && (D == 96 || D == 128) && nkv > 16) return sp;
+  const bool pc = f->dtype != ATTN_FP32 && (D == 96 || D == 128);  // producer / consumer dK/dV unsplit
+  const int64_t lim = pc ? 65 : 200, minlen = pc ? 2048 : 1024;
+  if (nkv == 0 || nq == 0 || (nkv >= lim && nq >= lim)) return sp;
+  const bool small = pc ? nkv <= 16 : (nkv < 64 || nq < 64);
+  if (!small && (Sq < minlen || Sk < minlen)) return sp;
   const int64_t tile = f->dtype == ATTN_FP32 ? 32 : 64;  // query tile of dK/dV, key tile of dQ
   auto groups = [](int64_t nblk, int64_t ntiles) {
     return (int)std::max<int64_t>(1, std::min<int64_t>({(256 + nblk - 1) / nblk, 8, ntiles}));
@@ -319,7 +328,7 @@ Split split_of(const attn_bwd_params* p) {
   sp.rows_q = qs.stacked() ? f->total_q : B * Sq;
   sp.rows_k = ks.stacked() ? f->total_k : B * Sk;
   auto bytes = [&] { return (uint64_t)(4 * D * H * (2 * sp.gkv * sp.rows_k + sp.gq * sp.rows_q)); };
-  constexpr uint64_t kCap = 8u << 20;
+  constexpr uint64_t kCap = 64u << 20;
   while (bytes() > kCap && (sp.gkv > 1 || sp.gq > 1)) (sp.gkv >= sp.gq ? sp.gkv : sp.gq) -= 1;
   if (bytes() > kCap || (sp.gkv == 1 && sp.gq == 1)) return Split{};
   // Counters per block of the finest split grid: 64 rows in fp32 (two-wave
@@ -911,7 +920,15 @@ hipError_t attn_bwd_noalloc(const attn_bwd_params* p_in, hipStream_t stream) {
   const attn_bwd_params* p = bwd_v3(p_in, &tmp);
   hipError_t err = check_bwd(p, false);
   if (err != hipSuccess) return err;
-  const uint64_t need = bwd_ws_bytes(p);
+  uint64_t need = bwd_ws_bytes(p);
+  attn_bwd_params unsplit;
+  if (need > (uint64_t)ATTN_NOALLOC_SCRATCH_BYTES && !(p->fwd.flags & ATTN_FLAG_NO_SPLIT)) {
+    // The split mode's partials do not fit the array: the call without it.
+    unsplit = *p;
+    unsplit.fwd.flags |= ATTN_FLAG_NO_SPLIT;
+    p = &unsplit;
+    need = bwd_ws_bytes(p);
+  }
   if (need > (uint64_t)ATTN_NOALLOC_SCRATCH_BYTES) return hipErrorOutOfMemory;
   return on_stream_device(stream, [&] {
     void* ws = nullptr;

@@ -323,19 +323,24 @@ def split_bytes(f):
     """Partial-sum bytes of the backward's split mode, from its documented
     rule: split when the dK/dV or the dQ grid (128 rows per workgroup) has
     fewer than 64 workgroups (at fp16 / bf16 head dims 96 and 128, only up
-    to 16 dK/dV workgroups); copies = min(ceil(256 / workgroups), 8, tiles
-    of the split axis (64 rows, 32 in fp32)); fp32 partials of dK, dV (per
-    key copy) and dQ (per query copy), capped at 8 MiB by dropping copies
-    from the larger count; then one 4-byte arrival counter per dK/dV and
-    per dQ block of 64 rows (fp32) or 128 (fp16 / bf16); 0 when no copy is
-    left to split."""
+    to 16 dK/dV workgroups), or, over axes of at least 1024 rows (2048 at
+    fp16 / bf16 head dims 96 and 128), fewer than 200 workgroups (65 at
+    those head dims); copies = min(ceil(256 / workgroups), 8, tiles of the
+    split axis (64 rows, 32 in fp32)); fp32 partials of dK, dV (per key
+    copy) and dQ (per query copy), capped at 64 MiB by dropping copies from
+    the larger count; then one 4-byte arrival counter per dK/dV and per dQ
+    block of 64 rows (fp32) or 128 (fp16 / bf16); 0 when no copy is left to
+    split."""
     if f.flags & bd.FLAG_NO_SPLIT:
         return 0
     B, H, D, Sq, Sk = f.batch, f.heads, f.head_dim, f.seqlen_q, f.seqlen_k
     nkv, nq = B * H * -(-Sk // 128), B * H * -(-Sq // 128)
-    if nkv == 0 or nq == 0 or (nkv >= 64 and nq >= 64):
+    pc = f.dtype != bd.FP32 and D in (96, 128)
+    lim, minlen = (65, 2048) if pc else (200, 1024)
+    if nkv == 0 or nq == 0 or (nkv >= lim and nq >= lim):
         return 0
-    if f.dtype != bd.FP32 and D in (96, 128) and nkv > 16:
+    small = nkv <= 16 if pc else (nkv < 64 or nq < 64)
+    if not small and (Sq < minlen or Sk < minlen):
         return 0
     tile = 32 if f.dtype == bd.FP32 else 64
     gkv = max(1, min(-(-256 // nkv), 8, -(-Sq // tile)))
@@ -343,12 +348,12 @@ def split_bytes(f):
     rq = f.total_q if f.layout == bd.THD else B * Sq
     rk = f.total_k if f.layout == bd.THD else B * Sk
     nbytes = lambda: 4 * D * H * (2 * gkv * rk + gq * rq)
-    while nbytes() > 8 << 20 and (gkv > 1 or gq > 1):
+    while nbytes() > 64 << 20 and (gkv > 1 or gq > 1):
         if gkv >= gq:
             gkv -= 1
         else:
             gq -= 1
-    if nbytes() > 8 << 20 or (gkv == 1 and gq == 1):
+    if nbytes() > 64 << 20 or (gkv == 1 and gq == 1):
         return 0
     crow = 64 if f.dtype == bd.FP32 else 128
     ncnt = B * H * (-(-Sk // crow) + -(-Sq // crow))
@@ -373,7 +378,11 @@ def test_workspace_size():
     assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(big))) == 2 * 8 * 16 * 1024 * 4
     for B, H, S, D, dt in ((1, 2, 128, 64, bd.FP32), (1, 1, 4000, 128, bd.BF16), (1, 2, 700, 128, bd.BF16), (3, 5, 700, 80, bd.FP16),
                            (1, 8, 1023, 128, bd.BF16), (2, 1, 8000, 64, bd.FP32),
-                           (1, 31, 200, 64, bd.FP32)):  # fp32 counters: twice the 128-row blocks
+                           (1, 31, 200, 64, bd.FP32),  # fp32 counters: twice the 128-row blocks
+                           (1, 4, 4096, 64, bd.BF16), (1, 12, 2048, 64, bd.BF16), (1, 30, 1024, 64, bd.BF16),
+                           (2, 16, 512, 64, bd.BF16), (1, 2, 4096, 128, bd.BF16), (1, 4, 2048, 128, bd.BF16),
+                           (1, 4, 4096, 128, bd.BF16), (1, 4, 1000, 128, bd.BF16), (1, 8, 2048, 64, bd.FP32),
+                           (1, 2, 16384, 80, bd.FP16)):
         f = dense_params(B=B, H=H, S=S, D=D, dtype=dt)
         stat = ((B * H * S * 4 + 255) // 256) * 256
         assert lib.attn_bwd_workspace_size(ctypes.byref(bwd_params(f))) == 2 * stat + split_bytes(f), (B, H, S, D)

@@ -73,7 +73,10 @@ def test_tiny_fp32_config():
 
 
 @pytest.mark.parametrize("dtype,D,B,H,S", [(torch.float32, 64, 1, 2, 128), (torch.bfloat16, 128, 1, 2, 1000),
-                                           (torch.float16, 80, 2, 3, 300)])
+                                           (torch.float16, 80, 2, 3, 300),
+                                           # mid-size grids over long axes: 128 dK/dV blocks at D = 64,
+                                           # 64 at D = 128
+                                           (torch.bfloat16, 64, 1, 8, 2048), (torch.bfloat16, 128, 1, 2, 4096)])
 def test_split_mode_plan_and_bits(dtype, D, B, H, S):
     """Small problems run the backward in split mode: the plan lists the
     preprocess and one grid of split dK/dV and dQ copies (in fp32 each

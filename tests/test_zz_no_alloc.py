@@ -42,3 +42,27 @@ def test_noalloc_equals_attn_bwd_twice_shrinking():
 def test_noalloc_fp32_after_larger():
     _run(Case(B=1, H=2, Sq=300, D=80, dtype=torch.float32, window=(INF, INF), seed=33))
     _run(Case(B=1, H=1, Sq=17, Sk=40, D=32, dtype=torch.float32, window=(5, 5), seed=34))
+
+
+def test_noalloc_unsplit_when_split_partials_exceed_the_array():
+    """A problem whose split-mode partial sums would not fit the array
+    (1x4x4096x64 bf16: two copies of each grid, 25 MB of partials) runs
+    without split mode: bit for bit attn_bwd with split off, and within the
+    oracle's bounds."""
+    case = Case(B=1, H=4, Sq=4096, D=64, dtype=torch.bfloat16, seed=35)
+    say(f"noalloc case B=1 H=4 Sq=Sk=4096 D=64 bf16 seed=35 (split partials over the array)")
+    q, k, v, do = (t.to("cuda:0") for t in case.cpu)
+    kw = case.kw_gpu("cuda:0")
+    o, lse = bd.attn_fwd(q, k, v, **kw)
+    assert bd.workspace_size(do, q, k, v, o, lse, **kw) > bd.NOALLOC_SCRATCH_BYTES
+    assert bd.workspace_size(do, q, k, v, o, lse, **dict(kw, split=False)) <= bd.NOALLOC_SCRATCH_BYTES
+    ref = bd.attn_bwd(do, q, k, v, o, lse, **dict(kw, split=False))
+    got = tuple(torch.full_like(t, float("nan")) for t in ref)
+    bd.attn_bwd_noalloc(do, q, k, v, o, lse, *got, **kw)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(a, b), f"{name}: attn_bwd_noalloc differs from attn_bwd without split mode"
+    orc = case.oracle(bwd=True)
+    tol = 2 * TOL[case.dtype] * case.tol_factor()
+    errs = {n: max_err(n, t, orc[n], tol) for n, t in zip(("dq", "dk", "dv"), got)}
+    say("  errs", {n: f"{e:.2e}" for n, e in errs.items()})
