@@ -1382,8 +1382,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // One workgroup = 32*NW queries; each wave keeps its 32 queries' Q and dO
 // rows, LSE and Delta in registers and walks the key tiles its rows can
 // see, K and V copied HBM -> LDS as in the forward.  Per 32-key slice:
-// S^T = K Q^T and dP^T = V dO^T from row reads, dS^T = P^T o (dP^T - Delta),
-// dQ^T += K^T dS^T with K^T taken by transposing reads.  Key rows past the
+// S^T = K Q^T and dP^T - Delta = V dO^T - Delta from row reads (the first
+// product of dP^T accumulates onto a register block of -Delta: a lane's
+// elements all belong to its query row, so the block is the same for every
+// tile), dS^T = P^T o (dP^T - Delta), dQ^T += K^T dS^T with K^T taken by
+// transposing reads.  Key rows past the
 // sequence are copies of its last key and are masked out.
 template <typename M, int D, int BN>
 struct Dq16 {
@@ -1402,12 +1405,12 @@ struct Dq16 {
   static constexpr int NA = 2 * NS, NB = 2 * DVT;  // products per slice: S and dP, dQ
   static __device__ __forceinline__ void tile(const T* Ks, const T* Vs, const LdsOffsets<M, D>& lo,
                                               const RowFrags<M, D>& qf, const RowFrags<M, D>& dof, f32x16* dq,
-                                              float c, float lse2, float delta, bool masked, Window w, int j0,
-                                              int qi, int sk, int g) {
+                                              float c, float lse2, const f32x16& ndelta, bool masked, Window w,
+                                              int j0, int qi, int sk, int g) {
     if constexpr (D > 80) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        f32x16 s = zero16(), dp = zero16();
+        f32x16 s = zero16(), dp = ndelta;
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           s = M::mma(ld_row<M>(Ks + 32 * kt * L::PITCH, lo.row[st]), qf.f[st], s);
@@ -1420,7 +1423,7 @@ struct Dq16 {
         float ds[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lse2)) * (dp[e] - delta);
+          ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lse2)) * dp[e];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           frag dsf;
@@ -1443,7 +1446,7 @@ struct Dq16 {
       float ds[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, -lse2)) * (dp[kt][e] - delta);
+        ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, -lse2)) * dp[kt][e];
       M::pack(&ds[0], dsf[kt][0]);
       M::pack(&ds[8], dsf[kt][1]);
     };
@@ -1463,7 +1466,7 @@ struct Dq16 {
           if constexpr (I < KT * NA) {
             constexpr int kt = I / NA, st = (I % NA) / 2;
             if constexpr (I & 1)
-              dp[kt] = M::mma(A, dof.f[st], st == 0 ? zero16() : dp[kt]);
+              dp[kt] = M::mma(A, dof.f[st], st == 0 ? ndelta : dp[kt]);
             else
               s[kt] = M::mma(A, qf.f[st], st == 0 ? zero16() : s[kt]);
           } else {
@@ -1629,6 +1632,9 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
   const float delta = row_ok ? delp[qi] : 0.f;
   const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
   if (P.scale_log2 < 0.f) qf.negate();
+  f32x16 ndelta;  // the first dP product's accumulator input (FEAT: unused)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) ndelta[e] = -delta;
 
   f32x16 dq[DVT];
 #pragma unroll
@@ -1662,7 +1668,8 @@ __device__ __forceinline__ void dq16_body(int hw, int nblk) {
                                    t * BN, qi, sq, sk, g, f, b, h, P.H, P.Sq, P.Sk, row_ok);
         } else {
           const bool masked = classify(w, iw0, 32, (long long)t * BN, BN, sk) == kPartial;
-          F::tile(Pq ? k_s1 : k_s0, Pq ? v_s1 : v_s0, lo, qf, dof, dq, c, lse2, delta, masked, w, t * BN, qi, sk, g);
+          F::tile(Pq ? k_s1 : k_s0, Pq ? v_s1 : v_s0, lo, qf, dof, dq, c, lse2, ndelta, masked, w, t * BN, qi, sk,
+                  g);
         }
       }
       __syncthreads();
