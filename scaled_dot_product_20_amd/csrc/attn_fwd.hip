@@ -19,7 +19,9 @@
 //     c * max_j s_j), p = 2^(x - m) in one FMA and one exp;
 //   the reference max m of a row is only raised when the tile's max exceeds
 //     it by more than kRescaleSlack (so p <= 2^kRescaleSlack); O and l are
-//     rescaled only then, and skipped when no row of the wave moved;
+//     rescaled only then, and skipped when no row of the wave moved (the
+//     ping-pong kernel computes the tile's max only when a lane's sum of p
+//     against the current m passes 2^kRescaleSlack, or the row has no m);
 //   P is rounded to the working type (round to nearest even, the fix in the
 //     AOTriton 0.15b notes) and O^T += V^T P^T on the matrix cores.
 // Epilogue: O = acc / l, LSE = ln(2) * (m + log2 l); rows with no visible key
@@ -35,6 +37,7 @@ namespace sdpa {
 
 // Largest log2 growth of a row max absorbed without rescaling.
 constexpr float kRescaleSlack = 8.f;
+constexpr float kRescaleBound = 256.f;  // 2^kRescaleSlack
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
@@ -498,26 +501,36 @@ struct Fwd16 {
   }
 
   // Masks one row block's scores of a tile cut by the window or the
-  // sequence end, then raises the row's reference max m when the tile's max
-  // exceeds it by more than kRescaleSlack, rescaling l and O.  c >= 1e-30,
-  // so a masked score (-inf) always maps to -inf and then to p = 0.
+  // sequence end: key j = jb + r(e) is visible iff qi + lo <= j <= min(qi +
+  // hi, sk - 1).  c >= 1e-30, so a masked score (-inf) always maps to -inf
+  // and then to p = 0.
+  static __device__ __forceinline__ void mask(f32x16* s, Window w, int j0, int qi, int sk, int g) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const long long jb = (long long)j0 + 32 * kt + 4 * g;
+      mask_block(s[kt], vis_bits((long long)qi + w.lo - jb, min((long long)qi + w.hi, (long long)sk - 1) - jb));
+    }
+  }
+
+  // mask (when `masked`), then raise.
   static __device__ __forceinline__ void finalize(f32x16* s, bool masked, Window w, int j0, int qi, int sk,
                                                   float c, float& m, float& l, f32x16* acc, int g) {
-    if (masked) {
-      // Key j = jb + r(e) is visible iff qi + lo <= j <= min(qi + hi, sk - 1).
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const long long jb = (long long)j0 + 32 * kt + 4 * g;
-        mask_block(s[kt], vis_bits((long long)qi + w.lo - jb, min((long long)qi + w.hi, (long long)sk - 1) - jb));
-      }
-    }
+    if (masked) mask(s, w, j0, qi, sk, g);
+    raise(s, c, m, l, acc);
+  }
+
+  // Raises the row's reference max m when the tile's max exceeds it by more
+  // than `slack`, rescaling l and O.  Wave-level (the row max is exchanged
+  // between the half-waves).
+  static __device__ __forceinline__ void raise(const f32x16* s, float c, float& m, float& l, f32x16* acc,
+                                               float slack = kRescaleSlack) {
     float smax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) smax = fmaxf(smax, s[kt][e]);
     const float mx = halves_max(smax) * c;
-    const bool raise = mx > m + kRescaleSlack;  // also when m is still -inf
+    const bool raise = mx > m + slack;  // also when m is still -inf
     if (__builtin_amdgcn_ballot_w64(raise)) {
       const float alpha = raise ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
       if (raise) m = mx;
@@ -899,19 +912,34 @@ struct FwdPP {
       }
       if (mine(kk)) {
         const int t = x.t0 + kk;
-        F::finalize(s[0], t < x.full.t0 || t > x.full.t1, x.w, t * BN, x.qi, x.sk, x.c, m, l, acc, x.g);
-        const float nm = m == -INFINITY ? 0.f : -m;
-        float ls = 0.f;
+        if (t < x.full.t0 || t > x.full.t1) F::mask(s[0], x.w, t * BN, x.qi, x.sk, x.g);
+        // P = 2^(c s - m) against the current reference max, packed, and
+        // this lane's share of the row sum.
+        auto probs = [&]() __attribute__((always_inline)) {
+          const float nm = m == -INFINITY ? 0.f : -m;
+          float sum = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          float e2[16];
+          for (int kt = 0; kt < KT; ++kt) {
+            float e2[16];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            e2[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][kt][e], x.c, nm));
-            ls += e2[e];
+            for (int e = 0; e < 16; ++e) {
+              e2[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][kt][e], x.c, nm));
+              sum += e2[e];
+            }
+            M::pack(&e2[0], pf[kt][0]);
+            M::pack(&e2[8], pf[kt][1]);
           }
-          M::pack(&e2[0], pf[kt][0]);
-          M::pack(&e2[8], pf[kt][1]);
+          return sum;
+        };
+        float ls = probs();
+        // Each P of a lane is at most the lane's sum, so a sum within
+        // 2^kRescaleSlack keeps every P there without the tile's max.  A row
+        // with no reference max yet, or a larger (or non-finite) sum, takes
+        // the max first, raises m to it (no slack: the next tiles of such a
+        // row start from its new max) and computes the P again.
+        if (__builtin_amdgcn_ballot_w64(m == -INFINITY || !(ls <= kRescaleBound))) {
+          F::raise(s[0], x.c, m, l, acc, 0.f);
+          ls = probs();
         }
         l += ls;
       }
