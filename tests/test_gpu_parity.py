@@ -637,3 +637,41 @@ def test_forward_key_split_tail_repacked():
     ro, rl = orc.fwd(q, k, v, scale=D ** -0.5)
     say(f"  O {max_err('O', o, ro, TOL[torch.bfloat16]):.2e} "
         f"LSE {max_err('LSE', lse, rl, TOL[torch.bfloat16], inf_exact=True):.2e}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("kind", ["large_logits", "growing_scores", "negative_scale"])
+def test_pingpong_rescale_paths(dtype, kind):
+    """The ping-pong forward computes a tile's row max only when a lane's
+    sum of P against the row's current reference max passes 2^8 (or the row
+    has none yet), then raises the max and recomputes P.  These inputs take
+    that path: logits of tens (scale 1.7 at head_dim 128: sums overflow to
+    inf before the rescale), keys whose scores grow along the sequence (the
+    max rises tile after tile), and a negative scale.  O and LSE against the
+    oracle in the wide band the ping-pong kernel runs, and the backward
+    where the inputs stay within the tolerance model (the growing keys reach
+    |K| near 1000, and dQ's error from rounding dS to 16 bits grows with
+    |K|, which the N(0, 1) bounds do not cover)."""
+    H, S, D = 2, 700, 128
+    q, k, v, do = wl.draw([(1, H, S, D)] * 4, 930, torch.float32)
+    scale = D ** -0.5
+    if kind == "large_logits":
+        scale = 1.7
+    elif kind == "growing_scores":
+        k = k * (1.0 + torch.arange(S, dtype=torch.float32).view(1, 1, S, 1) / 64.0)
+        q = q.abs()  # with k's first column shifted, the scores of row i grow with j
+        k[..., 0] += torch.arange(S, dtype=torch.float32).view(1, 1, S) / 8.0
+    else:
+        scale = -0.3
+    q, k, v, do = (t.to(dtype) for t in (q, k, v, do))
+    # Split paths off: the whole grid on the ping-pong kernel, whatever the
+    # device's CU count.
+    c = Case(B=1, H=H, Sq=S, D=D, dtype=dtype, scale=scale, seed=930, split=False)
+    c.cpu = (q, k, v, do)
+    pl = bd.plan("attn_fwd", bd.fwd_params(q.cuda(), k.cuda(), v.cuda(), torch.empty_like(q, device="cuda"),
+                                           torch.empty(1, H, S, device="cuda"), scale=scale,
+                                           window=(INF, INF), diag="top_left", cu_seqlens_q=None,
+                                           cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+                                           split=False))
+    assert [n for n, _, _ in pl][0] == "attn_fwd16pp_kernel", pl
+    c.check(bwd=kind != "growing_scores")
