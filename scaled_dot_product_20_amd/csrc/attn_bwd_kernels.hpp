@@ -1135,33 +1135,41 @@ struct DkdvPC {
 
   // Consumer: dS of the previous tile (stage sp, P buffer xb) and
   // dK += dS^T Q (when FIN), then dP^T = V dO^T of the current tile (stage
-  // sc, when DP).
+  // sc, when DP).  The consumer's V fragments are negated and its dP^T
+  // accumulators start from the tile's Delta (element e of slice mq is row
+  // 32 mq + 8 (e / 4) + 4 g + e % 4, the order of the Delta row in LDS), so
+  // they hold Delta - dP and dS comes out negated (one multiply per
+  // element); the dK epilogue scales by -scale.
   template <bool FIN, bool DP>
   static __device__ __forceinline__ void consume(const T* sp, const f16x8* xb, const T* sc,
                                                  const LdsOffsets<M, D>& lo, const RowFrags<M, D>& vf, f32x16* dp,
                                                  f32x16* dk, int kw, int lane, int g) {
     const T* Qp = sp;
-    const float* del = reinterpret_cast<const float*>(sp + 2 * TILE) + BMQ;
     const T* dOs = sc + TILE;
     frag dsf[MQ][2];
-    // dS of slice MQ, rounded for dK.
+    // -dS of slice MQ, rounded for dK.
     auto ds_slice = [&](auto mqc) __attribute__((always_inline)) {
       constexpr int mq = decltype(mqc)::value;
       const f16x8 h0 = xb[((kw * MQ + mq) * 2 + 0) * 64 + lane], h1 = xb[((kw * MQ + mq) * 2 + 1) * 64 + lane];
       float ds[16];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 dd = *reinterpret_cast<const float4*>(del + 32 * mq + 8 * q4 + 4 * g);
-        const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int e = 4 * q4 + u;
-          ds[e] = (float)(e < 8 ? h0[e] : h1[e - 8]) * (dp[mq][e] - dv4[u]);
-        }
-      }
+      for (int e = 0; e < 16; ++e) ds[e] = (float)(e < 8 ? h0[e] : h1[e - 8]) * dp[mq][e];
       M::pack(&ds[0], dsf[mq][0]);
       M::pack(&ds[8], dsf[mq][1]);
     };
+    if constexpr (DP) {
+      const float* del = reinterpret_cast<const float*>(sc + 2 * TILE) + BMQ;
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 dd = *reinterpret_cast<const float4*>(del + 32 * mq + 8 * q4 + 4 * g);
+          dp[mq][4 * q4] = dd.x;
+          dp[mq][4 * q4 + 1] = dd.y;
+          dp[mq][4 * q4 + 2] = dd.z;
+          dp[mq][4 * q4 + 3] = dd.w;
+        }
+    }
     constexpr int B = FIN ? 0 : NB, E = DP ? NB + NA : NB;
     mfma_stream<B, E, PD>(
         [&](auto i) __attribute__((always_inline)) { return decltype(i)::value < NB ? tr_op(Qp, lo, decltype(i)::value)
@@ -1173,7 +1181,7 @@ struct DkdvPC {
             dk[dt] = M::mma(A, dsf[I / (2 * DVT)][(I / DVT) % 2], dk[dt]);
           } else {
             constexpr int j = I - NB, mq = j / NS, k = j % NS;
-            dp[mq] = M::mma(A, vf.f[k], k == 0 ? zero16() : dp[mq]);
+            dp[mq] = M::mma(A, vf.f[k], dp[mq]);
           }
         },
         [&](auto i) __attribute__((always_inline)) {
@@ -1249,7 +1257,7 @@ __device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
   RowFrags<M, D> kv;
   kv.load(prod ? kp + (long long)kj * a.k.ss : vp + (long long)kj * a.v.ss, wave_live && kj < sk, g);
   const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
-  if (prod && P.scale_log2 < 0.f) kv.negate();
+  if (prod ? P.scale_log2 < 0.f : true) kv.negate();  // consumers: -V (their dP^T starts from Delta)
 
   f32x16 acc[DVT];  // producer: dV, consumer: dK
 #pragma unroll
@@ -1359,7 +1367,7 @@ __device__ __forceinline__ void dkdv_pc_body(int hw, int nblk) {
 
   if (wave_live && kj < sk) {
     T* row = prod ? dvp + (long long)kj * a.dv.ss : dkp + (long long)kj * a.dk.ss;
-    const float sc = prod ? 1.f : P.scale;
+    const float sc = prod ? 1.f : -P.scale;  // the consumer's sums are of -dS
 #pragma unroll
     for (int dt = 0; dt < DVT; ++dt)
 #pragma unroll
