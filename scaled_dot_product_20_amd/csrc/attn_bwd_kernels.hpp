@@ -661,6 +661,12 @@ struct Dkdv16 {
   using frag = typename M::frag;
   static constexpr int MQ = BMQ / 32, NS = D / 16, DVT = (D + 31) / 32;
   static constexpr int TILE = BMQ * L::PITCH;
+  // Up to head_dim 128 (where it adds no spill): vf holds -V and the dP
+  // accumulators start from the slice's Delta (element e is query row 32 mq
+  // + 8 (e / 4) + 4 g + e % 4, the order of the Delta row in LDS), so they
+  // end at Delta - dP and the dK sums are of -dS (the caller negates dK once
+  // at the end); above, dS = P o (dP - Delta).
+  static constexpr bool kFold = D <= 128;
 
   // One query tile against this wave's 32 keys, one 32-row slice at a time
   // (two waves per SIMD; one slice at a time keeps the registers low).
@@ -671,6 +677,16 @@ struct Dkdv16 {
 #pragma unroll
     for (int mq = 0; mq < MQ; ++mq) {
       f32x16 s = zero16(), dp = zero16();
+      if constexpr (kFold) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 dd = *reinterpret_cast<const float4*>(dels + 32 * mq + 8 * q4 + 4 * g);
+          dp[4 * q4] = dd.x;
+          dp[4 * q4 + 1] = dd.y;
+          dp[4 * q4 + 2] = dd.z;
+          dp[4 * q4 + 3] = dd.w;
+        }
+      }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         s = M::mma(ld_row<M>(Qs + 32 * mq * L::PITCH, lo.row[st]), kf.f[st], s);
@@ -683,15 +699,21 @@ struct Dkdv16 {
       float p[16], ds[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int il = 32 * mq + 8 * q4 + 4 * g;
-        const float4 ll = *reinterpret_cast<const float4*>(lse2s + il);
-        const float4 dd = *reinterpret_cast<const float4*>(dels + il);
-        const float lv[4] = {ll.x, ll.y, ll.z, ll.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+        const float4 ll = *reinterpret_cast<const float4*>(lse2s + 32 * mq + 8 * q4 + 4 * g);
+        const float lv[4] = {ll.x, ll.y, ll.z, ll.w};
+        float dv4[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!kFold) {
+          const float4 dd = *reinterpret_cast<const float4*>(dels + 32 * mq + 8 * q4 + 4 * g);
+          dv4[0] = dd.x;
+          dv4[1] = dd.y;
+          dv4[2] = dd.z;
+          dv4[3] = dd.w;
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int e = 4 * q4 + u;
           p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
-          ds[e] = p[e] * (dp[e] - dv4[u]);
+          ds[e] = kFold ? p[e] * dp[e] : p[e] * (dp[e] - dv4[u]);
         }
       }
 #pragma unroll
@@ -875,6 +897,7 @@ __device__ __forceinline__ void dkdv16_body(const BwdArgs& a, unsigned hw, unsig
   vf.load(vp + (long long)kj * a.v.ss, wave_live && kj < sk, g);
   const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
   if (P.scale_log2 < 0.f) kf.negate();
+  if constexpr (!FEAT && F::kFold) vf.negate();  // Dkdv16::tile takes -V (its dP starts from Delta)
 
   f32x16 dk[DVT], dv[DVT];
 #pragma unroll
@@ -936,6 +959,11 @@ __device__ __forceinline__ void dkdv16_body(const BwdArgs& a, unsigned hw, unsig
       step(std::integral_constant<int, 0>{}, t);
       if (t + 1 <= t1) step(std::integral_constant<int, 1>{}, t + 1);
     }
+  }
+  if constexpr (!FEAT && F::kFold) {
+    // Dkdv16::tile summed -dS: dK's sign back, once.
+#pragma unroll
+    for (int dt = 0; dt < DVT; ++dt) dk[dt] = -dk[dt];
   }
 
   if constexpr (SPLIT) {
